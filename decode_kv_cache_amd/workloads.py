@@ -1,0 +1,298 @@
+"""Seeded synthetic workloads for paged-KV block transfer.
+
+This module is shared by the tests, the bench and the oracle checks.  It holds
+only input generation -- pool shapes, prompt lengths, block tables as an
+engine's block allocator would hand them out, and KV values -- and none of
+the transfer's own arithmetic (how many tokens move, which blocks are used,
+run merging, offsets or the reuse decision live in the library and,
+separately, in the oracle).
+
+Block allocation: a request of ``prompt_len`` tokens holds ceil(prompt_len /
+block_size) blocks on each side, listed in order.  The transfer may use fewer
+of them (the consumer recomputes the final prompt token), so block lists are
+often one entry longer than what moves.
+
+Workload names (sizes as in their descriptions):
+  tiny_push      2 layers, 8 KV heads, head_dim 64, block 16, bf16 NHD, pools
+                 of 256 blocks, one 200-token prompt, random permutations.
+  qwen32b_push   64 layers, 8 KV heads, head_dim 128, block 16, bf16 NHD, pools
+                 of 4096 blocks, one 8192-token prompt, block tables made of
+                 contiguous runs with geometric length (mean 4).
+  batched_push   same KV shape, 64 prompts uniform in [1024, 16384], pools of
+                 65536 blocks, geometric runs of mean 2; 64 logical layers on
+                 16 physical layer slabs per pool.
+  tp4_share      producer NHD 8 heads, consumer HND 2 heads (one TP4 rank),
+                 64 layers, head_dim 128, block 16, bf16, 32 x 4096-token
+                 prompts, random tables, pools of 16384 blocks.
+  multiturn_fp8  fp8 e4m3 KV with one fp32 scale per (layer, K/V, block), 48
+                 layers, 8 heads, head_dim 128, block 16; 32 sessions x 8
+                 turns, context +2048 tokens per turn, pools of 32768 blocks.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+from typing import Dict, List, Optional, Sequence
+
+import numpy as np
+
+BF16, FP8, U8 = "bf16", "fp8_e4m3", "u8"
+ELEM_BYTES = {BF16: 2, FP8: 1, U8: 1}
+
+
+@dataclass(frozen=True)
+class PoolSpec:
+    num_layers: int          # logical layers
+    num_blocks: int
+    block_size: int
+    num_heads: int
+    head_dim: int
+    dtype: str
+    layout: str = "NHD"
+    has_scales: bool = False
+    phys_layers: int = 0     # physical layer slabs (0: one per logical layer)
+
+    @property
+    def elem_bytes(self) -> int:
+        return ELEM_BYTES[self.dtype]
+
+    @property
+    def n_phys(self) -> int:
+        return self.phys_layers or self.num_layers
+
+    @property
+    def region_bytes(self) -> int:
+        return self.num_blocks * self.block_size * self.num_heads * self.head_dim * self.elem_bytes
+
+    @property
+    def pool_bytes(self) -> int:
+        return self.n_phys * 2 * self.region_bytes
+
+    def phys(self, layer: int) -> int:
+        return layer % self.n_phys
+
+
+@dataclass
+class Workload:
+    name: str
+    seed: int
+    src: PoolSpec
+    dst: PoolSpec
+    prompt_lens: List[int]
+    src_tables: List[np.ndarray]      # int32 per request (allocated blocks, in order)
+    dst_tables: List[np.ndarray]
+    extra: Dict = field(default_factory=dict)
+
+
+# ---------------------------------------------------------------------------
+# block tables
+# ---------------------------------------------------------------------------
+def alloc_blocks(prompt_len: int, block_size: int) -> int:
+    """Blocks an engine's allocator reserves for a prompt (ceil)."""
+    return -(-prompt_len // block_size)
+
+
+def permutation_table(rng: np.random.Generator, num_blocks: int) -> np.ndarray:
+    return rng.permutation(num_blocks).astype(np.int32)
+
+
+def geometric_run_table(rng: np.random.Generator, num_blocks: int, mean_run: float) -> np.ndarray:
+    """All pool blocks, ordered as shuffled contiguous segments whose lengths
+    are geometric on {1, 2, ...} with the given mean (the last segment cut at
+    the pool end)."""
+    p = 1.0 / mean_run
+    lens = []
+    total = 0
+    while total < num_blocks:
+        ln = int(rng.geometric(p))
+        ln = min(ln, num_blocks - total)
+        lens.append(ln)
+        total += ln
+    starts = np.cumsum([0] + lens[:-1])
+    order = rng.permutation(len(lens))
+    return np.concatenate([np.arange(starts[i], starts[i] + lens[i]) for i in order]).astype(np.int32)
+
+
+def split_tables(seq: np.ndarray, counts: Sequence[int]) -> List[np.ndarray]:
+    out, pos = [], 0
+    for c in counts:
+        out.append(seq[pos:pos + c].copy())
+        pos += c
+    if pos > len(seq):
+        raise ValueError("pool too small for the allocation")
+    return out
+
+
+def _children(seed: int, n: int) -> List[np.random.Generator]:
+    return [np.random.Generator(np.random.PCG64(s)) for s in np.random.SeedSequence(seed).spawn(n)]
+
+
+# ---------------------------------------------------------------------------
+# the workloads
+# ---------------------------------------------------------------------------
+def tiny_push(seed: int = 1001) -> Workload:
+    spec = PoolSpec(2, 256, 16, 8, 64, BF16)
+    r_src, r_dst = _children(seed, 2)
+    plen = [200]
+    a = [alloc_blocks(x, spec.block_size) for x in plen]
+    return Workload("tiny_push", seed, spec, spec, plen,
+                    split_tables(permutation_table(r_src, spec.num_blocks), a),
+                    split_tables(permutation_table(r_dst, spec.num_blocks), a))
+
+
+def qwen32b_push(seed: int = 1002) -> Workload:
+    spec = PoolSpec(64, 4096, 16, 8, 128, BF16)
+    r_src, r_dst = _children(seed, 2)
+    plen = [8192]
+    a = [alloc_blocks(x, spec.block_size) for x in plen]
+    return Workload("qwen32b_push", seed, spec, spec, plen,
+                    split_tables(geometric_run_table(r_src, spec.num_blocks, 4.0), a),
+                    split_tables(geometric_run_table(r_dst, spec.num_blocks, 4.0), a))
+
+
+def batched_push(seed: int = 1003, phys_layers: int = 16) -> Workload:
+    spec = PoolSpec(64, 65536, 16, 8, 128, BF16, phys_layers=phys_layers)
+    r_len, r_src, r_dst = _children(seed, 3)
+    plen = [int(x) for x in r_len.integers(1024, 16384, size=64, endpoint=True)]
+    a = [alloc_blocks(x, spec.block_size) for x in plen]
+    return Workload("batched_push", seed, spec, spec, plen,
+                    split_tables(geometric_run_table(r_src, spec.num_blocks, 2.0), a),
+                    split_tables(geometric_run_table(r_dst, spec.num_blocks, 2.0), a))
+
+
+def tp4_share(seed: int = 1004, tp_rank: int = 0) -> Workload:
+    src = PoolSpec(64, 16384, 16, 8, 128, BF16, layout="NHD")
+    dst = PoolSpec(64, 16384, 16, 2, 128, BF16, layout="HND")
+    r_src, r_dst = _children(seed, 2)
+    plen = [4096] * 32
+    a = [alloc_blocks(x, src.block_size) for x in plen]
+    return Workload("tp4_share", seed, src, dst, plen,
+                    split_tables(permutation_table(r_src, src.num_blocks), a),
+                    split_tables(permutation_table(r_dst, dst.num_blocks), a),
+                    extra={"tp_size": 4, "tp_rank": tp_rank})
+
+
+def multiturn_fp8(seed: int = 1005) -> Workload:
+    """32 sessions, 8 turns, context growing 2048 tokens per turn.  The decode
+    side keeps each session's blocks for its whole conversation (session s
+    owns slice s of one permutation, 896 blocks = 7 turns' context); the
+    prefill side allocates fresh blocks for the full context of each turn
+    (128*t blocks per session at turn t, from a new permutation).  The
+    ``src``/``dst`` pools of this workload are the decode and prefill pools:
+    reuse copies decode -> prefill."""
+    spec = PoolSpec(48, 32768, 16, 8, 128, FP8, has_scales=True)
+    sessions, turns, growth = 32, 8, 2048
+    rngs = _children(seed, 1 + turns)
+    per_session = alloc_blocks(growth * (turns - 1), spec.block_size)
+    dec = split_tables(permutation_table(rngs[0], spec.num_blocks), [per_session] * sessions)
+    pre = {}
+    for t in range(1, turns + 1):
+        need = alloc_blocks(growth * t, spec.block_size)
+        pre[t] = split_tables(permutation_table(rngs[t], spec.num_blocks), [need] * sessions)
+    return Workload("multiturn_fp8", seed, spec, spec, [growth] * sessions, dec, pre[1],
+                    extra={"sessions": sessions, "turns": turns, "growth": growth,
+                           "threshold": 512, "decode_tables": dec, "prefill_tables": pre})
+
+
+WORKLOADS = {
+    "tiny_push": tiny_push,
+    "qwen32b_push": qwen32b_push,
+    "batched_push": batched_push,
+    "tp4_share": tp4_share,
+    "multiturn_fp8": multiturn_fp8,
+}
+
+
+# ---------------------------------------------------------------------------
+# values
+# ---------------------------------------------------------------------------
+def _torch():
+    import torch
+    return torch
+
+
+def region_seed(seed: int, pool_tag: int, phys_layer: int, kv: int) -> int:
+    return (seed * 1_000_003 + pool_tag * 10_007 + phys_layer * 2 + kv) & 0x7FFF_FFFF_FFFF
+
+
+def fill_region(out, dtype: str, seed: int, device=None) -> None:
+    """Fill a uint8 tensor (one (layer, K/V) region) with seeded values:
+    N(0,1) rounded to bf16 or to fp8 e4m3fn, or uniform random bytes."""
+    torch = _torch()
+    dev = out.device if device is None else device
+    g = torch.Generator(device=dev)
+    g.manual_seed(seed)
+    n = out.numel()
+    if dtype == U8:
+        out.copy_(torch.randint(0, 256, (n,), generator=g, device=dev, dtype=torch.uint8))
+        return
+    eb = ELEM_BYTES[dtype]
+    chunk = 1 << 28
+    flat = out.view(-1)
+    for s in range(0, n // eb, chunk):
+        e = min(n // eb, s + chunk)
+        x = torch.randn(e - s, generator=g, device=dev, dtype=torch.float32)
+        if dtype == BF16:
+            y = x.to(torch.bfloat16).view(torch.uint8)
+        else:
+            y = x.to(torch.float8_e4m3fn).view(torch.uint8)
+        flat[s * eb:e * eb].copy_(y)
+        del x, y
+
+
+def fill_scales(out, seed: int) -> None:
+    """fp32 scales uniform in [0.5, 1.5), stored into a float32 tensor."""
+    torch = _torch()
+    g = torch.Generator(device=out.device)
+    g.manual_seed(seed)
+    out.copy_(torch.rand(out.shape, generator=g, device=out.device, dtype=torch.float32) + 0.5)
+
+
+def alloc_pool(spec: PoolSpec, device):
+    """One tensor per pool: uint8 [phys_layers, 2, region_bytes], plus fp32
+    scales [phys_layers, 2, num_blocks] when the pool has them."""
+    torch = _torch()
+    kv = torch.empty((spec.n_phys, 2, spec.region_bytes), dtype=torch.uint8, device=device)
+    sc = (torch.empty((spec.n_phys, 2, spec.num_blocks), dtype=torch.float32, device=device)
+          if spec.has_scales else None)
+    return kv, sc
+
+
+def fill_pool(spec: PoolSpec, kv, sc, seed: int, pool_tag: int, dtype: Optional[str] = None) -> None:
+    for p in range(spec.n_phys):
+        for k in range(2):
+            fill_region(kv[p, k], dtype or spec.dtype, region_seed(seed, pool_tag, p, k))
+            if sc is not None:
+                fill_scales(sc[p, k], region_seed(seed, pool_tag + 7, p, k))
+
+
+def random_case(seed: int, *, layout="NHD", dst_layout=None, elem_bytes=2, num_layers=2,
+                num_blocks=24, dst_blocks=None, block_size=4, num_heads=3, dst_heads=None,
+                head_dim=8, has_scales=False, num_requests=3, max_tokens=30,
+                run_mean=2.0, extra_ids=1):
+    """Small random case for brute-force checks: random prompt lengths (0 and
+    exact block multiples included by chance), block tables of geometric runs
+    so that merging has work to do, each list ``extra_ids`` entries longer than
+    the prompt's allocation."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    dtype = BF16 if elem_bytes == 2 else U8
+    src = PoolSpec(num_layers, num_blocks, block_size, num_heads, head_dim, dtype, layout, has_scales)
+    dst = PoolSpec(num_layers, dst_blocks or num_blocks, block_size, dst_heads or num_heads, head_dim,
+                   dtype, dst_layout or layout, has_scales)
+    plen = [int(x) for x in rng.integers(0, max_tokens + 1, size=num_requests)]
+    need = [alloc_blocks(x, block_size) + extra_ids for x in plen]
+    st = geometric_run_table(rng, src.num_blocks, run_mean)
+    dt = geometric_run_table(rng, dst.num_blocks, run_mean)
+    if sum(need) > min(len(st), len(dt)):
+        raise ValueError("pools too small for this case")
+    return Workload(f"random_{seed}", seed, src, dst, plen, split_tables(st, need), split_tables(dt, need))
+
+
+def host_values(spec: PoolSpec, seed: int, pool_tag: int):
+    """Host (numpy) pool contents for small cases: uint8 [L, 2, region] and
+    uint32 scale bits [L, 2, NB] (or None); uniform random bytes so that every
+    bit pattern occurs."""
+    rng = np.random.Generator(np.random.PCG64([seed, pool_tag]))
+    kv = rng.integers(0, 256, size=(spec.n_phys, 2, spec.region_bytes), dtype=np.uint8)
+    sc = (rng.integers(0, 2**32, size=(spec.n_phys, 2, spec.num_blocks), dtype=np.uint32)
+          if spec.has_scales else None)
+    return kv, sc
