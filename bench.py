@@ -1,0 +1,251 @@
+#!/usr/bin/env python3
+"""Benchmark: paged-KV block transfer GB/s (read + write) on one MI355X.
+
+Default workload (qwen32b_push): Qwen3-32B-shaped KV -- 64 layers, K and V,
+8 KV heads, head_dim 128, block 16, bf16 -- one 8192-token prompt (8191 tokens
+move; the consumer recomputes the last one), block tables of contiguous runs
+with geometric length (mean 4) in pools of 4096 blocks.  One step = the
+layerwise push: for each of the 64 layers, a ready event recorded on the
+compute stream and kvx_push_layer(layer, ready) on a side stream.
+
+Prints ONE JSON line on stdout.  Everything else goes to stderr.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "KV block transfer GB/s (read+write) on 1 MI355X + % of HBM peak"
+HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, AMD published peak
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_digest() -> str:
+    h = hashlib.sha256()
+    for f in ("kvx_kernels.hip", "kvx_internal.h"):
+        with open(os.path.join(ROOT, "decode_kv_cache_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def counter_traffic(workload: str):
+    """HBM bytes per launch of the dominant kernel from the committed
+    rocprofv3 --pmc summary, scaled by the copy-kernel calibration factor;
+    None when no summary exists or the kernel source changed since."""
+    path = os.path.join(PROFILES, f"push_kernel_{workload}_pmc.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha256_16") != kernel_source_digest():
+        return None
+    try:
+        return float(kv["calibrated_hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_info():
+    cores = len(os.sched_getaffinity(0))
+    model = platform.processor() or "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return cores, os.cpu_count(), model
+
+
+def cpu_baseline_push(wl, gs, gd, tokens, seconds: float = 12.0):
+    """The oracle (as it stands) on the host: its triple-memcpy push over a
+    sample of the workload's layers (32 layers: more bytes than a host last-
+    level cache holds), repeated for about `seconds`."""
+    import oracle as O
+    from decode_kv_cache_amd import session as S
+    sample_layers = list(range(min(32, wl.src.num_layers)))
+    gsrc = O.Geometry(len(sample_layers), wl.src.num_blocks, wl.src.block_size, wl.src.num_heads,
+                      wl.src.head_dim, wl.src.elem_bytes, wl.src.layout, wl.src.has_scales)
+    gdst = O.Geometry(len(sample_layers), wl.dst.num_blocks, wl.dst.block_size, wl.dst.num_heads,
+                      wl.dst.head_dim, wl.dst.elem_bytes, wl.dst.layout, wl.dst.has_scales)
+    src = O.Pool(gsrc, np.stack([gs.kv[wl.src.phys(l)].cpu().numpy() for l in sample_layers]),
+                 np.stack([S.scale_bits(gs.sc[wl.src.phys(l)]) for l in sample_layers]) if gs.sc is not None else None)
+    dst = O.Pool(gdst, np.stack([gd.kv[wl.dst.phys(l)].cpu().numpy() for l in sample_layers]),
+                 np.stack([S.scale_bits(gd.sc[wl.dst.phys(l)]) for l in sample_layers]) if gd.sc is not None else None)
+    reqs = [O.Request(n, s, d) for n, s, d in zip(tokens, wl.src_tables, wl.dst_tables)]
+    t0 = time.perf_counter()
+    plan = O.make_plan(gsrc, gdst, reqs)
+    plan_s = time.perf_counter() - t0
+    per_pass = len(sample_layers) * sum(plan.bytes_per_layer())
+    passes = 0
+    t0 = time.perf_counter()
+    while True:
+        O.push(src, dst, plan)
+        passes += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    cores, ncpu, model = cpu_info()
+    return {"value": round(per_pass * passes / el / 1e9, 3), "unit": "GB/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"oracle push (numpy triple memcpy, single thread) of {len(sample_layers)} of "
+                      f"{wl.src.num_layers} layers, {passes} passes in {el:.1f} s; host has {cores} usable "
+                      f"cores ({ncpu} total, {model}); oracle plan {plan_s * 1e3:.1f} ms"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="qwen32b_push", choices=["qwen32b_push", "tiny_push"])
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
+              f"(the transfer shards per request/layer/head slice, see the design notes)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from decode_kv_cache_amd import kvx
+    from decode_kv_cache_amd import session as S
+    from decode_kv_cache_amd import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.cuda.get_device_properties(0)
+    log(f"device: {dev.name} {getattr(dev, 'gcnArchName', '')} CUs={dev.multi_processor_count} "
+        f"mem={dev.total_memory / 2**30:.0f} GiB")
+
+    wl = W.WORKLOADS[args.workload]()
+    log(f"workload {wl.name}: pools {wl.src.pool_bytes / 2**30:.1f} + {wl.dst.pool_bytes / 2**30:.1f} GiB")
+    t0 = time.perf_counter()
+    gs = S.device_side(wl.src, wl.seed, 1)
+    gd = S.device_side(wl.dst, wl.seed, 2)
+    torch.cuda.synchronize()
+    log(f"pools filled in {time.perf_counter() - t0:.1f} s")
+
+    tokens = [kvx.kvx_tokens_to_move(p, 0) for p in wl.prompt_lens]
+    side = torch.cuda.Stream()
+    compute = torch.cuda.current_stream()
+    t0 = time.perf_counter()
+    plan = kvx.kvx_plan(gs.pool, gd.pool, tokens, wl.src_tables, wl.dst_tables, stream=side)
+    plan_ms = (time.perf_counter() - t0) * 1e3
+    rd, wr = plan.bytes_per_layer()
+    L = wl.src.num_layers
+    step_bytes = (rd + wr) * L
+    nruns = len(plan.runs())
+    log(f"plan: {nruns} runs, {len(plan.triples())} triples/region, {rd + wr} B per layer, "
+        f"{step_bytes} B per step, host plan {plan_ms:.2f} ms")
+
+    # One ready event per layer, recorded on the compute stream.  The headline
+    # step uses events that have already fired (the layer's compute is done):
+    # kvx_push_layer then enqueues no wait and the side stream holds nothing
+    # but the 64 push kernels, so the per-step span over 64 launches is the
+    # push kernel's average launch duration.
+    ready = [torch.cuda.Event() for _ in range(L)]
+    for e in ready:
+        e.record(compute)
+    torch.cuda.synchronize()
+
+    def step():
+        for l in range(L):
+            kvx.kvx_push_layer(plan, l, ready=ready[l], stream=side)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    wall0 = time.perf_counter()
+    marks[0].record(side)
+    for i in range(args.steps):
+        step()
+        marks[i + 1].record(side)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    per_step = np.array([marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps)])  # ms
+    span_ms = marks[0].elapsed_time(marks[-1])
+    ms_per_step = span_ms / args.steps
+    gbs = step_bytes * args.steps / (span_ms * 1e-3) / 1e9
+    log(f"span {span_ms:.3f} ms for {args.steps} steps ({ms_per_step * 1e3:.1f} us/step, "
+        f"min {per_step.min() * 1e3:.1f}, max {per_step.max() * 1e3:.1f}), wall {wall * 1e3:.1f} ms, "
+        f"{gbs:.1f} GB/s = {100 * gbs / HBM_PEAK_GBS:.1f}% of {HBM_PEAK_GBS:.0f} GB/s")
+
+    # push kernel average launch duration over the timed region (events on
+    # the side stream, which carries only the push kernels)
+    k_avg_us = ms_per_step * 1e3 / L
+    per_launch = rd + wr
+    ach = per_launch / (k_avg_us * 1e-6) / 1e9
+    traffic = counter_traffic(args.workload)
+    roofline = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "kernel": "kvx::copy_kernel<0> (kvx_push_layer)", "avg_launch_us": round(k_avg_us, 3),
+                "algorithmic_bytes_per_launch": per_launch}
+    log(f"push kernel: avg {k_avg_us:.2f} us per launch -> {ach:.1f} GB/s")
+
+    # Secondary: the same step with fresh events (recorded on the compute
+    # stream right before each push, so each push enqueues a cross-stream wait).
+    def fresh_step():
+        for l in range(L):
+            ready[l].record(compute)
+            kvx.kvx_push_layer(plan, l, ready=ready[l], stream=side)
+    fresh_step()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(side)
+    for _ in range(args.steps):
+        fresh_step()
+    b.record(side)
+    torch.cuda.synchronize()
+    fresh_gbs = step_bytes * args.steps / (a.elapsed_time(b) * 1e-3) / 1e9
+    log(f"with fresh per-layer events: {fresh_gbs:.1f} GB/s")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("cpu baseline ...")
+        cpu = cpu_baseline_push(wl, gs, gd, tokens, args.cpu_seconds)
+        log(f"cpu baseline: {cpu['value']} GB/s ({cpu['sample']})")
+
+    out = {
+        "metric": METRIC, "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "u8", "data": "synthetic",
+        "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+        "config": {"workload": wl.name, "layers": L, "kv_heads": wl.src.num_heads, "head_dim": wl.src.head_dim,
+                   "block_size": wl.src.block_size, "payload_dtype": wl.src.dtype, "layout": wl.src.layout,
+                   "prompt_tokens": wl.prompt_lens, "tokens_moved": tokens, "pool_blocks": wl.src.num_blocks,
+                   "merged_runs": nruns, "bytes_per_step": step_bytes,
+                   "step": f"{L} x (ready event on compute stream + kvx_push_layer on side stream)",
+                   "host_plan_ms": round(plan_ms, 3),
+                   "fresh_event_GBs": round(fresh_gbs, 1)},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+    plan.close()
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,418 @@
+// libkvx host side: status strings, pool registry, transfer planning (run
+// merge, per-region triples, device work list) and plan lifetime.
+//
+// Sources: [PUSH] push-based NIXL connector post, [MORI] MoRIIO connector
+// note, [BIDIR] bidirectional KV transfer post (full titles in kvx.h).
+
+#include <hip/hip_runtime_api.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+
+#include "kvx_internal.h"
+
+namespace kvx {
+
+static thread_local std::string t_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  t_err = buf;
+  return code;
+}
+
+int fail_hip(hipError_t e, const char* what) {
+  return fail(KVX_E_HIP, "%s: %s (%d)", what, hipGetErrorString(e), int(e));
+}
+
+int enqueue_waits(kvx_plan_t* p, hipEvent_t ready, hipStream_t s) {
+  if (ready) {
+    // An event whose work has already completed needs no wait: skipping it
+    // saves the queue a barrier packet (several microseconds per layer).
+    hipError_t q = hipEventQuery(ready);
+    if (q == hipErrorNotReady) {
+      hipError_t e = hipStreamWaitEvent(s, ready, 0);
+      if (e != hipSuccess) return fail_hip(e, "hipStreamWaitEvent(ready)");
+    } else if (q != hipSuccess) {
+      return fail_hip(q, "hipEventQuery(ready)");
+    }
+  }
+  if (!p->upload_seen.load(std::memory_order_acquire)) {
+    hipError_t q = hipEventQuery(p->upload_ev);
+    if (q == hipSuccess) {
+      p->upload_seen.store(true, std::memory_order_release);
+    } else if (q == hipErrorNotReady) {
+      hipError_t e = hipStreamWaitEvent(s, p->upload_ev, 0);
+      if (e != hipSuccess) return fail_hip(e, "hipStreamWaitEvent(upload)");
+    } else {
+      return fail_hip(q, "hipEventQuery(upload)");
+    }
+  }
+  return KVX_OK;
+}
+
+int check_launch(const char* what) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail_hip(e, what);
+  return KVX_OK;
+}
+
+static int64_t pad16(int64_t x) { return (x + 15) / 16 * 16; }
+
+}  // namespace kvx
+
+using namespace kvx;
+
+extern "C" {
+
+int32_t kvx_abi_version(void) { return KVX_ABI_VERSION; }
+
+const char* kvx_status_str(int s) {
+  switch (s) {
+    case KVX_OK: return "KVX_OK";
+    case KVX_E_INVAL: return "KVX_E_INVAL";
+    case KVX_E_RANGE: return "KVX_E_RANGE";
+    case KVX_E_DUPDST: return "KVX_E_DUPDST";
+    case KVX_E_MISMATCH: return "KVX_E_MISMATCH";
+    case KVX_E_UNSUPPORTED: return "KVX_E_UNSUPPORTED";
+    case KVX_E_NOMEM: return "KVX_E_NOMEM";
+    case KVX_E_HIP: return "KVX_E_HIP";
+    default: return "KVX_E_UNKNOWN";
+  }
+}
+
+const char* kvx_last_error(void) { return t_err.c_str(); }
+
+// [MORI] §3.1: the consumer takes prompt - computed - 1 tokens and recomputes
+// the final prompt token itself.
+int64_t kvx_tokens_to_move(int64_t prompt_len, int64_t num_computed) {
+  int64_t n = prompt_len - num_computed - 1;
+  return n > 0 ? n : 0;
+}
+
+// [BIDIR] "KV-Recompute-Schwellenwert": pull at or above the threshold.
+int32_t kvx_should_reuse(int64_t reusable_tokens, int64_t threshold) {
+  return reusable_tokens >= threshold ? 1 : 0;
+}
+
+int kvx_pool_create(const kvx_pool_desc* d, kvx_pool** out) {
+  if (!d || !out) return fail(KVX_E_INVAL, "kvx_pool_create: null argument");
+  if (d->num_layers < 1 || d->num_blocks < 1 || d->block_size < 1 || d->num_heads < 1 ||
+      d->head_dim < 1)
+    return fail(KVX_E_INVAL, "kvx_pool_create: counts must be >= 1");
+  if (d->elem_bytes != 1 && d->elem_bytes != 2 && d->elem_bytes != 4)
+    return fail(KVX_E_INVAL, "kvx_pool_create: elem_bytes %d not in {1,2,4}", d->elem_bytes);
+  if (d->layout != KVX_NHD && d->layout != KVX_HND)
+    return fail(KVX_E_INVAL, "kvx_pool_create: unknown layout %d", d->layout);
+  if (!d->k_base || !d->v_base) return fail(KVX_E_INVAL, "kvx_pool_create: null base array");
+  if ((d->k_scale == nullptr) != (d->v_scale == nullptr))
+    return fail(KVX_E_INVAL, "kvx_pool_create: k_scale and v_scale must both be set or both NULL");
+  if ((int64_t(d->head_dim) * d->elem_bytes) % 16)
+    return fail(KVX_E_UNSUPPORTED, "kvx_pool_create: head_dim*elem_bytes=%lld not a multiple of 16",
+                (long long)(int64_t(d->head_dim) * d->elem_bytes));
+  kvx_pool* p = new (std::nothrow) kvx_pool;
+  if (!p) return fail(KVX_E_NOMEM, "kvx_pool_create: out of host memory");
+  Geom& g = p->g;
+  g.L = d->num_layers;
+  g.NB = d->num_blocks;
+  g.BS = d->block_size;
+  g.H = d->num_heads;
+  g.D = d->head_dim;
+  g.E = d->elem_bytes;
+  g.layout = d->layout;
+  g.scales = d->k_scale != nullptr;
+  try {
+    for (int l = 0; l < g.L; ++l) {
+      void* k = d->k_base[l];
+      void* v = d->v_base[l];
+      if (!k || !v) {
+        delete p;
+        return fail(KVX_E_INVAL, "kvx_pool_create: null base for layer %d", l);
+      }
+      if ((uintptr_t(k) | uintptr_t(v)) & 15) {
+        delete p;
+        return fail(KVX_E_UNSUPPORTED, "kvx_pool_create: layer %d base not 16-byte aligned", l);
+      }
+      g.k.push_back(k);
+      g.v.push_back(v);
+      if (g.scales) {
+        float* ks = d->k_scale[l];
+        float* vs = d->v_scale[l];
+        if (!ks || !vs) {
+          delete p;
+          return fail(KVX_E_INVAL, "kvx_pool_create: null scale pointer for layer %d", l);
+        }
+        if ((uintptr_t(ks) | uintptr_t(vs)) & 3) {
+          delete p;
+          return fail(KVX_E_UNSUPPORTED, "kvx_pool_create: layer %d scales not 4-byte aligned", l);
+        }
+        g.ks.push_back(ks);
+        g.vs.push_back(vs);
+      }
+    }
+  } catch (const std::bad_alloc&) {
+    delete p;
+    return fail(KVX_E_NOMEM, "kvx_pool_create: out of host memory");
+  }
+  *out = p;
+  return KVX_OK;
+}
+
+void kvx_pool_destroy(kvx_pool* p) { delete p; }
+
+}  // extern "C"
+
+namespace {
+
+// Append a byte range to the triple list, merging it into the previous triple
+// when both the source and the destination continue without a gap.
+void emit(std::vector<kvx_triple>& t, int64_t so, int64_t dso, int64_t len) {
+  if (!t.empty()) {
+    kvx_triple& b = t.back();
+    if (b.src_off + b.len == so && b.dst_off + b.len == dso) {
+      b.len += len;
+      return;
+    }
+  }
+  t.push_back(kvx_triple{so, dso, len});
+}
+
+// Triples of one (layer, K/V) region, in plan order ([MORI] §6: the
+// (local offset, remote offset, size) list of one batch call, adjacent
+// blocks merged).  NHD: a run's full blocks and its last block's first
+// `tail` token rows are one range.  HND: the full blocks are one range and
+// the partly filled last block adds one range of `tail` rows per head.
+void build_triples(kvx_plan_t* p) {
+  const Geom& g = p->src;
+  const int64_t bb = g.block_bytes(), tb = g.token_bytes(), rb = g.row_bytes();
+  for (const kvx_run& r : p->runs) {
+    const int64_t s0 = int64_t(r.src0) * bb, d0 = int64_t(r.dst0) * bb;
+    if (g.layout == KVX_NHD) {
+      emit(p->triples, s0, d0, int64_t(r.nblk - 1) * bb + int64_t(r.tail) * tb);
+    } else if (r.tail == g.BS) {
+      emit(p->triples, s0, d0, int64_t(r.nblk) * bb);
+    } else {
+      if (r.nblk > 1) emit(p->triples, s0, d0, int64_t(r.nblk - 1) * bb);
+      const int64_t sl = int64_t(r.src0 + r.nblk - 1) * bb, dl = int64_t(r.dst0 + r.nblk - 1) * bb;
+      for (int h = 0; h < g.H; ++h)
+        emit(p->triples, sl + h * g.BS * rb, dl + h * g.BS * rb, int64_t(r.tail) * rb);
+    }
+  }
+}
+
+// Split the triples into workgroup-sized pieces and give each its offset in
+// the staging region (the exclusive prefix of the triple lengths).
+void build_pieces(kvx_plan_t* p) {
+  int64_t stg = 0;
+  for (const kvx_triple& t : p->triples) {
+    for (int64_t o = 0; o < t.len; o += kPieceBytes) {
+      const int64_t len = std::min<int64_t>(kPieceBytes, t.len - o);
+      p->pieces.push_back(Piece{t.src_off + o, t.dst_off + o, stg + o, int32_t(len), 0});
+    }
+    stg += t.len;
+  }
+  p->payload_bytes = stg;
+}
+
+int upload(kvx_plan_t* p, hipStream_t s) {
+  const size_t pb = p->pieces.size() * sizeof(Piece);
+  const size_t bb = p->blocks.size() * sizeof(BlockPair);
+  const size_t total = std::max<size_t>(pb + bb, 256);
+  hipError_t e = hipMalloc(&p->dev_buf, total);
+  if (e != hipSuccess) {
+    p->dev_buf = nullptr;
+    return e == hipErrorOutOfMemory ? fail(KVX_E_NOMEM, "kvx_plan: device descriptors (%zu B)", total)
+                                    : fail_hip(e, "hipMalloc(plan)");
+  }
+  p->d_pieces = static_cast<const Piece*>(p->dev_buf);
+  p->d_blocks = reinterpret_cast<const BlockPair*>(static_cast<char*>(p->dev_buf) + pb);
+  if (pb) {
+    e = hipMemcpyAsync(p->dev_buf, p->pieces.data(), pb, hipMemcpyHostToDevice, s);
+    if (e != hipSuccess) return fail_hip(e, "hipMemcpyAsync(pieces)");
+  }
+  if (bb) {
+    e = hipMemcpyAsync(static_cast<char*>(p->dev_buf) + pb, p->blocks.data(), bb,
+                       hipMemcpyHostToDevice, s);
+    if (e != hipSuccess) return fail_hip(e, "hipMemcpyAsync(blocks)");
+  }
+  e = hipEventCreateWithFlags(&p->upload_ev, hipEventDisableTiming);
+  if (e != hipSuccess) {
+    p->upload_ev = nullptr;
+    return fail_hip(e, "hipEventCreate(upload)");
+  }
+  e = hipEventRecord(p->upload_ev, s);
+  if (e != hipSuccess) return fail_hip(e, "hipEventRecord(upload)");
+  return KVX_OK;
+}
+
+// Free a plan.  Kernels may still be reading its descriptors on any stream,
+// so the device is drained first (no per-launch bookkeeping is kept: a
+// marker per launch would cost every push a queue packet).
+void release(kvx_plan_t* p) {
+  if (!p) return;
+  if (p->dev_buf) (void)hipDeviceSynchronize();
+  if (p->upload_ev) {
+    (void)hipEventSynchronize(p->upload_ev);
+    (void)hipEventDestroy(p->upload_ev);
+  }
+  if (p->dev_buf) (void)hipFree(p->dev_buf);
+  delete p;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kvx_plan(const kvx_pool* src, const kvx_pool* dst, int32_t num_requests,
+             const int64_t* num_tokens, const int64_t* id_offsets, const int32_t* src_ids,
+             const int32_t* dst_ids, uint32_t flags, hipStream_t upload_stream,
+             kvx_plan_t** out) {
+  if (!src || !dst || !out) return fail(KVX_E_INVAL, "kvx_plan: null pool or output");
+  if (src == dst) return fail(KVX_E_INVAL, "kvx_plan: src and dst are the same pool");
+  if (flags & ~KVX_PLAN_HOST_ONLY) return fail(KVX_E_INVAL, "kvx_plan: unknown flags 0x%x", flags);
+  if (num_requests < 0) return fail(KVX_E_INVAL, "kvx_plan: negative request count");
+  if (num_requests > 0 && (!num_tokens || !id_offsets))
+    return fail(KVX_E_INVAL, "kvx_plan: null num_tokens or id_offsets");
+  const Geom& gs = src->g;
+  const Geom& gd = dst->g;
+  if (gs.L != gd.L || gs.BS != gd.BS || gs.D != gd.D || gs.E != gd.E || gs.scales != gd.scales)
+    return fail(KVX_E_MISMATCH,
+                "kvx_plan: pools differ in layers/block_size/head_dim/elem_bytes/scales");
+
+  kvx_plan_t* p = new (std::nothrow) kvx_plan_t;
+  if (!p) return fail(KVX_E_NOMEM, "kvx_plan: out of host memory");
+  try {
+    p->src = gs;
+    p->dst = gd;
+    p->push_ok = gs.H == gd.H && gs.layout == gd.layout;
+    p->host_only = (flags & KVX_PLAN_HOST_ONLY) != 0;
+    const int64_t BS = gs.BS;
+    std::vector<uint8_t> dst_used(size_t(gd.NB), 0);
+    if (num_requests > 0 && id_offsets[0] < 0) {
+      release(p);
+      return fail(KVX_E_INVAL, "kvx_plan: id_offsets[0] < 0");
+    }
+    for (int32_t r = 0; r < num_requests; ++r) {
+      const int64_t n = num_tokens[r];
+      const int64_t lo = id_offsets[r], hi = id_offsets[r + 1];
+      if (n < 0) {
+        release(p);
+        return fail(KVX_E_INVAL, "kvx_plan: request %d: negative token count", r);
+      }
+      if (hi < lo) {
+        release(p);
+        return fail(KVX_E_INVAL, "kvx_plan: id_offsets not monotone at request %d", r);
+      }
+      const int64_t nb = (n + BS - 1) / BS;
+      if (hi - lo < nb) {
+        release(p);
+        return fail(KVX_E_INVAL, "kvx_plan: request %d: %lld block IDs for %lld blocks", r,
+                    (long long)(hi - lo), (long long)nb);
+      }
+      if (nb == 0) continue;
+      if (!src_ids || !dst_ids) {
+        release(p);
+        return fail(KVX_E_INVAL, "kvx_plan: null block ID array");
+      }
+      const int32_t* S = src_ids + lo;
+      const int32_t* Dd = dst_ids + lo;
+      for (int64_t i = 0; i < nb; ++i) {
+        if (S[i] < 0 || S[i] >= gs.NB) {
+          release(p);
+          return fail(KVX_E_RANGE, "kvx_plan: request %d: src block %d outside [0,%d)", r, S[i], gs.NB);
+        }
+        if (Dd[i] < 0 || Dd[i] >= gd.NB) {
+          release(p);
+          return fail(KVX_E_RANGE, "kvx_plan: request %d: dst block %d outside [0,%d)", r, Dd[i], gd.NB);
+        }
+        if (dst_used[size_t(Dd[i])]) {
+          release(p);
+          return fail(KVX_E_DUPDST, "kvx_plan: dst block %d used twice", Dd[i]);
+        }
+        dst_used[size_t(Dd[i])] = 1;
+      }
+      // Merge ([PUSH] "Threading-Modell"; [MORI] §3.1, §6): a new run starts
+      // at the request's first block and wherever either side is not the
+      // previous block + 1.
+      const int32_t tail = int32_t(n - (nb - 1) * BS);
+      int64_t start = 0;
+      for (int64_t i = 1; i <= nb; ++i) {
+        if (i == nb || S[i] != S[i - 1] + 1 || Dd[i] != Dd[i - 1] + 1) {
+          p->runs.push_back(kvx_run{S[start], Dd[start], int32_t(i - start),
+                                    i == nb ? tail : int32_t(BS)});
+          start = i;
+        }
+      }
+    }
+    for (const kvx_run& r : p->runs)
+      for (int32_t k = 0; k < r.nblk; ++k)
+        p->blocks.push_back(BlockPair{r.src0 + k, r.dst0 + k, k == r.nblk - 1 ? r.tail : int32_t(BS), 0});
+    if (p->push_ok) {
+      build_triples(p);
+      build_pieces(p);
+    }
+    p->scale_seg_bytes = gs.scales ? pad16(4 * int64_t(p->blocks.size())) : 0;
+  } catch (const std::bad_alloc&) {
+    release(p);
+    return fail(KVX_E_NOMEM, "kvx_plan: out of host memory");
+  }
+  if (!p->host_only) {
+    int rc = upload(p, upload_stream);
+    if (rc != KVX_OK) {
+      release(p);
+      return rc;
+    }
+  }
+  *out = p;
+  return KVX_OK;
+}
+
+int kvx_plan_runs(const kvx_plan_t* p, kvx_run* out, int64_t cap, int64_t* n) {
+  if (!p || !n) return fail(KVX_E_INVAL, "kvx_plan_runs: null argument");
+  const int64_t cnt = int64_t(p->runs.size());
+  if (out && cap >= cnt) std::copy(p->runs.begin(), p->runs.end(), out);
+  *n = cnt;
+  return KVX_OK;
+}
+
+int kvx_plan_triples(const kvx_plan_t* p, int32_t layer, int32_t kv, kvx_triple* out, int64_t cap,
+                     int64_t* n) {
+  if (!p || !n) return fail(KVX_E_INVAL, "kvx_plan_triples: null argument");
+  if (layer < 0 || layer >= p->src.L || kv < 0 || kv > 1)
+    return fail(KVX_E_RANGE, "kvx_plan_triples: layer %d / kv %d out of range", layer, kv);
+  if (!p->push_ok)
+    return fail(KVX_E_MISMATCH, "kvx_plan_triples: pools differ in head count or layout");
+  const int64_t cnt = int64_t(p->triples.size());
+  if (out && cap >= cnt) std::copy(p->triples.begin(), p->triples.end(), out);
+  *n = cnt;
+  return KVX_OK;
+}
+
+int kvx_plan_bytes(const kvx_plan_t* p, int64_t* rd, int64_t* wr) {
+  if (!p || !rd || !wr) return fail(KVX_E_INVAL, "kvx_plan_bytes: null argument");
+  if (!p->push_ok) return fail(KVX_E_MISMATCH, "kvx_plan_bytes: pools differ in head count or layout");
+  const int64_t sc = p->src.scales ? 4 * int64_t(p->blocks.size()) : 0;
+  *rd = 2 * (p->payload_bytes + sc);
+  *wr = *rd;
+  return KVX_OK;
+}
+
+void kvx_plan_destroy(kvx_plan_t* p) { release(p); }
+
+int kvx_staging_bytes(const kvx_plan_t* p, int32_t l0, int32_t l1, int64_t* bytes) {
+  if (!p || !bytes) return fail(KVX_E_INVAL, "kvx_staging_bytes: null argument");
+  if (l0 < 0 || l1 < l0 || l1 > p->src.L)
+    return fail(KVX_E_RANGE, "kvx_staging_bytes: layers [%d,%d) outside [0,%d]", l0, l1, p->src.L);
+  if (!p->push_ok) return fail(KVX_E_MISMATCH, "kvx_staging_bytes: pools differ in head count or layout");
+  *bytes = int64_t(l1 - l0) * 2 * (p->payload_bytes + p->scale_seg_bytes);
+  return KVX_OK;
+}
+
+}  // extern "C"

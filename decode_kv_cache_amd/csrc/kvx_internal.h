@@ -1,0 +1,95 @@
+// Internal types shared by the libkvx host code (kvx_host.cpp) and the HIP
+// kernels (kvx_kernels.hip).  Not part of the ABI.
+#pragma once
+
+#include <atomic>
+#include <cstdint>
+#include <string>
+#include <vector>
+
+#include "kvx.h"
+
+namespace kvx {
+
+// One workgroup's share of a (layer, K/V) region: a contiguous byte range on
+// the source side, on the destination side and inside the staging region.
+// All offsets are region-relative and identical for every layer and for K
+// and V, so one list serves every launch.  32 bytes: read with one scalar
+// load per workgroup.
+struct Piece {
+  int64_t src_off;
+  int64_t dst_off;
+  int64_t stg_off;
+  int32_t len;  // bytes, multiple of 16, <= kPieceBytes
+  int32_t pad;
+};
+static_assert(sizeof(Piece) == 32, "Piece is 32 bytes");
+
+// One planned block: (source block, destination block, tokens it holds).
+struct BlockPair {
+  int32_t src, dst, nslots, pad;
+};
+static_assert(sizeof(BlockPair) == 16, "BlockPair is 16 bytes");
+
+// Launch shape of the layer copy kernel (compile-time tuning knobs).
+#ifndef KVX_THREADS
+#define KVX_THREADS 256
+#endif
+#ifndef KVX_VEC_PER_THREAD
+#define KVX_VEC_PER_THREAD 4
+#endif
+constexpr int kThreads = KVX_THREADS;            // 4 wave64 per workgroup
+constexpr int kVecPerThread = KVX_VEC_PER_THREAD;  // 16-B vectors each lane keeps in flight
+constexpr int64_t kPieceBytes = int64_t(kThreads) * kVecPerThread * 16;  // 16 KiB
+
+struct Geom {
+  int32_t L = 0, NB = 0, BS = 0, H = 0, D = 0, E = 0, layout = 0;
+  bool scales = false;
+  std::vector<void*> k, v;
+  std::vector<float*> ks, vs;
+
+  int64_t row_bytes() const { return int64_t(D) * E; }
+  int64_t token_bytes() const { return int64_t(H) * row_bytes(); }
+  int64_t block_bytes() const { return int64_t(BS) * token_bytes(); }
+  // byte strides of (block, slot, head) inside a region
+  int64_t slot_stride() const { return layout == KVX_NHD ? token_bytes() : row_bytes(); }
+  int64_t head_stride() const { return layout == KVX_NHD ? row_bytes() : int64_t(BS) * row_bytes(); }
+};
+
+}  // namespace kvx
+
+struct kvx_pool {
+  kvx::Geom g;
+};
+
+struct kvx_plan_s {
+  kvx::Geom src, dst;
+  bool push_ok = false;   // same head count and layout: triples and pieces exist
+  bool host_only = false;
+  std::vector<kvx_run> runs;
+  std::vector<kvx_triple> triples;
+  std::vector<kvx::Piece> pieces;
+  std::vector<kvx::BlockPair> blocks;
+  int64_t payload_bytes = 0;    // per (layer, K/V) region
+  int64_t scale_seg_bytes = 0;  // per region inside staging (16-B padded), 0 without scales
+
+  // device side
+  void* dev_buf = nullptr;
+  const kvx::Piece* d_pieces = nullptr;
+  const kvx::BlockPair* d_blocks = nullptr;
+  hipEvent_t upload_ev = nullptr;
+  std::atomic<bool> upload_seen{false};
+};
+
+namespace kvx {
+
+// Thread-local error message; returns `code`.
+int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail_hip(hipError_t e, const char* what);
+
+// Before a device call: enqueue the wait for `ready` and for the plan upload.
+int enqueue_waits(kvx_plan_t* plan, hipEvent_t ready, hipStream_t stream);
+// After a launch: turn a launch error into KVX_E_HIP.
+int check_launch(const char* what);
+
+}  // namespace kvx

@@ -1,0 +1,362 @@
+// libkvx device side for gfx950 (CDNA4): the layer copy kernel behind
+// kvx_push_layer / kvx_pack / kvx_unpack and the head-slice kernel behind
+// kvx_copy_heads, with their C entry points.
+//
+// The work is pure data movement bound by HBM bandwidth: no arithmetic, no
+// MFMA.  Each workgroup (256 lanes = 4 wave64) owns one 16 KiB piece of one
+// (layer, K/V) region; every lane issues all of its 16-byte loads before its
+// first store so that a workgroup keeps the whole piece in flight.  Piece
+// descriptors are workgroup-uniform and come in through scalar loads.
+//
+// Sources: [PUSH] push-based NIXL connector post, [MORI] MoRIIO connector
+// note, [BIDIR] bidirectional KV transfer post (full titles in kvx.h).
+
+#include <hip/hip_ext.h>
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+
+#include "kvx_internal.h"
+
+namespace kvx {
+
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+
+enum Mode : int { kPush = 0, kPack = 1, kUnpack = 2 };
+
+// Maximum workgroups per launch along x; larger work lists are split.
+constexpr int64_t kMaxGridX = int64_t(1) << 22;
+
+struct CopyArgs {
+  const Piece* pieces;       // already offset by the launch's first piece
+  const BlockPair* blocks;
+  int32_t n_pieces;          // pieces in this launch
+  int32_t n_blocks;          // planned blocks (scale entries)
+  int32_t n_scale_slots;     // scale entries to write (pack: padded to 16 B)
+  int32_t first_scale_wg;    // x index of the first scale workgroup (== n_pieces)
+  const uint8_t* in[2];      // K, V source region (pool or staging)
+  uint8_t* out[2];           // K, V destination region (pool or staging)
+  const uint32_t* in_sc[2];  // scale source (pool scales or staging scale segment)
+  uint32_t* out_sc[2];
+};
+
+#ifndef KVX_NONTEMPORAL
+#define KVX_NONTEMPORAL 1
+#endif
+#ifndef KVX_ANY_ORDER
+#define KVX_ANY_ORDER 0
+#endif
+
+// Streaming accesses: nothing is re-read, so loads and stores carry the
+// nontemporal hint and bypass cache allocation where the hardware allows.
+__device__ __forceinline__ v4u ld_stream(const v4u* p) {
+#if KVX_NONTEMPORAL
+  return __builtin_nontemporal_load(p);
+#else
+  return *p;
+#endif
+}
+__device__ __forceinline__ void st_stream(v4u* p, v4u v) {
+#if KVX_NONTEMPORAL
+  __builtin_nontemporal_store(v, p);
+#else
+  *p = v;
+#endif
+}
+
+// One workgroup copies one piece of the K (blockIdx.y == 0) or V (== 1)
+// region; workgroups past the pieces copy the planned blocks' scales.
+template <int MODE>
+__global__ __launch_bounds__(kThreads) void copy_kernel(CopyArgs a) {
+  const int kv = blockIdx.y;
+  const int x = blockIdx.x;
+  if (x < a.n_pieces) {
+    const Piece pc = a.pieces[x];
+    const int64_t ioff = MODE == kUnpack ? pc.stg_off : pc.src_off;
+    const int64_t ooff = MODE == kPack ? pc.stg_off : pc.dst_off;
+    const v4u* s = reinterpret_cast<const v4u*>(a.in[kv] + ioff);
+    v4u* d = reinterpret_cast<v4u*>(a.out[kv] + ooff);
+    const int nvec = pc.len >> 4;
+    const int t = threadIdx.x;
+    v4u r[kVecPerThread];
+    if (nvec == kVecPerThread * kThreads) {
+#pragma unroll
+      for (int k = 0; k < kVecPerThread; ++k) r[k] = ld_stream(s + t + k * kThreads);
+#pragma unroll
+      for (int k = 0; k < kVecPerThread; ++k) st_stream(d + t + k * kThreads, r[k]);
+    } else {
+      // Short piece: lanes past the end re-read the piece's last vector so
+      // that every load is issued unconditionally and stays in flight; only
+      // the stores are masked.
+#pragma unroll
+      for (int k = 0; k < kVecPerThread; ++k) r[k] = ld_stream(s + min(t + k * kThreads, nvec - 1));
+#pragma unroll
+      for (int k = 0; k < kVecPerThread; ++k)
+        if (t + k * kThreads < nvec) st_stream(d + t + k * kThreads, r[k]);
+    }
+    return;
+  }
+  const int i = (x - a.first_scale_wg) * kThreads + threadIdx.x;
+  if (MODE == kPush) {
+    if (i < a.n_blocks) {
+      const BlockPair b = a.blocks[i];
+      a.out_sc[kv][b.dst] = a.in_sc[kv][b.src];
+    }
+  } else if (MODE == kPack) {
+    if (i < a.n_blocks)
+      a.out_sc[kv][i] = a.in_sc[kv][a.blocks[i].src];
+    else if (i < a.n_scale_slots)
+      a.out_sc[kv][i] = 0u;
+  } else {
+    if (i < a.n_blocks) a.out_sc[kv][a.blocks[i].dst] = a.in_sc[kv][i];
+  }
+}
+
+struct HeadArgs {
+  const BlockPair* blocks;   // already offset by the launch's first block
+  const uint8_t* in[2];
+  uint8_t* out[2];
+  const uint32_t* in_sc[2];  // NULL without scales
+  uint32_t* out_sc[2];
+  int64_t s_blk, s_slot, s_head;  // source byte strides
+  int64_t d_blk, d_slot, d_head;  // destination byte strides
+  int32_t vpr;                    // 16-B vectors per (token, head) row
+  int32_t nh;                     // heads in the slice
+  int32_t dst_head_major;         // 1: enumerate (head, slot, vec) -- HND destination
+};
+
+constexpr int kHeadUnroll = 4;
+
+// One workgroup moves the head slice of one planned block of the K or V
+// region.  Lanes walk the block's rows in destination order so stores are
+// contiguous; each lane keeps kHeadUnroll vectors in flight.
+__global__ __launch_bounds__(kThreads) void heads_kernel(HeadArgs a) {
+  const int kv = blockIdx.y;
+  const BlockPair b = a.blocks[blockIdx.x];
+  const uint8_t* sb = a.in[kv] + int64_t(b.src) * a.s_blk;
+  uint8_t* db = a.out[kv] + int64_t(b.dst) * a.d_blk;
+  const int rows = a.nh * b.nslots;
+  const int total = rows * a.vpr;
+  for (int base = 0; base < total; base += kThreads * kHeadUnroll) {
+    v4u r[kHeadUnroll];
+    int64_t doff[kHeadUnroll];
+#pragma unroll
+    for (int k = 0; k < kHeadUnroll; ++k) {
+      const int i = base + k * kThreads + int(threadIdx.x);
+      if (i < total) {
+        const int v = i % a.vpr;
+        const int row = i / a.vpr;
+        int h, s;
+        if (a.dst_head_major) {
+          h = row / b.nslots;
+          s = row - h * b.nslots;
+        } else {
+          s = row / a.nh;
+          h = row - s * a.nh;
+        }
+        r[k] = ld_stream(reinterpret_cast<const v4u*>(sb + s * a.s_slot + h * a.s_head) + v);
+        doff[k] = s * a.d_slot + h * a.d_head + int64_t(v) * 16;
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < kHeadUnroll; ++k) {
+      const int i = base + k * kThreads + int(threadIdx.x);
+      if (i < total) st_stream(reinterpret_cast<v4u*>(db + doff[k]), r[k]);
+    }
+  }
+  if (a.out_sc[kv] && threadIdx.x == 0) a.out_sc[kv][b.dst] = a.in_sc[kv][b.src];
+}
+
+static int64_t scale_wgs(int64_t slots) { return (slots + kThreads - 1) / kThreads; }
+
+// Enqueue the copy kernel for one layer; `in`/`out` and the scale pointers
+// are already resolved for the mode.  Splits very long work lists.
+template <int MODE>
+static int launch_copy(kvx_plan_t* p, CopyArgs a, int64_t scale_slots, hipStream_t s) {
+  const int64_t np = int64_t(p->pieces.size());
+  const bool scales = a.in_sc[0] != nullptr;
+  const int64_t nsw = scales ? scale_wgs(scale_slots) : 0;
+  a.blocks = p->d_blocks;
+  a.n_blocks = int32_t(p->blocks.size());
+  a.n_scale_slots = int32_t(scale_slots);
+  int64_t first = 0;
+  // Pieces in chunks of kMaxGridX; the scale workgroups ride on the last chunk.
+  do {
+    const int64_t cnt = std::min<int64_t>(np - first, kMaxGridX);
+    const bool last = first + cnt >= np;
+    a.pieces = p->d_pieces + first;
+    a.n_pieces = int32_t(cnt);
+    a.first_scale_wg = int32_t(cnt);
+    const int64_t gx = cnt + (last ? nsw : 0);
+    if (gx > 0) {
+#if KVX_ANY_ORDER
+      hipExtLaunchKernelGGL(copy_kernel<MODE>, dim3(unsigned(gx), 2), dim3(kThreads), 0, s, nullptr, nullptr,
+                            hipExtAnyOrderLaunch, a);
+#else
+      hipLaunchKernelGGL(copy_kernel<MODE>, dim3(unsigned(gx), 2), dim3(kThreads), 0, s, a);
+#endif
+    }
+    first += cnt;
+  } while (first < np);
+  return check_launch("kvx copy kernel launch");
+}
+
+static int check_device_plan(const kvx_plan_t* p, const char* fn) {
+  if (!p) return fail(KVX_E_INVAL, "%s: null plan", fn);
+  if (p->host_only) return fail(KVX_E_INVAL, "%s: plan was built host-only", fn);
+  return KVX_OK;
+}
+
+}  // namespace kvx
+
+using namespace kvx;
+
+extern "C" {
+
+int kvx_push_layer(const kvx_plan_t* cp, int32_t layer, hipEvent_t ready, hipStream_t stream) {
+  int rc = check_device_plan(cp, "kvx_push_layer");
+  if (rc) return rc;
+  kvx_plan_t* p = const_cast<kvx_plan_t*>(cp);
+  if (!p->push_ok) return fail(KVX_E_MISMATCH, "kvx_push_layer: pools differ in head count or layout");
+  if (layer < 0 || layer >= p->src.L)
+    return fail(KVX_E_RANGE, "kvx_push_layer: layer %d outside [0,%d)", layer, p->src.L);
+  rc = enqueue_waits(p, ready, stream);
+  if (rc) return rc;
+  if (p->pieces.empty() && p->blocks.empty()) return KVX_OK;
+  CopyArgs a{};
+  a.in[0] = static_cast<const uint8_t*>(p->src.k[layer]);
+  a.in[1] = static_cast<const uint8_t*>(p->src.v[layer]);
+  a.out[0] = static_cast<uint8_t*>(p->dst.k[layer]);
+  a.out[1] = static_cast<uint8_t*>(p->dst.v[layer]);
+  if (p->src.scales) {
+    a.in_sc[0] = reinterpret_cast<const uint32_t*>(p->src.ks[layer]);
+    a.in_sc[1] = reinterpret_cast<const uint32_t*>(p->src.vs[layer]);
+    a.out_sc[0] = reinterpret_cast<uint32_t*>(p->dst.ks[layer]);
+    a.out_sc[1] = reinterpret_cast<uint32_t*>(p->dst.vs[layer]);
+  }
+  return launch_copy<kPush>(p, a, int64_t(p->blocks.size()), stream);
+}
+
+static int staging_call(const kvx_plan_t* cp, int32_t l0, int32_t l1, const void* staging,
+                        int64_t cap, const char* fn, kvx_plan_t** out) {
+  int rc = check_device_plan(cp, fn);
+  if (rc) return rc;
+  kvx_plan_t* p = const_cast<kvx_plan_t*>(cp);
+  if (!p->push_ok) return fail(KVX_E_MISMATCH, "%s: pools differ in head count or layout", fn);
+  if (l0 < 0 || l1 < l0 || l1 > p->src.L)
+    return fail(KVX_E_RANGE, "%s: layers [%d,%d) outside [0,%d]", fn, l0, l1, p->src.L);
+  const int64_t need = int64_t(l1 - l0) * 2 * (p->payload_bytes + p->scale_seg_bytes);
+  if (need > 0 && !staging) return fail(KVX_E_INVAL, "%s: null staging buffer", fn);
+  if (cap < need) return fail(KVX_E_INVAL, "%s: staging holds %lld bytes, needs %lld", fn,
+                              (long long)cap, (long long)need);
+  if (uintptr_t(staging) & 15) return fail(KVX_E_UNSUPPORTED, "%s: staging not 16-byte aligned", fn);
+  *out = p;
+  return KVX_OK;
+}
+
+int kvx_pack(const kvx_plan_t* cp, int32_t l0, int32_t l1, void* staging, int64_t cap,
+             hipStream_t stream) {
+  kvx_plan_t* p = nullptr;
+  int rc = staging_call(cp, l0, l1, staging, cap, "kvx_pack", &p);
+  if (rc) return rc;
+  rc = enqueue_waits(p, nullptr, stream);
+  if (rc) return rc;
+  const int64_t region = p->payload_bytes + p->scale_seg_bytes;
+  if (region == 0) return KVX_OK;
+  uint8_t* stg = static_cast<uint8_t*>(staging);
+  for (int32_t l = l0; l < l1; ++l) {
+    CopyArgs a{};
+    a.in[0] = static_cast<const uint8_t*>(p->src.k[l]);
+    a.in[1] = static_cast<const uint8_t*>(p->src.v[l]);
+    for (int kv = 0; kv < 2; ++kv) {
+      uint8_t* reg = stg + (int64_t(l - l0) * 2 + kv) * region;
+      a.out[kv] = reg;
+      if (p->src.scales) a.out_sc[kv] = reinterpret_cast<uint32_t*>(reg + p->payload_bytes);
+    }
+    if (p->src.scales) {
+      a.in_sc[0] = reinterpret_cast<const uint32_t*>(p->src.ks[l]);
+      a.in_sc[1] = reinterpret_cast<const uint32_t*>(p->src.vs[l]);
+    }
+    rc = launch_copy<kPack>(p, a, p->scale_seg_bytes / 4, stream);
+    if (rc) return rc;
+  }
+  return KVX_OK;
+}
+
+int kvx_unpack(const kvx_plan_t* cp, int32_t l0, int32_t l1, const void* staging, int64_t cap,
+               hipStream_t stream) {
+  kvx_plan_t* p = nullptr;
+  int rc = staging_call(cp, l0, l1, staging, cap, "kvx_unpack", &p);
+  if (rc) return rc;
+  rc = enqueue_waits(p, nullptr, stream);
+  if (rc) return rc;
+  const int64_t region = p->payload_bytes + p->scale_seg_bytes;
+  if (region == 0) return KVX_OK;
+  const uint8_t* stg = static_cast<const uint8_t*>(staging);
+  for (int32_t l = l0; l < l1; ++l) {
+    CopyArgs a{};
+    a.out[0] = static_cast<uint8_t*>(p->dst.k[l]);
+    a.out[1] = static_cast<uint8_t*>(p->dst.v[l]);
+    for (int kv = 0; kv < 2; ++kv) {
+      const uint8_t* reg = stg + (int64_t(l - l0) * 2 + kv) * region;
+      a.in[kv] = reg;
+      if (p->dst.scales) a.in_sc[kv] = reinterpret_cast<const uint32_t*>(reg + p->payload_bytes);
+    }
+    if (p->dst.scales) {
+      a.out_sc[0] = reinterpret_cast<uint32_t*>(p->dst.ks[l]);
+      a.out_sc[1] = reinterpret_cast<uint32_t*>(p->dst.vs[l]);
+    }
+    rc = launch_copy<kUnpack>(p, a, int64_t(p->blocks.size()), stream);
+    if (rc) return rc;
+  }
+  return KVX_OK;
+}
+
+int kvx_copy_heads(const kvx_plan_t* cp, int32_t layer, int32_t src_head0, int32_t dst_head0,
+                   int32_t num_heads, hipEvent_t ready, hipStream_t stream) {
+  int rc = check_device_plan(cp, "kvx_copy_heads");
+  if (rc) return rc;
+  kvx_plan_t* p = const_cast<kvx_plan_t*>(cp);
+  if (src_head0 < 0 || dst_head0 < 0 || num_heads < 0)
+    return fail(KVX_E_INVAL, "kvx_copy_heads: negative head index or count");
+  if (layer < 0 || layer >= p->src.L)
+    return fail(KVX_E_RANGE, "kvx_copy_heads: layer %d outside [0,%d)", layer, p->src.L);
+  if (int64_t(src_head0) + num_heads > p->src.H || int64_t(dst_head0) + num_heads > p->dst.H)
+    return fail(KVX_E_RANGE, "kvx_copy_heads: head slice [%d,+%d) -> [%d,+%d) outside %d / %d heads",
+                src_head0, num_heads, dst_head0, num_heads, p->src.H, p->dst.H);
+  rc = enqueue_waits(p, ready, stream);
+  if (rc) return rc;
+  if (p->blocks.empty()) return KVX_OK;
+  if (num_heads == 0) return KVX_OK;
+  const Geom& gs = p->src;
+  const Geom& gd = p->dst;
+  HeadArgs a{};
+  a.in[0] = static_cast<const uint8_t*>(gs.k[layer]) + int64_t(src_head0) * gs.head_stride();
+  a.in[1] = static_cast<const uint8_t*>(gs.v[layer]) + int64_t(src_head0) * gs.head_stride();
+  a.out[0] = static_cast<uint8_t*>(gd.k[layer]) + int64_t(dst_head0) * gd.head_stride();
+  a.out[1] = static_cast<uint8_t*>(gd.v[layer]) + int64_t(dst_head0) * gd.head_stride();
+  if (gs.scales) {
+    a.in_sc[0] = reinterpret_cast<const uint32_t*>(gs.ks[layer]);
+    a.in_sc[1] = reinterpret_cast<const uint32_t*>(gs.vs[layer]);
+    a.out_sc[0] = reinterpret_cast<uint32_t*>(gd.ks[layer]);
+    a.out_sc[1] = reinterpret_cast<uint32_t*>(gd.vs[layer]);
+  }
+  a.s_blk = gs.block_bytes();
+  a.s_slot = gs.slot_stride();
+  a.s_head = gs.head_stride();
+  a.d_blk = gd.block_bytes();
+  a.d_slot = gd.slot_stride();
+  a.d_head = gd.head_stride();
+  a.vpr = int32_t(gs.row_bytes() / 16);
+  a.nh = num_heads;
+  a.dst_head_major = gd.layout == KVX_HND;
+  const int64_t nb = int64_t(p->blocks.size());
+  for (int64_t first = 0; first < nb; first += kMaxGridX) {
+    const int64_t cnt = std::min<int64_t>(nb - first, kMaxGridX);
+    a.blocks = p->d_blocks + first;
+    hipLaunchKernelGGL(heads_kernel, dim3(unsigned(cnt), 2), dim3(kThreads), 0, stream, a);
+  }
+  return check_launch("kvx heads kernel launch");
+}
+
+}  // extern "C"

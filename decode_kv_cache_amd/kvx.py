@@ -1,0 +1,271 @@
+"""Thin ctypes binding of libkvx (C ABI: include/kvx.h).
+
+Argument marshalling only: every step of the transfer runs in libkvx's HIP
+kernels; torch supplies device memory (``data_ptr()``), streams
+(``cuda_stream``) and events (``cuda_event``).  The Python names are the C
+names.  A failing call raises :class:`KvxError` with the C status and
+``kvx_last_error()``.  If ``libkvx.so`` has not been built the first call
+raises; nothing falls back to another implementation.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from typing import Optional, Sequence
+
+import numpy as np
+import torch  # imported before libkvx so that both share torch's HIP runtime
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkvx.so")
+
+KVX_OK, KVX_E_INVAL, KVX_E_RANGE, KVX_E_DUPDST, KVX_E_MISMATCH, KVX_E_UNSUPPORTED, KVX_E_NOMEM, KVX_E_HIP = range(8)
+KVX_NHD, KVX_HND = 0, 1
+KVX_PLAN_HOST_ONLY = 1
+LAYOUTS = {"NHD": KVX_NHD, "HND": KVX_HND}
+
+
+class kvx_pool_desc(C.Structure):
+    _fields_ = [("num_layers", C.c_int32), ("num_blocks", C.c_int32), ("block_size", C.c_int32),
+                ("num_heads", C.c_int32), ("head_dim", C.c_int32), ("elem_bytes", C.c_int32),
+                ("layout", C.c_int32), ("k_base", C.POINTER(C.c_void_p)), ("v_base", C.POINTER(C.c_void_p)),
+                ("k_scale", C.POINTER(C.c_void_p)), ("v_scale", C.POINTER(C.c_void_p))]
+
+
+class kvx_run(C.Structure):
+    _fields_ = [("src0", C.c_int32), ("dst0", C.c_int32), ("nblk", C.c_int32), ("tail", C.c_int32)]
+
+
+class kvx_triple(C.Structure):
+    _fields_ = [("src_off", C.c_int64), ("dst_off", C.c_int64), ("len", C.c_int64)]
+
+
+_P = C.c_void_p
+_I32, _I64, _U32 = C.c_int32, C.c_int64, C.c_uint32
+_SIGS = {
+    "kvx_abi_version": (_I32, []),
+    "kvx_status_str": (C.c_char_p, [C.c_int]),
+    "kvx_last_error": (C.c_char_p, []),
+    "kvx_tokens_to_move": (_I64, [_I64, _I64]),
+    "kvx_should_reuse": (_I32, [_I64, _I64]),
+    "kvx_pool_create": (C.c_int, [C.POINTER(kvx_pool_desc), C.POINTER(_P)]),
+    "kvx_pool_destroy": (None, [_P]),
+    "kvx_plan": (C.c_int, [_P, _P, _I32, _P, _P, _P, _P, _U32, _P, C.POINTER(_P)]),
+    "kvx_plan_runs": (C.c_int, [_P, _P, _I64, C.POINTER(_I64)]),
+    "kvx_plan_triples": (C.c_int, [_P, _I32, _I32, _P, _I64, C.POINTER(_I64)]),
+    "kvx_plan_bytes": (C.c_int, [_P, C.POINTER(_I64), C.POINTER(_I64)]),
+    "kvx_plan_destroy": (None, [_P]),
+    "kvx_push_layer": (C.c_int, [_P, _I32, _P, _P]),
+    "kvx_staging_bytes": (C.c_int, [_P, _I32, _I32, C.POINTER(_I64)]),
+    "kvx_pack": (C.c_int, [_P, _I32, _I32, _P, _I64, _P]),
+    "kvx_unpack": (C.c_int, [_P, _I32, _I32, _P, _I64, _P]),
+    "kvx_copy_heads": (C.c_int, [_P, _I32, _I32, _I32, _I32, _P, _P]),
+}
+EXPORTED = tuple(_SIGS)
+
+_lib = None
+
+
+def lib() -> C.CDLL:
+    """Load libkvx.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m decode_kv_cache_amd.build`")
+        h = C.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            f = getattr(h, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = h
+    return _lib
+
+
+class KvxError(RuntimeError):
+    def __init__(self, fn: str, code: int):
+        L = lib()
+        self.code = code
+        self.status = L.kvx_status_str(code).decode()
+        self.detail = L.kvx_last_error().decode()
+        super().__init__(f"{fn}: {self.status}: {self.detail}")
+
+
+def _check(fn: str, rc: int) -> None:
+    if rc != KVX_OK:
+        raise KvxError(fn, rc)
+
+
+def _stream(s) -> Optional[int]:
+    if s is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(s, int):
+        return s
+    return s.cuda_stream
+
+
+def _event(e) -> Optional[int]:
+    if e is None:
+        return None
+    if isinstance(e, int):
+        return e or None
+    return e.cuda_event or None
+
+
+def kvx_abi_version() -> int:
+    return lib().kvx_abi_version()
+
+
+def kvx_tokens_to_move(prompt_len: int, num_computed: int = 0) -> int:
+    return lib().kvx_tokens_to_move(prompt_len, num_computed)
+
+
+def kvx_should_reuse(reusable_tokens: int, threshold: int) -> bool:
+    return bool(lib().kvx_should_reuse(reusable_tokens, threshold))
+
+
+class Pool:
+    """Owns a kvx_pool handle.  ``k_bases``/``v_bases``: one device address per
+    logical layer (may repeat); ``k_scales``/``v_scales``: fp32[num_blocks]
+    addresses per layer or None.  ``keep`` holds tensors alive with the pool."""
+
+    def __init__(self, *, num_blocks, block_size, num_heads, head_dim, elem_bytes, layout,
+                 k_bases: Sequence[int], v_bases: Sequence[int], k_scales=None, v_scales=None, keep=()):
+        L = len(k_bases)
+        arr = C.c_void_p * L
+        self._kb, self._vb = arr(*k_bases), arr(*v_bases)
+        self._ks = arr(*k_scales) if k_scales is not None else None
+        self._vs = arr(*v_scales) if v_scales is not None else None
+        d = kvx_pool_desc(L, num_blocks, block_size, num_heads, head_dim, elem_bytes,
+                          LAYOUTS.get(layout, layout), self._kb, self._vb,
+                          self._ks if self._ks is not None else None,
+                          self._vs if self._vs is not None else None)
+        h = C.c_void_p()
+        _check("kvx_pool_create", lib().kvx_pool_create(C.byref(d), C.byref(h)))
+        self.handle = h
+        self.num_layers, self.num_blocks, self.block_size = L, num_blocks, block_size
+        self.num_heads, self.head_dim, self.elem_bytes = num_heads, head_dim, elem_bytes
+        self.layout = layout
+        self.keep = keep
+
+    def close(self):
+        if getattr(self, "handle", None):
+            lib().kvx_pool_destroy(self.handle)
+            self.handle = None
+
+    __del__ = close
+
+
+def kvx_pool_create(*, kv, scales=None, num_layers: int, num_blocks: int, block_size: int,
+                    num_heads: int, head_dim: int, elem_bytes: int, layout="NHD", phys=None) -> Pool:
+    """Register a pool stored as one tensor ``kv`` of shape [P, 2, region]
+    (P physical layer slabs, K then V) with optional fp32 ``scales`` of shape
+    [P, 2, num_blocks].  Logical layer l uses slab ``phys(l)`` (default l)."""
+    phys = phys or (lambda l: l)
+    kb = [kv[phys(l), 0].data_ptr() for l in range(num_layers)]
+    vb = [kv[phys(l), 1].data_ptr() for l in range(num_layers)]
+    ks = vs = None
+    if scales is not None:
+        ks = [scales[phys(l), 0].data_ptr() for l in range(num_layers)]
+        vs = [scales[phys(l), 1].data_ptr() for l in range(num_layers)]
+    return Pool(num_blocks=num_blocks, block_size=block_size, num_heads=num_heads, head_dim=head_dim,
+                elem_bytes=elem_bytes, layout=layout, k_bases=kb, v_bases=vb, k_scales=ks, v_scales=vs,
+                keep=(kv, scales))
+
+
+class Plan:
+    """Owns a kvx_plan_t handle (destroyed on close / garbage collection)."""
+
+    def __init__(self, handle, src: Pool, dst: Pool):
+        self.handle, self.src, self.dst = handle, src, dst
+
+    def runs(self) -> np.ndarray:
+        n = C.c_int64()
+        _check("kvx_plan_runs", lib().kvx_plan_runs(self.handle, None, 0, C.byref(n)))
+        out = (kvx_run * max(n.value, 1))()
+        _check("kvx_plan_runs", lib().kvx_plan_runs(self.handle, out, n.value, C.byref(n)))
+        return np.frombuffer(out, np.int32, count=4 * n.value).reshape(-1, 4).copy()
+
+    def triples(self, layer: int = 0, kv: int = 0) -> np.ndarray:
+        n = C.c_int64()
+        _check("kvx_plan_triples", lib().kvx_plan_triples(self.handle, layer, kv, None, 0, C.byref(n)))
+        out = (kvx_triple * max(n.value, 1))()
+        _check("kvx_plan_triples", lib().kvx_plan_triples(self.handle, layer, kv, out, n.value, C.byref(n)))
+        return np.frombuffer(out, np.int64, count=3 * n.value).reshape(-1, 3).copy()
+
+    def bytes_per_layer(self):
+        r, w = C.c_int64(), C.c_int64()
+        _check("kvx_plan_bytes", lib().kvx_plan_bytes(self.handle, C.byref(r), C.byref(w)))
+        return r.value, w.value
+
+    def close(self):
+        if getattr(self, "handle", None):
+            lib().kvx_plan_destroy(self.handle)
+            self.handle = None
+
+    __del__ = close
+
+
+def kvx_plan(src: Pool, dst: Pool, num_tokens: Sequence[int], src_tables: Sequence[Sequence[int]],
+             dst_tables: Sequence[Sequence[int]], *, host_only: bool = False, stream=None) -> Plan:
+    """Build a plan.  ``num_tokens[r]`` tokens of request r move; its block
+    lists are ``src_tables[r]`` / ``dst_tables[r]``.  The C ABI takes one
+    offset array for both lists, so each request's two lists are passed cut to
+    the shorter length (entries past the blocks in use are ignored anyway)."""
+    R = len(num_tokens)
+    if len(src_tables) != R or len(dst_tables) != R:
+        raise ValueError("one src and one dst block list per request")
+    nt = np.ascontiguousarray(num_tokens, dtype=np.int64)
+    lens = [min(len(a), len(b)) for a, b in zip(src_tables, dst_tables)]
+    off = np.zeros(R + 1, np.int64)
+    off[1:] = np.cumsum(lens)
+    sid = np.ascontiguousarray(np.concatenate([np.asarray(t[:n], np.int32) for t, n in zip(src_tables, lens)])
+                               if R else np.zeros(0, np.int32), np.int32)
+    did = np.ascontiguousarray(np.concatenate([np.asarray(t[:n], np.int32) for t, n in zip(dst_tables, lens)])
+                               if R else np.zeros(0, np.int32), np.int32)
+    h = C.c_void_p()
+    us = None if host_only else _stream(stream)
+    rc = lib().kvx_plan(src.handle, dst.handle, R, nt.ctypes.data, off.ctypes.data,
+                        sid.ctypes.data if sid.size else None, did.ctypes.data if did.size else None,
+                        KVX_PLAN_HOST_ONLY if host_only else 0, us, C.byref(h))
+    _check("kvx_plan", rc)
+    return Plan(h, src, dst)
+
+
+def kvx_plan_raw(src: Pool, dst: Pool, num_requests: int, num_tokens, id_offsets, src_ids, dst_ids,
+                 flags: int = KVX_PLAN_HOST_ONLY, stream=None):
+    """Direct call with raw arrays (numpy) for error-path tests; returns
+    (status, Plan or None)."""
+    h = C.c_void_p()
+
+    def ptr(a):
+        return None if a is None else np.ascontiguousarray(a).ctypes.data
+    keep = [np.ascontiguousarray(a) if a is not None else None for a in (num_tokens, id_offsets, src_ids, dst_ids)]
+    rc = lib().kvx_plan(src.handle if src else None, dst.handle if dst else None, num_requests,
+                        *(ptr(a) for a in keep), flags, stream, C.byref(h))
+    return rc, (Plan(h, src, dst) if rc == KVX_OK else None)
+
+
+def kvx_push_layer(plan: Plan, layer: int, ready=None, stream=None) -> None:
+    _check("kvx_push_layer", lib().kvx_push_layer(plan.handle, layer, _event(ready), _stream(stream)))
+
+
+def kvx_staging_bytes(plan: Plan, l0: int, l1: int) -> int:
+    b = C.c_int64()
+    _check("kvx_staging_bytes", lib().kvx_staging_bytes(plan.handle, l0, l1, C.byref(b)))
+    return b.value
+
+
+def kvx_pack(plan: Plan, l0: int, l1: int, staging: torch.Tensor, stream=None) -> None:
+    cap = staging.numel() * staging.element_size()
+    _check("kvx_pack", lib().kvx_pack(plan.handle, l0, l1, staging.data_ptr(), cap, _stream(stream)))
+
+
+def kvx_unpack(plan: Plan, l0: int, l1: int, staging: torch.Tensor, stream=None) -> None:
+    cap = staging.numel() * staging.element_size()
+    _check("kvx_unpack", lib().kvx_unpack(plan.handle, l0, l1, staging.data_ptr(), cap, _stream(stream)))
+
+
+def kvx_copy_heads(plan: Plan, layer: int, src_head0: int, dst_head0: int, num_heads: int,
+                   ready=None, stream=None) -> None:
+    _check("kvx_copy_heads", lib().kvx_copy_heads(plan.handle, layer, src_head0, dst_head0, num_heads,
+                                                  _event(ready), _stream(stream)))

@@ -1,0 +1,247 @@
+/*
+ * libkvx -- paged-KV block transfer between a producer (prefill) pool and a
+ * consumer (decode) pool on one MI355X (gfx950).
+ *
+ * Sources this ABI follows (cited by page title and section):
+ *   [PUSH]  "Push-based KV transfer for vLLM prefill/decode disaggregation
+ *           with NIXL" (AWS blog, German translation,
+ *           www.spke.com/de/ai/article/3844)
+ *   [MORI]  "vLLM MoRIIO KV Connector (single-node PD disaggregation)"
+ *           (donggyun112.github.io knowledge-base note)
+ *   [BIDIR] "Bidirectional KV-cache transfer for multi-turn workloads"
+ *           (AWS blog, German translation, www.spke.com/de/ai/article/3845)
+ *
+ * Conventions shared by every call:
+ *   - Return value: KVX_OK (0) or one of the KVX_E_* codes.  No call throws,
+ *     aborts or prints.  kvx_last_error() holds a thread-local message for the
+ *     last failing call on this thread.  Output parameters are written only
+ *     when the call returns KVX_OK.
+ *   - Ownership: the caller owns all pool memory, staging buffers, streams and
+ *     events and must keep pool memory alive until enqueued work completes.
+ *     The library owns the opaque kvx_pool / kvx_plan_t handles and each
+ *     plan's device descriptor buffer.  Plans are immutable once built and
+ *     may be used concurrently on several streams as long as the destination
+ *     bytes of concurrent calls do not overlap.
+ *   - Device calls are asynchronous: they enqueue on the given stream and
+ *     return.  `ready` (may be NULL) is waited for with hipStreamWaitEvent
+ *     before the kernel runs.  Memory must be device memory of the current
+ *     device.
+ *   - Bytes are copied, never interpreted: bf16, fp8 or any other element type
+ *     of 1, 2 or 4 bytes moves bit-exactly.
+ */
+#ifndef KVX_H
+#define KVX_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KVX_ABI_VERSION 1
+
+/* Status codes. */
+enum {
+  KVX_OK = 0,
+  KVX_E_INVAL = 1,       /* null pointer, negative count, short block list, bad flags */
+  KVX_E_RANGE = 2,       /* block ID outside the pool, layer or head range out of bounds */
+  KVX_E_DUPDST = 3,      /* a destination block is used twice within one plan */
+  KVX_E_MISMATCH = 4,    /* the two pools' geometries are incompatible for the call */
+  KVX_E_UNSUPPORTED = 5, /* alignment: base not 16-B aligned, row bytes not a multiple of 16 */
+  KVX_E_NOMEM = 6,       /* host or device allocation failed */
+  KVX_E_HIP = 7          /* a HIP runtime or launch error; see kvx_last_error() */
+};
+
+/* Block layouts inside one (layer, K or V) region.  Each side maps block
+ * positions onto its own physical layout ([PUSH] "Implementierungsdetails",
+ * step 3). */
+enum {
+  KVX_NHD = 0, /* [block][slot][head][dim] */
+  KVX_HND = 1  /* [block][head][slot][dim] */
+};
+
+/* kvx_plan flags. */
+#define KVX_PLAN_HOST_ONLY 1u /* build the host tables only; no device upload,
+                                 device calls on the plan return KVX_E_INVAL */
+
+/*
+ * Pool descriptor: the paged KV cache of one side, as exchanged at the first
+ * handshake (KV base address, block size, per-layer strides: [MORI] §3) and
+ * registered per layer ([MORI] §6, register_kv_caches).  Layer l's K and V
+ * regions each hold num_blocks blocks of block_size slots of num_heads rows
+ * of head_dim elements, in `layout`.  A block ID addresses the same block in
+ * every layer and in both K and V.
+ *   k_base, v_base: host arrays of num_layers device pointers, 16-B aligned.
+ *     Entries may repeat (several logical layers aliasing one slab).
+ *   k_scale, v_scale: both NULL (no scales) or host arrays of num_layers
+ *     device pointers to fp32[num_blocks], one scale per (layer, K/V, block),
+ *     4-B aligned.  A scale travels with its block, unchanged.
+ * Requirements: all counts >= 1; elem_bytes in {1, 2, 4}; head_dim *
+ * elem_bytes a multiple of 16 (KVX_E_UNSUPPORTED otherwise).
+ * The library copies the descriptor; the arrays may be freed after the call.
+ */
+typedef struct kvx_pool_desc {
+  int32_t num_layers, num_blocks, block_size, num_heads, head_dim;
+  int32_t elem_bytes;
+  int32_t layout;
+  void* const* k_base;
+  void* const* v_base;
+  float* const* k_scale;
+  float* const* v_scale;
+} kvx_pool_desc;
+
+typedef struct kvx_pool kvx_pool;
+typedef struct kvx_plan_s kvx_plan_t;
+
+/* One merged run: blocks src0..src0+nblk-1 -> dst0..dst0+nblk-1, the last
+ * block holding `tail` tokens (block_size unless it ends its request). */
+typedef struct kvx_run {
+  int32_t src0, dst0, nblk, tail;
+} kvx_run;
+
+/* One contiguous copy inside a (layer, K/V) region: byte offsets relative to
+ * the region's base pointer on each side. */
+typedef struct kvx_triple {
+  int64_t src_off, dst_off, len;
+} kvx_triple;
+
+/* ABI version (KVX_ABI_VERSION of the built library). */
+int32_t kvx_abi_version(void);
+
+/* Static name of a status code; never NULL. */
+const char* kvx_status_str(int status);
+
+/* Thread-local detail of the last failing call on this thread ("" if none). */
+const char* kvx_last_error(void);
+
+/* Tokens a consumer takes from the producer: prompt_len - num_computed - 1,
+ * clamped at 0.  The consumer always recomputes the final prompt token
+ * ([MORI] §3.1, READ mode scheduler).  Callers pass the result to kvx_plan;
+ * D->P reuse passes the reusable prefix itself (no -1). */
+int64_t kvx_tokens_to_move(int64_t prompt_len, int64_t num_computed);
+
+/* 1 if a reusable prefix of `reusable_tokens` should be pulled rather than
+ * recomputed, i.e. reusable_tokens >= threshold; else 0.  The pages' default
+ * threshold is 64 tokens ([BIDIR] "KV-Recompute-Schwellenwert"). */
+int32_t kvx_should_reuse(int64_t reusable_tokens, int64_t threshold);
+
+/* Register one side's KV cache.  Host-only: no device call is made.
+ * Errors: INVAL (null/invalid field), UNSUPPORTED (alignment), NOMEM. */
+int kvx_pool_create(const kvx_pool_desc* desc, kvx_pool** out);
+
+/* Free a pool handle (never the pool memory).  NULL is a no-op.  Plans built
+ * from the pool stay valid: they hold their own copy of the descriptors. */
+void kvx_pool_destroy(kvx_pool* pool);
+
+/*
+ * Build a transfer plan from `src` to `dst` for `num_requests` requests.
+ *   num_tokens[r]: tokens request r moves (>= 0); the caller applies the
+ *     final-token rule (kvx_tokens_to_move) for P->D.
+ *   id_offsets[r], id_offsets[r+1]: CSR bounds of request r's block list in
+ *     both src_ids and dst_ids (non-decreasing, id_offsets[0] >= 0).  Only
+ *     the first ceil(num_tokens[r] / block_size) entries are used; later
+ *     entries are ignored and not validated.
+ *   src_ids / dst_ids: block IDs of the producer / consumer pool.
+ * The block pairs of each request are merged, in list order, into maximal
+ * runs consecutive on both sides; runs never cross requests.  This is the
+ * merge of contiguous blocks into larger transfer regions done by the push
+ * connector's background thread ([PUSH] "Threading-Modell") and by the
+ * per-layer offset computation ([MORI] §3.1, §6).  When both pools have the
+ * same head count and layout the plan also holds the per-region triple list
+ * and the device work list for kvx_push_layer / kvx_pack / kvx_unpack;
+ * otherwise only kvx_copy_heads may use it.
+ * Pools must agree on num_layers, block_size, head_dim, elem_bytes and
+ * scale presence (KVX_E_MISMATCH otherwise); src == dst is KVX_E_INVAL.
+ * Unless KVX_PLAN_HOST_ONLY is set the device work list is uploaded on
+ * `upload_stream` (NULL = the null stream); later device calls on any stream
+ * are ordered after the upload.
+ * Errors: INVAL, RANGE (ID outside its pool), DUPDST (a dst ID used twice),
+ * MISMATCH, NOMEM, HIP.
+ */
+int kvx_plan(const kvx_pool* src, const kvx_pool* dst, int32_t num_requests,
+             const int64_t* num_tokens, const int64_t* id_offsets,
+             const int32_t* src_ids, const int32_t* dst_ids, uint32_t flags,
+             hipStream_t upload_stream, kvx_plan_t** out);
+
+/* Copy the run table into out[0..cap); *n receives the run count.  With
+ * out == NULL or cap < count only *n is written (and KVX_OK returned). */
+int kvx_plan_runs(const kvx_plan_t* plan, kvx_run* out, int64_t cap, int64_t* n);
+
+/* The (src_off, dst_off, len) list of one (layer, kv) region (kv: 0 = K,
+ * 1 = V): maximal contiguous byte ranges in plan order, the list handed to one
+ * batch transfer per layer ([MORI] §6).  Offsets are relative to that layer's
+ * K or V base on each side; with uniform layers the list is the same for
+ * every layer and for K and V.  NHD gives one triple per run; HND gives the
+ * run's full blocks plus one range per head of a partly filled last block.
+ * Same cap/n protocol as kvx_plan_runs.  Errors: RANGE, MISMATCH (no
+ * triples: different head count or layout). */
+int kvx_plan_triples(const kvx_plan_t* plan, int32_t layer, int32_t kv,
+                     kvx_triple* out, int64_t cap, int64_t* n);
+
+/* Bytes one layer's push reads and writes (K and V payload plus scales). */
+int kvx_plan_bytes(const kvx_plan_t* plan, int64_t* read_bytes, int64_t* write_bytes);
+
+/* Free a plan.  Device calls already enqueued with it may still be running
+ * on any stream, so this first waits until the device is idle
+ * (hipDeviceSynchronize).  NULL is a no-op. */
+void kvx_plan_destroy(kvx_plan_t* plan);
+
+/*
+ * Layerwise push: copy layer `layer`'s K and V bytes of every planned token
+ * (and the scales of every planned block) from the src pool into the dst
+ * pool, after `ready` fires, on `stream`.  This is the per-layer write that
+ * starts once that layer's compute is done and overlaps the next layer's
+ * compute ([MORI] §3.2, save_kv_layer and the event sync before the write;
+ * [PUSH] "Implementierungsdetails" step 3).  Slots past a request's last
+ * token keep their old bytes, so the consumer never receives the final
+ * prompt token ([MORI] §3.1).
+ * Errors: INVAL (host-only plan, null plan), RANGE (layer), MISMATCH (pools
+ * differ in head count or layout), HIP.
+ */
+int kvx_push_layer(const kvx_plan_t* plan, int32_t layer, hipEvent_t ready, hipStream_t stream);
+
+/* Staging bytes for layers [l0, l1): (l1 - l0) * 2 * (payload + scale
+ * segment), where payload = sum of the region's triple lengths and the scale
+ * segment is 4 bytes per planned block rounded up to 16 (0 without scales).
+ * Errors: RANGE (0 <= l0 <= l1 <= num_layers violated), MISMATCH. */
+int kvx_staging_bytes(const kvx_plan_t* plan, int32_t l0, int32_t l1, int64_t* bytes);
+
+/*
+ * Gather layers [l0, l1) of the planned bytes from the src pool into a
+ * contiguous staging buffer (what a NIC would read), laid out for each layer
+ * in order, K then V: the region's triples' source bytes in plan order, then
+ * (with scales) the planned blocks' fp32 scales in plan order, zero-padded to
+ * 16 bytes.  `staging` is device memory, 16-B aligned, of `cap` bytes >=
+ * kvx_staging_bytes.  The src pool of the plan is read; nothing else is
+ * written.  Errors: INVAL (null, cap too small, host-only plan), RANGE,
+ * MISMATCH, UNSUPPORTED (staging misaligned), HIP.
+ */
+int kvx_pack(const kvx_plan_t* plan, int32_t l0, int32_t l1, void* staging, int64_t cap,
+             hipStream_t stream);
+
+/* Scatter a staging buffer laid out as by kvx_pack into the plan's dst pool.
+ * kvx_unpack(kvx_pack(x)) leaves dst exactly as kvx_push_layer over the same
+ * layers would.  Same errors as kvx_pack. */
+int kvx_unpack(const kvx_plan_t* plan, int32_t l0, int32_t l1, const void* staging, int64_t cap,
+               hipStream_t stream);
+
+/*
+ * Layout and head-slice transform for one layer: for every planned token,
+ * source heads [src_head0, src_head0 + num_heads) land on destination heads
+ * [dst_head0, dst_head0 + num_heads), each side addressed in its own layout
+ * and head count (NHD <-> HND); planned blocks' scales travel unchanged.
+ * This is one TP rank's share of a write that addresses each target TP rank
+ * ([PUSH] "Implementierungsdetails" step 3; rank mapping in [MORI] §6).
+ * num_heads == 0 is a no-op (the ready wait is still enqueued).
+ * Errors: INVAL (negative head index/count, host-only plan), RANGE (layer or
+ * head slice outside either pool), HIP.
+ */
+int kvx_copy_heads(const kvx_plan_t* plan, int32_t layer, int32_t src_head0, int32_t dst_head0,
+                   int32_t num_heads, hipEvent_t ready, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVX_H */

@@ -1,0 +1,337 @@
+"""GPU parity: libkvx's HIP kernels against the CPU oracle, byte for byte.
+
+Small cases cover every entry point, both layouts, 1- and 2-byte elements,
+scales, tails 1..BS, empty requests, prompt lengths = 1 mod BS and lists
+longer than needed; the five workloads run at their full sizes in the launch
+configuration the bench times (one kvx_push_layer per layer), and are checked
+against the oracle on sampled layers (every byte of those layers' K and V
+regions and scales, plus the source left untouched)."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import oracle_pins as P
+from decode_kv_cache_amd import kvx
+from decode_kv_cache_amd import session as S
+from decode_kv_cache_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def host_sides(wl):
+    src, dst = P.pools(O, wl)
+    gs = S.device_side(wl.src, wl.seed, 1, values=(src.kv, src.scales))
+    gd = S.device_side(wl.dst, wl.seed, 2, values=(dst.kv, dst.scales))
+    return src, dst, gs, gd
+
+
+def tokens(wl):
+    return [kvx.kvx_tokens_to_move(p, 0) for p in wl.prompt_lens]
+
+
+def oracle_requests(wl, toks):
+    return [O.Request(n, s, d) for n, s, d in zip(toks, wl.src_tables, wl.dst_tables)]
+
+
+def dev_scales(side):
+    return S.scale_bits(side.sc) if side.sc is not None else None
+
+
+def random_gpu_cases(count, seed0, **over):
+    rng = np.random.Generator(np.random.PCG64(seed0))
+    for i in range(count):
+        kw = dict(layout=["NHD", "HND"][i % 2], elem_bytes=int(rng.choice([1, 2])),
+                  num_layers=int(rng.integers(1, 4)), num_blocks=int(rng.integers(200, 300)),
+                  block_size=int(rng.choice([1, 3, 4, 16])), num_heads=int(rng.integers(1, 5)),
+                  head_dim=int(rng.choice([16, 32, 64, 128])), has_scales=bool(i % 2),
+                  num_requests=int(rng.integers(0, 6)), max_tokens=int(rng.choice([20, 60, 300])),
+                  run_mean=float(rng.choice([1.2, 2.0, 8.0])), extra_ids=int(rng.integers(0, 3)))
+        kw.update(over)
+        if kw["block_size"] == 1:
+            kw["max_tokens"] = min(kw["max_tokens"], 40)
+        yield W.random_case(7000 + seed0 + i, **kw)
+
+
+def test_push_random_small():
+    for wl in random_gpu_cases(40, 0):
+        say("case", wl.name, wl.src)
+        src, dst, gs, gd = host_sides(wl)
+        toks = tokens(wl)
+        plan = kvx.kvx_plan(gs.pool, gd.pool, toks, wl.src_tables, wl.dst_tables)
+        for l in range(wl.src.num_layers):
+            kvx.kvx_push_layer(plan, l)
+        torch.cuda.synchronize()
+        exp = dst.copy()
+        O.push(src, exp, O.make_plan(src.geom, dst.geom, oracle_requests(wl, toks)))
+        assert np.array_equal(gd.kv.cpu().numpy(), exp.kv), wl.name
+        assert np.array_equal(gs.kv.cpu().numpy(), src.kv), wl.name
+        if exp.scales is not None:
+            assert np.array_equal(dev_scales(gd), exp.scales), wl.name
+            assert np.array_equal(dev_scales(gs), src.scales), wl.name
+        plan.close()
+
+
+def test_pack_unpack_random_small():
+    for wl in random_gpu_cases(24, 100):
+        say("case", wl.name, wl.src)
+        src, dst, gs, gd = host_sides(wl)
+        toks = tokens(wl)
+        plan = kvx.kvx_plan(gs.pool, gd.pool, toks, wl.src_tables, wl.dst_tables)
+        op = O.make_plan(src.geom, dst.geom, oracle_requests(wl, toks))
+        L = wl.src.num_layers
+        for l0, l1 in ((0, L), (L - 1, L), (0, 0)):
+            nbytes = kvx.kvx_staging_bytes(plan, l0, l1)
+            assert nbytes == O.staging_bytes(op, l0, l1)
+            stg = torch.full((max(nbytes, 16),), 0xAB, dtype=torch.uint8, device="cuda")
+            kvx.kvx_pack(plan, l0, l1, stg)
+            torch.cuda.synchronize()
+            assert np.array_equal(stg[:nbytes].cpu().numpy(), O.pack(src, op, l0, l1)), (wl.name, l0, l1)
+            if l0 == 0 and l1 == L:
+                kvx.kvx_unpack(plan, l0, l1, stg)
+                torch.cuda.synchronize()
+                exp = dst.copy()
+                O.unpack(O.pack(src, op, l0, l1), exp, op, l0, l1)
+                assert np.array_equal(gd.kv.cpu().numpy(), exp.kv), wl.name
+                if exp.scales is not None:
+                    assert np.array_equal(dev_scales(gd), exp.scales)
+        plan.close()
+
+
+def test_copy_heads_random_small():
+    rng = np.random.Generator(np.random.PCG64(3))
+    for i, (sl, dl) in enumerate([("NHD", "HND"), ("HND", "NHD"), ("NHD", "NHD"), ("HND", "HND")] * 5):
+        hs = int(rng.integers(1, 9))
+        hd = int(rng.integers(1, 9))
+        wl = W.random_case(8000 + i, layout=sl, dst_layout=dl, elem_bytes=int(rng.choice([1, 2])),
+                           num_layers=2, num_blocks=120, block_size=int(rng.choice([1, 4, 16])),
+                           num_heads=hs, dst_heads=hd, head_dim=int(rng.choice([16, 64, 128])),
+                           has_scales=bool(i % 2), num_requests=3, max_tokens=40, run_mean=2.0)
+        say("case", wl.name, sl, dl, hs, hd)
+        src, dst, gs, gd = host_sides(wl)
+        toks = tokens(wl)
+        reqs = oracle_requests(wl, toks)
+        plan = kvx.kvx_plan(gs.pool, gd.pool, toks, wl.src_tables, wl.dst_tables)
+        op = O.make_plan(src.geom, dst.geom, reqs)
+        nh = int(rng.integers(0, min(hs, hd) + 1))
+        s0 = int(rng.integers(0, hs - nh + 1))
+        d0 = int(rng.integers(0, hd - nh + 1))
+        exp = dst.copy()
+        for l in range(2):
+            kvx.kvx_copy_heads(plan, l, s0, d0, nh)
+            if nh:
+                O.copy_heads(src, exp, op, reqs, l, s0, d0, nh)
+        torch.cuda.synchronize()
+        assert np.array_equal(gd.kv.cpu().numpy(), exp.kv), (wl.name, s0, d0, nh)
+        if exp.scales is not None:
+            assert np.array_equal(dev_scales(gd), exp.scales)
+        plan.close()
+
+
+def test_tiny_push_golden():
+    """tiny_push end to end, also against the oracle's stored digests."""
+    import hashlib
+    import test_golden as G
+    g = G.stored()
+    wl = W.tiny_push()
+    src, dst, gs, gd = host_sides(wl)
+    toks = tokens(wl)
+    assert toks == [199]
+    plan = kvx.kvx_plan(gs.pool, gd.pool, toks, wl.src_tables, wl.dst_tables)
+    assert " ".join(f"{a}:{b}:{c}:{d}" for a, b, c, d in plan.runs().tolist()) == g[("tiny_push", "runs")]
+    side = torch.cuda.Stream()
+    ev = torch.cuda.Event()
+    ev.record()
+    for l in range(2):
+        kvx.kvx_push_layer(plan, l, ready=ev, stream=side)
+    side.synchronize()
+    assert hashlib.sha256(gd.kv.cpu().numpy().tobytes()).hexdigest() == g[("tiny_push", "dst_after_sha256")]
+    stg = torch.empty(kvx.kvx_staging_bytes(plan, 0, 2), dtype=torch.uint8, device="cuda")
+    kvx.kvx_pack(plan, 0, 2, stg)
+    torch.cuda.synchronize()
+    assert hashlib.sha256(stg.cpu().numpy().tobytes()).hexdigest() == g[("tiny_push", "staging_sha256")]
+
+
+def test_edge_cases():
+    spec = W.PoolSpec(2, 64, 16, 2, 64, W.BF16)
+    hs, hd = W.host_values(spec, 5, 1), W.host_values(spec, 5, 2)
+    gs = S.device_side(spec, 5, 1, values=hs)
+    gd = S.device_side(spec, 5, 2, values=hd)
+    # empty plans: no requests, and requests with zero tokens
+    for toks, st, dt in (([], [], []), ([0, 0], [[1], []], [[2], []])):
+        plan = kvx.kvx_plan(gs.pool, gd.pool, toks, st, dt)
+        kvx.kvx_push_layer(plan, 1)
+        stg = torch.zeros(16, dtype=torch.uint8, device="cuda")
+        assert kvx.kvx_staging_bytes(plan, 0, 2) == 0
+        kvx.kvx_pack(plan, 0, 2, stg)
+        kvx.kvx_unpack(plan, 0, 2, stg)
+        kvx.kvx_copy_heads(plan, 0, 0, 0, 2)
+        plan.close()
+    torch.cuda.synchronize()
+    assert np.array_equal(gd.kv.cpu().numpy(), hd[0])
+    # whole pool in one run, last block ends the pool; a 1-token move; a
+    # prompt = 1 mod BS whose final block must stay untouched
+    g = P.geom(O, spec)
+    cases = [([64 * 16], [np.arange(64)], [np.arange(64)]),
+             ([1], [[63]], [[0]]),
+             ([kvx.kvx_tokens_to_move(33, 0)], [[5, 6, 7]], [[60, 61, 62]])]
+    for toks, st, dt in cases:
+        gd.kv.copy_(torch.from_numpy(hd[0]).cuda())
+        plan = kvx.kvx_plan(gs.pool, gd.pool, toks, st, dt)
+        for l in range(2):
+            kvx.kvx_push_layer(plan, l)
+        torch.cuda.synchronize()
+        exp = O.Pool(g, hd[0].copy(), None)
+        src = O.Pool(g, hs[0], None)
+        O.push(src, exp, O.make_plan(g, g, [O.Request(n, s, d) for n, s, d in zip(toks, st, dt)]))
+        assert np.array_equal(gd.kv.cpu().numpy(), exp.kv), toks
+        plan.close()
+    bb = g.block_bytes
+    assert np.array_equal(gd.kv[:, :, 62 * bb:63 * bb].cpu().numpy(), hd[0][:, :, 62 * bb:63 * bb])
+    # device-call argument errors
+    plan = kvx.kvx_plan(gs.pool, gd.pool, [5], [[1]], [[2]])
+    for call, code in ((lambda: kvx.kvx_push_layer(plan, 2), kvx.KVX_E_RANGE),
+                       (lambda: kvx.kvx_copy_heads(plan, 0, 1, 0, 2), kvx.KVX_E_RANGE),
+                       (lambda: kvx.kvx_copy_heads(plan, 0, -1, 0, 1), kvx.KVX_E_INVAL),
+                       (lambda: kvx.kvx_pack(plan, 0, 2, torch.empty(16, dtype=torch.uint8, device="cuda")),
+                        kvx.KVX_E_INVAL),
+                       (lambda: kvx.kvx_pack(plan, 0, 1, torch.empty(64 * 1024, dtype=torch.uint8,
+                                                                     device="cuda")[1:]),
+                        kvx.KVX_E_UNSUPPORTED)):
+        with pytest.raises(kvx.KvxError) as e:
+            call()
+        assert e.value.code == code
+    plan.close()
+
+
+# ---------------------------------------------------------------------------
+# full-size workloads, sampled layers checked against the oracle
+# ---------------------------------------------------------------------------
+def snapshot(side, layers):
+    out = {}
+    for l in layers:
+        p = side.spec.phys(l)
+        out[p] = (side.kv[p].cpu().numpy().copy(),
+                  S.scale_bits(side.sc[p]).copy() if side.sc is not None else None)
+    return out
+
+
+def check_layers(wl, gs, gd, src_snap, dst_snap, op, layers, label):
+    """Oracle result for the sampled layers, from pre-transfer snapshots."""
+    for l in layers:
+        p = wl.src.phys(l)
+        skv, ssc = src_snap[p]
+        dkv, dsc = dst_snap[p]
+        for kv in (0, 1):
+            exp = dkv[kv].copy()
+            O.push_region(skv[kv], exp, op.triples)
+            got = gd.kv[p, kv].cpu().numpy()
+            assert np.array_equal(got, exp), (label, l, kv)
+            assert np.array_equal(gs.kv[p, kv].cpu().numpy(), skv[kv]), (label, "src changed", l)
+            if ssc is not None:
+                es = dsc[kv].copy()
+                O.push_scales(ssc[kv], es, op.pairs)
+                assert np.array_equal(S.scale_bits(gd.sc[p, kv]), es), (label, l, kv)
+
+
+def full_push(wl, layers_checked, label):
+    say("workload", label)
+    gs = S.device_side(wl.src, wl.seed, 1)
+    gd = S.device_side(wl.dst, wl.seed, 2)
+    torch.cuda.synchronize()
+    src_snap, dst_snap = snapshot(gs, layers_checked), snapshot(gd, layers_checked)
+    toks = tokens(wl)
+    plan = kvx.kvx_plan(gs.pool, gd.pool, toks, wl.src_tables, wl.dst_tables)
+    side = torch.cuda.Stream()
+    evs = []
+    for l in range(wl.src.num_layers):
+        e = torch.cuda.Event()
+        e.record()
+        evs.append(e)
+        kvx.kvx_push_layer(plan, l, ready=e, stream=side)
+    side.synchronize()
+    op = O.make_plan(P.geom(O, wl.src), P.geom(O, wl.dst), oracle_requests(wl, toks))
+    check_layers(wl, gs, gd, src_snap, dst_snap, op, layers_checked, label)
+    plan.close()
+    del gs, gd
+    torch.cuda.empty_cache()
+
+
+def test_qwen32b_push_full():
+    full_push(W.qwen32b_push(), [0, 1, 37, 63], "qwen32b_push")
+
+
+def test_batched_push_full():
+    wl = W.batched_push()
+    full_push(wl, [0, 15], "batched_push")
+
+
+def test_tp4_share_full():
+    wl = W.tp4_share()
+    say("workload tp4_share")
+    gs = S.device_side(wl.src, wl.seed, 1)
+    gd = S.device_side(wl.dst, wl.seed, 2)
+    torch.cuda.synchronize()
+    toks = tokens(wl)
+    plan = kvx.kvx_plan(gs.pool, gd.pool, toks, wl.src_tables, wl.dst_tables)
+    reqs = oracle_requests(wl, toks)
+    op = O.make_plan(P.geom(O, wl.src), P.geom(O, wl.dst), reqs)
+    layers = [0, 63]
+    for rank in range(4):
+        pre_s, pre_d = snapshot(gs, layers), snapshot(gd, layers)
+        for l in range(wl.src.num_layers):
+            kvx.kvx_copy_heads(plan, l, 2 * rank, 0, 2)
+        torch.cuda.synchronize()
+        for l in layers:
+            exp = O.Pool(P.geom(O, wl.dst), pre_d[l][0][None].copy(), None)
+            src = O.Pool(P.geom(O, wl.src), pre_s[l][0][None], None)
+            sr, dr = O.head_rows(op, 2 * rank, 0, 2, reqs)
+            for kv in (0, 1):
+                O.copy_heads_region(src.kv[0, kv], exp.kv[0, kv], src.geom.row_bytes, sr, dr)
+                assert np.array_equal(gd.kv[l, kv].cpu().numpy(), exp.kv[0, kv]), (rank, l, kv)
+    plan.close()
+
+
+def test_multiturn_fp8_full():
+    wl = W.multiturn_fp8()
+    ex = wl.extra
+    say("workload multiturn_fp8")
+    dec = S.device_side(wl.src, wl.seed, 1)
+    pre = S.device_side(wl.dst, wl.seed, 2)
+    torch.cuda.synchronize()
+    layers = [0, 47]
+    dsnap = snapshot(dec, layers)
+    psnap = snapshot(pre, layers)
+    state = {l: (psnap[l][0].copy(), psnap[l][1].copy()) for l in layers}
+    g = P.geom(O, wl.src)
+    side = torch.cuda.Stream()
+    for t in range(1, ex["turns"] + 1):
+        reusable = ex["growth"] * (t - 1)
+        if t == 1 or not kvx.kvx_should_reuse(reusable, ex["threshold"]):
+            continue
+        toks = [reusable] * ex["sessions"]
+        plan = kvx.kvx_plan(dec.pool, pre.pool, toks, ex["decode_tables"], ex["prefill_tables"][t], stream=side)
+        for l in range(wl.src.num_layers):
+            kvx.kvx_push_layer(plan, l, stream=side)
+        side.synchronize()
+        reqs = [O.reuse_request(t, ex["growth"], ex["threshold"], ex["decode_tables"][s], ex["prefill_tables"][t][s])
+                for s in range(ex["sessions"])]
+        op = O.make_plan(g, g, reqs)
+        for l in layers:
+            for kv in (0, 1):
+                O.push_region(dsnap[l][0][kv], state[l][0][kv], op.triples)
+                O.push_scales(dsnap[l][1][kv], state[l][1][kv], op.pairs)
+        plan.close()
+        if t in (2, ex["turns"]):
+            for l in layers:
+                assert np.array_equal(pre.kv[l].cpu().numpy(), state[l][0]), (t, l)
+                assert np.array_equal(S.scale_bits(pre.sc[l]), state[l][1]), (t, l)
+    for l in layers:
+        assert np.array_equal(dec.kv[l].cpu().numpy(), dsnap[l][0])
