@@ -5,8 +5,9 @@ Default workload (qwen32b_push): Qwen3-32B-shaped KV -- 64 layers, K and V,
 8 KV heads, head_dim 128, block 16, bf16 -- one 8192-token prompt (8191 tokens
 move; the consumer recomputes the last one), block tables of contiguous runs
 with geometric length (mean 4) in pools of 4096 blocks.  One step = the
-layerwise push: for each of the 64 layers, a ready event recorded on the
-compute stream and kvx_push_layer(layer, ready) on a side stream.
+layerwise push: kvx_push_layer(layer, ready[layer]) on a side stream for each
+of the 64 layers, ready[layer] being the (already fired) event of that
+layer's compute.
 
 Prints ONE JSON line on stdout.  Everything else goes to stderr.
 
@@ -113,6 +114,30 @@ def cpu_baseline_push(wl, gs, gd, tokens, seconds: float = 12.0):
                       f"cores ({ncpu} total, {model}); oracle plan {plan_s * 1e3:.1f} ms"}
 
 
+def two_stream_rate(kvx, torch, plan, ready, side, L, steps, step_bytes):
+    """The step with layers alternating between two side streams (already-
+    fired events): one layer's drain overlaps the next layer's ramp-up.  Not
+    part of the default run: the overlapping kernels would skew a kernel-trace
+    average of the push kernel."""
+    sides = [side, torch.cuda.Stream()]
+    for _ in range(2):
+        for l in range(L):
+            kvx.kvx_push_layer(plan, l, ready=ready[l], stream=sides[l % 2])
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(sides[0])
+    sides[1].wait_event(a)
+    for _ in range(steps):
+        for l in range(L):
+            kvx.kvx_push_layer(plan, l, ready=ready[l], stream=sides[l % 2])
+    j = torch.cuda.Event()
+    j.record(sides[1])
+    sides[0].wait_event(j)
+    b.record(sides[0])
+    torch.cuda.synchronize()
+    return step_bytes * steps / (a.elapsed_time(b) * 1e-3) / 1e9
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -121,6 +146,8 @@ def main():
     ap.add_argument("--workload", default="qwen32b_push", choices=["qwen32b_push", "tiny_push"])
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--two-stream", action="store_true",
+                    help="also time the step with layers alternating over two side streams")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
@@ -222,6 +249,11 @@ def main():
     fresh_gbs = step_bytes * args.steps / (a.elapsed_time(b) * 1e-3) / 1e9
     log(f"with fresh per-layer events: {fresh_gbs:.1f} GB/s")
 
+    two_gbs = None
+    if args.two_stream:
+        two_gbs = two_stream_rate(kvx, torch, plan, ready, side, L, args.steps, step_bytes)
+        log(f"layers alternating over two side streams: {two_gbs:.1f} GB/s")
+
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline ...")
@@ -239,7 +271,7 @@ def main():
                    "merged_runs": nruns, "bytes_per_step": step_bytes,
                    "step": f"{L} x (ready event on compute stream + kvx_push_layer on side stream)",
                    "host_plan_ms": round(plan_ms, 3),
-                   "fresh_event_GBs": round(fresh_gbs, 1)},
+                   "fresh_event_GBs": round(fresh_gbs, 1), "two_stream_GBs": None if two_gbs is None else round(two_gbs, 1)},
         "roofline": roofline,
         "cpu_baseline": cpu,
     }

@@ -36,11 +36,11 @@ static_assert(sizeof(BlockPair) == 16, "BlockPair is 16 bytes");
 #define KVX_THREADS 256
 #endif
 #ifndef KVX_VEC_PER_THREAD
-#define KVX_VEC_PER_THREAD 4
+#define KVX_VEC_PER_THREAD 8
 #endif
 constexpr int kThreads = KVX_THREADS;            // 4 wave64 per workgroup
 constexpr int kVecPerThread = KVX_VEC_PER_THREAD;  // 16-B vectors each lane keeps in flight
-constexpr int64_t kPieceBytes = int64_t(kThreads) * kVecPerThread * 16;  // 16 KiB
+constexpr int64_t kPieceBytes = int64_t(kThreads) * kVecPerThread * 16;  // 32 KiB
 
 struct Geom {
   int32_t L = 0, NB = 0, BS = 0, H = 0, D = 0, E = 0, layout = 0;

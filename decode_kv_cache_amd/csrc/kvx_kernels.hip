@@ -40,29 +40,24 @@ struct CopyArgs {
   uint32_t* out_sc[2];
 };
 
-#ifndef KVX_NONTEMPORAL
-#define KVX_NONTEMPORAL 1
-#endif
 #ifndef KVX_ANY_ORDER
 #define KVX_ANY_ORDER 0
 #endif
 
-// Streaming accesses: nothing is re-read, so loads and stores carry the
-// nontemporal hint and bypass cache allocation where the hardware allows.
-__device__ __forceinline__ v4u ld_stream(const v4u* p) {
-#if KVX_NONTEMPORAL
-  return __builtin_nontemporal_load(p);
-#else
-  return *p;
+// Cache policy of the streaming copy (buffer instruction aux bits on gfx950:
+// bit 0 = sc0, bit 1 = nt, bit 4 = sc1).  Nothing is re-read, so loads are
+// non-temporal; stores are non-temporal at device scope (nt sc1), which
+// measured best among the combinations of these bits.
+#ifndef KVX_LD_AUX
+#define KVX_LD_AUX 2
 #endif
-}
-__device__ __forceinline__ void st_stream(v4u* p, v4u v) {
-#if KVX_NONTEMPORAL
-  __builtin_nontemporal_store(v, p);
-#else
-  *p = v;
+#ifndef KVX_ST_AUX
+#define KVX_ST_AUX 18
 #endif
-}
+constexpr int kBufferWord3 = 0x00020000;  // raw byte buffer, gfx9 family
+
+__device__ __forceinline__ v4u ld_stream(const v4u* p) { return __builtin_nontemporal_load(p); }
+__device__ __forceinline__ void st_stream(v4u* p, v4u v) { __builtin_nontemporal_store(v, p); }
 
 // One workgroup copies one piece of the K (blockIdx.y == 0) or V (== 1)
 // region; workgroups past the pieces copy the planned blocks' scales.
@@ -74,26 +69,21 @@ __global__ __launch_bounds__(kThreads) void copy_kernel(CopyArgs a) {
     const Piece pc = a.pieces[x];
     const int64_t ioff = MODE == kUnpack ? pc.stg_off : pc.src_off;
     const int64_t ooff = MODE == kPack ? pc.stg_off : pc.dst_off;
-    const v4u* s = reinterpret_cast<const v4u*>(a.in[kv] + ioff);
-    v4u* d = reinterpret_cast<v4u*>(a.out[kv] + ooff);
-    const int nvec = pc.len >> 4;
+    // One buffer resource per piece (base = piece start, size = piece
+    // length): lanes past a short piece's end read zeros and their stores
+    // are dropped by the hardware range check, so every lane issues all of
+    // its loads before its first store without any masking.
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(a.in[kv] + ioff), (short)0, pc.len, kBufferWord3);
+    const __amdgpu_buffer_rsrc_t rd = __builtin_amdgcn_make_buffer_rsrc(a.out[kv] + ooff, (short)0, pc.len, kBufferWord3);
     const int t = threadIdx.x;
     v4u r[kVecPerThread];
-    if (nvec == kVecPerThread * kThreads) {
 #pragma unroll
-      for (int k = 0; k < kVecPerThread; ++k) r[k] = ld_stream(s + t + k * kThreads);
+    for (int k = 0; k < kVecPerThread; ++k)
+      r[k] = __builtin_amdgcn_raw_buffer_load_b128(rs, (t + k * kThreads) * 16, 0, KVX_LD_AUX);
 #pragma unroll
-      for (int k = 0; k < kVecPerThread; ++k) st_stream(d + t + k * kThreads, r[k]);
-    } else {
-      // Short piece: lanes past the end re-read the piece's last vector so
-      // that every load is issued unconditionally and stays in flight; only
-      // the stores are masked.
-#pragma unroll
-      for (int k = 0; k < kVecPerThread; ++k) r[k] = ld_stream(s + min(t + k * kThreads, nvec - 1));
-#pragma unroll
-      for (int k = 0; k < kVecPerThread; ++k)
-        if (t + k * kThreads < nvec) st_stream(d + t + k * kThreads, r[k]);
-    }
+    for (int k = 0; k < kVecPerThread; ++k)
+      __builtin_amdgcn_raw_buffer_store_b128(r[k], rd, (t + k * kThreads) * 16, 0, KVX_ST_AUX);
     return;
   }
   const int i = (x - a.first_scale_wg) * kThreads + threadIdx.x;
