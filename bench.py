@@ -16,7 +16,6 @@ Prints ONE JSON line on stdout.  Everything else goes to stderr.
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import platform
@@ -37,18 +36,12 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_source_digest() -> str:
-    h = hashlib.sha256()
-    for f in ("kvx_kernels.hip", "kvx_internal.h"):
-        with open(os.path.join(ROOT, "decode_kv_cache_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
-    return h.hexdigest()[:16]
-
-
 def counter_traffic(workload: str):
-    """HBM bytes per launch of the dominant kernel from the committed
-    rocprofv3 --pmc summary, scaled by the copy-kernel calibration factor;
-    None when no summary exists or the kernel source changed since."""
+    """HBM bytes per launch of the push kernel from the committed rocprofv3
+    --pmc summary (FETCH_SIZE and WRITE_SIZE passes, each scaled by the
+    counter's reading for a plain copy of known size); None when there is no
+    summary or the kernel sources changed since it was taken."""
+    from decode_kv_cache_amd.profiling import kernel_source_digest
     path = os.path.join(PROFILES, f"push_kernel_{workload}_pmc.txt")
     if not os.path.exists(path):
         return None
@@ -56,7 +49,7 @@ def counter_traffic(workload: str):
     for line in open(path):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
-            kv[k.strip()] = v.strip()
+            kv[k.strip()] = v.strip().split()[0] if v.strip() else ""
     if kv.get("kernel_source_sha256_16") != kernel_source_digest():
         return None
     try:
@@ -138,6 +131,26 @@ def two_stream_rate(kvx, torch, plan, ready, side, L, steps, step_bytes):
     return step_bytes * steps / (a.elapsed_time(b) * 1e-3) / 1e9
 
 
+CALIB_BYTES = 1 << 30
+
+
+def counters_run(torch, plan, side, L, step_bytes):
+    """Kernels for a counter pass: kvxb_copy of CALIB_BYTES (known traffic:
+    CALIB_BYTES read + CALIB_BYTES written) three times, then two layerwise
+    push steps."""
+    from decode_kv_cache_amd import bench_support as B
+    from decode_kv_cache_amd import kvx
+    buf = torch.empty(2 * CALIB_BYTES, dtype=torch.uint8, device="cuda")
+    for _ in range(3):
+        B.copy(buf[CALIB_BYTES:], buf[:CALIB_BYTES], CALIB_BYTES, stream=side)
+    for _ in range(2):
+        for l in range(L):
+            kvx.kvx_push_layer(plan, l, stream=side)
+    torch.cuda.synchronize()
+    print(json.dumps({"counters_run": True, "calib_copy_bytes": CALIB_BYTES, "push_launches": 2 * L,
+                      "push_bytes_per_launch": step_bytes // L}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -146,6 +159,8 @@ def main():
     ap.add_argument("--workload", default="qwen32b_push", choices=["qwen32b_push", "tiny_push"])
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--counters", action="store_true",
+                    help="short run for rocprofv3 --pmc: a 1 GiB plain copy (calibration) x3, then 2 steps")
     ap.add_argument("--two-stream", action="store_true",
                     help="also time the step with layers alternating over two side streams")
     args = ap.parse_args()
@@ -187,6 +202,11 @@ def main():
     log(f"plan: {nruns} runs, {len(plan.triples())} triples/region, {rd + wr} B per layer, "
         f"{step_bytes} B per step, host plan {plan_ms:.2f} ms")
 
+    if args.counters:
+        counters_run(torch, plan, side, L, step_bytes)
+        plan.close()
+        return
+
     # One ready event per layer, recorded on the compute stream.  The headline
     # step uses events that have already fired (the layer's compute is done):
     # kvx_push_layer then enqueues no wait and the side stream holds nothing
@@ -220,15 +240,31 @@ def main():
         f"min {per_step.min() * 1e3:.1f}, max {per_step.max() * 1e3:.1f}), wall {wall * 1e3:.1f} ms, "
         f"{gbs:.1f} GB/s = {100 * gbs / HBM_PEAK_GBS:.1f}% of {HBM_PEAK_GBS:.0f} GB/s")
 
-    # push kernel average launch duration over the timed region (events on
-    # the side stream, which carries only the push kernels)
+    # The side stream carries nothing but the push kernels, back to back (a
+    # kernel trace shows no gaps between them), so the timed region's span
+    # over its launches is the push kernel's average launch duration.
     k_avg_us = ms_per_step * 1e3 / L
+
+    # Cross-check in a separate short pass: every push kernel records its own
+    # start/end timestamps (from the dispatch packet).  Such launches are
+    # spaced out on the queue, so this pass is not used for throughput.
+    n_chk = min(3, args.steps)
+    k0 = [torch.cuda.Event(enable_timing=True) for _ in range(L * n_chk)]
+    k1 = [torch.cuda.Event(enable_timing=True) for _ in range(L * n_chk)]
+    for i in range(n_chk):
+        for l in range(L):
+            kvx.kvx_push_layer_timed(plan, l, k0[i * L + l], k1[i * L + l], ready=ready[l], stream=side)
+    torch.cuda.synchronize()
+    kd = np.array([k0[j].elapsed_time(k1[j]) for j in range(L * n_chk)]) * 1e3  # us
+    log(f"push kernel: {k_avg_us:.2f} us per launch over the timed region; dispatch timestamps in a "
+        f"separate pass: avg {kd.mean():.2f} us (min {kd.min():.2f}, max {kd.max():.2f})")
     per_launch = rd + wr
     ach = per_launch / (k_avg_us * 1e-6) / 1e9
     traffic = counter_traffic(args.workload)
     roofline = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic,
                 "kernel": "kvx::copy_kernel<0> (kvx_push_layer)", "avg_launch_us": round(k_avg_us, 3),
+                "kernel_us_dispatch_stamps": round(float(kd.mean()), 3),
                 "algorithmic_bytes_per_launch": per_launch}
     log(f"push kernel: avg {k_avg_us:.2f} us per launch -> {ach:.1f} GB/s")
 

@@ -40,10 +40,6 @@ struct CopyArgs {
   uint32_t* out_sc[2];
 };
 
-#ifndef KVX_ANY_ORDER
-#define KVX_ANY_ORDER 0
-#endif
-
 // Cache policy of the streaming copy (buffer instruction aux bits on gfx950:
 // bit 0 = sc0, bit 1 = nt, bit 4 = sc1).  Nothing is re-read, so loads are
 // non-temporal; stores are non-temporal at device scope (nt sc1), which
@@ -162,7 +158,8 @@ static int64_t scale_wgs(int64_t slots) { return (slots + kThreads - 1) / kThrea
 // Enqueue the copy kernel for one layer; `in`/`out` and the scale pointers
 // are already resolved for the mode.  Splits very long work lists.
 template <int MODE>
-static int launch_copy(kvx_plan_t* p, CopyArgs a, int64_t scale_slots, hipStream_t s) {
+static int launch_copy(kvx_plan_t* p, CopyArgs a, int64_t scale_slots, hipStream_t s,
+                       hipEvent_t started = nullptr, hipEvent_t finished = nullptr) {
   const int64_t np = int64_t(p->pieces.size());
   const bool scales = a.in_sc[0] != nullptr;
   const int64_t nsw = scales ? scale_wgs(scale_slots) : 0;
@@ -179,12 +176,13 @@ static int launch_copy(kvx_plan_t* p, CopyArgs a, int64_t scale_slots, hipStream
     a.first_scale_wg = int32_t(cnt);
     const int64_t gx = cnt + (last ? nsw : 0);
     if (gx > 0) {
-#if KVX_ANY_ORDER
-      hipExtLaunchKernelGGL(copy_kernel<MODE>, dim3(unsigned(gx), 2), dim3(kThreads), 0, s, nullptr, nullptr,
-                            hipExtAnyOrderLaunch, a);
-#else
-      hipLaunchKernelGGL(copy_kernel<MODE>, dim3(unsigned(gx), 2), dim3(kThreads), 0, s, a);
-#endif
+      if (started || finished) {
+        // timestamps come from the dispatch packet itself: no extra packets
+        hipExtLaunchKernelGGL(copy_kernel<MODE>, dim3(unsigned(gx), 2), dim3(kThreads), 0, s,
+                              first == 0 ? started : nullptr, last ? finished : nullptr, 0u, a);
+      } else {
+        hipLaunchKernelGGL(copy_kernel<MODE>, dim3(unsigned(gx), 2), dim3(kThreads), 0, s, a);
+      }
     }
     first += cnt;
   } while (first < np);
@@ -204,6 +202,11 @@ using namespace kvx;
 extern "C" {
 
 int kvx_push_layer(const kvx_plan_t* cp, int32_t layer, hipEvent_t ready, hipStream_t stream) {
+  return kvx_push_layer_timed(cp, layer, ready, stream, nullptr, nullptr);
+}
+
+int kvx_push_layer_timed(const kvx_plan_t* cp, int32_t layer, hipEvent_t ready, hipStream_t stream,
+                         hipEvent_t started, hipEvent_t finished) {
   int rc = check_device_plan(cp, "kvx_push_layer");
   if (rc) return rc;
   kvx_plan_t* p = const_cast<kvx_plan_t*>(cp);
@@ -224,7 +227,7 @@ int kvx_push_layer(const kvx_plan_t* cp, int32_t layer, hipEvent_t ready, hipStr
     a.out_sc[0] = reinterpret_cast<uint32_t*>(p->dst.ks[layer]);
     a.out_sc[1] = reinterpret_cast<uint32_t*>(p->dst.vs[layer]);
   }
-  return launch_copy<kPush>(p, a, int64_t(p->blocks.size()), stream);
+  return launch_copy<kPush>(p, a, int64_t(p->blocks.size()), stream, started, finished);
 }
 
 static int staging_call(const kvx_plan_t* cp, int32_t l0, int32_t l1, const void* staging,

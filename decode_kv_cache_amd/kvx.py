@@ -56,6 +56,7 @@ _SIGS = {
     "kvx_plan_bytes": (C.c_int, [_P, C.POINTER(_I64), C.POINTER(_I64)]),
     "kvx_plan_destroy": (None, [_P]),
     "kvx_push_layer": (C.c_int, [_P, _I32, _P, _P]),
+    "kvx_push_layer_timed": (C.c_int, [_P, _I32, _P, _P, _P, _P]),
     "kvx_staging_bytes": (C.c_int, [_P, _I32, _I32, C.POINTER(_I64)]),
     "kvx_pack": (C.c_int, [_P, _I32, _I32, _P, _I64, _P]),
     "kvx_unpack": (C.c_int, [_P, _I32, _I32, _P, _I64, _P]),
@@ -247,6 +248,17 @@ def kvx_plan_raw(src: Pool, dst: Pool, num_requests: int, num_tokens, id_offsets
 
 def kvx_push_layer(plan: Plan, layer: int, ready=None, stream=None) -> None:
     _check("kvx_push_layer", lib().kvx_push_layer(plan.handle, layer, _event(ready), _stream(stream)))
+
+
+def kvx_push_layer_timed(plan: Plan, layer: int, started, finished, ready=None, stream=None) -> None:
+    """kvx_push_layer with the kernel's own start/end timestamps recorded into
+    two timing-enabled torch.cuda.Event objects."""
+    for e in (started, finished):
+        if e is not None and not e.cuda_event:
+            # torch creates the underlying event lazily; make it exist first
+            e.record(torch.cuda.current_stream())
+    _check("kvx_push_layer_timed", lib().kvx_push_layer_timed(
+        plan.handle, layer, _event(ready), _stream(stream), _event(started), _event(finished)))
 
 
 def kvx_staging_bytes(plan: Plan, l0: int, l1: int) -> int:

@@ -1,0 +1,140 @@
+"""Summaries of rocprofv3 CSV output for the files under profiles/.
+
+  python -m decode_kv_cache_amd.profiling trace <dir> <out.txt> --command "..."
+      per-kernel call count and durations from <dir>/*_kernel_stats.csv and
+      *_kernel_trace.csv (rocprofv3 --kernel-trace --stats -f csv)
+  python -m decode_kv_cache_amd.profiling pmc <fetch_dir> <write_dir> <out.txt> \\
+          --workload NAME --command-fetch "..." --command-write "..."
+      HBM traffic per push-kernel dispatch from a FETCH_SIZE pass and a
+      WRITE_SIZE pass of ``bench.py --counters``, each scaled by what the same
+      counter reads for the plain copy kernel of known size run first.
+
+The pmc summary carries the digest of the kernel sources it was taken with;
+bench.py reports its traffic only while the sources are unchanged.
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import os
+import statistics
+from collections import defaultdict
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+PUSH_KERNEL = "kvx::copy_kernel<0>"
+CALIB_KERNEL = "copy_kernel(unsigned int __vector(4)*"   # kvxb_copy in libkvx_bench.so
+CALIB_BYTES = 1 << 30
+
+
+def kernel_source_digest() -> str:
+    h = hashlib.sha256()
+    for f in ("kvx_kernels.hip", "kvx_internal.h"):
+        with open(os.path.join(PKG, "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def _one(pattern: str) -> str:
+    hits = glob.glob(pattern, recursive=True)
+    if not hits:
+        raise FileNotFoundError(pattern)
+    return hits[0]
+
+
+def _short(name: str) -> str:
+    return name if len(name) <= 90 else name[:87] + "..."
+
+
+def trace_summary(d: str, command: str) -> str:
+    rows = list(csv.DictReader(open(_one(os.path.join(d, "**", "*kernel_stats.csv")))))
+    trace = list(csv.DictReader(open(_one(os.path.join(d, "**", "*kernel_trace.csv")))))
+    per = defaultdict(list)
+    for r in trace:
+        per[r["Kernel_Name"]].append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    out = ["# rocprofv3 --kernel-trace --stats summary", f"command: {command}",
+           f"kernel_source_sha256_16: {kernel_source_digest()}", "",
+           "| kernel | calls | avg us | median us | min us | max us | share |", "|---|---|---|---|---|---|---|"]
+    for r in rows:
+        name = r["Name"]
+        durs = per.get(name, [])
+        med = statistics.median(durs) / 1e3 if durs else float("nan")
+        out.append(f"| {_short(name)} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | {med:.2f} | "
+                   f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.1f}% |")
+    return "\n".join(out) + "\n"
+
+
+def counters(d: str):
+    rows = list(csv.DictReader(open(_one(os.path.join(d, "**", "*counter_collection.csv")))))
+    per = defaultdict(list)
+    for r in rows:
+        per[r["Kernel_Name"]].append(float(r["Counter_Value"]))
+    return per
+
+
+def _avg_for(per, key):
+    vals = [v for k, vs in per.items() if key in k for v in vs]
+    if not vals:
+        raise KeyError(key)
+    return sum(vals) / len(vals), len(vals)
+
+
+def pmc_summary(fetch_dir: str, write_dir: str, workload: str, push_bytes: int, cmd_f: str, cmd_w: str) -> str:
+    f, w = counters(fetch_dir), counters(write_dir)
+    cf, ncf = _avg_for(f, CALIB_KERNEL)
+    cw, ncw = _avg_for(w, CALIB_KERNEL)
+    pf, npf = _avg_for(f, PUSH_KERNEL)
+    pw, npw = _avg_for(w, PUSH_KERNEL)
+    ff = CALIB_BYTES / (cf * 1024)
+    fw = CALIB_BYTES / (cw * 1024)
+    rd = pf * 1024 * ff
+    wr = pw * 1024 * fw
+    lines = [
+        f"# push kernel HBM traffic, workload {workload}: rocprofv3 --pmc FETCH_SIZE, then --pmc WRITE_SIZE",
+        f"command_fetch: {cmd_f}",
+        f"command_write: {cmd_w}",
+        f"kernel_source_sha256_16: {kernel_source_digest()}",
+        f"calib_kernel: kvxb_copy, {CALIB_BYTES} B read and {CALIB_BYTES} B written per dispatch",
+        f"calib_fetch_kib_per_dispatch: {cf:.1f}  (dispatches: {ncf})",
+        f"calib_write_kib_per_dispatch: {cw:.1f}  (dispatches: {ncw})",
+        f"fetch_factor: {ff:.5f}",
+        f"write_factor: {fw:.5f}",
+        f"push_fetch_kib_per_dispatch: {pf:.1f}  (dispatches: {npf})",
+        f"push_write_kib_per_dispatch: {pw:.1f}  (dispatches: {npw})",
+        f"calibrated_read_bytes_per_launch: {rd:.0f}",
+        f"calibrated_write_bytes_per_launch: {wr:.0f}",
+        f"calibrated_hbm_bytes_per_launch: {rd + wr:.0f}",
+        f"algorithmic_bytes_per_launch: {push_bytes}",
+        f"traffic_over_algorithmic: {(rd + wr) / push_bytes:.4f}",
+    ]
+    return "\n".join(lines) + "\n"
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="what", required=True)
+    t = sub.add_parser("trace")
+    t.add_argument("dir")
+    t.add_argument("out")
+    t.add_argument("--command", required=True)
+    p = sub.add_parser("pmc")
+    p.add_argument("fetch_dir")
+    p.add_argument("write_dir")
+    p.add_argument("out")
+    p.add_argument("--workload", required=True)
+    p.add_argument("--push-bytes", type=int, required=True)
+    p.add_argument("--command-fetch", required=True)
+    p.add_argument("--command-write", required=True)
+    a = ap.parse_args()
+    if a.what == "trace":
+        text = trace_summary(a.dir, a.command)
+    else:
+        text = pmc_summary(a.fetch_dir, a.write_dir, a.workload, a.push_bytes, a.command_fetch, a.command_write)
+    with open(a.out, "w") as fh:
+        fh.write(text)
+    print(text)
+
+
+if __name__ == "__main__":
+    main()

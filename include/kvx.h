@@ -201,6 +201,15 @@ void kvx_plan_destroy(kvx_plan_t* plan);
  */
 int kvx_push_layer(const kvx_plan_t* plan, int32_t layer, hipEvent_t ready, hipStream_t stream);
 
+/* kvx_push_layer whose kernel records its own start and end timestamps into
+ * `started` / `finished` (events created with timing enabled; either may be
+ * NULL).  The timestamps are taken from the kernel dispatch itself, so no
+ * extra queue packets are added: hipEventElapsedTime(started, finished) is
+ * the kernel's execution time.  A plan whose work list is empty launches
+ * nothing and leaves both events untouched.  Same errors as kvx_push_layer. */
+int kvx_push_layer_timed(const kvx_plan_t* plan, int32_t layer, hipEvent_t ready, hipStream_t stream,
+                         hipEvent_t started, hipEvent_t finished);
+
 /* Staging bytes for layers [l0, l1): (l1 - l0) * 2 * (payload + scale
  * segment), where payload = sum of the region's triple lengths and the scale
  * segment is 4 bytes per planned block rounded up to 16 (0 without scales).

@@ -149,9 +149,11 @@ def test_tiny_push_golden():
     side = torch.cuda.Stream()
     ev = torch.cuda.Event()
     ev.record()
-    for l in range(2):
-        kvx.kvx_push_layer(plan, l, ready=ev, stream=side)
+    kvx.kvx_push_layer(plan, 0, ready=ev, stream=side)
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    kvx.kvx_push_layer_timed(plan, 1, t0, t1, ready=ev, stream=side)
     side.synchronize()
+    assert 0 < t0.elapsed_time(t1) < 1000  # ms: the kernel's own start/end
     assert hashlib.sha256(gd.kv.cpu().numpy().tobytes()).hexdigest() == g[("tiny_push", "dst_after_sha256")]
     stg = torch.empty(kvx.kvx_staging_bytes(plan, 0, 2), dtype=torch.uint8, device="cuda")
     kvx.kvx_pack(plan, 0, 2, stg)
