@@ -9,6 +9,16 @@ layerwise push: kvx_push_layer(layer, ready[layer]) on a side stream for each
 of the 64 layers, ready[layer] being the (already fired) event of that
 layer's compute.
 
+Other workloads (--workload), one JSON line each:
+  batched_push   64 prompts uniform in [1024, 16384], fragmented tables (mean
+                 run 2), each layer's push waiting on a synthetic compute
+                 kernel of that layer running concurrently on the compute stream
+  tp4_share      NHD 8 heads -> HND 2-head slice (TP4 rank 0), 32 x 4096 tokens
+  multiturn_fp8  fp8 KV + fp32 per-block scales, 32 sessions, turns 2..8 copy
+                 the decode side's retained prefix back to the prefill pool
+  pack_unpack    the default workload through a contiguous staging buffer
+  tiny_push      2 layers, one 200-token prompt (launch-bound; no claim)
+
 Prints ONE JSON line on stdout.  Everything else goes to stderr.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
@@ -30,6 +40,8 @@ sys.path.insert(0, ROOT)
 METRIC = "KV block transfer GB/s (read+write) on 1 MI355X + % of HBM peak"
 HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, AMD published peak
 PROFILES = os.path.join(ROOT, "profiles")
+CALIB_BYTES = 1 << 30
+WORKLOAD_NAMES = ["qwen32b_push", "batched_push", "tp4_share", "multiturn_fp8", "pack_unpack", "tiny_push"]
 
 
 def log(*a):
@@ -37,10 +49,10 @@ def log(*a):
 
 
 def counter_traffic(workload: str):
-    """HBM bytes per launch of the push kernel from the committed rocprofv3
-    --pmc summary (FETCH_SIZE and WRITE_SIZE passes, each scaled by the
-    counter's reading for a plain copy of known size); None when there is no
-    summary or the kernel sources changed since it was taken."""
+    """HBM bytes per launch of the dominant kernel from the committed
+    rocprofv3 --pmc summary (FETCH_SIZE and WRITE_SIZE passes, each scaled by
+    the counter's reading for a plain copy of known size); None when there is
+    no summary or the kernel sources changed since it was taken."""
     from decode_kv_cache_amd.profiling import kernel_source_digest
     path = os.path.join(PROFILES, f"push_kernel_{workload}_pmc.txt")
     if not os.path.exists(path):
@@ -71,43 +83,189 @@ def cpu_info():
     return cores, os.cpu_count(), model
 
 
-def cpu_baseline_push(wl, gs, gd, tokens, seconds: float = 12.0):
-    """The oracle (as it stands) on the host: its triple-memcpy push over a
-    sample of the workload's layers (32 layers: more bytes than a host last-
-    level cache holds), repeated for about `seconds`."""
-    import oracle as O
-    from decode_kv_cache_amd import session as S
-    sample_layers = list(range(min(32, wl.src.num_layers)))
-    gsrc = O.Geometry(len(sample_layers), wl.src.num_blocks, wl.src.block_size, wl.src.num_heads,
-                      wl.src.head_dim, wl.src.elem_bytes, wl.src.layout, wl.src.has_scales)
-    gdst = O.Geometry(len(sample_layers), wl.dst.num_blocks, wl.dst.block_size, wl.dst.num_heads,
-                      wl.dst.head_dim, wl.dst.elem_bytes, wl.dst.layout, wl.dst.has_scales)
-    src = O.Pool(gsrc, np.stack([gs.kv[wl.src.phys(l)].cpu().numpy() for l in sample_layers]),
-                 np.stack([S.scale_bits(gs.sc[wl.src.phys(l)]) for l in sample_layers]) if gs.sc is not None else None)
-    dst = O.Pool(gdst, np.stack([gd.kv[wl.dst.phys(l)].cpu().numpy() for l in sample_layers]),
-                 np.stack([S.scale_bits(gd.sc[wl.dst.phys(l)]) for l in sample_layers]) if gd.sc is not None else None)
-    reqs = [O.Request(n, s, d) for n, s, d in zip(tokens, wl.src_tables, wl.dst_tables)]
-    t0 = time.perf_counter()
-    plan = O.make_plan(gsrc, gdst, reqs)
-    plan_s = time.perf_counter() - t0
-    per_pass = len(sample_layers) * sum(plan.bytes_per_layer())
+def cpu_baseline(what: str, pass_fn, bytes_per_pass: int, seconds: float, setup_s: float):
+    """Time the oracle's own copy routine, single-threaded, for ~`seconds`."""
     passes = 0
     t0 = time.perf_counter()
     while True:
-        O.push(src, dst, plan)
+        pass_fn()
         passes += 1
         el = time.perf_counter() - t0
         if el >= seconds:
             break
     cores, ncpu, model = cpu_info()
-    return {"value": round(per_pass * passes / el / 1e9, 3), "unit": "GB/s", "cores": 1,
-            "kind": "oracle",
-            "sample": f"oracle push (numpy triple memcpy, single thread) of {len(sample_layers)} of "
-                      f"{wl.src.num_layers} layers, {passes} passes in {el:.1f} s; host has {cores} usable "
-                      f"cores ({ncpu} total, {model}); oracle plan {plan_s * 1e3:.1f} ms"}
+    return {"value": round(bytes_per_pass * passes / el / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{what}; {passes} passes in {el:.1f} s (single thread; the host has {cores} usable cores, "
+                      f"{ncpu} total, {model}); oracle plan {setup_s * 1e3:.1f} ms"}
 
 
-def two_stream_rate(kvx, torch, plan, ready, side, L, steps, step_bytes):
+def oracle_pools(wl, gs, gd, layers):
+    """Host copies of the sampled layers of both pools as oracle pools."""
+    import oracle as O
+    from decode_kv_cache_amd import session as S
+
+    def geom(spec, n):
+        return O.Geometry(n, spec.num_blocks, spec.block_size, spec.num_heads, spec.head_dim, spec.elem_bytes,
+                          spec.layout, spec.has_scales)
+
+    def pool(spec, side):
+        kv = np.stack([side.kv[spec.phys(l)].cpu().numpy() for l in layers])
+        sc = np.stack([S.scale_bits(side.sc[spec.phys(l)]) for l in layers]) if side.sc is not None else None
+        return O.Pool(geom(spec, len(layers)), kv, sc)
+    return pool(wl.src, gs), pool(wl.dst, gd)
+
+
+class Timer:
+    """Events on one stream around a region."""
+
+    def __init__(self, torch, stream):
+        self.torch, self.stream = torch, stream
+        self.a = torch.cuda.Event(enable_timing=True)
+        self.b = torch.cuda.Event(enable_timing=True)
+
+    def __enter__(self):
+        self.torch.cuda.synchronize()
+        self.a.record(self.stream)
+        return self
+
+    def __exit__(self, *exc):
+        self.b.record(self.stream)
+        self.torch.cuda.synchronize()
+        self.ms = self.a.elapsed_time(self.b)
+
+
+def roofline(bytes_per_launch: int, avg_us: float, kernel: str, workload: str, extra=None):
+    ach = bytes_per_launch / (avg_us * 1e-6) / 1e9
+    r = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+         "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": counter_traffic(workload), "kernel": kernel,
+         "avg_launch_us": round(avg_us, 3), "algorithmic_bytes_per_launch": bytes_per_launch}
+    if extra:
+        r.update(extra)
+    return r
+
+
+# ---------------------------------------------------------------------------
+# workloads
+# ---------------------------------------------------------------------------
+def bench_push(args, torch, kvx, S, W):
+    """qwen32b_push (default) and tiny_push: the layerwise push."""
+    wl = W.WORKLOADS[args.workload]()
+    gs, gd = S.device_side(wl.src, wl.seed, 1), S.device_side(wl.dst, wl.seed, 2)
+    tokens = [kvx.kvx_tokens_to_move(p, 0) for p in wl.prompt_lens]
+    side = torch.cuda.Stream()
+    compute = torch.cuda.current_stream()
+    t0 = time.perf_counter()
+    plan = kvx.kvx_plan(gs.pool, gd.pool, tokens, wl.src_tables, wl.dst_tables, stream=side)
+    plan_ms = (time.perf_counter() - t0) * 1e3
+    rd, wr = plan.bytes_per_layer()
+    L = wl.src.num_layers
+    step_bytes = (rd + wr) * L
+    nruns = len(plan.runs())
+    log(f"plan: {nruns} runs, {len(plan.triples())} triples/region, {rd + wr} B per layer, "
+        f"{step_bytes} B per step, host plan {plan_ms:.2f} ms")
+
+    if args.counters:
+        counters_run(torch, kvx, plan, side, L, rd + wr)
+        plan.close()
+        return None
+
+    # One ready event per layer, recorded on the compute stream.  The headline
+    # step uses events that have already fired (the layer's compute is done):
+    # kvx_push_layer then enqueues no wait and the side stream holds nothing
+    # but the push kernels.
+    ready = [torch.cuda.Event() for _ in range(L)]
+    for e in ready:
+        e.record(compute)
+    torch.cuda.synchronize()
+
+    def step():
+        for l in range(L):
+            kvx.kvx_push_layer(plan, l, ready=ready[l], stream=side)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    marks[0].record(side)
+    for i in range(args.steps):
+        step()
+        marks[i + 1].record(side)
+    torch.cuda.synchronize()
+    per_step = np.array([marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps)])  # ms
+    span_ms = marks[0].elapsed_time(marks[-1])
+    ms_per_step = span_ms / args.steps
+    gbs = step_bytes * args.steps / (span_ms * 1e-3) / 1e9
+    log(f"span {span_ms:.3f} ms for {args.steps} steps ({ms_per_step * 1e3:.1f} us/step, "
+        f"min {per_step.min() * 1e3:.1f}, max {per_step.max() * 1e3:.1f}): "
+        f"{gbs:.1f} GB/s = {100 * gbs / HBM_PEAK_GBS:.1f}% of {HBM_PEAK_GBS:.0f} GB/s")
+
+    # The side stream carries nothing but the push kernels, back to back (a
+    # kernel trace shows no gaps between them), so the timed region's span
+    # over its launches is the push kernel's average launch duration.
+    k_avg_us = ms_per_step * 1e3 / L
+    # Cross-check in a separate short pass: every push kernel records its own
+    # start/end timestamps (from the dispatch packet).  Such launches are
+    # spaced out on the queue, so this pass is not used for throughput.
+    n_chk = min(3, args.steps)
+    k0 = [torch.cuda.Event(enable_timing=True) for _ in range(L * n_chk)]
+    k1 = [torch.cuda.Event(enable_timing=True) for _ in range(L * n_chk)]
+    for i in range(n_chk):
+        for l in range(L):
+            kvx.kvx_push_layer_timed(plan, l, k0[i * L + l], k1[i * L + l], ready=ready[l], stream=side)
+    torch.cuda.synchronize()
+    kd = np.array([k0[j].elapsed_time(k1[j]) for j in range(L * n_chk)]) * 1e3  # us
+    log(f"push kernel: {k_avg_us:.2f} us per launch over the timed region; dispatch timestamps in a "
+        f"separate pass: avg {kd.mean():.2f} us (min {kd.min():.2f}, max {kd.max():.2f})")
+
+    # Secondary: the same step with fresh events (recorded on the compute
+    # stream right before each push, so each push enqueues a cross-stream wait).
+    def fresh_step():
+        for l in range(L):
+            ready[l].record(compute)
+            kvx.kvx_push_layer(plan, l, ready=ready[l], stream=side)
+    fresh_step()
+    with Timer(torch, side) as t:
+        for _ in range(args.steps):
+            fresh_step()
+    fresh_gbs = step_bytes * args.steps / (t.ms * 1e-3) / 1e9
+    log(f"with fresh per-layer events: {fresh_gbs:.1f} GB/s")
+
+    two_gbs = None
+    if args.two_stream:
+        two_gbs = two_stream_rate(torch, kvx, plan, ready, side, L, args.steps, step_bytes)
+        log(f"layers alternating over two side streams: {two_gbs:.1f} GB/s")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle as O
+        layers = list(range(min(32, L)))
+        src, dst = oracle_pools(wl, gs, gd, layers)
+        t0 = time.perf_counter()
+        oplan = O.make_plan(src.geom, dst.geom, [O.Request(n, s, d) for n, s, d in
+                                                 zip(tokens, wl.src_tables, wl.dst_tables)])
+        setup = time.perf_counter() - t0
+        cpu = cpu_baseline(f"oracle push (numpy copy of each triple) of {len(layers)} of {L} layers",
+                           lambda: O.push(src, dst, oplan), len(layers) * sum(oplan.bytes_per_layer()),
+                           args.cpu_seconds, setup)
+        log(f"cpu baseline: {cpu['value']} GB/s ({cpu['sample']})")
+
+    plan.close()
+    return {
+        "value": gbs, "ms_per_step": ms_per_step, "dtype": "u8",
+        "config": {"workload": wl.name, "layers": L, "kv_heads": wl.src.num_heads, "head_dim": wl.src.head_dim,
+                   "block_size": wl.src.block_size, "payload_dtype": wl.src.dtype, "layout": wl.src.layout,
+                   "prompt_tokens": wl.prompt_lens, "tokens_moved": tokens, "pool_blocks": wl.src.num_blocks,
+                   "merged_runs": nruns, "bytes_per_step": step_bytes,
+                   "step": f"{L} x kvx_push_layer on one side stream, each after its layer's (fired) event",
+                   "host_plan_ms": round(plan_ms, 3), "fresh_event_GBs": round(fresh_gbs, 1),
+                   "two_stream_GBs": None if two_gbs is None else round(two_gbs, 1)},
+        "roofline": roofline(rd + wr, k_avg_us, "kvx::copy_kernel<0> (kvx_push_layer)", args.workload,
+                             {"kernel_us_dispatch_stamps": round(float(kd.mean()), 3)}),
+        "cpu_baseline": cpu,
+    }
+
+
+def two_stream_rate(torch, kvx, plan, ready, side, L, steps, step_bytes):
     """The step with layers alternating between two side streams (already-
     fired events): one layer's drain overlaps the next layer's ramp-up.  Not
     part of the default run: the overlapping kernels would skew a kernel-trace
@@ -131,15 +289,11 @@ def two_stream_rate(kvx, torch, plan, ready, side, L, steps, step_bytes):
     return step_bytes * steps / (a.elapsed_time(b) * 1e-3) / 1e9
 
 
-CALIB_BYTES = 1 << 30
-
-
-def counters_run(torch, plan, side, L, step_bytes):
+def counters_run(torch, kvx, plan, side, L, bytes_per_launch):
     """Kernels for a counter pass: kvxb_copy of CALIB_BYTES (known traffic:
     CALIB_BYTES read + CALIB_BYTES written) three times, then two layerwise
     push steps."""
     from decode_kv_cache_amd import bench_support as B
-    from decode_kv_cache_amd import kvx
     buf = torch.empty(2 * CALIB_BYTES, dtype=torch.uint8, device="cuda")
     for _ in range(3):
         B.copy(buf[CALIB_BYTES:], buf[:CALIB_BYTES], CALIB_BYTES, stream=side)
@@ -148,7 +302,293 @@ def counters_run(torch, plan, side, L, step_bytes):
             kvx.kvx_push_layer(plan, l, stream=side)
     torch.cuda.synchronize()
     print(json.dumps({"counters_run": True, "calib_copy_bytes": CALIB_BYTES, "push_launches": 2 * L,
-                      "push_bytes_per_launch": step_bytes // L}), flush=True)
+                      "push_bytes_per_launch": bytes_per_launch}), flush=True)
+
+
+def bench_batched(args, torch, kvx, S, W):
+    """batched_push: 64 requests; layer l's push waits for a synthetic compute
+    kernel of layer l running on the compute stream (ALU-bound, one workgroup
+    per CU so that push workgroups co-reside; it writes a canary into layer l's
+    planned source blocks as its last act, so the push must see it)."""
+    from decode_kv_cache_amd import bench_support as B
+    wl = W.batched_push()
+    gs, gd = S.device_side(wl.src, wl.seed, 1), S.device_side(wl.dst, wl.seed, 2)
+    tokens = [kvx.kvx_tokens_to_move(p, 0) for p in wl.prompt_lens]
+    side = torch.cuda.Stream()
+    compute = torch.cuda.current_stream()
+    t0 = time.perf_counter()
+    plan = kvx.kvx_plan(gs.pool, gd.pool, tokens, wl.src_tables, wl.dst_tables, stream=side)
+    plan_ms = (time.perf_counter() - t0) * 1e3
+    rd, wr = plan.bytes_per_layer()
+    L = wl.src.num_layers
+    step_bytes = (rd + wr) * L
+    nruns = len(plan.runs())
+    log(f"plan: {nruns} runs for {sum(tokens)} tokens, {rd + wr} B per layer, host plan {plan_ms:.1f} ms")
+    bb = wl.src.block_size * wl.src.num_heads * wl.src.head_dim * wl.src.elem_bytes
+    used = np.concatenate([t[:-(-n // wl.src.block_size)] for t, n in zip(wl.src_tables, tokens)])
+    blocks = torch.from_numpy(used.astype(np.int32)).cuda()
+    grid = 256
+    sink = torch.empty(grid * 256, dtype=torch.float32, device="cuda")
+    ready = [torch.cuda.Event() for _ in range(L)]
+
+    def compute_layer(l, iters):
+        B.layer_compute(sink, iters, grid, gs.region(l, 0), gs.region(l, 1), blocks, bb, 0xC0DE0000 + l,
+                        stream=compute)
+
+    def push_only():
+        for l in range(L):
+            kvx.kvx_push_layer(plan, l, stream=side)
+
+    # push alone
+    push_only()
+    with Timer(torch, side) as t:
+        for _ in range(args.steps):
+            push_only()
+    t_p = t.ms / args.steps
+    # calibrate the compute kernel to about one layer's push time
+    probe = 20000
+    compute_layer(0, probe)
+    with Timer(torch, compute) as t:
+        compute_layer(0, probe)
+    iters = max(1000, int(probe * (t_p / L) / t.ms))
+
+    def compute_only():
+        for l in range(L):
+            compute_layer(l, iters)
+    compute_only()
+    with Timer(torch, compute) as t:
+        for _ in range(args.steps):
+            compute_only()
+    t_c = t.ms / args.steps
+
+    def both():
+        for l in range(L):
+            compute_layer(l, iters)
+            ready[l].record(compute)
+            kvx.kvx_push_layer(plan, l, ready=ready[l], stream=side)
+    both()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(compute)
+    for _ in range(args.steps):
+        both()
+    j = torch.cuda.Event()
+    j.record(side)
+    compute.wait_event(j)
+    b.record(compute)
+    torch.cuda.synchronize()
+    t_b = a.elapsed_time(b) / args.steps
+    # canary delivered: layer L-1's pushed destination holds its compute's canary
+    d0 = int(wl.dst_tables[0][0])
+    got = gd.region(L - 1, 0)[d0 * bb:d0 * bb + 4].cpu().numpy().view(np.uint32)[0]
+    canary_ok = bool(got == ((0xC0DE0000 + L - 1) & 0xFFFFFFFF))
+    gbs = step_bytes / (t_b * 1e-3) / 1e9
+    push_alone = step_bytes / (t_p * 1e-3) / 1e9
+    eff = (t_c + t_p - t_b) / min(t_c, t_p)
+    log(f"push alone {t_p:.2f} ms ({push_alone:.1f} GB/s), compute alone {t_c:.2f} ms, overlapped {t_b:.2f} ms "
+        f"-> {gbs:.1f} GB/s, overlap efficiency {eff:.2f}, canary {'ok' if canary_ok else 'MISSING'}")
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle as O
+        layers = [0, 1]
+        src, dst = oracle_pools(wl, gs, gd, layers)
+        t0 = time.perf_counter()
+        oplan = O.make_plan(src.geom, dst.geom, [O.Request(n, s, d) for n, s, d in
+                                                 zip(tokens, wl.src_tables, wl.dst_tables)])
+        setup = time.perf_counter() - t0
+        cpu = cpu_baseline(f"oracle push of {len(layers)} of {L} layers", lambda: O.push(src, dst, oplan),
+                           len(layers) * sum(oplan.bytes_per_layer()), args.cpu_seconds, setup)
+        log(f"cpu baseline: {cpu['value']} GB/s")
+    plan.close()
+    return {
+        "value": gbs, "ms_per_step": t_b, "dtype": "u8",
+        "config": {"workload": wl.name, "layers": L, "physical_layer_slabs": wl.src.n_phys,
+                   "kv_heads": wl.src.num_heads, "head_dim": wl.src.head_dim, "block_size": wl.src.block_size,
+                   "payload_dtype": wl.src.dtype, "requests": len(tokens), "tokens_moved_total": int(sum(tokens)),
+                   "pool_blocks": wl.src.num_blocks, "merged_runs": nruns, "bytes_per_step": step_bytes,
+                   "step": f"{L} x (synthetic compute of layer l on the compute stream, its event, "
+                           f"kvx_push_layer(l) on a side stream)",
+                   "push_alone_GBs": round(push_alone, 1), "push_alone_ms": round(t_p, 3),
+                   "compute_alone_ms": round(t_c, 3), "overlapped_ms": round(t_b, 3),
+                   "compute_iters": iters, "compute_grid": grid, "overlap_efficiency": round(eff, 3),
+                   "canary_delivered": canary_ok, "host_plan_ms": round(plan_ms, 2)},
+        "roofline": roofline(rd + wr, t_p * 1e3 / L, "kvx::copy_kernel<0> (kvx_push_layer)", wl.name,
+                             {"note": "push alone, span over its launches"}),
+        "cpu_baseline": cpu,
+    }
+
+
+def bench_tp4(args, torch, kvx, S, W):
+    """tp4_share: per layer, TP4 rank 0's 2-head slice NHD -> HND."""
+    wl = W.tp4_share()
+    gs, gd = S.device_side(wl.src, wl.seed, 1), S.device_side(wl.dst, wl.seed, 2)
+    tokens = [kvx.kvx_tokens_to_move(p, 0) for p in wl.prompt_lens]
+    side = torch.cuda.Stream()
+    plan = kvx.kvx_plan(gs.pool, gd.pool, tokens, wl.src_tables, wl.dst_tables, stream=side)
+    L = wl.src.num_layers
+    nh = wl.dst.num_heads
+    rank = wl.extra["tp_rank"]
+    row = wl.src.head_dim * wl.src.elem_bytes
+    per_layer = 2 * 2 * sum(tokens) * nh * row   # K and V, read + write
+    step_bytes = per_layer * L
+
+    def step():
+        for l in range(L):
+            kvx.kvx_copy_heads(plan, l, rank * nh, 0, nh, stream=side)
+    for _ in range(args.warmup):
+        step()
+    with Timer(torch, side) as t:
+        for _ in range(args.steps):
+            step()
+    ms = t.ms / args.steps
+    gbs = step_bytes / (ms * 1e-3) / 1e9
+    log(f"copy_heads: {ms * 1e3:.1f} us per step, {gbs:.1f} GB/s ({100 * gbs / HBM_PEAK_GBS:.1f}%)")
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle as O
+        layers = [0, 1, 2, 3]
+        src, dst = oracle_pools(wl, gs, gd, layers)
+        reqs = [O.Request(n, s, d) for n, s, d in zip(tokens, wl.src_tables, wl.dst_tables)]
+        t0 = time.perf_counter()
+        oplan = O.make_plan(src.geom, dst.geom, reqs)
+        setup = time.perf_counter() - t0
+
+        def one():
+            for l in range(len(layers)):
+                O.copy_heads(src, dst, oplan, reqs, l, rank * nh, 0, nh)
+        cpu = cpu_baseline(f"oracle copy_heads (numpy row gather/scatter) of {len(layers)} of {L} layers", one,
+                           len(layers) * per_layer, args.cpu_seconds, setup)
+        log(f"cpu baseline: {cpu['value']} GB/s")
+    plan.close()
+    return {
+        "value": gbs, "ms_per_step": ms, "dtype": "u8",
+        "config": {"workload": wl.name, "layers": L, "src": "NHD, 8 KV heads", "dst": f"HND, {nh} KV heads",
+                   "tp_rank": rank, "tp_size": wl.extra["tp_size"], "head_dim": wl.src.head_dim,
+                   "block_size": wl.src.block_size, "payload_dtype": wl.src.dtype, "requests": len(tokens),
+                   "tokens_moved": tokens[0], "bytes_per_step": step_bytes,
+                   "step": f"{L} x kvx_copy_heads(rank {rank} slice) on one stream"},
+        "roofline": roofline(per_layer, ms * 1e3 / L, "kvx::heads_kernel (kvx_copy_heads)", wl.name),
+        "cpu_baseline": cpu,
+    }
+
+
+def bench_multiturn(args, torch, kvx, S, W):
+    """multiturn_fp8: turns 2..8, each copies every session's retained prefix
+    (2048 (t-1) tokens, reused because it reaches the 512-token threshold)
+    from the decode pool back to the prefill pool, layer by layer."""
+    wl = W.multiturn_fp8()
+    ex = wl.extra
+    dec, pre = S.device_side(wl.src, wl.seed, 1), S.device_side(wl.dst, wl.seed, 2)
+    side = torch.cuda.Stream()
+    L = wl.src.num_layers
+    plans, step_bytes, plan_ms = [], 0, 0.0
+    for t in range(1, ex["turns"] + 1):
+        reusable = ex["growth"] * (t - 1)
+        if t == 1 or not kvx.kvx_should_reuse(reusable, ex["threshold"]):
+            continue
+        t0 = time.perf_counter()
+        p = kvx.kvx_plan(dec.pool, pre.pool, [reusable] * ex["sessions"], ex["decode_tables"],
+                         ex["prefill_tables"][t], stream=side)
+        plan_ms += (time.perf_counter() - t0) * 1e3
+        plans.append((t, p))
+        step_bytes += sum(p.bytes_per_layer()) * L
+
+    def step():
+        for _, p in plans:
+            for l in range(L):
+                kvx.kvx_push_layer(p, l, stream=side)
+    for _ in range(args.warmup):
+        step()
+    with Timer(torch, side) as t:
+        for _ in range(args.steps):
+            step()
+    ms = t.ms / args.steps
+    gbs = step_bytes / (ms * 1e-3) / 1e9
+    launches = len(plans) * L
+    log(f"multiturn: {ms:.2f} ms per step (turns {[t for t, _ in plans]}), {gbs:.1f} GB/s "
+        f"({100 * gbs / HBM_PEAK_GBS:.1f}%)")
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle as O
+        layers = [0]
+        src, dst = oracle_pools(wl, dec, pre, layers)
+        t_last = plans[-1][0]
+        t0 = time.perf_counter()
+        reqs = [O.reuse_request(t_last, ex["growth"], ex["threshold"], ex["decode_tables"][s],
+                                ex["prefill_tables"][t_last][s]) for s in range(ex["sessions"])]
+        oplan = O.make_plan(src.geom, dst.geom, reqs)
+        setup = time.perf_counter() - t0
+        cpu = cpu_baseline(f"oracle push (payload + scales) of turn {t_last}, {len(layers)} of {L} layers",
+                           lambda: O.push(src, dst, oplan), sum(oplan.bytes_per_layer()) * len(layers),
+                           args.cpu_seconds, setup)
+        log(f"cpu baseline: {cpu['value']} GB/s")
+    turns = [t for t, _ in plans]
+    for _, p in plans:
+        p.close()
+    return {
+        "value": gbs, "ms_per_step": ms, "dtype": "u8",
+        "config": {"workload": wl.name, "layers": L, "kv_heads": wl.src.num_heads, "head_dim": wl.src.head_dim,
+                   "block_size": wl.src.block_size, "payload_dtype": wl.src.dtype, "scales": "fp32 per block",
+                   "sessions": ex["sessions"], "turns_copied": turns, "threshold_tokens": ex["threshold"],
+                   "bytes_per_step": step_bytes,
+                   "step": f"turns 2..8: {L} x kvx_push_layer (decode -> prefill) per turn",
+                   "host_plan_ms_all_turns": round(plan_ms, 2)},
+        "roofline": roofline(step_bytes // launches, ms * 1e3 / launches, "kvx::copy_kernel<0> (kvx_push_layer)",
+                             wl.name, {"note": "average over the turns' launches (sizes grow with the turn)"}),
+        "cpu_baseline": cpu,
+    }
+
+
+def bench_pack(args, torch, kvx, S, W):
+    """pack_unpack: the default workload's 64 layers gathered into a staging
+    buffer and scattered from it into the consumer pool."""
+    wl = W.qwen32b_push()
+    gs, gd = S.device_side(wl.src, wl.seed, 1), S.device_side(wl.dst, wl.seed, 2)
+    tokens = [kvx.kvx_tokens_to_move(p, 0) for p in wl.prompt_lens]
+    side = torch.cuda.Stream()
+    plan = kvx.kvx_plan(gs.pool, gd.pool, tokens, wl.src_tables, wl.dst_tables, stream=side)
+    L = wl.src.num_layers
+    nbytes = kvx.kvx_staging_bytes(plan, 0, L)
+    stg = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    step_bytes = 4 * nbytes  # pack reads + writes nbytes, unpack reads + writes nbytes
+
+    def step():
+        kvx.kvx_pack(plan, 0, L, stg, stream=side)
+        kvx.kvx_unpack(plan, 0, L, stg, stream=side)
+    for _ in range(args.warmup):
+        step()
+    with Timer(torch, side) as t:
+        for _ in range(args.steps):
+            step()
+    ms = t.ms / args.steps
+    gbs = step_bytes / (ms * 1e-3) / 1e9
+    log(f"pack+unpack: {ms * 1e3:.1f} us per step for {nbytes} staged bytes, {gbs:.1f} GB/s")
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle as O
+        layers = list(range(8))
+        src, dst = oracle_pools(wl, gs, gd, layers)
+        t0 = time.perf_counter()
+        oplan = O.make_plan(src.geom, dst.geom, [O.Request(n, s, d) for n, s, d in
+                                                 zip(tokens, wl.src_tables, wl.dst_tables)])
+        setup = time.perf_counter() - t0
+
+        def one():
+            O.unpack(O.pack(src, oplan, 0, len(layers)), dst, oplan, 0, len(layers))
+        cpu = cpu_baseline(f"oracle pack + unpack of {len(layers)} of {L} layers", one,
+                           4 * O.staging_bytes(oplan, 0, len(layers)), args.cpu_seconds, setup)
+        log(f"cpu baseline: {cpu['value']} GB/s")
+    plan.close()
+    launches = 2 * L
+    return {
+        "value": gbs, "ms_per_step": ms, "dtype": "u8",
+        "config": {"workload": "pack_unpack", "geometry": "qwen32b_push", "layers": L, "staging_bytes": nbytes,
+                   "bytes_per_step": step_bytes,
+                   "step": f"kvx_pack of {L} layers then kvx_unpack of {L} layers ({launches} launches)"},
+        "roofline": roofline(step_bytes // launches, ms * 1e3 / launches,
+                             "kvx::copy_kernel<1>/<2> (kvx_pack / kvx_unpack)", "pack_unpack"),
+        "cpu_baseline": cpu,
+    }
 
 
 def main():
@@ -156,7 +596,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="qwen32b_push", choices=["qwen32b_push", "tiny_push"])
+    ap.add_argument("--workload", default="qwen32b_push", choices=WORKLOAD_NAMES)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--counters", action="store_true",
@@ -166,7 +606,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
-              f"(the transfer shards per request/layer/head slice, see the design notes)", file=sys.stderr)
+              f"(the transfer shards per request, layer and head slice; see the design notes)", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -179,140 +619,23 @@ def main():
         sys.exit(1)
     dev = torch.cuda.get_device_properties(0)
     log(f"device: {dev.name} {getattr(dev, 'gcnArchName', '')} CUs={dev.multi_processor_count} "
-        f"mem={dev.total_memory / 2**30:.0f} GiB")
-
-    wl = W.WORKLOADS[args.workload]()
-    log(f"workload {wl.name}: pools {wl.src.pool_bytes / 2**30:.1f} + {wl.dst.pool_bytes / 2**30:.1f} GiB")
-    t0 = time.perf_counter()
-    gs = S.device_side(wl.src, wl.seed, 1)
-    gd = S.device_side(wl.dst, wl.seed, 2)
-    torch.cuda.synchronize()
-    log(f"pools filled in {time.perf_counter() - t0:.1f} s")
-
-    tokens = [kvx.kvx_tokens_to_move(p, 0) for p in wl.prompt_lens]
-    side = torch.cuda.Stream()
-    compute = torch.cuda.current_stream()
-    t0 = time.perf_counter()
-    plan = kvx.kvx_plan(gs.pool, gd.pool, tokens, wl.src_tables, wl.dst_tables, stream=side)
-    plan_ms = (time.perf_counter() - t0) * 1e3
-    rd, wr = plan.bytes_per_layer()
-    L = wl.src.num_layers
-    step_bytes = (rd + wr) * L
-    nruns = len(plan.runs())
-    log(f"plan: {nruns} runs, {len(plan.triples())} triples/region, {rd + wr} B per layer, "
-        f"{step_bytes} B per step, host plan {plan_ms:.2f} ms")
-
-    if args.counters:
-        counters_run(torch, plan, side, L, step_bytes)
-        plan.close()
+        f"mem={dev.total_memory / 2**30:.0f} GiB; workload {args.workload}")
+    fn = {"qwen32b_push": bench_push, "tiny_push": bench_push, "batched_push": bench_batched,
+          "tp4_share": bench_tp4, "multiturn_fp8": bench_multiturn, "pack_unpack": bench_pack}[args.workload]
+    if args.counters and fn is not bench_push:
+        print("bench.py: --counters is for the push workloads", file=sys.stderr)
+        sys.exit(2)
+    r = fn(args, torch, kvx, S, W)
+    if r is None:
         return
-
-    # One ready event per layer, recorded on the compute stream.  The headline
-    # step uses events that have already fired (the layer's compute is done):
-    # kvx_push_layer then enqueues no wait and the side stream holds nothing
-    # but the 64 push kernels, so the per-step span over 64 launches is the
-    # push kernel's average launch duration.
-    ready = [torch.cuda.Event() for _ in range(L)]
-    for e in ready:
-        e.record(compute)
-    torch.cuda.synchronize()
-
-    def step():
-        for l in range(L):
-            kvx.kvx_push_layer(plan, l, ready=ready[l], stream=side)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
-    wall0 = time.perf_counter()
-    marks[0].record(side)
-    for i in range(args.steps):
-        step()
-        marks[i + 1].record(side)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    per_step = np.array([marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps)])  # ms
-    span_ms = marks[0].elapsed_time(marks[-1])
-    ms_per_step = span_ms / args.steps
-    gbs = step_bytes * args.steps / (span_ms * 1e-3) / 1e9
-    log(f"span {span_ms:.3f} ms for {args.steps} steps ({ms_per_step * 1e3:.1f} us/step, "
-        f"min {per_step.min() * 1e3:.1f}, max {per_step.max() * 1e3:.1f}), wall {wall * 1e3:.1f} ms, "
-        f"{gbs:.1f} GB/s = {100 * gbs / HBM_PEAK_GBS:.1f}% of {HBM_PEAK_GBS:.0f} GB/s")
-
-    # The side stream carries nothing but the push kernels, back to back (a
-    # kernel trace shows no gaps between them), so the timed region's span
-    # over its launches is the push kernel's average launch duration.
-    k_avg_us = ms_per_step * 1e3 / L
-
-    # Cross-check in a separate short pass: every push kernel records its own
-    # start/end timestamps (from the dispatch packet).  Such launches are
-    # spaced out on the queue, so this pass is not used for throughput.
-    n_chk = min(3, args.steps)
-    k0 = [torch.cuda.Event(enable_timing=True) for _ in range(L * n_chk)]
-    k1 = [torch.cuda.Event(enable_timing=True) for _ in range(L * n_chk)]
-    for i in range(n_chk):
-        for l in range(L):
-            kvx.kvx_push_layer_timed(plan, l, k0[i * L + l], k1[i * L + l], ready=ready[l], stream=side)
-    torch.cuda.synchronize()
-    kd = np.array([k0[j].elapsed_time(k1[j]) for j in range(L * n_chk)]) * 1e3  # us
-    log(f"push kernel: {k_avg_us:.2f} us per launch over the timed region; dispatch timestamps in a "
-        f"separate pass: avg {kd.mean():.2f} us (min {kd.min():.2f}, max {kd.max():.2f})")
-    per_launch = rd + wr
-    ach = per_launch / (k_avg_us * 1e-6) / 1e9
-    traffic = counter_traffic(args.workload)
-    roofline = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "kernel": "kvx::copy_kernel<0> (kvx_push_layer)", "avg_launch_us": round(k_avg_us, 3),
-                "kernel_us_dispatch_stamps": round(float(kd.mean()), 3),
-                "algorithmic_bytes_per_launch": per_launch}
-    log(f"push kernel: avg {k_avg_us:.2f} us per launch -> {ach:.1f} GB/s")
-
-    # Secondary: the same step with fresh events (recorded on the compute
-    # stream right before each push, so each push enqueues a cross-stream wait).
-    def fresh_step():
-        for l in range(L):
-            ready[l].record(compute)
-            kvx.kvx_push_layer(plan, l, ready=ready[l], stream=side)
-    fresh_step()
-    torch.cuda.synchronize()
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record(side)
-    for _ in range(args.steps):
-        fresh_step()
-    b.record(side)
-    torch.cuda.synchronize()
-    fresh_gbs = step_bytes * args.steps / (a.elapsed_time(b) * 1e-3) / 1e9
-    log(f"with fresh per-layer events: {fresh_gbs:.1f} GB/s")
-
-    two_gbs = None
-    if args.two_stream:
-        two_gbs = two_stream_rate(kvx, torch, plan, ready, side, L, args.steps, step_bytes)
-        log(f"layers alternating over two side streams: {two_gbs:.1f} GB/s")
-
-    cpu = None
-    if not args.no_cpu_baseline:
-        log("cpu baseline ...")
-        cpu = cpu_baseline_push(wl, gs, gd, tokens, args.cpu_seconds)
-        log(f"cpu baseline: {cpu['value']} GB/s ({cpu['sample']})")
-
     out = {
-        "metric": METRIC, "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "u8", "data": "synthetic",
-        "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
-        "config": {"workload": wl.name, "layers": L, "kv_heads": wl.src.num_heads, "head_dim": wl.src.head_dim,
-                   "block_size": wl.src.block_size, "payload_dtype": wl.src.dtype, "layout": wl.src.layout,
-                   "prompt_tokens": wl.prompt_lens, "tokens_moved": tokens, "pool_blocks": wl.src.num_blocks,
-                   "merged_runs": nruns, "bytes_per_step": step_bytes,
-                   "step": f"{L} x (ready event on compute stream + kvx_push_layer on side stream)",
-                   "host_plan_ms": round(plan_ms, 3),
-                   "fresh_event_GBs": round(fresh_gbs, 1), "two_stream_GBs": None if two_gbs is None else round(two_gbs, 1)},
-        "roofline": roofline,
-        "cpu_baseline": cpu,
+        "metric": METRIC, "value": round(r["value"], 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(r["ms_per_step"], 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": r["dtype"], "data": "synthetic",
+        "pct_of_hbm_peak": round(100 * r["value"] / HBM_PEAK_GBS, 2),
+        "config": r["config"], "roofline": r["roofline"], "cpu_baseline": r["cpu_baseline"],
     }
     print(json.dumps(out), flush=True)
-    plan.close()
 
 
 if __name__ == "__main__":
