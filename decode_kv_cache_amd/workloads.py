@@ -266,8 +266,8 @@ def fill_pool(spec: PoolSpec, kv, sc, seed: int, pool_tag: int, dtype: Optional[
 
 
 def random_case(seed: int, *, layout="NHD", dst_layout=None, elem_bytes=2, num_layers=2,
-                num_blocks=24, dst_blocks=None, block_size=4, num_heads=3, dst_heads=None,
-                head_dim=8, has_scales=False, num_requests=3, max_tokens=30,
+                num_blocks=24, dst_blocks=None, block_size=4, dst_block_size=None, num_heads=3,
+                dst_heads=None, head_dim=8, has_scales=False, num_requests=3, max_tokens=30,
                 run_mean=2.0, extra_ids=1):
     """Small random case for brute-force checks: random prompt lengths (0 and
     exact block multiples included by chance), block tables of geometric runs
@@ -276,15 +276,16 @@ def random_case(seed: int, *, layout="NHD", dst_layout=None, elem_bytes=2, num_l
     rng = np.random.Generator(np.random.PCG64(seed))
     dtype = BF16 if elem_bytes == 2 else U8
     src = PoolSpec(num_layers, num_blocks, block_size, num_heads, head_dim, dtype, layout, has_scales)
-    dst = PoolSpec(num_layers, dst_blocks or num_blocks, block_size, dst_heads or num_heads, head_dim,
-                   dtype, dst_layout or layout, has_scales)
+    dst = PoolSpec(num_layers, dst_blocks or num_blocks, dst_block_size or block_size, dst_heads or num_heads,
+                   head_dim, dtype, dst_layout or layout, has_scales)
     plen = [int(x) for x in rng.integers(0, max_tokens + 1, size=num_requests)]
-    need = [alloc_blocks(x, block_size) + extra_ids for x in plen]
+    need_s = [alloc_blocks(x, src.block_size) + extra_ids for x in plen]
+    need_d = [alloc_blocks(x, dst.block_size) + extra_ids for x in plen]
     st = geometric_run_table(rng, src.num_blocks, run_mean)
     dt = geometric_run_table(rng, dst.num_blocks, run_mean)
-    if sum(need) > min(len(st), len(dt)):
+    if sum(need_s) > len(st) or sum(need_d) > len(dt):
         raise ValueError("pools too small for this case")
-    return Workload(f"random_{seed}", seed, src, dst, plen, split_tables(st, need), split_tables(dt, need))
+    return Workload(f"random_{seed}", seed, src, dst, plen, split_tables(st, need_s), split_tables(dt, need_d))
 
 
 def host_values(spec: PoolSpec, seed: int, pool_tag: int):

@@ -11,4 +11,5 @@ from .kv_oracle import (  # noqa: F401
     head_rows, last_block_fill, make_plan, pack, plan_runs, push, push_plain,
     push_region, push_scales, reusable_prefix, reuse_request, should_reuse,
     staging_bytes, staging_region_bytes, tokens_to_move, triples, unpack, validate,
+    Segment, token_segments, triples_reblock,
 )

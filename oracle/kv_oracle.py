@@ -161,26 +161,40 @@ def last_block_fill(num_tokens: int, block_size: int) -> int:
 # Validation shared by both formulations.
 # ---------------------------------------------------------------------------
 def _check_same_push_geometry(gs: Geometry, gd: Geometry) -> None:
-    for f in ("num_layers", "block_size", "num_heads", "head_dim", "elem_bytes", "layout", "has_scales"):
+    for f in ("num_layers", "num_heads", "head_dim", "elem_bytes", "layout", "has_scales"):
         if getattr(gs, f) != getattr(gd, f):
             raise OracleError("MISMATCH", f"{f} differs: {getattr(gs, f)} vs {getattr(gd, f)}")
+    _check_block_sizes(gs, gd)
 
 
-def validate(requests: Sequence[Request], block_size: int, src_blocks: int, dst_blocks: int) -> None:
+def _check_block_sizes(gs: Geometry, gd: Geometry) -> None:
+    """Block sizes may differ per side ([PUSH] "Implementierungsdetails" step
+    3: each side maps block positions onto its own layout).  A per-block scale
+    then has no single source block, so scales need equal block sizes."""
+    if gs.block_size != gd.block_size and (gs.has_scales or gd.has_scales):
+        raise OracleError("UNSUPPORTED", "per-block scales need equal block sizes")
+
+
+def validate(requests: Sequence[Request], block_size: int, src_blocks: int, dst_blocks: int,
+             dst_block_size: Optional[int] = None) -> None:
     """Error classes of the transfer (argument errors, IDs out of range,
     destination used twice).  Only the first ceil(n/BS) IDs of each list are
-    looked at."""
+    looked at, BS being that side's block size."""
+    bsd = block_size if dst_block_size is None else dst_block_size
     used_dst = set()
     for r, req in enumerate(requests):
         if req.num_tokens < 0:
             raise OracleError("INVAL", f"request {r}: negative token count")
-        nb = blocks_in_use(req.num_tokens, block_size)
-        if len(req.src_ids) < nb or len(req.dst_ids) < nb:
-            raise OracleError("INVAL", f"request {r}: block list shorter than {nb}")
-        for i in range(nb):
-            s, d = int(req.src_ids[i]), int(req.dst_ids[i])
+        nbs = blocks_in_use(req.num_tokens, block_size)
+        nbd = blocks_in_use(req.num_tokens, bsd)
+        if len(req.src_ids) < nbs or len(req.dst_ids) < nbd:
+            raise OracleError("INVAL", f"request {r}: block list shorter than needed")
+        for i in range(nbs):
+            s = int(req.src_ids[i])
             if not 0 <= s < src_blocks:
                 raise OracleError("RANGE", f"request {r}: src block {s} outside pool")
+        for i in range(nbd):
+            d = int(req.dst_ids[i])
             if not 0 <= d < dst_blocks:
                 raise OracleError("RANGE", f"request {r}: dst block {d} outside pool")
             if d in used_dst:
@@ -198,7 +212,6 @@ def push_plain(src: Pool, dst: Pool, requests: Sequence[Request],
                layers: Optional[Sequence[int]] = None) -> None:
     gs, gd = src.geom, dst.geom
     _check_same_push_geometry(gs, gd)
-    validate(requests, gs.block_size, gs.num_blocks, gd.num_blocks)
     copy_heads_plain(src, dst, requests, 0, 0, gs.num_heads, layers)
 
 
@@ -212,18 +225,19 @@ def copy_heads_plain(src: Pool, dst: Pool, requests: Sequence[Request],
     side maps blocks onto its own layout); [MORI] §6 (rank mapping under TP)."""
     gs, gd = src.geom, dst.geom
     _check_head_slice(gs, gd, src_head0, dst_head0, num_heads)
-    validate(requests, gs.block_size, gs.num_blocks, gd.num_blocks)
-    bs = gs.block_size
+    validate(requests, gs.block_size, gs.num_blocks, gd.num_blocks, gd.block_size)
+    bs, bsd = gs.block_size, gd.block_size
     row = gs.row_bytes
     lay = range(gs.num_layers) if layers is None else layers
     for req in requests:
         n = req.num_tokens
         for p in range(n):
             j, s = divmod(p, bs)
-            sb, db = int(req.src_ids[j]), int(req.dst_ids[j])
+            jd, sd = divmod(p, bsd)
+            sb, db = int(req.src_ids[j]), int(req.dst_ids[jd])
             for h in range(src_head0, src_head0 + num_heads):
                 so = gs.row_offset(sb, s, h)
-                do = gd.row_offset(db, s, h - src_head0 + dst_head0)
+                do = gd.row_offset(db, sd, h - src_head0 + dst_head0)
                 for l in lay:
                     for kv in (K, V):
                         dst.kv[l, kv, do:do + row] = src.kv[l, kv, so:so + row]
@@ -236,9 +250,10 @@ def copy_heads_plain(src: Pool, dst: Pool, requests: Sequence[Request],
 
 
 def _check_head_slice(gs: Geometry, gd: Geometry, s0: int, d0: int, nh: int) -> None:
-    for f in ("num_layers", "block_size", "head_dim", "elem_bytes", "has_scales"):
+    for f in ("num_layers", "head_dim", "elem_bytes", "has_scales"):
         if getattr(gs, f) != getattr(gd, f):
             raise OracleError("MISMATCH", f"{f} differs")
+    _check_block_sizes(gs, gd)
     if nh < 0 or s0 < 0 or d0 < 0:
         raise OracleError("INVAL", "negative head index or count")
     if s0 + nh > gs.num_heads or d0 + nh > gd.num_heads:
@@ -362,11 +377,92 @@ class Plan:
 
 
 def make_plan(src_geom: Geometry, dst_geom: Geometry, requests: Sequence[Request]) -> Plan:
-    runs = plan_runs(requests, src_geom.block_size, src_geom.num_blocks, dst_geom.num_blocks)
     same = all(getattr(src_geom, f) == getattr(dst_geom, f) for f in
-               ("num_layers", "block_size", "num_heads", "head_dim", "elem_bytes", "layout", "has_scales"))
-    tr = triples(runs, src_geom) if same else []
-    return Plan(src_geom, dst_geom, runs, tr, block_pairs(runs))
+               ("num_layers", "num_heads", "head_dim", "elem_bytes", "layout", "has_scales"))
+    if src_geom.block_size == dst_geom.block_size:
+        runs = plan_runs(requests, src_geom.block_size, src_geom.num_blocks, dst_geom.num_blocks)
+        tr = triples(runs, src_geom) if same else []
+        return Plan(src_geom, dst_geom, runs, tr, block_pairs(runs))
+    _check_block_sizes(src_geom, dst_geom)
+    validate(requests, src_geom.block_size, src_geom.num_blocks, dst_geom.num_blocks, dst_geom.block_size)
+    segs = token_segments(requests, src_geom.block_size, dst_geom.block_size)
+    tr = triples_reblock(segs, src_geom, dst_geom) if same else []
+    return Plan(src_geom, dst_geom, [], tr, [])
+
+
+# ---------------------------------------------------------------------------
+# Different block sizes per side ([PUSH] "Implementierungsdetails" step 3:
+# each side maps the block positions onto its own physical layout, which
+# allows different block sizes).  Token p of a request sits in source block
+# src_ids[p // BS_src], slot p % BS_src and lands in destination block
+# dst_ids[p // BS_dst], slot p % BS_dst.  The merge then works on tokens:
+# a segment is a maximal token range whose source positions and destination
+# positions both advance without a jump (within a block, or into the block
+# with the next ID).
+# ---------------------------------------------------------------------------
+@dataclass(frozen=True)
+class Segment:
+    src_block: int
+    src_slot: int
+    dst_block: int
+    dst_slot: int
+    ntok: int
+
+
+def token_segments(requests: Sequence[Request], bs_src: int, bs_dst: int) -> List[Segment]:
+    out: List[Segment] = []
+    for req in requests:
+        n = req.num_tokens
+        p = 0
+        while p < n:
+            start = p
+            p += 1
+            while p < n:
+                src_ok = p % bs_src != 0 or int(req.src_ids[p // bs_src]) == int(req.src_ids[p // bs_src - 1]) + 1
+                dst_ok = p % bs_dst != 0 or int(req.dst_ids[p // bs_dst]) == int(req.dst_ids[p // bs_dst - 1]) + 1
+                if not (src_ok and dst_ok):
+                    break
+                p += 1
+            out.append(Segment(int(req.src_ids[start // bs_src]), start % bs_src,
+                               int(req.dst_ids[start // bs_dst]), start % bs_dst, p - start))
+    return out
+
+
+def _split_in_blocks(seg: Segment, bs_src: int, bs_dst: int):
+    """Pieces of a segment that stay inside one source and one destination
+    block: (src block, src slot, dst block, dst slot, tokens)."""
+    sb, ss, db, ds, left = seg.src_block, seg.src_slot, seg.dst_block, seg.dst_slot, seg.ntok
+    while left > 0:
+        k = min(left, bs_src - ss, bs_dst - ds)
+        yield sb, ss, db, ds, k
+        left -= k
+        ss += k
+        ds += k
+        if ss == bs_src:
+            sb, ss = sb + 1, 0
+        if ds == bs_dst:
+            db, ds = db + 1, 0
+
+
+def triples_reblock(segs: Sequence[Segment], gs: Geometry, gd: Geometry) -> List[Tuple[int, int, int]]:
+    """Per-region (src offset, dst offset, length) list for different block
+    sizes, same head count and layout: each token segment's rows per block
+    pair (per head in HND), neighbours merged where both sides continue."""
+    out: List[List[int]] = []
+
+    def emit(so, do, ln):
+        if out and out[-1][0] + out[-1][2] == so and out[-1][1] + out[-1][2] == do:
+            out[-1][2] += ln
+        else:
+            out.append([so, do, ln])
+    for seg in segs:
+        for sb, ss, db, ds, k in _split_in_blocks(seg, gs.block_size, gd.block_size):
+            if gs.layout == NHD:
+                emit(gs.row_offset(sb, ss, 0), gd.row_offset(db, ds, 0), k * gs.token_bytes)
+            else:
+                for h in range(gs.num_heads):
+                    emit(gs.row_offset(sb, ss, h), gd.row_offset(db, ds, h), k * gs.row_bytes)
+    return [tuple(t) for t in out]
 
 
 def push_region(src_region: np.ndarray, dst_region: np.ndarray,
@@ -464,20 +560,20 @@ def head_rows(plan: Plan, src_head0: int, dst_head0: int, num_heads: int,
               requests: Sequence[Request]) -> Tuple[np.ndarray, np.ndarray]:
     """Row indices (source, destination) of every moved (token, head)."""
     gs, gd = plan.src_geom, plan.dst_geom
-    sb, db, sl = [], [], []
+    sb, db, sl, dl = [], [], [], []
     for req in requests:
         n = req.num_tokens
         p = np.arange(n, dtype=np.int64)
-        j, s = p // gs.block_size, p % gs.block_size
-        sb.append(np.asarray(req.src_ids, np.int64)[j])
-        db.append(np.asarray(req.dst_ids, np.int64)[j])
-        sl.append(s)
+        sb.append(np.asarray(req.src_ids, np.int64)[p // gs.block_size])
+        db.append(np.asarray(req.dst_ids, np.int64)[p // gd.block_size])
+        sl.append(p % gs.block_size)
+        dl.append(p % gd.block_size)
     if not sb:
         return np.zeros(0, np.int64), np.zeros(0, np.int64)
-    sb, db, sl = np.concatenate(sb), np.concatenate(db), np.concatenate(sl)
+    sb, db, sl, dl = np.concatenate(sb), np.concatenate(db), np.concatenate(sl), np.concatenate(dl)
     h = np.arange(num_heads, dtype=np.int64)
     src_rows = _row_index(gs, sb[:, None], sl[:, None], (src_head0 + h)[None, :]).ravel()
-    dst_rows = _row_index(gd, db[:, None], sl[:, None], (dst_head0 + h)[None, :]).ravel()
+    dst_rows = _row_index(gd, db[:, None], dl[:, None], (dst_head0 + h)[None, :]).ravel()
     return src_rows, dst_rows
 
 

@@ -467,7 +467,117 @@ def pin_errors(O):
         assert e.kind == "MISMATCH"
 
 
+def reblock_cases(count=30, seed0=41):
+    rng = np.random.Generator(np.random.PCG64(seed0))
+    for i in range(count):
+        bs, bsd = [int(x) for x in rng.choice([1, 2, 3, 4, 8, 16], size=2, replace=False)]
+        yield W.random_case(
+            3000 + seed0 + i, layout=["NHD", "HND"][i % 2], elem_bytes=int(rng.choice([1, 2])),
+            num_layers=int(rng.integers(1, 3)), num_blocks=160, block_size=bs, dst_block_size=bsd,
+            num_heads=int(rng.integers(1, 4)), head_dim=int(rng.choice([4, 8])),
+            num_requests=int(rng.integers(1, 4)), max_tokens=40, run_mean=float(rng.choice([1.5, 4.0])),
+            extra_ids=int(rng.integers(0, 2)))
+
+
+def pin_reblock_brute_vs_procedure(O):
+    """Different block sizes per side: the plain per-token definition equals
+    the token-segment procedure, byte for byte; pack/unpack round-trips."""
+    for wl in reblock_cases():
+        src, dst = pools(O, wl)
+        reqs = requests_for(O, wl)
+        a, b, c = dst.copy(), dst.copy(), dst.copy()
+        O.push_plain(src, a, reqs)
+        plan = O.make_plan(src.geom, dst.geom, reqs)
+        O.push(src, b, plan)
+        assert np.array_equal(a.kv, b.kv), wl.name
+        L = src.geom.num_layers
+        O.unpack(O.pack(src, plan, 0, L), c, plan, 0, L)
+        assert np.array_equal(c.kv, b.kv), wl.name
+        assert plan.payload_bytes == sum(r.num_tokens for r in reqs) * src.geom.token_bytes
+
+
+def pin_reblock_equal_sizes_agree(O):
+    """With equal block sizes the token-segment procedure gives exactly the
+    run-based triple list."""
+    for wl in random_cases(24, seed0=51):
+        g = geom(O, wl.src)
+        reqs = requests_for(O, wl)
+        runs = O.plan_runs(reqs, g.block_size, g.num_blocks, wl.dst.num_blocks)
+        segs = O.token_segments(reqs, g.block_size, g.block_size)
+        assert O.triples_reblock(segs, g, g) == O.triples(runs, g), wl.name
+
+
+def pin_reblock_torch_pairs(O):
+    """NHD, destination blocks twice the source size, each destination block
+    filled by two source blocks: equals torch index_select of source block
+    pairs viewed as one destination block."""
+    src_spec = W.PoolSpec(2, 40, 4, 2, 8, W.BF16)
+    dst_spec = W.PoolSpec(2, 30, 8, 2, 8, W.BF16)
+    rng = np.random.Generator(np.random.PCG64(9))
+    st = rng.permutation(40)[:12].astype(np.int32)
+    dt = rng.permutation(30)[:6].astype(np.int32)
+    wl = W.Workload("pairs", 21, src_spec, dst_spec, [48], [st], [dt])
+    src, dst = pools(O, wl)
+    got = dst.copy()
+    reqs = requests_for(O, wl, [48])
+    O.push(src, got, O.make_plan(src.geom, dst.geom, reqs))
+    exp = torch.from_numpy(dst.kv.copy())
+    s = torch.from_numpy(src.kv)
+    for l in range(2):
+        for kv in range(2):
+            blk = s[l, kv].view(40, -1).index_select(0, torch.from_numpy(st.astype(np.int64)))
+            exp[l, kv].view(30, -1).index_copy_(0, torch.from_numpy(dt.astype(np.int64)), blk.reshape(6, -1))
+    assert np.array_equal(got.kv, exp.numpy())
+
+
+def pin_reblock_round_trip(O):
+    """16-slot blocks -> 6-slot blocks -> 16-slot blocks restores every moved
+    token row, both layouts."""
+    for layout in ("NHD", "HND"):
+        a_spec = W.PoolSpec(1, 20, 16, 2, 8, W.U8, layout)
+        b_spec = W.PoolSpec(1, 60, 6, 2, 8, W.U8, layout)
+        rng = np.random.Generator(np.random.PCG64(33))
+        n = 70
+        at = rng.permutation(20)[:5].astype(np.int32)
+        bt = rng.permutation(60)[:12].astype(np.int32)
+        wl = W.Workload("rt", 5, a_spec, b_spec, [n + 1], [at], [bt])
+        a, b = pools(O, wl)
+        reqs = [O.Request(n, at, bt)]
+        O.push(a, b, O.make_plan(a.geom, b.geom, reqs))
+        back = O.Pool(a.geom, np.zeros_like(a.kv), None)
+        rev = [O.Request(n, bt, at)]
+        O.push(b, back, O.make_plan(b.geom, a.geom, rev))
+        g = a.geom
+        for p in range(n):
+            j, sl = divmod(p, 16)
+            for h in range(2):
+                o = g.row_offset(int(at[j]), sl, h)
+                assert np.array_equal(back.kv[0, :, o:o + g.row_bytes], a.kv[0, :, o:o + g.row_bytes])
+
+
+def pin_reblock_errors(O):
+    """Scales need equal block sizes; each side's list must cover its own
+    block count."""
+    gs = O.Geometry(1, 8, 4, 1, 4, 1, "NHD", True)
+    gd = O.Geometry(1, 8, 8, 1, 4, 1, "NHD", True)
+    try:
+        O.make_plan(gs, gd, [O.Request(8, [0, 1], [2])])
+        raise AssertionError("scales with different block sizes accepted")
+    except O.OracleError as e:
+        assert e.kind == "UNSUPPORTED"
+    gs = O.Geometry(1, 8, 4, 1, 4, 1, "NHD")
+    gd = O.Geometry(1, 8, 8, 1, 4, 1, "NHD")
+    assert len(O.make_plan(gs, gd, [O.Request(8, [0, 1], [2])]).triples) >= 1
+    for bad in ([O.Request(9, [0, 1], [2, 3])], [O.Request(9, [0, 1, 2], [2])]):
+        try:
+            O.make_plan(gs, gd, bad)
+            raise AssertionError("short list accepted")
+        except O.OracleError as e:
+            assert e.kind == "INVAL"
+
+
 ALL_PINS = [pin_brute_vs_procedure, pin_full_blocks_index_copy, pin_single_run_slice,
             pin_nhd_to_hnd_permute, pin_final_token_never_sent, pin_untouched_bytes,
             pin_plan_invariants, pin_closed_forms, pin_threshold, pin_pack_unpack,
-            pin_copy_heads, pin_errors]
+            pin_copy_heads, pin_errors, pin_reblock_brute_vs_procedure, pin_reblock_equal_sizes_agree,
+            pin_reblock_torch_pairs, pin_reblock_round_trip, pin_reblock_errors]

@@ -161,10 +161,20 @@ def m_dupdst_allowed(O):
     O.validate = validate
 
 
+def m_reblock_dst_uses_src_size(O):
+    orig = O.token_segments
+    O.token_segments = lambda requests, bs_src, bs_dst: orig(requests, bs_src, bs_src)
+
+
+def m_reblock_no_split(O):
+    O._split_in_blocks = lambda seg, bs_src, bs_dst: iter([(seg.src_block, seg.src_slot, seg.dst_block,
+                                                           seg.dst_slot, seg.ntok)])
+
+
 MUTATIONS = [m_no_minus_one, m_minus_two, m_merge_src_only, m_hnd_swap, m_tail_ignored,
              m_tail_off_by_one, m_coalesce_src_only, m_scale_swap, m_reuse_strict, m_reuse_turn,
              m_nhd_row_swap, m_pack_kv_order, m_scale_pad_garbage, m_hnd_tail_one_segment,
-             m_dupdst_allowed]
+             m_dupdst_allowed, m_reblock_dst_uses_src_size, m_reblock_no_split]
 
 
 @pytest.mark.parametrize("mutation", MUTATIONS, ids=lambda f: f.__name__)
