@@ -17,6 +17,7 @@ Other workloads (--workload), one JSON line each:
   multiturn_fp8  fp8 KV + fp32 per-block scales, 32 sessions, turns 2..8 copy
                  the decode side's retained prefix back to the prefill pool
   pack_unpack    the default workload through a contiguous staging buffer
+  qwen32b_reblock  the default KV with 64-slot consumer blocks (16-slot producer)
   tiny_push      2 layers, one 200-token prompt (launch-bound; no claim)
 
 Prints ONE JSON line on stdout.  Everything else goes to stderr.
@@ -41,7 +42,8 @@ METRIC = "KV block transfer GB/s (read+write) on 1 MI355X + % of HBM peak"
 HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, AMD published peak
 PROFILES = os.path.join(ROOT, "profiles")
 CALIB_BYTES = 1 << 30
-WORKLOAD_NAMES = ["qwen32b_push", "batched_push", "tp4_share", "multiturn_fp8", "pack_unpack", "tiny_push"]
+WORKLOAD_NAMES = ["qwen32b_push", "batched_push", "tp4_share", "multiturn_fp8", "pack_unpack", "qwen32b_reblock",
+                  "tiny_push"]
 
 
 def log(*a):
@@ -160,8 +162,9 @@ def bench_push(args, torch, kvx, S, W):
     rd, wr = plan.bytes_per_layer()
     L = wl.src.num_layers
     step_bytes = (rd + wr) * L
-    nruns = len(plan.runs())
-    log(f"plan: {nruns} runs, {len(plan.triples())} triples/region, {rd + wr} B per layer, "
+    nruns = len(plan.runs()) if wl.src.block_size == wl.dst.block_size else None
+    ntrip = len(plan.triples())
+    log(f"plan: {nruns} runs, {ntrip} triples/region, {rd + wr} B per layer, "
         f"{step_bytes} B per step, host plan {plan_ms:.2f} ms")
 
     if args.counters:
@@ -255,7 +258,8 @@ def bench_push(args, torch, kvx, S, W):
         "config": {"workload": wl.name, "layers": L, "kv_heads": wl.src.num_heads, "head_dim": wl.src.head_dim,
                    "block_size": wl.src.block_size, "payload_dtype": wl.src.dtype, "layout": wl.src.layout,
                    "prompt_tokens": wl.prompt_lens, "tokens_moved": tokens, "pool_blocks": wl.src.num_blocks,
-                   "merged_runs": nruns, "bytes_per_step": step_bytes,
+                   "dst_block_size": wl.dst.block_size, "dst_pool_blocks": wl.dst.num_blocks,
+                   "merged_runs": nruns, "triples_per_region": ntrip, "bytes_per_step": step_bytes,
                    "step": f"{L} x kvx_push_layer on one side stream, each after its layer's (fired) event",
                    "host_plan_ms": round(plan_ms, 3), "fresh_event_GBs": round(fresh_gbs, 1),
                    "two_stream_GBs": None if two_gbs is None else round(two_gbs, 1)},
@@ -620,7 +624,8 @@ def main():
     dev = torch.cuda.get_device_properties(0)
     log(f"device: {dev.name} {getattr(dev, 'gcnArchName', '')} CUs={dev.multi_processor_count} "
         f"mem={dev.total_memory / 2**30:.0f} GiB; workload {args.workload}")
-    fn = {"qwen32b_push": bench_push, "tiny_push": bench_push, "batched_push": bench_batched,
+    fn = {"qwen32b_push": bench_push, "tiny_push": bench_push, "qwen32b_reblock": bench_push,
+          "batched_push": bench_batched,
           "tp4_share": bench_tp4, "multiturn_fp8": bench_multiturn, "pack_unpack": bench_pack}[args.workload]
     if args.counters and fn is not bench_push:
         print("bench.py: --counters is for the push workloads", file=sys.stderr)

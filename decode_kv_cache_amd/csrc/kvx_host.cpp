@@ -114,6 +114,8 @@ int kvx_pool_create(const kvx_pool_desc* d, kvx_pool** out) {
   if (!d->k_base || !d->v_base) return fail(KVX_E_INVAL, "kvx_pool_create: null base array");
   if ((d->k_scale == nullptr) != (d->v_scale == nullptr))
     return fail(KVX_E_INVAL, "kvx_pool_create: k_scale and v_scale must both be set or both NULL");
+  if (d->block_size > 32768)
+    return fail(KVX_E_UNSUPPORTED, "kvx_pool_create: block_size %d above 32768", d->block_size);
   if ((int64_t(d->head_dim) * d->elem_bytes) % 16)
     return fail(KVX_E_UNSUPPORTED, "kvx_pool_create: head_dim*elem_bytes=%lld not a multiple of 16",
                 (long long)(int64_t(d->head_dim) * d->elem_bytes));
@@ -186,23 +188,24 @@ void emit(std::vector<kvx_triple>& t, int64_t so, int64_t dso, int64_t len) {
 
 // Triples of one (layer, K/V) region, in plan order ([MORI] §6: the
 // (local offset, remote offset, size) list of one batch call, adjacent
-// blocks merged).  NHD: a run's full blocks and its last block's first
-// `tail` token rows are one range.  HND: the full blocks are one range and
-// the partly filled last block adds one range of `tail` rows per head.
+// blocks merged).  Each planned block (or, with different block sizes, each
+// piece of a token range inside one source and one destination block)
+// contributes its token rows: one range in NHD, one range per head in HND;
+// `emit` merges ranges that continue on both sides, so consecutive blocks of
+// a run become one range.
 void build_triples(kvx_plan_t* p) {
-  const Geom& g = p->src;
-  const int64_t bb = g.block_bytes(), tb = g.token_bytes(), rb = g.row_bytes();
-  for (const kvx_run& r : p->runs) {
-    const int64_t s0 = int64_t(r.src0) * bb, d0 = int64_t(r.dst0) * bb;
-    if (g.layout == KVX_NHD) {
-      emit(p->triples, s0, d0, int64_t(r.nblk - 1) * bb + int64_t(r.tail) * tb);
-    } else if (r.tail == g.BS) {
-      emit(p->triples, s0, d0, int64_t(r.nblk) * bb);
+  const Geom& gs = p->src;
+  const Geom& gd = p->dst;
+  const int64_t tb = gs.token_bytes(), rb = gs.row_bytes();
+  for (const BlockPair& b : p->blocks) {
+    const int64_t ss = slot_src(b.slots), ds = slot_dst(b.slots);
+    const int64_t sbase = int64_t(b.src) * gs.block_bytes(), dbase = int64_t(b.dst) * gd.block_bytes();
+    if (gs.layout == KVX_NHD) {
+      emit(p->triples, sbase + ss * tb, dbase + ds * tb, int64_t(b.nslots) * tb);
     } else {
-      if (r.nblk > 1) emit(p->triples, s0, d0, int64_t(r.nblk - 1) * bb);
-      const int64_t sl = int64_t(r.src0 + r.nblk - 1) * bb, dl = int64_t(r.dst0 + r.nblk - 1) * bb;
-      for (int h = 0; h < g.H; ++h)
-        emit(p->triples, sl + h * g.BS * rb, dl + h * g.BS * rb, int64_t(r.tail) * rb);
+      for (int h = 0; h < gs.H; ++h)
+        emit(p->triples, sbase + (int64_t(h) * gs.BS + ss) * rb, dbase + (int64_t(h) * gd.BS + ds) * rb,
+             int64_t(b.nslots) * rb);
     }
   }
 }
@@ -266,109 +269,110 @@ void release(kvx_plan_t* p) {
   delete p;
 }
 
+// Validate the requests and build the plan's block list, runs and triples.
+// Validation order per request: token count, both list lengths, source IDs,
+// then destination IDs (range, then reuse across the plan).
+int build_plan(kvx_plan_t* p, int32_t R, const int64_t* num_tokens, const int64_t* so,
+               const int64_t* dof, const int32_t* src_ids, const int32_t* dst_ids) {
+  const Geom& gs = p->src;
+  const Geom& gd = p->dst;
+  const int64_t bss = gs.BS, bsd = gd.BS;
+  if (R > 0 && (so[0] < 0 || dof[0] < 0)) return fail(KVX_E_INVAL, "kvx_plan: negative first offset");
+  std::vector<uint8_t> dst_used(size_t(gd.NB), 0);
+  for (int32_t r = 0; r < R; ++r) {
+    const int64_t n = num_tokens[r];
+    if (n < 0) return fail(KVX_E_INVAL, "kvx_plan: request %d: negative token count", r);
+    if (so[r + 1] < so[r] || dof[r + 1] < dof[r])
+      return fail(KVX_E_INVAL, "kvx_plan: offsets not monotone at request %d", r);
+    const int64_t nbs = (n + bss - 1) / bss, nbd = (n + bsd - 1) / bsd;
+    if (so[r + 1] - so[r] < nbs || dof[r + 1] - dof[r] < nbd)
+      return fail(KVX_E_INVAL, "kvx_plan: request %d: block list shorter than its %lld/%lld blocks", r,
+                  (long long)nbs, (long long)nbd);
+    if (n == 0) continue;
+    if (!src_ids || !dst_ids) return fail(KVX_E_INVAL, "kvx_plan: null block ID array");
+    const int32_t* S = src_ids + so[r];
+    const int32_t* Dd = dst_ids + dof[r];
+    for (int64_t i = 0; i < nbs; ++i)
+      if (S[i] < 0 || S[i] >= gs.NB)
+        return fail(KVX_E_RANGE, "kvx_plan: request %d: src block %d outside [0,%d)", r, S[i], gs.NB);
+    for (int64_t i = 0; i < nbd; ++i) {
+      if (Dd[i] < 0 || Dd[i] >= gd.NB)
+        return fail(KVX_E_RANGE, "kvx_plan: request %d: dst block %d outside [0,%d)", r, Dd[i], gd.NB);
+      if (dst_used[size_t(Dd[i])]) return fail(KVX_E_DUPDST, "kvx_plan: dst block %d used twice", Dd[i]);
+      dst_used[size_t(Dd[i])] = 1;
+    }
+    if (bss == bsd) {
+      // Merge ([PUSH] "Threading-Modell"; [MORI] §3.1, §6): a new run starts
+      // at the request's first block and wherever either side is not the
+      // previous block + 1.
+      const int32_t tail = int32_t(n - (nbs - 1) * bss);
+      int64_t start = 0;
+      for (int64_t i = 1; i <= nbs; ++i) {
+        if (i == nbs || S[i] != S[i - 1] + 1 || Dd[i] != Dd[i - 1] + 1) {
+          p->runs.push_back(kvx_run{S[start], Dd[start], int32_t(i - start), i == nbs ? tail : int32_t(bss)});
+          start = i;
+        }
+      }
+      for (int64_t i = 0; i < nbs; ++i)
+        p->blocks.push_back(BlockPair{S[i], Dd[i], i == nbs - 1 ? tail : int32_t(bss), 0});
+    } else {
+      // Different block sizes ([PUSH] "Implementierungsdetails" step 3):
+      // token t sits in source block S[t / BSs], slot t % BSs and lands in
+      // destination block Dd[t / BSd], slot t % BSd.  Cut the token range
+      // wherever either side enters a new block.
+      for (int64_t t = 0; t < n;) {
+        const int64_t ss = t % bss, ds = t % bsd;
+        const int64_t k = std::min({bss - ss, bsd - ds, n - t});
+        p->blocks.push_back(BlockPair{S[t / bss], Dd[t / bsd], int32_t(k), pack_slots(ss, ds)});
+        t += k;
+      }
+    }
+  }
+  if (p->push_ok) {
+    build_triples(p);
+    build_pieces(p);
+  }
+  p->scale_seg_bytes = gs.scales ? pad16(4 * int64_t(p->blocks.size())) : 0;
+  return KVX_OK;
+}
+
 }  // namespace
 
 extern "C" {
 
 int kvx_plan(const kvx_pool* src, const kvx_pool* dst, int32_t num_requests,
-             const int64_t* num_tokens, const int64_t* id_offsets, const int32_t* src_ids,
-             const int32_t* dst_ids, uint32_t flags, hipStream_t upload_stream,
+             const int64_t* num_tokens, const int64_t* src_offsets, const int64_t* dst_offsets,
+             const int32_t* src_ids, const int32_t* dst_ids, uint32_t flags, hipStream_t upload_stream,
              kvx_plan_t** out) {
   if (!src || !dst || !out) return fail(KVX_E_INVAL, "kvx_plan: null pool or output");
   if (src == dst) return fail(KVX_E_INVAL, "kvx_plan: src and dst are the same pool");
   if (flags & ~KVX_PLAN_HOST_ONLY) return fail(KVX_E_INVAL, "kvx_plan: unknown flags 0x%x", flags);
   if (num_requests < 0) return fail(KVX_E_INVAL, "kvx_plan: negative request count");
-  if (num_requests > 0 && (!num_tokens || !id_offsets))
-    return fail(KVX_E_INVAL, "kvx_plan: null num_tokens or id_offsets");
+  if (num_requests > 0 && (!num_tokens || !src_offsets || !dst_offsets))
+    return fail(KVX_E_INVAL, "kvx_plan: null num_tokens or offsets");
   const Geom& gs = src->g;
   const Geom& gd = dst->g;
-  if (gs.L != gd.L || gs.BS != gd.BS || gs.D != gd.D || gs.E != gd.E || gs.scales != gd.scales)
-    return fail(KVX_E_MISMATCH,
-                "kvx_plan: pools differ in layers/block_size/head_dim/elem_bytes/scales");
+  if (gs.L != gd.L || gs.D != gd.D || gs.E != gd.E || gs.scales != gd.scales)
+    return fail(KVX_E_MISMATCH, "kvx_plan: pools differ in layers/head_dim/elem_bytes/scales");
+  if (gs.BS != gd.BS && gs.scales)
+    return fail(KVX_E_UNSUPPORTED, "kvx_plan: per-block scales need equal block sizes (%d vs %d)", gs.BS, gd.BS);
 
   kvx_plan_t* p = new (std::nothrow) kvx_plan_t;
   if (!p) return fail(KVX_E_NOMEM, "kvx_plan: out of host memory");
+  int rc = KVX_OK;
   try {
     p->src = gs;
     p->dst = gd;
     p->push_ok = gs.H == gd.H && gs.layout == gd.layout;
     p->host_only = (flags & KVX_PLAN_HOST_ONLY) != 0;
-    const int64_t BS = gs.BS;
-    std::vector<uint8_t> dst_used(size_t(gd.NB), 0);
-    if (num_requests > 0 && id_offsets[0] < 0) {
-      release(p);
-      return fail(KVX_E_INVAL, "kvx_plan: id_offsets[0] < 0");
-    }
-    for (int32_t r = 0; r < num_requests; ++r) {
-      const int64_t n = num_tokens[r];
-      const int64_t lo = id_offsets[r], hi = id_offsets[r + 1];
-      if (n < 0) {
-        release(p);
-        return fail(KVX_E_INVAL, "kvx_plan: request %d: negative token count", r);
-      }
-      if (hi < lo) {
-        release(p);
-        return fail(KVX_E_INVAL, "kvx_plan: id_offsets not monotone at request %d", r);
-      }
-      const int64_t nb = (n + BS - 1) / BS;
-      if (hi - lo < nb) {
-        release(p);
-        return fail(KVX_E_INVAL, "kvx_plan: request %d: %lld block IDs for %lld blocks", r,
-                    (long long)(hi - lo), (long long)nb);
-      }
-      if (nb == 0) continue;
-      if (!src_ids || !dst_ids) {
-        release(p);
-        return fail(KVX_E_INVAL, "kvx_plan: null block ID array");
-      }
-      const int32_t* S = src_ids + lo;
-      const int32_t* Dd = dst_ids + lo;
-      for (int64_t i = 0; i < nb; ++i) {
-        if (S[i] < 0 || S[i] >= gs.NB) {
-          release(p);
-          return fail(KVX_E_RANGE, "kvx_plan: request %d: src block %d outside [0,%d)", r, S[i], gs.NB);
-        }
-        if (Dd[i] < 0 || Dd[i] >= gd.NB) {
-          release(p);
-          return fail(KVX_E_RANGE, "kvx_plan: request %d: dst block %d outside [0,%d)", r, Dd[i], gd.NB);
-        }
-        if (dst_used[size_t(Dd[i])]) {
-          release(p);
-          return fail(KVX_E_DUPDST, "kvx_plan: dst block %d used twice", Dd[i]);
-        }
-        dst_used[size_t(Dd[i])] = 1;
-      }
-      // Merge ([PUSH] "Threading-Modell"; [MORI] §3.1, §6): a new run starts
-      // at the request's first block and wherever either side is not the
-      // previous block + 1.
-      const int32_t tail = int32_t(n - (nb - 1) * BS);
-      int64_t start = 0;
-      for (int64_t i = 1; i <= nb; ++i) {
-        if (i == nb || S[i] != S[i - 1] + 1 || Dd[i] != Dd[i - 1] + 1) {
-          p->runs.push_back(kvx_run{S[start], Dd[start], int32_t(i - start),
-                                    i == nb ? tail : int32_t(BS)});
-          start = i;
-        }
-      }
-    }
-    for (const kvx_run& r : p->runs)
-      for (int32_t k = 0; k < r.nblk; ++k)
-        p->blocks.push_back(BlockPair{r.src0 + k, r.dst0 + k, k == r.nblk - 1 ? r.tail : int32_t(BS), 0});
-    if (p->push_ok) {
-      build_triples(p);
-      build_pieces(p);
-    }
-    p->scale_seg_bytes = gs.scales ? pad16(4 * int64_t(p->blocks.size())) : 0;
+    rc = build_plan(p, num_requests, num_tokens, src_offsets, dst_offsets, src_ids, dst_ids);
   } catch (const std::bad_alloc&) {
-    release(p);
-    return fail(KVX_E_NOMEM, "kvx_plan: out of host memory");
+    rc = fail(KVX_E_NOMEM, "kvx_plan: out of host memory");
   }
-  if (!p->host_only) {
-    int rc = upload(p, upload_stream);
-    if (rc != KVX_OK) {
-      release(p);
-      return rc;
-    }
+  if (rc == KVX_OK && !p->host_only) rc = upload(p, upload_stream);
+  if (rc != KVX_OK) {
+    release(p);
+    return rc;
   }
   *out = p;
   return KVX_OK;
@@ -376,6 +380,8 @@ int kvx_plan(const kvx_pool* src, const kvx_pool* dst, int32_t num_requests,
 
 int kvx_plan_runs(const kvx_plan_t* p, kvx_run* out, int64_t cap, int64_t* n) {
   if (!p || !n) return fail(KVX_E_INVAL, "kvx_plan_runs: null argument");
+  if (p->src.BS != p->dst.BS)
+    return fail(KVX_E_MISMATCH, "kvx_plan_runs: block runs need equal block sizes (%d vs %d)", p->src.BS, p->dst.BS);
   const int64_t cnt = int64_t(p->runs.size());
   if (out && cap >= cnt) std::copy(p->runs.begin(), p->runs.end(), out);
   *n = cnt;

@@ -26,10 +26,17 @@ struct Piece {
 static_assert(sizeof(Piece) == 32, "Piece is 32 bytes");
 
 // One planned block: (source block, destination block, tokens it holds).
+// With different block sizes per side it is a piece of a token range that
+// stays inside one source and one destination block, starting at slot
+// `slots & 0xffff` of the source block and `slots >> 16` of the destination
+// block (both 0 with equal block sizes).
 struct BlockPair {
-  int32_t src, dst, nslots, pad;
+  int32_t src, dst, nslots, slots;
 };
 static_assert(sizeof(BlockPair) == 16, "BlockPair is 16 bytes");
+inline int32_t pack_slots(int64_t src_slot, int64_t dst_slot) { return int32_t(src_slot | (dst_slot << 16)); }
+__host__ __device__ inline int32_t slot_src(int32_t slots) { return slots & 0xffff; }
+__host__ __device__ inline int32_t slot_dst(int32_t slots) { return (slots >> 16) & 0xffff; }
 
 // Launch shape of the layer copy kernel (compile-time tuning knobs).
 #ifndef KVX_THREADS

@@ -113,14 +113,14 @@ struct HeadArgs {
 
 constexpr int kHeadUnroll = 4;
 
-// One workgroup moves the head slice of one planned block of the K or V
-// region.  Lanes walk the block's rows in destination order so stores are
+// One workgroup moves the head slice of one planned block (or block piece,
+// with different block sizes per side) of the K or V region.  Lanes walk the block's rows in destination order so stores are
 // contiguous; each lane keeps kHeadUnroll vectors in flight.
 __global__ __launch_bounds__(kThreads) void heads_kernel(HeadArgs a) {
   const int kv = blockIdx.y;
   const BlockPair b = a.blocks[blockIdx.x];
-  const uint8_t* sb = a.in[kv] + int64_t(b.src) * a.s_blk;
-  uint8_t* db = a.out[kv] + int64_t(b.dst) * a.d_blk;
+  const uint8_t* sb = a.in[kv] + int64_t(b.src) * a.s_blk + slot_src(b.slots) * a.s_slot;
+  uint8_t* db = a.out[kv] + int64_t(b.dst) * a.d_blk + slot_dst(b.slots) * a.d_slot;
   const int rows = a.nh * b.nslots;
   const int total = rows * a.vpr;
   for (int base = 0; base < total; base += kThreads * kHeadUnroll) {

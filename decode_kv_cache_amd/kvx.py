@@ -50,7 +50,7 @@ _SIGS = {
     "kvx_should_reuse": (_I32, [_I64, _I64]),
     "kvx_pool_create": (C.c_int, [C.POINTER(kvx_pool_desc), C.POINTER(_P)]),
     "kvx_pool_destroy": (None, [_P]),
-    "kvx_plan": (C.c_int, [_P, _P, _I32, _P, _P, _P, _P, _U32, _P, C.POINTER(_P)]),
+    "kvx_plan": (C.c_int, [_P, _P, _I32, _P, _P, _P, _P, _P, _U32, _P, C.POINTER(_P)]),
     "kvx_plan_runs": (C.c_int, [_P, _P, _I64, C.POINTER(_I64)]),
     "kvx_plan_triples": (C.c_int, [_P, _I32, _I32, _P, _I64, C.POINTER(_I64)]),
     "kvx_plan_bytes": (C.c_int, [_P, C.POINTER(_I64), C.POINTER(_I64)]),
@@ -206,43 +206,42 @@ class Plan:
     __del__ = close
 
 
+def _csr(tables):
+    off = np.zeros(len(tables) + 1, np.int64)
+    off[1:] = np.cumsum([len(t) for t in tables])
+    ids = (np.concatenate([np.asarray(t, np.int32) for t in tables]) if len(tables) else np.zeros(0, np.int32))
+    return off, np.ascontiguousarray(ids, np.int32)
+
+
 def kvx_plan(src: Pool, dst: Pool, num_tokens: Sequence[int], src_tables: Sequence[Sequence[int]],
              dst_tables: Sequence[Sequence[int]], *, host_only: bool = False, stream=None) -> Plan:
     """Build a plan.  ``num_tokens[r]`` tokens of request r move; its block
-    lists are ``src_tables[r]`` / ``dst_tables[r]``.  The C ABI takes one
-    offset array for both lists, so each request's two lists are passed cut to
-    the shorter length (entries past the blocks in use are ignored anyway)."""
+    lists are ``src_tables[r]`` / ``dst_tables[r]`` (each at least as long as
+    its side needs)."""
     R = len(num_tokens)
     if len(src_tables) != R or len(dst_tables) != R:
         raise ValueError("one src and one dst block list per request")
     nt = np.ascontiguousarray(num_tokens, dtype=np.int64)
-    lens = [min(len(a), len(b)) for a, b in zip(src_tables, dst_tables)]
-    off = np.zeros(R + 1, np.int64)
-    off[1:] = np.cumsum(lens)
-    sid = np.ascontiguousarray(np.concatenate([np.asarray(t[:n], np.int32) for t, n in zip(src_tables, lens)])
-                               if R else np.zeros(0, np.int32), np.int32)
-    did = np.ascontiguousarray(np.concatenate([np.asarray(t[:n], np.int32) for t, n in zip(dst_tables, lens)])
-                               if R else np.zeros(0, np.int32), np.int32)
+    so, sid = _csr(src_tables)
+    do, did = _csr(dst_tables)
     h = C.c_void_p()
     us = None if host_only else _stream(stream)
-    rc = lib().kvx_plan(src.handle, dst.handle, R, nt.ctypes.data, off.ctypes.data,
+    rc = lib().kvx_plan(src.handle, dst.handle, R, nt.ctypes.data, so.ctypes.data, do.ctypes.data,
                         sid.ctypes.data if sid.size else None, did.ctypes.data if did.size else None,
                         KVX_PLAN_HOST_ONLY if host_only else 0, us, C.byref(h))
     _check("kvx_plan", rc)
     return Plan(h, src, dst)
 
 
-def kvx_plan_raw(src: Pool, dst: Pool, num_requests: int, num_tokens, id_offsets, src_ids, dst_ids,
-                 flags: int = KVX_PLAN_HOST_ONLY, stream=None):
+def kvx_plan_raw(src: Pool, dst: Pool, num_requests: int, num_tokens, src_offsets, dst_offsets, src_ids,
+                 dst_ids, flags: int = KVX_PLAN_HOST_ONLY, stream=None):
     """Direct call with raw arrays (numpy) for error-path tests; returns
     (status, Plan or None)."""
     h = C.c_void_p()
-
-    def ptr(a):
-        return None if a is None else np.ascontiguousarray(a).ctypes.data
-    keep = [np.ascontiguousarray(a) if a is not None else None for a in (num_tokens, id_offsets, src_ids, dst_ids)]
+    keep = [None if a is None else np.ascontiguousarray(a)
+            for a in (num_tokens, src_offsets, dst_offsets, src_ids, dst_ids)]
     rc = lib().kvx_plan(src.handle if src else None, dst.handle if dst else None, num_requests,
-                        *(ptr(a) for a in keep), flags, stream, C.byref(h))
+                        *(None if a is None else a.ctypes.data for a in keep), flags, stream, C.byref(h))
     return rc, (Plan(h, src, dst) if rc == KVX_OK else None)
 
 

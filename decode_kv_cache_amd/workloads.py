@@ -27,6 +27,8 @@ Workload names (sizes as in their descriptions):
   multiturn_fp8  fp8 e4m3 KV with one fp32 scale per (layer, K/V, block), 48
                  layers, 8 heads, head_dim 128, block 16; 32 sessions x 8
                  turns, context +2048 tokens per turn, pools of 32768 blocks.
+  qwen32b_reblock  qwen32b_push's KV with 64-slot consumer blocks (1024 of
+                 them) and 16-slot producer blocks.
 """
 from __future__ import annotations
 
@@ -193,12 +195,27 @@ def multiturn_fp8(seed: int = 1005) -> Workload:
                            "threshold": 512, "decode_tables": dec, "prefill_tables": pre})
 
 
+def qwen32b_reblock(seed: int = 1006) -> Workload:
+    """qwen32b_push's KV, but the consumer pages KV in 64-slot blocks while
+    the producer uses 16-slot blocks; both tables of geometric runs (mean 4)."""
+    src = PoolSpec(64, 4096, 16, 8, 128, BF16)
+    dst = PoolSpec(64, 1024, 64, 8, 128, BF16)
+    r_src, r_dst = _children(seed, 2)
+    plen = [8192]
+    return Workload("qwen32b_reblock", seed, src, dst, plen,
+                    split_tables(geometric_run_table(r_src, src.num_blocks, 4.0),
+                                 [alloc_blocks(x, src.block_size) for x in plen]),
+                    split_tables(geometric_run_table(r_dst, dst.num_blocks, 4.0),
+                                 [alloc_blocks(x, dst.block_size) for x in plen]))
+
+
 WORKLOADS = {
     "tiny_push": tiny_push,
     "qwen32b_push": qwen32b_push,
     "batched_push": batched_push,
     "tp4_share": tp4_share,
     "multiturn_fp8": multiturn_fp8,
+    "qwen32b_reblock": qwen32b_reblock,
 }
 
 

@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define KVX_ABI_VERSION 1
+#define KVX_ABI_VERSION 2
 
 /* Status codes. */
 enum {
@@ -78,7 +78,8 @@ enum {
  *     device pointers to fp32[num_blocks], one scale per (layer, K/V, block),
  *     4-B aligned.  A scale travels with its block, unchanged.
  * Requirements: all counts >= 1; elem_bytes in {1, 2, 4}; head_dim *
- * elem_bytes a multiple of 16 (KVX_E_UNSUPPORTED otherwise).
+ * elem_bytes a multiple of 16 and block_size <= 32768 (KVX_E_UNSUPPORTED
+ * otherwise).
  * The library copies the descriptor; the arrays may be freed after the call.
  */
 typedef struct kvx_pool_desc {
@@ -138,34 +139,44 @@ void kvx_pool_destroy(kvx_pool* pool);
  * Build a transfer plan from `src` to `dst` for `num_requests` requests.
  *   num_tokens[r]: tokens request r moves (>= 0); the caller applies the
  *     final-token rule (kvx_tokens_to_move) for P->D.
- *   id_offsets[r], id_offsets[r+1]: CSR bounds of request r's block list in
- *     both src_ids and dst_ids (non-decreasing, id_offsets[0] >= 0).  Only
- *     the first ceil(num_tokens[r] / block_size) entries are used; later
- *     entries are ignored and not validated.
+ *   src_offsets[r], src_offsets[r+1] (and dst_offsets likewise): CSR bounds
+ *     of request r's block list in src_ids (dst_ids); non-decreasing, first
+ *     entry >= 0.  Only the first ceil(num_tokens[r] / block_size) entries of
+ *     each list are used, block_size being that side's; later entries are
+ *     ignored and not validated.
  *   src_ids / dst_ids: block IDs of the producer / consumer pool.
- * The block pairs of each request are merged, in list order, into maximal
- * runs consecutive on both sides; runs never cross requests.  This is the
- * merge of contiguous blocks into larger transfer regions done by the push
- * connector's background thread ([PUSH] "Threading-Modell") and by the
- * per-layer offset computation ([MORI] §3.1, §6).  When both pools have the
- * same head count and layout the plan also holds the per-region triple list
- * and the device work list for kvx_push_layer / kvx_pack / kvx_unpack;
+ * Token t of a request sits in source block src_ids[t / BS_src], slot
+ * t % BS_src, and lands in destination block dst_ids[t / BS_dst], slot
+ * t % BS_dst: each side maps block positions onto its own layout, so block
+ * sizes may differ ([PUSH] "Implementierungsdetails" step 3).  With equal
+ * block sizes the block pairs of each request are merged, in list order,
+ * into maximal runs consecutive on both sides; runs never cross requests.
+ * This is the merge of contiguous blocks into larger transfer regions done by
+ * the push connector's background thread ([PUSH] "Threading-Modell") and by
+ * the per-layer offset computation ([MORI] §3.1, §6).  When both pools have
+ * the same head count and layout the plan also holds the per-region triple
+ * list and the device work list for kvx_push_layer / kvx_pack / kvx_unpack;
  * otherwise only kvx_copy_heads may use it.
- * Pools must agree on num_layers, block_size, head_dim, elem_bytes and
- * scale presence (KVX_E_MISMATCH otherwise); src == dst is KVX_E_INVAL.
+ * Pools must agree on num_layers, head_dim, elem_bytes and scale presence
+ * (KVX_E_MISMATCH otherwise); pools with scales must also agree on
+ * block_size (KVX_E_UNSUPPORTED: a per-block scale has no single source block
+ * otherwise); src == dst is KVX_E_INVAL.
  * Unless KVX_PLAN_HOST_ONLY is set the device work list is uploaded on
  * `upload_stream` (NULL = the null stream); later device calls on any stream
  * are ordered after the upload.
- * Errors: INVAL, RANGE (ID outside its pool), DUPDST (a dst ID used twice),
- * MISMATCH, NOMEM, HIP.
+ * Validation order per request: token count, list lengths, source IDs, then
+ * destination IDs.  Errors: INVAL, RANGE (ID outside its pool), DUPDST (a dst
+ * ID used twice in the plan), MISMATCH, UNSUPPORTED, NOMEM, HIP.
  */
 int kvx_plan(const kvx_pool* src, const kvx_pool* dst, int32_t num_requests,
-             const int64_t* num_tokens, const int64_t* id_offsets,
+             const int64_t* num_tokens, const int64_t* src_offsets, const int64_t* dst_offsets,
              const int32_t* src_ids, const int32_t* dst_ids, uint32_t flags,
              hipStream_t upload_stream, kvx_plan_t** out);
 
 /* Copy the run table into out[0..cap); *n receives the run count.  With
- * out == NULL or cap < count only *n is written (and KVX_OK returned). */
+ * out == NULL or cap < count only *n is written (and KVX_OK returned).
+ * Runs are block pairs, defined for equal block sizes only (KVX_E_MISMATCH
+ * otherwise; the triples describe such plans). */
 int kvx_plan_runs(const kvx_plan_t* plan, kvx_run* out, int64_t cap, int64_t* n);
 
 /* The (src_off, dst_off, len) list of one (layer, kv) region (kv: 0 = K,

@@ -35,7 +35,7 @@ def test_library_exports_every_declared_symbol():
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(kvx.EXPORTED)
-    assert kvx.kvx_abi_version() == 1
+    assert kvx.kvx_abi_version() == 2
     assert L.kvx_status_str(kvx.KVX_E_DUPDST) == b"KVX_E_DUPDST"
 
 
@@ -151,7 +151,7 @@ def test_error_classes_match_oracle():
         off[1:] = np.cumsum([len(x) for x in st])
         sid = np.array([x for s in st for x in s] or [0], np.int32)
         did = np.array([x for d in dt for x in d] or [0], np.int32)
-        rc, plan = kvx.kvx_plan_raw(sp, dp, len(toks), np.array(toks or [0], np.int64), off, sid, did)
+        rc, plan = kvx.kvx_plan_raw(sp, dp, len(toks), np.array(toks or [0], np.int64), off, off, sid, did)
         got = "OK" if rc == 0 else kvx.lib().kvx_status_str(rc).decode().replace("KVX_E_", "")
         assert got == exp, (toks, st, dt, got, exp)
         if plan:
@@ -164,24 +164,24 @@ def test_argument_errors():
     off = np.array([0, 1], np.int64)
     ids = np.array([0], np.int32)
     n = np.array([4], np.int64)
-    assert kvx.kvx_plan_raw(sp, sp, 1, n, off, ids, ids)[0] == kvx.KVX_E_INVAL  # same pool
-    assert kvx.kvx_plan_raw(sp, dp, -1, n, off, ids, ids)[0] == kvx.KVX_E_INVAL
-    assert kvx.kvx_plan_raw(sp, dp, 1, n, off, ids, ids, flags=8)[0] == kvx.KVX_E_INVAL
-    assert kvx.kvx_plan_raw(sp, dp, 1, n, np.array([1, 0], np.int64), ids, ids)[0] == kvx.KVX_E_INVAL
-    assert kvx.kvx_plan_raw(sp, dp, 1, None, off, ids, ids)[0] == kvx.KVX_E_INVAL
+    assert kvx.kvx_plan_raw(sp, sp, 1, n, off, off, ids, ids)[0] == kvx.KVX_E_INVAL  # same pool
+    assert kvx.kvx_plan_raw(sp, dp, -1, n, off, off, ids, ids)[0] == kvx.KVX_E_INVAL
+    assert kvx.kvx_plan_raw(sp, dp, 1, n, off, off, ids, ids, flags=8)[0] == kvx.KVX_E_INVAL
+    assert kvx.kvx_plan_raw(sp, dp, 1, n, np.array([1, 0], np.int64), off, ids, ids)[0] == kvx.KVX_E_INVAL
+    assert kvx.kvx_plan_raw(sp, dp, 1, None, off, off, ids, ids)[0] == kvx.KVX_E_INVAL
     # geometry mismatch at plan time: head_dim differs
     other = fake_pool(W.PoolSpec(2, 8, 4, 2, 32, W.BF16), 2)
-    assert kvx.kvx_plan_raw(sp, other, 1, n, off, ids, ids)[0] == kvx.KVX_E_MISMATCH
+    assert kvx.kvx_plan_raw(sp, other, 1, n, off, off, ids, ids)[0] == kvx.KVX_E_MISMATCH
     # head count differs: plan is fine, push-only queries are mismatches
     fewer = fake_pool(W.PoolSpec(2, 8, 4, 1, 16, W.BF16, "HND"), 3)
-    rc, plan = kvx.kvx_plan_raw(sp, fewer, 1, n, off, ids, ids)
+    rc, plan = kvx.kvx_plan_raw(sp, fewer, 1, n, off, off, ids, ids)
     assert rc == 0
     with pytest.raises(kvx.KvxError) as e:
         plan.triples()
     assert e.value.code == kvx.KVX_E_MISMATCH
     assert plan.runs().tolist() == [[0, 0, 1, 4]]
     # device calls on a host-only plan are argument errors, and range checks hold
-    rc, plan = kvx.kvx_plan_raw(sp, dp, 1, n, off, ids, ids)
+    rc, plan = kvx.kvx_plan_raw(sp, dp, 1, n, off, off, ids, ids)
     L = kvx.lib()
     assert L.kvx_push_layer(plan.handle, 0, None, None) == kvx.KVX_E_INVAL
     assert L.kvx_copy_heads(plan.handle, 0, 0, 0, 1, None, None) == kvx.KVX_E_INVAL
@@ -216,3 +216,44 @@ def test_pool_create_errors():
                  k_bases=[FAKE], v_bases=[FAKE * 2])
     assert e.value.code == kvx.KVX_E_INVAL
     fake_pool(spec, 0).close()
+
+
+def test_reblock_plan_matches_oracle():
+    """Different block sizes per side: triples, bytes and staging sizes equal
+    the oracle's token-segment procedure; runs are refused."""
+    rng = np.random.Generator(np.random.PCG64(17))
+    for i in range(40):
+        bs, bsd = [int(x) for x in rng.choice([1, 2, 3, 4, 8, 16, 32], size=2, replace=False)]
+        wl = W.random_case(9000 + i, layout=["NHD", "HND"][i % 2], elem_bytes=int(rng.choice([1, 2])),
+                           num_layers=2, num_blocks=400, block_size=bs, dst_block_size=bsd,
+                           num_heads=int(rng.integers(1, 4)), head_dim=int(rng.choice([16, 32])),
+                           num_requests=int(rng.integers(0, 4)), max_tokens=80,
+                           run_mean=float(rng.choice([1.5, 4.0])), extra_ids=int(rng.integers(0, 2)))
+        plan, n = host_plan(wl)
+        op = oracle_plan(wl, n)
+        assert plan.triples(0, 0).tolist() == [list(t) for t in op.triples], wl.name
+        assert plan.bytes_per_layer() == op.bytes_per_layer()
+        assert kvx.kvx_staging_bytes(plan, 0, 2) == O.staging_bytes(op, 0, 2)
+        with pytest.raises(kvx.KvxError) as e:
+            plan.runs()
+        assert e.value.code == kvx.KVX_E_MISMATCH
+        plan.close()
+
+
+def test_reblock_errors():
+    a = W.PoolSpec(1, 8, 4, 1, 16, W.U8, has_scales=True)
+    b = W.PoolSpec(1, 8, 8, 1, 16, W.U8, has_scales=True)
+    with pytest.raises(kvx.KvxError) as e:
+        kvx.kvx_plan(fake_pool(a, 0), fake_pool(b, 1), [8], [[0, 1]], [[2]], host_only=True)
+    assert e.value.code == kvx.KVX_E_UNSUPPORTED
+    a, b = W.PoolSpec(1, 8, 4, 1, 16, W.U8), W.PoolSpec(1, 8, 8, 1, 16, W.U8)
+    pa, pb = fake_pool(a, 0), fake_pool(b, 1)
+    kvx.kvx_plan(pa, pb, [8], [[0, 1]], [[2]], host_only=True).close()
+    for st, dt in (([0, 1], [2, 3]), ([0, 1, 2], [2])):
+        with pytest.raises(kvx.KvxError) as e:
+            kvx.kvx_plan(pa, pb, [9], [st], [dt], host_only=True)
+        assert e.value.code == kvx.KVX_E_INVAL
+    with pytest.raises(kvx.KvxError) as e:
+        kvx.Pool(num_blocks=8, block_size=65536, num_heads=1, head_dim=16, elem_bytes=1, layout="NHD",
+                 k_bases=[FAKE], v_bases=[FAKE * 2])
+    assert e.value.code == kvx.KVX_E_UNSUPPORTED

@@ -337,3 +337,52 @@ def test_multiturn_fp8_full():
                 assert np.array_equal(S.scale_bits(pre.sc[l]), state[l][1]), (t, l)
     for l in layers:
         assert np.array_equal(dec.kv[l].cpu().numpy(), dsnap[l][0])
+
+
+# ---------------------------------------------------------------------------
+# different block sizes per side
+# ---------------------------------------------------------------------------
+def test_reblock_random_small():
+    """push, pack/unpack and copy_heads with different block sizes per side."""
+    rng = np.random.Generator(np.random.PCG64(23))
+    for i in range(30):
+        bs, bsd = [int(x) for x in rng.choice([1, 3, 4, 8, 16, 32], size=2, replace=False)]
+        same = i % 3 != 0
+        hs = int(rng.integers(1, 5))
+        hd = hs if same else int(rng.integers(1, 5))
+        sl = ["NHD", "HND"][i % 2]
+        dl = sl if same else ["NHD", "HND"][(i // 2) % 2]
+        wl = W.random_case(9500 + i, layout=sl, dst_layout=dl, elem_bytes=int(rng.choice([1, 2])), num_layers=2,
+                           num_blocks=300, block_size=bs, dst_block_size=bsd, num_heads=hs, dst_heads=hd,
+                           head_dim=int(rng.choice([16, 64, 128])), num_requests=int(rng.integers(1, 4)),
+                           max_tokens=120, run_mean=float(rng.choice([1.5, 4.0])), extra_ids=int(rng.integers(0, 2)))
+        say("case", wl.name, bs, bsd, sl, dl, hs, hd)
+        src, dst, gs, gd = host_sides(wl)
+        toks = tokens(wl)
+        reqs = oracle_requests(wl, toks)
+        plan = kvx.kvx_plan(gs.pool, gd.pool, toks, wl.src_tables, wl.dst_tables)
+        op = O.make_plan(src.geom, dst.geom, reqs)
+        exp = dst.copy()
+        if same:
+            for l in range(2):
+                kvx.kvx_push_layer(plan, l)
+            O.push(src, exp, op)
+            nbytes = kvx.kvx_staging_bytes(plan, 0, 2)
+            stg = torch.empty(max(nbytes, 16), dtype=torch.uint8, device="cuda")
+            kvx.kvx_pack(plan, 0, 2, stg)
+            torch.cuda.synchronize()
+            assert np.array_equal(stg[:nbytes].cpu().numpy(), O.pack(src, op, 0, 2)), wl.name
+        else:
+            nh = int(rng.integers(1, min(hs, hd) + 1))
+            s0, d0 = int(rng.integers(0, hs - nh + 1)), int(rng.integers(0, hd - nh + 1))
+            for l in range(2):
+                kvx.kvx_copy_heads(plan, l, s0, d0, nh)
+                O.copy_heads(src, exp, op, reqs, l, s0, d0, nh)
+        torch.cuda.synchronize()
+        assert np.array_equal(gd.kv.cpu().numpy(), exp.kv), wl.name
+        plan.close()
+
+
+def test_qwen32b_reblock_full():
+    torch.cuda.empty_cache()
+    full_push(W.qwen32b_reblock(), [0, 63], "qwen32b_reblock")
