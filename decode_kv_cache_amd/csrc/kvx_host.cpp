@@ -66,6 +66,16 @@ int check_launch(const char* what) {
 
 static int64_t pad16(int64_t x) { return (x + 15) / 16 * 16; }
 
+void plan_free_idle(kvx_plan_t* p) {
+  if (!p) return;
+  if (p->upload_ev) {
+    (void)hipEventSynchronize(p->upload_ev);
+    (void)hipEventDestroy(p->upload_ev);
+  }
+  if (p->dev_buf) (void)hipFree(p->dev_buf);
+  delete p;
+}
+
 }  // namespace kvx
 
 using namespace kvx;
@@ -261,12 +271,7 @@ int upload(kvx_plan_t* p, hipStream_t s) {
 void release(kvx_plan_t* p) {
   if (!p) return;
   if (p->dev_buf) (void)hipDeviceSynchronize();
-  if (p->upload_ev) {
-    (void)hipEventSynchronize(p->upload_ev);
-    (void)hipEventDestroy(p->upload_ev);
-  }
-  if (p->dev_buf) (void)hipFree(p->dev_buf);
-  delete p;
+  kvx::plan_free_idle(p);
 }
 
 // Validate the requests and build the plan's block list, runs and triples.

@@ -99,4 +99,8 @@ int enqueue_waits(kvx_plan_t* plan, hipEvent_t ready, hipStream_t stream);
 // After a launch: turn a launch error into KVX_E_HIP.
 int check_launch(const char* what);
 
+// Free a plan whose enqueued work is known to have finished (no device
+// drain, unlike kvx_plan_destroy).
+void plan_free_idle(kvx_plan_t* plan);
+
 }  // namespace kvx

@@ -1,0 +1,435 @@
+// libkvx transfer state machine (kvx_xfer_*): when each layer write of a
+// request is issued and when the request is done, failed or expired.
+//
+// Sources: [PUSH] push-based NIXL connector post, "Implementierungsdetails"
+// steps 1-3; [MORI] MoRIIO connector note §3.1, §3.2, §6 (full titles in
+// kvx.h; the readings taken are listed in kvx_xfer.h).
+
+#include <hip/hip_runtime_api.h>
+
+#include <map>
+#include <mutex>
+#include <new>
+#include <vector>
+
+#include "kvx_internal.h"
+#include "kvx_xfer.h"
+
+namespace {
+
+using namespace kvx;
+
+enum LayerState : int8_t { kDeferred = 0, kIssued = 1, kDone = 2, kFailed = 3 };
+
+struct Layer {
+  LayerState st = kDeferred;
+  double issued_at = 0;
+  hipEvent_t gate = nullptr;  // captured readiness of a deferred write (device mode)
+  hipEvent_t done = nullptr;  // recorded after the write (device mode)
+};
+
+struct Req {
+  uint32_t attempt = 0;
+  bool has_src = false, has_dst = false;
+  int64_t ntok = 0;
+  std::vector<int32_t> src, dst;
+  const kvx_pool* consumer = nullptr;
+  std::map<int32_t, Layer> layers;  // ordered by layer
+  double deferred_since = -1;       // < 0: nothing deferred
+  bool sealed = false;
+  int64_t expected = 0;
+  int32_t state = KVX_REQ_PENDING;
+  bool reported = false;
+  kvx_plan_t* plan = nullptr;
+};
+
+}  // namespace
+
+struct kvx_xfer_s {
+  const kvx_pool* producer = nullptr;
+  kvx_xfer_config cfg{};
+  hipStream_t stream = nullptr;
+  bool host_only = false;
+  std::map<uint64_t, Req> reqs;
+  std::vector<uint64_t> log_req;
+  std::vector<uint32_t> log_attempt;
+  std::vector<int32_t> log_layer;
+  std::vector<hipEvent_t> spare;  // recycled events
+  // plans of finished requests waiting for their enqueued work to finish
+  std::vector<std::pair<kvx_plan_t*, hipEvent_t>> retired;
+  mutable std::mutex mu;
+};
+
+namespace {
+
+int get_event(kvx_xfer* x, hipEvent_t* ev) {
+  if (!x->spare.empty()) {
+    *ev = x->spare.back();
+    x->spare.pop_back();
+    return KVX_OK;
+  }
+  hipError_t e = hipEventCreateWithFlags(ev, hipEventDisableTiming);
+  return e == hipSuccess ? KVX_OK : fail_hip(e, "hipEventCreate(xfer)");
+}
+
+// Find the request for (req, attempt): nullptr for a stale attempt; a newer
+// attempt starts from a fresh record ([PUSH] step 2: re-sent and retried
+// requests map to the right state).
+Req* lookup(kvx_xfer* x, uint64_t id, uint32_t attempt, bool create);
+
+// A request finished or was replaced: recycle its events and retire its
+// plan.  Its layer states stay for status queries.
+void release_req(kvx_xfer* x, Req& r) {
+  for (auto& kv : r.layers) {
+    if (kv.second.gate) x->spare.push_back(kv.second.gate);
+    if (kv.second.done) x->spare.push_back(kv.second.done);
+    kv.second.gate = kv.second.done = nullptr;
+  }
+  if (!r.plan) return;
+  if (x->host_only) {
+    plan_free_idle(r.plan);
+  } else {
+    // Work already enqueued on the stream (the plan upload, issued writes)
+    // may still read the plan's descriptors: free it once a mark recorded
+    // behind that work has fired.
+    hipEvent_t mark = nullptr;
+    if (get_event(x, &mark) == KVX_OK && hipEventRecord(mark, x->stream) == hipSuccess) {
+      x->retired.emplace_back(r.plan, mark);
+    } else {
+      (void)hipStreamSynchronize(x->stream);
+      plan_free_idle(r.plan);
+    }
+  }
+  r.plan = nullptr;
+}
+
+Req* lookup(kvx_xfer* x, uint64_t id, uint32_t attempt, bool create) {
+  auto it = x->reqs.find(id);
+  if (it != x->reqs.end() && attempt < it->second.attempt) return nullptr;
+  if (it == x->reqs.end() || attempt > it->second.attempt) {
+    if (!create) return nullptr;
+    if (it != x->reqs.end()) release_req(x, it->second);
+    Req fresh;
+    fresh.attempt = attempt;
+    x->reqs[id] = std::move(fresh);
+    return &x->reqs[id];
+  }
+  return &it->second;
+}
+
+void settle(kvx_xfer* x, Req& r) {
+  if (r.state != KVX_REQ_PENDING) return;
+  int64_t done = 0;
+  bool failed = false;
+  for (auto& kv : r.layers) {
+    failed |= kv.second.st == kFailed;
+    done += kv.second.st == kDone;
+  }
+  if (failed)
+    r.state = KVX_REQ_FAILED;
+  else if (r.sealed && done == r.expected)
+    r.state = KVX_REQ_DONE;
+  if (r.state != KVX_REQ_PENDING) release_req(x, r);
+}
+
+// Issue one layer's write: kvx_push_layer gated on the layer's readiness,
+// then a completion event (device mode); host-only mode only logs it.
+int issue(kvx_xfer* x, uint64_t id, Req& r, int32_t layer, Layer& ly, hipEvent_t ready, double now) {
+  if (!x->host_only) {
+    int rc = kvx_push_layer(r.plan, layer, ready, x->stream);
+    if (rc != KVX_OK) return rc;
+    if (!ly.done) {
+      rc = get_event(x, &ly.done);
+      if (rc != KVX_OK) return rc;
+    }
+    hipError_t e = hipEventRecord(ly.done, x->stream);
+    if (e != hipSuccess) return fail_hip(e, "hipEventRecord(xfer done)");
+  }
+  ly.st = kIssued;
+  ly.issued_at = now;
+  x->log_req.push_back(id);
+  x->log_attempt.push_back(r.attempt);
+  x->log_layer.push_back(layer);
+  return KVX_OK;
+}
+
+// Both sides known: build the plan and issue every deferred layer in layer
+// order ([PUSH] step 2: the second of registration and prefill triggers).
+int start(kvx_xfer* x, uint64_t id, Req& r, double now) {
+  if (r.state != KVX_REQ_PENDING || !r.has_src || !r.has_dst) return KVX_OK;
+  if (!r.plan) {
+    const int64_t so[2] = {0, int64_t(r.src.size())};
+    const int64_t dof[2] = {0, int64_t(r.dst.size())};
+    int rc = kvx_plan(x->producer, r.consumer, 1, &r.ntok, so, dof, r.src.data(), r.dst.data(),
+                      x->host_only ? KVX_PLAN_HOST_ONLY : 0u, x->stream, &r.plan);
+    if (rc != KVX_OK) {
+      r.plan = nullptr;
+      r.state = KVX_REQ_FAILED;
+      release_req(x, r);
+      return rc;
+    }
+  }
+  for (auto& kv : r.layers) {
+    if (kv.second.st != kDeferred) continue;
+    int rc = issue(x, id, r, kv.first, kv.second, kv.second.gate, now);
+    if (rc != KVX_OK) return rc;
+  }
+  r.deferred_since = -1;
+  return KVX_OK;
+}
+
+void set(int32_t* p, int32_t v) {
+  if (p) *p = v;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kvx_xfer_create(const kvx_pool* producer, const kvx_xfer_config* cfg, hipStream_t stream, kvx_xfer** out) {
+  if (!producer || !out) return fail(KVX_E_INVAL, "kvx_xfer_create: null argument");
+  kvx_xfer* x = new (std::nothrow) kvx_xfer;
+  if (!x) return fail(KVX_E_NOMEM, "kvx_xfer_create: out of host memory");
+  x->producer = producer;
+  x->cfg = cfg ? *cfg : kvx_xfer_config{60.0, 30.0, 0u};
+  if (x->cfg.flags & ~KVX_XFER_HOST_ONLY) {
+    delete x;
+    return fail(KVX_E_INVAL, "kvx_xfer_create: unknown flags 0x%x", x->cfg.flags);
+  }
+  x->host_only = (x->cfg.flags & KVX_XFER_HOST_ONLY) != 0;
+  x->stream = stream;
+  *out = x;
+  return KVX_OK;
+}
+
+void kvx_xfer_destroy(kvx_xfer* x) {
+  if (!x) return;
+  if (!x->host_only) (void)hipStreamSynchronize(x->stream);
+  for (auto& kv : x->reqs) {
+    Req& r = kv.second;
+    if (r.plan) plan_free_idle(r.plan);
+    for (auto& l : r.layers) {
+      if (l.second.gate) (void)hipEventDestroy(l.second.gate);
+      if (l.second.done) (void)hipEventDestroy(l.second.done);
+    }
+  }
+  for (auto& rp : x->retired) {
+    plan_free_idle(rp.first);
+    (void)hipEventDestroy(rp.second);
+  }
+  for (hipEvent_t e : x->spare) (void)hipEventDestroy(e);
+  delete x;
+}
+
+int kvx_xfer_register(kvx_xfer* x, uint64_t id, uint32_t attempt, const kvx_pool* consumer,
+                      const int32_t* dst_ids, int64_t n, double now, int32_t* accepted) {
+  if (!x || !consumer || n < 0 || (n > 0 && !dst_ids)) return fail(KVX_E_INVAL, "kvx_xfer_register: bad argument");
+  std::lock_guard<std::mutex> lk(x->mu);
+  set(accepted, 0);
+  try {
+    Req* r = lookup(x, id, attempt, true);
+    if (!r || r->state != KVX_REQ_PENDING || r->has_dst) return KVX_OK;
+    r->dst.assign(dst_ids, dst_ids + n);
+    r->consumer = consumer;
+    r->has_dst = true;
+    set(accepted, 1);
+    return start(x, id, *r, now);
+  } catch (const std::bad_alloc&) {
+    return fail(KVX_E_NOMEM, "kvx_xfer_register: out of host memory");
+  }
+}
+
+int kvx_xfer_prefill(kvx_xfer* x, uint64_t id, uint32_t attempt, int64_t num_tokens, const int32_t* src_ids,
+                     int64_t n, double now, int32_t* accepted) {
+  if (!x || num_tokens < 0 || n < 0 || (n > 0 && !src_ids))
+    return fail(KVX_E_INVAL, "kvx_xfer_prefill: bad argument");
+  std::lock_guard<std::mutex> lk(x->mu);
+  set(accepted, 0);
+  try {
+    Req* r = lookup(x, id, attempt, true);
+    if (!r || r->state != KVX_REQ_PENDING || r->has_src) return KVX_OK;
+    r->src.assign(src_ids, src_ids + n);
+    r->ntok = num_tokens;
+    r->has_src = true;
+    set(accepted, 1);
+    return start(x, id, *r, now);
+  } catch (const std::bad_alloc&) {
+    return fail(KVX_E_NOMEM, "kvx_xfer_prefill: out of host memory");
+  }
+}
+
+int kvx_xfer_save_layer(kvx_xfer* x, uint64_t id, uint32_t attempt, int32_t layer, hipEvent_t ready, double now,
+                        int32_t* accepted) {
+  if (!x) return fail(KVX_E_INVAL, "kvx_xfer_save_layer: null argument");
+  if (layer < 0 || layer >= x->producer->g.L)
+    return fail(KVX_E_RANGE, "kvx_xfer_save_layer: layer %d outside [0,%d)", layer, x->producer->g.L);
+  std::lock_guard<std::mutex> lk(x->mu);
+  set(accepted, 0);
+  try {
+    Req* r = lookup(x, id, attempt, false);
+    if (!r || r->state != KVX_REQ_PENDING || r->sealed) return KVX_OK;
+    set(accepted, 1);
+    if (r->layers.count(layer)) return KVX_OK;
+    Layer& ly = r->layers[layer];
+    if (r->has_src && r->has_dst && r->plan) return issue(x, id, *r, layer, ly, ready, now);
+    // Deferred: capture the readiness now, so the caller may reuse `ready`.
+    ly.st = kDeferred;
+    if (r->deferred_since < 0) r->deferred_since = now;
+    if (!x->host_only && ready) {
+      hipError_t q = hipEventQuery(ready);
+      if (q == hipErrorNotReady) {
+        int rc = get_event(x, &ly.gate);
+        if (rc != KVX_OK) return rc;
+        hipError_t e = hipStreamWaitEvent(x->stream, ready, 0);
+        if (e == hipSuccess) e = hipEventRecord(ly.gate, x->stream);
+        if (e != hipSuccess) return fail_hip(e, "capture of a deferred layer's readiness");
+      } else if (q != hipSuccess) {
+        return fail_hip(q, "hipEventQuery(ready)");
+      }
+    }
+    return KVX_OK;
+  } catch (const std::bad_alloc&) {
+    return fail(KVX_E_NOMEM, "kvx_xfer_save_layer: out of host memory");
+  }
+}
+
+int kvx_xfer_seal(kvx_xfer* x, uint64_t id, uint32_t attempt, int32_t* accepted) {
+  if (!x) return fail(KVX_E_INVAL, "kvx_xfer_seal: null argument");
+  std::lock_guard<std::mutex> lk(x->mu);
+  set(accepted, 0);
+  Req* r = lookup(x, id, attempt, false);
+  if (!r || r->state != KVX_REQ_PENDING || r->sealed) return KVX_OK;
+  r->sealed = true;
+  r->expected = int64_t(r->layers.size());
+  set(accepted, 1);
+  settle(x, *r);
+  return KVX_OK;
+}
+
+int kvx_xfer_poll(kvx_xfer* x, double now) {
+  if (!x) return fail(KVX_E_INVAL, "kvx_xfer_poll: null argument");
+  std::lock_guard<std::mutex> lk(x->mu);
+  if (!x->host_only) {
+    for (auto& kv : x->reqs) {
+      for (auto& l : kv.second.layers) {
+        if (l.second.st != kIssued || !l.second.done) continue;
+        hipError_t q = hipEventQuery(l.second.done);
+        if (q == hipSuccess)
+          l.second.st = kDone;
+        else if (q != hipErrorNotReady)
+          return fail_hip(q, "hipEventQuery(xfer done)");
+      }
+    }
+    // retired plans whose last write has finished
+    for (size_t i = 0; i < x->retired.size();) {
+      hipError_t q = hipEventQuery(x->retired[i].second);
+      if (q == hipSuccess) {
+        plan_free_idle(x->retired[i].first);
+        x->spare.push_back(x->retired[i].second);
+        x->retired[i] = x->retired.back();
+        x->retired.pop_back();
+      } else {
+        ++i;
+      }
+    }
+  }
+  for (auto& kv : x->reqs) {
+    Req& r = kv.second;
+    if (r.state != KVX_REQ_PENDING) continue;
+    if (r.deferred_since >= 0 && now - r.deferred_since >= x->cfg.defer_timeout_s) {
+      r.state = KVX_REQ_EXPIRED;
+      release_req(x, r);
+      continue;
+    }
+    for (auto& l : r.layers)
+      if (l.second.st == kIssued && now - l.second.issued_at >= x->cfg.transfer_timeout_s) l.second.st = kFailed;
+    settle(x, r);
+  }
+  return KVX_OK;
+}
+
+int kvx_xfer_complete(kvx_xfer* x, uint64_t id, uint32_t attempt, int32_t layer, int32_t ok) {
+  if (!x) return fail(KVX_E_INVAL, "kvx_xfer_complete: null argument");
+  if (ok && !x->host_only)
+    return fail(KVX_E_INVAL, "kvx_xfer_complete: completion is observed by kvx_xfer_poll on the device");
+  std::lock_guard<std::mutex> lk(x->mu);
+  Req* r = lookup(x, id, attempt, false);
+  if (!r) return KVX_OK;
+  auto it = r->layers.find(layer);
+  if (it == r->layers.end() || it->second.st != kIssued) return KVX_OK;
+  it->second.st = ok ? kDone : kFailed;
+  settle(x, *r);
+  return KVX_OK;
+}
+
+int kvx_xfer_status(const kvx_xfer* x, uint64_t id, uint32_t* attempt, int32_t* state) {
+  if (!x || !attempt || !state) return fail(KVX_E_INVAL, "kvx_xfer_status: null argument");
+  std::lock_guard<std::mutex> lk(x->mu);
+  auto it = x->reqs.find(id);
+  if (it == x->reqs.end()) return fail(KVX_E_RANGE, "kvx_xfer_status: unknown request");
+  *attempt = it->second.attempt;
+  *state = it->second.state;
+  return KVX_OK;
+}
+
+int kvx_xfer_pop_finished(kvx_xfer* x, uint64_t* reqs, uint32_t* attempts, int32_t* states, int64_t cap,
+                          int64_t* n) {
+  if (!x || !n || (cap > 0 && (!reqs || !attempts || !states)))
+    return fail(KVX_E_INVAL, "kvx_xfer_pop_finished: bad argument");
+  std::lock_guard<std::mutex> lk(x->mu);
+  int64_t k = 0;
+  for (auto& kv : x->reqs) {
+    if (k >= cap) break;
+    Req& r = kv.second;
+    if (r.state == KVX_REQ_PENDING || r.reported) continue;
+    r.reported = true;
+    reqs[k] = kv.first;
+    attempts[k] = r.attempt;
+    states[k] = r.state;
+    ++k;
+  }
+  *n = k;
+  return KVX_OK;
+}
+
+int kvx_xfer_recompute_blocks(const kvx_xfer* x, uint64_t id, int32_t* out, int64_t cap, int64_t* n) {
+  if (!x || !n) return fail(KVX_E_INVAL, "kvx_xfer_recompute_blocks: null argument");
+  std::lock_guard<std::mutex> lk(x->mu);
+  auto it = x->reqs.find(id);
+  if (it == x->reqs.end()) return fail(KVX_E_RANGE, "kvx_xfer_recompute_blocks: unknown request");
+  const Req& r = it->second;
+  const bool lost = r.state == KVX_REQ_FAILED || r.state == KVX_REQ_EXPIRED;
+  const int64_t cnt = lost && r.has_dst ? int64_t(r.dst.size()) : 0;
+  if (out && cap >= cnt)
+    for (int64_t i = 0; i < cnt; ++i) out[i] = r.dst[size_t(i)];
+  *n = cnt;
+  return KVX_OK;
+}
+
+int kvx_xfer_issued(const kvx_xfer* x, int64_t first, uint64_t* reqs, uint32_t* attempts, int32_t* layers,
+                    int64_t cap, int64_t* n) {
+  if (!x || !n || first < 0 || (cap > 0 && (!reqs || !attempts || !layers)))
+    return fail(KVX_E_INVAL, "kvx_xfer_issued: bad argument");
+  std::lock_guard<std::mutex> lk(x->mu);
+  int64_t k = 0;
+  for (int64_t i = first; i < int64_t(x->log_req.size()) && k < cap; ++i, ++k) {
+    reqs[k] = x->log_req[size_t(i)];
+    attempts[k] = x->log_attempt[size_t(i)];
+    layers[k] = x->log_layer[size_t(i)];
+  }
+  *n = k;
+  return KVX_OK;
+}
+
+int kvx_xfer_forget(kvx_xfer* x, uint64_t id) {
+  if (!x) return fail(KVX_E_INVAL, "kvx_xfer_forget: null argument");
+  std::lock_guard<std::mutex> lk(x->mu);
+  auto it = x->reqs.find(id);
+  if (it == x->reqs.end()) return fail(KVX_E_RANGE, "kvx_xfer_forget: unknown request");
+  if (it->second.state == KVX_REQ_PENDING) return fail(KVX_E_INVAL, "kvx_xfer_forget: request still pending");
+  release_req(x, it->second);
+  x->reqs.erase(it);
+  return KVX_OK;
+}
+
+}  // extern "C"

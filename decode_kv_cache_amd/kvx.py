@@ -62,7 +62,30 @@ _SIGS = {
     "kvx_unpack": (C.c_int, [_P, _I32, _I32, _P, _I64, _P]),
     "kvx_copy_heads": (C.c_int, [_P, _I32, _I32, _I32, _I32, _P, _P]),
 }
+_D = C.c_double
+_U64 = C.c_uint64
+_SIGS.update({
+    "kvx_xfer_create": (C.c_int, [_P, _P, _P, C.POINTER(_P)]),
+    "kvx_xfer_destroy": (None, [_P]),
+    "kvx_xfer_register": (C.c_int, [_P, _U64, _U32, _P, _P, _I64, _D, C.POINTER(_I32)]),
+    "kvx_xfer_prefill": (C.c_int, [_P, _U64, _U32, _I64, _P, _I64, _D, C.POINTER(_I32)]),
+    "kvx_xfer_save_layer": (C.c_int, [_P, _U64, _U32, _I32, _P, _D, C.POINTER(_I32)]),
+    "kvx_xfer_seal": (C.c_int, [_P, _U64, _U32, C.POINTER(_I32)]),
+    "kvx_xfer_poll": (C.c_int, [_P, _D]),
+    "kvx_xfer_complete": (C.c_int, [_P, _U64, _U32, _I32, _I32]),
+    "kvx_xfer_status": (C.c_int, [_P, _U64, C.POINTER(_U32), C.POINTER(_I32)]),
+    "kvx_xfer_pop_finished": (C.c_int, [_P, _P, _P, _P, _I64, C.POINTER(_I64)]),
+    "kvx_xfer_recompute_blocks": (C.c_int, [_P, _U64, _P, _I64, C.POINTER(_I64)]),
+    "kvx_xfer_issued": (C.c_int, [_P, _I64, _P, _P, _P, _I64, C.POINTER(_I64)]),
+    "kvx_xfer_forget": (C.c_int, [_P, _U64]),
+})
 EXPORTED = tuple(_SIGS)
+KVX_REQ_PENDING, KVX_REQ_DONE, KVX_REQ_FAILED, KVX_REQ_EXPIRED = range(4)
+KVX_XFER_HOST_ONLY = 1
+
+
+class kvx_xfer_config(C.Structure):
+    _fields_ = [("defer_timeout_s", C.c_double), ("transfer_timeout_s", C.c_double), ("flags", C.c_uint32)]
 
 _lib = None
 
@@ -280,3 +303,89 @@ def kvx_copy_heads(plan: Plan, layer: int, src_head0: int, dst_head0: int, num_h
                    ready=None, stream=None) -> None:
     _check("kvx_copy_heads", lib().kvx_copy_heads(plan.handle, layer, src_head0, dst_head0, num_heads,
                                                   _event(ready), _stream(stream)))
+
+
+class Xfer:
+    """Owns a kvx_xfer handle: the transfer state machine of kvx_xfer.h.
+    Methods return the C call's `accepted` flag where it has one."""
+
+    def __init__(self, producer: Pool, *, defer_timeout: float = 60.0, transfer_timeout: float = 30.0,
+                 host_only: bool = False, stream=None):
+        cfg = kvx_xfer_config(defer_timeout, transfer_timeout, KVX_XFER_HOST_ONLY if host_only else 0)
+        h = C.c_void_p()
+        st = None if host_only else _stream(stream)
+        _check("kvx_xfer_create", lib().kvx_xfer_create(producer.handle, C.byref(cfg), st, C.byref(h)))
+        self.handle, self.producer = h, producer
+        self._consumers = {}   # the C side keeps pool pointers: keep the Pool objects alive
+
+    def _acc(self, name, *args) -> bool:
+        acc = C.c_int32(-1)
+        _check(name, getattr(lib(), name)(self.handle, *args, C.byref(acc)))
+        return bool(acc.value)
+
+    def register(self, req: int, attempt: int, consumer: Pool, dst_ids, now: float) -> bool:
+        a = np.ascontiguousarray(dst_ids, np.int32)
+        self._consumers[id(consumer)] = consumer
+        return self._acc("kvx_xfer_register", req, attempt, consumer.handle, a.ctypes.data if a.size else None,
+                         a.size, now)
+
+    def prefill(self, req: int, attempt: int, num_tokens: int, src_ids, now: float) -> bool:
+        a = np.ascontiguousarray(src_ids, np.int32)
+        return self._acc("kvx_xfer_prefill", req, attempt, num_tokens, a.ctypes.data if a.size else None, a.size, now)
+
+    def save_layer(self, req: int, attempt: int, layer: int, now: float, ready=None) -> bool:
+        return self._acc("kvx_xfer_save_layer", req, attempt, layer, _event(ready), now)
+
+    def seal(self, req: int, attempt: int) -> bool:
+        return self._acc("kvx_xfer_seal", req, attempt)
+
+    def poll(self, now: float) -> None:
+        _check("kvx_xfer_poll", lib().kvx_xfer_poll(self.handle, now))
+
+    def complete(self, req: int, attempt: int, layer: int, ok: bool = True) -> None:
+        _check("kvx_xfer_complete", lib().kvx_xfer_complete(self.handle, req, attempt, layer, int(ok)))
+
+    def status(self, req: int):
+        a, st = C.c_uint32(), C.c_int32()
+        rc = lib().kvx_xfer_status(self.handle, req, C.byref(a), C.byref(st))
+        if rc == KVX_E_RANGE:
+            return None
+        _check("kvx_xfer_status", rc)
+        return a.value, st.value
+
+    def pop_finished(self, cap: int = 1024):
+        r = (C.c_uint64 * cap)()
+        a = (C.c_uint32 * cap)()
+        st = (C.c_int32 * cap)()
+        n = C.c_int64()
+        _check("kvx_xfer_pop_finished", lib().kvx_xfer_pop_finished(self.handle, r, a, st, cap, C.byref(n)))
+        return [(r[i], a[i], st[i]) for i in range(n.value)]
+
+    def recompute_blocks(self, req: int):
+        n = C.c_int64()
+        rc = lib().kvx_xfer_recompute_blocks(self.handle, req, None, 0, C.byref(n))
+        if rc == KVX_E_RANGE:
+            return None
+        _check("kvx_xfer_recompute_blocks", rc)
+        out = (C.c_int32 * max(n.value, 1))()
+        _check("kvx_xfer_recompute_blocks", lib().kvx_xfer_recompute_blocks(self.handle, req, out, n.value,
+                                                                            C.byref(n)))
+        return list(out[:n.value])
+
+    def issued(self, first: int = 0, cap: int = 1 << 16):
+        r = (C.c_uint64 * cap)()
+        a = (C.c_uint32 * cap)()
+        ly = (C.c_int32 * cap)()
+        n = C.c_int64()
+        _check("kvx_xfer_issued", lib().kvx_xfer_issued(self.handle, first, r, a, ly, cap, C.byref(n)))
+        return [(r[i], a[i], ly[i]) for i in range(n.value)]
+
+    def forget(self, req: int) -> None:
+        _check("kvx_xfer_forget", lib().kvx_xfer_forget(self.handle, req))
+
+    def close(self):
+        if getattr(self, "handle", None):
+            lib().kvx_xfer_destroy(self.handle)
+            self.handle = None
+
+    __del__ = close

@@ -195,6 +195,14 @@ class XferModel:
                 out.append((rid, r.attempt, r.state))
         return out
 
+    def forget(self, rid: int) -> bool:
+        """Drop a finished request's record."""
+        r = self.reqs.get(rid)
+        if r is None or r.state == PENDING:
+            return False
+        del self.reqs[rid]
+        return True
+
     def recompute_blocks(self, rid: int) -> List[int]:
         """Destination blocks the consumer has to recompute ([MORI] §3.1)."""
         r = self.reqs.get(rid)

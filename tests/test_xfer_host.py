@@ -1,0 +1,115 @@
+"""The native transfer state machine (kvx_xfer_*, host-only mode) against the
+oracle model on random event sequences: same issued writes in the same order,
+same request states, finished reports and recompute lists after every event."""
+import numpy as np
+import pytest
+
+from decode_kv_cache_amd import kvx
+from decode_kv_cache_amd import workloads as W
+from oracle import xfer_model as X
+from test_abi_host import fake_pool
+
+STATE = {kvx.KVX_REQ_PENDING: X.PENDING, kvx.KVX_REQ_DONE: X.DONE, kvx.KVX_REQ_FAILED: X.FAILED,
+         kvx.KVX_REQ_EXPIRED: X.EXPIRED}
+SPEC = W.PoolSpec(4, 64, 4, 1, 16, W.U8)
+
+
+def run_sequence(seed, steps=300, ids=(1, 2, 3, 4, 5)):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    prod, cons = fake_pool(SPEC, 0), fake_pool(SPEC, 1)
+    defer_t, xfer_t = float(rng.choice([5.0, 20.0])), float(rng.choice([3.0, 10.0]))
+    nat = kvx.Xfer(prod, defer_timeout=defer_t, transfer_timeout=xfer_t, host_only=True)
+    mod = X.XferModel(defer_timeout=defer_t, transfer_timeout=xfer_t)
+    now = 0.0
+    seen = set()
+    attempts = {i: 0 for i in ids}
+    for step in range(steps):
+        rid = int(rng.choice(ids))
+        att = attempts[rid] + int(rng.choice([0, 0, 0, 0, 0, 1, -1])) if attempts[rid] > 0 else \
+            attempts[rid] + int(rng.choice([0, 0, 0, 0, 1]))
+        att = max(att, 0)
+        attempts[rid] = max(attempts[rid], att)
+        op = rng.choice(["register", "prefill", "save", "save", "save", "seal", "complete", "complete",
+                         "fail", "tick", "pop", "forget"])
+        if op == "register":
+            ids_d = (rng.permutation(64)[:3]).astype(np.int32)
+            a = nat.register(rid, att, cons, ids_d, now)
+            b = mod.register(rid, att, ids_d, now)
+        elif op == "prefill":
+            ids_s = (rng.permutation(64)[:3]).astype(np.int32)
+            n = int(rng.integers(0, 13))
+            a = nat.prefill(rid, att, n, ids_s, now)
+            b = mod.prefill(rid, att, n, ids_s, now)
+        elif op == "save":
+            layer = int(rng.integers(0, 4))
+            a = nat.save_layer(rid, att, layer, now)
+            b = mod.save_layer(rid, att, layer, now)
+        elif op == "seal":
+            a, b = nat.seal(rid, att), mod.seal(rid, att)
+        elif op in ("complete", "fail"):
+            issued = [e for e in mod.issued if e[0] == rid]
+            if not issued:
+                continue
+            _, at2, layer = issued[int(rng.integers(0, len(issued)))]
+            nat.complete(rid, at2, layer, ok=(op == "complete"))
+            (mod.complete if op == "complete" else mod.fail)(rid, at2, layer)
+            a = b = None
+        elif op == "tick":
+            now += float(rng.choice([0.5, 1.0, 4.0, 8.0]))
+            nat.poll(now)
+            mod.tick(now)
+            a = b = None
+        elif op == "pop":
+            a = [(r, at2, STATE[s]) for r, at2, s in nat.pop_finished()]
+            b = mod.pop_finished()
+            seen |= {s for _, _, s in b}
+        else:
+            st = mod.status(rid)
+            if st is None or st[1] == X.PENDING:
+                continue
+            nat.forget(rid)
+            mod.forget(rid)
+            a = b = None
+        assert a == b, (seed, step, op, rid, att, a, b)
+        assert nat.issued() == mod.issued, (seed, step, op)
+        for i in ids:
+            s_nat, s_mod = nat.status(i), mod.status(i)
+            assert (None if s_nat is None else (s_nat[0], STATE[s_nat[1]])) == s_mod, (seed, step, i)
+            r_nat = nat.recompute_blocks(i)
+            assert (r_nat or []) == mod.recompute_blocks(i), (seed, step, i)
+    nat.close()
+    return len(mod.issued), {r.state for r in mod.reqs.values()} | seen
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_native_matches_model(seed):
+    run_sequence(seed)
+
+
+def test_sequences_exercise_every_outcome():
+    """The random sequences issue writes and reach DONE, FAILED and EXPIRED."""
+    outcomes, issued = set(), 0
+    for seed in range(40):
+        n, seen = run_sequence(seed, steps=300)
+        issued += n
+        outcomes |= seen
+    assert {X.DONE, X.FAILED, X.EXPIRED} <= outcomes
+    assert issued > 100
+
+
+def test_native_errors():
+    prod = fake_pool(SPEC, 0)
+    x = kvx.Xfer(prod, host_only=True)
+    with pytest.raises(kvx.KvxError) as e:
+        x.save_layer(1, 0, 4, 0.0)           # layer out of range
+    assert e.value.code == kvx.KVX_E_RANGE
+    assert not x.save_layer(1, 0, 0, 0.0)    # unknown request: ignored
+    assert x.status(9) is None
+    x.register(1, 0, fake_pool(SPEC, 1), [70, 71], 0.0)   # IDs outside the consumer pool
+    with pytest.raises(kvx.KvxError) as e:
+        x.prefill(1, 0, 4, [1], 0.0)         # rendezvous builds the plan: range error, request failed
+    assert e.value.code == kvx.KVX_E_RANGE
+    assert x.status(1) == (0, kvx.KVX_REQ_FAILED)
+    with pytest.raises(kvx.KvxError):
+        x.forget(2)
+    x.close()
