@@ -18,6 +18,8 @@ Other workloads (--workload), one JSON line each:
                  the decode side's retained prefix back to the prefill pool
   pack_unpack    the default workload through a contiguous staging buffer
   qwen32b_reblock  the default KV with 64-slot consumer blocks (16-slot producer)
+  xfer_pipeline  batched_push's requests driven through the transfer state
+                 machine (kvx_xfer), layer by layer
   tiny_push      2 layers, one 200-token prompt (launch-bound; no claim)
 
 Prints ONE JSON line on stdout.  Everything else goes to stderr.
@@ -43,7 +45,7 @@ HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, AMD published peak
 PROFILES = os.path.join(ROOT, "profiles")
 CALIB_BYTES = 1 << 30
 WORKLOAD_NAMES = ["qwen32b_push", "batched_push", "tp4_share", "multiturn_fp8", "pack_unpack", "qwen32b_reblock",
-                  "tiny_push"]
+                  "xfer_pipeline", "tiny_push"]
 
 
 def log(*a):
@@ -595,6 +597,96 @@ def bench_pack(args, torch, kvx, S, W):
     }
 
 
+def bench_xfer(args, torch, kvx, S, W):
+    """xfer_pipeline: batched_push's 64 requests driven through the transfer
+    state machine: all requests prefilled, half registered up front and half
+    after the forward pass (deferred writes); per layer one synthetic compute
+    kernel then one save of that layer for all requests with the layer's
+    event; seal; poll until every request is done.  Compared with the same
+    bytes moved by one multi-request plan per layer."""
+    from decode_kv_cache_amd import bench_support as B
+    wl = W.batched_push()
+    gs, gd = S.device_side(wl.src, wl.seed, 1), S.device_side(wl.dst, wl.seed, 2)
+    tokens = [kvx.kvx_tokens_to_move(p, 0) for p in wl.prompt_lens]
+    R, L = len(tokens), wl.src.num_layers
+    side = torch.cuda.Stream()
+    compute = torch.cuda.current_stream()
+    sink = torch.empty(256 * 256, dtype=torch.float32, device="cuda")
+    bb = wl.src.block_size * wl.src.num_heads * wl.src.head_dim * wl.src.elem_bytes
+    ref = kvx.kvx_plan(gs.pool, gd.pool, tokens, wl.src_tables, wl.dst_tables, stream=side)
+    step_bytes = sum(ref.bytes_per_layer()) * L
+
+    def run(step_no):
+        x = kvx.Xfer(gs.pool, stream=side)
+        t_host = 0.0
+        now = float(step_no)
+        for r in range(R):
+            if r % 2 == 0:
+                x.register(r, 0, gd.pool, wl.dst_tables[r], now)
+            x.prefill(r, 0, tokens[r], wl.src_tables[r], now)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record(compute)
+        side.wait_event(a)
+        for l in range(L):
+            B.layer_compute(sink, 1000, 64, stream=compute)
+            ev = torch.cuda.Event()
+            ev.record(compute)
+            t0 = time.perf_counter()
+            x.save_layer_many(l, range(R), [0] * R, now, ready=ev)
+            t_host += time.perf_counter() - t0
+        for r in range(R):
+            x.seal(r, 0)
+        t0 = time.perf_counter()
+        for r in range(1, R, 2):
+            x.register(r, 0, gd.pool, wl.dst_tables[r], now)
+        t_host += time.perf_counter() - t0
+        j = torch.cuda.Event()
+        j.record(side)
+        compute.wait_event(j)
+        b.record(compute)
+        done = 0
+        for _ in range(100):
+            x.poll(now)
+            done += len(x.pop_finished())
+            if done == R:
+                break
+            torch.cuda.synchronize()
+        if done != R:
+            raise RuntimeError(f"xfer pipeline: {R - done} requests did not finish")
+        ms = a.elapsed_time(b)
+        x.close()
+        return ms, t_host
+
+    run(0)
+    res = [run(i + 1) for i in range(args.steps)]
+    ms = float(np.mean([r[0] for r in res]))
+    host_us = float(np.mean([r[1] for r in res])) * 1e6 / (R * L)
+    gbs = step_bytes / (ms * 1e-3) / 1e9
+    # same bytes through one multi-request plan per layer, no state machine
+    for l in range(L):
+        kvx.kvx_push_layer(ref, l, stream=side)
+    with Timer(torch, side) as t:
+        for _ in range(args.steps):
+            for l in range(L):
+                kvx.kvx_push_layer(ref, l, stream=side)
+    raw = step_bytes / (t.ms / args.steps * 1e-3) / 1e9
+    log(f"xfer pipeline: {ms:.2f} ms per step, {gbs:.1f} GB/s; host {host_us:.2f} us per (request, layer) saved; "
+        f"one plan per layer without the state machine: {raw:.1f} GB/s")
+    ref.close()
+    return {
+        "value": gbs, "ms_per_step": ms, "dtype": "u8",
+        "config": {"workload": "xfer_pipeline", "geometry": "batched_push", "requests": R, "layers": L,
+                   "bytes_per_step": step_bytes,
+                   "step": f"{R} requests x {L} layers through kvx_xfer (half registered after the forward pass), "
+                           f"one synthetic compute kernel per layer",
+                   "host_us_per_save": round(host_us, 3), "one_plan_per_layer_GBs": round(raw, 1)},
+        "roofline": roofline(step_bytes // (R * L), ms * 1e3 / (R * L), "kvx::copy_kernel<0> via kvx_xfer",
+                             "xfer_pipeline", {"note": "per (request, layer) write, span of the whole step"}),
+        "cpu_baseline": None,
+    }
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -625,7 +717,7 @@ def main():
     log(f"device: {dev.name} {getattr(dev, 'gcnArchName', '')} CUs={dev.multi_processor_count} "
         f"mem={dev.total_memory / 2**30:.0f} GiB; workload {args.workload}")
     fn = {"qwen32b_push": bench_push, "tiny_push": bench_push, "qwen32b_reblock": bench_push,
-          "batched_push": bench_batched,
+          "batched_push": bench_batched, "xfer_pipeline": bench_xfer,
           "tp4_share": bench_tp4, "multiturn_fp8": bench_multiturn, "pack_unpack": bench_pack}[args.workload]
     if args.counters and fn is not bench_push:
         print("bench.py: --counters is for the push workloads", file=sys.stderr)

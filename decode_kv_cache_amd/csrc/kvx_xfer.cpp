@@ -4,6 +4,13 @@
 // Sources: [PUSH] push-based NIXL connector post, "Implementierungsdetails"
 // steps 1-3; [MORI] MoRIIO connector note §3.1, §3.2, §6 (full titles in
 // kvx.h; the readings taken are listed in kvx_xfer.h).
+//
+// Device-side bookkeeping keeps queue packets few: a layer save for many
+// requests waits on the layer's event once (later writes on the same stream
+// are ordered after it); deferred writes of one save share one captured
+// "gate" event; completion of issued writes is observed through one "mark"
+// event recorded per poll behind every write issued since the previous poll
+// (writes on one stream finish in order).
 
 #include <hip/hip_runtime_api.h>
 
@@ -24,8 +31,7 @@ enum LayerState : int8_t { kDeferred = 0, kIssued = 1, kDone = 2, kFailed = 3 };
 struct Layer {
   LayerState st = kDeferred;
   double issued_at = 0;
-  hipEvent_t gate = nullptr;  // captured readiness of a deferred write (device mode)
-  hipEvent_t done = nullptr;  // recorded after the write (device mode)
+  int32_t gate = -1;  // shared captured readiness of a deferred write (device mode)
 };
 
 struct Req {
@@ -43,6 +49,18 @@ struct Req {
   kvx_plan_t* plan = nullptr;
 };
 
+struct WriteRef {
+  uint64_t id;
+  uint32_t attempt;
+  int32_t layer;
+};
+
+// A reference-counted event slot.
+struct Sig {
+  hipEvent_t ev = nullptr;
+  int32_t refs = 0;
+};
+
 }  // namespace
 
 struct kvx_xfer_s {
@@ -51,39 +69,64 @@ struct kvx_xfer_s {
   hipStream_t stream = nullptr;
   bool host_only = false;
   std::map<uint64_t, Req> reqs;
-  std::vector<uint64_t> log_req;
-  std::vector<uint32_t> log_attempt;
-  std::vector<int32_t> log_layer;
-  std::vector<hipEvent_t> spare;  // recycled events
-  // plans of finished requests waiting for their enqueued work to finish
-  std::vector<std::pair<kvx_plan_t*, hipEvent_t>> retired;
+  std::vector<WriteRef> log;
+  std::vector<Sig> sigs;
+  std::vector<int32_t> free_sigs;
+  std::vector<WriteRef> unmarked;                                  // issued since the last mark
+  std::vector<std::pair<int32_t, std::vector<WriteRef>>> marks;    // mark -> writes it covers
+  std::vector<std::pair<kvx_plan_t*, int32_t>> retired;            // plan freed when the mark fires
   mutable std::mutex mu;
 };
 
 namespace {
 
-int get_event(kvx_xfer* x, hipEvent_t* ev) {
-  if (!x->spare.empty()) {
-    *ev = x->spare.back();
-    x->spare.pop_back();
-    return KVX_OK;
+int sig_new(kvx_xfer* x, int32_t* idx) {
+  int32_t i;
+  if (!x->free_sigs.empty()) {
+    i = x->free_sigs.back();
+    x->free_sigs.pop_back();
+  } else {
+    x->sigs.push_back(Sig{});
+    i = int32_t(x->sigs.size() - 1);
   }
-  hipError_t e = hipEventCreateWithFlags(ev, hipEventDisableTiming);
-  return e == hipSuccess ? KVX_OK : fail_hip(e, "hipEventCreate(xfer)");
+  Sig& s = x->sigs[size_t(i)];
+  if (!s.ev) {
+    hipError_t e = hipEventCreateWithFlags(&s.ev, hipEventDisableTiming);
+    if (e != hipSuccess) {
+      s.ev = nullptr;
+      x->free_sigs.push_back(i);
+      return fail_hip(e, "hipEventCreate(xfer)");
+    }
+  }
+  s.refs = 1;
+  *idx = i;
+  return KVX_OK;
 }
 
-// Find the request for (req, attempt): nullptr for a stale attempt; a newer
-// attempt starts from a fresh record ([PUSH] step 2: re-sent and retried
-// requests map to the right state).
-Req* lookup(kvx_xfer* x, uint64_t id, uint32_t attempt, bool create);
+// Record a new signal behind everything enqueued on the stream so far.
+int sig_mark(kvx_xfer* x, int32_t* idx) {
+  int rc = sig_new(x, idx);
+  if (rc != KVX_OK) return rc;
+  hipError_t e = hipEventRecord(x->sigs[size_t(*idx)].ev, x->stream);
+  if (e != hipSuccess) {
+    x->sigs[size_t(*idx)].refs = 0;
+    x->free_sigs.push_back(*idx);
+    return fail_hip(e, "hipEventRecord(xfer)");
+  }
+  return KVX_OK;
+}
 
-// A request finished or was replaced: recycle its events and retire its
-// plan.  Its layer states stay for status queries.
+void sig_unref(kvx_xfer* x, int32_t idx) {
+  if (idx < 0) return;
+  if (--x->sigs[size_t(idx)].refs == 0) x->free_sigs.push_back(idx);
+}
+
+// A request finished or was replaced: drop its gates and retire its plan.
+// Its layer states stay for status queries.
 void release_req(kvx_xfer* x, Req& r) {
   for (auto& kv : r.layers) {
-    if (kv.second.gate) x->spare.push_back(kv.second.gate);
-    if (kv.second.done) x->spare.push_back(kv.second.done);
-    kv.second.gate = kv.second.done = nullptr;
+    sig_unref(x, kv.second.gate);
+    kv.second.gate = -1;
   }
   if (!r.plan) return;
   if (x->host_only) {
@@ -92,9 +135,9 @@ void release_req(kvx_xfer* x, Req& r) {
     // Work already enqueued on the stream (the plan upload, issued writes)
     // may still read the plan's descriptors: free it once a mark recorded
     // behind that work has fired.
-    hipEvent_t mark = nullptr;
-    if (get_event(x, &mark) == KVX_OK && hipEventRecord(mark, x->stream) == hipSuccess) {
-      x->retired.emplace_back(r.plan, mark);
+    int32_t m = -1;
+    if (sig_mark(x, &m) == KVX_OK) {
+      x->retired.emplace_back(r.plan, m);
     } else {
       (void)hipStreamSynchronize(x->stream);
       plan_free_idle(r.plan);
@@ -103,6 +146,9 @@ void release_req(kvx_xfer* x, Req& r) {
   r.plan = nullptr;
 }
 
+// Find the request for (req, attempt): nullptr for a stale attempt; a newer
+// attempt starts from a fresh record ([PUSH] step 2: re-sent and retried
+// requests map to the right state).
 Req* lookup(kvx_xfer* x, uint64_t id, uint32_t attempt, bool create) {
   auto it = x->reqs.find(id);
   if (it != x->reqs.end() && attempt < it->second.attempt) return nullptr;
@@ -117,6 +163,7 @@ Req* lookup(kvx_xfer* x, uint64_t id, uint32_t attempt, bool create) {
   return &it->second;
 }
 
+// The outcome over every layer batch ([MORI] §6).
 void settle(kvx_xfer* x, Req& r) {
   if (r.state != KVX_REQ_PENDING) return;
   int64_t done = 0;
@@ -132,24 +179,17 @@ void settle(kvx_xfer* x, Req& r) {
   if (r.state != KVX_REQ_PENDING) release_req(x, r);
 }
 
-// Issue one layer's write: kvx_push_layer gated on the layer's readiness,
-// then a completion event (device mode); host-only mode only logs it.
+// Issue one layer's write: kvx_push_layer gated on `ready` (device mode);
+// host-only mode only logs it.
 int issue(kvx_xfer* x, uint64_t id, Req& r, int32_t layer, Layer& ly, hipEvent_t ready, double now) {
   if (!x->host_only) {
     int rc = kvx_push_layer(r.plan, layer, ready, x->stream);
     if (rc != KVX_OK) return rc;
-    if (!ly.done) {
-      rc = get_event(x, &ly.done);
-      if (rc != KVX_OK) return rc;
-    }
-    hipError_t e = hipEventRecord(ly.done, x->stream);
-    if (e != hipSuccess) return fail_hip(e, "hipEventRecord(xfer done)");
+    x->unmarked.push_back(WriteRef{id, r.attempt, layer});
   }
   ly.st = kIssued;
   ly.issued_at = now;
-  x->log_req.push_back(id);
-  x->log_attempt.push_back(r.attempt);
-  x->log_layer.push_back(layer);
+  x->log.push_back(WriteRef{id, r.attempt, layer});
   return KVX_OK;
 }
 
@@ -171,7 +211,8 @@ int start(kvx_xfer* x, uint64_t id, Req& r, double now) {
   }
   for (auto& kv : r.layers) {
     if (kv.second.st != kDeferred) continue;
-    int rc = issue(x, id, r, kv.first, kv.second, kv.second.gate, now);
+    hipEvent_t gate = kv.second.gate >= 0 ? x->sigs[size_t(kv.second.gate)].ev : nullptr;
+    int rc = issue(x, id, r, kv.first, kv.second, gate, now);
     if (rc != KVX_OK) return rc;
   }
   r.deferred_since = -1;
@@ -180,6 +221,60 @@ int start(kvx_xfer* x, uint64_t id, Req& r, double now) {
 
 void set(int32_t* p, int32_t v) {
   if (p) *p = v;
+}
+
+int save_many(kvx_xfer* x, int32_t layer, hipEvent_t ready, int64_t n, const uint64_t* ids,
+              const uint32_t* attempts, double now, int32_t* accepted) {
+  // Classify first, so that the stream waits on `ready` once and the
+  // deferred writes share one captured gate.
+  std::vector<Req*> take(size_t(n), nullptr);
+  int64_t n_issue = 0, n_defer = 0;
+  for (int64_t i = 0; i < n; ++i) {
+    set(accepted ? accepted + i : nullptr, 0);
+    Req* r = lookup(x, ids[i], attempts[i], false);
+    if (!r || r->state != KVX_REQ_PENDING || r->sealed) continue;
+    set(accepted ? accepted + i : nullptr, 1);
+    if (r->layers.count(layer)) continue;
+    for (int64_t j = 0; j < i; ++j)  // the same request twice in one call counts once
+      if (take[size_t(j)] == r) r = nullptr;
+    if (!r) continue;
+    take[size_t(i)] = r;
+    if (r->plan)
+      ++n_issue;
+    else
+      ++n_defer;
+  }
+  int32_t gate = -1;
+  if (!x->host_only && ready && (n_issue || n_defer)) {
+    hipError_t q = hipEventQuery(ready);
+    if (q == hipErrorNotReady) {
+      hipError_t e = hipStreamWaitEvent(x->stream, ready, 0);
+      if (e != hipSuccess) return fail_hip(e, "hipStreamWaitEvent(ready)");
+      if (n_defer) {
+        // Capture the readiness now, so the caller may reuse `ready`.
+        int rc = sig_mark(x, &gate);
+        if (rc != KVX_OK) return rc;
+        x->sigs[size_t(gate)].refs = int32_t(n_defer);
+      }
+    } else if (q != hipSuccess) {
+      return fail_hip(q, "hipEventQuery(ready)");
+    }
+  }
+  for (int64_t i = 0; i < n; ++i) {
+    Req* r = take[size_t(i)];
+    if (!r) continue;
+    Layer& ly = r->layers[layer];
+    if (r->plan) {
+      // stream order already follows `ready`
+      int rc = issue(x, ids[i], *r, layer, ly, nullptr, now);
+      if (rc != KVX_OK) return rc;
+    } else {
+      ly.st = kDeferred;
+      ly.gate = gate;
+      if (r->deferred_since < 0) r->deferred_since = now;
+    }
+  }
+  return KVX_OK;
 }
 
 }  // namespace
@@ -205,19 +300,11 @@ int kvx_xfer_create(const kvx_pool* producer, const kvx_xfer_config* cfg, hipStr
 void kvx_xfer_destroy(kvx_xfer* x) {
   if (!x) return;
   if (!x->host_only) (void)hipStreamSynchronize(x->stream);
-  for (auto& kv : x->reqs) {
-    Req& r = kv.second;
-    if (r.plan) plan_free_idle(r.plan);
-    for (auto& l : r.layers) {
-      if (l.second.gate) (void)hipEventDestroy(l.second.gate);
-      if (l.second.done) (void)hipEventDestroy(l.second.done);
-    }
-  }
-  for (auto& rp : x->retired) {
-    plan_free_idle(rp.first);
-    (void)hipEventDestroy(rp.second);
-  }
-  for (hipEvent_t e : x->spare) (void)hipEventDestroy(e);
+  for (auto& kv : x->reqs)
+    if (kv.second.plan) plan_free_idle(kv.second.plan);
+  for (auto& rp : x->retired) plan_free_idle(rp.first);
+  for (Sig& s : x->sigs)
+    if (s.ev) (void)hipEventDestroy(s.ev);
   delete x;
 }
 
@@ -260,34 +347,17 @@ int kvx_xfer_prefill(kvx_xfer* x, uint64_t id, uint32_t attempt, int64_t num_tok
 
 int kvx_xfer_save_layer(kvx_xfer* x, uint64_t id, uint32_t attempt, int32_t layer, hipEvent_t ready, double now,
                         int32_t* accepted) {
-  if (!x) return fail(KVX_E_INVAL, "kvx_xfer_save_layer: null argument");
+  return kvx_xfer_save_layer_many(x, layer, ready, 1, &id, &attempt, now, accepted);
+}
+
+int kvx_xfer_save_layer_many(kvx_xfer* x, int32_t layer, hipEvent_t ready, int64_t n, const uint64_t* reqs,
+                             const uint32_t* attempts, double now, int32_t* accepted) {
+  if (!x || n < 0 || (n > 0 && (!reqs || !attempts))) return fail(KVX_E_INVAL, "kvx_xfer_save_layer: bad argument");
   if (layer < 0 || layer >= x->producer->g.L)
     return fail(KVX_E_RANGE, "kvx_xfer_save_layer: layer %d outside [0,%d)", layer, x->producer->g.L);
   std::lock_guard<std::mutex> lk(x->mu);
-  set(accepted, 0);
   try {
-    Req* r = lookup(x, id, attempt, false);
-    if (!r || r->state != KVX_REQ_PENDING || r->sealed) return KVX_OK;
-    set(accepted, 1);
-    if (r->layers.count(layer)) return KVX_OK;
-    Layer& ly = r->layers[layer];
-    if (r->has_src && r->has_dst && r->plan) return issue(x, id, *r, layer, ly, ready, now);
-    // Deferred: capture the readiness now, so the caller may reuse `ready`.
-    ly.st = kDeferred;
-    if (r->deferred_since < 0) r->deferred_since = now;
-    if (!x->host_only && ready) {
-      hipError_t q = hipEventQuery(ready);
-      if (q == hipErrorNotReady) {
-        int rc = get_event(x, &ly.gate);
-        if (rc != KVX_OK) return rc;
-        hipError_t e = hipStreamWaitEvent(x->stream, ready, 0);
-        if (e == hipSuccess) e = hipEventRecord(ly.gate, x->stream);
-        if (e != hipSuccess) return fail_hip(e, "capture of a deferred layer's readiness");
-      } else if (q != hipSuccess) {
-        return fail_hip(q, "hipEventQuery(ready)");
-      }
-    }
-    return KVX_OK;
+    return save_many(x, layer, ready, n, reqs, attempts, now, accepted);
   } catch (const std::bad_alloc&) {
     return fail(KVX_E_NOMEM, "kvx_xfer_save_layer: out of host memory");
   }
@@ -309,43 +379,65 @@ int kvx_xfer_seal(kvx_xfer* x, uint64_t id, uint32_t attempt, int32_t* accepted)
 int kvx_xfer_poll(kvx_xfer* x, double now) {
   if (!x) return fail(KVX_E_INVAL, "kvx_xfer_poll: null argument");
   std::lock_guard<std::mutex> lk(x->mu);
-  if (!x->host_only) {
+  try {
+    if (!x->host_only) {
+      // marks that fired: every write behind them is done
+      for (size_t i = 0; i < x->marks.size();) {
+        hipError_t q = hipEventQuery(x->sigs[size_t(x->marks[i].first)].ev);
+        if (q == hipErrorNotReady) {
+          ++i;
+          continue;
+        }
+        if (q != hipSuccess) return fail_hip(q, "hipEventQuery(xfer mark)");
+        for (const WriteRef& w : x->marks[i].second) {
+          auto it = x->reqs.find(w.id);
+          if (it == x->reqs.end() || it->second.attempt != w.attempt) continue;
+          auto ly = it->second.layers.find(w.layer);
+          if (ly != it->second.layers.end() && ly->second.st == kIssued) ly->second.st = kDone;
+        }
+        sig_unref(x, x->marks[i].first);
+        x->marks[i] = std::move(x->marks.back());
+        x->marks.pop_back();
+      }
+      // one mark behind the writes issued since the previous poll
+      if (!x->unmarked.empty()) {
+        int32_t m = -1;
+        int rc = sig_mark(x, &m);
+        if (rc != KVX_OK) return rc;
+        x->marks.emplace_back(m, std::move(x->unmarked));
+        x->unmarked.clear();
+      }
+      // retired plans whose enqueued work has finished
+      for (size_t i = 0; i < x->retired.size();) {
+        hipError_t q = hipEventQuery(x->sigs[size_t(x->retired[i].second)].ev);
+        if (q == hipSuccess) {
+          plan_free_idle(x->retired[i].first);
+          sig_unref(x, x->retired[i].second);
+          x->retired[i] = x->retired.back();
+          x->retired.pop_back();
+        } else if (q == hipErrorNotReady) {
+          ++i;
+        } else {
+          return fail_hip(q, "hipEventQuery(xfer retired plan)");
+        }
+      }
+    }
     for (auto& kv : x->reqs) {
-      for (auto& l : kv.second.layers) {
-        if (l.second.st != kIssued || !l.second.done) continue;
-        hipError_t q = hipEventQuery(l.second.done);
-        if (q == hipSuccess)
-          l.second.st = kDone;
-        else if (q != hipErrorNotReady)
-          return fail_hip(q, "hipEventQuery(xfer done)");
+      Req& r = kv.second;
+      if (r.state != KVX_REQ_PENDING) continue;
+      if (r.deferred_since >= 0 && now - r.deferred_since >= x->cfg.defer_timeout_s) {
+        r.state = KVX_REQ_EXPIRED;
+        release_req(x, r);
+        continue;
       }
+      for (auto& l : r.layers)
+        if (l.second.st == kIssued && now - l.second.issued_at >= x->cfg.transfer_timeout_s) l.second.st = kFailed;
+      settle(x, r);
     }
-    // retired plans whose last write has finished
-    for (size_t i = 0; i < x->retired.size();) {
-      hipError_t q = hipEventQuery(x->retired[i].second);
-      if (q == hipSuccess) {
-        plan_free_idle(x->retired[i].first);
-        x->spare.push_back(x->retired[i].second);
-        x->retired[i] = x->retired.back();
-        x->retired.pop_back();
-      } else {
-        ++i;
-      }
-    }
+    return KVX_OK;
+  } catch (const std::bad_alloc&) {
+    return fail(KVX_E_NOMEM, "kvx_xfer_poll: out of host memory");
   }
-  for (auto& kv : x->reqs) {
-    Req& r = kv.second;
-    if (r.state != KVX_REQ_PENDING) continue;
-    if (r.deferred_since >= 0 && now - r.deferred_since >= x->cfg.defer_timeout_s) {
-      r.state = KVX_REQ_EXPIRED;
-      release_req(x, r);
-      continue;
-    }
-    for (auto& l : r.layers)
-      if (l.second.st == kIssued && now - l.second.issued_at >= x->cfg.transfer_timeout_s) l.second.st = kFailed;
-    settle(x, r);
-  }
-  return KVX_OK;
 }
 
 int kvx_xfer_complete(kvx_xfer* x, uint64_t id, uint32_t attempt, int32_t layer, int32_t ok) {
@@ -412,10 +504,10 @@ int kvx_xfer_issued(const kvx_xfer* x, int64_t first, uint64_t* reqs, uint32_t* 
     return fail(KVX_E_INVAL, "kvx_xfer_issued: bad argument");
   std::lock_guard<std::mutex> lk(x->mu);
   int64_t k = 0;
-  for (int64_t i = first; i < int64_t(x->log_req.size()) && k < cap; ++i, ++k) {
-    reqs[k] = x->log_req[size_t(i)];
-    attempts[k] = x->log_attempt[size_t(i)];
-    layers[k] = x->log_layer[size_t(i)];
+  for (int64_t i = first; i < int64_t(x->log.size()) && k < cap; ++i, ++k) {
+    reqs[k] = x->log[size_t(i)].id;
+    attempts[k] = x->log[size_t(i)].attempt;
+    layers[k] = x->log[size_t(i)].layer;
   }
   *n = k;
   return KVX_OK;

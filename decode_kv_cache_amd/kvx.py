@@ -70,6 +70,7 @@ _SIGS.update({
     "kvx_xfer_register": (C.c_int, [_P, _U64, _U32, _P, _P, _I64, _D, C.POINTER(_I32)]),
     "kvx_xfer_prefill": (C.c_int, [_P, _U64, _U32, _I64, _P, _I64, _D, C.POINTER(_I32)]),
     "kvx_xfer_save_layer": (C.c_int, [_P, _U64, _U32, _I32, _P, _D, C.POINTER(_I32)]),
+    "kvx_xfer_save_layer_many": (C.c_int, [_P, _I32, _P, _I64, _P, _P, _D, _P]),
     "kvx_xfer_seal": (C.c_int, [_P, _U64, _U32, C.POINTER(_I32)]),
     "kvx_xfer_poll": (C.c_int, [_P, _D]),
     "kvx_xfer_complete": (C.c_int, [_P, _U64, _U32, _I32, _I32]),
@@ -335,6 +336,15 @@ class Xfer:
 
     def save_layer(self, req: int, attempt: int, layer: int, now: float, ready=None) -> bool:
         return self._acc("kvx_xfer_save_layer", req, attempt, layer, _event(ready), now)
+
+    def save_layer_many(self, layer: int, reqs, attempts, now: float, ready=None):
+        r = np.ascontiguousarray(reqs, np.uint64)
+        a = np.ascontiguousarray(attempts, np.uint32)
+        acc = np.zeros(len(r), np.int32)
+        _check("kvx_xfer_save_layer_many", lib().kvx_xfer_save_layer_many(
+            self.handle, layer, _event(ready), len(r), r.ctypes.data if r.size else None,
+            a.ctypes.data if a.size else None, now, acc.ctypes.data if acc.size else None))
+        return [bool(v) for v in acc]
 
     def seal(self, req: int, attempt: int) -> bool:
         return self._acc("kvx_xfer_seal", req, attempt)

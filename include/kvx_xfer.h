@@ -95,10 +95,21 @@ int kvx_xfer_prefill(kvx_xfer* x, uint64_t req, uint32_t attempt, int64_t num_to
 int kvx_xfer_save_layer(kvx_xfer* x, uint64_t req, uint32_t attempt, int32_t layer, hipEvent_t ready, double now,
                         int32_t* accepted);
 
+/* kvx_xfer_save_layer for n requests at once, all gated by the same `ready`
+ * (one save per layer for the whole batch, as an engine calls it after each
+ * layer): the stream waits on `ready` once and the deferred writes share one
+ * captured event.  accepted (nullable) receives n flags.  Equivalent to n
+ * kvx_xfer_save_layer calls in order. */
+int kvx_xfer_save_layer_many(kvx_xfer* x, int32_t layer, hipEvent_t ready, int64_t n, const uint64_t* reqs,
+                             const uint32_t* attempts, double now, int32_t* accepted);
+
 /* End of the forward pass: the writes queued so far are the expected ones. */
 int kvx_xfer_seal(kvx_xfer* x, uint64_t req, uint32_t attempt, int32_t* accepted);
 
-/* Observe finished writes (device mode) and apply the timeouts at `now`. */
+/* Observe finished writes (device mode) and apply the timeouts at `now`.
+ * Completion is observed through one event recorded per poll behind the
+ * writes issued since the previous poll, so a write is seen done at the
+ * first poll after the one following its issue. */
 int kvx_xfer_poll(kvx_xfer* x, double now);
 
 /* Report the outcome of an issued write: ok = 0 marks it failed (a transport

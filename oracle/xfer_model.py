@@ -135,6 +135,11 @@ class XferModel:
                 r.deferred_since = now
         return True
 
+    def save_layer_many(self, layer: int, rids: Sequence[int], attempts: Sequence[int], now: float) -> List[bool]:
+        """One layer saved for a batch of requests: the same as saving it for
+        each in order."""
+        return [self.save_layer(r, a, layer, now) for r, a in zip(rids, attempts)]
+
     def seal(self, rid: int, attempt: int) -> bool:
         """End of the forward pass: the writes queued so far are the expected ones."""
         r = self._get(rid, attempt, create=False)

@@ -45,13 +45,22 @@ def test_xfer_drives_pushes():
             assert x.register(r, 0, gd.pool, dt[r], now)
         assert x.prefill(r, 0, toks[r], st[r], now)
     for l in range(spec.num_layers):
-        for r in range(R):
-            blocks = torch.from_numpy(st[r][:-(-toks[r] // 16)].astype(np.int32)).cuda()
-            B.layer_compute(sink, 3000, 64, gs.region(l, 0), gs.region(l, 1), blocks, bb, 0xAB00 + 16 * r + l,
-                            stream=compute)
+        if l % 2 == 0:    # one save per request
+            for r in range(R):
+                blocks = torch.from_numpy(st[r][:-(-toks[r] // 16)].astype(np.int32)).cuda()
+                B.layer_compute(sink, 3000, 64, gs.region(l, 0), gs.region(l, 1), blocks, bb,
+                                0xAB00 + 16 * r + l, stream=compute)
+                ev = torch.cuda.Event()
+                ev.record(compute)
+                assert x.save_layer(r, 0, l, now, ready=ev)
+        else:             # one save of the layer for the whole batch
+            for r in range(R):
+                blocks = torch.from_numpy(st[r][:-(-toks[r] // 16)].astype(np.int32)).cuda()
+                B.layer_compute(sink, 3000, 64, gs.region(l, 0), gs.region(l, 1), blocks, bb,
+                                0xAB00 + 16 * r + l, stream=compute)
             ev = torch.cuda.Event()
             ev.record(compute)
-            assert x.save_layer(r, 0, l, now, ready=ev)
+            assert all(x.save_layer_many(l, range(R), [0] * R, now, ready=ev))
     for r in range(R):
         assert x.seal(r, 0)
     now = 1.0

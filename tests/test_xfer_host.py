@@ -29,8 +29,8 @@ def run_sequence(seed, steps=300, ids=(1, 2, 3, 4, 5)):
             attempts[rid] + int(rng.choice([0, 0, 0, 0, 1]))
         att = max(att, 0)
         attempts[rid] = max(attempts[rid], att)
-        op = rng.choice(["register", "prefill", "save", "save", "save", "seal", "complete", "complete",
-                         "fail", "tick", "pop", "forget"])
+        op = rng.choice(["register", "prefill", "save", "save", "save", "save_many", "seal", "complete",
+                         "complete", "fail", "tick", "pop", "forget"])
         if op == "register":
             ids_d = (rng.permutation(64)[:3]).astype(np.int32)
             a = nat.register(rid, att, cons, ids_d, now)
@@ -44,6 +44,14 @@ def run_sequence(seed, steps=300, ids=(1, 2, 3, 4, 5)):
             layer = int(rng.integers(0, 4))
             a = nat.save_layer(rid, att, layer, now)
             b = mod.save_layer(rid, att, layer, now)
+        elif op == "save_many":
+            layer = int(rng.integers(0, 4))
+            k = int(rng.integers(0, 4))
+            rs = [int(v) for v in rng.choice(ids, size=k)]
+            ats = [attempts[v] + int(rng.choice([0, 0, -1])) for v in rs]
+            ats = [max(v, 0) for v in ats]
+            a = nat.save_layer_many(layer, rs, ats, now)
+            b = mod.save_layer_many(layer, rs, ats, now)
         elif op == "seal":
             a, b = nat.seal(rid, att), mod.seal(rid, att)
         elif op in ("complete", "fail"):
