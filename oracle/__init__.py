@@ -11,5 +11,7 @@ from .kv_oracle import (  # noqa: F401
     head_rows, last_block_fill, make_plan, pack, plan_runs, push, push_plain,
     push_region, push_scales, reusable_prefix, reuse_request, should_reuse,
     staging_bytes, staging_region_bytes, tokens_to_move, triples, unpack, validate,
-    Segment, token_segments, triples_reblock,
+    Segment, token_segments, triples_reblock, window_start,
+    StateGeometry, StatePool, StatePlan, make_state_plan, pack_state, push_state,
+    push_state_plain, state_staging_bytes, unpack_state, validate_state,
 )

@@ -67,6 +67,8 @@ class Geometry:
     elem_bytes: int
     layout: str = NHD
     has_scales: bool = False
+    regions: int = 2      # 2: K and V; 1: one latent region (MLA)
+    window: int = 0       # 0: full attention; W > 0: sliding window of W positions
 
     @property
     def row_bytes(self) -> int:
@@ -99,17 +101,19 @@ class Geometry:
 
 @dataclass
 class Pool:
-    """Host copy of one KV pool: ``kv[l, kv]`` is the byte region of layer l,
-    K (0) or V (1); ``scales[l, kv, block]`` the fp32 scale bits, or None."""
+    """Host copy of one KV pool: ``kv[l, r]`` is the byte region r of layer l
+    (K = 0 and V = 1, or the single latent region 0 of an MLA pool);
+    ``scales[l, r, block]`` the fp32 scale bits, or None."""
 
     geom: Geometry
-    kv: np.ndarray                 # uint8 [L, 2, region_bytes]
-    scales: Optional[np.ndarray]   # uint32 [L, 2, num_blocks] or None
+    kv: np.ndarray                 # uint8 [L, regions, region_bytes]
+    scales: Optional[np.ndarray]   # uint32 [L, regions, num_blocks] or None
 
     @staticmethod
     def zeros(geom: Geometry) -> "Pool":
-        kv = np.zeros((geom.num_layers, 2, geom.region_bytes), np.uint8)
-        sc = np.zeros((geom.num_layers, 2, geom.num_blocks), np.uint32) if geom.has_scales else None
+        kv = np.zeros((geom.num_layers, geom.regions, geom.region_bytes), np.uint8)
+        sc = (np.zeros((geom.num_layers, geom.regions, geom.num_blocks), np.uint32)
+              if geom.has_scales else None)
         return Pool(geom, kv, sc)
 
     def copy(self) -> "Pool":
@@ -157,11 +161,29 @@ def last_block_fill(num_tokens: int, block_size: int) -> int:
     return num_tokens - (nb - 1) * block_size if nb else 0
 
 
+def window_start(num_tokens: int, window: int, bs_src: int, bs_dst: int) -> int:
+    """First token a sliding-window layer group moves ([MORI] §6: layers of
+    other shapes, sliding window among them, get their own geometry).
+
+    The receiving side computes position n = num_tokens next, and a query
+    with a window of W positions sees positions n-W+1 .. n.  Blocks holding
+    none of those are not kept (their block-table entries may be null), so
+    the move starts at the later of the two sides' starts of the block that
+    holds position n-W+1.  Window 0 is full attention: everything moves."""
+    if window <= 0:
+        return 0
+    first = max(0, num_tokens - window + 1)
+    return max(first // bs_src * bs_src, first // bs_dst * bs_dst)
+
+
 # ---------------------------------------------------------------------------
 # Validation shared by both formulations.
 # ---------------------------------------------------------------------------
+_COMMON = ("num_layers", "head_dim", "elem_bytes", "has_scales", "regions", "window")
+
+
 def _check_same_push_geometry(gs: Geometry, gd: Geometry) -> None:
-    for f in ("num_layers", "num_heads", "head_dim", "elem_bytes", "layout", "has_scales"):
+    for f in _COMMON + ("num_heads", "layout"):
         if getattr(gs, f) != getattr(gd, f):
             raise OracleError("MISMATCH", f"{f} differs: {getattr(gs, f)} vs {getattr(gd, f)}")
     _check_block_sizes(gs, gd)
@@ -176,10 +198,11 @@ def _check_block_sizes(gs: Geometry, gd: Geometry) -> None:
 
 
 def validate(requests: Sequence[Request], block_size: int, src_blocks: int, dst_blocks: int,
-             dst_block_size: Optional[int] = None) -> None:
+             dst_block_size: Optional[int] = None, window: int = 0) -> None:
     """Error classes of the transfer (argument errors, IDs out of range,
-    destination used twice).  Only the first ceil(n/BS) IDs of each list are
-    looked at, BS being that side's block size."""
+    destination used twice).  Each list must hold ceil(n/BS) IDs, BS being
+    that side's block size; later entries are not looked at, nor (with a
+    sliding window) the entries of blocks the window no longer holds."""
     bsd = block_size if dst_block_size is None else dst_block_size
     used_dst = set()
     for r, req in enumerate(requests):
@@ -189,11 +212,12 @@ def validate(requests: Sequence[Request], block_size: int, src_blocks: int, dst_
         nbd = blocks_in_use(req.num_tokens, bsd)
         if len(req.src_ids) < nbs or len(req.dst_ids) < nbd:
             raise OracleError("INVAL", f"request {r}: block list shorter than needed")
-        for i in range(nbs):
+        t0 = window_start(req.num_tokens, window, block_size, bsd)
+        for i in range(t0 // block_size, nbs):
             s = int(req.src_ids[i])
             if not 0 <= s < src_blocks:
                 raise OracleError("RANGE", f"request {r}: src block {s} outside pool")
-        for i in range(nbd):
+        for i in range(t0 // bsd, nbd):
             d = int(req.dst_ids[i])
             if not 0 <= d < dst_blocks:
                 raise OracleError("RANGE", f"request {r}: dst block {d} outside pool")
@@ -225,13 +249,14 @@ def copy_heads_plain(src: Pool, dst: Pool, requests: Sequence[Request],
     side maps blocks onto its own layout); [MORI] §6 (rank mapping under TP)."""
     gs, gd = src.geom, dst.geom
     _check_head_slice(gs, gd, src_head0, dst_head0, num_heads)
-    validate(requests, gs.block_size, gs.num_blocks, gd.num_blocks, gd.block_size)
+    validate(requests, gs.block_size, gs.num_blocks, gd.num_blocks, gd.block_size, gs.window)
     bs, bsd = gs.block_size, gd.block_size
     row = gs.row_bytes
     lay = range(gs.num_layers) if layers is None else layers
     for req in requests:
         n = req.num_tokens
-        for p in range(n):
+        t0 = window_start(n, gs.window, bs, bsd)
+        for p in range(t0, n):
             j, s = divmod(p, bs)
             jd, sd = divmod(p, bsd)
             sb, db = int(req.src_ids[j]), int(req.dst_ids[jd])
@@ -239,18 +264,18 @@ def copy_heads_plain(src: Pool, dst: Pool, requests: Sequence[Request],
                 so = gs.row_offset(sb, s, h)
                 do = gd.row_offset(db, sd, h - src_head0 + dst_head0)
                 for l in lay:
-                    for kv in (K, V):
+                    for kv in range(gs.regions):
                         dst.kv[l, kv, do:do + row] = src.kv[l, kv, so:so + row]
         if src.scales is not None:
-            for j in range(blocks_in_use(n, bs)):
+            for j in range(t0 // bs, blocks_in_use(n, bs)):
                 sb, db = int(req.src_ids[j]), int(req.dst_ids[j])
                 for l in lay:
-                    for kv in (K, V):
+                    for kv in range(gs.regions):
                         dst.scales[l, kv, db] = src.scales[l, kv, sb]
 
 
 def _check_head_slice(gs: Geometry, gd: Geometry, s0: int, d0: int, nh: int) -> None:
-    for f in ("num_layers", "head_dim", "elem_bytes", "has_scales"):
+    for f in _COMMON:
         if getattr(gs, f) != getattr(gd, f):
             raise OracleError("MISMATCH", f"{f} differs")
     _check_block_sizes(gs, gd)
@@ -275,23 +300,25 @@ class Run:
 
 
 def plan_runs(requests: Sequence[Request], block_size: int, src_blocks: int,
-              dst_blocks: int) -> List[Run]:
+              dst_blocks: int, window: int = 0) -> List[Run]:
     """Merge each request's block pairs into maximal runs that are consecutive
     on both sides, in list order; a run never spans two requests.  The
     background transfer thread merges contiguous blocks into larger transfer
     regions ([PUSH] "Threading-Modell"); the per-layer offset computation
     merges contiguous blocks into one transfer ([MORI] §3.1) and adjacent
-    blocks are merged to cut the work-request count ([MORI] §6)."""
-    validate(requests, block_size, src_blocks, dst_blocks)
+    blocks are merged to cut the work-request count ([MORI] §6).  With a
+    sliding window the runs start at the first block the window holds."""
+    validate(requests, block_size, src_blocks, dst_blocks, window=window)
     runs: List[Run] = []
     for req in requests:
         n = req.num_tokens
         nb = blocks_in_use(n, block_size)
-        if nb == 0:
+        j0 = window_start(n, window, block_size, block_size) // block_size
+        if nb - j0 <= 0:
             continue
         tail = last_block_fill(n, block_size)
-        start = 0
-        for i in range(1, nb + 1):
+        start = j0
+        for i in range(j0 + 1, nb + 1):
             breaks = (i == nb
                       or int(req.src_ids[i]) != int(req.src_ids[i - 1]) + 1
                       or int(req.dst_ids[i]) != int(req.dst_ids[i - 1]) + 1)
@@ -371,21 +398,24 @@ class Plan:
         return 4 * len(self.pairs) if self.src_geom.has_scales else 0
 
     def bytes_per_layer(self) -> Tuple[int, int]:
-        """(read, written) bytes of one layer, K and V, payload and scales."""
-        b = 2 * (self.payload_bytes + self.scale_bytes)
+        """(read, written) bytes of one layer, every region, payload and scales."""
+        b = self.src_geom.regions * (self.payload_bytes + self.scale_bytes)
         return b, b
 
 
 def make_plan(src_geom: Geometry, dst_geom: Geometry, requests: Sequence[Request]) -> Plan:
-    same = all(getattr(src_geom, f) == getattr(dst_geom, f) for f in
-               ("num_layers", "num_heads", "head_dim", "elem_bytes", "layout", "has_scales"))
+    for f in ("regions", "window"):
+        if getattr(src_geom, f) != getattr(dst_geom, f):
+            raise OracleError("MISMATCH", f"{f} differs")
+    same = all(getattr(src_geom, f) == getattr(dst_geom, f) for f in _COMMON + ("num_heads", "layout"))
+    w = src_geom.window
     if src_geom.block_size == dst_geom.block_size:
-        runs = plan_runs(requests, src_geom.block_size, src_geom.num_blocks, dst_geom.num_blocks)
+        runs = plan_runs(requests, src_geom.block_size, src_geom.num_blocks, dst_geom.num_blocks, w)
         tr = triples(runs, src_geom) if same else []
         return Plan(src_geom, dst_geom, runs, tr, block_pairs(runs))
     _check_block_sizes(src_geom, dst_geom)
-    validate(requests, src_geom.block_size, src_geom.num_blocks, dst_geom.num_blocks, dst_geom.block_size)
-    segs = token_segments(requests, src_geom.block_size, dst_geom.block_size)
+    validate(requests, src_geom.block_size, src_geom.num_blocks, dst_geom.num_blocks, dst_geom.block_size, w)
+    segs = token_segments(requests, src_geom.block_size, dst_geom.block_size, w)
     tr = triples_reblock(segs, src_geom, dst_geom) if same else []
     return Plan(src_geom, dst_geom, [], tr, [])
 
@@ -409,11 +439,12 @@ class Segment:
     ntok: int
 
 
-def token_segments(requests: Sequence[Request], bs_src: int, bs_dst: int) -> List[Segment]:
+def token_segments(requests: Sequence[Request], bs_src: int, bs_dst: int,
+                   window: int = 0) -> List[Segment]:
     out: List[Segment] = []
     for req in requests:
         n = req.num_tokens
-        p = 0
+        p = window_start(n, window, bs_src, bs_dst)
         while p < n:
             start = p
             p += 1
@@ -486,7 +517,7 @@ def push(src: Pool, dst: Pool, plan: Plan, layers: Optional[Sequence[int]] = Non
     _check_same_push_geometry(src.geom, dst.geom)
     lay = range(src.geom.num_layers) if layers is None else layers
     for l in lay:
-        for kv in (K, V):
+        for kv in range(src.geom.regions):
             push_region(src.kv[l, kv], dst.kv[l, kv], plan.triples)
             if src.scales is not None:
                 push_scales(src.scales[l, kv], dst.scales[l, kv], plan.pairs)
@@ -494,7 +525,7 @@ def push(src: Pool, dst: Pool, plan: Plan, layers: Optional[Sequence[int]] = Non
 
 # ---------------------------------------------------------------------------
 # a6: contiguous staging buffer (what a NIC would read).  Layout, for each
-# layer in [l0, l1), K then V: the source bytes of the region's triples in
+# layer in [l0, l1), region by region (K then V): the source bytes of the region's triples in
 # plan order, then (if the pool has scales) the used blocks' scales in plan
 # order as little-endian uint32, zero-padded to a multiple of 16 bytes.
 # ---------------------------------------------------------------------------
@@ -508,14 +539,14 @@ def staging_region_bytes(plan: Plan) -> int:
 
 
 def staging_bytes(plan: Plan, l0: int, l1: int) -> int:
-    return (l1 - l0) * 2 * staging_region_bytes(plan)
+    return (l1 - l0) * plan.src_geom.regions * staging_region_bytes(plan)
 
 
 def pack(src: Pool, plan: Plan, l0: int, l1: int) -> np.ndarray:
     out = np.empty(staging_bytes(plan, l0, l1), np.uint8)
     pos = 0
     for l in range(l0, l1):
-        for kv in (K, V):
+        for kv in range(src.geom.regions):
             for so, _, ln in plan.triples:
                 out[pos:pos + ln] = src.kv[l, kv, so:so + ln]
                 pos += ln
@@ -533,7 +564,7 @@ def pack(src: Pool, plan: Plan, l0: int, l1: int) -> np.ndarray:
 def unpack(staging: np.ndarray, dst: Pool, plan: Plan, l0: int, l1: int) -> None:
     pos = 0
     for l in range(l0, l1):
-        for kv in (K, V):
+        for kv in range(dst.geom.regions):
             for _, do, ln in plan.triples:
                 dst.kv[l, kv, do:do + ln] = staging[pos:pos + ln]
                 pos += ln
@@ -563,7 +594,7 @@ def head_rows(plan: Plan, src_head0: int, dst_head0: int, num_heads: int,
     sb, db, sl, dl = [], [], [], []
     for req in requests:
         n = req.num_tokens
-        p = np.arange(n, dtype=np.int64)
+        p = np.arange(window_start(n, gs.window, gs.block_size, gd.block_size), n, dtype=np.int64)
         sb.append(np.asarray(req.src_ids, np.int64)[p // gs.block_size])
         db.append(np.asarray(req.dst_ids, np.int64)[p // gd.block_size])
         sl.append(p % gs.block_size)
@@ -591,7 +622,7 @@ def copy_heads(src: Pool, dst: Pool, plan: Plan, requests: Sequence[Request], la
     if not 0 <= layer < gs.num_layers:
         raise OracleError("RANGE", "layer")
     sr, dr = head_rows(plan, src_head0, dst_head0, num_heads, requests)
-    for kv in (K, V):
+    for kv in range(gs.regions):
         copy_heads_region(src.kv[layer, kv], dst.kv[layer, kv], gs.row_bytes, sr, dr)
         if src.scales is not None:
             push_scales(src.scales[layer, kv], dst.scales[layer, kv], plan.pairs)
@@ -616,3 +647,148 @@ def reuse_request(turn: int, growth: int, threshold: int, decode_ids: Sequence[i
     if r <= 0 or not should_reuse(r, threshold):
         return None
     return Request(r, decode_ids, prefill_ids)
+
+
+# ---------------------------------------------------------------------------
+# State-slot layer groups ([MORI] §6, hybrid model support): a mamba-like
+# layer keeps its recurrent state in two separately registered regions, the
+# convolution state and the SSM state, and the state is moved slot by slot.
+# Region r of layer l holds num_slots slots of slot_bytes[r] bytes each.
+#
+# Readings: each request holds one state slot per side, the first entry of
+# its list; a request that moves at least one token moves its whole slot in
+# both regions, one that moves none moves nothing.  The bytes move as they
+# are: which recurrent state the slot holds is the engine's business.
+# ---------------------------------------------------------------------------
+@dataclass(frozen=True)
+class StateGeometry:
+    num_layers: int
+    num_slots: int
+    slot_bytes: Tuple[int, int]   # (convolution state, SSM state) bytes per slot
+
+
+@dataclass
+class StatePool:
+    """``regions[r][l]`` is region r (0 = conv, 1 = SSM) of layer l as a
+    uint8 array of num_slots * slot_bytes[r] bytes."""
+
+    geom: StateGeometry
+    regions: List[np.ndarray]     # two uint8 arrays [L, num_slots * slot_bytes[r]]
+
+    def copy(self) -> "StatePool":
+        return StatePool(self.geom, [a.copy() for a in self.regions])
+
+
+def _check_state_geometry(gs: StateGeometry, gd: StateGeometry) -> None:
+    if gs.num_layers != gd.num_layers or tuple(gs.slot_bytes) != tuple(gd.slot_bytes):
+        raise OracleError("MISMATCH", "state pools differ in layers or slot sizes")
+
+
+def validate_state(requests: Sequence[Request], src_slots: int, dst_slots: int) -> None:
+    """Requests that move tokens need one slot on each side, inside the pool;
+    a destination slot may be written once per plan."""
+    used = set()
+    for r, req in enumerate(requests):
+        if req.num_tokens < 0:
+            raise OracleError("INVAL", f"request {r}: negative token count")
+        if req.num_tokens == 0:
+            continue
+        if len(req.src_ids) < 1 or len(req.dst_ids) < 1:
+            raise OracleError("INVAL", f"request {r}: no state slot")
+        s, d = int(req.src_ids[0]), int(req.dst_ids[0])
+        if not 0 <= s < src_slots:
+            raise OracleError("RANGE", f"request {r}: src slot {s} outside pool")
+        if not 0 <= d < dst_slots:
+            raise OracleError("RANGE", f"request {r}: dst slot {d} outside pool")
+        if d in used:
+            raise OracleError("DUPDST", f"dst slot {d} used twice")
+        used.add(d)
+
+
+def push_state_plain(src: StatePool, dst: StatePool, requests: Sequence[Request],
+                     layers: Optional[Sequence[int]] = None) -> None:
+    """Plain definition: every moving request's slot, in every layer and both
+    regions, is copied whole from its source slot to its destination slot."""
+    gs, gd = src.geom, dst.geom
+    _check_state_geometry(gs, gd)
+    validate_state(requests, gs.num_slots, gd.num_slots)
+    lay = range(gs.num_layers) if layers is None else layers
+    for req in requests:
+        if req.num_tokens == 0:
+            continue
+        s, d = int(req.src_ids[0]), int(req.dst_ids[0])
+        for r in range(2):
+            sb = gs.slot_bytes[r]
+            for l in lay:
+                dst.regions[r][l, d * sb:(d + 1) * sb] = src.regions[r][l, s * sb:(s + 1) * sb]
+
+
+@dataclass
+class StatePlan:
+    src_geom: StateGeometry
+    dst_geom: StateGeometry
+    runs: List[Run]                                   # one per moving request, tail 1
+    triples: Tuple[List[Tuple[int, int, int]], List[Tuple[int, int, int]]]
+
+    def payload_bytes(self, region: int) -> int:
+        return sum(t[2] for t in self.triples[region])
+
+    def bytes_per_layer(self) -> Tuple[int, int]:
+        b = self.payload_bytes(0) + self.payload_bytes(1)
+        return b, b
+
+
+def make_state_plan(src_geom: StateGeometry, dst_geom: StateGeometry,
+                    requests: Sequence[Request]) -> StatePlan:
+    """The procedure: one run per moving request (its slot pair), then per
+    region the slot byte ranges in plan order, neighbours merged wherever
+    both sides continue ([MORI] §6: adjacent blocks merged into one range)."""
+    _check_state_geometry(src_geom, dst_geom)
+    validate_state(requests, src_geom.num_slots, dst_geom.num_slots)
+    runs = [Run(int(q.src_ids[0]), int(q.dst_ids[0]), 1, 1) for q in requests if q.num_tokens > 0]
+    lists = []
+    for r in range(2):
+        sb = src_geom.slot_bytes[r]
+        out: List[List[int]] = []
+        for run in runs:
+            so, do = run.src0 * sb, run.dst0 * sb
+            if out and out[-1][0] + out[-1][2] == so and out[-1][1] + out[-1][2] == do:
+                out[-1][2] += sb
+            else:
+                out.append([so, do, sb])
+        lists.append([tuple(t) for t in out])
+    return StatePlan(src_geom, dst_geom, runs, (lists[0], lists[1]))
+
+
+def push_state(src: StatePool, dst: StatePool, plan: StatePlan,
+               layers: Optional[Sequence[int]] = None) -> None:
+    lay = range(src.geom.num_layers) if layers is None else layers
+    for l in lay:
+        for r in range(2):
+            push_region(src.regions[r][l], dst.regions[r][l], plan.triples[r])
+
+
+def state_staging_bytes(plan: StatePlan, l0: int, l1: int) -> int:
+    """Staging per layer: region 0's moved bytes in plan order, then region 1's."""
+    return (l1 - l0) * (plan.payload_bytes(0) + plan.payload_bytes(1))
+
+
+def pack_state(src: StatePool, plan: StatePlan, l0: int, l1: int) -> np.ndarray:
+    out = np.empty(state_staging_bytes(plan, l0, l1), np.uint8)
+    pos = 0
+    for l in range(l0, l1):
+        for r in range(2):
+            for so, _, ln in plan.triples[r]:
+                out[pos:pos + ln] = src.regions[r][l, so:so + ln]
+                pos += ln
+    assert pos == out.size
+    return out
+
+
+def unpack_state(staging: np.ndarray, dst: StatePool, plan: StatePlan, l0: int, l1: int) -> None:
+    pos = 0
+    for l in range(l0, l1):
+        for r in range(2):
+            for _, do, ln in plan.triples[r]:
+                dst.regions[r][l, do:do + ln] = staging[pos:pos + ln]
+                pos += ln

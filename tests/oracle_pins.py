@@ -46,7 +46,12 @@ def pages_values():
 # ---------------------------------------------------------------------------
 def geom(O, spec):
     return O.Geometry(spec.num_layers, spec.num_blocks, spec.block_size, spec.num_heads,
-                      spec.head_dim, spec.elem_bytes, spec.layout, spec.has_scales)
+                      spec.head_dim, spec.elem_bytes, spec.layout, spec.has_scales,
+                      spec.regions, spec.window)
+
+
+def state_geom(O, spec):
+    return O.StateGeometry(spec.num_layers, spec.num_slots, tuple(spec.slot_bytes))
 
 
 def pools(O, wl):
@@ -576,8 +581,278 @@ def pin_reblock_errors(O):
             assert e.kind == "INVAL"
 
 
+# ---------------------------------------------------------------------------
+# layer groups of other shapes: one latent region (MLA), sliding window,
+# state slots
+# ---------------------------------------------------------------------------
+def latent_cases(count=24, seed0=61):
+    rng = np.random.Generator(np.random.PCG64(seed0))
+    for i in range(count):
+        bs = int(rng.choice([1, 2, 4, 16]))
+        yield W.random_case(
+            4000 + i, layout=["NHD", "HND"][i % 2], elem_bytes=int(rng.choice([1, 2])),
+            num_layers=int(rng.integers(1, 3)), num_blocks=int(max(48, 8 * bs)), block_size=bs, num_heads=1,
+            head_dim=int(rng.choice([8, 16, 24])), has_scales=bool(i % 3 == 0),
+            num_requests=int(rng.integers(1, 4)), max_tokens=int(min(5 * bs, 40)),
+            run_mean=float(rng.choice([1.5, 4.0])), regions=1)
+
+
+def pin_latent_region(O):
+    """A pool of one latent region per layer (MLA) moves exactly what region
+    0 of a K/V pool holding the same bytes would; with block size 1 every
+    token is a block and the move is torch index_select -> index_copy_ of
+    token rows; staging holds one region per layer."""
+    for wl in latent_cases():
+        src, dst = pools(O, wl)
+        reqs = requests_for(O, wl)
+        plan = O.make_plan(src.geom, dst.geom, reqs)
+        a, b = dst.copy(), dst.copy()
+        O.push_plain(src, a, reqs)
+        O.push(src, b, plan)
+        assert np.array_equal(a.kv, b.kv), wl.name
+        # the same bytes as region 0 of a two-region pool
+        g2s = O.Geometry(*[getattr(src.geom, f) for f in ("num_layers", "num_blocks", "block_size", "num_heads",
+                                                           "head_dim", "elem_bytes", "layout", "has_scales")])
+        g2d = O.Geometry(*[getattr(dst.geom, f) for f in ("num_layers", "num_blocks", "block_size", "num_heads",
+                                                           "head_dim", "elem_bytes", "layout", "has_scales")])
+        rng = np.random.Generator(np.random.PCG64(wl.seed))
+        s2 = O.Pool(g2s, np.concatenate([src.kv, rng.integers(0, 256, src.kv.shape, dtype=np.uint8)], 1),
+                    None if src.scales is None else np.concatenate([src.scales, src.scales], 1))
+        d2 = O.Pool(g2d, np.concatenate([dst.kv, dst.kv], 1),
+                    None if dst.scales is None else np.concatenate([dst.scales, dst.scales], 1))
+        O.push(s2, d2, O.make_plan(g2s, g2d, reqs))
+        assert np.array_equal(d2.kv[:, :1], b.kv), wl.name
+        if b.scales is not None:
+            assert np.array_equal(d2.scales[:, :1], b.scales), wl.name
+        L = src.geom.num_layers
+        stg = O.pack(src, plan, 0, L)
+        sc = -(-4 * len(plan.pairs) // 16) * 16 if src.scales is not None else 0
+        assert stg.size == O.staging_bytes(plan, 0, L) == L * (plan.payload_bytes + sc)
+        c = dst.copy()
+        O.unpack(stg, c, plan, 0, L)
+        assert np.array_equal(c.kv, b.kv), wl.name
+        if wl.src.block_size == 1:
+            nb = wl.src.num_blocks
+            exp = torch.from_numpy(dst.kv.copy())
+            s = torch.from_numpy(src.kv)
+            sid = torch.from_numpy(np.concatenate([t[:q.num_tokens] for t, q in zip(wl.src_tables, reqs)]
+                                                  ).astype(np.int64))
+            did = torch.from_numpy(np.concatenate([t[:q.num_tokens] for t, q in zip(wl.dst_tables, reqs)]
+                                                  ).astype(np.int64))
+            for l in range(L):
+                exp[l, 0].view(nb, -1).index_copy_(0, did, s[l, 0].view(nb, -1).index_select(0, sid))
+            assert np.array_equal(b.kv, exp.numpy()), wl.name
+
+
+def window_cases(count=40, seed0=71):
+    rng = np.random.Generator(np.random.PCG64(seed0))
+    for i in range(count):
+        mixed = i % 3 == 2
+        bs = int(rng.choice([1, 2, 3, 4, 8]))
+        bsd = int(rng.choice([x for x in (1, 2, 3, 4, 8) if x != bs])) if mixed else bs
+        w = int(rng.choice([1, 2, 3, bs, bs + 1, 2 * bs + 1, 7, 64]))
+        yield W.random_case(
+            5000 + i, layout=["NHD", "HND"][i % 2], elem_bytes=1, num_layers=1, num_blocks=120,
+            block_size=bs, dst_block_size=bsd, num_heads=int(rng.integers(1, 3)), head_dim=16,
+            has_scales=bool(i % 4 == 0 and not mixed), num_requests=int(rng.integers(1, 4)), max_tokens=30,
+            run_mean=float(rng.choice([1.5, 4.0])), window=w)
+
+
+def _attended(n, w):
+    """Positions the query at position n sees under a sliding window of w
+    positions: row n of torch's banded causal mask."""
+    m = torch.ones(n + 1, n + 1, dtype=torch.bool).tril().triu(-(w - 1))
+    return set(int(k) for k in torch.nonzero(m[n]).flatten())
+
+
+def pin_window_mask(O):
+    """Sliding window, checked against the band mask: every key position the
+    receiving side's next query (at position n) sees arrives; no block that
+    holds none of the positions that query sees (its own included) is read or
+    written; with equal block sizes each kept block moves whole; table
+    entries of dropped blocks are neither read nor validated; a window of at
+    least n + 1 positions moves what full attention moves."""
+    for wl in window_cases():
+        src, dst = pools(O, wl)
+        reqs = requests_for(O, wl)
+        a, b = dst.copy(), dst.copy()
+        O.push_plain(src, a, reqs)
+        plan = O.make_plan(src.geom, dst.geom, reqs)
+        O.push(src, b, plan)
+        assert np.array_equal(a.kv, b.kv), wl.name
+        gs, gd = src.geom, dst.geom
+        w, bss, bsd = gs.window, gs.block_size, gd.block_size
+        for q in reqs:
+            n = q.num_tokens
+            seen = _attended(n, w)
+            for p in range(n):
+                for h in range(gs.num_heads):
+                    so = gs.row_offset(int(q.src_ids[p // bss]), p % bss, h)
+                    do = gd.row_offset(int(q.dst_ids[p // bsd]), p % bsd, h)
+                    same = np.array_equal(b.kv[:, :, do:do + gs.row_bytes], src.kv[:, :, so:so + gs.row_bytes])
+                    if p in seen:
+                        assert same, (wl.name, "a seen position did not arrive", p)
+                    kept_s = any(k // bss == p // bss for k in seen)
+                    kept_d = any(k // bsd == p // bsd for k in seen)
+                    if bss == bsd and kept_s:
+                        assert same, (wl.name, "a kept block did not move whole", p)
+                    if not kept_d:
+                        changed = not np.array_equal(b.kv[:, :, do:do + gs.row_bytes],
+                                                     dst.kv[:, :, do:do + gs.row_bytes])
+                        assert not changed, (wl.name, "a dropped destination block was written", p)
+        # dropped entries: poison them; nothing may read or validate them
+        poisoned = []
+        for q in reqs:
+            n = q.num_tokens
+            seen = _attended(n, w)
+            s_ids = np.array(q.src_ids, np.int64)
+            d_ids = np.array(q.dst_ids, np.int64)
+            for j in range(O.blocks_in_use(n, bss)):
+                if not any(k // bss == j for k in seen):
+                    s_ids[j] = -1
+            for j in range(O.blocks_in_use(n, bsd)):
+                if not any(k // bsd == j for k in seen):
+                    d_ids[j] = -1
+            poisoned.append(O.Request(n, s_ids, d_ids))
+        c = dst.copy()
+        O.push(src, c, O.make_plan(gs, gd, poisoned))
+        assert np.array_equal(c.kv, b.kv), wl.name
+        if b.scales is not None:
+            assert np.array_equal(c.scales, b.scales), wl.name
+        # a window covering everything is full attention
+        full = [O.Request(q.num_tokens, q.src_ids, q.dst_ids) for q in reqs]
+        wide = max(q.num_tokens for q in reqs) + 1
+        gsw = O.Geometry(*[getattr(gs, f) for f in ("num_layers", "num_blocks", "block_size", "num_heads",
+                                                     "head_dim", "elem_bytes", "layout", "has_scales",
+                                                     "regions")], wide)
+        gdw = O.Geometry(*[getattr(gd, f) for f in ("num_layers", "num_blocks", "block_size", "num_heads",
+                                                     "head_dim", "elem_bytes", "layout", "has_scales",
+                                                     "regions")], wide)
+        g0s = O.Geometry(*[getattr(gs, f) for f in ("num_layers", "num_blocks", "block_size", "num_heads",
+                                                     "head_dim", "elem_bytes", "layout", "has_scales")])
+        g0d = O.Geometry(*[getattr(gd, f) for f in ("num_layers", "num_blocks", "block_size", "num_heads",
+                                                     "head_dim", "elem_bytes", "layout", "has_scales")])
+        x, y = dst.copy(), dst.copy()
+        O.push(O.Pool(gsw, src.kv, src.scales), O.Pool(gdw, x.kv, x.scales), O.make_plan(gsw, gdw, full))
+        O.push(O.Pool(g0s, src.kv, src.scales), O.Pool(g0d, y.kv, y.scales), O.make_plan(g0s, g0d, full))
+        assert np.array_equal(x.kv, y.kv), wl.name
+
+
+def pin_window_closed_form(O):
+    """Worked by hand: an 8192-token prompt (8191 tokens move) under a
+    128-position window with 16-slot blocks keeps positions 8064..8190 of the
+    moved range, i.e. blocks 504..511 (127 tokens); a window of one position
+    moves only the tokens sharing position n's block."""
+    g = O.Geometry(1, 600, 16, 8, 64, 2, "NHD", False, 2, 128)
+    ids = list(range(512))
+    plan = O.make_plan(g, g, [O.Request(8191, ids, ids)])
+    assert plan.runs == [O.Run(504, 504, 8, 15)]
+    assert plan.payload_bytes == 127 * 8 * 64 * 2
+    assert plan.bytes_per_layer() == (2 * 127 * 1024, 2 * 127 * 1024)
+    g1 = O.Geometry(1, 20, 8, 1, 16, 1, "NHD", False, 2, 1)
+    assert O.make_plan(g1, g1, [O.Request(40, list(range(5)), list(range(5)))]).payload_bytes == 0
+    assert O.make_plan(g1, g1, [O.Request(43, list(range(6)), list(range(6)))]).payload_bytes == 3 * 16
+
+
+def state_cases(count=30, seed0=81):
+    rng = np.random.Generator(np.random.PCG64(seed0))
+    for i in range(count):
+        yield W.random_state_case(6000 + i, num_layers=int(rng.integers(1, 3)), num_slots=40,
+                                  slot_bytes=(int(rng.choice([16, 48, 96])), int(rng.choice([32, 160, 256]))),
+                                  num_requests=int(rng.integers(1, 9)), max_tokens=int(rng.choice([3, 20])),
+                                  extra_ids=int(rng.integers(0, 2)))
+
+
+def _state_pools(O, wl):
+    gs, gd = state_geom(O, wl.src), state_geom(O, wl.dst)
+    return (O.StatePool(gs, W.state_host_values(wl.src, wl.seed, 1)),
+            O.StatePool(gd, W.state_host_values(wl.dst, wl.seed, 2)))
+
+
+def pin_state_slots(O):
+    """State slots: the procedure equals the plain slot copy and torch
+    index_select -> index_copy_ on the slot dimension of each region (rows of
+    that region's slot size) for the requests that move tokens; requests that
+    move none leave their destination slot untouched; the triple list is the
+    unique maximal merge; pack/unpack round-trips."""
+    for wl in state_cases():
+        src, dst = _state_pools(O, wl)
+        reqs = requests_for(O, wl, wl.prompt_lens)
+        plan = O.make_state_plan(src.geom, dst.geom, reqs)
+        a, b = dst.copy(), dst.copy()
+        O.push_state_plain(src, a, reqs)
+        O.push_state(src, b, plan)
+        for r in range(2):
+            assert np.array_equal(a.regions[r], b.regions[r]), wl.name
+        mv = [q for q in reqs if q.num_tokens > 0]
+        sid = torch.tensor([int(q.src_ids[0]) for q in mv], dtype=torch.int64)
+        did = torch.tensor([int(q.dst_ids[0]) for q in mv], dtype=torch.int64)
+        for r in range(2):
+            sb = wl.src.slot_bytes[r]
+            exp = torch.from_numpy(dst.regions[r].copy())
+            s = torch.from_numpy(src.regions[r])
+            for l in range(wl.src.num_layers):
+                exp[l].view(-1, sb).index_copy_(0, did, s[l].view(-1, sb).index_select(0, sid))
+            assert np.array_equal(b.regions[r], exp.numpy()), wl.name
+            tr = plan.triples[r]
+            assert sum(t[2] for t in tr) == len(mv) * sb
+            for x, y in zip(tr, tr[1:]):
+                assert not (x[0] + x[2] == y[0] and x[1] + x[2] == y[1]), "not maximal"
+        L = wl.src.num_layers
+        stg = O.pack_state(src, plan, 0, L)
+        assert stg.size == O.state_staging_bytes(plan, 0, L) == L * len(mv) * sum(wl.src.slot_bytes)
+        c = dst.copy()
+        O.unpack_state(stg, c, plan, 0, L)
+        for r in range(2):
+            assert np.array_equal(c.regions[r], b.regions[r]), wl.name
+
+
+def pin_state_closed_form_and_errors(O):
+    """Worked by hand: sixteen requests with 48 KiB + 1 MiB slots move
+    16 * 1,097,728 = 17,563,648 bytes per layer; slots 3, 4, 5 -> 10, 11, 12
+    merge into one range per region and 9 -> 20 stays apart.  Errors: a
+    destination slot used twice, a slot outside the pool, a moving request
+    without a slot, different slot sizes."""
+    g = O.StateGeometry(1, 64, (49152, 1048576))
+    reqs = [O.Request(8191, [i], [63 - i]) for i in range(16)]
+    assert O.make_state_plan(g, g, reqs).bytes_per_layer() == (17563648, 17563648)
+    g2 = O.StateGeometry(1, 32, (16, 48))
+    p = O.make_state_plan(g2, g2, [O.Request(5, [3], [10]), O.Request(1, [4], [11]), O.Request(2, [5], [12]),
+                                   O.Request(0, [7], [13]), O.Request(9, [9], [20])])
+    assert p.triples[0] == [(48, 160, 48), (144, 320, 16)]
+    assert p.triples[1] == [(144, 480, 144), (432, 960, 48)]
+    for bad, kind in (([O.Request(1, [0], [5]), O.Request(1, [1], [5])], "DUPDST"),
+                      ([O.Request(1, [32], [0])], "RANGE"), ([O.Request(1, [0], [-1])], "RANGE"),
+                      ([O.Request(1, [], [0])], "INVAL"), ([O.Request(-1, [0], [0])], "INVAL")):
+        try:
+            O.make_state_plan(g2, g2, bad)
+            raise AssertionError(f"accepted {kind}")
+        except O.OracleError as e:
+            assert e.kind == kind, (e.kind, kind)
+    assert O.make_state_plan(g2, g2, [O.Request(0, [], [])]).triples == ([], [])
+    try:
+        O.make_state_plan(g2, O.StateGeometry(1, 32, (16, 64)), [])
+        raise AssertionError("slot sizes differ")
+    except O.OracleError as e:
+        assert e.kind == "MISMATCH"
+
+
+def pin_group_mismatch(O):
+    """Pools of one transfer agree on their region count and window."""
+    a = O.Geometry(1, 8, 4, 1, 16, 1, "NHD", False, 2, 0)
+    for other in (O.Geometry(1, 8, 4, 1, 16, 1, "NHD", False, 1, 0),
+                  O.Geometry(1, 8, 4, 1, 16, 1, "NHD", False, 2, 8)):
+        try:
+            O.make_plan(a, other, [])
+            raise AssertionError("mismatch accepted")
+        except O.OracleError as e:
+            assert e.kind == "MISMATCH"
+
+
 ALL_PINS = [pin_brute_vs_procedure, pin_full_blocks_index_copy, pin_single_run_slice,
             pin_nhd_to_hnd_permute, pin_final_token_never_sent, pin_untouched_bytes,
             pin_plan_invariants, pin_closed_forms, pin_threshold, pin_pack_unpack,
             pin_copy_heads, pin_errors, pin_reblock_brute_vs_procedure, pin_reblock_equal_sizes_agree,
-            pin_reblock_torch_pairs, pin_reblock_round_trip, pin_reblock_errors]
+            pin_reblock_torch_pairs, pin_reblock_round_trip, pin_reblock_errors,
+            pin_latent_region, pin_window_mask, pin_window_closed_form, pin_state_slots,
+            pin_state_closed_form_and_errors, pin_group_mismatch]

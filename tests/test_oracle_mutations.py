@@ -152,9 +152,9 @@ def m_hnd_tail_one_segment(O):
 def m_dupdst_allowed(O):
     orig = O.validate
 
-    def validate(requests, bs, nsrc, ndst):
+    def validate(requests, bs, nsrc, ndst, *args, **kw):
         try:
-            orig(requests, bs, nsrc, ndst)
+            orig(requests, bs, nsrc, ndst, *args, **kw)
         except O.OracleError as e:
             if e.kind != "DUPDST":
                 raise
@@ -163,7 +163,7 @@ def m_dupdst_allowed(O):
 
 def m_reblock_dst_uses_src_size(O):
     orig = O.token_segments
-    O.token_segments = lambda requests, bs_src, bs_dst: orig(requests, bs_src, bs_src)
+    O.token_segments = lambda requests, bs_src, bs_dst, window=0: orig(requests, bs_src, bs_src, window)
 
 
 def m_reblock_no_split(O):
@@ -171,10 +171,78 @@ def m_reblock_no_split(O):
                                                            seg.dst_slot, seg.ntok)])
 
 
+def m_window_off_by_one(O):
+    def window_start(n, w, bss, bsd):
+        if w <= 0:
+            return 0
+        first = max(0, n - w)
+        return max(first // bss * bss, first // bsd * bsd)
+    O.window_start = window_start
+
+
+def m_window_token_granular(O):
+    O.window_start = lambda n, w, bss, bsd: max(0, n - w + 1) if w > 0 else 0
+
+
+def m_window_ignored(O):
+    O.window_start = lambda n, w, bss, bsd: 0
+
+
+def m_window_src_blocks_only(O):
+    O.window_start = lambda n, w, bss, bsd: (max(0, n - w + 1) // bss * bss) if w > 0 else 0
+
+
+def m_latent_staging_two_regions(O):
+    O.staging_bytes = lambda plan, l0, l1: (l1 - l0) * 2 * O.staging_region_bytes(plan)
+
+
+def m_state_moves_empty(O):
+    orig = O.make_state_plan
+
+    def make_state_plan(gs, gd, requests):
+        return orig(gs, gd, [O.Request(max(q.num_tokens, 1) if len(q.src_ids) and len(q.dst_ids) else 0,
+                                       q.src_ids, q.dst_ids) for q in requests])
+    O.make_state_plan = make_state_plan
+
+
+def m_state_one_slot_size(O):
+    orig = O.make_state_plan
+
+    def make_state_plan(gs, gd, requests):
+        p = orig(gs, gd, requests)
+        sb0, sb1 = gs.slot_bytes
+        t1 = [(so // sb1 * sb0, do // sb1 * sb0, ln // sb1 * sb0) for so, do, ln in p.triples[1]]
+        return O.StatePlan(gs, gd, p.runs, (p.triples[0], t1))
+    O.make_state_plan = make_state_plan
+
+
+def m_state_merge_src_only(O):
+    orig = O.make_state_plan
+
+    def make_state_plan(gs, gd, requests):
+        p = orig(gs, gd, requests)
+        lists = []
+        for r in range(2):
+            sb = gs.slot_bytes[r]
+            out = []
+            for run in p.runs:
+                so, do = run.src0 * sb, run.dst0 * sb
+                if out and out[-1][0] + out[-1][2] == so:
+                    out[-1][2] += sb
+                else:
+                    out.append([so, do, sb])
+            lists.append([tuple(t) for t in out])
+        return O.StatePlan(gs, gd, p.runs, (lists[0], lists[1]))
+    O.make_state_plan = make_state_plan
+
+
 MUTATIONS = [m_no_minus_one, m_minus_two, m_merge_src_only, m_hnd_swap, m_tail_ignored,
              m_tail_off_by_one, m_coalesce_src_only, m_scale_swap, m_reuse_strict, m_reuse_turn,
              m_nhd_row_swap, m_pack_kv_order, m_scale_pad_garbage, m_hnd_tail_one_segment,
-             m_dupdst_allowed, m_reblock_dst_uses_src_size, m_reblock_no_split]
+             m_dupdst_allowed, m_reblock_dst_uses_src_size, m_reblock_no_split,
+             m_window_off_by_one, m_window_token_granular, m_window_ignored, m_window_src_blocks_only,
+             m_latent_staging_two_regions, m_state_moves_empty, m_state_one_slot_size,
+             m_state_merge_src_only]
 
 
 @pytest.mark.parametrize("mutation", MUTATIONS, ids=lambda f: f.__name__)
