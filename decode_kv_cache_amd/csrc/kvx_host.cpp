@@ -121,9 +121,13 @@ int kvx_pool_create(const kvx_pool_desc* d, kvx_pool** out) {
     return fail(KVX_E_INVAL, "kvx_pool_create: elem_bytes %d not in {1,2,4}", d->elem_bytes);
   if (d->layout != KVX_NHD && d->layout != KVX_HND)
     return fail(KVX_E_INVAL, "kvx_pool_create: unknown layout %d", d->layout);
-  if (!d->k_base || !d->v_base) return fail(KVX_E_INVAL, "kvx_pool_create: null base array");
-  if ((d->k_scale == nullptr) != (d->v_scale == nullptr))
+  if (!d->k_base) return fail(KVX_E_INVAL, "kvx_pool_create: null k_base array");
+  const bool latent = d->v_base == nullptr;  // one region per layer (MLA)
+  if (latent && d->v_scale)
+    return fail(KVX_E_INVAL, "kvx_pool_create: v_scale set for a pool without a V region");
+  if (!latent && (d->k_scale == nullptr) != (d->v_scale == nullptr))
     return fail(KVX_E_INVAL, "kvx_pool_create: k_scale and v_scale must both be set or both NULL");
+  if (d->sliding_window < 0) return fail(KVX_E_INVAL, "kvx_pool_create: negative sliding_window");
   if (d->block_size > 32768)
     return fail(KVX_E_UNSUPPORTED, "kvx_pool_create: block_size %d above 32768", d->block_size);
   if ((int64_t(d->head_dim) * d->elem_bytes) % 16)
@@ -139,11 +143,13 @@ int kvx_pool_create(const kvx_pool_desc* d, kvx_pool** out) {
   g.D = d->head_dim;
   g.E = d->elem_bytes;
   g.layout = d->layout;
+  g.nreg = latent ? 1 : 2;
+  g.window = d->sliding_window;
   g.scales = d->k_scale != nullptr;
   try {
     for (int l = 0; l < g.L; ++l) {
       void* k = d->k_base[l];
-      void* v = d->v_base[l];
+      void* v = latent ? k : d->v_base[l];
       if (!k || !v) {
         delete p;
         return fail(KVX_E_INVAL, "kvx_pool_create: null base for layer %d", l);
@@ -153,10 +159,10 @@ int kvx_pool_create(const kvx_pool_desc* d, kvx_pool** out) {
         return fail(KVX_E_UNSUPPORTED, "kvx_pool_create: layer %d base not 16-byte aligned", l);
       }
       g.k.push_back(k);
-      g.v.push_back(v);
+      if (!latent) g.v.push_back(v);
       if (g.scales) {
         float* ks = d->k_scale[l];
-        float* vs = d->v_scale[l];
+        float* vs = latent ? ks : d->v_scale[l];
         if (!ks || !vs) {
           delete p;
           return fail(KVX_E_INVAL, "kvx_pool_create: null scale pointer for layer %d", l);
@@ -166,12 +172,53 @@ int kvx_pool_create(const kvx_pool_desc* d, kvx_pool** out) {
           return fail(KVX_E_UNSUPPORTED, "kvx_pool_create: layer %d scales not 4-byte aligned", l);
         }
         g.ks.push_back(ks);
-        g.vs.push_back(vs);
+        if (!latent) g.vs.push_back(vs);
       }
     }
   } catch (const std::bad_alloc&) {
     delete p;
     return fail(KVX_E_NOMEM, "kvx_pool_create: out of host memory");
+  }
+  *out = p;
+  return KVX_OK;
+}
+
+int kvx_state_pool_create(const kvx_state_pool_desc* d, kvx_pool** out) {
+  if (!d || !out) return fail(KVX_E_INVAL, "kvx_state_pool_create: null argument");
+  if (d->num_layers < 1 || d->num_slots < 1)
+    return fail(KVX_E_INVAL, "kvx_state_pool_create: counts must be >= 1");
+  if (!d->base[0] || !d->base[1]) return fail(KVX_E_INVAL, "kvx_state_pool_create: null base array");
+  for (int r = 0; r < 2; ++r)
+    if (d->slot_bytes[r] < 16 || d->slot_bytes[r] % 16)
+      return fail(KVX_E_UNSUPPORTED, "kvx_state_pool_create: slot_bytes[%d]=%lld not a positive multiple of 16",
+                  r, (long long)d->slot_bytes[r]);
+  kvx_pool* p = new (std::nothrow) kvx_pool;
+  if (!p) return fail(KVX_E_NOMEM, "kvx_state_pool_create: out of host memory");
+  Geom& g = p->g;
+  g.state = true;
+  g.L = d->num_layers;
+  g.NB = d->num_slots;
+  g.nreg = 2;
+  g.slot_bytes[0] = d->slot_bytes[0];
+  g.slot_bytes[1] = d->slot_bytes[1];
+  try {
+    for (int l = 0; l < g.L; ++l) {
+      void* b0 = d->base[0][l];
+      void* b1 = d->base[1][l];
+      if (!b0 || !b1) {
+        delete p;
+        return fail(KVX_E_INVAL, "kvx_state_pool_create: null base for layer %d", l);
+      }
+      if ((uintptr_t(b0) | uintptr_t(b1)) & 15) {
+        delete p;
+        return fail(KVX_E_UNSUPPORTED, "kvx_state_pool_create: layer %d base not 16-byte aligned", l);
+      }
+      g.k.push_back(b0);
+      g.v.push_back(b1);
+    }
+  } catch (const std::bad_alloc&) {
+    delete p;
+    return fail(KVX_E_NOMEM, "kvx_state_pool_create: out of host memory");
   }
   *out = p;
   return KVX_OK;
@@ -211,27 +258,31 @@ void build_triples(kvx_plan_t* p) {
     const int64_t ss = slot_src(b.slots), ds = slot_dst(b.slots);
     const int64_t sbase = int64_t(b.src) * gs.block_bytes(), dbase = int64_t(b.dst) * gd.block_bytes();
     if (gs.layout == KVX_NHD) {
-      emit(p->triples, sbase + ss * tb, dbase + ds * tb, int64_t(b.nslots) * tb);
+      emit(p->triples[0], sbase + ss * tb, dbase + ds * tb, int64_t(b.nslots) * tb);
     } else {
       for (int h = 0; h < gs.H; ++h)
-        emit(p->triples, sbase + (int64_t(h) * gs.BS + ss) * rb, dbase + (int64_t(h) * gd.BS + ds) * rb,
+        emit(p->triples[0], sbase + (int64_t(h) * gs.BS + ss) * rb, dbase + (int64_t(h) * gd.BS + ds) * rb,
              int64_t(b.nslots) * rb);
     }
   }
 }
 
-// Split the triples into workgroup-sized pieces and give each its offset in
-// the staging region (the exclusive prefix of the triple lengths).
+// Split each triple list into workgroup-sized pieces and give each its
+// offset in its region's staging (the exclusive prefix of the triple
+// lengths).  Pieces of list r carry r as their region tag.
 void build_pieces(kvx_plan_t* p) {
-  int64_t stg = 0;
-  for (const kvx_triple& t : p->triples) {
-    for (int64_t o = 0; o < t.len; o += kPieceBytes) {
-      const int64_t len = std::min<int64_t>(kPieceBytes, t.len - o);
-      p->pieces.push_back(Piece{t.src_off + o, t.dst_off + o, stg + o, int32_t(len), 0});
+  for (int32_t r = 0; r < p->nlists; ++r) {
+    int64_t stg = 0;
+    for (const kvx_triple& t : p->triples[r]) {
+      for (int64_t o = 0; o < t.len; o += kPieceBytes) {
+        const int64_t len = std::min<int64_t>(kPieceBytes, t.len - o);
+        p->pieces.push_back(Piece{t.src_off + o, t.dst_off + o, stg + o, int32_t(len), r});
+      }
+      stg += t.len;
     }
-    stg += t.len;
+    p->payload[r] = stg;
   }
-  p->payload_bytes = stg;
+  if (p->nlists == 1) p->payload[1] = p->payload[0];
 }
 
 int upload(kvx_plan_t* p, hipStream_t s) {
@@ -274,9 +325,21 @@ void release(kvx_plan_t* p) {
   kvx::plan_free_idle(p);
 }
 
+// First token a sliding-window group moves ([MORI] §6: sliding-window layers
+// get their own geometry).  The receiving side's next query, at position n,
+// sees positions n-W+1 .. n; blocks holding none of them are skipped, so the
+// move starts at the later of the two sides' starts of the block holding
+// position n-W+1.
+int64_t window_first(int64_t n, int32_t w, int64_t bss, int64_t bsd) {
+  if (w <= 0) return 0;
+  const int64_t first = std::max<int64_t>(0, n - w + 1);
+  return std::max(first / bss * bss, first / bsd * bsd);
+}
+
 // Validate the requests and build the plan's block list, runs and triples.
 // Validation order per request: token count, both list lengths, source IDs,
-// then destination IDs (range, then reuse across the plan).
+// then destination IDs (range, then reuse across the plan).  With a sliding
+// window, the entries of skipped blocks are not looked at.
 int build_plan(kvx_plan_t* p, int32_t R, const int64_t* num_tokens, const int64_t* so,
                const int64_t* dof, const int32_t* src_ids, const int32_t* dst_ids) {
   const Geom& gs = p->src;
@@ -297,35 +360,38 @@ int build_plan(kvx_plan_t* p, int32_t R, const int64_t* num_tokens, const int64_
     if (!src_ids || !dst_ids) return fail(KVX_E_INVAL, "kvx_plan: null block ID array");
     const int32_t* S = src_ids + so[r];
     const int32_t* Dd = dst_ids + dof[r];
-    for (int64_t i = 0; i < nbs; ++i)
+    const int64_t t0 = window_first(n, gs.window, bss, bsd);
+    const int64_t js = t0 / bss;
+    for (int64_t i = js; i < nbs; ++i)
       if (S[i] < 0 || S[i] >= gs.NB)
         return fail(KVX_E_RANGE, "kvx_plan: request %d: src block %d outside [0,%d)", r, S[i], gs.NB);
-    for (int64_t i = 0; i < nbd; ++i) {
+    for (int64_t i = t0 / bsd; i < nbd; ++i) {
       if (Dd[i] < 0 || Dd[i] >= gd.NB)
         return fail(KVX_E_RANGE, "kvx_plan: request %d: dst block %d outside [0,%d)", r, Dd[i], gd.NB);
       if (dst_used[size_t(Dd[i])]) return fail(KVX_E_DUPDST, "kvx_plan: dst block %d used twice", Dd[i]);
       dst_used[size_t(Dd[i])] = 1;
     }
+    if (t0 >= n) continue;
     if (bss == bsd) {
       // Merge ([PUSH] "Threading-Modell"; [MORI] §3.1, §6): a new run starts
-      // at the request's first block and wherever either side is not the
-      // previous block + 1.
+      // at the request's first moved block and wherever either side is not
+      // the previous block + 1.
       const int32_t tail = int32_t(n - (nbs - 1) * bss);
-      int64_t start = 0;
-      for (int64_t i = 1; i <= nbs; ++i) {
+      int64_t start = js;
+      for (int64_t i = js + 1; i <= nbs; ++i) {
         if (i == nbs || S[i] != S[i - 1] + 1 || Dd[i] != Dd[i - 1] + 1) {
           p->runs.push_back(kvx_run{S[start], Dd[start], int32_t(i - start), i == nbs ? tail : int32_t(bss)});
           start = i;
         }
       }
-      for (int64_t i = 0; i < nbs; ++i)
+      for (int64_t i = js; i < nbs; ++i)
         p->blocks.push_back(BlockPair{S[i], Dd[i], i == nbs - 1 ? tail : int32_t(bss), 0});
     } else {
       // Different block sizes ([PUSH] "Implementierungsdetails" step 3):
       // token t sits in source block S[t / BSs], slot t % BSs and lands in
       // destination block Dd[t / BSd], slot t % BSd.  Cut the token range
       // wherever either side enters a new block.
-      for (int64_t t = 0; t < n;) {
+      for (int64_t t = t0; t < n;) {
         const int64_t ss = t % bss, ds = t % bsd;
         const int64_t k = std::min({bss - ss, bsd - ds, n - t});
         p->blocks.push_back(BlockPair{S[t / bss], Dd[t / bsd], int32_t(k), pack_slots(ss, ds)});
@@ -338,6 +404,41 @@ int build_plan(kvx_plan_t* p, int32_t R, const int64_t* num_tokens, const int64_
     build_pieces(p);
   }
   p->scale_seg_bytes = gs.scales ? pad16(4 * int64_t(p->blocks.size())) : 0;
+  return KVX_OK;
+}
+
+// State-slot plan ([MORI] §6: the conv and SSM regions move slot by slot).
+// A request moving at least one token moves the slot its list starts with;
+// each one is a run, and each region's triples merge neighbouring slots.
+int build_state_plan(kvx_plan_t* p, int32_t R, const int64_t* num_tokens, const int64_t* so,
+                     const int64_t* dof, const int32_t* src_ids, const int32_t* dst_ids) {
+  const Geom& gs = p->src;
+  const Geom& gd = p->dst;
+  if (R > 0 && (so[0] < 0 || dof[0] < 0)) return fail(KVX_E_INVAL, "kvx_plan: negative first offset");
+  std::vector<uint8_t> dst_used(size_t(gd.NB), 0);
+  for (int32_t r = 0; r < R; ++r) {
+    const int64_t n = num_tokens[r];
+    if (n < 0) return fail(KVX_E_INVAL, "kvx_plan: request %d: negative token count", r);
+    if (so[r + 1] < so[r] || dof[r + 1] < dof[r])
+      return fail(KVX_E_INVAL, "kvx_plan: offsets not monotone at request %d", r);
+    if (n == 0) continue;
+    if (so[r + 1] - so[r] < 1 || dof[r + 1] - dof[r] < 1)
+      return fail(KVX_E_INVAL, "kvx_plan: request %d: no state slot", r);
+    if (!src_ids || !dst_ids) return fail(KVX_E_INVAL, "kvx_plan: null slot ID array");
+    const int32_t s = src_ids[so[r]], d = dst_ids[dof[r]];
+    if (s < 0 || s >= gs.NB)
+      return fail(KVX_E_RANGE, "kvx_plan: request %d: src slot %d outside [0,%d)", r, s, gs.NB);
+    if (d < 0 || d >= gd.NB)
+      return fail(KVX_E_RANGE, "kvx_plan: request %d: dst slot %d outside [0,%d)", r, d, gd.NB);
+    if (dst_used[size_t(d)]) return fail(KVX_E_DUPDST, "kvx_plan: dst slot %d used twice", d);
+    dst_used[size_t(d)] = 1;
+    p->runs.push_back(kvx_run{s, d, 1, 1});
+    for (int reg = 0; reg < 2; ++reg) {
+      const int64_t sb = gs.slot_bytes[reg];
+      emit(p->triples[reg], int64_t(s) * sb, int64_t(d) * sb, sb);
+    }
+  }
+  build_pieces(p);
   return KVX_OK;
 }
 
@@ -357,10 +458,18 @@ int kvx_plan(const kvx_pool* src, const kvx_pool* dst, int32_t num_requests,
     return fail(KVX_E_INVAL, "kvx_plan: null num_tokens or offsets");
   const Geom& gs = src->g;
   const Geom& gd = dst->g;
-  if (gs.L != gd.L || gs.D != gd.D || gs.E != gd.E || gs.scales != gd.scales)
-    return fail(KVX_E_MISMATCH, "kvx_plan: pools differ in layers/head_dim/elem_bytes/scales");
-  if (gs.BS != gd.BS && gs.scales)
-    return fail(KVX_E_UNSUPPORTED, "kvx_plan: per-block scales need equal block sizes (%d vs %d)", gs.BS, gd.BS);
+  if (gs.state != gd.state) return fail(KVX_E_MISMATCH, "kvx_plan: one pool holds state slots, the other KV");
+  if (gs.state) {
+    if (gs.L != gd.L || gs.slot_bytes[0] != gd.slot_bytes[0] || gs.slot_bytes[1] != gd.slot_bytes[1])
+      return fail(KVX_E_MISMATCH, "kvx_plan: state pools differ in layers or slot sizes");
+  } else {
+    if (gs.L != gd.L || gs.D != gd.D || gs.E != gd.E || gs.scales != gd.scales || gs.nreg != gd.nreg)
+      return fail(KVX_E_MISMATCH, "kvx_plan: pools differ in layers/head_dim/elem_bytes/scales/regions");
+    if (gs.window != gd.window)
+      return fail(KVX_E_MISMATCH, "kvx_plan: sliding windows differ (%d vs %d)", gs.window, gd.window);
+    if (gs.BS != gd.BS && gs.scales)
+      return fail(KVX_E_UNSUPPORTED, "kvx_plan: per-block scales need equal block sizes (%d vs %d)", gs.BS, gd.BS);
+  }
 
   kvx_plan_t* p = new (std::nothrow) kvx_plan_t;
   if (!p) return fail(KVX_E_NOMEM, "kvx_plan: out of host memory");
@@ -368,9 +477,12 @@ int kvx_plan(const kvx_pool* src, const kvx_pool* dst, int32_t num_requests,
   try {
     p->src = gs;
     p->dst = gd;
-    p->push_ok = gs.H == gd.H && gs.layout == gd.layout;
+    p->push_ok = gs.state || (gs.H == gd.H && gs.layout == gd.layout);
     p->host_only = (flags & KVX_PLAN_HOST_ONLY) != 0;
-    rc = build_plan(p, num_requests, num_tokens, src_offsets, dst_offsets, src_ids, dst_ids);
+    p->nreg = gs.nreg;
+    p->nlists = gs.state ? 2 : 1;
+    rc = gs.state ? build_state_plan(p, num_requests, num_tokens, src_offsets, dst_offsets, src_ids, dst_ids)
+                  : build_plan(p, num_requests, num_tokens, src_offsets, dst_offsets, src_ids, dst_ids);
   } catch (const std::bad_alloc&) {
     rc = fail(KVX_E_NOMEM, "kvx_plan: out of host memory");
   }
@@ -385,7 +497,7 @@ int kvx_plan(const kvx_pool* src, const kvx_pool* dst, int32_t num_requests,
 
 int kvx_plan_runs(const kvx_plan_t* p, kvx_run* out, int64_t cap, int64_t* n) {
   if (!p || !n) return fail(KVX_E_INVAL, "kvx_plan_runs: null argument");
-  if (p->src.BS != p->dst.BS)
+  if (!p->src.state && p->src.BS != p->dst.BS)
     return fail(KVX_E_MISMATCH, "kvx_plan_runs: block runs need equal block sizes (%d vs %d)", p->src.BS, p->dst.BS);
   const int64_t cnt = int64_t(p->runs.size());
   if (out && cap >= cnt) std::copy(p->runs.begin(), p->runs.end(), out);
@@ -396,12 +508,13 @@ int kvx_plan_runs(const kvx_plan_t* p, kvx_run* out, int64_t cap, int64_t* n) {
 int kvx_plan_triples(const kvx_plan_t* p, int32_t layer, int32_t kv, kvx_triple* out, int64_t cap,
                      int64_t* n) {
   if (!p || !n) return fail(KVX_E_INVAL, "kvx_plan_triples: null argument");
-  if (layer < 0 || layer >= p->src.L || kv < 0 || kv > 1)
-    return fail(KVX_E_RANGE, "kvx_plan_triples: layer %d / kv %d out of range", layer, kv);
+  if (layer < 0 || layer >= p->src.L || kv < 0 || kv >= p->nreg)
+    return fail(KVX_E_RANGE, "kvx_plan_triples: layer %d / region %d out of range", layer, kv);
   if (!p->push_ok)
     return fail(KVX_E_MISMATCH, "kvx_plan_triples: pools differ in head count or layout");
-  const int64_t cnt = int64_t(p->triples.size());
-  if (out && cap >= cnt) std::copy(p->triples.begin(), p->triples.end(), out);
+  const std::vector<kvx_triple>& t = p->region_triples(kv);
+  const int64_t cnt = int64_t(t.size());
+  if (out && cap >= cnt) std::copy(t.begin(), t.end(), out);
   *n = cnt;
   return KVX_OK;
 }
@@ -410,8 +523,10 @@ int kvx_plan_bytes(const kvx_plan_t* p, int64_t* rd, int64_t* wr) {
   if (!p || !rd || !wr) return fail(KVX_E_INVAL, "kvx_plan_bytes: null argument");
   if (!p->push_ok) return fail(KVX_E_MISMATCH, "kvx_plan_bytes: pools differ in head count or layout");
   const int64_t sc = p->src.scales ? 4 * int64_t(p->blocks.size()) : 0;
-  *rd = 2 * (p->payload_bytes + sc);
-  *wr = *rd;
+  int64_t b = 0;
+  for (int r = 0; r < p->nreg; ++r) b += p->payload[r] + sc;
+  *rd = b;
+  *wr = b;
   return KVX_OK;
 }
 
@@ -422,7 +537,7 @@ int kvx_staging_bytes(const kvx_plan_t* p, int32_t l0, int32_t l1, int64_t* byte
   if (l0 < 0 || l1 < l0 || l1 > p->src.L)
     return fail(KVX_E_RANGE, "kvx_staging_bytes: layers [%d,%d) outside [0,%d]", l0, l1, p->src.L);
   if (!p->push_ok) return fail(KVX_E_MISMATCH, "kvx_staging_bytes: pools differ in head count or layout");
-  *bytes = int64_t(l1 - l0) * 2 * (p->payload_bytes + p->scale_seg_bytes);
+  *bytes = int64_t(l1 - l0) * p->stg_layer();
   return KVX_OK;
 }
 

@@ -11,17 +11,19 @@
 
 namespace kvx {
 
-// One workgroup's share of a (layer, K/V) region: a contiguous byte range on
-// the source side, on the destination side and inside the staging region.
-// All offsets are region-relative and identical for every layer and for K
-// and V, so one list serves every launch.  32 bytes: read with one scalar
-// load per workgroup.
+// One workgroup's share of a (layer, region) pair: a contiguous byte range
+// on the source side, on the destination side and inside the staging region.
+// All offsets are region-relative and identical for every layer, so one list
+// serves every launch.  When all regions share one triple list (K and V) the
+// launch's y index picks the region and `reg` is 0; when each region has its
+// own list (state slots) the pieces of all lists are concatenated and `reg`
+// names the region.  32 bytes: read with one scalar load per workgroup.
 struct Piece {
   int64_t src_off;
   int64_t dst_off;
   int64_t stg_off;
   int32_t len;  // bytes, multiple of 16, <= kPieceBytes
-  int32_t pad;
+  int32_t reg;  // region offset added to blockIdx.y
 };
 static_assert(sizeof(Piece) == 32, "Piece is 32 bytes");
 
@@ -49,11 +51,21 @@ constexpr int kThreads = KVX_THREADS;            // 4 wave64 per workgroup
 constexpr int kVecPerThread = KVX_VEC_PER_THREAD;  // 16-B vectors each lane keeps in flight
 constexpr int64_t kPieceBytes = int64_t(kThreads) * kVecPerThread * 16;  // 32 KiB
 
+// One side's layer group.  Attention pools: nreg regions (K and V, or one
+// latent region) of NB blocks.  State pools: two regions of NB slots of
+// slot_bytes[r] bytes; BS, H, D, E and layout are unused.
 struct Geom {
   int32_t L = 0, NB = 0, BS = 0, H = 0, D = 0, E = 0, layout = 0;
+  int32_t nreg = 2;
+  int32_t window = 0;          // sliding window in positions, 0 = full attention
+  bool state = false;
+  int64_t slot_bytes[2] = {0, 0};
   bool scales = false;
-  std::vector<void*> k, v;
+  std::vector<void*> k, v;     // region 0 and region 1 bases per layer (v empty with one region)
   std::vector<float*> ks, vs;
+
+  void* base(int r, int l) const { return r == 0 ? k[size_t(l)] : v[size_t(l)]; }
+  float* scale(int r, int l) const { return r == 0 ? ks[size_t(l)] : vs[size_t(l)]; }
 
   int64_t row_bytes() const { return int64_t(D) * E; }
   int64_t token_bytes() const { return int64_t(H) * row_bytes(); }
@@ -73,12 +85,21 @@ struct kvx_plan_s {
   kvx::Geom src, dst;
   bool push_ok = false;   // same head count and layout: triples and pieces exist
   bool host_only = false;
+  int32_t nreg = 2;       // regions per layer
+  int32_t nlists = 1;     // 1: one triple list shared by every region; 2: one per region
   std::vector<kvx_run> runs;
-  std::vector<kvx_triple> triples;
-  std::vector<kvx::Piece> pieces;
+  std::vector<kvx_triple> triples[2];
+  std::vector<kvx::Piece> pieces;     // list 0's pieces, then list 1's
   std::vector<kvx::BlockPair> blocks;
-  int64_t payload_bytes = 0;    // per (layer, K/V) region
+  int64_t payload[2] = {0, 0};  // moved bytes per (layer, region)
   int64_t scale_seg_bytes = 0;  // per region inside staging (16-B padded), 0 without scales
+
+  const std::vector<kvx_triple>& region_triples(int r) const { return triples[nlists == 1 ? 0 : r]; }
+  // Bytes of one region (payload and scale segment) inside a layer's staging,
+  // the offset of region r inside the layer, and one layer's staging bytes.
+  int64_t stg_region(int r) const { return payload[r] + scale_seg_bytes; }
+  int64_t stg_offset(int r) const { return r == 0 ? 0 : stg_region(0); }
+  int64_t stg_layer() const { return nreg == 1 ? stg_region(0) : stg_region(0) + stg_region(1); }
 
   // device side
   void* dev_buf = nullptr;

@@ -3,8 +3,8 @@
 // kvx_copy_heads, with their C entry points.
 //
 // The work is pure data movement bound by HBM bandwidth: no arithmetic, no
-// MFMA.  Each workgroup (256 lanes = 4 wave64) owns one 16 KiB piece of one
-// (layer, K/V) region; every lane issues all of its 16-byte loads before its
+// MFMA.  Each workgroup (256 lanes = 4 wave64) owns one 32 KiB piece of one
+// (layer, region) pair; every lane issues all of its 16-byte loads before its
 // first store so that a workgroup keeps the whole piece in flight.  Piece
 // descriptors are workgroup-uniform and come in through scalar loads.
 //
@@ -34,8 +34,8 @@ struct CopyArgs {
   int32_t n_blocks;          // planned blocks (scale entries)
   int32_t n_scale_slots;     // scale entries to write (pack: padded to 16 B)
   int32_t first_scale_wg;    // x index of the first scale workgroup (== n_pieces)
-  const uint8_t* in[2];      // K, V source region (pool or staging)
-  uint8_t* out[2];           // K, V destination region (pool or staging)
+  const uint8_t* in[2];      // region 0 / 1 source (pool or staging): K, V or conv, SSM
+  uint8_t* out[2];           // region 0 / 1 destination (pool or staging)
   const uint32_t* in_sc[2];  // scale source (pool scales or staging scale segment)
   uint32_t* out_sc[2];
 };
@@ -55,14 +55,15 @@ constexpr int kBufferWord3 = 0x00020000;  // raw byte buffer, gfx9 family
 __device__ __forceinline__ v4u ld_stream(const v4u* p) { return __builtin_nontemporal_load(p); }
 __device__ __forceinline__ void st_stream(v4u* p, v4u v) { __builtin_nontemporal_store(v, p); }
 
-// One workgroup copies one piece of the K (blockIdx.y == 0) or V (== 1)
-// region; workgroups past the pieces copy the planned blocks' scales.
+// One workgroup copies one piece of region blockIdx.y + piece.reg (one list
+// shared by K and V: y picks the region; one list per region: the tag does);
+// workgroups past the pieces copy the planned blocks' scales.
 template <int MODE>
 __global__ __launch_bounds__(kThreads) void copy_kernel(CopyArgs a) {
-  const int kv = blockIdx.y;
   const int x = blockIdx.x;
   if (x < a.n_pieces) {
     const Piece pc = a.pieces[x];
+    const int kv = int(blockIdx.y) + pc.reg;
     const int64_t ioff = MODE == kUnpack ? pc.stg_off : pc.src_off;
     const int64_t ooff = MODE == kPack ? pc.stg_off : pc.dst_off;
     // One buffer resource per piece (base = piece start, size = piece
@@ -82,6 +83,7 @@ __global__ __launch_bounds__(kThreads) void copy_kernel(CopyArgs a) {
       __builtin_amdgcn_raw_buffer_store_b128(r[k], rd, (t + k * kThreads) * 16, 0, KVX_ST_AUX);
     return;
   }
+  const int kv = blockIdx.y;
   const int i = (x - a.first_scale_wg) * kThreads + threadIdx.x;
   if (MODE == kPush) {
     if (i < a.n_blocks) {
@@ -114,8 +116,9 @@ struct HeadArgs {
 constexpr int kHeadUnroll = 4;
 
 // One workgroup moves the head slice of one planned block (or block piece,
-// with different block sizes per side) of the K or V region.  Lanes walk the block's rows in destination order so stores are
-// contiguous; each lane keeps kHeadUnroll vectors in flight.
+// with different block sizes per side) of region blockIdx.y (K, V or the
+// latent region).  Lanes walk the block's rows in destination order so
+// stores are contiguous; each lane keeps kHeadUnroll vectors in flight.
 __global__ __launch_bounds__(kThreads) void heads_kernel(HeadArgs a) {
   const int kv = blockIdx.y;
   const BlockPair b = a.blocks[blockIdx.x];
@@ -162,6 +165,8 @@ static int launch_copy(kvx_plan_t* p, CopyArgs a, int64_t scale_slots, hipStream
                        hipEvent_t started = nullptr, hipEvent_t finished = nullptr) {
   const int64_t np = int64_t(p->pieces.size());
   const bool scales = a.in_sc[0] != nullptr;
+  // one shared list: one y row per region; one list per region: the tags
+  const unsigned gy = p->nlists == 1 ? unsigned(p->nreg) : 1u;
   const int64_t nsw = scales ? scale_wgs(scale_slots) : 0;
   a.blocks = p->d_blocks;
   a.n_blocks = int32_t(p->blocks.size());
@@ -178,10 +183,10 @@ static int launch_copy(kvx_plan_t* p, CopyArgs a, int64_t scale_slots, hipStream
     if (gx > 0) {
       if (started || finished) {
         // timestamps come from the dispatch packet itself: no extra packets
-        hipExtLaunchKernelGGL(copy_kernel<MODE>, dim3(unsigned(gx), 2), dim3(kThreads), 0, s,
+        hipExtLaunchKernelGGL(copy_kernel<MODE>, dim3(unsigned(gx), gy), dim3(kThreads), 0, s,
                               first == 0 ? started : nullptr, last ? finished : nullptr, 0u, a);
       } else {
-        hipLaunchKernelGGL(copy_kernel<MODE>, dim3(unsigned(gx), 2), dim3(kThreads), 0, s, a);
+        hipLaunchKernelGGL(copy_kernel<MODE>, dim3(unsigned(gx), gy), dim3(kThreads), 0, s, a);
       }
     }
     first += cnt;
@@ -217,15 +222,13 @@ int kvx_push_layer_timed(const kvx_plan_t* cp, int32_t layer, hipEvent_t ready, 
   if (rc) return rc;
   if (p->pieces.empty() && p->blocks.empty()) return KVX_OK;
   CopyArgs a{};
-  a.in[0] = static_cast<const uint8_t*>(p->src.k[layer]);
-  a.in[1] = static_cast<const uint8_t*>(p->src.v[layer]);
-  a.out[0] = static_cast<uint8_t*>(p->dst.k[layer]);
-  a.out[1] = static_cast<uint8_t*>(p->dst.v[layer]);
-  if (p->src.scales) {
-    a.in_sc[0] = reinterpret_cast<const uint32_t*>(p->src.ks[layer]);
-    a.in_sc[1] = reinterpret_cast<const uint32_t*>(p->src.vs[layer]);
-    a.out_sc[0] = reinterpret_cast<uint32_t*>(p->dst.ks[layer]);
-    a.out_sc[1] = reinterpret_cast<uint32_t*>(p->dst.vs[layer]);
+  for (int r = 0; r < p->nreg; ++r) {
+    a.in[r] = static_cast<const uint8_t*>(p->src.base(r, layer));
+    a.out[r] = static_cast<uint8_t*>(p->dst.base(r, layer));
+    if (p->src.scales) {
+      a.in_sc[r] = reinterpret_cast<const uint32_t*>(p->src.scale(r, layer));
+      a.out_sc[r] = reinterpret_cast<uint32_t*>(p->dst.scale(r, layer));
+    }
   }
   return launch_copy<kPush>(p, a, int64_t(p->blocks.size()), stream, started, finished);
 }
@@ -238,7 +241,7 @@ static int staging_call(const kvx_plan_t* cp, int32_t l0, int32_t l1, const void
   if (!p->push_ok) return fail(KVX_E_MISMATCH, "%s: pools differ in head count or layout", fn);
   if (l0 < 0 || l1 < l0 || l1 > p->src.L)
     return fail(KVX_E_RANGE, "%s: layers [%d,%d) outside [0,%d]", fn, l0, l1, p->src.L);
-  const int64_t need = int64_t(l1 - l0) * 2 * (p->payload_bytes + p->scale_seg_bytes);
+  const int64_t need = int64_t(l1 - l0) * p->stg_layer();
   if (need > 0 && !staging) return fail(KVX_E_INVAL, "%s: null staging buffer", fn);
   if (cap < need) return fail(KVX_E_INVAL, "%s: staging holds %lld bytes, needs %lld", fn,
                               (long long)cap, (long long)need);
@@ -254,21 +257,19 @@ int kvx_pack(const kvx_plan_t* cp, int32_t l0, int32_t l1, void* staging, int64_
   if (rc) return rc;
   rc = enqueue_waits(p, nullptr, stream);
   if (rc) return rc;
-  const int64_t region = p->payload_bytes + p->scale_seg_bytes;
-  if (region == 0) return KVX_OK;
+  const int64_t layer_bytes = p->stg_layer();
+  if (layer_bytes == 0) return KVX_OK;
   uint8_t* stg = static_cast<uint8_t*>(staging);
   for (int32_t l = l0; l < l1; ++l) {
     CopyArgs a{};
-    a.in[0] = static_cast<const uint8_t*>(p->src.k[l]);
-    a.in[1] = static_cast<const uint8_t*>(p->src.v[l]);
-    for (int kv = 0; kv < 2; ++kv) {
-      uint8_t* reg = stg + (int64_t(l - l0) * 2 + kv) * region;
-      a.out[kv] = reg;
-      if (p->src.scales) a.out_sc[kv] = reinterpret_cast<uint32_t*>(reg + p->payload_bytes);
-    }
-    if (p->src.scales) {
-      a.in_sc[0] = reinterpret_cast<const uint32_t*>(p->src.ks[l]);
-      a.in_sc[1] = reinterpret_cast<const uint32_t*>(p->src.vs[l]);
+    for (int r = 0; r < p->nreg; ++r) {
+      uint8_t* reg = stg + int64_t(l - l0) * layer_bytes + p->stg_offset(r);
+      a.in[r] = static_cast<const uint8_t*>(p->src.base(r, l));
+      a.out[r] = reg;
+      if (p->src.scales) {
+        a.in_sc[r] = reinterpret_cast<const uint32_t*>(p->src.scale(r, l));
+        a.out_sc[r] = reinterpret_cast<uint32_t*>(reg + p->payload[r]);
+      }
     }
     rc = launch_copy<kPack>(p, a, p->scale_seg_bytes / 4, stream);
     if (rc) return rc;
@@ -283,21 +284,19 @@ int kvx_unpack(const kvx_plan_t* cp, int32_t l0, int32_t l1, const void* staging
   if (rc) return rc;
   rc = enqueue_waits(p, nullptr, stream);
   if (rc) return rc;
-  const int64_t region = p->payload_bytes + p->scale_seg_bytes;
-  if (region == 0) return KVX_OK;
+  const int64_t layer_bytes = p->stg_layer();
+  if (layer_bytes == 0) return KVX_OK;
   const uint8_t* stg = static_cast<const uint8_t*>(staging);
   for (int32_t l = l0; l < l1; ++l) {
     CopyArgs a{};
-    a.out[0] = static_cast<uint8_t*>(p->dst.k[l]);
-    a.out[1] = static_cast<uint8_t*>(p->dst.v[l]);
-    for (int kv = 0; kv < 2; ++kv) {
-      const uint8_t* reg = stg + (int64_t(l - l0) * 2 + kv) * region;
-      a.in[kv] = reg;
-      if (p->dst.scales) a.in_sc[kv] = reinterpret_cast<const uint32_t*>(reg + p->payload_bytes);
-    }
-    if (p->dst.scales) {
-      a.out_sc[0] = reinterpret_cast<uint32_t*>(p->dst.ks[l]);
-      a.out_sc[1] = reinterpret_cast<uint32_t*>(p->dst.vs[l]);
+    for (int r = 0; r < p->nreg; ++r) {
+      const uint8_t* reg = stg + int64_t(l - l0) * layer_bytes + p->stg_offset(r);
+      a.in[r] = reg;
+      a.out[r] = static_cast<uint8_t*>(p->dst.base(r, l));
+      if (p->dst.scales) {
+        a.in_sc[r] = reinterpret_cast<const uint32_t*>(reg + p->payload[r]);
+        a.out_sc[r] = reinterpret_cast<uint32_t*>(p->dst.scale(r, l));
+      }
     }
     rc = launch_copy<kUnpack>(p, a, int64_t(p->blocks.size()), stream);
     if (rc) return rc;
@@ -310,6 +309,7 @@ int kvx_copy_heads(const kvx_plan_t* cp, int32_t layer, int32_t src_head0, int32
   int rc = check_device_plan(cp, "kvx_copy_heads");
   if (rc) return rc;
   kvx_plan_t* p = const_cast<kvx_plan_t*>(cp);
+  if (p->src.state) return fail(KVX_E_MISMATCH, "kvx_copy_heads: state pools have no heads");
   if (src_head0 < 0 || dst_head0 < 0 || num_heads < 0)
     return fail(KVX_E_INVAL, "kvx_copy_heads: negative head index or count");
   if (layer < 0 || layer >= p->src.L)
@@ -324,15 +324,13 @@ int kvx_copy_heads(const kvx_plan_t* cp, int32_t layer, int32_t src_head0, int32
   const Geom& gs = p->src;
   const Geom& gd = p->dst;
   HeadArgs a{};
-  a.in[0] = static_cast<const uint8_t*>(gs.k[layer]) + int64_t(src_head0) * gs.head_stride();
-  a.in[1] = static_cast<const uint8_t*>(gs.v[layer]) + int64_t(src_head0) * gs.head_stride();
-  a.out[0] = static_cast<uint8_t*>(gd.k[layer]) + int64_t(dst_head0) * gd.head_stride();
-  a.out[1] = static_cast<uint8_t*>(gd.v[layer]) + int64_t(dst_head0) * gd.head_stride();
-  if (gs.scales) {
-    a.in_sc[0] = reinterpret_cast<const uint32_t*>(gs.ks[layer]);
-    a.in_sc[1] = reinterpret_cast<const uint32_t*>(gs.vs[layer]);
-    a.out_sc[0] = reinterpret_cast<uint32_t*>(gd.ks[layer]);
-    a.out_sc[1] = reinterpret_cast<uint32_t*>(gd.vs[layer]);
+  for (int r = 0; r < p->nreg; ++r) {
+    a.in[r] = static_cast<const uint8_t*>(gs.base(r, layer)) + int64_t(src_head0) * gs.head_stride();
+    a.out[r] = static_cast<uint8_t*>(gd.base(r, layer)) + int64_t(dst_head0) * gd.head_stride();
+    if (gs.scales) {
+      a.in_sc[r] = reinterpret_cast<const uint32_t*>(gs.scale(r, layer));
+      a.out_sc[r] = reinterpret_cast<uint32_t*>(gd.scale(r, layer));
+    }
   }
   a.s_blk = gs.block_bytes();
   a.s_slot = gs.slot_stride();
@@ -347,7 +345,7 @@ int kvx_copy_heads(const kvx_plan_t* cp, int32_t layer, int32_t src_head0, int32
   for (int64_t first = 0; first < nb; first += kMaxGridX) {
     const int64_t cnt = std::min<int64_t>(nb - first, kMaxGridX);
     a.blocks = p->d_blocks + first;
-    hipLaunchKernelGGL(heads_kernel, dim3(unsigned(cnt), 2), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL(heads_kernel, dim3(unsigned(cnt), unsigned(p->nreg)), dim3(kThreads), 0, stream, a);
   }
   return check_launch("kvx heads kernel launch");
 }

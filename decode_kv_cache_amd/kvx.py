@@ -29,7 +29,13 @@ class kvx_pool_desc(C.Structure):
     _fields_ = [("num_layers", C.c_int32), ("num_blocks", C.c_int32), ("block_size", C.c_int32),
                 ("num_heads", C.c_int32), ("head_dim", C.c_int32), ("elem_bytes", C.c_int32),
                 ("layout", C.c_int32), ("k_base", C.POINTER(C.c_void_p)), ("v_base", C.POINTER(C.c_void_p)),
-                ("k_scale", C.POINTER(C.c_void_p)), ("v_scale", C.POINTER(C.c_void_p))]
+                ("k_scale", C.POINTER(C.c_void_p)), ("v_scale", C.POINTER(C.c_void_p)),
+                ("sliding_window", C.c_int32)]
+
+
+class kvx_state_pool_desc(C.Structure):
+    _fields_ = [("num_layers", C.c_int32), ("num_slots", C.c_int32), ("slot_bytes", C.c_int64 * 2),
+                ("base", C.POINTER(C.c_void_p) * 2)]
 
 
 class kvx_run(C.Structure):
@@ -49,6 +55,7 @@ _SIGS = {
     "kvx_tokens_to_move": (_I64, [_I64, _I64]),
     "kvx_should_reuse": (_I32, [_I64, _I64]),
     "kvx_pool_create": (C.c_int, [C.POINTER(kvx_pool_desc), C.POINTER(_P)]),
+    "kvx_state_pool_create": (C.c_int, [C.POINTER(kvx_state_pool_desc), C.POINTER(_P)]),
     "kvx_pool_destroy": (None, [_P]),
     "kvx_plan": (C.c_int, [_P, _P, _I32, _P, _P, _P, _P, _P, _U32, _P, C.POINTER(_P)]),
     "kvx_plan_runs": (C.c_int, [_P, _P, _I64, C.POINTER(_I64)]),
@@ -150,58 +157,96 @@ def kvx_should_reuse(reusable_tokens: int, threshold: int) -> bool:
 
 class Pool:
     """Owns a kvx_pool handle.  ``k_bases``/``v_bases``: one device address per
-    logical layer (may repeat); ``k_scales``/``v_scales``: fp32[num_blocks]
-    addresses per layer or None.  ``keep`` holds tensors alive with the pool."""
+    logical layer (may repeat; ``v_bases`` None for a pool of one latent
+    region); ``k_scales``/``v_scales``: fp32[num_blocks] addresses per layer
+    or None.  ``keep`` holds tensors alive with the pool."""
 
     def __init__(self, *, num_blocks, block_size, num_heads, head_dim, elem_bytes, layout,
-                 k_bases: Sequence[int], v_bases: Sequence[int], k_scales=None, v_scales=None, keep=()):
+                 k_bases: Sequence[int], v_bases: Optional[Sequence[int]], k_scales=None, v_scales=None,
+                 sliding_window: int = 0, keep=()):
         L = len(k_bases)
         arr = C.c_void_p * L
-        self._kb, self._vb = arr(*k_bases), arr(*v_bases)
+        self._kb = arr(*k_bases)
+        self._vb = arr(*v_bases) if v_bases is not None else None
         self._ks = arr(*k_scales) if k_scales is not None else None
         self._vs = arr(*v_scales) if v_scales is not None else None
         d = kvx_pool_desc(L, num_blocks, block_size, num_heads, head_dim, elem_bytes,
-                          LAYOUTS.get(layout, layout), self._kb, self._vb,
-                          self._ks if self._ks is not None else None,
-                          self._vs if self._vs is not None else None)
+                          LAYOUTS.get(layout, layout), self._kb, self._vb, self._ks, self._vs, sliding_window)
         h = C.c_void_p()
         _check("kvx_pool_create", lib().kvx_pool_create(C.byref(d), C.byref(h)))
-        self.handle = h
+        self.handle, self._L = h, lib()
         self.num_layers, self.num_blocks, self.block_size = L, num_blocks, block_size
         self.num_heads, self.head_dim, self.elem_bytes = num_heads, head_dim, elem_bytes
         self.layout = layout
+        self.regions = 1 if v_bases is None else 2
+        self.sliding_window = sliding_window
         self.keep = keep
 
     def close(self):
         if getattr(self, "handle", None):
-            lib().kvx_pool_destroy(self.handle)
+            self._L.kvx_pool_destroy(self.handle)
             self.handle = None
 
     __del__ = close
 
 
 def kvx_pool_create(*, kv, scales=None, num_layers: int, num_blocks: int, block_size: int,
-                    num_heads: int, head_dim: int, elem_bytes: int, layout="NHD", phys=None) -> Pool:
-    """Register a pool stored as one tensor ``kv`` of shape [P, 2, region]
-    (P physical layer slabs, K then V) with optional fp32 ``scales`` of shape
-    [P, 2, num_blocks].  Logical layer l uses slab ``phys(l)`` (default l)."""
+                    num_heads: int, head_dim: int, elem_bytes: int, layout="NHD", phys=None,
+                    sliding_window: int = 0) -> Pool:
+    """Register a pool stored as one tensor ``kv`` of shape [P, R, region]
+    (P physical layer slabs; R = 2 regions K then V, or R = 1 latent region)
+    with optional fp32 ``scales`` of shape [P, R, num_blocks].  Logical layer
+    l uses slab ``phys(l)`` (default l)."""
     phys = phys or (lambda l: l)
+    two = kv.shape[1] == 2
     kb = [kv[phys(l), 0].data_ptr() for l in range(num_layers)]
-    vb = [kv[phys(l), 1].data_ptr() for l in range(num_layers)]
+    vb = [kv[phys(l), 1].data_ptr() for l in range(num_layers)] if two else None
     ks = vs = None
     if scales is not None:
         ks = [scales[phys(l), 0].data_ptr() for l in range(num_layers)]
-        vs = [scales[phys(l), 1].data_ptr() for l in range(num_layers)]
+        vs = [scales[phys(l), 1].data_ptr() for l in range(num_layers)] if two else None
     return Pool(num_blocks=num_blocks, block_size=block_size, num_heads=num_heads, head_dim=head_dim,
                 elem_bytes=elem_bytes, layout=layout, k_bases=kb, v_bases=vb, k_scales=ks, v_scales=vs,
-                keep=(kv, scales))
+                sliding_window=sliding_window, keep=(kv, scales))
+
+
+class StatePool:
+    """Owns a kvx_pool handle of a state-slot pool (kvx_state_pool_create)."""
+
+    def __init__(self, *, num_slots: int, slot_bytes, bases0: Sequence[int], bases1: Sequence[int], keep=()):
+        L = len(bases0)
+        arr = C.c_void_p * L
+        self._b = (arr(*bases0), arr(*bases1))
+        d = kvx_state_pool_desc(L, num_slots, (C.c_int64 * 2)(*slot_bytes),
+                                (C.POINTER(C.c_void_p) * 2)(self._b[0], self._b[1]))
+        h = C.c_void_p()
+        _check("kvx_state_pool_create", lib().kvx_state_pool_create(C.byref(d), C.byref(h)))
+        self.handle, self._L = h, lib()
+        self.num_layers, self.num_slots, self.slot_bytes = L, num_slots, tuple(slot_bytes)
+        self.keep = keep
+
+    def close(self):
+        if getattr(self, "handle", None):
+            self._L.kvx_pool_destroy(self.handle)
+            self.handle = None
+
+    __del__ = close
+
+
+def kvx_state_pool_create(*, regions: Sequence[torch.Tensor], num_slots: int, slot_bytes) -> StatePool:
+    """Register a state pool stored as two uint8 tensors [layers, num_slots *
+    slot_bytes[r]] (r = 0: convolution state, 1: SSM state)."""
+    L = regions[0].shape[0]
+    return StatePool(num_slots=num_slots, slot_bytes=slot_bytes,
+                     bases0=[regions[0][l].data_ptr() for l in range(L)],
+                     bases1=[regions[1][l].data_ptr() for l in range(L)], keep=tuple(regions))
 
 
 class Plan:
     """Owns a kvx_plan_t handle (destroyed on close / garbage collection)."""
 
     def __init__(self, handle, src: Pool, dst: Pool):
-        self.handle, self.src, self.dst = handle, src, dst
+        self.handle, self.src, self.dst, self._L = handle, src, dst, lib()
 
     def runs(self) -> np.ndarray:
         n = C.c_int64()
@@ -224,7 +269,7 @@ class Plan:
 
     def close(self):
         if getattr(self, "handle", None):
-            lib().kvx_plan_destroy(self.handle)
+            self._L.kvx_plan_destroy(self.handle)
             self.handle = None
 
     __del__ = close
@@ -316,7 +361,7 @@ class Xfer:
         h = C.c_void_p()
         st = None if host_only else _stream(stream)
         _check("kvx_xfer_create", lib().kvx_xfer_create(producer.handle, C.byref(cfg), st, C.byref(h)))
-        self.handle, self.producer = h, producer
+        self.handle, self.producer, self._L = h, producer, lib()
         self._consumers = {}   # the C side keeps pool pointers: keep the Pool objects alive
 
     def _acc(self, name, *args) -> bool:
@@ -395,7 +440,7 @@ class Xfer:
 
     def close(self):
         if getattr(self, "handle", None):
-            lib().kvx_xfer_destroy(self.handle)
+            self._L.kvx_xfer_destroy(self.handle)
             self.handle = None
 
     __del__ = close

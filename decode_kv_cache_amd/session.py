@@ -28,7 +28,7 @@ def register(spec: W.PoolSpec, kv: torch.Tensor, sc: Optional[torch.Tensor]) -> 
     return kvx.kvx_pool_create(kv=kv, scales=sc, num_layers=spec.num_layers, num_blocks=spec.num_blocks,
                                block_size=spec.block_size, num_heads=spec.num_heads,
                                head_dim=spec.head_dim, elem_bytes=spec.elem_bytes, layout=spec.layout,
-                               phys=spec.phys)
+                               phys=spec.phys, sliding_window=spec.window)
 
 
 def device_side(spec: W.PoolSpec, seed: int, tag: int, device="cuda", values=None) -> Side:
@@ -49,3 +49,29 @@ def device_side(spec: W.PoolSpec, seed: int, tag: int, device="cuda", values=Non
 def scale_bits(sc: torch.Tensor) -> np.ndarray:
     """Host copy of fp32 scales as uint32 bit patterns."""
     return sc.view(torch.int32).cpu().numpy().view(np.uint32)
+
+
+@dataclass
+class StateSide:
+    spec: W.StateSpec
+    regions: list                    # two uint8 tensors [layers, num_slots * slot_bytes[r]]
+    pool: kvx.StatePool
+
+
+def state_device_side(spec: W.StateSpec, seed: int, tag: int, device="cuda", values=None) -> StateSide:
+    """State pool on the device: seeded values of the pool's dtype, or the
+    given pair of host uint8 arrays."""
+    if values is None:
+        regions = W.alloc_state_pool(spec, device)
+        W.fill_state_pool(spec, regions, seed, tag)
+    else:
+        regions = [torch.from_numpy(np.ascontiguousarray(v)).to(device) for v in values]
+    pool = kvx.kvx_state_pool_create(regions=regions, num_slots=spec.num_slots, slot_bytes=spec.slot_bytes)
+    return StateSide(spec, regions, pool)
+
+
+def group_side(spec, seed: int, tag: int, device="cuda", values=None):
+    """Side of either pool kind."""
+    if isinstance(spec, W.StateSpec):
+        return state_device_side(spec, seed, tag, device, values)
+    return device_side(spec, seed, tag, device, values)

@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define KVX_ABI_VERSION 2
+#define KVX_ABI_VERSION 3
 
 /* Status codes. */
 enum {
@@ -66,20 +66,28 @@ enum {
                                  device calls on the plan return KVX_E_INVAL */
 
 /*
- * Pool descriptor: the paged KV cache of one side, as exchanged at the first
- * handshake (KV base address, block size, per-layer strides: [MORI] §3) and
- * registered per layer ([MORI] §6, register_kv_caches).  Layer l's K and V
- * regions each hold num_blocks blocks of block_size slots of num_heads rows
- * of head_dim elements, in `layout`.  A block ID addresses the same block in
- * every layer and in both K and V.
+ * Pool descriptor: the paged KV cache of one layer group on one side, as
+ * exchanged at the first handshake (KV base address, block size, per-layer
+ * strides: [MORI] §3) and registered per layer ([MORI] §6,
+ * register_kv_caches).  Layer l's K and V regions each hold num_blocks blocks
+ * of block_size slots of num_heads rows of head_dim elements, in `layout`.
+ * A block ID addresses the same block in every layer and in both K and V.
  *   k_base, v_base: host arrays of num_layers device pointers, 16-B aligned.
  *     Entries may repeat (several logical layers aliasing one slab).
- *   k_scale, v_scale: both NULL (no scales) or host arrays of num_layers
- *     device pointers to fp32[num_blocks], one scale per (layer, K/V, block),
+ *     v_base NULL: each layer has one region only, the latent KV shared by
+ *     keys and values of an MLA layer ([MORI] §6: layers of other shapes,
+ *     MLA among them, get their own geometry); v_scale must be NULL then.
+ *   k_scale, v_scale: NULL (no scales) or host arrays of num_layers device
+ *     pointers to fp32[num_blocks], one scale per (layer, region, block),
  *     4-B aligned.  A scale travels with its block, unchanged.
+ *   sliding_window: 0 for full attention; W > 0 for a sliding-window group
+ *     whose queries see the last W positions, their own included ([MORI] §6).
+ *     A transfer then skips the blocks the receiving side's next query no
+ *     longer sees (see kvx_plan).
  * Requirements: all counts >= 1; elem_bytes in {1, 2, 4}; head_dim *
  * elem_bytes a multiple of 16 and block_size <= 32768 (KVX_E_UNSUPPORTED
- * otherwise).
+ * otherwise); sliding_window >= 0.  Zero-initialise the struct so that
+ * fields added by later versions read as 0.
  * The library copies the descriptor; the arrays may be freed after the call.
  */
 typedef struct kvx_pool_desc {
@@ -90,7 +98,24 @@ typedef struct kvx_pool_desc {
   void* const* v_base;
   float* const* k_scale;
   float* const* v_scale;
+  int32_t sliding_window;
 } kvx_pool_desc;
+
+/*
+ * State-slot pool: the recurrent state of a mamba-like layer group ([MORI]
+ * §6, hybrid models: the state is registered as two regions, the
+ * convolution state and the SSM state, and moved slot by slot).  Region r of
+ * layer l holds num_slots slots of slot_bytes[r] bytes; a slot ID addresses
+ * the same slot in every layer and both regions.
+ *   base[r]: host array of num_layers device pointers, 16-B aligned.
+ * Requirements: counts >= 1; slot_bytes[r] >= 16 and a multiple of 16
+ * (KVX_E_UNSUPPORTED otherwise).
+ */
+typedef struct kvx_state_pool_desc {
+  int32_t num_layers, num_slots;
+  int64_t slot_bytes[2];
+  void* const* base[2];
+} kvx_state_pool_desc;
 
 typedef struct kvx_pool kvx_pool;
 typedef struct kvx_plan_s kvx_plan_t;
@@ -131,6 +156,9 @@ int32_t kvx_should_reuse(int64_t reusable_tokens, int64_t threshold);
  * Errors: INVAL (null/invalid field), UNSUPPORTED (alignment), NOMEM. */
 int kvx_pool_create(const kvx_pool_desc* desc, kvx_pool** out);
 
+/* Register a state-slot pool.  Host-only.  Errors: INVAL, UNSUPPORTED, NOMEM. */
+int kvx_state_pool_create(const kvx_state_pool_desc* desc, kvx_pool** out);
+
 /* Free a pool handle (never the pool memory).  NULL is a no-op.  Plans built
  * from the pool stay valid: they hold their own copy of the descriptors. */
 void kvx_pool_destroy(kvx_pool* pool);
@@ -157,10 +185,22 @@ void kvx_pool_destroy(kvx_pool* pool);
  * the same head count and layout the plan also holds the per-region triple
  * list and the device work list for kvx_push_layer / kvx_pack / kvx_unpack;
  * otherwise only kvx_copy_heads may use it.
- * Pools must agree on num_layers, head_dim, elem_bytes and scale presence
- * (KVX_E_MISMATCH otherwise); pools with scales must also agree on
- * block_size (KVX_E_UNSUPPORTED: a per-block scale has no single source block
- * otherwise); src == dst is KVX_E_INVAL.
+ * Sliding-window pools: request r's next query, at position n =
+ * num_tokens[r], sees positions n-W+1 .. n.  Blocks holding none of them
+ * are skipped: the move covers tokens [t0, n), t0 being the later of the two
+ * sides' starts of the block that holds position max(0, n-W+1).  List
+ * entries of skipped blocks are neither read nor validated (an engine's null
+ * block may stand there).
+ * State-slot pools (both sides): a request with num_tokens[r] >= 1 moves its
+ * slot, the first entry of its list on each side, in both regions; one with
+ * 0 tokens moves nothing.  Each moving request is one run (tail 1), and each
+ * region's triples merge neighbouring slots.
+ * Pools must be of the same kind (KVX_E_MISMATCH otherwise).  Attention pools
+ * must agree on num_layers, head_dim, elem_bytes, region count, scale
+ * presence and sliding_window (KVX_E_MISMATCH otherwise); pools with scales
+ * must also agree on block_size (KVX_E_UNSUPPORTED: a per-block scale has no
+ * single source block otherwise).  State pools must agree on num_layers and
+ * slot_bytes (KVX_E_MISMATCH).  src == dst is KVX_E_INVAL.
  * Unless KVX_PLAN_HOST_ONLY is set the device work list is uploaded on
  * `upload_stream` (NULL = the null stream); later device calls on any stream
  * are ordered after the upload.
@@ -176,21 +216,23 @@ int kvx_plan(const kvx_pool* src, const kvx_pool* dst, int32_t num_requests,
 /* Copy the run table into out[0..cap); *n receives the run count.  With
  * out == NULL or cap < count only *n is written (and KVX_OK returned).
  * Runs are block pairs, defined for equal block sizes only (KVX_E_MISMATCH
- * otherwise; the triples describe such plans). */
+ * otherwise; the triples describe such plans).  A state plan has one run per
+ * moving request: its slot pair, nblk 1, tail 1. */
 int kvx_plan_runs(const kvx_plan_t* plan, kvx_run* out, int64_t cap, int64_t* n);
 
-/* The (src_off, dst_off, len) list of one (layer, kv) region (kv: 0 = K,
- * 1 = V): maximal contiguous byte ranges in plan order, the list handed to one
- * batch transfer per layer ([MORI] §6).  Offsets are relative to that layer's
- * K or V base on each side; with uniform layers the list is the same for
- * every layer and for K and V.  NHD gives one triple per run; HND gives the
- * run's full blocks plus one range per head of a partly filled last block.
+/* The (src_off, dst_off, len) list of one (layer, region) pair (kv: 0 = K,
+ * 1 = V; the latent region of an MLA pool is 0; a state pool's regions are 0
+ * = conv, 1 = SSM): maximal contiguous byte ranges in plan order, the list
+ * handed to one batch transfer per layer ([MORI] §6).  Offsets are relative
+ * to that layer's region base on each side; the list is the same for every
+ * layer, and for K and V.  NHD gives one triple per run; HND gives the run's
+ * full blocks plus one range per head of a partly filled last block.
  * Same cap/n protocol as kvx_plan_runs.  Errors: RANGE, MISMATCH (no
  * triples: different head count or layout). */
 int kvx_plan_triples(const kvx_plan_t* plan, int32_t layer, int32_t kv,
                      kvx_triple* out, int64_t cap, int64_t* n);
 
-/* Bytes one layer's push reads and writes (K and V payload plus scales). */
+/* Bytes one layer's push reads and writes (every region's payload plus scales). */
 int kvx_plan_bytes(const kvx_plan_t* plan, int64_t* read_bytes, int64_t* write_bytes);
 
 /* Free a plan.  Device calls already enqueued with it may still be running
@@ -199,9 +241,10 @@ int kvx_plan_bytes(const kvx_plan_t* plan, int64_t* read_bytes, int64_t* write_b
 void kvx_plan_destroy(kvx_plan_t* plan);
 
 /*
- * Layerwise push: copy layer `layer`'s K and V bytes of every planned token
- * (and the scales of every planned block) from the src pool into the dst
- * pool, after `ready` fires, on `stream`.  This is the per-layer write that
+ * Layerwise push: copy layer `layer`'s bytes of every planned token in every
+ * region (and the scales of every planned block; for state pools, every
+ * planned slot) from the src pool into the dst pool, after `ready` fires, on
+ * `stream`.  This is the per-layer write that
  * starts once that layer's compute is done and overlaps the next layer's
  * compute ([MORI] §3.2, save_kv_layer and the event sync before the write;
  * [PUSH] "Implementierungsdetails" step 3).  Slots past a request's last
@@ -221,16 +264,18 @@ int kvx_push_layer(const kvx_plan_t* plan, int32_t layer, hipEvent_t ready, hipS
 int kvx_push_layer_timed(const kvx_plan_t* plan, int32_t layer, hipEvent_t ready, hipStream_t stream,
                          hipEvent_t started, hipEvent_t finished);
 
-/* Staging bytes for layers [l0, l1): (l1 - l0) * 2 * (payload + scale
- * segment), where payload = sum of the region's triple lengths and the scale
- * segment is 4 bytes per planned block rounded up to 16 (0 without scales).
+/* Staging bytes for layers [l0, l1): (l1 - l0) * sum over the layer's
+ * regions of (payload + scale segment), where payload = sum of the region's
+ * triple lengths and the scale segment is 4 bytes per planned block rounded
+ * up to 16 (0 without scales).
  * Errors: RANGE (0 <= l0 <= l1 <= num_layers violated), MISMATCH. */
 int kvx_staging_bytes(const kvx_plan_t* plan, int32_t l0, int32_t l1, int64_t* bytes);
 
 /*
  * Gather layers [l0, l1) of the planned bytes from the src pool into a
  * contiguous staging buffer (what a NIC would read), laid out for each layer
- * in order, K then V: the region's triples' source bytes in plan order, then
+ * in order, region by region (K then V; conv then SSM): the region's
+ * triples' source bytes in plan order, then
  * (with scales) the planned blocks' fp32 scales in plan order, zero-padded to
  * 16 bytes.  `staging` is device memory, 16-B aligned, of `cap` bytes >=
  * kvx_staging_bytes.  The src pool of the plan is read; nothing else is
@@ -255,7 +300,7 @@ int kvx_unpack(const kvx_plan_t* plan, int32_t l0, int32_t l1, const void* stagi
  * ([PUSH] "Implementierungsdetails" step 3; rank mapping in [MORI] §6).
  * num_heads == 0 is a no-op (the ready wait is still enqueued).
  * Errors: INVAL (negative head index/count, host-only plan), RANGE (layer or
- * head slice outside either pool), HIP.
+ * head slice outside either pool), MISMATCH (state pools have no heads), HIP.
  */
 int kvx_copy_heads(const kvx_plan_t* plan, int32_t layer, int32_t src_head0, int32_t dst_head0,
                    int32_t num_heads, hipEvent_t ready, hipStream_t stream);

@@ -592,7 +592,7 @@ def latent_cases(count=24, seed0=61):
         yield W.random_case(
             4000 + i, layout=["NHD", "HND"][i % 2], elem_bytes=int(rng.choice([1, 2])),
             num_layers=int(rng.integers(1, 3)), num_blocks=int(max(48, 8 * bs)), block_size=bs, num_heads=1,
-            head_dim=int(rng.choice([8, 16, 24])), has_scales=bool(i % 3 == 0),
+            head_dim=int(rng.choice([16, 32, 48])), has_scales=bool(i % 3 == 0),
             num_requests=int(rng.integers(1, 4)), max_tokens=int(min(5 * bs, 40)),
             run_mean=float(rng.choice([1.5, 4.0])), regions=1)
 

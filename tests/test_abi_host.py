@@ -35,7 +35,7 @@ def test_library_exports_every_declared_symbol():
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(kvx.EXPORTED)
-    assert kvx.kvx_abi_version() == 2
+    assert kvx.kvx_abi_version() == 3
     assert L.kvx_status_str(kvx.KVX_E_DUPDST) == b"KVX_E_DUPDST"
 
 
@@ -50,9 +50,19 @@ def fake_pool(spec: W.PoolSpec, tag: int, scales=None):
     sc = spec.has_scales if scales is None else scales
     ks = [base // 2 + 8 * spec.num_blocks * l for l in range(L)] if sc else None
     vs = [base // 2 + 8 * spec.num_blocks * l + 4 * spec.num_blocks for l in range(L)] if sc else None
+    two = spec.regions == 2
     return kvx.Pool(num_blocks=spec.num_blocks, block_size=spec.block_size, num_heads=spec.num_heads,
                     head_dim=spec.head_dim, elem_bytes=spec.elem_bytes, layout=spec.layout,
-                    k_bases=kb, v_bases=vb, k_scales=ks, v_scales=vs)
+                    k_bases=kb, v_bases=vb if two else None, k_scales=ks, v_scales=vs if two else None,
+                    sliding_window=spec.window)
+
+
+def fake_state_pool(spec: W.StateSpec, tag: int):
+    base = FAKE * (tag + 1)
+    L = spec.num_layers
+    b0 = [base + l * (spec.region_bytes(0) + spec.region_bytes(1)) for l in range(L)]
+    b1 = [x + spec.region_bytes(0) for x in b0]
+    return kvx.StatePool(num_slots=spec.num_slots, slot_bytes=spec.slot_bytes, bases0=b0, bases1=b1)
 
 
 def host_plan(wl, tokens=None):
@@ -84,7 +94,7 @@ def compare(wl, tokens=None):
     assert runs.tolist() == [[r.src0, r.dst0, r.nblk, r.tail] for r in op.runs]
     if wl.src.num_heads == wl.dst.num_heads and wl.src.layout == wl.dst.layout:
         for layer in (0, wl.src.num_layers - 1):
-            for kv in (0, 1):
+            for kv in range(wl.src.regions):
                 assert plan.triples(layer, kv).tolist() == [list(t) for t in op.triples]
         rd, wr = plan.bytes_per_layer()
         assert (rd, wr) == op.bytes_per_layer()

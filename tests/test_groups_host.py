@@ -1,0 +1,133 @@
+"""Host-only planning of layer groups of other shapes against the oracle:
+pools of one latent region (MLA), sliding-window groups and state-slot
+groups.  Run tables, per-region triples, byte counts, staging sizes and
+error classes must equal the oracle's; no device memory is touched."""
+import numpy as np
+import pytest
+
+import oracle as O
+import oracle_pins as P
+from decode_kv_cache_amd import kvx
+from decode_kv_cache_amd import workloads as W
+from test_abi_host import compare, fake_pool, fake_state_pool
+
+
+def test_latent_plans_match_oracle():
+    for wl in P.latent_cases(24, seed0=91):
+        compare(wl)
+    wl = W.dsr1_mla_push()
+    g = wl.groups[0]
+    compare(W.Workload("mla", wl.seed, g.src, g.dst, wl.prompt_lens, g.src_tables, g.dst_tables))
+
+
+def test_window_plans_match_oracle():
+    for wl in P.window_cases(60, seed0=93):
+        if wl.src.block_size == wl.dst.block_size:
+            compare(wl)
+        else:
+            plan = kvx.kvx_plan(fake_pool(wl.src, 0), fake_pool(wl.dst, 1),
+                                [kvx.kvx_tokens_to_move(p, 0) for p in wl.prompt_lens],
+                                wl.src_tables, wl.dst_tables, host_only=True)
+            reqs = P.requests_for(O, wl)
+            op = O.make_plan(P.geom(O, wl.src), P.geom(O, wl.dst), reqs)
+            assert plan.triples(0, 0).tolist() == [list(t) for t in op.triples]
+            assert plan.bytes_per_layer() == op.bytes_per_layer()
+            with pytest.raises(kvx.KvxError) as e:
+                plan.runs()
+            assert e.value.code == kvx.KVX_E_MISMATCH
+    wl = W.gptoss_swa_push()
+    for g in wl.groups:
+        compare(W.Workload(g.name, wl.seed, g.src, g.dst, wl.prompt_lens, g.src_tables, g.dst_tables))
+
+
+def test_window_skipped_entries_are_not_validated():
+    spec = W.PoolSpec(1, 64, 4, 1, 16, W.U8, window=3)
+    sp, dp = fake_pool(spec, 0), fake_pool(spec, 1)
+    # 21 tokens: next query at 21 sees 19..21 -> blocks 4 and 5 are kept
+    src = [-1, -1, -1, -1, 10, 11]
+    dst = [99999, 7, 7, 7, 20, 21]
+    plan = kvx.kvx_plan(sp, dp, [21], [src], [dst], host_only=True)
+    assert plan.runs().tolist() == [[10, 20, 2, 1]]
+    assert plan.triples(0, 1).tolist() == [[10 * 64, 20 * 64, 5 * 16]]
+    rc, _ = kvx.kvx_plan_raw(sp, dp, 1, np.array([21], np.int64), np.array([0, 6], np.int64),
+                             np.array([0, 6], np.int64), np.array([-1] * 4 + [10, 64], np.int32),
+                             np.array(dst, np.int32))
+    assert rc == kvx.KVX_E_RANGE
+
+
+def state_compare(wl):
+    sp, dp = fake_state_pool(wl.src, 0), fake_state_pool(wl.dst, 1)
+    plan = kvx.kvx_plan(sp, dp, wl.prompt_lens, wl.src_tables, wl.dst_tables, host_only=True)
+    reqs = [O.Request(n, s, d) for n, s, d in zip(wl.prompt_lens, wl.src_tables, wl.dst_tables)]
+    op = O.make_state_plan(P.state_geom(O, wl.src), P.state_geom(O, wl.dst), reqs)
+    assert plan.runs().tolist() == [[r.src0, r.dst0, r.nblk, r.tail] for r in op.runs]
+    for layer in (0, wl.src.num_layers - 1):
+        for r in range(2):
+            assert plan.triples(layer, r).tolist() == [list(t) for t in op.triples[r]]
+    assert plan.bytes_per_layer() == op.bytes_per_layer()
+    L = wl.src.num_layers
+    assert kvx.kvx_staging_bytes(plan, 0, L) == O.state_staging_bytes(op, 0, L)
+    plan.close()
+
+
+def test_state_plans_match_oracle():
+    for wl in P.state_cases(40, seed0=95):
+        state_compare(wl)
+    wl = W.qwen3next_state_push()
+    g = wl.groups[1]
+    state_compare(W.Workload("state", wl.seed, g.src, g.dst, [8191] * len(wl.prompt_lens),
+                             g.src_tables, g.dst_tables))
+
+
+def test_state_errors():
+    spec = W.StateSpec(1, 32, (16, 48), W.U8)
+    sp, dp = fake_state_pool(spec, 0), fake_state_pool(spec, 1)
+    cases = [([1, 1], [[0], [1]], [[5], [5]], kvx.KVX_E_DUPDST),
+             ([1], [[32]], [[0]], kvx.KVX_E_RANGE),
+             ([1], [[0]], [[-1]], kvx.KVX_E_RANGE),
+             ([1], [[]], [[0]], kvx.KVX_E_INVAL),
+             ([-1], [[0]], [[0]], kvx.KVX_E_INVAL)]
+    for toks, st, dt, code in cases:
+        with pytest.raises(kvx.KvxError) as e:
+            kvx.kvx_plan(sp, dp, toks, st, dt, host_only=True)
+        assert e.value.code == code, (toks, st, dt)
+    # the same error classes in the oracle
+    g = O.StateGeometry(1, 32, (16, 48))
+    for toks, st, dt, code in cases:
+        with pytest.raises(O.OracleError) as e:
+            O.make_state_plan(g, g, [O.Request(n, s, d) for n, s, d in zip(toks, st, dt)])
+        assert e.value.kind == KIND[code]
+    assert kvx.kvx_plan(sp, dp, [0], [[]], [[]], host_only=True).triples(0, 1).tolist() == []
+    other = fake_state_pool(W.StateSpec(1, 32, (16, 64), W.U8), 2)
+    attn = fake_pool(W.PoolSpec(1, 32, 4, 1, 16, W.U8), 3)
+    for a, b in ((sp, other), (sp, attn), (attn, sp)):
+        with pytest.raises(kvx.KvxError) as e:
+            kvx.kvx_plan(a, b, [], [], [], host_only=True)
+        assert e.value.code == kvx.KVX_E_MISMATCH
+    with pytest.raises(kvx.KvxError) as e:
+        kvx.kvx_copy_heads(kvx.kvx_plan(sp, dp, [], [], [], host_only=True), 0, 0, 0, 1, stream=0)
+    assert e.value.code == kvx.KVX_E_INVAL    # host-only plan: checked first
+
+
+def test_group_pool_errors():
+    spec = W.PoolSpec(1, 32, 4, 1, 16, W.U8)
+    a = fake_pool(spec, 0)
+    for other in (W.PoolSpec(1, 32, 4, 1, 16, W.U8, regions=1), W.PoolSpec(1, 32, 4, 1, 16, W.U8, window=8)):
+        with pytest.raises(kvx.KvxError) as e:
+            kvx.kvx_plan(a, fake_pool(other, 1), [], [], [], host_only=True)
+        assert e.value.code == kvx.KVX_E_MISMATCH
+    with pytest.raises(kvx.KvxError) as e:
+        fake_pool(W.PoolSpec(1, 32, 4, 1, 16, W.U8, window=-1), 2)
+    assert e.value.code == kvx.KVX_E_INVAL
+    for sb, code in (((8, 16), kvx.KVX_E_UNSUPPORTED), ((16, 40), kvx.KVX_E_UNSUPPORTED)):
+        with pytest.raises(kvx.KvxError) as e:
+            fake_state_pool(W.StateSpec(1, 8, sb, W.U8), 3)
+        assert e.value.code == code
+    with pytest.raises(kvx.KvxError) as e:
+        kvx.Pool(num_blocks=8, block_size=4, num_heads=1, head_dim=16, elem_bytes=1, layout="NHD",
+                 k_bases=[FAKE_BASE], v_bases=None, k_scales=[FAKE_BASE // 2], v_scales=[FAKE_BASE // 4])
+    assert e.value.code == kvx.KVX_E_INVAL
+
+
+FAKE_BASE = 1 << 41
+KIND = {kvx.KVX_E_INVAL: "INVAL", kvx.KVX_E_RANGE: "RANGE", kvx.KVX_E_DUPDST: "DUPDST"}
