@@ -21,6 +21,14 @@ Other workloads (--workload), one JSON line each:
   xfer_pipeline  batched_push's requests driven through the transfer state
                  machine (kvx_xfer), layer by layer
   tiny_push      2 layers, one 200-token prompt (launch-bound; no claim)
+  dsr1_mla_push  DeepSeek-R1-shaped MLA: 61 layers of one 576-element latent
+                 region, token-granular blocks, 8 x 8192-token prompts
+  gptoss_swa_push  gpt-oss-120b-shaped: 36 layers alternating full attention
+                 and a 128-position sliding window (only the blocks the next
+                 query still sees move), 8 x 8192-token prompts
+  qwen3next_state_push  Qwen3-Next-shaped hybrid: 12 full-attention layers
+                 and 36 gated-delta-net layers whose conv (48 KiB) and
+                 recurrent (1 MiB) state slots move, 16 x 8192-token prompts
 
 Prints ONE JSON line on stdout.  Everything else goes to stderr.
 
@@ -45,7 +53,7 @@ HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, AMD published peak
 PROFILES = os.path.join(ROOT, "profiles")
 CALIB_BYTES = 1 << 30
 WORKLOAD_NAMES = ["qwen32b_push", "batched_push", "tp4_share", "multiturn_fp8", "pack_unpack", "qwen32b_reblock",
-                  "xfer_pipeline", "tiny_push"]
+                  "xfer_pipeline", "tiny_push", "dsr1_mla_push", "gptoss_swa_push", "qwen3next_state_push"]
 
 
 def log(*a):
@@ -110,7 +118,7 @@ def oracle_pools(wl, gs, gd, layers):
 
     def geom(spec, n):
         return O.Geometry(n, spec.num_blocks, spec.block_size, spec.num_heads, spec.head_dim, spec.elem_bytes,
-                          spec.layout, spec.has_scales)
+                          spec.layout, spec.has_scales, spec.regions, spec.window)
 
     def pool(spec, side):
         kv = np.stack([side.kv[spec.phys(l)].cpu().numpy() for l in layers])
@@ -267,6 +275,127 @@ def bench_push(args, torch, kvx, S, W):
                    "two_stream_GBs": None if two_gbs is None else round(two_gbs, 1)},
         "roofline": roofline(rd + wr, k_avg_us, "kvx::copy_kernel<0> (kvx_push_layer)", args.workload,
                              {"kernel_us_dispatch_stamps": round(float(kd.mean()), 3)}),
+        "cpu_baseline": cpu,
+    }
+
+
+def bench_hybrid(args, torch, kvx, S, W):
+    """Layer groups of other shapes (MLA, sliding window, state slots): one
+    step pushes every model layer, in model order, from its group's plan."""
+    import oracle as O
+    wl = W.HYBRID_WORKLOADS[args.workload]()
+    tokens = [kvx.kvx_tokens_to_move(p, 0) for p in wl.prompt_lens]
+    side = torch.cuda.Stream()
+    compute = torch.cuda.current_stream()
+    sides, plans, gbytes = [], [], []
+    for gi, g in enumerate(wl.groups):
+        gs, gd = S.group_side(g.src, wl.seed, 1 + 10 * gi), S.group_side(g.dst, wl.seed, 2 + 10 * gi)
+        sides.append((gs, gd))
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for gi, g in enumerate(wl.groups):
+        gs, gd = sides[gi]
+        plans.append(kvx.kvx_plan(gs.pool, gd.pool, tokens, g.src_tables, g.dst_tables, stream=side))
+    plan_ms = (time.perf_counter() - t0) * 1e3
+    groups_cfg = []
+    for gi, g in enumerate(wl.groups):
+        rd, wr = plans[gi].bytes_per_layer()
+        gbytes.append(rd + wr)
+        nl = sum(1 for x, _ in wl.layer_map if x == gi)
+        ntrip = [len(plans[gi].triples(0, r)) for r in range(2 if isinstance(g.src, W.StateSpec) else g.src.regions)]
+        groups_cfg.append({"group": g.name, "layers": nl, "bytes_per_layer": rd + wr, "triples_per_region": ntrip,
+                           "pool": repr(g.src)})
+        log(f"group {g.name}: {nl} layers, {rd + wr} B per layer, triples per region {ntrip}")
+    M = len(wl.layer_map)
+    step_bytes = sum(gbytes[gi] for gi, _ in wl.layer_map)
+    log(f"{M} model layers, {step_bytes} B per step, host plans {plan_ms:.2f} ms")
+
+    ready = [torch.cuda.Event() for _ in range(M)]
+    for e in ready:
+        e.record(compute)
+    torch.cuda.synchronize()
+
+    def step():
+        for i, (gi, l) in enumerate(wl.layer_map):
+            kvx.kvx_push_layer(plans[gi], l, ready=ready[i], stream=side)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    marks[0].record(side)
+    for i in range(args.steps):
+        step()
+        marks[i + 1].record(side)
+    torch.cuda.synchronize()
+    span_ms = marks[0].elapsed_time(marks[-1])
+    ms_per_step = span_ms / args.steps
+    gbs = step_bytes * args.steps / (span_ms * 1e-3) / 1e9
+    log(f"span {span_ms:.3f} ms for {args.steps} steps ({ms_per_step * 1e3:.1f} us/step): {gbs:.1f} GB/s "
+        f"= {100 * gbs / HBM_PEAK_GBS:.1f}% of {HBM_PEAK_GBS:.0f} GB/s")
+    k_avg_us = ms_per_step * 1e3 / M
+
+    # Per group: kernel durations from dispatch timestamps in a separate pass.
+    n_chk = min(3, args.steps)
+    per_group = {gi: [] for gi in range(len(wl.groups))}
+    evs = []
+    for _ in range(n_chk):
+        for i, (gi, l) in enumerate(wl.layer_map):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            kvx.kvx_push_layer_timed(plans[gi], l, a, b, ready=ready[i], stream=side)
+            evs.append((gi, a, b))
+    torch.cuda.synchronize()
+    for gi, a, b in evs:
+        per_group[gi].append(a.elapsed_time(b) * 1e3)
+    for gi, g in enumerate(wl.groups):
+        us = float(np.mean(per_group[gi]))
+        groups_cfg[gi]["kernel_us_dispatch_stamps"] = round(us, 3)
+        groups_cfg[gi]["kernel_GBs"] = round(gbytes[gi] / (us * 1e-6) / 1e9, 1)
+        log(f"group {g.name}: push kernel {us:.2f} us per launch (dispatch stamps), "
+            f"{groups_cfg[gi]['kernel_GBs']} GB/s")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        sample = list(range(min(8, M)))
+        work = []
+        setup = 0.0
+        nbytes = 0
+        for i in sample:
+            gi, l = wl.layer_map[i]
+            g = wl.groups[gi]
+            gs, gd = sides[gi]
+            reqs = [O.Request(n, s, d) for n, s, d in zip(tokens, g.src_tables, g.dst_tables)]
+            t0 = time.perf_counter()
+            if isinstance(g.src, W.StateSpec):
+                geo = O.StateGeometry(1, g.src.num_slots, tuple(g.src.slot_bytes))
+                src = O.StatePool(geo, [gs.regions[r][l:l + 1].cpu().numpy() for r in range(2)])
+                dst = O.StatePool(geo, [gd.regions[r][l:l + 1].cpu().numpy() for r in range(2)])
+                op = O.make_state_plan(geo, geo, reqs)
+                work.append((O.push_state, src, dst, op))
+            else:
+                src, dst = oracle_pools(W.Workload(g.name, wl.seed, g.src, g.dst, [], [], []), gs, gd, [l])
+                op = O.make_plan(src.geom, dst.geom, reqs)
+                work.append((O.push, src, dst, op))
+            setup += time.perf_counter() - t0
+            nbytes += sum(op.bytes_per_layer())
+
+        def one_pass():
+            for fn, src, dst, op in work:
+                fn(src, dst, op)
+        cpu = cpu_baseline(f"oracle push of model layers {sample[0]}..{sample[-1]} of {M}", one_pass, nbytes,
+                           args.cpu_seconds, setup)
+        log(f"cpu baseline: {cpu['value']} GB/s ({cpu['sample']})")
+
+    for p in plans:
+        p.close()
+    return {
+        "value": gbs, "ms_per_step": ms_per_step, "dtype": "u8",
+        "config": {"workload": wl.name, "model_layers": M, "prompt_tokens": wl.prompt_lens, "tokens_moved": tokens,
+                   "groups": groups_cfg, "bytes_per_step": step_bytes, "host_plan_ms": round(plan_ms, 3),
+                   "step": f"{M} x kvx_push_layer in model order on one side stream, each after its layer's "
+                           f"(fired) event"},
+        "roofline": roofline(step_bytes // M, k_avg_us, "kvx::copy_kernel<0> (kvx_push_layer), all groups",
+                             args.workload, {"note": "bytes and duration averaged over the step's launches"}),
         "cpu_baseline": cpu,
     }
 
@@ -718,7 +847,9 @@ def main():
         f"mem={dev.total_memory / 2**30:.0f} GiB; workload {args.workload}")
     fn = {"qwen32b_push": bench_push, "tiny_push": bench_push, "qwen32b_reblock": bench_push,
           "batched_push": bench_batched, "xfer_pipeline": bench_xfer,
-          "tp4_share": bench_tp4, "multiturn_fp8": bench_multiturn, "pack_unpack": bench_pack}[args.workload]
+          "tp4_share": bench_tp4, "multiturn_fp8": bench_multiturn, "pack_unpack": bench_pack,
+          "dsr1_mla_push": bench_hybrid, "gptoss_swa_push": bench_hybrid,
+          "qwen3next_state_push": bench_hybrid}[args.workload]
     if args.counters and fn is not bench_push:
         print("bench.py: --counters is for the push workloads", file=sys.stderr)
         sys.exit(2)
