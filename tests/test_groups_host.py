@@ -131,3 +131,32 @@ def test_group_pool_errors():
 
 FAKE_BASE = 1 << 41
 KIND = {kvx.KVX_E_INVAL: "INVAL", kvx.KVX_E_RANGE: "RANGE", kvx.KVX_E_DUPDST: "DUPDST"}
+
+
+def test_xfer_drives_any_group_kind():
+    """The transfer state machine plans through kvx_plan and is blind to the
+    group's shape: a state-slot group and a sliding-window group go through
+    register / prefill / save / seal / complete like a K/V group, and the
+    recompute list of a failed request is its registered entries."""
+    cases = [(fake_state_pool(W.StateSpec(3, 16, (16, 48), W.U8), 0),
+              fake_state_pool(W.StateSpec(3, 16, (16, 48), W.U8), 1), [4], [9]),
+             (fake_pool(W.PoolSpec(3, 64, 4, 1, 16, W.U8, window=5), 2),
+              fake_pool(W.PoolSpec(3, 64, 4, 1, 16, W.U8, window=5), 3), list(range(10, 20)), list(range(30, 40)))]
+    for prod, cons, src, dst in cases:
+        x = kvx.Xfer(prod, host_only=True)
+        assert x.prefill(1, 0, 37, src, 0.0)
+        for l in range(3):
+            assert x.save_layer(1, 0, l, 0.0)
+        assert x.register(1, 0, cons, dst, 0.5)
+        assert x.seal(1, 0)
+        for l in range(3):
+            x.complete(1, 0, l, ok=True)
+        x.poll(1.0)
+        assert x.pop_finished() == [(1, 0, kvx.KVX_REQ_DONE)]
+        assert x.register(2, 0, cons, dst[::-1] if len(dst) > 1 else [10], 2.0)
+        assert x.prefill(2, 0, 37, src, 2.0)
+        assert x.save_layer(2, 0, 0, 2.0)
+        x.complete(2, 0, 0, ok=False)
+        assert x.status(2) == (0, kvx.KVX_REQ_FAILED)
+        assert x.recompute_blocks(2) == (dst[::-1] if len(dst) > 1 else [10])
+        x.close()
