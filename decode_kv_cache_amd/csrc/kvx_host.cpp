@@ -32,18 +32,23 @@ int fail_hip(hipError_t e, const char* what) {
   return fail(KVX_E_HIP, "%s: %s (%d)", what, hipGetErrorString(e), int(e));
 }
 
-int enqueue_waits(kvx_plan_t* p, hipEvent_t ready, hipStream_t s) {
-  if (ready) {
-    // An event whose work has already completed needs no wait: skipping it
-    // saves the queue a barrier packet (several microseconds per layer).
-    hipError_t q = hipEventQuery(ready);
-    if (q == hipErrorNotReady) {
-      hipError_t e = hipStreamWaitEvent(s, ready, 0);
-      if (e != hipSuccess) return fail_hip(e, "hipStreamWaitEvent(ready)");
-    } else if (q != hipSuccess) {
-      return fail_hip(q, "hipEventQuery(ready)");
-    }
+int wait_event(hipEvent_t ev, hipStream_t s) {
+  if (!ev) return KVX_OK;
+  // An event whose work has already completed needs no wait: skipping it
+  // saves the queue a barrier packet (several microseconds per layer).
+  hipError_t q = hipEventQuery(ev);
+  if (q == hipErrorNotReady) {
+    hipError_t e = hipStreamWaitEvent(s, ev, 0);
+    if (e != hipSuccess) return fail_hip(e, "hipStreamWaitEvent(ready)");
+  } else if (q != hipSuccess) {
+    return fail_hip(q, "hipEventQuery(ready)");
   }
+  return KVX_OK;
+}
+
+int enqueue_waits(kvx_plan_t* p, hipEvent_t ready, hipStream_t s) {
+  int rc = wait_event(ready, s);
+  if (rc) return rc;
   if (!p->upload_seen.load(std::memory_order_acquire)) {
     hipError_t q = hipEventQuery(p->upload_ev);
     if (q == hipSuccess) {

@@ -115,6 +115,8 @@ namespace kvx {
 int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
 int fail_hip(hipError_t e, const char* what);
 
+// Make `stream` wait for `ev` unless it has already fired (NULL: nothing).
+int wait_event(hipEvent_t ev, hipStream_t stream);
 // Before a device call: enqueue the wait for `ready` and for the plan upload.
 int enqueue_waits(kvx_plan_t* plan, hipEvent_t ready, hipStream_t stream);
 // After a launch: turn a launch error into KVX_E_HIP.

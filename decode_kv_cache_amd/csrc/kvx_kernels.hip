@@ -55,6 +55,25 @@ constexpr int kBufferWord3 = 0x00020000;  // raw byte buffer, gfx9 family
 __device__ __forceinline__ v4u ld_stream(const v4u* p) { return __builtin_nontemporal_load(p); }
 __device__ __forceinline__ void st_stream(v4u* p, v4u v) { __builtin_nontemporal_store(v, p); }
 
+// Copy `len` bytes (a piece) from `src` to `dst` with the whole workgroup.
+// One buffer resource per piece (base = piece start, size = piece length):
+// lanes past a short piece's end read zeros and their stores are dropped by
+// the hardware range check, so every lane issues all of its loads before its
+// first store without any masking.
+__device__ __forceinline__ void copy_piece(const uint8_t* src, uint8_t* dst, int32_t len) {
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(src), (short)0, len, kBufferWord3);
+  const __amdgpu_buffer_rsrc_t rd = __builtin_amdgcn_make_buffer_rsrc(dst, (short)0, len, kBufferWord3);
+  const int t = threadIdx.x;
+  v4u r[kVecPerThread];
+#pragma unroll
+  for (int k = 0; k < kVecPerThread; ++k)
+    r[k] = __builtin_amdgcn_raw_buffer_load_b128(rs, (t + k * kThreads) * 16, 0, KVX_LD_AUX);
+#pragma unroll
+  for (int k = 0; k < kVecPerThread; ++k)
+    __builtin_amdgcn_raw_buffer_store_b128(r[k], rd, (t + k * kThreads) * 16, 0, KVX_ST_AUX);
+}
+
 // One workgroup copies one piece of region blockIdx.y + piece.reg (one list
 // shared by K and V: y picks the region; one list per region: the tag does);
 // workgroups past the pieces copy the planned blocks' scales.
@@ -66,21 +85,7 @@ __global__ __launch_bounds__(kThreads) void copy_kernel(CopyArgs a) {
     const int kv = int(blockIdx.y) + pc.reg;
     const int64_t ioff = MODE == kUnpack ? pc.stg_off : pc.src_off;
     const int64_t ooff = MODE == kPack ? pc.stg_off : pc.dst_off;
-    // One buffer resource per piece (base = piece start, size = piece
-    // length): lanes past a short piece's end read zeros and their stores
-    // are dropped by the hardware range check, so every lane issues all of
-    // its loads before its first store without any masking.
-    const __amdgpu_buffer_rsrc_t rs =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(a.in[kv] + ioff), (short)0, pc.len, kBufferWord3);
-    const __amdgpu_buffer_rsrc_t rd = __builtin_amdgcn_make_buffer_rsrc(a.out[kv] + ooff, (short)0, pc.len, kBufferWord3);
-    const int t = threadIdx.x;
-    v4u r[kVecPerThread];
-#pragma unroll
-    for (int k = 0; k < kVecPerThread; ++k)
-      r[k] = __builtin_amdgcn_raw_buffer_load_b128(rs, (t + k * kThreads) * 16, 0, KVX_LD_AUX);
-#pragma unroll
-    for (int k = 0; k < kVecPerThread; ++k)
-      __builtin_amdgcn_raw_buffer_store_b128(r[k], rd, (t + k * kThreads) * 16, 0, KVX_ST_AUX);
+    copy_piece(a.in[kv] + ioff, a.out[kv] + ooff, pc.len);
     return;
   }
   const int kv = blockIdx.y;
@@ -98,6 +103,40 @@ __global__ __launch_bounds__(kThreads) void copy_kernel(CopyArgs a) {
   } else {
     if (i < a.n_blocks) a.out_sc[kv][a.blocks[i].dst] = a.in_sc[kv][i];
   }
+}
+
+// Several (plan, layer) pushes in one launch: entry j owns workgroups
+// [first_j, first_{j+1}) and copies its plan's pieces between its layer's
+// region bases.
+constexpr int kManyMax = 32;
+struct ManyEntry {
+  const Piece* pieces;
+  const uint8_t* in[2];
+  uint8_t* out[2];
+  int32_t first;  // x index of the entry's first workgroup
+  int32_t pad;
+};
+struct ManyArgs {
+  int32_t n;  // entries
+  int32_t pad;
+  ManyEntry e[kManyMax];
+};
+
+__global__ __launch_bounds__(kThreads) void copy_many_kernel(ManyArgs a) {
+  const int x = blockIdx.x;
+  // the last entry whose first workgroup is <= x (uniform: scalar loads)
+  int lo = 0, hi = a.n - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (a.e[mid].first <= x)
+      lo = mid;
+    else
+      hi = mid - 1;
+  }
+  const ManyEntry& en = a.e[lo];
+  const Piece pc = en.pieces[x - en.first];
+  const int kv = int(blockIdx.y) + pc.reg;
+  copy_piece(en.in[kv] + pc.src_off, en.out[kv] + pc.dst_off, pc.len);
 }
 
 struct HeadArgs {
@@ -158,6 +197,9 @@ __global__ __launch_bounds__(kThreads) void heads_kernel(HeadArgs a) {
 
 static int64_t scale_wgs(int64_t slots) { return (slots + kThreads - 1) / kThreads; }
 
+// One shared piece list: one y row per region; one list per region: the tags.
+static unsigned grid_y(const kvx_plan_t* p) { return p->nlists == 1 ? unsigned(p->nreg) : 1u; }
+
 // Enqueue the copy kernel for one layer; `in`/`out` and the scale pointers
 // are already resolved for the mode.  Splits very long work lists.
 template <int MODE>
@@ -165,8 +207,7 @@ static int launch_copy(kvx_plan_t* p, CopyArgs a, int64_t scale_slots, hipStream
                        hipEvent_t started = nullptr, hipEvent_t finished = nullptr) {
   const int64_t np = int64_t(p->pieces.size());
   const bool scales = a.in_sc[0] != nullptr;
-  // one shared list: one y row per region; one list per region: the tags
-  const unsigned gy = p->nlists == 1 ? unsigned(p->nreg) : 1u;
+  const unsigned gy = grid_y(p);
   const int64_t nsw = scales ? scale_wgs(scale_slots) : 0;
   a.blocks = p->d_blocks;
   a.n_blocks = int32_t(p->blocks.size());
@@ -200,6 +241,19 @@ static int check_device_plan(const kvx_plan_t* p, const char* fn) {
   return KVX_OK;
 }
 
+static CopyArgs push_args(const kvx_plan_t* p, int32_t layer) {
+  CopyArgs a{};
+  for (int r = 0; r < p->nreg; ++r) {
+    a.in[r] = static_cast<const uint8_t*>(p->src.base(r, layer));
+    a.out[r] = static_cast<uint8_t*>(p->dst.base(r, layer));
+    if (p->src.scales) {
+      a.in_sc[r] = reinterpret_cast<const uint32_t*>(p->src.scale(r, layer));
+      a.out_sc[r] = reinterpret_cast<uint32_t*>(p->dst.scale(r, layer));
+    }
+  }
+  return a;
+}
+
 }  // namespace kvx
 
 using namespace kvx;
@@ -221,16 +275,66 @@ int kvx_push_layer_timed(const kvx_plan_t* cp, int32_t layer, hipEvent_t ready, 
   rc = enqueue_waits(p, ready, stream);
   if (rc) return rc;
   if (p->pieces.empty() && p->blocks.empty()) return KVX_OK;
-  CopyArgs a{};
-  for (int r = 0; r < p->nreg; ++r) {
-    a.in[r] = static_cast<const uint8_t*>(p->src.base(r, layer));
-    a.out[r] = static_cast<uint8_t*>(p->dst.base(r, layer));
-    if (p->src.scales) {
-      a.in_sc[r] = reinterpret_cast<const uint32_t*>(p->src.scale(r, layer));
-      a.out_sc[r] = reinterpret_cast<uint32_t*>(p->dst.scale(r, layer));
-    }
+  return launch_copy<kPush>(p, push_args(p, layer), int64_t(p->blocks.size()), stream, started, finished);
+}
+
+int kvx_push_many(const kvx_plan_t* const* plans, const int32_t* layers, int32_t n, hipEvent_t ready,
+                  hipStream_t stream) {
+  if (n < 0 || (n > 0 && (!plans || !layers))) return fail(KVX_E_INVAL, "kvx_push_many: bad arguments");
+  for (int32_t i = 0; i < n; ++i) {
+    const kvx_plan_t* p = plans[i];
+    int rc = check_device_plan(p, "kvx_push_many");
+    if (rc) return rc;
+    if (!p->push_ok) return fail(KVX_E_MISMATCH, "kvx_push_many: pair %d: pools differ in head count or layout", i);
+    if (layers[i] < 0 || layers[i] >= p->src.L)
+      return fail(KVX_E_RANGE, "kvx_push_many: pair %d: layer %d outside [0,%d)", i, layers[i], p->src.L);
   }
-  return launch_copy<kPush>(p, a, int64_t(p->blocks.size()), stream, started, finished);
+  int rc = wait_event(ready, stream);
+  if (rc) return rc;
+  for (int32_t i = 0; i < n; ++i) {
+    rc = enqueue_waits(const_cast<kvx_plan_t*>(plans[i]), nullptr, stream);
+    if (rc) return rc;
+  }
+  // Consecutive pairs without scales and with the same grid height share a
+  // launch (up to kManyMax entries and kMaxGridX workgroups); the others are
+  // launched alone, in order.
+  ManyArgs m{};
+  int64_t total = 0;
+  unsigned gy = 0;
+  auto flush = [&]() -> int {
+    if (m.n == 0) return KVX_OK;
+    hipLaunchKernelGGL(copy_many_kernel, dim3(unsigned(total), gy), dim3(kThreads), 0, stream, m);
+    m.n = 0;
+    total = 0;
+    return check_launch("kvx copy_many kernel launch");
+  };
+  for (int32_t i = 0; i < n; ++i) {
+    kvx_plan_t* p = const_cast<kvx_plan_t*>(plans[i]);
+    const int64_t np = int64_t(p->pieces.size());
+    if (p->src.scales || np > kMaxGridX) {
+      if (np == 0 && p->blocks.empty()) continue;
+      rc = flush();
+      if (rc) return rc;
+      rc = launch_copy<kPush>(p, push_args(p, layers[i]), int64_t(p->blocks.size()), stream);
+      if (rc) return rc;
+      continue;
+    }
+    if (np == 0) continue;
+    if (m.n == kManyMax || (m.n > 0 && (grid_y(p) != gy || total + np > kMaxGridX))) {
+      rc = flush();
+      if (rc) return rc;
+    }
+    gy = grid_y(p);
+    ManyEntry& e = m.e[m.n++];
+    e.pieces = p->d_pieces;
+    for (int r = 0; r < p->nreg; ++r) {
+      e.in[r] = static_cast<const uint8_t*>(p->src.base(r, layers[i]));
+      e.out[r] = static_cast<uint8_t*>(p->dst.base(r, layers[i]));
+    }
+    e.first = int32_t(total);
+    total += np;
+  }
+  return flush();
 }
 
 static int staging_call(const kvx_plan_t* cp, int32_t l0, int32_t l1, const void* staging,

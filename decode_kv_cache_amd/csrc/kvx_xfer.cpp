@@ -5,12 +5,14 @@
 // steps 1-3; [MORI] MoRIIO connector note §3.1, §3.2, §6 (full titles in
 // kvx.h; the readings taken are listed in kvx_xfer.h).
 //
-// Device-side bookkeeping keeps queue packets few: a layer save for many
-// requests waits on the layer's event once (later writes on the same stream
-// are ordered after it); deferred writes of one save share one captured
-// "gate" event; completion of issued writes is observed through one "mark"
-// event recorded per poll behind every write issued since the previous poll
-// (writes on one stream finish in order).
+// Device-side bookkeeping keeps queue packets and launches few: a layer save
+// for many requests waits on the layer's event once (later writes on the
+// same stream are ordered after it) and issues its writes as one batch
+// (kvx_push_many); deferred writes of one save share one captured "gate"
+// event, and a request's deferred layers go out as one batch; completion of
+// issued writes is observed through one "mark" event recorded per poll
+// behind every write issued since the previous poll (writes on one stream
+// finish in order).
 
 #include <hip/hip_runtime_api.h>
 
@@ -179,17 +181,37 @@ void settle(kvx_xfer* x, Req& r) {
   if (r.state != KVX_REQ_PENDING) release_req(x, r);
 }
 
-// Issue one layer's write: kvx_push_layer gated on `ready` (device mode);
-// host-only mode only logs it.
-int issue(kvx_xfer* x, uint64_t id, Req& r, int32_t layer, Layer& ly, hipEvent_t ready, double now) {
+// A layer write about to be issued.
+struct Item {
+  uint64_t id;
+  Req* r;
+  int32_t layer;
+  Layer* ly;
+};
+
+// Issue layer writes, in order: one kvx_push_many on the stream, which is
+// already ordered after their readiness (device mode); host-only mode only
+// logs them.
+int issue(kvx_xfer* x, const std::vector<Item>& items, double now) {
+  if (items.empty()) return KVX_OK;
   if (!x->host_only) {
-    int rc = kvx_push_layer(r.plan, layer, ready, x->stream);
+    std::vector<const kvx_plan_t*> plans;
+    std::vector<int32_t> layers;
+    plans.reserve(items.size());
+    layers.reserve(items.size());
+    for (const Item& it : items) {
+      plans.push_back(it.r->plan);
+      layers.push_back(it.layer);
+    }
+    int rc = kvx_push_many(plans.data(), layers.data(), int32_t(items.size()), nullptr, x->stream);
     if (rc != KVX_OK) return rc;
-    x->unmarked.push_back(WriteRef{id, r.attempt, layer});
+    for (const Item& it : items) x->unmarked.push_back(WriteRef{it.id, it.r->attempt, it.layer});
   }
-  ly.st = kIssued;
-  ly.issued_at = now;
-  x->log.push_back(WriteRef{id, r.attempt, layer});
+  for (const Item& it : items) {
+    it.ly->st = kIssued;
+    it.ly->issued_at = now;
+    x->log.push_back(WriteRef{it.id, it.r->attempt, it.layer});
+  }
   return KVX_OK;
 }
 
@@ -209,12 +231,22 @@ int start(kvx_xfer* x, uint64_t id, Req& r, double now) {
       return rc;
     }
   }
+  // Every deferred layer, in layer order, in one batch behind the captured
+  // readiness of each (layers saved together share one gate).
+  std::vector<Item> items;
+  int32_t waited = -1;
   for (auto& kv : r.layers) {
     if (kv.second.st != kDeferred) continue;
-    hipEvent_t gate = kv.second.gate >= 0 ? x->sigs[size_t(kv.second.gate)].ev : nullptr;
-    int rc = issue(x, id, r, kv.first, kv.second, gate, now);
-    if (rc != KVX_OK) return rc;
+    const int32_t g = kv.second.gate;
+    if (!x->host_only && g >= 0 && g != waited) {
+      int rc = wait_event(x->sigs[size_t(g)].ev, x->stream);
+      if (rc != KVX_OK) return rc;
+      waited = g;
+    }
+    items.push_back(Item{id, &r, kv.first, &kv.second});
   }
+  int rc = issue(x, items, now);
+  if (rc != KVX_OK) return rc;
   r.deferred_since = -1;
   return KVX_OK;
 }
@@ -260,21 +292,21 @@ int save_many(kvx_xfer* x, int32_t layer, hipEvent_t ready, int64_t n, const uin
       return fail_hip(q, "hipEventQuery(ready)");
     }
   }
+  std::vector<Item> items;
+  items.reserve(size_t(n_issue));
   for (int64_t i = 0; i < n; ++i) {
     Req* r = take[size_t(i)];
     if (!r) continue;
     Layer& ly = r->layers[layer];
     if (r->plan) {
-      // stream order already follows `ready`
-      int rc = issue(x, ids[i], *r, layer, ly, nullptr, now);
-      if (rc != KVX_OK) return rc;
+      items.push_back(Item{ids[i], r, layer, &ly});  // stream order already follows `ready`
     } else {
       ly.st = kDeferred;
       ly.gate = gate;
       if (r->deferred_since < 0) r->deferred_since = now;
     }
   }
-  return KVX_OK;
+  return issue(x, items, now);
 }
 
 }  // namespace

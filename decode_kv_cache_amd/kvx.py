@@ -64,6 +64,7 @@ _SIGS = {
     "kvx_plan_destroy": (None, [_P]),
     "kvx_push_layer": (C.c_int, [_P, _I32, _P, _P]),
     "kvx_push_layer_timed": (C.c_int, [_P, _I32, _P, _P, _P, _P]),
+    "kvx_push_many": (C.c_int, [_P, _P, _I32, _P, _P]),
     "kvx_staging_bytes": (C.c_int, [_P, _I32, _I32, C.POINTER(_I64)]),
     "kvx_pack": (C.c_int, [_P, _I32, _I32, _P, _I64, _P]),
     "kvx_unpack": (C.c_int, [_P, _I32, _I32, _P, _I64, _P]),
@@ -327,6 +328,17 @@ def kvx_push_layer_timed(plan: Plan, layer: int, started, finished, ready=None, 
             e.record(torch.cuda.current_stream())
     _check("kvx_push_layer_timed", lib().kvx_push_layer_timed(
         plan.handle, layer, _event(ready), _stream(stream), _event(started), _event(finished)))
+
+
+def kvx_push_many(plans: Sequence[Plan], layers: Sequence[int], ready=None, stream=None) -> None:
+    """Push layers[i] of plans[i] for every i, batched into few launches."""
+    n = len(plans)
+    if len(layers) != n:
+        raise ValueError("one layer per plan")
+    hp = (C.c_void_p * max(n, 1))(*[p.handle for p in plans])
+    ly = np.ascontiguousarray(layers, dtype=np.int32)
+    _check("kvx_push_many", lib().kvx_push_many(hp, ly.ctypes.data if n else None, n, _event(ready),
+                                                _stream(stream)))
 
 
 def kvx_staging_bytes(plan: Plan, l0: int, l1: int) -> int:

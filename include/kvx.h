@@ -264,6 +264,26 @@ int kvx_push_layer(const kvx_plan_t* plan, int32_t layer, hipEvent_t ready, hipS
 int kvx_push_layer_timed(const kvx_plan_t* plan, int32_t layer, hipEvent_t ready, hipStream_t stream,
                          hipEvent_t started, hipEvent_t finished);
 
+/*
+ * Several layer pushes with one kernel launch: pair i copies layer layers[i]
+ * of plans[i] exactly as kvx_push_layer would, all after `ready` fires, on
+ * `stream`.  Unlike n kvx_push_layer calls, the pairs' copies may run at the
+ * same time, so no two pairs may write the same destination bytes (sources
+ * may overlap).  This is one batch write per layer over many requests'
+ * (offset, offset, size) lists ([MORI] §6), for requests whose plans were
+ * built at different times (a transfer starts when its consumer registers),
+ * and the flush of several deferred layers of one request.  Plans may have
+ * different pools.  Consecutive pairs share a launch of up to 32 entries;
+ * pairs with per-block scales, or whose work list alone fills a launch, run
+ * as launches of their own, in order.  Everything is ordered after `ready`
+ * and before later work on `stream`.  All pairs are validated before
+ * anything is enqueued.
+ * Errors: INVAL (n < 0, null arrays with n > 0, a null or host-only plan),
+ * RANGE (a layer), MISMATCH (a plan without a push work list), HIP.
+ */
+int kvx_push_many(const kvx_plan_t* const* plans, const int32_t* layers, int32_t n, hipEvent_t ready,
+                  hipStream_t stream);
+
 /* Staging bytes for layers [l0, l1): (l1 - l0) * sum over the layer's
  * regions of (payload + scale segment), where payload = sum of the region's
  * triple lengths and the scale segment is 4 bytes per planned block rounded
