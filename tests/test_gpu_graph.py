@@ -1,0 +1,53 @@
+"""The layerwise push captured in a HIP graph (torch.cuda.CUDAGraph on ROCm)
+and replayed: once the plan's upload has been observed, kvx_push_layer
+without a ready event enqueues nothing but its kernel (a captured step
+orders the push after the captured compute by stream order), so a serving
+loop can capture a step once and replay it.  The source is rewritten between replays
+by ordinary eager work; every replay must equal the oracle's push of the
+source as it stood, and the layers that no push touches stay unchanged."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import oracle_pins as P
+from decode_kv_cache_amd import kvx
+from decode_kv_cache_amd import session as S
+from decode_kv_cache_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+
+def test_push_replayed_from_graph():
+    wl = W.random_case(9500, num_layers=4, num_blocks=300, block_size=16, num_heads=4, head_dim=64,
+                       num_requests=3, max_tokens=700, run_mean=3.0)
+    src, dst = P.pools(O, wl)
+    gs = S.device_side(wl.src, wl.seed, 1, values=(src.kv, src.scales))
+    gd = S.device_side(wl.dst, wl.seed, 2, values=(dst.kv, dst.scales))
+    toks = [kvx.kvx_tokens_to_move(p, 0) for p in wl.prompt_lens]
+    side = torch.cuda.Stream()
+    plan = kvx.kvx_plan(gs.pool, gd.pool, toks, wl.src_tables, wl.dst_tables, stream=side)
+    op = O.make_plan(src.geom, dst.geom, [O.Request(n, s, d) for n, s, d in zip(toks, wl.src_tables, wl.dst_tables)])
+    ready = [torch.cuda.Event() for _ in range(4)]
+    for e in ready:
+        e.record()
+    kvx.kvx_push_layer(plan, 0, ready=ready[0], stream=side)   # upload observed, events fired
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        for l in (0, 1, 3):
+            kvx.kvx_push_layer(plan, l, stream=torch.cuda.current_stream())
+    exp = dst.copy()
+    rng = np.random.Generator(np.random.PCG64(3))
+    for rep in range(3):
+        new = rng.integers(0, 256, size=src.kv.shape, dtype=np.uint8)
+        gs.kv.copy_(torch.from_numpy(new).cuda())        # eager work between replays
+        src.kv[...] = new
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        O.push(src, exp, op, layers=[0, 1, 3])
+        got = gd.kv.cpu().numpy()
+        assert np.array_equal(got, exp.kv), rep
+        assert np.array_equal(got[2], dst.kv[2]), rep          # layer 2 is not in the graph
+    plan.close()

@@ -160,3 +160,19 @@ def test_xfer_drives_any_group_kind():
         assert x.status(2) == (0, kvx.KVX_REQ_FAILED)
         assert x.recompute_blocks(2) == (dst[::-1] if len(dst) > 1 else [10])
         x.close()
+
+
+def test_push_many_argument_errors():
+    """Argument errors of kvx_push_many need no device: they are reported
+    before anything is enqueued."""
+    spec = W.PoolSpec(2, 32, 4, 1, 16, W.U8)
+    p = kvx.kvx_plan(fake_pool(spec, 0), fake_pool(spec, 1), [5], [[1, 2]], [[3, 4]], host_only=True)
+    L = kvx.lib()
+    assert L.kvx_push_many(None, None, -1, None, None) == kvx.KVX_E_INVAL
+    assert L.kvx_push_many(None, None, 2, None, None) == kvx.KVX_E_INVAL
+    assert L.kvx_push_many(None, None, 0, None, None) == kvx.KVX_OK
+    with pytest.raises(kvx.KvxError) as e:
+        kvx.kvx_push_many([p], [0], stream=0)
+    assert e.value.code == kvx.KVX_E_INVAL     # host-only plan
+    with pytest.raises(ValueError):
+        kvx.kvx_push_many([p], [0, 1], stream=0)
