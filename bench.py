@@ -254,6 +254,20 @@ def bench_push(args, torch, kvx, S, W):
     fresh_gbs = step_bytes * args.steps / (t.ms * 1e-3) / 1e9
     log(f"with fresh per-layer events: {fresh_gbs:.1f} GB/s")
 
+    # Secondary: the step captured once in a HIP graph and replayed.
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        for l in range(L):
+            kvx.kvx_push_layer(plan, l, stream=torch.cuda.current_stream())
+    with torch.cuda.stream(side):   # replay() launches on the current stream
+        graph.replay()
+        with Timer(torch, side) as t:
+            for _ in range(args.steps):
+                graph.replay()
+    graph_gbs = step_bytes * args.steps / (t.ms * 1e-3) / 1e9
+    log(f"step replayed from a HIP graph: {graph_gbs:.1f} GB/s")
+    del graph
+
     two_gbs = None
     if args.two_stream:
         two_gbs = two_stream_rate(torch, kvx, plan, ready, side, L, args.steps, step_bytes)
@@ -283,6 +297,7 @@ def bench_push(args, torch, kvx, S, W):
                    "merged_runs": nruns, "triples_per_region": ntrip, "bytes_per_step": step_bytes,
                    "step": f"{L} x kvx_push_layer on one side stream, each after its layer's (fired) event",
                    "host_plan_ms": round(plan_ms, 3), "fresh_event_GBs": round(fresh_gbs, 1),
+                   "graph_replay_GBs": round(graph_gbs, 1),
                    "two_stream_GBs": None if two_gbs is None else round(two_gbs, 1)},
         "roofline": roofline(rd + wr, k_avg_us, "kvx::copy_kernel<0> (kvx_push_layer)", args.workload,
                              {"kernel_us_dispatch_stamps": round(float(kd.mean()), 3)}),
