@@ -272,15 +272,42 @@ void build_triples(kvx_plan_t* p) {
   }
 }
 
+// 32 KiB pieces per launch from which one-wave workgroups of 32 KiB keep
+// every compute unit of an MI355X busy (4 per CU, 256 CUs).
+constexpr int64_t kFullLaunchPieces = 1024;
+
+// Launch shape for a plan, from its triples, as measured on MI355X (all
+// shapes side by side on the same pools).  Runs that fill 32 KiB pieces to at
+// least 90% (whole blocks of 16 KiB or more, long state slots) copy fastest
+// with one-wave workgroups: 32 KiB pieces when a launch has enough of them,
+// 16 KiB pieces otherwise.  Shorter runs (blocks of a few KiB, ragged run
+// ends) copy fastest with four-wave workgroups of 16 KiB pieces.
+int32_t pick_shape(const kvx_plan_t* p) {
+  int64_t n32 = 0, bytes = 0;
+  for (int32_t r = 0; r < p->nlists; ++r)
+    for (const kvx_triple& t : p->triples[r]) {
+      n32 += (t.len + 32767) / 32768;
+      bytes += t.len;
+    }
+  if (p->nlists == 1) {  // every region copies the shared list
+    n32 *= p->nreg;
+    bytes *= p->nreg;
+  }
+  if (n32 == 0 || bytes * 10 < n32 * 32768 * 9) return kShapeShort;
+  return n32 >= kFullLaunchPieces ? kShapeLong : kShapeLongSmall;
+}
+
 // Split each triple list into workgroup-sized pieces and give each its
 // offset in its region's staging (the exclusive prefix of the triple
 // lengths).  Pieces of list r carry r as their region tag.
 void build_pieces(kvx_plan_t* p) {
+  p->shape = pick_shape(p);
+  const int64_t piece = shape_piece_bytes(p->shape);
   for (int32_t r = 0; r < p->nlists; ++r) {
     int64_t stg = 0;
     for (const kvx_triple& t : p->triples[r]) {
-      for (int64_t o = 0; o < t.len; o += kPieceBytes) {
-        const int64_t len = std::min<int64_t>(kPieceBytes, t.len - o);
+      for (int64_t o = 0; o < t.len; o += piece) {
+        const int64_t len = std::min<int64_t>(piece, t.len - o);
         p->pieces.push_back(Piece{t.src_off + o, t.dst_off + o, stg + o, int32_t(len), r});
       }
       stg += t.len;

@@ -22,7 +22,7 @@ struct Piece {
   int64_t src_off;
   int64_t dst_off;
   int64_t stg_off;
-  int32_t len;  // bytes, multiple of 16, <= kPieceBytes
+  int32_t len;  // bytes, multiple of 16, <= the plan's piece size
   int32_t reg;  // region offset added to blockIdx.y
 };
 static_assert(sizeof(Piece) == 32, "Piece is 32 bytes");
@@ -40,16 +40,20 @@ inline int32_t pack_slots(int64_t src_slot, int64_t dst_slot) { return int32_t(s
 __host__ __device__ inline int32_t slot_src(int32_t slots) { return slots & 0xffff; }
 __host__ __device__ inline int32_t slot_dst(int32_t slots) { return (slots >> 16) & 0xffff; }
 
-// Launch shape of the layer copy kernel (compile-time tuning knobs).
-#ifndef KVX_THREADS
-#define KVX_THREADS 256
-#endif
-#ifndef KVX_VEC_PER_THREAD
-#define KVX_VEC_PER_THREAD 8
-#endif
-constexpr int kThreads = KVX_THREADS;            // 4 wave64 per workgroup
-constexpr int kVecPerThread = KVX_VEC_PER_THREAD;  // 16-B vectors each lane keeps in flight
-constexpr int64_t kPieceBytes = int64_t(kThreads) * kVecPerThread * 16;  // 32 KiB
+// Launch shapes of the layer copy kernels: lanes per workgroup and 16-byte
+// vectors each lane keeps in flight; a workgroup copies one piece of at most
+// lanes x vectors x 16 bytes.  A plan picks one shape for all its pieces
+// from its own triples (pick_shape in kvx_host.cpp).
+enum CopyShape : int32_t {
+  kShapeLong = 0,       // one wave64 x 32 vectors: 32 KiB pieces
+  kShapeLongSmall = 1,  // one wave64 x 16 vectors: 16 KiB pieces
+  kShapeShort = 2,      // four wave64 x 4 vectors: 16 KiB pieces
+};
+struct ShapeDims {
+  int32_t threads, vecs;
+};
+constexpr ShapeDims kShapes[3] = {{64, 32}, {64, 16}, {256, 4}};
+constexpr int64_t shape_piece_bytes(int32_t s) { return int64_t(kShapes[s].threads) * kShapes[s].vecs * 16; }
 
 // One side's layer group.  Attention pools: nreg regions (K and V, or one
 // latent region) of NB blocks.  State pools: two regions of NB slots of
@@ -87,6 +91,7 @@ struct kvx_plan_s {
   bool host_only = false;
   int32_t nreg = 2;       // regions per layer
   int32_t nlists = 1;     // 1: one triple list shared by every region; 2: one per region
+  int32_t shape = kvx::kShapeLong;  // launch shape of the copy kernels (CopyShape)
   std::vector<kvx_run> runs;
   std::vector<kvx_triple> triples[2];
   std::vector<kvx::Piece> pieces;     // list 0's pieces, then list 1's

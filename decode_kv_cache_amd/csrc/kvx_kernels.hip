@@ -3,10 +3,11 @@
 // kvx_copy_heads, with their C entry points.
 //
 // The work is pure data movement bound by HBM bandwidth: no arithmetic, no
-// MFMA.  Each workgroup (256 lanes = 4 wave64) owns one 32 KiB piece of one
-// (layer, region) pair; every lane issues all of its 16-byte loads before its
-// first store so that a workgroup keeps the whole piece in flight.  Piece
-// descriptors are workgroup-uniform and come in through scalar loads.
+// MFMA.  Each workgroup owns one piece (16 or 32 KiB, by the plan's launch
+// shape) of one (layer, region) pair; every lane issues all of its 16-byte
+// loads before its first store so that a workgroup keeps the whole piece in
+// flight.  Piece descriptors are workgroup-uniform and come in through
+// scalar loads.
 //
 // Sources: [PUSH] push-based NIXL connector post, [MORI] MoRIIO connector
 // note, [BIDIR] bidirectional KV transfer post (full titles in kvx.h).
@@ -55,41 +56,43 @@ constexpr int kBufferWord3 = 0x00020000;  // raw byte buffer, gfx9 family
 __device__ __forceinline__ v4u ld_stream(const v4u* p) { return __builtin_nontemporal_load(p); }
 __device__ __forceinline__ void st_stream(v4u* p, v4u v) { __builtin_nontemporal_store(v, p); }
 
-// Copy `len` bytes (a piece) from `src` to `dst` with the whole workgroup.
+// Copy `len` bytes (a piece, at most T x V x 16) from `src` to `dst` with
+// the whole workgroup of T lanes, each keeping V 16-byte vectors in flight.
 // One buffer resource per piece (base = piece start, size = piece length):
 // lanes past a short piece's end read zeros and their stores are dropped by
 // the hardware range check, so every lane issues all of its loads before its
 // first store without any masking.
+template <int T, int V>
 __device__ __forceinline__ void copy_piece(const uint8_t* src, uint8_t* dst, int32_t len) {
   const __amdgpu_buffer_rsrc_t rs =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(src), (short)0, len, kBufferWord3);
   const __amdgpu_buffer_rsrc_t rd = __builtin_amdgcn_make_buffer_rsrc(dst, (short)0, len, kBufferWord3);
   const int t = threadIdx.x;
-  v4u r[kVecPerThread];
+  v4u r[V];
 #pragma unroll
-  for (int k = 0; k < kVecPerThread; ++k)
-    r[k] = __builtin_amdgcn_raw_buffer_load_b128(rs, (t + k * kThreads) * 16, 0, KVX_LD_AUX);
+  for (int k = 0; k < V; ++k)
+    r[k] = __builtin_amdgcn_raw_buffer_load_b128(rs, (t + k * T) * 16, 0, KVX_LD_AUX);
 #pragma unroll
-  for (int k = 0; k < kVecPerThread; ++k)
-    __builtin_amdgcn_raw_buffer_store_b128(r[k], rd, (t + k * kThreads) * 16, 0, KVX_ST_AUX);
+  for (int k = 0; k < V; ++k)
+    __builtin_amdgcn_raw_buffer_store_b128(r[k], rd, (t + k * T) * 16, 0, KVX_ST_AUX);
 }
 
 // One workgroup copies one piece of region blockIdx.y + piece.reg (one list
 // shared by K and V: y picks the region; one list per region: the tag does);
-// workgroups past the pieces copy the planned blocks' scales.
-template <int MODE>
-__global__ __launch_bounds__(kThreads) void copy_kernel(CopyArgs a) {
+// workgroups past the pieces copy the planned blocks' scales, one per lane.
+template <int MODE, int T, int V>
+__global__ __launch_bounds__(T) void copy_kernel(CopyArgs a) {
   const int x = blockIdx.x;
   if (x < a.n_pieces) {
     const Piece pc = a.pieces[x];
     const int kv = int(blockIdx.y) + pc.reg;
     const int64_t ioff = MODE == kUnpack ? pc.stg_off : pc.src_off;
     const int64_t ooff = MODE == kPack ? pc.stg_off : pc.dst_off;
-    copy_piece(a.in[kv] + ioff, a.out[kv] + ooff, pc.len);
+    copy_piece<T, V>(a.in[kv] + ioff, a.out[kv] + ooff, pc.len);
     return;
   }
   const int kv = blockIdx.y;
-  const int i = (x - a.first_scale_wg) * kThreads + threadIdx.x;
+  const int i = (x - a.first_scale_wg) * T + threadIdx.x;
   if (MODE == kPush) {
     if (i < a.n_blocks) {
       const BlockPair b = a.blocks[i];
@@ -122,7 +125,8 @@ struct ManyArgs {
   ManyEntry e[kManyMax];
 };
 
-__global__ __launch_bounds__(kThreads) void copy_many_kernel(ManyArgs a) {
+template <int T, int V>
+__global__ __launch_bounds__(T) void copy_many_kernel(ManyArgs a) {
   const int x = blockIdx.x;
   // the last entry whose first workgroup is <= x (uniform: scalar loads)
   int lo = 0, hi = a.n - 1;
@@ -136,7 +140,7 @@ __global__ __launch_bounds__(kThreads) void copy_many_kernel(ManyArgs a) {
   const ManyEntry& en = a.e[lo];
   const Piece pc = en.pieces[x - en.first];
   const int kv = int(blockIdx.y) + pc.reg;
-  copy_piece(en.in[kv] + pc.src_off, en.out[kv] + pc.dst_off, pc.len);
+  copy_piece<T, V>(en.in[kv] + pc.src_off, en.out[kv] + pc.dst_off, pc.len);
 }
 
 struct HeadArgs {
@@ -152,25 +156,26 @@ struct HeadArgs {
   int32_t dst_head_major;         // 1: enumerate (head, slot, vec) -- HND destination
 };
 
+constexpr int kHeadThreads = 256;
 constexpr int kHeadUnroll = 4;
 
 // One workgroup moves the head slice of one planned block (or block piece,
 // with different block sizes per side) of region blockIdx.y (K, V or the
 // latent region).  Lanes walk the block's rows in destination order so
 // stores are contiguous; each lane keeps kHeadUnroll vectors in flight.
-__global__ __launch_bounds__(kThreads) void heads_kernel(HeadArgs a) {
+__global__ __launch_bounds__(kHeadThreads) void heads_kernel(HeadArgs a) {
   const int kv = blockIdx.y;
   const BlockPair b = a.blocks[blockIdx.x];
   const uint8_t* sb = a.in[kv] + int64_t(b.src) * a.s_blk + slot_src(b.slots) * a.s_slot;
   uint8_t* db = a.out[kv] + int64_t(b.dst) * a.d_blk + slot_dst(b.slots) * a.d_slot;
   const int rows = a.nh * b.nslots;
   const int total = rows * a.vpr;
-  for (int base = 0; base < total; base += kThreads * kHeadUnroll) {
+  for (int base = 0; base < total; base += kHeadThreads * kHeadUnroll) {
     v4u r[kHeadUnroll];
     int64_t doff[kHeadUnroll];
 #pragma unroll
     for (int k = 0; k < kHeadUnroll; ++k) {
-      const int i = base + k * kThreads + int(threadIdx.x);
+      const int i = base + k * kHeadThreads + int(threadIdx.x);
       if (i < total) {
         const int v = i % a.vpr;
         const int row = i / a.vpr;
@@ -188,27 +193,26 @@ __global__ __launch_bounds__(kThreads) void heads_kernel(HeadArgs a) {
     }
 #pragma unroll
     for (int k = 0; k < kHeadUnroll; ++k) {
-      const int i = base + k * kThreads + int(threadIdx.x);
+      const int i = base + k * kHeadThreads + int(threadIdx.x);
       if (i < total) st_stream(reinterpret_cast<v4u*>(db + doff[k]), r[k]);
     }
   }
   if (a.out_sc[kv] && threadIdx.x == 0) a.out_sc[kv][b.dst] = a.in_sc[kv][b.src];
 }
 
-static int64_t scale_wgs(int64_t slots) { return (slots + kThreads - 1) / kThreads; }
-
 // One shared piece list: one y row per region; one list per region: the tags.
 static unsigned grid_y(const kvx_plan_t* p) { return p->nlists == 1 ? unsigned(p->nreg) : 1u; }
 
-// Enqueue the copy kernel for one layer; `in`/`out` and the scale pointers
-// are already resolved for the mode.  Splits very long work lists.
-template <int MODE>
-static int launch_copy(kvx_plan_t* p, CopyArgs a, int64_t scale_slots, hipStream_t s,
-                       hipEvent_t started = nullptr, hipEvent_t finished = nullptr) {
+// Enqueue the copy kernel of shape (T, V) for one layer; `in`/`out` and the
+// scale pointers are already resolved for the mode.  Splits very long work
+// lists.
+template <int MODE, int T, int V>
+static int launch_copy_shape(kvx_plan_t* p, CopyArgs a, int64_t scale_slots, hipStream_t s, hipEvent_t started,
+                             hipEvent_t finished) {
   const int64_t np = int64_t(p->pieces.size());
   const bool scales = a.in_sc[0] != nullptr;
   const unsigned gy = grid_y(p);
-  const int64_t nsw = scales ? scale_wgs(scale_slots) : 0;
+  const int64_t nsw = scales ? (scale_slots + T - 1) / T : 0;
   a.blocks = p->d_blocks;
   a.n_blocks = int32_t(p->blocks.size());
   a.n_scale_slots = int32_t(scale_slots);
@@ -224,15 +228,48 @@ static int launch_copy(kvx_plan_t* p, CopyArgs a, int64_t scale_slots, hipStream
     if (gx > 0) {
       if (started || finished) {
         // timestamps come from the dispatch packet itself: no extra packets
-        hipExtLaunchKernelGGL(copy_kernel<MODE>, dim3(unsigned(gx), gy), dim3(kThreads), 0, s,
+        hipExtLaunchKernelGGL(copy_kernel<MODE, T, V>, dim3(unsigned(gx), gy), dim3(T), 0, s,
                               first == 0 ? started : nullptr, last ? finished : nullptr, 0u, a);
       } else {
-        hipLaunchKernelGGL(copy_kernel<MODE>, dim3(unsigned(gx), gy), dim3(kThreads), 0, s, a);
+        hipLaunchKernelGGL((copy_kernel<MODE, T, V>), dim3(unsigned(gx), gy), dim3(T), 0, s, a);
       }
     }
     first += cnt;
   } while (first < np);
   return check_launch("kvx copy kernel launch");
+}
+
+template <int MODE>
+static int launch_copy(kvx_plan_t* p, CopyArgs a, int64_t scale_slots, hipStream_t s,
+                       hipEvent_t started = nullptr, hipEvent_t finished = nullptr) {
+  switch (p->shape) {
+    case kShapeLong:
+      return launch_copy_shape<MODE, kShapes[kShapeLong].threads, kShapes[kShapeLong].vecs>(p, a, scale_slots, s,
+                                                                                           started, finished);
+    case kShapeLongSmall:
+      return launch_copy_shape<MODE, kShapes[kShapeLongSmall].threads, kShapes[kShapeLongSmall].vecs>(
+          p, a, scale_slots, s, started, finished);
+    default:
+      return launch_copy_shape<MODE, kShapes[kShapeShort].threads, kShapes[kShapeShort].vecs>(p, a, scale_slots, s,
+                                                                                             started, finished);
+  }
+}
+
+static void launch_many(const ManyArgs& m, int32_t shape, int64_t total, unsigned gy, hipStream_t s) {
+  const dim3 grid(unsigned(total), gy);
+  switch (shape) {
+    case kShapeLong:
+      hipLaunchKernelGGL((copy_many_kernel<kShapes[kShapeLong].threads, kShapes[kShapeLong].vecs>), grid,
+                         dim3(kShapes[kShapeLong].threads), 0, s, m);
+      break;
+    case kShapeLongSmall:
+      hipLaunchKernelGGL((copy_many_kernel<kShapes[kShapeLongSmall].threads, kShapes[kShapeLongSmall].vecs>), grid,
+                         dim3(kShapes[kShapeLongSmall].threads), 0, s, m);
+      break;
+    default:
+      hipLaunchKernelGGL((copy_many_kernel<kShapes[kShapeShort].threads, kShapes[kShapeShort].vecs>), grid,
+                         dim3(kShapes[kShapeShort].threads), 0, s, m);
+  }
 }
 
 static int check_device_plan(const kvx_plan_t* p, const char* fn) {
@@ -295,15 +332,16 @@ int kvx_push_many(const kvx_plan_t* const* plans, const int32_t* layers, int32_t
     rc = enqueue_waits(const_cast<kvx_plan_t*>(plans[i]), nullptr, stream);
     if (rc) return rc;
   }
-  // Consecutive pairs without scales and with the same grid height share a
-  // launch (up to kManyMax entries and kMaxGridX workgroups); the others are
-  // launched alone, in order.
+  // Consecutive pairs without scales and with the same grid height and
+  // launch shape share a launch (up to kManyMax entries and kMaxGridX
+  // workgroups); the others are launched alone, in order.
   ManyArgs m{};
   int64_t total = 0;
   unsigned gy = 0;
+  int32_t shape = 0;
   auto flush = [&]() -> int {
     if (m.n == 0) return KVX_OK;
-    hipLaunchKernelGGL(copy_many_kernel, dim3(unsigned(total), gy), dim3(kThreads), 0, stream, m);
+    launch_many(m, shape, total, gy, stream);
     m.n = 0;
     total = 0;
     return check_launch("kvx copy_many kernel launch");
@@ -320,11 +358,12 @@ int kvx_push_many(const kvx_plan_t* const* plans, const int32_t* layers, int32_t
       continue;
     }
     if (np == 0) continue;
-    if (m.n == kManyMax || (m.n > 0 && (grid_y(p) != gy || total + np > kMaxGridX))) {
+    if (m.n == kManyMax || (m.n > 0 && (grid_y(p) != gy || p->shape != shape || total + np > kMaxGridX))) {
       rc = flush();
       if (rc) return rc;
     }
     gy = grid_y(p);
+    shape = p->shape;
     ManyEntry& e = m.e[m.n++];
     e.pieces = p->d_pieces;
     for (int r = 0; r < p->nreg; ++r) {
@@ -449,7 +488,7 @@ int kvx_copy_heads(const kvx_plan_t* cp, int32_t layer, int32_t src_head0, int32
   for (int64_t first = 0; first < nb; first += kMaxGridX) {
     const int64_t cnt = std::min<int64_t>(nb - first, kMaxGridX);
     a.blocks = p->d_blocks + first;
-    hipLaunchKernelGGL(heads_kernel, dim3(unsigned(cnt), unsigned(p->nreg)), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL(heads_kernel, dim3(unsigned(cnt), unsigned(p->nreg)), dim3(kHeadThreads), 0, stream, a);
   }
   return check_launch("kvx heads kernel launch");
 }

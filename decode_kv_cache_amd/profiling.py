@@ -23,7 +23,7 @@ import statistics
 from collections import defaultdict
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-PUSH_KERNEL = "kvx::copy_kernel<0>"
+PUSH_KERNEL = "kvx::copy_kernel<0, "   # any launch shape of the push mode
 CALIB_KERNEL = "copy_kernel(unsigned int __vector(4)*"   # kvxb_copy in libkvx_bench.so
 CALIB_BYTES = 1 << 30
 

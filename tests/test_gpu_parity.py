@@ -270,6 +270,35 @@ def test_qwen32b_push_full():
     full_push(W.qwen32b_push(), [0, 1, 37, 63], "qwen32b_push")
 
 
+def test_qwen32b_pack_unpack_sampled():
+    """Staging at full size (whole 32 KiB blocks in long runs, the 32 KiB
+    one-wave launch shape): pack of layers [37, 40) byte for byte against the
+    oracle's pack of those layers, and unpack into the consumer pool equal to
+    the oracle's push of them."""
+    wl = W.qwen32b_push()
+    say("workload qwen32b_push staging")
+    gs = S.device_side(wl.src, wl.seed, 1)
+    gd = S.device_side(wl.dst, wl.seed, 2)
+    torch.cuda.synchronize()
+    layers = [37, 38, 39]
+    src_snap, dst_snap = snapshot(gs, layers), snapshot(gd, layers)
+    toks = tokens(wl)
+    plan = kvx.kvx_plan(gs.pool, gd.pool, toks, wl.src_tables, wl.dst_tables)
+    nbytes = kvx.kvx_staging_bytes(plan, 37, 40)
+    stg = torch.full((nbytes,), 0x3C, dtype=torch.uint8, device="cuda")
+    kvx.kvx_pack(plan, 37, 40, stg)
+    kvx.kvx_unpack(plan, 37, 40, stg)
+    torch.cuda.synchronize()
+    op = O.make_plan(P.geom(O, wl.src), P.geom(O, wl.dst), oracle_requests(wl, toks))
+    g3 = O.Geometry(3, *[getattr(op.src_geom, f) for f in ("num_blocks", "block_size", "num_heads", "head_dim",
+                                                            "elem_bytes", "layout", "has_scales")])
+    src3 = O.Pool(g3, np.stack([src_snap[l][0] for l in layers]), None)
+    assert nbytes == O.staging_bytes(op, 37, 40)
+    assert np.array_equal(stg.cpu().numpy(), O.pack(src3, op, 0, 3))
+    check_layers(wl, gs, gd, src_snap, dst_snap, op, layers, "qwen32b staging")
+    plan.close()
+
+
 def test_batched_push_full():
     wl = W.batched_push()
     full_push(wl, [0, 15], "batched_push")

@@ -2,8 +2,10 @@
 launches, leaves every destination exactly as the oracle's push of each pair
 does.  The list mixes K/V, latent, sliding-window and state-slot plans with
 different pools (so grid heights differ between neighbours), more than 32
-pairs (several launches), a plan with scales and an empty plan in the
-middle (launched alone or skipped), and a pair repeated in a later call.
+pairs (several launches), the three launch shapes (long runs of whole
+blocks, long state slots in a small launch, short runs), a plan with scales
+and an empty plan in the middle (launched alone or skipped), and a pair
+repeated in a later call.
 Argument errors enqueue nothing."""
 import numpy as np
 import pytest
@@ -73,13 +75,23 @@ def cases():
                                   elem_bytes=1, has_scales=True, num_requests=3, max_tokens=300)))
     out.append(Case(W.random_case(9014, num_layers=4, num_blocks=64, block_size=16, num_heads=2, head_dim=64,
                                   num_requests=1, max_tokens=0)))
+    # whole 32 KiB blocks in long runs, enough of them for the 32 KiB one-wave
+    # launch shape; and state slots of 64 KiB + 128 KiB (16 KiB one-wave shape)
+    spec = W.PoolSpec(4, 1200, 16, 8, 128, W.BF16)
+    rng = np.random.Generator(np.random.PCG64(9016))
+    need = [W.alloc_blocks(9000, 16)]
+    out.append(Case(W.Workload("long_runs", 9016, spec, spec, [9000],
+                               W.split_tables(W.geometric_run_table(rng, 1200, 8.0), need),
+                               W.split_tables(W.geometric_run_table(rng, 1200, 8.0), need))))
+    out.append(Case(W.random_state_case(9017, num_layers=4, num_slots=16, slot_bytes=(65536, 131072),
+                                        num_requests=6, max_tokens=3), state=True))
     return out
 
 
 def test_push_many_matches_oracle():
     cs = cases()
     rng = np.random.Generator(np.random.PCG64(5))
-    # every (case, layer) pair once, shuffled: 44 pairs, destinations disjoint
+    # every (case, layer) pair once, shuffled: 52 pairs, destinations disjoint
     pairs = [(c, l) for c in cs for l in range(4)]
     order = rng.permutation(len(pairs))
     pairs = [pairs[i] for i in order]
