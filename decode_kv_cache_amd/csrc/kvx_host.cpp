@@ -277,11 +277,13 @@ void build_triples(kvx_plan_t* p) {
 constexpr int64_t kFullLaunchPieces = 1024;
 
 // Launch shape for a plan, from its triples, as measured on MI355X (all
-// shapes side by side on the same pools).  Runs that fill 32 KiB pieces to at
-// least 90% (whole blocks of 16 KiB or more, long state slots) copy fastest
+// shapes side by side on the same pools).  "Fill" is the plan's bytes over
+// the capacity of 32 KiB pieces covering its triples.  Runs that fill them
+// to at least 90% (whole blocks of 32 KiB, long state slots) copy fastest
 // with one-wave workgroups: 32 KiB pieces when a launch has enough of them,
-// 16 KiB pieces otherwise.  Shorter runs (blocks of a few KiB, ragged run
-// ends) copy fastest with four-wave workgroups of 16 KiB pieces.
+// 16 KiB pieces otherwise.  Runs of a few blocks of 16 KiB with ragged ends
+// (fill 50-90%) copy fastest as 4 KiB pieces of four-wave workgroups, and
+// still shorter runs (token rows of an MLA latent) as 8 KiB pieces.
 int32_t pick_shape(const kvx_plan_t* p) {
   int64_t n32 = 0, bytes = 0;
   for (int32_t r = 0; r < p->nlists; ++r)
@@ -293,7 +295,8 @@ int32_t pick_shape(const kvx_plan_t* p) {
     n32 *= p->nreg;
     bytes *= p->nreg;
   }
-  if (n32 == 0 || bytes * 10 < n32 * 32768 * 9) return kShapeShort;
+  if (n32 == 0 || bytes * 2 < n32 * 32768) return kShapeShort;
+  if (bytes * 10 < n32 * 32768 * 9) return kShapeMedium;
   return n32 >= kFullLaunchPieces ? kShapeLong : kShapeLongSmall;
 }
 

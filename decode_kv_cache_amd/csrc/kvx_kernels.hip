@@ -3,7 +3,7 @@
 // kvx_copy_heads, with their C entry points.
 //
 // The work is pure data movement bound by HBM bandwidth: no arithmetic, no
-// MFMA.  Each workgroup owns one piece (16 or 32 KiB, by the plan's launch
+// MFMA.  Each workgroup owns one piece (4 to 32 KiB, by the plan's launch
 // shape) of one (layer, region) pair; every lane issues all of its 16-byte
 // loads before its first store so that a workgroup keeps the whole piece in
 // flight.  Piece descriptors are workgroup-uniform and come in through
@@ -42,14 +42,14 @@ struct CopyArgs {
 };
 
 // Cache policy of the streaming copy (buffer instruction aux bits on gfx950:
-// bit 0 = sc0, bit 1 = nt, bit 4 = sc1).  Nothing is re-read, so loads are
-// non-temporal; stores are non-temporal at device scope (nt sc1), which
-// measured best among the combinations of these bits.
+// bit 0 = sc0, bit 1 = nt, bit 4 = sc1).  Nothing is re-read, so loads and
+// stores are non-temporal (nt); adding sc0 or sc1 measured no better, and
+// dropping nt measured slower.
 #ifndef KVX_LD_AUX
 #define KVX_LD_AUX 2
 #endif
 #ifndef KVX_ST_AUX
-#define KVX_ST_AUX 18
+#define KVX_ST_AUX 2
 #endif
 constexpr int kBufferWord3 = 0x00020000;  // raw byte buffer, gfx9 family
 
@@ -249,6 +249,9 @@ static int launch_copy(kvx_plan_t* p, CopyArgs a, int64_t scale_slots, hipStream
     case kShapeLongSmall:
       return launch_copy_shape<MODE, kShapes[kShapeLongSmall].threads, kShapes[kShapeLongSmall].vecs>(
           p, a, scale_slots, s, started, finished);
+    case kShapeMedium:
+      return launch_copy_shape<MODE, kShapes[kShapeMedium].threads, kShapes[kShapeMedium].vecs>(p, a, scale_slots, s,
+                                                                                               started, finished);
     default:
       return launch_copy_shape<MODE, kShapes[kShapeShort].threads, kShapes[kShapeShort].vecs>(p, a, scale_slots, s,
                                                                                              started, finished);
@@ -265,6 +268,10 @@ static void launch_many(const ManyArgs& m, int32_t shape, int64_t total, unsigne
     case kShapeLongSmall:
       hipLaunchKernelGGL((copy_many_kernel<kShapes[kShapeLongSmall].threads, kShapes[kShapeLongSmall].vecs>), grid,
                          dim3(kShapes[kShapeLongSmall].threads), 0, s, m);
+      break;
+    case kShapeMedium:
+      hipLaunchKernelGGL((copy_many_kernel<kShapes[kShapeMedium].threads, kShapes[kShapeMedium].vecs>), grid,
+                         dim3(kShapes[kShapeMedium].threads), 0, s, m);
       break;
     default:
       hipLaunchKernelGGL((copy_many_kernel<kShapes[kShapeShort].threads, kShapes[kShapeShort].vecs>), grid,
