@@ -565,6 +565,17 @@ int kvx_plan_bytes(const kvx_plan_t* p, int64_t* rd, int64_t* wr) {
   return KVX_OK;
 }
 
+int kvx_plan_launch_shape(const kvx_plan_t* p, kvx_launch_shape* out) {
+  if (!p || !out) return fail(KVX_E_INVAL, "kvx_plan_launch_shape: null argument");
+  if (!p->push_ok) return fail(KVX_E_MISMATCH, "kvx_plan_launch_shape: pools differ in head count or layout");
+  out->pieces = int64_t(p->pieces.size()) * (p->nlists == 1 ? p->nreg : 1);
+  out->piece_bytes = int32_t(shape_piece_bytes(p->shape));
+  out->lanes = kShapes[p->shape].threads;
+  out->vectors = kShapes[p->shape].vecs;
+  out->pad = 0;
+  return KVX_OK;
+}
+
 void kvx_plan_destroy(kvx_plan_t* p) { release(p); }
 
 int kvx_staging_bytes(const kvx_plan_t* p, int32_t l0, int32_t l1, int64_t* bytes) {

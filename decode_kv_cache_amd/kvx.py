@@ -42,6 +42,11 @@ class kvx_run(C.Structure):
     _fields_ = [("src0", C.c_int32), ("dst0", C.c_int32), ("nblk", C.c_int32), ("tail", C.c_int32)]
 
 
+class kvx_launch_shape(C.Structure):
+    _fields_ = [("pieces", C.c_int64), ("piece_bytes", C.c_int32), ("lanes", C.c_int32), ("vectors", C.c_int32),
+                ("pad", C.c_int32)]
+
+
 class kvx_triple(C.Structure):
     _fields_ = [("src_off", C.c_int64), ("dst_off", C.c_int64), ("len", C.c_int64)]
 
@@ -61,6 +66,7 @@ _SIGS = {
     "kvx_plan_runs": (C.c_int, [_P, _P, _I64, C.POINTER(_I64)]),
     "kvx_plan_triples": (C.c_int, [_P, _I32, _I32, _P, _I64, C.POINTER(_I64)]),
     "kvx_plan_bytes": (C.c_int, [_P, C.POINTER(_I64), C.POINTER(_I64)]),
+    "kvx_plan_launch_shape": (C.c_int, [_P, C.POINTER(kvx_launch_shape)]),
     "kvx_plan_destroy": (None, [_P]),
     "kvx_push_layer": (C.c_int, [_P, _I32, _P, _P]),
     "kvx_push_layer_timed": (C.c_int, [_P, _I32, _P, _P, _P, _P]),
@@ -262,6 +268,11 @@ class Plan:
         out = (kvx_triple * max(n.value, 1))()
         _check("kvx_plan_triples", lib().kvx_plan_triples(self.handle, layer, kv, out, n.value, C.byref(n)))
         return np.frombuffer(out, np.int64, count=3 * n.value).reshape(-1, 3).copy()
+
+    def launch_shape(self) -> dict:
+        s = kvx_launch_shape()
+        _check("kvx_plan_launch_shape", lib().kvx_plan_launch_shape(self.handle, C.byref(s)))
+        return {"pieces": s.pieces, "piece_bytes": s.piece_bytes, "lanes": s.lanes, "vectors": s.vectors}
 
     def bytes_per_layer(self):
         r, w = C.c_int64(), C.c_int64()

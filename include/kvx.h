@@ -232,6 +232,21 @@ int kvx_plan_runs(const kvx_plan_t* plan, kvx_run* out, int64_t cap, int64_t* n)
 int kvx_plan_triples(const kvx_plan_t* plan, int32_t layer, int32_t kv,
                      kvx_triple* out, int64_t cap, int64_t* n);
 
+/* Launch shape of a plan's copy kernels, chosen when the plan is built from
+ * its own triples: every workgroup of kvx_push_layer / kvx_pack /
+ * kvx_unpack has `lanes` lanes, each keeping `vectors` 16-byte vectors in
+ * flight, and copies one piece of at most piece_bytes; `pieces` is the
+ * number of such workgroups in one layer's launch (all regions, scale
+ * workgroups not counted).  For diagnostics and tuning only:
+ * the copied bytes do not depend on it. */
+typedef struct kvx_launch_shape {
+  int64_t pieces;
+  int32_t piece_bytes, lanes, vectors, pad;
+} kvx_launch_shape;
+
+/* Errors: INVAL (null), MISMATCH (no push work list). */
+int kvx_plan_launch_shape(const kvx_plan_t* plan, kvx_launch_shape* out);
+
 /* Bytes one layer's push reads and writes (every region's payload plus scales). */
 int kvx_plan_bytes(const kvx_plan_t* plan, int64_t* read_bytes, int64_t* write_bytes);
 

@@ -176,3 +176,42 @@ def test_push_many_argument_errors():
     assert e.value.code == kvx.KVX_E_INVAL     # host-only plan
     with pytest.raises(ValueError):
         kvx.kvx_push_many([p], [0, 1], stream=0)
+
+
+def test_launch_shape_rule():
+    """The copy kernels' launch shape follows how fully a plan's runs fill
+    32 KiB pieces and how many pieces a launch has: long runs of whole 32 KiB
+    blocks take one-wave workgroups (32 KiB pieces from 1024 pieces per
+    launch, 16 KiB below), runs of a few 16 KiB blocks 4 KiB pieces, shorter
+    runs 8 KiB pieces; the work list is cut to that size."""
+    big = W.PoolSpec(1, 2000, 16, 8, 128, W.BF16)       # 32 KiB blocks
+    mid = W.PoolSpec(1, 2000, 16, 8, 64, W.BF16)        # 16 KiB blocks
+    tiny = W.PoolSpec(1, 4000, 1, 1, 576, W.BF16)       # 1152-byte blocks
+
+    def shape(spec, tokens, ids_src, ids_dst):
+        p = kvx.kvx_plan(fake_pool(spec, 0), fake_pool(spec, 1), [tokens], [ids_src], [ids_dst], host_only=True)
+        s = p.launch_shape()
+        t = p.triples(0, 0)
+        assert s["pieces"] == 2 * sum(-(-int(x) // s["piece_bytes"]) for x in t[:, 2])   # K and V
+        return s["lanes"], s["vectors"], s["piece_bytes"]
+    seq = list(range(2000))
+    assert shape(big, 16 * 512, seq[:512], seq[:512]) == (64, 32, 32768)        # 1024 pieces, full
+    assert shape(big, 16 * 511, seq[:511], seq[:511]) == (64, 16, 16384)        # 1022 pieces
+    pairs = [b for k in range(0, 4000, 3) for b in (k, k + 1)][:600]
+    assert shape(mid, 16 * 600, pairs, pairs) == (64, 16, 16384)                # 32 KiB runs, 600 pieces
+    threes = [b for k in range(0, 4000, 4) for b in (k, k + 1, k + 2)][:600]
+    assert shape(mid, 16 * 600, threes, threes) == (256, 1, 4096)               # 48 KiB runs: fill 0.75
+    scattered = list(range(0, 4000, 7))[:500]
+    assert shape(tiny, 500, scattered, scattered) == (256, 2, 8192)             # 1152-byte runs
+
+
+def test_launch_shape_fill_boundaries():
+    """Fill exactly 0.5 takes 4 KiB pieces, just under 0.5 8 KiB pieces;
+    exactly 0.9 one-wave workgroups."""
+    mid = W.PoolSpec(1, 4000, 16, 8, 64, W.BF16)        # 16 KiB blocks
+    sp, dp = fake_pool(mid, 0), fake_pool(mid, 1)
+    alt = list(range(0, 8000, 2))[:1000]
+    s = kvx.kvx_plan(sp, dp, [16 * 1000], [alt], [alt], host_only=True).launch_shape()
+    assert (s["lanes"], s["vectors"]) == (256, 1)          # every run one 16 KiB block: fill exactly 0.5
+    s = kvx.kvx_plan(sp, dp, [16 * 1000 - 1], [alt], [alt], host_only=True).launch_shape()
+    assert (s["lanes"], s["vectors"]) == (256, 2)          # one token short: fill just under 0.5
