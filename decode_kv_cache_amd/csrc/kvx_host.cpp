@@ -272,18 +272,25 @@ void build_triples(kvx_plan_t* p) {
   }
 }
 
-// 32 KiB pieces per launch from which one-wave workgroups of 32 KiB keep
-// every compute unit of an MI355X busy (4 per CU, 256 CUs).
-constexpr int64_t kFullLaunchPieces = 1024;
+// Launch shape for a plan, from its triples, as measured on MI355X (every
+// shape side by side on the same pools, and plain copies of 12 MiB to 4 GiB
+// per launch in each shape).  "Fill" is the plan's bytes over the capacity
+// of the 32 KiB pieces covering its triples; n32 is the number of those
+// pieces in one layer's launch.
+//  - Runs that fill 32 KiB pieces to at least 90% (whole blocks of 32 KiB,
+//    long state slots) in a launch of about one round of one-wave
+//    workgroups per SIMD copy fastest as one-wave workgroups: every load of
+//    a piece issued before its first store, the launch's reads and writes
+//    largely in two phases.  32 KiB pieces from 608 to 1312 of them (19 to
+//    41 MiB read per launch), 16 KiB pieces below that.
+//  - Larger launches (past about 42 MiB read) and runs that fill pieces
+//    less (blocks of 16 KiB or smaller, ragged run ends) stream fastest as
+//    4 KiB pieces of four-wave workgroups: a plain copy in that shape
+//    reaches 6.5 TB/s read+write from 256 MiB per launch, where one-wave
+//    32 KiB pieces stay near 5.3-5.6.
+constexpr int64_t kLongMinPieces = 608;
+constexpr int64_t kLongMaxPieces = 1312;
 
-// Launch shape for a plan, from its triples, as measured on MI355X (all
-// shapes side by side on the same pools).  "Fill" is the plan's bytes over
-// the capacity of 32 KiB pieces covering its triples.  Runs that fill them
-// to at least 90% (whole blocks of 32 KiB, long state slots) copy fastest
-// with one-wave workgroups: 32 KiB pieces when a launch has enough of them,
-// 16 KiB pieces otherwise.  Runs of a few blocks of 16 KiB with ragged ends
-// (fill 50-90%) copy fastest as 4 KiB pieces of four-wave workgroups, and
-// still shorter runs (token rows of an MLA latent) as 8 KiB pieces.
 int32_t pick_shape(const kvx_plan_t* p) {
   int64_t n32 = 0, bytes = 0;
   for (int32_t r = 0; r < p->nlists; ++r)
@@ -295,9 +302,8 @@ int32_t pick_shape(const kvx_plan_t* p) {
     n32 *= p->nreg;
     bytes *= p->nreg;
   }
-  if (n32 == 0 || bytes * 2 < n32 * 32768) return kShapeShort;
-  if (bytes * 10 < n32 * 32768 * 9) return kShapeMedium;
-  return n32 >= kFullLaunchPieces ? kShapeLong : kShapeLongSmall;
+  if (n32 == 0 || n32 > kLongMaxPieces || bytes * 10 < n32 * 32768 * 9) return kShapeFine;
+  return n32 >= kLongMinPieces ? kShapeLong : kShapeLongSmall;
 }
 
 // Split each triple list into workgroup-sized pieces and give each its

@@ -47,14 +47,13 @@ __host__ __device__ inline int32_t slot_dst(int32_t slots) { return (slots >> 16
 enum CopyShape : int32_t {
   kShapeLong = 0,       // one wave64 x 32 vectors: 32 KiB pieces
   kShapeLongSmall = 1,  // one wave64 x 16 vectors: 16 KiB pieces
-  kShapeMedium = 2,     // four wave64 x 1 vector: 4 KiB pieces
-  kShapeShort = 3,      // four wave64 x 2 vectors: 8 KiB pieces
+  kShapeFine = 2,       // four wave64 x 1 vector: 4 KiB pieces
 };
-constexpr int kNumShapes = 4;
+constexpr int kNumShapes = 3;
 struct ShapeDims {
   int32_t threads, vecs;
 };
-constexpr ShapeDims kShapes[kNumShapes] = {{64, 32}, {64, 16}, {256, 1}, {256, 2}};
+constexpr ShapeDims kShapes[kNumShapes] = {{64, 32}, {64, 16}, {256, 1}};
 constexpr int64_t shape_piece_bytes(int32_t s) { return int64_t(kShapes[s].threads) * kShapes[s].vecs * 16; }
 
 // One side's layer group.  Attention pools: nreg regions (K and V, or one

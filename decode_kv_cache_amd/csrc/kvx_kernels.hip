@@ -56,6 +56,28 @@ constexpr int kBufferWord3 = 0x00020000;  // raw byte buffer, gfx9 family
 __device__ __forceinline__ v4u ld_stream(const v4u* p) { return __builtin_nontemporal_load(p); }
 __device__ __forceinline__ void st_stream(v4u* p, v4u v) { __builtin_nontemporal_store(v, p); }
 
+// A workgroup's piece record, read through the constant address space so
+// that it arrives in scalar registers in one 32-byte scalar load.  Read as
+// an ordinary global load, part of it landed in vector registers; the
+// buffer resources built from it were then not provably uniform and every
+// buffer instruction was wrapped in a readfirstlane loop.
+typedef const __attribute__((address_space(4))) v4u* ConstVecs;
+struct PieceBits {
+  v4u lo, hi;
+};
+static_assert(sizeof(PieceBits) == sizeof(Piece), "a piece record is two 16-byte vectors");
+__device__ __forceinline__ Piece load_piece(const Piece* list, int i) {
+  const ConstVecs q = (ConstVecs)(list + i);
+  const PieceBits b = {q[0], q[1]};
+  return __builtin_bit_cast(Piece, b);
+}
+
+// Region pointer r (0 or 1) of a two-entry kernel-argument array, as a
+// select: both entries load with the other arguments, and no second
+// argument load waits on the piece record.
+template <typename P>
+__device__ __forceinline__ P pick(P const (&a)[2], int r) { return r ? a[1] : a[0]; }
+
 // Copy `len` bytes (a piece, at most T x V x 16) from `src` to `dst` with
 // the whole workgroup of T lanes, each keeping V 16-byte vectors in flight.
 // One buffer resource per piece (base = piece start, size = piece length):
@@ -84,11 +106,11 @@ template <int MODE, int T, int V>
 __global__ __launch_bounds__(T) void copy_kernel(CopyArgs a) {
   const int x = blockIdx.x;
   if (x < a.n_pieces) {
-    const Piece pc = a.pieces[x];
+    const Piece pc = load_piece(a.pieces, x);
     const int kv = int(blockIdx.y) + pc.reg;
     const int64_t ioff = MODE == kUnpack ? pc.stg_off : pc.src_off;
     const int64_t ooff = MODE == kPack ? pc.stg_off : pc.dst_off;
-    copy_piece<T, V>(a.in[kv] + ioff, a.out[kv] + ooff, pc.len);
+    copy_piece<T, V>(pick(a.in, kv) + ioff, pick(a.out, kv) + ooff, pc.len);
     return;
   }
   const int kv = blockIdx.y;
@@ -138,9 +160,9 @@ __global__ __launch_bounds__(T) void copy_many_kernel(ManyArgs a) {
       hi = mid - 1;
   }
   const ManyEntry& en = a.e[lo];
-  const Piece pc = en.pieces[x - en.first];
+  const Piece pc = load_piece(en.pieces, x - en.first);
   const int kv = int(blockIdx.y) + pc.reg;
-  copy_piece<T, V>(en.in[kv] + pc.src_off, en.out[kv] + pc.dst_off, pc.len);
+  copy_piece<T, V>(pick(en.in, kv) + pc.src_off, pick(en.out, kv) + pc.dst_off, pc.len);
 }
 
 struct HeadArgs {
@@ -249,12 +271,9 @@ static int launch_copy(kvx_plan_t* p, CopyArgs a, int64_t scale_slots, hipStream
     case kShapeLongSmall:
       return launch_copy_shape<MODE, kShapes[kShapeLongSmall].threads, kShapes[kShapeLongSmall].vecs>(
           p, a, scale_slots, s, started, finished);
-    case kShapeMedium:
-      return launch_copy_shape<MODE, kShapes[kShapeMedium].threads, kShapes[kShapeMedium].vecs>(p, a, scale_slots, s,
-                                                                                               started, finished);
     default:
-      return launch_copy_shape<MODE, kShapes[kShapeShort].threads, kShapes[kShapeShort].vecs>(p, a, scale_slots, s,
-                                                                                             started, finished);
+      return launch_copy_shape<MODE, kShapes[kShapeFine].threads, kShapes[kShapeFine].vecs>(p, a, scale_slots, s,
+                                                                                           started, finished);
   }
 }
 
@@ -269,13 +288,9 @@ static void launch_many(const ManyArgs& m, int32_t shape, int64_t total, unsigne
       hipLaunchKernelGGL((copy_many_kernel<kShapes[kShapeLongSmall].threads, kShapes[kShapeLongSmall].vecs>), grid,
                          dim3(kShapes[kShapeLongSmall].threads), 0, s, m);
       break;
-    case kShapeMedium:
-      hipLaunchKernelGGL((copy_many_kernel<kShapes[kShapeMedium].threads, kShapes[kShapeMedium].vecs>), grid,
-                         dim3(kShapes[kShapeMedium].threads), 0, s, m);
-      break;
     default:
-      hipLaunchKernelGGL((copy_many_kernel<kShapes[kShapeShort].threads, kShapes[kShapeShort].vecs>), grid,
-                         dim3(kShapes[kShapeShort].threads), 0, s, m);
+      hipLaunchKernelGGL((copy_many_kernel<kShapes[kShapeFine].threads, kShapes[kShapeFine].vecs>), grid,
+                         dim3(kShapes[kShapeFine].threads), 0, s, m);
   }
 }
 

@@ -30,8 +30,10 @@ def make(name, seed, spec, prompts, run_mean):
 
 
 CASES = [
-    # whole 32 KiB blocks, long runs, > 1024 pieces per launch
-    make("long_large", 31, W.PoolSpec(2, 1400, 16, 8, 128, W.BF16), [9000, 2100], 12.0),
+    # whole 32 KiB blocks, long runs, about one round of one-wave workgroups (1126 pieces per launch)
+    make("long_round", 31, W.PoolSpec(2, 1400, 16, 8, 128, W.BF16), [9000], 12.0),
+    # whole 32 KiB blocks, long runs, more pieces than one round (2390 per launch): 4 KiB pieces
+    make("long_large", 36, W.PoolSpec(2, 1400, 16, 8, 128, W.BF16), [9000, 2100, 8000], 12.0),
     # whole 32 KiB blocks, long runs, a few hundred pieces per launch
     make("long_small", 32, W.PoolSpec(2, 400, 16, 8, 128, W.BF16), [3000], 12.0),
     # 16 KiB blocks in runs of about 2.5 with ragged request ends
@@ -41,6 +43,11 @@ CASES = [
     # 2 KiB blocks with scales, short runs
     make("short_scales", 35, W.PoolSpec(2, 2000, 16, 1, 64, W.BF16, has_scales=True), [3000, 1200, 4100], 1.5),
 ]
+
+
+# (lanes, vectors per lane) the library picks for each case
+EXPECT = {"long_round": (64, 32), "long_large": (256, 1), "long_small": (64, 16), "medium": (256, 1),
+          "medium_fp8_scales": (256, 1), "short_scales": (256, 1)}
 
 
 @pytest.mark.parametrize("wl", CASES, ids=lambda w: w.name)
@@ -68,6 +75,8 @@ def test_shape_parity(wl):
     # push, layer by layer
     gd = side()
     plan = kvx.kvx_plan(gs.pool, gd.pool, toks, wl.src_tables, wl.dst_tables)
+    shape = plan.launch_shape()
+    assert (shape["lanes"], shape["vectors"]) == EXPECT[wl.name], shape
     for l in range(L):
         kvx.kvx_push_layer(plan, l)
     torch.cuda.synchronize()

@@ -180,10 +180,12 @@ def test_push_many_argument_errors():
 
 def test_launch_shape_rule():
     """The copy kernels' launch shape follows how fully a plan's runs fill
-    32 KiB pieces and how many pieces a launch has: long runs of whole 32 KiB
-    blocks take one-wave workgroups (32 KiB pieces from 1024 pieces per
-    launch, 16 KiB below), runs of a few 16 KiB blocks 4 KiB pieces, shorter
-    runs 8 KiB pieces; the work list is cut to that size."""
+    32 KiB pieces and how many of those pieces one layer's launch has: runs
+    of whole 32 KiB blocks take one-wave workgroups, 32 KiB pieces from 608
+    to 1312 pieces per launch and 16 KiB pieces below; larger launches and
+    runs that fill pieces less (blocks of 16 KiB or smaller, ragged ends)
+    take 4 KiB pieces of four-wave workgroups.  The work list is cut to that
+    size."""
     big = W.PoolSpec(1, 2000, 16, 8, 128, W.BF16)       # 32 KiB blocks
     mid = W.PoolSpec(1, 2000, 16, 8, 64, W.BF16)        # 16 KiB blocks
     tiny = W.PoolSpec(1, 4000, 1, 1, 576, W.BF16)       # 1152-byte blocks
@@ -195,23 +197,27 @@ def test_launch_shape_rule():
         assert s["pieces"] == 2 * sum(-(-int(x) // s["piece_bytes"]) for x in t[:, 2])   # K and V
         return s["lanes"], s["vectors"], s["piece_bytes"]
     seq = list(range(2000))
-    assert shape(big, 16 * 512, seq[:512], seq[:512]) == (64, 32, 32768)        # 1024 pieces, full
-    assert shape(big, 16 * 511, seq[:511], seq[:511]) == (64, 16, 16384)        # 1022 pieces
+    assert shape(big, 16 * 512, seq[:512], seq[:512]) == (64, 32, 32768)        # 1024 pieces
+    assert shape(big, 16 * 656, seq[:656], seq[:656]) == (64, 32, 32768)        # 1312 pieces
+    assert shape(big, 16 * 657, seq[:657], seq[:657]) == (256, 1, 4096)         # 1314 pieces: streams
+    assert shape(big, 16 * 304, seq[:304], seq[:304]) == (64, 32, 32768)        # 608 pieces
+    assert shape(big, 16 * 303, seq[:303], seq[:303]) == (64, 16, 16384)        # 606 pieces
     pairs = [b for k in range(0, 4000, 3) for b in (k, k + 1)][:600]
     assert shape(mid, 16 * 600, pairs, pairs) == (64, 16, 16384)                # 32 KiB runs, 600 pieces
     threes = [b for k in range(0, 4000, 4) for b in (k, k + 1, k + 2)][:600]
     assert shape(mid, 16 * 600, threes, threes) == (256, 1, 4096)               # 48 KiB runs: fill 0.75
     scattered = list(range(0, 4000, 7))[:500]
-    assert shape(tiny, 500, scattered, scattered) == (256, 2, 8192)             # 1152-byte runs
+    assert shape(tiny, 500, scattered, scattered) == (256, 1, 4096)             # 1152-byte runs
 
 
-def test_launch_shape_fill_boundaries():
-    """Fill exactly 0.5 takes 4 KiB pieces, just under 0.5 8 KiB pieces;
-    exactly 0.9 one-wave workgroups."""
+def test_launch_shape_fill_boundary():
+    """Fill exactly 0.9 takes one-wave workgroups, one token less four-wave
+    workgroups of 4 KiB pieces: runs of nine 16 KiB blocks (144 KiB) cover
+    five 32 KiB pieces (160 KiB)."""
     mid = W.PoolSpec(1, 4000, 16, 8, 64, W.BF16)        # 16 KiB blocks
     sp, dp = fake_pool(mid, 0), fake_pool(mid, 1)
-    alt = list(range(0, 8000, 2))[:1000]
-    s = kvx.kvx_plan(sp, dp, [16 * 1000], [alt], [alt], host_only=True).launch_shape()
-    assert (s["lanes"], s["vectors"]) == (256, 1)          # every run one 16 KiB block: fill exactly 0.5
-    s = kvx.kvx_plan(sp, dp, [16 * 1000 - 1], [alt], [alt], host_only=True).launch_shape()
-    assert (s["lanes"], s["vectors"]) == (256, 2)          # one token short: fill just under 0.5
+    nines = [10 * k + j for k in range(100) for j in range(9)]     # 100 runs of 9 blocks: 1000 pieces
+    s = kvx.kvx_plan(sp, dp, [16 * 900], [nines], [nines], host_only=True).launch_shape()
+    assert (s["lanes"], s["vectors"]) == (64, 32)
+    s = kvx.kvx_plan(sp, dp, [16 * 900 - 1], [nines], [nines], host_only=True).launch_shape()
+    assert (s["lanes"], s["vectors"]) == (256, 1)
