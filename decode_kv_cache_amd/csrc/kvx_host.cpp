@@ -32,33 +32,50 @@ int fail_hip(hipError_t e, const char* what) {
   return fail(KVX_E_HIP, "%s: %s (%d)", what, hipGetErrorString(e), int(e));
 }
 
-int wait_event(hipEvent_t ev, hipStream_t s) {
+// True while `s` is capturing a graph.  An event query or a host wait on
+// another thread's behalf would then invalidate the capture, so the waits
+// below take the graph path instead.
+static bool capturing(hipStream_t s) {
+  hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+  return hipStreamIsCapturing(s, &st) == hipSuccess && st == hipStreamCaptureStatusActive;
+}
+
+static int wait_event_on(hipEvent_t ev, hipStream_t s, bool cap) {
   if (!ev) return KVX_OK;
-  // An event whose work has already completed needs no wait: skipping it
-  // saves the queue a barrier packet (several microseconds per layer).
-  hipError_t q = hipEventQuery(ev);
-  if (q == hipErrorNotReady) {
-    hipError_t e = hipStreamWaitEvent(s, ev, 0);
-    if (e != hipSuccess) return fail_hip(e, "hipStreamWaitEvent(ready)");
-  } else if (q != hipSuccess) {
-    return fail_hip(q, "hipEventQuery(ready)");
+  if (!cap) {
+    // An event whose work has already completed needs no wait: skipping it
+    // saves the queue a barrier packet (several microseconds per layer).
+    hipError_t q = hipEventQuery(ev);
+    if (q == hipSuccess) return KVX_OK;
+    if (q != hipErrorNotReady) return fail_hip(q, "hipEventQuery(ready)");
   }
+  // Under capture the wait becomes a graph dependency (the event must have
+  // been recorded in the same capture).
+  hipError_t e = hipStreamWaitEvent(s, ev, 0);
+  if (e != hipSuccess) return fail_hip(e, "hipStreamWaitEvent(ready)");
   return KVX_OK;
 }
 
+int wait_event(hipEvent_t ev, hipStream_t s) { return wait_event_on(ev, s, ev && capturing(s)); }
+
 int enqueue_waits(kvx_plan_t* p, hipEvent_t ready, hipStream_t s) {
-  int rc = wait_event(ready, s);
+  const bool seen = p->upload_seen.load(std::memory_order_acquire);
+  const bool cap = (ready || !seen) && capturing(s);
+  int rc = wait_event_on(ready, s, cap);
   if (rc) return rc;
-  if (!p->upload_seen.load(std::memory_order_acquire)) {
-    hipError_t q = hipEventQuery(p->upload_ev);
-    if (q == hipSuccess) {
-      p->upload_seen.store(true, std::memory_order_release);
-    } else if (q == hipErrorNotReady) {
-      hipError_t e = hipStreamWaitEvent(s, p->upload_ev, 0);
-      if (e != hipSuccess) return fail_hip(e, "hipStreamWaitEvent(upload)");
-    } else {
-      return fail_hip(q, "hipEventQuery(upload)");
-    }
+  if (seen) return KVX_OK;
+  if (cap)  // no query of the upload event is allowed inside the capture
+    return fail(KVX_E_INVAL,
+                "first device call of a plan inside a graph capture: call kvx_plan_wait (or use the plan once) "
+                "before capturing");
+  hipError_t q = hipEventQuery(p->upload_ev);
+  if (q == hipSuccess) {
+    p->upload_seen.store(true, std::memory_order_release);
+  } else if (q == hipErrorNotReady) {
+    hipError_t e = hipStreamWaitEvent(s, p->upload_ev, 0);
+    if (e != hipSuccess) return fail_hip(e, "hipStreamWaitEvent(upload)");
+  } else {
+    return fail_hip(q, "hipEventQuery(upload)");
   }
   return KVX_OK;
 }
@@ -494,6 +511,8 @@ int kvx_plan(const kvx_pool* src, const kvx_pool* dst, int32_t num_requests,
   if (!src || !dst || !out) return fail(KVX_E_INVAL, "kvx_plan: null pool or output");
   if (src == dst) return fail(KVX_E_INVAL, "kvx_plan: src and dst are the same pool");
   if (flags & ~KVX_PLAN_HOST_ONLY) return fail(KVX_E_INVAL, "kvx_plan: unknown flags 0x%x", flags);
+  if (!(flags & KVX_PLAN_HOST_ONLY) && capturing(upload_stream))
+    return fail(KVX_E_INVAL, "kvx_plan: the upload stream is capturing a graph (build plans outside a capture)");
   if (num_requests < 0) return fail(KVX_E_INVAL, "kvx_plan: negative request count");
   if (num_requests > 0 && (!num_tokens || !src_offsets || !dst_offsets))
     return fail(KVX_E_INVAL, "kvx_plan: null num_tokens or offsets");
@@ -557,6 +576,16 @@ int kvx_plan_triples(const kvx_plan_t* p, int32_t layer, int32_t kv, kvx_triple*
   const int64_t cnt = int64_t(t.size());
   if (out && cap >= cnt) std::copy(t.begin(), t.end(), out);
   *n = cnt;
+  return KVX_OK;
+}
+
+int kvx_plan_wait(const kvx_plan_t* cp) {
+  if (!cp) return fail(KVX_E_INVAL, "kvx_plan_wait: null plan");
+  kvx_plan_t* p = const_cast<kvx_plan_t*>(cp);
+  if (p->host_only || p->upload_seen.load(std::memory_order_acquire)) return KVX_OK;
+  const hipError_t e = hipEventSynchronize(p->upload_ev);
+  if (e != hipSuccess) return fail_hip(e, "hipEventSynchronize(upload)");
+  p->upload_seen.store(true, std::memory_order_release);
   return KVX_OK;
 }
 

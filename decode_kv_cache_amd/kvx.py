@@ -67,6 +67,7 @@ _SIGS = {
     "kvx_plan_triples": (C.c_int, [_P, _I32, _I32, _P, _I64, C.POINTER(_I64)]),
     "kvx_plan_bytes": (C.c_int, [_P, C.POINTER(_I64), C.POINTER(_I64)]),
     "kvx_plan_launch_shape": (C.c_int, [_P, C.POINTER(kvx_launch_shape)]),
+    "kvx_plan_wait": (C.c_int, [_P]),
     "kvx_plan_destroy": (None, [_P]),
     "kvx_push_layer": (C.c_int, [_P, _I32, _P, _P]),
     "kvx_push_layer_timed": (C.c_int, [_P, _I32, _P, _P, _P, _P]),
@@ -324,6 +325,12 @@ def kvx_plan_raw(src: Pool, dst: Pool, num_requests: int, num_tokens, src_offset
     rc = lib().kvx_plan(src.handle if src else None, dst.handle if dst else None, num_requests,
                         *(None if a is None else a.ctypes.data for a in keep), flags, stream, C.byref(h))
     return rc, (Plan(h, src, dst) if rc == KVX_OK else None)
+
+
+def kvx_plan_wait(plan: Plan) -> None:
+    """Wait on the host for the plan's descriptor upload (before capturing
+    its device calls into a graph)."""
+    _check("kvx_plan_wait", lib().kvx_plan_wait(plan.handle))
 
 
 def kvx_push_layer(plan: Plan, layer: int, ready=None, stream=None) -> None:

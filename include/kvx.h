@@ -24,8 +24,15 @@
  *     bytes of concurrent calls do not overlap.
  *   - Device calls are asynchronous: they enqueue on the given stream and
  *     return.  `ready` (may be NULL) is waited for with hipStreamWaitEvent
- *     before the kernel runs.  Memory must be device memory of the current
- *     device.
+ *     before the kernel runs (skipped when it has already completed).
+ *     Memory must be device memory of the current device.
+ *   - Graph capture: device calls may be captured into a HIP graph.  Under
+ *     capture, `ready` must have been recorded in the same capture (the wait
+ *     becomes a graph edge), and the plan's descriptor upload must already
+ *     have been observed: by kvx_plan_wait or by one device call outside
+ *     the capture (KVX_E_INVAL otherwise; the capture stays valid).
+ *     kvx_plan must be called outside a capture (KVX_E_INVAL when its
+ *     upload stream is capturing).
  *   - Bytes are copied, never interpreted: bf16, fp8 or any other element type
  *     of 1, 2 or 4 bytes moves bit-exactly.
  */
@@ -205,8 +212,9 @@ void kvx_pool_destroy(kvx_pool* pool);
  * `upload_stream` (NULL = the null stream); later device calls on any stream
  * are ordered after the upload.
  * Validation order per request: token count, list lengths, source IDs, then
- * destination IDs.  Errors: INVAL, RANGE (ID outside its pool), DUPDST (a dst
- * ID used twice in the plan), MISMATCH, UNSUPPORTED, NOMEM, HIP.
+ * destination IDs.  Errors: INVAL (also: upload_stream is capturing a
+ * graph), RANGE (ID outside its pool), DUPDST (a dst ID used twice in the
+ * plan), MISMATCH, UNSUPPORTED, NOMEM, HIP.
  */
 int kvx_plan(const kvx_pool* src, const kvx_pool* dst, int32_t num_requests,
              const int64_t* num_tokens, const int64_t* src_offsets, const int64_t* dst_offsets,
@@ -246,6 +254,12 @@ typedef struct kvx_launch_shape {
 
 /* Errors: INVAL (null), MISMATCH (no push work list). */
 int kvx_plan_launch_shape(const kvx_plan_t* plan, kvx_launch_shape* out);
+
+/* Wait on the host until the plan's descriptor upload has completed, so
+ * that its device calls can be captured into a graph.  Call it outside a
+ * capture.  A host-only plan, or one already observed, returns at once.
+ * Errors: INVAL (null plan), HIP. */
+int kvx_plan_wait(const kvx_plan_t* plan);
 
 /* Bytes one layer's push reads and writes (every region's payload plus scales). */
 int kvx_plan_bytes(const kvx_plan_t* plan, int64_t* read_bytes, int64_t* write_bytes);

@@ -195,6 +195,8 @@ def test_argument_errors():
     L = kvx.lib()
     assert L.kvx_push_layer(plan.handle, 0, None, None) == kvx.KVX_E_INVAL
     assert L.kvx_copy_heads(plan.handle, 0, 0, 0, 1, None, None) == kvx.KVX_E_INVAL
+    assert L.kvx_plan_wait(plan.handle) == kvx.KVX_OK          # nothing uploaded: returns at once
+    assert L.kvx_plan_wait(None) == kvx.KVX_E_INVAL
     with pytest.raises(kvx.KvxError):
         plan.triples(2, 0)
     b = ctypes.c_int64()

@@ -51,3 +51,84 @@ def test_push_replayed_from_graph():
         assert np.array_equal(got, exp.kv), rep
         assert np.array_equal(got[2], dst.kv[2]), rep          # layer 2 is not in the graph
     plan.close()
+
+
+def test_fresh_plan_captured_after_plan_wait():
+    """A plan whose first device call comes inside a capture: without
+    kvx_plan_wait that call is an argument error and the capture stays
+    valid; after kvx_plan_wait its calls capture, and a ready event recorded
+    on a forked stream inside the capture becomes a graph edge (the forked
+    stream writes the source before the push reads it)."""
+    wl = W.random_case(9501, num_layers=3, num_blocks=200, block_size=16, num_heads=2, head_dim=64,
+                       num_requests=2, max_tokens=500, run_mean=2.0)
+    src, dst = P.pools(O, wl)
+    gs = S.device_side(wl.src, wl.seed, 1, values=(src.kv, src.scales))
+    gd = S.device_side(wl.dst, wl.seed, 2, values=(dst.kv, dst.scales))
+    toks = [kvx.kvx_tokens_to_move(p, 0) for p in wl.prompt_lens]
+    side = torch.cuda.Stream()
+    other = torch.cuda.Stream()
+    op = O.make_plan(src.geom, dst.geom, [O.Request(n, s, d) for n, s, d in zip(toks, wl.src_tables, wl.dst_tables)])
+    stage = torch.empty_like(gs.kv)
+    torch.cuda.synchronize()
+    plan = kvx.kvx_plan(gs.pool, gd.pool, toks, wl.src_tables, wl.dst_tables, stream=side)
+    g0 = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g0, stream=side):
+        stage.zero_()
+        with pytest.raises(kvx.KvxError) as e:
+            kvx.kvx_push_layer(plan, 0, stream=torch.cuda.current_stream())
+        assert e.value.code == kvx.KVX_E_INVAL
+    del g0
+    kvx.kvx_plan_wait(plan)
+    ready = torch.cuda.Event()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        cap = torch.cuda.current_stream()
+        other.wait_stream(cap)                      # fork
+        with torch.cuda.stream(other):
+            gs.kv.copy_(stage)                      # "compute" that produces the source
+            ready.record(other)
+        for l in range(3):
+            kvx.kvx_push_layer(plan, l, ready=ready if l == 0 else None, stream=cap)   # join at layer 0
+    exp = dst.copy()
+    rng = np.random.Generator(np.random.PCG64(4))
+    for rep in range(3):
+        new = rng.integers(0, 256, size=src.kv.shape, dtype=np.uint8)
+        stage.copy_(torch.from_numpy(new).cuda())
+        src.kv[...] = new
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        O.push(src, exp, op)
+        assert np.array_equal(gd.kv.cpu().numpy(), exp.kv), rep
+        assert np.array_equal(gs.kv.cpu().numpy(), new), rep
+    plan.close()
+
+
+def test_plan_on_capturing_stream_is_rejected():
+    """kvx_plan's upload would only run at replay, so a capturing upload
+    stream is an argument error; the capture itself stays valid."""
+    wl = W.random_case(9502, num_layers=2, num_blocks=64, block_size=16, num_heads=2, head_dim=64,
+                       num_requests=1, max_tokens=100)
+    src, dst = P.pools(O, wl)
+    gs = S.device_side(wl.src, wl.seed, 1, values=(src.kv, src.scales))
+    gd = S.device_side(wl.dst, wl.seed, 2, values=(dst.kv, dst.scales))
+    toks = [kvx.kvx_tokens_to_move(p, 0) for p in wl.prompt_lens]
+    side = torch.cuda.Stream()
+    plan = kvx.kvx_plan(gs.pool, gd.pool, toks, wl.src_tables, wl.dst_tables, stream=side)
+    kvx.kvx_push_layer(plan, 0, stream=side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        with pytest.raises(kvx.KvxError) as e:
+            kvx.kvx_plan(gs.pool, gd.pool, toks, wl.src_tables, wl.dst_tables, stream=torch.cuda.current_stream())
+        assert e.value.code == kvx.KVX_E_INVAL
+        kvx.kvx_push_layer(plan, 1, stream=torch.cuda.current_stream())
+    gd.kv.copy_(torch.from_numpy(dst.kv).cuda())
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    op = O.make_plan(src.geom, dst.geom, [O.Request(n, s, d) for n, s, d in zip(toks, wl.src_tables, wl.dst_tables)])
+    exp = dst.copy()
+    O.push(src, exp, op, layers=[1])
+    assert np.array_equal(gd.kv.cpu().numpy(), exp.kv)
+    plan.close()
