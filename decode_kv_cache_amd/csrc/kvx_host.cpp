@@ -305,10 +305,7 @@ void build_triples(kvx_plan_t* p) {
 //    4 KiB pieces of four-wave workgroups: a plain copy in that shape
 //    reaches 6.5 TB/s read+write from 256 MiB per launch, where one-wave
 //    32 KiB pieces stay near 5.3-5.6.
-constexpr int64_t kLongMinPieces = 608;
-constexpr int64_t kLongMaxPieces = 1312;
-
-int32_t pick_shape(const kvx_plan_t* p) {
+int32_t pick_shape(kvx_plan_t* p) {
   int64_t n32 = 0, bytes = 0;
   for (int32_t r = 0; r < p->nlists; ++r)
     for (const kvx_triple& t : p->triples[r]) {
@@ -319,6 +316,7 @@ int32_t pick_shape(const kvx_plan_t* p) {
     n32 *= p->nreg;
     bytes *= p->nreg;
   }
+  p->n32 = n32;
   if (n32 == 0 || n32 > kLongMaxPieces || bytes * 10 < n32 * 32768 * 9) return kShapeFine;
   return n32 >= kLongMinPieces ? kShapeLong : kShapeLongSmall;
 }

@@ -55,6 +55,18 @@ struct ShapeDims {
 };
 constexpr ShapeDims kShapes[kNumShapes] = {{64, 32}, {64, 16}, {256, 1}};
 constexpr int64_t shape_piece_bytes(int32_t s) { return int64_t(kShapes[s].threads) * kShapes[s].vecs * 16; }
+// log2 of the 4 KiB chunks in one piece of shape s (kvx_push_many runs any
+// plan's pieces as such chunks when its launch streams).
+constexpr int32_t piece_shift(int32_t s) {
+  return shape_piece_bytes(s) == 32768 ? 3 : shape_piece_bytes(s) == 16384 ? 2 : 0;
+}
+static_assert(shape_piece_bytes(kShapeFine) == 4096, "chunks of kvx_push_many are 4 KiB");
+static_assert(piece_shift(kShapeLong) == 3 && piece_shift(kShapeLongSmall) == 2, "piece sizes");
+// One-wave workgroups of 32 KiB pieces copy fastest when one launch holds
+// kLongMinPieces..kLongMaxPieces of them (about one round per SIMD); see
+// pick_shape in kvx_host.cpp.
+constexpr int64_t kLongMinPieces = 608;
+constexpr int64_t kLongMaxPieces = 1312;
 
 // One side's layer group.  Attention pools: nreg regions (K and V, or one
 // latent region) of NB blocks.  State pools: two regions of NB slots of
@@ -93,6 +105,7 @@ struct kvx_plan_s {
   int32_t nreg = 2;       // regions per layer
   int32_t nlists = 1;     // 1: one triple list shared by every region; 2: one per region
   int32_t shape = kvx::kShapeLong;  // launch shape of the copy kernels (CopyShape)
+  int64_t n32 = 0;                  // 32 KiB pieces covering one layer's triples (all regions)
   std::vector<kvx_run> runs;
   std::vector<kvx_triple> triples[2];
   std::vector<kvx::Piece> pieces;     // list 0's pieces, then list 1's

@@ -132,14 +132,16 @@ __global__ __launch_bounds__(T) void copy_kernel(CopyArgs a) {
 
 // Several (plan, layer) pushes in one launch: entry j owns workgroups
 // [first_j, first_{j+1}) and copies its plan's pieces between its layer's
-// region bases.
+// region bases, each piece as 2^shift_j chunks of T x V x 16 bytes (one
+// workgroup per chunk), so plans cut into larger pieces can run in a
+// smaller launch shape without re-cutting their work lists.
 constexpr int kManyMax = 32;
 struct ManyEntry {
   const Piece* pieces;
   const uint8_t* in[2];
   uint8_t* out[2];
   int32_t first;  // x index of the entry's first workgroup
-  int32_t pad;
+  int32_t shift;  // log2 of workgroups per piece
 };
 struct ManyArgs {
   int32_t n;  // entries
@@ -160,9 +162,13 @@ __global__ __launch_bounds__(T) void copy_many_kernel(ManyArgs a) {
       hi = mid - 1;
   }
   const ManyEntry& en = a.e[lo];
-  const Piece pc = load_piece(en.pieces, x - en.first);
+  const int local = x - en.first;
+  const Piece pc = load_piece(en.pieces, local >> en.shift);
+  const int32_t off = (local & ((1 << en.shift) - 1)) * (T * V * 16);
+  const int32_t len = std::min(pc.len - off, T * V * 16);
+  if (len <= 0) return;  // a chunk past the end of a short piece
   const int kv = int(blockIdx.y) + pc.reg;
-  copy_piece<T, V>(pick(en.in, kv) + pc.src_off, pick(en.out, kv) + pc.dst_off, pc.len);
+  copy_piece<T, V>(pick(en.in, kv) + pc.src_off + off, pick(en.out, kv) + pc.dst_off + off, len);
 }
 
 struct HeadArgs {
@@ -354,24 +360,42 @@ int kvx_push_many(const kvx_plan_t* const* plans, const int32_t* layers, int32_t
     rc = enqueue_waits(const_cast<kvx_plan_t*>(plans[i]), nullptr, stream);
     if (rc) return rc;
   }
-  // Consecutive pairs without scales and with the same grid height and
-  // launch shape share a launch (up to kManyMax entries and kMaxGridX
-  // workgroups); the others are launched alone, in order.
+  // Consecutive pairs without scales and with the same grid height share a
+  // launch (up to kManyMax entries and kMaxGridX workgroups); the others
+  // are launched alone, in order.  A launch whose entries all take the same
+  // one-wave shape and together stay within one round of it (at most
+  // kLongMaxPieces pieces of 32 KiB) runs in that shape; any other launch
+  // streams its pieces as 4 KiB chunks of four-wave workgroups, the shape
+  // that copies long launches fastest.
   ManyArgs m{};
-  int64_t total = 0;
+  int64_t n32 = 0;            // 32 KiB pieces in the launch (all regions)
+  int64_t fine = 0;           // workgroups of the launch in the 4 KiB shape
   unsigned gy = 0;
-  int32_t shape = 0;
+  int32_t shape = -1;         // common shape of the entries, -1 when they differ
+  int32_t np_e[kManyMax] = {};
+  int32_t sh_e[kManyMax] = {};
   auto flush = [&]() -> int {
     if (m.n == 0) return KVX_OK;
-    launch_many(m, shape, total, gy, stream);
+    const bool one_round = shape == kShapeLong || shape == kShapeLongSmall;
+    const bool keep = one_round && n32 <= kLongMaxPieces;
+    int64_t total = 0;
+    for (int32_t j = 0; j < m.n; ++j) {
+      m.e[j].first = int32_t(total);
+      m.e[j].shift = keep ? 0 : sh_e[j];
+      total += int64_t(np_e[j]) << m.e[j].shift;
+    }
+    launch_many(m, keep ? shape : int32_t(kShapeFine), total, gy, stream);
     m.n = 0;
-    total = 0;
+    n32 = 0;
+    fine = 0;
+    shape = -1;
     return check_launch("kvx copy_many kernel launch");
   };
   for (int32_t i = 0; i < n; ++i) {
     kvx_plan_t* p = const_cast<kvx_plan_t*>(plans[i]);
     const int64_t np = int64_t(p->pieces.size());
-    if (p->src.scales || np > kMaxGridX) {
+    const int32_t shift = piece_shift(p->shape);
+    if (p->src.scales || (np << shift) > kMaxGridX) {
       if (np == 0 && p->blocks.empty()) continue;
       rc = flush();
       if (rc) return rc;
@@ -380,20 +404,23 @@ int kvx_push_many(const kvx_plan_t* const* plans, const int32_t* layers, int32_t
       continue;
     }
     if (np == 0) continue;
-    if (m.n == kManyMax || (m.n > 0 && (grid_y(p) != gy || p->shape != shape || total + np > kMaxGridX))) {
+    if (m.n == kManyMax || (m.n > 0 && (grid_y(p) != gy || fine + (np << shift) > kMaxGridX))) {
       rc = flush();
       if (rc) return rc;
     }
+    shape = m.n == 0 || p->shape == shape ? p->shape : -1;
     gy = grid_y(p);
-    shape = p->shape;
-    ManyEntry& e = m.e[m.n++];
+    ManyEntry& e = m.e[m.n];
     e.pieces = p->d_pieces;
     for (int r = 0; r < p->nreg; ++r) {
       e.in[r] = static_cast<const uint8_t*>(p->src.base(r, layers[i]));
       e.out[r] = static_cast<uint8_t*>(p->dst.base(r, layers[i]));
     }
-    e.first = int32_t(total);
-    total += np;
+    np_e[m.n] = int32_t(np);
+    sh_e[m.n] = shift;
+    ++m.n;
+    n32 += p->n32;
+    fine += np << shift;
   }
   return flush();
 }

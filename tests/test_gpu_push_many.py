@@ -115,6 +115,40 @@ def test_push_many_matches_oracle():
         c.plan.close()
 
 
+def test_push_many_launch_choices():
+    """Each launch choice of kvx_push_many against the oracle: one layer of a
+    plan of whole 32 KiB blocks alone (its own one-wave shape, one round),
+    four of its layers together (past one round: each 32 KiB piece runs as
+    eight 4 KiB chunks, the ragged last piece of each run with fewer), state
+    layers of one shape (kept), and a plan of 16 KiB pieces sharing a launch
+    with the 32 KiB one (shapes differ: four and eight chunks per piece).
+    That plan moves the first 200 blocks of the long case's own tables, so
+    its bytes are a subset of the long plan's push of the same layer."""
+    cs = cases()
+    longc = next(c for c in cs if c.wl.name == "long_runs")
+    state = cs[-1]
+    assert longc.plan.launch_shape()["piece_bytes"] == 32768 and longc.plan.launch_shape()["pieces"] > 608
+    assert state.plan.launch_shape()["piece_bytes"] == 16384
+    wl = longc.wl
+    prefix = kvx.kvx_plan(longc.gs.pool, longc.gd.pool, [200 * 16], [wl.src_tables[0][:200]],
+                          [wl.dst_tables[0][:200]])
+    assert prefix.launch_shape()["piece_bytes"] == 16384
+    side = torch.cuda.Stream()
+    for plans, layers in (([longc.plan], [2]), ([longc.plan] * 4, [0, 1, 2, 3]),
+                          ([state.plan] * 4, [0, 1, 2, 3]),
+                          ([prefix, longc.plan, prefix], [1, 1, 3])):
+        kvx.kvx_push_many(plans, layers, stream=side)
+    side.synchronize()
+    for l in (0, 1, 2, 3):
+        longc.expect(l)
+        state.expect(l)
+    longc.check()
+    state.check()
+    prefix.close()
+    for c in cs:
+        c.plan.close()
+
+
 def test_push_many_errors_enqueue_nothing():
     cs = cases()[:2]
     host_plan = kvx.kvx_plan(cs[0].gs.pool, cs[0].gd.pool, [0], [[0]], [[0]], host_only=True)
