@@ -106,6 +106,7 @@ struct kvx_plan_s {
   int32_t nlists = 1;     // 1: one triple list shared by every region; 2: one per region
   int32_t shape = kvx::kShapeLong;  // launch shape of the copy kernels (CopyShape)
   int64_t n32 = 0;                  // 32 KiB pieces covering one layer's triples (all regions)
+  bool overlap = false;             // KVX_PLAN_OVERLAP: launches of this plan overlap each other
   std::vector<kvx_run> runs;
   std::vector<kvx_triple> triples[2];
   std::vector<kvx::Piece> pieces;     // list 0's pieces, then list 1's

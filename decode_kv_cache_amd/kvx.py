@@ -22,6 +22,7 @@ LIB_PATH = os.path.join(_HERE, "libkvx.so")
 KVX_OK, KVX_E_INVAL, KVX_E_RANGE, KVX_E_DUPDST, KVX_E_MISMATCH, KVX_E_UNSUPPORTED, KVX_E_NOMEM, KVX_E_HIP = range(8)
 KVX_NHD, KVX_HND = 0, 1
 KVX_PLAN_HOST_ONLY = 1
+KVX_PLAN_OVERLAP = 2
 LAYOUTS = {"NHD": KVX_NHD, "HND": KVX_HND}
 
 
@@ -296,10 +297,12 @@ def _csr(tables):
 
 
 def kvx_plan(src: Pool, dst: Pool, num_tokens: Sequence[int], src_tables: Sequence[Sequence[int]],
-             dst_tables: Sequence[Sequence[int]], *, host_only: bool = False, stream=None) -> Plan:
+             dst_tables: Sequence[Sequence[int]], *, host_only: bool = False, overlap: bool = False,
+             stream=None) -> Plan:
     """Build a plan.  ``num_tokens[r]`` tokens of request r move; its block
     lists are ``src_tables[r]`` / ``dst_tables[r]`` (each at least as long as
-    its side needs)."""
+    its side needs).  ``overlap``: KVX_PLAN_OVERLAP (the caller keeps several
+    of the plan's device calls in flight at once)."""
     R = len(num_tokens)
     if len(src_tables) != R or len(dst_tables) != R:
         raise ValueError("one src and one dst block list per request")
@@ -310,7 +313,8 @@ def kvx_plan(src: Pool, dst: Pool, num_tokens: Sequence[int], src_tables: Sequen
     us = None if host_only else _stream(stream)
     rc = lib().kvx_plan(src.handle, dst.handle, R, nt.ctypes.data, so.ctypes.data, do.ctypes.data,
                         sid.ctypes.data if sid.size else None, did.ctypes.data if did.size else None,
-                        KVX_PLAN_HOST_ONLY if host_only else 0, us, C.byref(h))
+                        (KVX_PLAN_HOST_ONLY if host_only else 0) | (KVX_PLAN_OVERLAP if overlap else 0), us,
+                        C.byref(h))
     _check("kvx_plan", rc)
     return Plan(h, src, dst)
 

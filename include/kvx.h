@@ -71,6 +71,10 @@ enum {
 /* kvx_plan flags. */
 #define KVX_PLAN_HOST_ONLY 1u /* build the host tables only; no device upload,
                                  device calls on the plan return KVX_E_INVAL */
+#define KVX_PLAN_OVERLAP 2u   /* the caller keeps several device calls of this
+                                 plan in flight at once (e.g. layers alternating
+                                 over two side streams): launches stream small
+                                 pieces instead of filling the chip alone */
 
 /*
  * Pool descriptor: the paged KV cache of one layer group on one side, as

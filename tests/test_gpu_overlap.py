@@ -105,3 +105,38 @@ def test_plan_destroy_waits():
     exp = O.Pool(g, hd[0].copy(), None)
     O.push(O.Pool(g, hs[0], None), exp, O.make_plan(g, g, [O.Request(500 * 16, st[0], dt[0])]))
     assert np.array_equal(gd.kv.cpu().numpy(), exp.kv)
+
+
+def test_overlap_plan_two_streams():
+    """A plan built with KVX_PLAN_OVERLAP (whole 32 KiB blocks, 4 KiB pieces)
+    pushed with its layers alternating over two side streams, each layer
+    after its own fired event: byte-exact against the oracle, and the same
+    bytes as the plan without the flag."""
+    spec = W.PoolSpec(6, 1200, 16, 8, 128, W.BF16)
+    rng = np.random.Generator(np.random.PCG64(9600))
+    need = [W.alloc_blocks(9000, 16)]
+    wl = W.Workload("overlap_two_streams", 9600, spec, spec, [9000],
+                    W.split_tables(W.geometric_run_table(rng, 1200, 4.0), need),
+                    W.split_tables(W.geometric_run_table(rng, 1200, 4.0), need))
+    src, dst = P.pools(O, wl)
+    gs = S.device_side(wl.src, wl.seed, 1, values=(src.kv, src.scales))
+    gd = S.device_side(wl.dst, wl.seed, 2, values=(dst.kv, dst.scales))
+    toks = [kvx.kvx_tokens_to_move(p, 0) for p in wl.prompt_lens]
+    sides = [torch.cuda.Stream(), torch.cuda.Stream()]
+    plan = kvx.kvx_plan(gs.pool, gd.pool, toks, wl.src_tables, wl.dst_tables, overlap=True, stream=sides[0])
+    base = kvx.kvx_plan(gs.pool, gd.pool, toks, wl.src_tables, wl.dst_tables, host_only=True)
+    assert plan.launch_shape()["piece_bytes"] == 4096 and base.launch_shape()["piece_bytes"] == 32768
+    assert np.array_equal(plan.triples(), base.triples())
+    ready = [torch.cuda.Event() for _ in range(spec.num_layers)]
+    for e in ready:
+        e.record()
+    torch.cuda.synchronize()
+    for l in range(spec.num_layers):
+        kvx.kvx_push_layer(plan, l, ready=ready[l], stream=sides[l % 2])
+    torch.cuda.synchronize()
+    op = O.make_plan(src.geom, dst.geom, [O.Request(n, s, d) for n, s, d in zip(toks, wl.src_tables, wl.dst_tables)])
+    exp = dst.copy()
+    O.push(src, exp, op)
+    assert np.array_equal(gd.kv.cpu().numpy(), exp.kv)
+    assert np.array_equal(gs.kv.cpu().numpy(), src.kv)
+    plan.close()

@@ -221,3 +221,22 @@ def test_launch_shape_fill_boundary():
     assert (s["lanes"], s["vectors"]) == (64, 32)
     s = kvx.kvx_plan(sp, dp, [16 * 900 - 1], [nines], [nines], host_only=True).launch_shape()
     assert (s["lanes"], s["vectors"]) == (256, 1)
+
+
+def test_launch_shape_overlap_flag():
+    """KVX_PLAN_OVERLAP: the caller keeps several launches of the plan in
+    flight, so even runs of whole 32 KiB blocks in a launch of one round
+    take 4 KiB pieces of four-wave workgroups; the copied bytes (triples) are
+    those of the plan without the flag."""
+    big = W.PoolSpec(1, 2000, 16, 8, 128, W.BF16)
+    sp, dp = fake_pool(big, 0), fake_pool(big, 1)
+    seq = list(range(512))
+    a = kvx.kvx_plan(sp, dp, [16 * 512], [seq], [seq], host_only=True)
+    b = kvx.kvx_plan(sp, dp, [16 * 512], [seq], [seq], host_only=True, overlap=True)
+    assert (a.launch_shape()["lanes"], a.launch_shape()["vectors"]) == (64, 32)
+    assert (b.launch_shape()["lanes"], b.launch_shape()["vectors"], b.launch_shape()["pieces"]) == (256, 1, 8192)
+    assert np.array_equal(a.triples(), b.triples()) and a.bytes_per_layer() == b.bytes_per_layer()
+    rc, _ = kvx.kvx_plan_raw(sp, dp, 1, np.array([16], np.int64), np.array([0, 1], np.int64),
+                             np.array([0, 1], np.int64), np.array([0], np.int32), np.array([0], np.int32),
+                             flags=kvx.KVX_PLAN_HOST_ONLY | kvx.KVX_PLAN_OVERLAP | 4)
+    assert rc == kvx.KVX_E_INVAL
