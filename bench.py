@@ -743,14 +743,16 @@ def bench_pack(args, torch, kvx, S, W):
                            4 * O.staging_bytes(oplan, 0, len(layers)), args.cpu_seconds, setup)
         log(f"cpu baseline: {cpu['value']} GB/s")
     plan.close()
-    launches = 2 * L
+    # a plan without scales packs and unpacks up to 32 layers per launch (kvx.h)
+    assert not wl.src.has_scales
+    launches = 2 * -(-L // 32)
     return {
         "value": gbs, "ms_per_step": ms, "dtype": "u8",
         "config": {"workload": "pack_unpack", "geometry": "qwen32b_push", "layers": L, "staging_bytes": nbytes,
                    "bytes_per_step": step_bytes,
                    "step": f"kvx_pack of {L} layers then kvx_unpack of {L} layers ({launches} launches)"},
         "roofline": roofline(step_bytes // launches, ms * 1e3 / launches,
-                             "kvx::copy_kernel<1>/<2> (kvx_pack / kvx_unpack)", "pack_unpack"),
+                             "kvx::copy_many_kernel<1>/<2> (kvx_pack / kvx_unpack)", "pack_unpack"),
         "cpu_baseline": cpu,
     }
 

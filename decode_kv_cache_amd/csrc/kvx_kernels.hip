@@ -130,11 +130,13 @@ __global__ __launch_bounds__(T) void copy_kernel(CopyArgs a) {
   }
 }
 
-// Several (plan, layer) pushes in one launch: entry j owns workgroups
-// [first_j, first_{j+1}) and copies its plan's pieces between its layer's
-// region bases, each piece as 2^shift_j chunks of T x V x 16 bytes (one
-// workgroup per chunk), so plans cut into larger pieces can run in a
-// smaller launch shape without re-cutting their work lists.
+// Several (plan, layer) copies of one mode in one launch (kvx_push_many;
+// kvx_pack / kvx_unpack over several layers): entry j owns workgroups
+// [first_j, first_{j+1}) and copies its plan's pieces between its region
+// bases (pool regions of its layer, or that layer's staging segments), each
+// piece as 2^shift_j chunks of T x V x 16 bytes (one workgroup per chunk),
+// so plans cut into larger pieces can run in a smaller launch shape without
+// re-cutting their work lists.
 constexpr int kManyMax = 32;
 struct ManyEntry {
   const Piece* pieces;
@@ -149,7 +151,7 @@ struct ManyArgs {
   ManyEntry e[kManyMax];
 };
 
-template <int T, int V>
+template <int MODE, int T, int V>
 __global__ __launch_bounds__(T) void copy_many_kernel(ManyArgs a) {
   const int x = blockIdx.x;
   // the last entry whose first workgroup is <= x (uniform: scalar loads)
@@ -168,7 +170,9 @@ __global__ __launch_bounds__(T) void copy_many_kernel(ManyArgs a) {
   const int32_t len = std::min(pc.len - off, T * V * 16);
   if (len <= 0) return;  // a chunk past the end of a short piece
   const int kv = int(blockIdx.y) + pc.reg;
-  copy_piece<T, V>(pick(en.in, kv) + pc.src_off + off, pick(en.out, kv) + pc.dst_off + off, len);
+  const int64_t ioff = MODE == kUnpack ? pc.stg_off : pc.src_off;
+  const int64_t ooff = MODE == kPack ? pc.stg_off : pc.dst_off;
+  copy_piece<T, V>(pick(en.in, kv) + ioff + off, pick(en.out, kv) + ooff + off, len);
 }
 
 struct HeadArgs {
@@ -283,22 +287,92 @@ static int launch_copy(kvx_plan_t* p, CopyArgs a, int64_t scale_slots, hipStream
   }
 }
 
+template <int MODE>
 static void launch_many(const ManyArgs& m, int32_t shape, int64_t total, unsigned gy, hipStream_t s) {
   const dim3 grid(unsigned(total), gy);
   switch (shape) {
     case kShapeLong:
-      hipLaunchKernelGGL((copy_many_kernel<kShapes[kShapeLong].threads, kShapes[kShapeLong].vecs>), grid,
+      hipLaunchKernelGGL((copy_many_kernel<MODE, kShapes[kShapeLong].threads, kShapes[kShapeLong].vecs>), grid,
                          dim3(kShapes[kShapeLong].threads), 0, s, m);
       break;
     case kShapeLongSmall:
-      hipLaunchKernelGGL((copy_many_kernel<kShapes[kShapeLongSmall].threads, kShapes[kShapeLongSmall].vecs>), grid,
-                         dim3(kShapes[kShapeLongSmall].threads), 0, s, m);
+      hipLaunchKernelGGL((copy_many_kernel<MODE, kShapes[kShapeLongSmall].threads, kShapes[kShapeLongSmall].vecs>),
+                         grid, dim3(kShapes[kShapeLongSmall].threads), 0, s, m);
       break;
     default:
-      hipLaunchKernelGGL((copy_many_kernel<kShapes[kShapeFine].threads, kShapes[kShapeFine].vecs>), grid,
+      hipLaunchKernelGGL((copy_many_kernel<MODE, kShapes[kShapeFine].threads, kShapes[kShapeFine].vecs>), grid,
                          dim3(kShapes[kShapeFine].threads), 0, s, m);
   }
 }
+
+// Entries of one mode batched into as few launches as the limits allow, in
+// order: consecutive entries with the same grid height share a launch (up
+// to kManyMax entries and kMaxGridX workgroups).  A launch whose entries all
+// take the same one-wave shape and together stay within one round of it (at
+// most kLongMaxPieces pieces of 32 KiB) runs in that shape; any other launch
+// streams its pieces as 4 KiB chunks of four-wave workgroups, the shape that
+// copies long launches fastest.
+template <int MODE>
+class ManyBatch {
+ public:
+  explicit ManyBatch(hipStream_t s) : s_(s) {}
+
+  // Whether plan p's pieces fit a batched launch at all.
+  static bool fits(const kvx_plan_t* p) {
+    return (int64_t(p->pieces.size()) << piece_shift(p->shape)) <= kMaxGridX;
+  }
+
+  int add(const kvx_plan_t* p, const uint8_t* const in[2], uint8_t* const out[2]) {
+    const int64_t np = int64_t(p->pieces.size());
+    if (np == 0) return KVX_OK;
+    const int32_t shift = piece_shift(p->shape);
+    if (m_.n == kManyMax || (m_.n > 0 && (grid_y(p) != gy_ || fine_ + (np << shift) > kMaxGridX))) {
+      const int rc = flush();
+      if (rc) return rc;
+    }
+    shape_ = m_.n == 0 || p->shape == shape_ ? p->shape : -1;
+    gy_ = grid_y(p);
+    ManyEntry& e = m_.e[m_.n];
+    e.pieces = p->d_pieces;
+    for (int r = 0; r < 2; ++r) {
+      e.in[r] = r < p->nreg ? in[r] : nullptr;
+      e.out[r] = r < p->nreg ? out[r] : nullptr;
+    }
+    np_[m_.n] = int32_t(np);
+    shift_[m_.n] = shift;
+    ++m_.n;
+    n32_ += p->n32;
+    fine_ += np << shift;
+    return KVX_OK;
+  }
+
+  int flush() {
+    if (m_.n == 0) return KVX_OK;
+    const bool keep = (shape_ == kShapeLong || shape_ == kShapeLongSmall) && n32_ <= kLongMaxPieces;
+    int64_t total = 0;
+    for (int32_t j = 0; j < m_.n; ++j) {
+      m_.e[j].first = int32_t(total);
+      m_.e[j].shift = keep ? 0 : shift_[j];
+      total += int64_t(np_[j]) << m_.e[j].shift;
+    }
+    launch_many<MODE>(m_, keep ? shape_ : int32_t(kShapeFine), total, gy_, s_);
+    m_.n = 0;
+    n32_ = 0;
+    fine_ = 0;
+    shape_ = -1;
+    return check_launch("kvx copy_many kernel launch");
+  }
+
+ private:
+  hipStream_t s_;
+  ManyArgs m_{};
+  int64_t n32_ = 0;   // 32 KiB pieces in the launch (all regions)
+  int64_t fine_ = 0;  // workgroups of the launch in the 4 KiB shape
+  unsigned gy_ = 0;
+  int32_t shape_ = -1;  // common shape of the entries, -1 when they differ
+  int32_t np_[kManyMax] = {};
+  int32_t shift_[kManyMax] = {};
+};
 
 static int check_device_plan(const kvx_plan_t* p, const char* fn) {
   if (!p) return fail(KVX_E_INVAL, "%s: null plan", fn);
@@ -360,69 +434,24 @@ int kvx_push_many(const kvx_plan_t* const* plans, const int32_t* layers, int32_t
     rc = enqueue_waits(const_cast<kvx_plan_t*>(plans[i]), nullptr, stream);
     if (rc) return rc;
   }
-  // Consecutive pairs without scales and with the same grid height share a
-  // launch (up to kManyMax entries and kMaxGridX workgroups); the others
-  // are launched alone, in order.  A launch whose entries all take the same
-  // one-wave shape and together stay within one round of it (at most
-  // kLongMaxPieces pieces of 32 KiB) runs in that shape; any other launch
-  // streams its pieces as 4 KiB chunks of four-wave workgroups, the shape
-  // that copies long launches fastest.
-  ManyArgs m{};
-  int64_t n32 = 0;            // 32 KiB pieces in the launch (all regions)
-  int64_t fine = 0;           // workgroups of the launch in the 4 KiB shape
-  unsigned gy = 0;
-  int32_t shape = -1;         // common shape of the entries, -1 when they differ
-  int32_t np_e[kManyMax] = {};
-  int32_t sh_e[kManyMax] = {};
-  auto flush = [&]() -> int {
-    if (m.n == 0) return KVX_OK;
-    const bool one_round = shape == kShapeLong || shape == kShapeLongSmall;
-    const bool keep = one_round && n32 <= kLongMaxPieces;
-    int64_t total = 0;
-    for (int32_t j = 0; j < m.n; ++j) {
-      m.e[j].first = int32_t(total);
-      m.e[j].shift = keep ? 0 : sh_e[j];
-      total += int64_t(np_e[j]) << m.e[j].shift;
-    }
-    launch_many(m, keep ? shape : int32_t(kShapeFine), total, gy, stream);
-    m.n = 0;
-    n32 = 0;
-    fine = 0;
-    shape = -1;
-    return check_launch("kvx copy_many kernel launch");
-  };
+  // Pairs without scales share launches (ManyBatch); a pair with scales, or
+  // too many pieces for one launch, is launched alone, in order.
+  ManyBatch<kPush> batch(stream);
   for (int32_t i = 0; i < n; ++i) {
     kvx_plan_t* p = const_cast<kvx_plan_t*>(plans[i]);
-    const int64_t np = int64_t(p->pieces.size());
-    const int32_t shift = piece_shift(p->shape);
-    if (p->src.scales || (np << shift) > kMaxGridX) {
-      if (np == 0 && p->blocks.empty()) continue;
-      rc = flush();
+    if (p->src.scales || !ManyBatch<kPush>::fits(p)) {
+      if (p->pieces.empty() && p->blocks.empty()) continue;
+      rc = batch.flush();
       if (rc) return rc;
       rc = launch_copy<kPush>(p, push_args(p, layers[i]), int64_t(p->blocks.size()), stream);
       if (rc) return rc;
       continue;
     }
-    if (np == 0) continue;
-    if (m.n == kManyMax || (m.n > 0 && (grid_y(p) != gy || fine + (np << shift) > kMaxGridX))) {
-      rc = flush();
-      if (rc) return rc;
-    }
-    shape = m.n == 0 || p->shape == shape ? p->shape : -1;
-    gy = grid_y(p);
-    ManyEntry& e = m.e[m.n];
-    e.pieces = p->d_pieces;
-    for (int r = 0; r < p->nreg; ++r) {
-      e.in[r] = static_cast<const uint8_t*>(p->src.base(r, layers[i]));
-      e.out[r] = static_cast<uint8_t*>(p->dst.base(r, layers[i]));
-    }
-    np_e[m.n] = int32_t(np);
-    sh_e[m.n] = shift;
-    ++m.n;
-    n32 += p->n32;
-    fine += np << shift;
+    const CopyArgs a = push_args(p, layers[i]);
+    rc = batch.add(p, a.in, a.out);
+    if (rc) return rc;
   }
-  return flush();
+  return batch.flush();
 }
 
 static int staging_call(const kvx_plan_t* cp, int32_t l0, int32_t l1, const void* staging,
@@ -452,6 +481,20 @@ int kvx_pack(const kvx_plan_t* cp, int32_t l0, int32_t l1, void* staging, int64_
   const int64_t layer_bytes = p->stg_layer();
   if (layer_bytes == 0) return KVX_OK;
   uint8_t* stg = static_cast<uint8_t*>(staging);
+  if (!p->src.scales && ManyBatch<kPack>::fits(p)) {  // several layers per launch
+    ManyBatch<kPack> batch(stream);
+    for (int32_t l = l0; l < l1; ++l) {
+      const uint8_t* in[2] = {nullptr, nullptr};
+      uint8_t* out[2] = {nullptr, nullptr};
+      for (int r = 0; r < p->nreg; ++r) {
+        in[r] = static_cast<const uint8_t*>(p->src.base(r, l));
+        out[r] = stg + int64_t(l - l0) * layer_bytes + p->stg_offset(r);
+      }
+      rc = batch.add(p, in, out);
+      if (rc) return rc;
+    }
+    return batch.flush();
+  }
   for (int32_t l = l0; l < l1; ++l) {
     CopyArgs a{};
     for (int r = 0; r < p->nreg; ++r) {
@@ -479,6 +522,20 @@ int kvx_unpack(const kvx_plan_t* cp, int32_t l0, int32_t l1, const void* staging
   const int64_t layer_bytes = p->stg_layer();
   if (layer_bytes == 0) return KVX_OK;
   const uint8_t* stg = static_cast<const uint8_t*>(staging);
+  if (!p->dst.scales && ManyBatch<kUnpack>::fits(p)) {  // several layers per launch
+    ManyBatch<kUnpack> batch(stream);
+    for (int32_t l = l0; l < l1; ++l) {
+      const uint8_t* in[2] = {nullptr, nullptr};
+      uint8_t* out[2] = {nullptr, nullptr};
+      for (int r = 0; r < p->nreg; ++r) {
+        in[r] = stg + int64_t(l - l0) * layer_bytes + p->stg_offset(r);
+        out[r] = static_cast<uint8_t*>(p->dst.base(r, l));
+      }
+      rc = batch.add(p, in, out);
+      if (rc) return rc;
+    }
+    return batch.flush();
+  }
   for (int32_t l = l0; l < l1; ++l) {
     CopyArgs a{};
     for (int r = 0; r < p->nreg; ++r) {

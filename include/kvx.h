@@ -332,8 +332,11 @@ int kvx_staging_bytes(const kvx_plan_t* plan, int32_t l0, int32_t l1, int64_t* b
  * (with scales) the planned blocks' fp32 scales in plan order, zero-padded to
  * 16 bytes.  `staging` is device memory, 16-B aligned, of `cap` bytes >=
  * kvx_staging_bytes.  The src pool of the plan is read; nothing else is
- * written.  Errors: INVAL (null, cap too small, host-only plan), RANGE,
- * MISMATCH, UNSUPPORTED (staging misaligned), HIP.
+ * written.  Launches: a plan without scales copies up to 32 layers per
+ * kernel launch (fewer when a launch would exceed 2^22 workgroups of 4 KiB),
+ * a plan with scales one layer per launch.  Errors: INVAL (null, cap too
+ * small, host-only plan), RANGE, MISMATCH, UNSUPPORTED (staging
+ * misaligned), HIP.
  */
 int kvx_pack(const kvx_plan_t* plan, int32_t l0, int32_t l1, void* staging, int64_t cap,
              hipStream_t stream);
