@@ -255,6 +255,7 @@ def bench_push(args, torch, kvx, S, W):
     log(f"with fresh per-layer events: {fresh_gbs:.1f} GB/s")
 
     # Secondary: the step captured once in a HIP graph and replayed.
+    kvx.kvx_plan_wait(plan)
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph, stream=side):
         for l in range(L):

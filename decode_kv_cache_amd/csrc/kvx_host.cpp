@@ -66,8 +66,8 @@ int enqueue_waits(kvx_plan_t* p, hipEvent_t ready, hipStream_t s) {
   if (seen) return KVX_OK;
   if (cap)  // no query of the upload event is allowed inside the capture
     return fail(KVX_E_INVAL,
-                "first device call of a plan inside a graph capture: call kvx_plan_wait (or use the plan once) "
-                "before capturing");
+                "plan's upload not yet observed complete inside a graph capture: call kvx_plan_wait before "
+                "capturing");
   hipError_t q = hipEventQuery(p->upload_ev);
   if (q == hipSuccess) {
     p->upload_seen.store(true, std::memory_order_release);

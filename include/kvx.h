@@ -29,8 +29,8 @@
  *   - Graph capture: device calls may be captured into a HIP graph.  Under
  *     capture, `ready` must have been recorded in the same capture (the wait
  *     becomes a graph edge), and the plan's descriptor upload must already
- *     have been observed: by kvx_plan_wait or by one device call outside
- *     the capture (KVX_E_INVAL otherwise; the capture stays valid).
+ *     have been observed complete on the host: call kvx_plan_wait before
+ *     capturing (KVX_E_INVAL otherwise; the capture stays valid).
  *     kvx_plan must be called outside a capture (KVX_E_INVAL when its
  *     upload stream is capturing).
  *   - Bytes are copied, never interpreted: bf16, fp8 or any other element type

@@ -1,5 +1,5 @@
 """The layerwise push captured in a HIP graph (torch.cuda.CUDAGraph on ROCm)
-and replayed: once the plan's upload has been observed, kvx_push_layer
+and replayed: once the plan's upload has been observed (kvx_plan_wait), kvx_push_layer
 without a ready event enqueues nothing but its kernel (a captured step
 orders the push after the captured compute by stream order), so a serving
 loop can capture a step once and replay it.  The source is rewritten between replays
@@ -31,7 +31,8 @@ def test_push_replayed_from_graph():
     ready = [torch.cuda.Event() for _ in range(4)]
     for e in ready:
         e.record()
-    kvx.kvx_push_layer(plan, 0, ready=ready[0], stream=side)   # upload observed, events fired
+    kvx.kvx_push_layer(plan, 0, ready=ready[0], stream=side)   # events fired
+    kvx.kvx_plan_wait(plan)                                   # upload observed before capturing
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=side):
@@ -54,8 +55,8 @@ def test_push_replayed_from_graph():
 
 
 def test_fresh_plan_captured_after_plan_wait():
-    """A plan whose first device call comes inside a capture: without
-    kvx_plan_wait that call is an argument error and the capture stays
+    """A plan whose upload has not been observed on the host: inside a
+    capture its device call is an argument error and the capture stays
     valid; after kvx_plan_wait its calls capture, and a ready event recorded
     on a forked stream inside the capture becomes a graph edge (the forked
     stream writes the source before the push reads it)."""
@@ -116,6 +117,7 @@ def test_plan_on_capturing_stream_is_rejected():
     side = torch.cuda.Stream()
     plan = kvx.kvx_plan(gs.pool, gd.pool, toks, wl.src_tables, wl.dst_tables, stream=side)
     kvx.kvx_push_layer(plan, 0, stream=side)
+    kvx.kvx_plan_wait(plan)
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=side):
