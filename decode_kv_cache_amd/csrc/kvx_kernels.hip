@@ -1,13 +1,14 @@
 // libkvx device side for gfx950 (CDNA4): the layer copy kernel behind
-// kvx_push_layer / kvx_pack / kvx_unpack and the head-slice kernel behind
-// kvx_copy_heads, with their C entry points.
+// kvx_push_layer / kvx_pack / kvx_unpack, the batched copy kernel behind
+// kvx_push_many and multi-layer kvx_pack / kvx_unpack, and the head-slice
+// kernel behind kvx_copy_heads, with their C entry points.
 //
 // The work is pure data movement bound by HBM bandwidth: no arithmetic, no
-// MFMA.  Each workgroup owns one piece (4 to 32 KiB, by the plan's launch
-// shape) of one (layer, region) pair; every lane issues all of its 16-byte
-// loads before its first store so that a workgroup keeps the whole piece in
-// flight.  Piece descriptors are workgroup-uniform and come in through
-// scalar loads.
+// MFMA.  Each workgroup owns one piece, or one 4 KiB chunk of a piece, of
+// one (layer, region) pair (4 to 32 KiB, by the launch shape); every lane
+// issues all of its 16-byte loads before its first store so that a
+// workgroup keeps the whole piece in flight.  Piece records are
+// workgroup-uniform and come in through scalar loads.
 //
 // Sources: [PUSH] push-based NIXL connector post, [MORI] MoRIIO connector
 // note, [BIDIR] bidirectional KV transfer post (full titles in kvx.h).
@@ -57,10 +58,10 @@ __device__ __forceinline__ v4u ld_stream(const v4u* p) { return __builtin_nontem
 __device__ __forceinline__ void st_stream(v4u* p, v4u v) { __builtin_nontemporal_store(v, p); }
 
 // A workgroup's piece record, read through the constant address space so
-// that it arrives in scalar registers in one 32-byte scalar load.  Read as
-// an ordinary global load, part of it landed in vector registers; the
-// buffer resources built from it were then not provably uniform and every
-// buffer instruction was wrapped in a readfirstlane loop.
+// that it arrives in scalar registers through scalar loads.  Read as an
+// ordinary global load, part of it landed in vector registers; the buffer
+// resources built from it were then not provably uniform and every buffer
+// instruction was wrapped in a readfirstlane loop.
 typedef const __attribute__((address_space(4))) v4u* ConstVecs;
 struct PieceBits {
   v4u lo, hi;
@@ -72,9 +73,9 @@ __device__ __forceinline__ Piece load_piece(const Piece* list, int i) {
   return __builtin_bit_cast(Piece, b);
 }
 
-// Region pointer r (0 or 1) of a two-entry kernel-argument array, as a
-// select: both entries load with the other arguments, and no second
-// argument load waits on the piece record.
+// Region pointer r (0 or 1) of a two-entry kernel-argument array, chosen
+// by a select rather than an indexed access into the argument block (the
+// compiler turns it into one scalar-cache load at the selected offset).
 template <typename P>
 __device__ __forceinline__ P pick(P const (&a)[2], int r) { return r ? a[1] : a[0]; }
 
