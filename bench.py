@@ -269,6 +269,17 @@ def bench_push(args, torch, kvx, S, W):
     log(f"step replayed from a HIP graph: {graph_gbs:.1f} GB/s")
     del graph
 
+    # Secondary: catch-up -- all layers' events already fired, pushed by one
+    # kvx_push_many call (it batches up to 32 layers per launch and streams
+    # them in 4 KiB chunks).
+    many_plans, many_layers = [plan] * L, list(range(L))
+    kvx.kvx_push_many(many_plans, many_layers, stream=side)
+    with Timer(torch, side) as t:
+        for _ in range(args.steps):
+            kvx.kvx_push_many(many_plans, many_layers, stream=side)
+    many_gbs = step_bytes * args.steps / (t.ms * 1e-3) / 1e9
+    log(f"all layers in one kvx_push_many call: {many_gbs:.1f} GB/s")
+
     # Secondary: layers alternating over two side streams, with a plan built
     # for overlapped launches (KVX_PLAN_OVERLAP: 4 KiB pieces of four-wave
     # workgroups, a kernel instantiation of its own, so the headline kernel's
@@ -303,7 +314,8 @@ def bench_push(args, torch, kvx, S, W):
                    "step": f"{L} x kvx_push_layer on one side stream, each after its layer's (fired) event",
                    "host_plan_ms": round(plan_ms, 3), "fresh_event_GBs": round(fresh_gbs, 1),
                    "graph_replay_GBs": round(graph_gbs, 1),
-                   "two_stream_GBs": None if two_gbs is None else round(two_gbs, 1)},
+                   "two_stream_GBs": None if two_gbs is None else round(two_gbs, 1),
+                   "push_many_all_layers_GBs": round(many_gbs, 1)},
         "roofline": roofline(rd + wr, k_avg_us, "kvx::copy_kernel<0> (kvx_push_layer)", args.workload,
                              {"kernel_us_dispatch_stamps": round(float(kd.mean()), 3)}),
         "cpu_baseline": cpu,
