@@ -522,12 +522,15 @@ def bench_batched(args, torch, kvx, S, W):
         for _ in range(args.steps):
             push_only()
     t_p = t.ms / args.steps
-    # calibrate the compute kernel to about one layer's push time
+    # calibrate the compute kernel to about one layer's push time (five
+    # launches timed after two untimed ones, so clock ramp-up does not skew it)
     probe = 20000
-    compute_layer(0, probe)
-    with Timer(torch, compute) as t:
+    for _ in range(2):
         compute_layer(0, probe)
-    iters = max(1000, int(probe * (t_p / L) / t.ms))
+    with Timer(torch, compute) as t:
+        for _ in range(5):
+            compute_layer(0, probe)
+    iters = max(1000, int(probe * (t_p / L) / (t.ms / 5)))
 
     def compute_only():
         for l in range(L):

@@ -42,15 +42,26 @@ struct CopyArgs {
   uint32_t* out_sc[2];
 };
 
-// Cache policy of the streaming copy (buffer instruction aux bits on gfx950:
-// bit 0 = sc0, bit 1 = nt, bit 4 = sc1).  Nothing is re-read, so loads and
-// stores are non-temporal (nt); adding sc0 or sc1 measured no better, and
-// dropping nt measured slower.
+// Cache policy of the copies (buffer instruction aux bits on gfx950: bit 0 =
+// sc0, bit 1 = nt, bit 4 = sc1).  Nothing is re-read, so loads are
+// non-temporal (nt).  Stores depend on the launch shape, from side-by-side
+// measurements:
+//  - one-wave pieces (a launch of about one round) store nt: adding sc0 and
+//    sc1 made the Qwen3-32B-shaped layer 1.8% slower;
+//  - 4 KiB pieces of four-wave workgroups (streaming launches) store nt sc0
+//    sc1, write-through at system scope: 2.8-4% faster on the large
+//    attention layers and the batched push, and about 10% faster when a
+//    compute kernel that ends in stores of its own runs beside the push
+//    (each such kernel's end waits for dirty lines in L2, the push's
+//    included).
 #ifndef KVX_LD_AUX
 #define KVX_LD_AUX 2
 #endif
-#ifndef KVX_ST_AUX
-#define KVX_ST_AUX 2
+#ifndef KVX_ST_AUX_ONE_WAVE
+#define KVX_ST_AUX_ONE_WAVE 2
+#endif
+#ifndef KVX_ST_AUX_FINE
+#define KVX_ST_AUX_FINE 19
 #endif
 constexpr int kBufferWord3 = 0x00020000;  // raw byte buffer, gfx9 family
 
@@ -87,6 +98,7 @@ __device__ __forceinline__ P pick(P const (&a)[2], int r) { return r ? a[1] : a[
 // first store without any masking.
 template <int T, int V>
 __device__ __forceinline__ void copy_piece(const uint8_t* src, uint8_t* dst, int32_t len) {
+  constexpr int kStAux = T == 64 ? KVX_ST_AUX_ONE_WAVE : KVX_ST_AUX_FINE;
   const __amdgpu_buffer_rsrc_t rs =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(src), (short)0, len, kBufferWord3);
   const __amdgpu_buffer_rsrc_t rd = __builtin_amdgcn_make_buffer_rsrc(dst, (short)0, len, kBufferWord3);
@@ -97,7 +109,7 @@ __device__ __forceinline__ void copy_piece(const uint8_t* src, uint8_t* dst, int
     r[k] = __builtin_amdgcn_raw_buffer_load_b128(rs, (t + k * T) * 16, 0, KVX_LD_AUX);
 #pragma unroll
   for (int k = 0; k < V; ++k)
-    __builtin_amdgcn_raw_buffer_store_b128(r[k], rd, (t + k * T) * 16, 0, KVX_ST_AUX);
+    __builtin_amdgcn_raw_buffer_store_b128(r[k], rd, (t + k * T) * 16, 0, kStAux);
 }
 
 // One workgroup copies one piece of region blockIdx.y + piece.reg (one list
