@@ -65,8 +65,6 @@ struct CopyArgs {
 #endif
 constexpr int kBufferWord3 = 0x00020000;  // raw byte buffer, gfx9 family
 
-__device__ __forceinline__ v4u ld_stream(const v4u* p) { return __builtin_nontemporal_load(p); }
-__device__ __forceinline__ void st_stream(v4u* p, v4u v) { __builtin_nontemporal_store(v, p); }
 
 // A workgroup's piece record, read through the constant address space so
 // that it arrives in scalar registers through scalar loads.  Read as an
@@ -201,6 +199,13 @@ struct HeadArgs {
   int32_t dst_head_major;         // 1: enumerate (head, slot, vec) -- HND destination
 };
 
+// Store policy of heads_kernel: the streaming copies' write-through nt sc0
+// sc1 (side by side with nt alone on the TP4 head slice: 53.1 against 53.3
+// us per layer, no real difference; this kernel is bound by its strided
+// source rows).
+#ifndef KVX_HEAD_ST_AUX
+#define KVX_HEAD_ST_AUX KVX_ST_AUX_FINE
+#endif
 constexpr int kHeadThreads = 256;
 constexpr int kHeadUnroll = 4;
 
@@ -213,11 +218,16 @@ __global__ __launch_bounds__(kHeadThreads) void heads_kernel(HeadArgs a) {
   const BlockPair b = a.blocks[blockIdx.x];
   const uint8_t* sb = a.in[kv] + int64_t(b.src) * a.s_blk + slot_src(b.slots) * a.s_slot;
   uint8_t* db = a.out[kv] + int64_t(b.dst) * a.d_blk + slot_dst(b.slots) * a.d_slot;
+  // buffer resources over one block's bytes from the slice's first row on
+  // (every offset below stays inside the block)
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(sb), (short)0, int(a.s_blk), kBufferWord3);
+  const __amdgpu_buffer_rsrc_t rd = __builtin_amdgcn_make_buffer_rsrc(db, (short)0, int(a.d_blk), kBufferWord3);
   const int rows = a.nh * b.nslots;
   const int total = rows * a.vpr;
   for (int base = 0; base < total; base += kHeadThreads * kHeadUnroll) {
     v4u r[kHeadUnroll];
-    int64_t doff[kHeadUnroll];
+    int doff[kHeadUnroll];
 #pragma unroll
     for (int k = 0; k < kHeadUnroll; ++k) {
       const int i = base + k * kHeadThreads + int(threadIdx.x);
@@ -232,14 +242,14 @@ __global__ __launch_bounds__(kHeadThreads) void heads_kernel(HeadArgs a) {
           s = row / a.nh;
           h = row - s * a.nh;
         }
-        r[k] = ld_stream(reinterpret_cast<const v4u*>(sb + s * a.s_slot + h * a.s_head) + v);
-        doff[k] = s * a.d_slot + h * a.d_head + int64_t(v) * 16;
+        r[k] = __builtin_amdgcn_raw_buffer_load_b128(rs, int(s * a.s_slot + h * a.s_head) + v * 16, 0, KVX_LD_AUX);
+        doff[k] = int(s * a.d_slot + h * a.d_head) + v * 16;
       }
     }
 #pragma unroll
     for (int k = 0; k < kHeadUnroll; ++k) {
       const int i = base + k * kHeadThreads + int(threadIdx.x);
-      if (i < total) st_stream(reinterpret_cast<v4u*>(db + doff[k]), r[k]);
+      if (i < total) __builtin_amdgcn_raw_buffer_store_b128(r[k], rd, doff[k], 0, KVX_HEAD_ST_AUX);
     }
   }
   if (a.out_sc[kv] && threadIdx.x == 0) a.out_sc[kv][b.dst] = a.in_sc[kv][b.src];
