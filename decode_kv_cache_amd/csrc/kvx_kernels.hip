@@ -65,7 +65,6 @@ struct CopyArgs {
 #endif
 constexpr int kBufferWord3 = 0x00020000;  // raw byte buffer, gfx9 family
 
-
 // A workgroup's piece record, read through the constant address space so
 // that it arrives in scalar registers through scalar loads.  Read as an
 // ordinary global load, part of it landed in vector registers; the buffer
