@@ -19,6 +19,7 @@ import csv
 import glob
 import hashlib
 import os
+import re
 import statistics
 from collections import defaultdict
 
@@ -28,11 +29,21 @@ CALIB_KERNEL = "copy_kernel(unsigned int __vector(4)*"   # kvxb_copy in libkvx_b
 CALIB_BYTES = 1 << 30
 
 
+def _code_only(text: str) -> str:
+    """Source text without comments and with whitespace runs collapsed, so
+    that edits to comments or layout (which do not change the compiled
+    kernels) keep a counter summary valid.  String literals in these files
+    hold no comment markers."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def kernel_source_digest() -> str:
     h = hashlib.sha256()
     for f in ("kvx_kernels.hip", "kvx_internal.h"):
-        with open(os.path.join(PKG, "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(PKG, "csrc", f), encoding="utf-8") as fh:
+            h.update(_code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 
