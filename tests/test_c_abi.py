@@ -1,8 +1,10 @@
 """The C ABI from C: include/kvx.h and include/kvx_xfer.h compile as strict
-C99 (-pedantic -Werror), and tests/c_abi/plan_from_c.c, linked against the
-in-tree libkvx.so, plans a small case worked by hand through the ABI and
-checks its runs, triples, byte counts and error classes (host-only plans;
-no device memory is touched)."""
+C99 (-pedantic -Werror), and two C programs linked against the in-tree
+libkvx.so check cases worked by hand (host-only: no device memory is
+touched): tests/c_abi/plan_from_c.c plans a transfer and checks its runs,
+triples, byte counts and error classes; tests/c_abi/xfer_from_c.c drives
+the transfer state machine through prefill-first deferral, a failed write
+with its recompute list, and a deferral timeout."""
 import os
 import shutil
 import subprocess
@@ -25,11 +27,12 @@ def test_headers_compile_as_c99():
         assert r.returncode == 0, r.stderr
 
 
-def test_plan_from_c(tmp_path):
+@pytest.mark.parametrize("prog", ["plan_from_c", "xfer_from_c"])
+def test_c_program(prog, tmp_path):
     lib = os.path.join(PKG, "libkvx.so")
     assert os.path.exists(lib), "build libkvx.so first (python -m decode_kv_cache_amd.build)"
-    exe = str(tmp_path / "plan_from_c")
-    r = subprocess.run(["gcc"] + FLAGS + [os.path.join(ROOT, "tests", "c_abi", "plan_from_c.c"), f"-L{PKG}", "-lkvx",
+    exe = str(tmp_path / prog)
+    r = subprocess.run(["gcc"] + FLAGS + [os.path.join(ROOT, "tests", "c_abi", prog + ".c"), f"-L{PKG}", "-lkvx",
                                           f"-Wl,-rpath,{PKG}", "-o", exe], capture_output=True, text=True)
     assert r.returncode == 0, r.stderr
     r = subprocess.run([exe], capture_output=True, text=True, timeout=60)
