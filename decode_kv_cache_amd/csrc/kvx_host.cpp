@@ -343,6 +343,19 @@ void build_pieces(kvx_plan_t* p) {
     }
     p->payload[r] = stg;
   }
+  // Streaming launches take their pieces in destination order: the
+  // workgroups resident at any moment then write a narrow address range
+  // (measured side by side against plan order: the multi-turn fp8 layer 15%
+  // faster, the MLA layer 10%, the batched push 7%, large attention layers
+  // 6%, unpack 5.5%; pack unchanged).  One-wave plans keep plan order: a
+  // launch of about one round issues every piece at once, and their pieces
+  // run fastest in plan order when kvx_push_many streams several plans'
+  // pieces in 4 KiB chunks.  Each piece keeps its staging offset, so the
+  // staging layout does not depend on this order.
+  if (p->shape == kShapeFine)
+    std::stable_sort(p->pieces.begin(), p->pieces.end(), [](const Piece& a, const Piece& b) {
+      return a.reg != b.reg ? a.reg < b.reg : a.dst_off < b.dst_off;
+    });
   if (p->nlists == 1) p->payload[1] = p->payload[0];
 }
 
