@@ -332,17 +332,6 @@ int32_t pick_shape(kvx_plan_t* p) {
 void build_pieces(kvx_plan_t* p) {
   p->shape = pick_shape(p);
   const int64_t piece = shape_piece_bytes(p->shape);
-  for (int32_t r = 0; r < p->nlists; ++r) {
-    int64_t stg = 0;
-    for (const kvx_triple& t : p->triples[r]) {
-      for (int64_t o = 0; o < t.len; o += piece) {
-        const int64_t len = std::min<int64_t>(piece, t.len - o);
-        p->pieces.push_back(Piece{t.src_off + o, t.dst_off + o, stg + o, int32_t(len), r});
-      }
-      stg += t.len;
-    }
-    p->payload[r] = stg;
-  }
   // Streaming launches take their pieces in destination order: the
   // workgroups resident at any moment then write a narrow address range
   // (measured side by side against plan order: the multi-turn fp8 layer 15%
@@ -350,12 +339,30 @@ void build_pieces(kvx_plan_t* p) {
   // 6%, unpack 5.5%; pack unchanged).  One-wave plans keep plan order: a
   // launch of about one round issues every piece at once, and their pieces
   // run fastest in plan order when kvx_push_many streams several plans'
-  // pieces in 4 KiB chunks.  Each piece keeps its staging offset, so the
-  // staging layout does not depend on this order.
-  if (p->shape == kShapeFine)
-    std::stable_sort(p->pieces.begin(), p->pieces.end(), [](const Piece& a, const Piece& b) {
-      return a.reg != b.reg ? a.reg < b.reg : a.dst_off < b.dst_off;
-    });
+  // pieces in 4 KiB chunks.  The triples of one list write disjoint
+  // destination ranges, so ordering the triples orders their pieces; each
+  // piece keeps its staging offset (the exclusive prefix of the triple
+  // lengths in plan order), so the staging layout does not depend on it.
+  const bool by_dst = p->shape == kShapeFine;
+  std::vector<int64_t> stg;
+  std::vector<int32_t> order;
+  for (int32_t r = 0; r < p->nlists; ++r) {
+    const std::vector<kvx_triple>& tr = p->triples[r];
+    stg.assign(tr.size() + 1, 0);
+    for (size_t i = 0; i < tr.size(); ++i) stg[i + 1] = stg[i] + tr[i].len;
+    order.resize(tr.size());
+    for (size_t i = 0; i < tr.size(); ++i) order[i] = int32_t(i);
+    if (by_dst)
+      std::sort(order.begin(), order.end(), [&tr](int32_t a, int32_t b) { return tr[a].dst_off < tr[b].dst_off; });
+    for (const int32_t i : order) {
+      const kvx_triple& t = tr[size_t(i)];
+      for (int64_t o = 0; o < t.len; o += piece) {
+        const int64_t len = std::min<int64_t>(piece, t.len - o);
+        p->pieces.push_back(Piece{t.src_off + o, t.dst_off + o, stg[size_t(i)] + o, int32_t(len), r});
+      }
+    }
+    p->payload[r] = stg.back();
+  }
   if (p->nlists == 1) p->payload[1] = p->payload[0];
 }
 
