@@ -501,6 +501,10 @@ def bench_batched(args, torch, kvx, S, W):
     step_bytes = (rd + wr) * L
     nruns = len(plan.runs())
     log(f"plan: {nruns} runs for {sum(tokens)} tokens, {rd + wr} B per layer, host plan {plan_ms:.1f} ms")
+    if args.counters:
+        counters_run(torch, kvx, plan, side, L, rd + wr)
+        plan.close()
+        return None
     bb = wl.src.block_size * wl.src.num_heads * wl.src.head_dim * wl.src.elem_bytes
     used = np.concatenate([t[:-(-n // wl.src.block_size)] for t, n in zip(wl.src_tables, tokens)])
     blocks = torch.from_numpy(used.astype(np.int32)).cuda()
@@ -895,8 +899,8 @@ def main():
           "tp4_share": bench_tp4, "multiturn_fp8": bench_multiturn, "pack_unpack": bench_pack,
           "dsr1_mla_push": bench_hybrid, "gptoss_swa_push": bench_hybrid,
           "qwen3next_state_push": bench_hybrid}[args.workload]
-    if args.counters and fn is not bench_push:
-        print("bench.py: --counters is for the push workloads", file=sys.stderr)
+    if args.counters and fn not in (bench_push, bench_batched):
+        print("bench.py: --counters is for the qwen32b_push, tiny_push and batched_push workloads", file=sys.stderr)
         sys.exit(2)
     r = fn(args, torch, kvx, S, W)
     if r is None:
