@@ -37,6 +37,7 @@ Prints ONE JSON line on stdout.  Everything else goes to stderr.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import platform
@@ -158,6 +159,28 @@ class Timer:
         self.ms = self.a.elapsed_time(self.b)
 
 
+def inputs_digest(tables, sides, prompt_lens) -> str:
+    """SHA-256 (first 16 hex digits) of a run's inputs: every block table,
+    the prompt lengths, and the first MiB of every physical region (and all
+    scales) of every pool, source and destination pre-fill alike.  Enough to
+    show that two runs used the same seeded bytes without copying whole pools
+    to the host; taken before anything is pushed."""
+    h = hashlib.sha256()
+    for t in tables:
+        h.update(np.ascontiguousarray(t, dtype=np.int32).tobytes())
+    h.update(np.asarray(prompt_lens, dtype=np.int64).tobytes())
+    for side in sides:
+        if hasattr(side, "kv"):
+            regions = [side.kv[p, r] for p in range(side.kv.shape[0]) for r in range(side.kv.shape[1])]
+            if side.sc is not None:
+                h.update(side.sc.cpu().numpy().tobytes())
+        else:
+            regions = [reg[l] for reg in side.regions for l in range(reg.shape[0])]
+        for reg in regions:
+            h.update(reg[:1 << 20].cpu().numpy().tobytes())
+    return h.hexdigest()[:16]
+
+
 def roofline(bytes_per_launch: int, avg_us: float, kernel: str, workload: str, extra=None):
     ach = bytes_per_launch / (avg_us * 1e-6) / 1e9
     r = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -192,6 +215,7 @@ def bench_push(args, torch, kvx, S, W):
         counters_run(torch, kvx, plan, side, L, rd + wr)
         plan.close()
         return None
+    digest = inputs_digest(wl.src_tables + wl.dst_tables, [gs, gd], wl.prompt_lens)
 
     # One ready event per layer, recorded on the compute stream.  The headline
     # step uses events that have already fired (the layer's compute is done):
@@ -306,7 +330,8 @@ def bench_push(args, torch, kvx, S, W):
     plan.close()
     return {
         "value": gbs, "ms_per_step": ms_per_step, "dtype": "u8",
-        "config": {"workload": wl.name, "layers": L, "kv_heads": wl.src.num_heads, "head_dim": wl.src.head_dim,
+        "config": {"workload": wl.name, "seed": wl.seed, "inputs_sha256_16": digest, "layers": L,
+                   "kv_heads": wl.src.num_heads, "head_dim": wl.src.head_dim,
                    "block_size": wl.src.block_size, "payload_dtype": wl.src.dtype, "layout": wl.src.layout,
                    "prompt_tokens": wl.prompt_lens, "tokens_moved": tokens, "pool_blocks": wl.src.num_blocks,
                    "dst_block_size": wl.dst.block_size, "dst_pool_blocks": wl.dst.num_blocks,
@@ -325,7 +350,6 @@ def bench_push(args, torch, kvx, S, W):
 def bench_hybrid(args, torch, kvx, S, W):
     """Layer groups of other shapes (MLA, sliding window, state slots): one
     step pushes every model layer, in model order, from its group's plan."""
-    import oracle as O
     wl = W.HYBRID_WORKLOADS[args.workload]()
     tokens = [kvx.kvx_tokens_to_move(p, 0) for p in wl.prompt_lens]
     side = torch.cuda.Stream()
@@ -335,6 +359,8 @@ def bench_hybrid(args, torch, kvx, S, W):
         gs, gd = S.group_side(g.src, wl.seed, 1 + 10 * gi), S.group_side(g.dst, wl.seed, 2 + 10 * gi)
         sides.append((gs, gd))
     torch.cuda.synchronize()
+    digest = inputs_digest([t for g in wl.groups for t in g.src_tables + g.dst_tables],
+                           [x for pair in sides for x in pair], wl.prompt_lens)
     plan_ms = 0.0
     for gi, g in enumerate(wl.groups):
         gs, gd = sides[gi]
@@ -399,6 +425,7 @@ def bench_hybrid(args, torch, kvx, S, W):
 
     cpu = None
     if not args.no_cpu_baseline:
+        import oracle as O
         sample = list(range(min(8, M)))
         work = []
         setup = 0.0
@@ -433,7 +460,7 @@ def bench_hybrid(args, torch, kvx, S, W):
         p.close()
     return {
         "value": gbs, "ms_per_step": ms_per_step, "dtype": "u8",
-        "config": {"workload": wl.name, "model_layers": M, "prompt_tokens": wl.prompt_lens, "tokens_moved": tokens,
+        "config": {"workload": wl.name, "seed": wl.seed, "inputs_sha256_16": digest, "model_layers": M, "prompt_tokens": wl.prompt_lens, "tokens_moved": tokens,
                    "groups": groups_cfg, "bytes_per_step": step_bytes, "host_plan_ms": round(plan_ms, 3),
                    "step": f"{M} x kvx_push_layer in model order on one side stream, each after its layer's "
                            f"(fired) event"},
@@ -505,6 +532,7 @@ def bench_batched(args, torch, kvx, S, W):
         counters_run(torch, kvx, plan, side, L, rd + wr)
         plan.close()
         return None
+    digest = inputs_digest(wl.src_tables + wl.dst_tables, [gs, gd], wl.prompt_lens)
     bb = wl.src.block_size * wl.src.num_heads * wl.src.head_dim * wl.src.elem_bytes
     used = np.concatenate([t[:-(-n // wl.src.block_size)] for t, n in zip(wl.src_tables, tokens)])
     blocks = torch.from_numpy(used.astype(np.int32)).cuda()
@@ -586,7 +614,8 @@ def bench_batched(args, torch, kvx, S, W):
     plan.close()
     return {
         "value": gbs, "ms_per_step": t_b, "dtype": "u8",
-        "config": {"workload": wl.name, "layers": L, "physical_layer_slabs": wl.src.n_phys,
+        "config": {"workload": wl.name, "seed": wl.seed, "inputs_sha256_16": digest, "layers": L,
+                   "physical_layer_slabs": wl.src.n_phys,
                    "kv_heads": wl.src.num_heads, "head_dim": wl.src.head_dim, "block_size": wl.src.block_size,
                    "payload_dtype": wl.src.dtype, "requests": len(tokens), "tokens_moved_total": int(sum(tokens)),
                    "pool_blocks": wl.src.num_blocks, "merged_runs": nruns, "bytes_per_step": step_bytes,
@@ -606,6 +635,7 @@ def bench_tp4(args, torch, kvx, S, W):
     """tp4_share: per layer, TP4 rank 0's 2-head slice NHD -> HND."""
     wl = W.tp4_share()
     gs, gd = S.device_side(wl.src, wl.seed, 1), S.device_side(wl.dst, wl.seed, 2)
+    digest = inputs_digest(wl.src_tables + wl.dst_tables, [gs, gd], wl.prompt_lens)
     tokens = [kvx.kvx_tokens_to_move(p, 0) for p in wl.prompt_lens]
     side = torch.cuda.Stream()
     plan = kvx.kvx_plan(gs.pool, gd.pool, tokens, wl.src_tables, wl.dst_tables, stream=side)
@@ -646,7 +676,8 @@ def bench_tp4(args, torch, kvx, S, W):
     plan.close()
     return {
         "value": gbs, "ms_per_step": ms, "dtype": "u8",
-        "config": {"workload": wl.name, "layers": L, "src": "NHD, 8 KV heads", "dst": f"HND, {nh} KV heads",
+        "config": {"workload": wl.name, "seed": wl.seed, "inputs_sha256_16": digest, "layers": L,
+                   "src": "NHD, 8 KV heads", "dst": f"HND, {nh} KV heads",
                    "tp_rank": rank, "tp_size": wl.extra["tp_size"], "head_dim": wl.src.head_dim,
                    "block_size": wl.src.block_size, "payload_dtype": wl.src.dtype, "requests": len(tokens),
                    "tokens_moved": tokens[0], "bytes_per_step": step_bytes,
@@ -663,6 +694,8 @@ def bench_multiturn(args, torch, kvx, S, W):
     wl = W.multiturn_fp8()
     ex = wl.extra
     dec, pre = S.device_side(wl.src, wl.seed, 1), S.device_side(wl.dst, wl.seed, 2)
+    digest = inputs_digest(list(ex["decode_tables"]) + [t for k in sorted(ex["prefill_tables"])
+                                                        for t in ex["prefill_tables"][k]], [dec, pre], wl.prompt_lens)
     side = torch.cuda.Stream()
     L = wl.src.num_layers
     plans, step_bytes, plan_ms = [], 0, 0.0
@@ -711,7 +744,8 @@ def bench_multiturn(args, torch, kvx, S, W):
         p.close()
     return {
         "value": gbs, "ms_per_step": ms, "dtype": "u8",
-        "config": {"workload": wl.name, "layers": L, "kv_heads": wl.src.num_heads, "head_dim": wl.src.head_dim,
+        "config": {"workload": wl.name, "seed": wl.seed, "inputs_sha256_16": digest, "layers": L,
+                   "kv_heads": wl.src.num_heads, "head_dim": wl.src.head_dim,
                    "block_size": wl.src.block_size, "payload_dtype": wl.src.dtype, "scales": "fp32 per block",
                    "sessions": ex["sessions"], "turns_copied": turns, "threshold_tokens": ex["threshold"],
                    "bytes_per_step": step_bytes,
@@ -728,6 +762,7 @@ def bench_pack(args, torch, kvx, S, W):
     buffer and scattered from it into the consumer pool."""
     wl = W.qwen32b_push()
     gs, gd = S.device_side(wl.src, wl.seed, 1), S.device_side(wl.dst, wl.seed, 2)
+    digest = inputs_digest(wl.src_tables + wl.dst_tables, [gs, gd], wl.prompt_lens)
     tokens = [kvx.kvx_tokens_to_move(p, 0) for p in wl.prompt_lens]
     side = torch.cuda.Stream()
     plan = kvx.kvx_plan(gs.pool, gd.pool, tokens, wl.src_tables, wl.dst_tables, stream=side)
@@ -768,7 +803,7 @@ def bench_pack(args, torch, kvx, S, W):
     launches = 2 * -(-L // 32)
     return {
         "value": gbs, "ms_per_step": ms, "dtype": "u8",
-        "config": {"workload": "pack_unpack", "geometry": "qwen32b_push", "layers": L, "staging_bytes": nbytes,
+        "config": {"workload": "pack_unpack", "seed": wl.seed, "inputs_sha256_16": digest, "geometry": "qwen32b_push", "layers": L, "staging_bytes": nbytes,
                    "bytes_per_step": step_bytes,
                    "step": f"kvx_pack of {L} layers then kvx_unpack of {L} layers ({launches} launches)"},
         "roofline": roofline(step_bytes // launches, ms * 1e3 / launches,
@@ -787,6 +822,7 @@ def bench_xfer(args, torch, kvx, S, W):
     from decode_kv_cache_amd import bench_support as B
     wl = W.batched_push()
     gs, gd = S.device_side(wl.src, wl.seed, 1), S.device_side(wl.dst, wl.seed, 2)
+    digest = inputs_digest(wl.src_tables + wl.dst_tables, [gs, gd], wl.prompt_lens)
     tokens = [kvx.kvx_tokens_to_move(p, 0) for p in wl.prompt_lens]
     R, L = len(tokens), wl.src.num_layers
     side = torch.cuda.Stream()
@@ -856,7 +892,7 @@ def bench_xfer(args, torch, kvx, S, W):
     ref.close()
     return {
         "value": gbs, "ms_per_step": ms, "dtype": "u8",
-        "config": {"workload": "xfer_pipeline", "geometry": "batched_push", "requests": R, "layers": L,
+        "config": {"workload": "xfer_pipeline", "seed": wl.seed, "inputs_sha256_16": digest, "geometry": "batched_push", "requests": R, "layers": L,
                    "bytes_per_step": step_bytes,
                    "step": f"{R} requests x {L} layers through kvx_xfer (half registered after the forward pass), "
                            f"one synthetic compute kernel per layer",
