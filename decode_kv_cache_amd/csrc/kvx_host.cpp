@@ -336,13 +336,16 @@ void build_pieces(kvx_plan_t* p) {
   // workgroups resident at any moment then write a narrow address range
   // (measured side by side against plan order: the multi-turn fp8 layer 15%
   // faster, the MLA layer 10%, the batched push 7%, large attention layers
-  // 6%, unpack 5.5%; pack unchanged).  One-wave plans keep plan order: a
-  // launch of about one round issues every piece at once, and their pieces
-  // run fastest in plan order when kvx_push_many streams several plans'
-  // pieces in 4 KiB chunks.  The triples of one list write disjoint
-  // destination ranges, so ordering the triples orders their pieces; each
-  // piece keeps its staging offset (the exclusive prefix of the triple
-  // lengths in plan order), so the staging layout does not depend on it.
+  // 6%, unpack 5.5%; pack unchanged).  One-wave launches keep plan order: a
+  // launch of about one round issues every piece at once, and in plan order
+  // it is as fast or faster (state slots 4%).  A one-wave plan also keeps its
+  // pieces in destination order (stream_pieces) for the launches that
+  // stream them as 4 KiB chunks, several layers at once: all 64 layers of
+  // the Qwen3-32B-shaped push in one kvx_push_many call run 4% faster so.
+  // The triples of one list write disjoint destination ranges, so ordering
+  // the triples orders their pieces; each piece keeps its staging offset
+  // (the exclusive prefix of the triple lengths in plan order), so the
+  // staging layout does not depend on it.
   const bool by_dst = p->shape == kShapeFine;
   std::vector<int64_t> stg;
   std::vector<int32_t> order;
@@ -364,27 +367,39 @@ void build_pieces(kvx_plan_t* p) {
     p->payload[r] = stg.back();
   }
   if (p->nlists == 1) p->payload[1] = p->payload[0];
+  if (!by_dst) {
+    p->stream_pieces = p->pieces;
+    std::sort(p->stream_pieces.begin(), p->stream_pieces.end(), [](const Piece& a, const Piece& b) {
+      return a.reg != b.reg ? a.reg < b.reg : a.dst_off < b.dst_off;
+    });
+  }
 }
 
 int upload(kvx_plan_t* p, hipStream_t s) {
   const size_t pb = p->pieces.size() * sizeof(Piece);
+  const size_t sb = p->stream_pieces.size() * sizeof(Piece);
   const size_t bb = p->blocks.size() * sizeof(BlockPair);
-  const size_t total = std::max<size_t>(pb + bb, 256);
+  const size_t total = std::max<size_t>(pb + sb + bb, 256);
   hipError_t e = hipMalloc(&p->dev_buf, total);
   if (e != hipSuccess) {
     p->dev_buf = nullptr;
     return e == hipErrorOutOfMemory ? fail(KVX_E_NOMEM, "kvx_plan: device descriptors (%zu B)", total)
                                     : fail_hip(e, "hipMalloc(plan)");
   }
-  p->d_pieces = static_cast<const Piece*>(p->dev_buf);
-  p->d_blocks = reinterpret_cast<const BlockPair*>(static_cast<char*>(p->dev_buf) + pb);
+  char* const buf = static_cast<char*>(p->dev_buf);
+  p->d_pieces = reinterpret_cast<const Piece*>(buf);
+  p->d_stream = sb ? reinterpret_cast<const Piece*>(buf + pb) : p->d_pieces;
+  p->d_blocks = reinterpret_cast<const BlockPair*>(buf + pb + sb);
   if (pb) {
-    e = hipMemcpyAsync(p->dev_buf, p->pieces.data(), pb, hipMemcpyHostToDevice, s);
+    e = hipMemcpyAsync(buf, p->pieces.data(), pb, hipMemcpyHostToDevice, s);
+    if (e != hipSuccess) return fail_hip(e, "hipMemcpyAsync(pieces)");
+  }
+  if (sb) {
+    e = hipMemcpyAsync(buf + pb, p->stream_pieces.data(), sb, hipMemcpyHostToDevice, s);
     if (e != hipSuccess) return fail_hip(e, "hipMemcpyAsync(pieces)");
   }
   if (bb) {
-    e = hipMemcpyAsync(static_cast<char*>(p->dev_buf) + pb, p->blocks.data(), bb,
-                       hipMemcpyHostToDevice, s);
+    e = hipMemcpyAsync(buf + pb + sb, p->blocks.data(), bb, hipMemcpyHostToDevice, s);
     if (e != hipSuccess) return fail_hip(e, "hipMemcpyAsync(blocks)");
   }
   e = hipEventCreateWithFlags(&p->upload_ev, hipEventDisableTiming);

@@ -110,6 +110,9 @@ struct kvx_plan_s {
   std::vector<kvx_run> runs;
   std::vector<kvx_triple> triples[2];
   std::vector<kvx::Piece> pieces;     // list 0's pieces, then list 1's
+  // One-wave plans only: the same pieces, each list in destination order,
+  // for launches that stream them as 4 KiB chunks (empty otherwise).
+  std::vector<kvx::Piece> stream_pieces;
   std::vector<kvx::BlockPair> blocks;
   int64_t payload[2] = {0, 0};  // moved bytes per (layer, region)
   int64_t scale_seg_bytes = 0;  // per region inside staging (16-B padded), 0 without scales
@@ -124,6 +127,7 @@ struct kvx_plan_s {
   // device side
   void* dev_buf = nullptr;
   const kvx::Piece* d_pieces = nullptr;
+  const kvx::Piece* d_stream = nullptr;  // pieces in streaming order (d_pieces for streaming plans)
   const kvx::BlockPair* d_blocks = nullptr;
   hipEvent_t upload_ev = nullptr;
   std::atomic<bool> upload_seen{false};

@@ -333,7 +333,8 @@ static void launch_many(const ManyArgs& m, int32_t shape, int64_t total, unsigne
 // take the same one-wave shape and together stay within one round of it (at
 // most kLongMaxPieces pieces of 32 KiB) runs in that shape; any other launch
 // streams its pieces as 4 KiB chunks of four-wave workgroups, the shape that
-// copies long launches fastest.
+// copies long launches fastest, taking each plan's pieces in destination
+// order.
 template <int MODE>
 class ManyBatch {
  public:
@@ -356,6 +357,7 @@ class ManyBatch {
     gy_ = grid_y(p);
     ManyEntry& e = m_.e[m_.n];
     e.pieces = p->d_pieces;
+    stream_[m_.n] = p->d_stream;
     for (int r = 0; r < 2; ++r) {
       e.in[r] = r < p->nreg ? in[r] : nullptr;
       e.out[r] = r < p->nreg ? out[r] : nullptr;
@@ -375,6 +377,7 @@ class ManyBatch {
     for (int32_t j = 0; j < m_.n; ++j) {
       m_.e[j].first = int32_t(total);
       m_.e[j].shift = keep ? 0 : shift_[j];
+      if (!keep) m_.e[j].pieces = stream_[j];
       total += int64_t(np_[j]) << m_.e[j].shift;
     }
     launch_many<MODE>(m_, keep ? shape_ : int32_t(kShapeFine), total, gy_, s_);
@@ -394,6 +397,7 @@ class ManyBatch {
   int32_t shape_ = -1;  // common shape of the entries, -1 when they differ
   int32_t np_[kManyMax] = {};
   int32_t shift_[kManyMax] = {};
+  const Piece* stream_[kManyMax] = {};  // each entry's pieces in streaming order
 };
 
 static int check_device_plan(const kvx_plan_t* p, const char* fn) {

@@ -310,8 +310,9 @@ int kvx_push_layer_timed(const kvx_plan_t* plan, int32_t layer, hipEvent_t ready
  * launch of up to 32 entries; pairs with per-block scales, or whose work
  * list alone fills a launch, run as launches of their own, in order.  A
  * shared launch runs in its plans' common one-wave shape when it stays
- * within about one round of it, else as 4 KiB chunks of every plan's pieces
- * (see kvx_plan_launch_shape).  Everything is ordered after `ready`
+ * within about one round of it, else as 4 KiB chunks of every plan's pieces,
+ * each plan's taken in destination order (see kvx_plan_launch_shape).
+ * Everything is ordered after `ready`
  * and before later work on `stream`.  All pairs are validated before
  * anything is enqueued.
  * Errors: INVAL (n < 0, null arrays with n > 0, a null or host-only plan),
