@@ -8,6 +8,7 @@
 
 #include <algorithm>
 #include <cstdarg>
+#include <cstdint>
 #include <cstdio>
 #include <cstring>
 #include <new>
@@ -155,6 +156,10 @@ int kvx_pool_create(const kvx_pool_desc* d, kvx_pool** out) {
   if ((int64_t(d->head_dim) * d->elem_bytes) % 16)
     return fail(KVX_E_UNSUPPORTED, "kvx_pool_create: head_dim*elem_bytes=%lld not a multiple of 16",
                 (long long)(int64_t(d->head_dim) * d->elem_bytes));
+  // The head-slice kernel addresses inside one block with 32-bit offsets.
+  const int64_t blk = int64_t(d->block_size) * d->num_heads * d->head_dim * d->elem_bytes;
+  if (blk > INT32_MAX)
+    return fail(KVX_E_UNSUPPORTED, "kvx_pool_create: block of %lld bytes (2^31 or more)", (long long)blk);
   kvx_pool* p = new (std::nothrow) kvx_pool;
   if (!p) return fail(KVX_E_NOMEM, "kvx_pool_create: out of host memory");
   Geom& g = p->g;

@@ -164,7 +164,9 @@ int64_t kvx_tokens_to_move(int64_t prompt_len, int64_t num_computed);
 int32_t kvx_should_reuse(int64_t reusable_tokens, int64_t threshold);
 
 /* Register one side's KV cache.  Host-only: no device call is made.
- * Errors: INVAL (null/invalid field), UNSUPPORTED (alignment), NOMEM. */
+ * Errors: INVAL (null/invalid field), UNSUPPORTED (a base not 16-byte or a
+ * scale array not 4-byte aligned, head_dim*elem_bytes not a multiple of 16,
+ * block_size above 32768, a block of 2^31 bytes or more per region), NOMEM. */
 int kvx_pool_create(const kvx_pool_desc* desc, kvx_pool** out);
 
 /* Register a state-slot pool.  Host-only.  Errors: INVAL, UNSUPPORTED, NOMEM. */

@@ -227,6 +227,14 @@ def test_pool_create_errors():
         kvx.Pool(num_blocks=8, block_size=4, num_heads=1, head_dim=16, elem_bytes=3, layout="NHD",
                  k_bases=[FAKE], v_bases=[FAKE * 2])
     assert e.value.code == kvx.KVX_E_INVAL
+    # a block of 2^31 bytes per region (32768 slots x 16 heads x 1024 x 4 B) is refused; one slot less is not
+    with pytest.raises(kvx.KvxError) as e:
+        kvx.Pool(num_blocks=1, block_size=32768, num_heads=16, head_dim=1024, elem_bytes=4, layout="HND",
+                 k_bases=[FAKE], v_bases=[FAKE * 2])
+    assert e.value.code == kvx.KVX_E_UNSUPPORTED
+    assert b"2^31" in kvx.lib().kvx_last_error()
+    kvx.Pool(num_blocks=1, block_size=32767, num_heads=16, head_dim=1024, elem_bytes=4, layout="HND",
+             k_bases=[FAKE], v_bases=[FAKE * 2]).close()
     fake_pool(spec, 0).close()
 
 
