@@ -135,6 +135,42 @@ def test_copy_heads_random_small():
         plan.close()
 
 
+
+def test_copy_heads_shared_source_prefix():
+    """Head transform (4 heads NHD -> 2 heads HND, so copy_heads is the plan's
+    only device call) for requests that share a source prefix: equal source
+    blocks occur in several block pairs.  Equal and different block sizes."""
+    for dst_bs in (4, 8):
+        src_spec = W.PoolSpec(2, 64, 4, 4, 16, W.BF16, "NHD", has_scales=True)
+        dst_spec = W.PoolSpec(2, 64, dst_bs, 2, 16, W.BF16, "HND", has_scales=dst_bs == 4)
+        if dst_bs != 4:
+            src_spec = W.PoolSpec(2, 64, 4, 4, 16, W.BF16, "NHD")
+        shared = [9, 10, 11, 40, 41]
+        src_tables = [shared + [3, 4, 5], shared + [20], shared[:3] + [50, 51, 52]]
+        prompts = [30, 24, 23]
+        dst_free = list(range(63, 0, -1))
+        dst_tables = []
+        for pl in prompts:
+            n = W.alloc_blocks(pl, dst_bs)
+            dst_tables.append(dst_free[:n])
+            dst_free = dst_free[n:]
+        wl = W.Workload(f"shared_prefix_bs{dst_bs}", 4100 + dst_bs, src_spec, dst_spec, prompts, src_tables, dst_tables)
+        say("case", wl.name)
+        src, dst, gs, gd = host_sides(wl)
+        toks = tokens(wl)
+        reqs = oracle_requests(wl, toks)
+        plan = kvx.kvx_plan(gs.pool, gd.pool, toks, wl.src_tables, wl.dst_tables)
+        op = O.make_plan(src.geom, dst.geom, reqs)
+        exp = dst.copy()
+        for l in range(2):
+            kvx.kvx_copy_heads(plan, l, 2, 0, 2)
+            O.copy_heads(src, exp, op, reqs, l, 2, 0, 2)
+        torch.cuda.synchronize()
+        assert np.array_equal(gd.kv.cpu().numpy(), exp.kv), wl.name
+        if exp.scales is not None:
+            assert np.array_equal(dev_scales(gd), exp.scales), wl.name
+        plan.close()
+
 def test_tiny_push_golden():
     """tiny_push end to end, also against the oracle's stored digests."""
     import hashlib
