@@ -61,13 +61,18 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+# The dominant kernel of each workload's bench line, as named in profiles/.
+COUNTER_KERNEL = {"tp4_share": "heads_kernel"}
+
+
 def counter_traffic(workload: str):
     """HBM bytes per launch of the dominant kernel from the committed
     rocprofv3 --pmc summary (FETCH_SIZE and WRITE_SIZE passes, each scaled by
     the counter's reading for a plain copy of known size); None when there is
     no summary or the kernel sources changed since it was taken."""
     from decode_kv_cache_amd.profiling import kernel_source_digest
-    path = os.path.join(PROFILES, f"push_kernel_{workload}_pmc.txt")
+    kernel = COUNTER_KERNEL.get(workload, "push_kernel")
+    path = os.path.join(PROFILES, f"{kernel}_{workload}_pmc.txt")
     if not os.path.exists(path):
         return None
     kv = {}
@@ -494,20 +499,23 @@ def two_stream_rate(torch, kvx, plan, ready, side, L, steps, step_bytes):
     return step_bytes * steps / (a.elapsed_time(b) * 1e-3) / 1e9
 
 
-def counters_run(torch, kvx, plan, side, L, bytes_per_launch):
+def counters_run(torch, kvx, plan, side, L, bytes_per_launch, launch=None):
     """Kernels for a counter pass: kvxb_copy of CALIB_BYTES (known traffic:
-    CALIB_BYTES read + CALIB_BYTES written) three times, then two layerwise
-    push steps."""
+    CALIB_BYTES read + CALIB_BYTES written) three times, then two steps of
+    `launch(layer)` over every layer (default: the layerwise push)."""
     from decode_kv_cache_amd import bench_support as B
+    if launch is None:
+        def launch(l):
+            kvx.kvx_push_layer(plan, l, stream=side)
     buf = torch.empty(2 * CALIB_BYTES, dtype=torch.uint8, device="cuda")
     for _ in range(3):
         B.copy(buf[CALIB_BYTES:], buf[:CALIB_BYTES], CALIB_BYTES, stream=side)
     for _ in range(2):
         for l in range(L):
-            kvx.kvx_push_layer(plan, l, stream=side)
+            launch(l)
     torch.cuda.synchronize()
-    print(json.dumps({"counters_run": True, "calib_copy_bytes": CALIB_BYTES, "push_launches": 2 * L,
-                      "push_bytes_per_launch": bytes_per_launch}), flush=True)
+    print(json.dumps({"counters_run": True, "calib_copy_bytes": CALIB_BYTES, "launches": 2 * L,
+                      "bytes_per_launch": bytes_per_launch}), flush=True)
 
 
 def bench_batched(args, torch, kvx, S, W):
@@ -649,6 +657,11 @@ def bench_tp4(args, torch, kvx, S, W):
     def step():
         for l in range(L):
             kvx.kvx_copy_heads(plan, l, rank * nh, 0, nh, stream=side)
+    if args.counters:
+        counters_run(torch, kvx, plan, side, L, per_layer,
+                     launch=lambda l: kvx.kvx_copy_heads(plan, l, rank * nh, 0, nh, stream=side))
+        plan.close()
+        return None
     for _ in range(args.warmup):
         step()
     with Timer(torch, side) as t:
@@ -935,8 +948,9 @@ def main():
           "tp4_share": bench_tp4, "multiturn_fp8": bench_multiturn, "pack_unpack": bench_pack,
           "dsr1_mla_push": bench_hybrid, "gptoss_swa_push": bench_hybrid,
           "qwen3next_state_push": bench_hybrid}[args.workload]
-    if args.counters and fn not in (bench_push, bench_batched):
-        print("bench.py: --counters is for the qwen32b_push, tiny_push and batched_push workloads", file=sys.stderr)
+    if args.counters and fn not in (bench_push, bench_batched, bench_tp4):
+        print("bench.py: --counters is for the qwen32b_push, tiny_push, batched_push and tp4_share workloads",
+              file=sys.stderr)
         sys.exit(2)
     r = fn(args, torch, kvx, S, W)
     if r is None:

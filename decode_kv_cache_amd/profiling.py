@@ -25,6 +25,8 @@ from collections import defaultdict
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 PUSH_KERNEL = "kvx::copy_kernel<0, "   # any launch shape of the push mode
+HEADS_KERNEL = "kvx::heads_kernel"
+KERNELS = {"push": PUSH_KERNEL, "heads": HEADS_KERNEL}
 CALIB_KERNEL = "copy_kernel(unsigned int __vector(4)*"   # kvxb_copy in libkvx_bench.so
 CALIB_BYTES = 1 << 30
 
@@ -91,18 +93,19 @@ def _avg_for(per, key):
     return sum(vals) / len(vals), len(vals)
 
 
-def pmc_summary(fetch_dir: str, write_dir: str, workload: str, push_bytes: int, cmd_f: str, cmd_w: str) -> str:
+def pmc_summary(fetch_dir: str, write_dir: str, workload: str, push_bytes: int, cmd_f: str, cmd_w: str,
+                kernel: str = "push") -> str:
     f, w = counters(fetch_dir), counters(write_dir)
     cf, ncf = _avg_for(f, CALIB_KERNEL)
     cw, ncw = _avg_for(w, CALIB_KERNEL)
-    pf, npf = _avg_for(f, PUSH_KERNEL)
-    pw, npw = _avg_for(w, PUSH_KERNEL)
+    pf, npf = _avg_for(f, KERNELS[kernel])
+    pw, npw = _avg_for(w, KERNELS[kernel])
     ff = CALIB_BYTES / (cf * 1024)
     fw = CALIB_BYTES / (cw * 1024)
     rd = pf * 1024 * ff
     wr = pw * 1024 * fw
     lines = [
-        f"# push kernel HBM traffic, workload {workload}: rocprofv3 --pmc FETCH_SIZE, then --pmc WRITE_SIZE",
+        f"# {kernel} kernel HBM traffic, workload {workload}: rocprofv3 --pmc FETCH_SIZE, then --pmc WRITE_SIZE",
         f"command_fetch: {cmd_f}",
         f"command_write: {cmd_w}",
         f"kernel_source_sha256_16: {kernel_source_digest()}",
@@ -111,8 +114,8 @@ def pmc_summary(fetch_dir: str, write_dir: str, workload: str, push_bytes: int, 
         f"calib_write_kib_per_dispatch: {cw:.1f}  (dispatches: {ncw})",
         f"fetch_factor: {ff:.5f}",
         f"write_factor: {fw:.5f}",
-        f"push_fetch_kib_per_dispatch: {pf:.1f}  (dispatches: {npf})",
-        f"push_write_kib_per_dispatch: {pw:.1f}  (dispatches: {npw})",
+        f"kernel_fetch_kib_per_dispatch: {pf:.1f}  (dispatches: {npf})",
+        f"kernel_write_kib_per_dispatch: {pw:.1f}  (dispatches: {npw})",
         f"calibrated_read_bytes_per_launch: {rd:.0f}",
         f"calibrated_write_bytes_per_launch: {wr:.0f}",
         f"calibrated_hbm_bytes_per_launch: {rd + wr:.0f}",
@@ -137,11 +140,13 @@ def main():
     p.add_argument("--push-bytes", type=int, required=True)
     p.add_argument("--command-fetch", required=True)
     p.add_argument("--command-write", required=True)
+    p.add_argument("--kernel", choices=sorted(KERNELS), default="push")
     a = ap.parse_args()
     if a.what == "trace":
         text = trace_summary(a.dir, a.command)
     else:
-        text = pmc_summary(a.fetch_dir, a.write_dir, a.workload, a.push_bytes, a.command_fetch, a.command_write)
+        text = pmc_summary(a.fetch_dir, a.write_dir, a.workload, a.push_bytes, a.command_fetch, a.command_write,
+                           a.kernel)
     with open(a.out, "w") as fh:
         fh.write(text)
     print(text)
