@@ -727,6 +727,13 @@ def bench_multiturn(args, torch, kvx, S, W):
         for _, p in plans:
             for l in range(L):
                 kvx.kvx_push_layer(p, l, stream=side)
+    if args.counters:   # every (turn, layer) launch of a step; bytes are the average per launch
+        n = len(plans) * L
+        counters_run(torch, kvx, None, side, n, step_bytes // n,
+                     launch=lambda i: kvx.kvx_push_layer(plans[i // L][1], i % L, stream=side))
+        for _, p in plans:
+            p.close()
+        return None
     for _ in range(args.warmup):
         step()
     with Timer(torch, side) as t:
@@ -948,9 +955,9 @@ def main():
           "tp4_share": bench_tp4, "multiturn_fp8": bench_multiturn, "pack_unpack": bench_pack,
           "dsr1_mla_push": bench_hybrid, "gptoss_swa_push": bench_hybrid,
           "qwen3next_state_push": bench_hybrid}[args.workload]
-    if args.counters and fn not in (bench_push, bench_batched, bench_tp4):
-        print("bench.py: --counters is for the qwen32b_push, tiny_push, batched_push and tp4_share workloads",
-              file=sys.stderr)
+    if args.counters and fn not in (bench_push, bench_batched, bench_tp4, bench_multiturn):
+        print("bench.py: --counters is for the qwen32b_push, tiny_push, batched_push, tp4_share and multiturn_fp8 "
+              "workloads", file=sys.stderr)
         sys.exit(2)
     r = fn(args, torch, kvx, S, W)
     if r is None:
