@@ -199,9 +199,24 @@ def roofline(bytes_per_launch: int, avg_us: float, kernel: str, workload: str, e
 # ---------------------------------------------------------------------------
 # workloads
 # ---------------------------------------------------------------------------
+def workload(W, name: str, args):
+    """The named workload's generator with the command line's overrides
+    (--seed for any workload, --tp-rank for tp4_share, --phys-layers for the
+    batched_push geometry)."""
+    ctor = {**W.WORKLOADS, **W.HYBRID_WORKLOADS}[name]
+    kw = {}
+    if args.seed is not None:
+        kw["seed"] = args.seed
+    if name == "tp4_share" and args.tp_rank is not None:
+        kw["tp_rank"] = args.tp_rank
+    if name == "batched_push" and args.phys_layers is not None:
+        kw["phys_layers"] = args.phys_layers
+    return ctor(**kw)
+
+
 def bench_push(args, torch, kvx, S, W):
     """qwen32b_push (default) and tiny_push: the layerwise push."""
-    wl = W.WORKLOADS[args.workload]()
+    wl = workload(W, args.workload, args)
     gs, gd = S.device_side(wl.src, wl.seed, 1), S.device_side(wl.dst, wl.seed, 2)
     tokens = [kvx.kvx_tokens_to_move(p, 0) for p in wl.prompt_lens]
     side = torch.cuda.Stream()
@@ -355,7 +370,7 @@ def bench_push(args, torch, kvx, S, W):
 def bench_hybrid(args, torch, kvx, S, W):
     """Layer groups of other shapes (MLA, sliding window, state slots): one
     step pushes every model layer, in model order, from its group's plan."""
-    wl = W.HYBRID_WORKLOADS[args.workload]()
+    wl = workload(W, args.workload, args)
     tokens = [kvx.kvx_tokens_to_move(p, 0) for p in wl.prompt_lens]
     side = torch.cuda.Stream()
     compute = torch.cuda.current_stream()
@@ -524,7 +539,7 @@ def bench_batched(args, torch, kvx, S, W):
     per CU so that push workgroups co-reside; it writes a canary into layer l's
     planned source blocks as its last act, so the push must see it)."""
     from decode_kv_cache_amd import bench_support as B
-    wl = W.batched_push()
+    wl = workload(W, "batched_push", args)
     gs, gd = S.device_side(wl.src, wl.seed, 1), S.device_side(wl.dst, wl.seed, 2)
     tokens = [kvx.kvx_tokens_to_move(p, 0) for p in wl.prompt_lens]
     side = torch.cuda.Stream()
@@ -641,7 +656,7 @@ def bench_batched(args, torch, kvx, S, W):
 
 def bench_tp4(args, torch, kvx, S, W):
     """tp4_share: per layer, TP4 rank 0's 2-head slice NHD -> HND."""
-    wl = W.tp4_share()
+    wl = workload(W, "tp4_share", args)
     gs, gd = S.device_side(wl.src, wl.seed, 1), S.device_side(wl.dst, wl.seed, 2)
     digest = inputs_digest(wl.src_tables + wl.dst_tables, [gs, gd], wl.prompt_lens)
     tokens = [kvx.kvx_tokens_to_move(p, 0) for p in wl.prompt_lens]
@@ -704,7 +719,7 @@ def bench_multiturn(args, torch, kvx, S, W):
     """multiturn_fp8: turns 2..8, each copies every session's retained prefix
     (2048 (t-1) tokens, reused because it reaches the 512-token threshold)
     from the decode pool back to the prefill pool, layer by layer."""
-    wl = W.multiturn_fp8()
+    wl = workload(W, "multiturn_fp8", args)
     ex = wl.extra
     dec, pre = S.device_side(wl.src, wl.seed, 1), S.device_side(wl.dst, wl.seed, 2)
     digest = inputs_digest(list(ex["decode_tables"]) + [t for k in sorted(ex["prefill_tables"])
@@ -780,7 +795,7 @@ def bench_multiturn(args, torch, kvx, S, W):
 def bench_pack(args, torch, kvx, S, W):
     """pack_unpack: the default workload's 64 layers gathered into a staging
     buffer and scattered from it into the consumer pool."""
-    wl = W.qwen32b_push()
+    wl = workload(W, "qwen32b_push", args)
     gs, gd = S.device_side(wl.src, wl.seed, 1), S.device_side(wl.dst, wl.seed, 2)
     digest = inputs_digest(wl.src_tables + wl.dst_tables, [gs, gd], wl.prompt_lens)
     tokens = [kvx.kvx_tokens_to_move(p, 0) for p in wl.prompt_lens]
@@ -840,7 +855,7 @@ def bench_xfer(args, torch, kvx, S, W):
     event; seal; poll until every request is done.  Compared with the same
     bytes moved by one multi-request plan per layer."""
     from decode_kv_cache_amd import bench_support as B
-    wl = W.batched_push()
+    wl = workload(W, "batched_push", args)
     gs, gd = S.device_side(wl.src, wl.seed, 1), S.device_side(wl.dst, wl.seed, 2)
     digest = inputs_digest(wl.src_tables + wl.dst_tables, [gs, gd], wl.prompt_lens)
     tokens = [kvx.kvx_tokens_to_move(p, 0) for p in wl.prompt_lens]
@@ -933,7 +948,14 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--counters", action="store_true",
                     help="short run for rocprofv3 --pmc: a 1 GiB plain copy (calibration) x3, then 2 steps")
+    ap.add_argument("--seed", type=int, default=None, help="workload seed (default: the workload's own)")
+    ap.add_argument("--tp-rank", type=int, default=None, choices=range(4), help="tp4_share: the TP4 rank timed")
+    ap.add_argument("--phys-layers", type=int, default=None,
+                    help="batched_push geometry: physical layer slabs behind the 64 layers (1..24, default 16)")
     args = ap.parse_args()
+    if args.phys_layers is not None and not 1 <= args.phys_layers <= 24:
+        print("bench.py: --phys-layers must be in 1..24 (each slab is 8 GiB over both pools)", file=sys.stderr)
+        sys.exit(2)
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
               f"(the transfer shards per request, layer and head slice; see the design notes)", file=sys.stderr)
