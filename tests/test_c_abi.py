@@ -4,7 +4,8 @@ libkvx.so check cases worked by hand (host-only: no device memory is
 touched): tests/c_abi/plan_from_c.c plans a transfer and checks its runs,
 triples, byte counts and error classes; tests/c_abi/xfer_from_c.c drives
 the transfer state machine through prefill-first deferral, a failed write
-with its recompute list, and a deferral timeout."""
+with its recompute list, and a deferral timeout.  On a GPU,
+tests/c_abi/push_from_c.c runs the device calls from C."""
 import os
 import shutil
 import subprocess
@@ -36,4 +37,22 @@ def test_c_program(prog, tmp_path):
                                           f"-Wl,-rpath,{PKG}", "-o", exe], capture_output=True, text=True)
     assert r.returncode == 0, r.stderr
     r = subprocess.run([exe], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 0 and r.stdout.strip() == "ok", r.stdout + r.stderr
+
+
+@pytest.mark.gpu
+def test_device_calls_from_c(tmp_path):
+    """tests/c_abi/push_from_c.c: device pools allocated from C, then
+    kvx_push_layer, kvx_pack + kvx_unpack and kvx_push_many, each checked
+    byte for byte against the per-token definition written in the program."""
+    lib = os.path.join(PKG, "libkvx.so")
+    assert os.path.exists(lib), "build libkvx.so first (python -m decode_kv_cache_amd.build)"
+    rocm_lib = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "lib")
+    exe = str(tmp_path / "push_from_c")
+    r = subprocess.run(["gcc"] + FLAGS + [os.path.join(ROOT, "tests", "c_abi", "push_from_c.c"), f"-L{PKG}", "-lkvx",
+                                          f"-L{rocm_lib}", "-lamdhip64", f"-Wl,-rpath,{PKG}",
+                                          f"-Wl,-rpath,{rocm_lib}", "-o", exe], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    print("running", exe, flush=True)
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=120)
     assert r.returncode == 0 and r.stdout.strip() == "ok", r.stdout + r.stderr
