@@ -70,8 +70,9 @@ struct kvx_xfer_s {
   kvx_xfer_config cfg{};
   hipStream_t stream = nullptr;
   bool host_only = false;
+  bool keep_log = false;  // KVX_XFER_LOG
   std::map<uint64_t, Req> reqs;
-  std::vector<WriteRef> log;
+  std::vector<WriteRef> log;  // issued writes, in order (KVX_XFER_LOG only)
   std::vector<Sig> sigs;
   std::vector<int32_t> free_sigs;
   std::vector<WriteRef> unmarked;                                  // issued since the last mark
@@ -210,7 +211,7 @@ int issue(kvx_xfer* x, const std::vector<Item>& items, double now) {
   for (const Item& it : items) {
     it.ly->st = kIssued;
     it.ly->issued_at = now;
-    x->log.push_back(WriteRef{it.id, it.r->attempt, it.layer});
+    if (x->keep_log) x->log.push_back(WriteRef{it.id, it.r->attempt, it.layer});
   }
   return KVX_OK;
 }
@@ -319,11 +320,13 @@ int kvx_xfer_create(const kvx_pool* producer, const kvx_xfer_config* cfg, hipStr
   if (!x) return fail(KVX_E_NOMEM, "kvx_xfer_create: out of host memory");
   x->producer = producer;
   x->cfg = cfg ? *cfg : kvx_xfer_config{60.0, 30.0, 0u};
-  if (x->cfg.flags & ~KVX_XFER_HOST_ONLY) {
+  if (x->cfg.flags & ~(KVX_XFER_HOST_ONLY | KVX_XFER_LOG)) {
+    const uint32_t f = x->cfg.flags;
     delete x;
-    return fail(KVX_E_INVAL, "kvx_xfer_create: unknown flags 0x%x", x->cfg.flags);
+    return fail(KVX_E_INVAL, "kvx_xfer_create: unknown flags 0x%x", f);
   }
   x->host_only = (x->cfg.flags & KVX_XFER_HOST_ONLY) != 0;
+  x->keep_log = (x->cfg.flags & KVX_XFER_LOG) != 0;
   x->stream = stream;
   *out = x;
   return KVX_OK;
@@ -534,6 +537,7 @@ int kvx_xfer_issued(const kvx_xfer* x, int64_t first, uint64_t* reqs, uint32_t* 
                     int64_t cap, int64_t* n) {
   if (!x || !n || first < 0 || (cap > 0 && (!reqs || !attempts || !layers)))
     return fail(KVX_E_INVAL, "kvx_xfer_issued: bad argument");
+  if (!x->keep_log) return fail(KVX_E_INVAL, "kvx_xfer_issued: created without KVX_XFER_LOG");
   std::lock_guard<std::mutex> lk(x->mu);
   int64_t k = 0;
   for (int64_t i = first; i < int64_t(x->log.size()) && k < cap; ++i, ++k) {

@@ -99,6 +99,7 @@ _SIGS.update({
 EXPORTED = tuple(_SIGS)
 KVX_REQ_PENDING, KVX_REQ_DONE, KVX_REQ_FAILED, KVX_REQ_EXPIRED = range(4)
 KVX_XFER_HOST_ONLY = 1
+KVX_XFER_LOG = 2
 
 
 class kvx_xfer_config(C.Structure):
@@ -390,8 +391,10 @@ class Xfer:
     Methods return the C call's `accepted` flag where it has one."""
 
     def __init__(self, producer: Pool, *, defer_timeout: float = 60.0, transfer_timeout: float = 30.0,
-                 host_only: bool = False, stream=None):
-        cfg = kvx_xfer_config(defer_timeout, transfer_timeout, KVX_XFER_HOST_ONLY if host_only else 0)
+                 host_only: bool = False, log: bool = False, stream=None):
+        """``log``: KVX_XFER_LOG (keep the issued-write log that issued() reads)."""
+        cfg = kvx_xfer_config(defer_timeout, transfer_timeout,
+                              (KVX_XFER_HOST_ONLY if host_only else 0) | (KVX_XFER_LOG if log else 0))
         h = C.c_void_p()
         st = None if host_only else _stream(stream)
         _check("kvx_xfer_create", lib().kvx_xfer_create(producer.handle, C.byref(cfg), st, C.byref(h)))

@@ -57,6 +57,9 @@ enum { KVX_REQ_PENDING = 0, KVX_REQ_DONE = 1, KVX_REQ_FAILED = 2, KVX_REQ_EXPIRE
 /* kvx_xfer_config.flags */
 #define KVX_XFER_HOST_ONLY 1u /* plans are host-only and nothing is launched; issued writes
                                  finish only through kvx_xfer_complete (CPU tests) */
+#define KVX_XFER_LOG 2u       /* keep the log of issued writes that kvx_xfer_issued reads (tests,
+                                 tracing); it grows with every write.  Without it nothing is
+                                 logged, and memory is bounded by the requests held. */
 
 typedef struct kvx_xfer_config {
   double defer_timeout_s;    /* pages' default: 60 */
@@ -132,7 +135,8 @@ int kvx_xfer_pop_finished(kvx_xfer* x, uint64_t* reqs, uint32_t* attempts, int32
 int kvx_xfer_recompute_blocks(const kvx_xfer* x, uint64_t req, int32_t* out, int64_t cap, int64_t* n);
 
 /* Issued writes in issue order, from index `first`: (request, attempt,
- * layer).  *n receives how many were written (at most cap). */
+ * layer).  *n receives how many were written (at most cap).  Needs
+ * KVX_XFER_LOG at creation; without it, KVX_E_INVAL. */
 int kvx_xfer_issued(const kvx_xfer* x, int64_t first, uint64_t* reqs, uint32_t* attempts, int32_t* layers,
                     int64_t cap, int64_t* n);
 

@@ -72,7 +72,7 @@ int main(void) {
   memset(&cfg, 0, sizeof cfg);
   cfg.defer_timeout_s = 60.0;
   cfg.transfer_timeout_s = 30.0;
-  cfg.flags = KVX_XFER_HOST_ONLY;
+  cfg.flags = KVX_XFER_HOST_ONLY | KVX_XFER_LOG;
   CHECK(kvx_xfer_create(prod, &cfg, NULL, &x) == KVX_OK);
 
   { /* 1. prefill first */

@@ -35,7 +35,7 @@ def test_xfer_drives_pushes():
     dst0 = gd.kv.cpu().numpy().copy()
     side = torch.cuda.Stream()
     compute = torch.cuda.current_stream()
-    x = kvx.Xfer(gs.pool, stream=side)
+    x = kvx.Xfer(gs.pool, log=True, stream=side)
     toks = [kvx.kvx_tokens_to_move(p, 0) for p in plen]
     bb = 16 * 8 * 128 * 2
     sink = torch.empty(256 * 256, dtype=torch.float32, device="cuda")

@@ -18,7 +18,7 @@ def run_sequence(seed, steps=300, ids=(1, 2, 3, 4, 5)):
     rng = np.random.Generator(np.random.PCG64(seed))
     prod, cons = fake_pool(SPEC, 0), fake_pool(SPEC, 1)
     defer_t, xfer_t = float(rng.choice([5.0, 20.0])), float(rng.choice([3.0, 10.0]))
-    nat = kvx.Xfer(prod, defer_timeout=defer_t, transfer_timeout=xfer_t, host_only=True)
+    nat = kvx.Xfer(prod, defer_timeout=defer_t, transfer_timeout=xfer_t, host_only=True, log=True)
     mod = X.XferModel(defer_timeout=defer_t, transfer_timeout=xfer_t)
     now = 0.0
     seen = set()
@@ -120,4 +120,12 @@ def test_native_errors():
     assert x.status(1) == (0, kvx.KVX_REQ_FAILED)
     with pytest.raises(kvx.KvxError):
         x.forget(2)
+    with pytest.raises(kvx.KvxError) as e:   # no issue log without KVX_XFER_LOG
+        x.issued()
+    assert e.value.code == kvx.KVX_E_INVAL
     x.close()
+    import ctypes
+    cfg = kvx.kvx_xfer_config(60.0, 30.0, kvx.KVX_XFER_HOST_ONLY | 4)
+    h = ctypes.c_void_p()
+    assert kvx.lib().kvx_xfer_create(prod.handle, ctypes.byref(cfg), None, ctypes.byref(h)) == kvx.KVX_E_INVAL
+    assert b"unknown flags 0x5" in kvx.lib().kvx_last_error()
