@@ -134,3 +134,56 @@ def test_plan_on_capturing_stream_is_rejected():
     O.push(src, exp, op, layers=[1])
     assert np.array_equal(gd.kv.cpu().numpy(), exp.kv)
     plan.close()
+
+
+def test_push_many_and_staging_replayed_from_graph():
+    """kvx_push_many over every layer and kvx_pack + kvx_unpack over every
+    layer, captured once and replayed with the source rewritten eagerly
+    between replays.  The plan takes the 16 KiB one-wave shape, and four
+    layers of it exceed one round, so the batched launches stream its
+    pieces as 4 KiB chunks from the destination-ordered copy."""
+    spec = W.PoolSpec(4, 400, 16, 8, 128, W.BF16)
+    rng = np.random.Generator(np.random.PCG64(9502))
+    need = [W.alloc_blocks(3000, 16)]
+    wl = W.Workload("graph_many", 9502, spec, spec, [3000],
+                    W.split_tables(W.geometric_run_table(rng, 400, 12.0), need),
+                    W.split_tables(W.geometric_run_table(rng, 400, 12.0), need))
+    src, dst = P.pools(O, wl)
+    gs = S.device_side(wl.src, wl.seed, 1, values=(src.kv, src.scales))
+    gd = S.device_side(wl.dst, wl.seed, 2, values=(dst.kv, dst.scales))
+    gd2 = S.device_side(wl.dst, wl.seed, 2, values=(dst.kv, dst.scales))
+    toks = [kvx.kvx_tokens_to_move(p, 0) for p in wl.prompt_lens]
+    side = torch.cuda.Stream()
+    plan = kvx.kvx_plan(gs.pool, gd.pool, toks, wl.src_tables, wl.dst_tables, stream=side)
+    plan2 = kvx.kvx_plan(gs.pool, gd2.pool, toks, wl.src_tables, wl.dst_tables, stream=side)
+    shape = plan.launch_shape()
+    L = spec.num_layers
+    assert (shape["lanes"], shape["vectors"]) == (64, 16), shape
+    # 32 KiB units over all four layers beyond one round (1312): the batched launches stream
+    assert L * shape["pieces"] * shape["piece_bytes"] // 32768 > 1312, shape
+    op = O.make_plan(src.geom, dst.geom, [O.Request(n, s, d) for n, s, d in zip(toks, wl.src_tables, wl.dst_tables)])
+    stg = torch.empty(kvx.kvx_staging_bytes(plan2, 0, L), dtype=torch.uint8, device="cuda")
+    kvx.kvx_plan_wait(plan)
+    kvx.kvx_plan_wait(plan2)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        cur = torch.cuda.current_stream()
+        kvx.kvx_push_many([plan] * L, list(range(L)), stream=cur)
+        kvx.kvx_pack(plan2, 0, L, stg, stream=cur)
+        kvx.kvx_unpack(plan2, 0, L, stg, stream=cur)
+    exp = dst.copy()
+    rng = np.random.Generator(np.random.PCG64(4))
+    for rep in range(3):
+        new = rng.integers(0, 256, size=src.kv.shape, dtype=np.uint8)
+        gs.kv.copy_(torch.from_numpy(new).cuda())        # eager work between replays
+        src.kv[...] = new
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        O.push(src, exp, op)
+        assert np.array_equal(gd.kv.cpu().numpy(), exp.kv), ("push_many", rep)
+        assert np.array_equal(stg.cpu().numpy(), O.pack(src, op, 0, L)), ("pack", rep)
+        assert np.array_equal(gd2.kv.cpu().numpy(), exp.kv), ("unpack", rep)
+    plan.close()
+    plan2.close()
