@@ -55,7 +55,9 @@ enum {
   KVX_E_RANGE = 2,       /* block ID outside the pool, layer or head range out of bounds */
   KVX_E_DUPDST = 3,      /* a destination block is used twice within one plan */
   KVX_E_MISMATCH = 4,    /* the two pools' geometries are incompatible for the call */
-  KVX_E_UNSUPPORTED = 5, /* alignment: base not 16-B aligned, row bytes not a multiple of 16 */
+  KVX_E_UNSUPPORTED = 5, /* alignment or a geometry limit: a base not 16-B aligned, row bytes not a
+                            multiple of 16, block_size above 32768, a block of 2^31 B or more,
+                            per-block scales with different block sizes per side */
   KVX_E_NOMEM = 6,       /* host or device allocation failed */
   KVX_E_HIP = 7          /* a HIP runtime or launch error; see kvx_last_error() */
 };
@@ -96,8 +98,9 @@ enum {
  *     A transfer then skips the blocks the receiving side's next query no
  *     longer sees (see kvx_plan).
  * Requirements: all counts >= 1; elem_bytes in {1, 2, 4}; head_dim *
- * elem_bytes a multiple of 16 and block_size <= 32768 (KVX_E_UNSUPPORTED
- * otherwise); sliding_window >= 0.  Zero-initialise the struct so that
+ * elem_bytes a multiple of 16, block_size <= 32768 and block_size *
+ * num_heads * head_dim * elem_bytes < 2^31 (KVX_E_UNSUPPORTED otherwise);
+ * sliding_window >= 0.  Zero-initialise the struct so that
  * fields added by later versions read as 0.
  * The library copies the descriptor; the arrays may be freed after the call.
  */
@@ -216,7 +219,10 @@ void kvx_pool_destroy(kvx_pool* pool);
  * slot_bytes (KVX_E_MISMATCH).  src == dst is KVX_E_INVAL.
  * Unless KVX_PLAN_HOST_ONLY is set the device work list is uploaded on
  * `upload_stream` (NULL = the null stream); later device calls on any stream
- * are ordered after the upload.
+ * are ordered after the upload.  The plan owns that one device buffer
+ * (hipMalloc at build, hipFree at kvx_plan_destroy): 32 B per piece of at
+ * most 32 KiB (twice for a plan in a one-wave launch shape, whose batched
+ * launches read a destination-ordered copy) plus 16 B per planned block.
  * Validation order per request: token count, list lengths, source IDs, then
  * destination IDs.  Errors: INVAL (also: upload_stream is capturing a
  * graph), RANGE (ID outside its pool), DUPDST (a dst ID used twice in the
@@ -267,7 +273,9 @@ int kvx_plan_launch_shape(const kvx_plan_t* plan, kvx_launch_shape* out);
  * Errors: INVAL (null plan), HIP. */
 int kvx_plan_wait(const kvx_plan_t* plan);
 
-/* Bytes one layer's push reads and writes (every region's payload plus scales). */
+/* Bytes one layer's push reads and writes (every region's payload plus
+ * scales), into *read_bytes and *write_bytes.  Errors: INVAL (null),
+ * MISMATCH (pools differ in head count or layout: no push). */
 int kvx_plan_bytes(const kvx_plan_t* plan, int64_t* read_bytes, int64_t* write_bytes);
 
 /* Free a plan.  Device calls already enqueued with it may still be running
@@ -327,7 +335,8 @@ int kvx_push_many(const kvx_plan_t* const* plans, const int32_t* layers, int32_t
  * regions of (payload + scale segment), where payload = sum of the region's
  * triple lengths and the scale segment is 4 bytes per planned block rounded
  * up to 16 (0 without scales).
- * Errors: RANGE (0 <= l0 <= l1 <= num_layers violated), MISMATCH. */
+ * Errors: INVAL (null), RANGE (0 <= l0 <= l1 <= num_layers violated),
+ * MISMATCH (pools differ in head count or layout). */
 int kvx_staging_bytes(const kvx_plan_t* plan, int32_t l0, int32_t l1, int64_t* bytes);
 
 /*
