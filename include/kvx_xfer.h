@@ -38,9 +38,16 @@
  * in seconds on a clock of the caller's choice.
  *
  * Threading: calls on one kvx_xfer are serialized internally (a mutex).
- * Return values follow kvx.h (KVX_OK or KVX_E_*).  `accepted` outputs
+ * Return values follow kvx.h (KVX_OK or KVX_E_*).  Unless a call lists
+ * more: INVAL for a null handle or argument, HIP for a runtime failure
+ * (device mode), NOMEM when host memory runs out.  `accepted` outputs
  * (nullable) report whether the message changed the state: 1 = applied,
  * 0 = ignored (stale attempt, finished request, duplicate).
+ *
+ * Memory: a request's plan (and its device work list) is released when the
+ * request finishes, once the writes already enqueued with it are done.  Its
+ * record (state, layer states, recompute list) stays for queries until
+ * kvx_xfer_forget.  The issued-write log is kept only with KVX_XFER_LOG.
  */
 #ifndef KVX_XFER_H
 #define KVX_XFER_H
