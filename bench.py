@@ -957,7 +957,7 @@ def main():
         print("bench.py: --phys-layers must be in 1..24 (each slab is 8 GiB over both pools)", file=sys.stderr)
         sys.exit(2)
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
+        print(f"bench.py: libkvx runs on one GPU; --gpus {args.gpus} is not supported "
               f"(the transfer shards per request, layer and head slice; see the design notes)", file=sys.stderr)
         sys.exit(2)
 
