@@ -4,7 +4,8 @@ libkvx.so check cases worked by hand (host-only: no device memory is
 touched): tests/c_abi/plan_from_c.c plans a transfer and checks its runs,
 triples, byte counts and error classes; tests/c_abi/xfer_from_c.c drives
 the transfer state machine through prefill-first deferral, a failed write
-with its recompute list, and a deferral timeout.  On a GPU,
+with its recompute list, and a deferral timeout; tests/c_abi/xfer_threads_from_c.c
+shares one state machine between eight threads.  On a GPU,
 tests/c_abi/push_from_c.c runs the device calls from C."""
 import os
 import shutil
@@ -28,13 +29,13 @@ def test_headers_compile_as_c99():
         assert r.returncode == 0, r.stderr
 
 
-@pytest.mark.parametrize("prog", ["plan_from_c", "xfer_from_c"])
+@pytest.mark.parametrize("prog", ["plan_from_c", "xfer_from_c", "xfer_threads_from_c"])
 def test_c_program(prog, tmp_path):
     lib = os.path.join(PKG, "libkvx.so")
     assert os.path.exists(lib), "build libkvx.so first (python -m decode_kv_cache_amd.build)"
     exe = str(tmp_path / prog)
     r = subprocess.run(["gcc"] + FLAGS + [os.path.join(ROOT, "tests", "c_abi", prog + ".c"), f"-L{PKG}", "-lkvx",
-                                          f"-Wl,-rpath,{PKG}", "-o", exe], capture_output=True, text=True)
+                                          f"-Wl,-rpath,{PKG}", "-lpthread", "-o", exe], capture_output=True, text=True)
     assert r.returncode == 0, r.stderr
     r = subprocess.run([exe], capture_output=True, text=True, timeout=60)
     assert r.returncode == 0 and r.stdout.strip() == "ok", r.stdout + r.stderr

@@ -129,3 +129,59 @@ def test_native_errors():
     h = ctypes.c_void_p()
     assert kvx.lib().kvx_xfer_create(prod.handle, ctypes.byref(cfg), None, ctypes.byref(h)) == kvx.KVX_E_INVAL
     assert b"unknown flags 0x5" in kvx.lib().kvx_last_error()
+
+
+def test_threads_share_one_instance():
+    """Calls on one kvx_xfer are serialized internally: eight threads drive
+    disjoint requests through registration, prefill, layer saves (half of
+    them deferred), seal and completion at once (ctypes releases the GIL
+    around each foreign call).  Every request ends DONE, every write is logged
+    exactly once, and each request's writes keep layer order in the log."""
+    import threading
+    prod, cons = fake_pool(SPEC, 0), fake_pool(SPEC, 1)
+    x = kvx.Xfer(prod, host_only=True, log=True)
+    T, PER, L = 8, 40, SPEC.num_layers
+    errors = []
+
+    def worker(t):
+        try:
+            for k in range(PER):
+                rid = t * 1000 + k
+                first = (lambda: x.register(rid, 0, cons, [3, 4], 0.0)) if k % 2 else \
+                        (lambda: x.prefill(rid, 0, 8, [1, 2], 0.0))
+                second = (lambda: x.prefill(rid, 0, 8, [1, 2], 0.0)) if k % 2 else \
+                         (lambda: x.register(rid, 0, cons, [3, 4], 0.0))
+                assert first()
+                for l in range(L // 2):
+                    assert x.save_layer(rid, 0, l, 0.0)         # deferred: one side unknown
+                assert second()                                 # both sides known: deferred writes go out
+                for l in range(L // 2, L):
+                    assert x.save_layer(rid, 0, l, 0.0)
+                assert x.seal(rid, 0)
+                for l in range(L):
+                    x.complete(rid, 0, l, True)
+                assert x.status(rid) == (0, kvx.KVX_REQ_DONE), rid
+        except Exception as e:   # reported by the main thread
+            errors.append((t, repr(e)))
+
+    threads = [threading.Thread(target=worker, args=(t,)) for t in range(T)]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join()
+    assert not errors, errors
+    log = x.issued()
+    assert len(log) == T * PER * L
+    assert len(set(log)) == len(log)
+    for t in range(T):
+        for k in range(PER):
+            rid = t * 1000 + k
+            assert [e[2] for e in log if e[0] == rid] == list(range(L)), rid
+    done = []
+    while True:
+        got = x.pop_finished()
+        if not got:
+            break
+        done += got
+    assert len(done) == T * PER and all(s == kvx.KVX_REQ_DONE for _, _, s in done)
+    x.close()
