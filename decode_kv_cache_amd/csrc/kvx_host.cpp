@@ -11,7 +11,11 @@
 #include <cstdint>
 #include <cstdio>
 #include <cstring>
+#include <iterator>
+#include <map>
+#include <mutex>
 #include <new>
+#include <vector>
 
 #include "kvx_internal.h"
 
@@ -89,13 +93,97 @@ int check_launch(const char* what) {
 
 static int64_t pad16(int64_t x) { return (x + 15) / 16 * 16; }
 
+// Work-list arena, one per device.  Chunks of at least 64 MiB come from
+// hipMalloc and stay mapped until the process ends; work lists are carved
+// from them first fit, and a freed range merges with free neighbours of the
+// same chunk.  Freeing never calls hipFree, which synchronizes the whole
+// device: a finished request's plan is released while other work runs
+// (kvx_xfer_poll).  Memory held is the peak of live work lists.
+class DescArena {
+ public:
+  int alloc(size_t n, void** out) {
+    std::lock_guard<std::mutex> lk(mu_);
+    for (auto it = free_.begin(); it != free_.end(); ++it) {
+      if (it->second.size < n) continue;
+      const uintptr_t a = it->first;
+      const Range r = it->second;
+      free_.erase(it);
+      if (r.size > n) free_.emplace(a + n, Range{r.size - n, r.chunk});
+      *out = reinterpret_cast<void*>(a);
+      return KVX_OK;
+    }
+    const size_t cs = std::max(kChunk, (n + kChunkAlign - 1) / kChunkAlign * kChunkAlign);
+    void* base = nullptr;
+    const hipError_t e = hipMalloc(&base, cs);
+    if (e != hipSuccess)
+      return e == hipErrorOutOfMemory ? fail(KVX_E_NOMEM, "kvx_plan: device work list (%zu B)", n)
+                                      : fail_hip(e, "hipMalloc(work-list chunk)");
+    const int id = int(chunks_.size());
+    chunks_.push_back({uintptr_t(base), cs});
+    if (cs > n) free_.emplace(uintptr_t(base) + n, Range{cs - n, id});
+    *out = base;
+    return KVX_OK;
+  }
+
+  void release(void* p, size_t n) {
+    std::lock_guard<std::mutex> lk(mu_);
+    const uintptr_t a = uintptr_t(p);
+    int id = -1;
+    for (size_t c = 0; c < chunks_.size(); ++c)
+      if (a >= chunks_[c].first && a < chunks_[c].first + chunks_[c].second) id = int(c);
+    if (id < 0) return;  // not from this arena
+    uintptr_t start = a;
+    auto next = free_.lower_bound(a);
+    if (next != free_.end() && next->first == a + n && next->second.chunk == id) {
+      n += next->second.size;
+      next = free_.erase(next);
+    }
+    if (next != free_.begin()) {
+      auto prev = std::prev(next);
+      if (prev->first + prev->second.size == a && prev->second.chunk == id) {
+        prev->second.size += n;
+        return;
+      }
+    }
+    free_.emplace(start, Range{n, id});
+  }
+
+ private:
+  struct Range {
+    size_t size;
+    int chunk;
+  };
+  static constexpr size_t kChunk = size_t(64) << 20;
+  static constexpr size_t kChunkAlign = size_t(2) << 20;
+  std::mutex mu_;
+  std::map<uintptr_t, Range> free_;                   // start address -> free range
+  std::vector<std::pair<uintptr_t, size_t>> chunks_;  // (base, bytes)
+};
+
+constexpr int kMaxDevices = 64;
+// Never destroyed: a plan may be freed while the process shuts down.
+static DescArena* const g_arena = new DescArena[kMaxDevices];
+
+int desc_alloc(size_t bytes, void** out, int* device) {
+  int dev = 0;
+  const hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail_hip(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(KVX_E_UNSUPPORTED, "kvx_plan: device %d beyond %d", dev, kMaxDevices);
+  *device = dev;
+  return g_arena[dev].alloc((bytes + 255) / 256 * 256, out);
+}
+
+void desc_free(void* p, size_t bytes, int device) {
+  if (p && device >= 0 && device < kMaxDevices) g_arena[device].release(p, (bytes + 255) / 256 * 256);
+}
+
 void plan_free_idle(kvx_plan_t* p) {
   if (!p) return;
   if (p->upload_ev) {
     (void)hipEventSynchronize(p->upload_ev);
     (void)hipEventDestroy(p->upload_ev);
   }
-  if (p->dev_buf) (void)hipFree(p->dev_buf);
+  desc_free(p->dev_buf, p->dev_bytes, p->device);
   delete p;
 }
 
@@ -385,12 +473,13 @@ int upload(kvx_plan_t* p, hipStream_t s) {
   const size_t sb = p->stream_pieces.size() * sizeof(Piece);
   const size_t bb = p->blocks.size() * sizeof(BlockPair);
   const size_t total = std::max<size_t>(pb + sb + bb, 256);
-  hipError_t e = hipMalloc(&p->dev_buf, total);
-  if (e != hipSuccess) {
+  int rc = desc_alloc(total, &p->dev_buf, &p->device);
+  if (rc != KVX_OK) {
     p->dev_buf = nullptr;
-    return e == hipErrorOutOfMemory ? fail(KVX_E_NOMEM, "kvx_plan: device descriptors (%zu B)", total)
-                                    : fail_hip(e, "hipMalloc(plan)");
+    return rc;
   }
+  p->dev_bytes = total;
+  hipError_t e;
   char* const buf = static_cast<char*>(p->dev_buf);
   p->d_pieces = reinterpret_cast<const Piece*>(buf);
   p->d_stream = sb ? reinterpret_cast<const Piece*>(buf + pb) : p->d_pieces;

@@ -125,7 +125,9 @@ struct kvx_plan_s {
   int64_t stg_layer() const { return nreg == 1 ? stg_region(0) : stg_region(0) + stg_region(1); }
 
   // device side
-  void* dev_buf = nullptr;
+  void* dev_buf = nullptr;   // from the work-list arena (desc_alloc)
+  size_t dev_bytes = 0;
+  int device = 0;
   const kvx::Piece* d_pieces = nullptr;
   const kvx::Piece* d_stream = nullptr;  // pieces in streaming order (d_pieces for streaming plans)
   const kvx::BlockPair* d_blocks = nullptr;
@@ -145,6 +147,13 @@ int wait_event(hipEvent_t ev, hipStream_t stream);
 int enqueue_waits(kvx_plan_t* plan, hipEvent_t ready, hipStream_t stream);
 // After a launch: turn a launch error into KVX_E_HIP.
 int check_launch(const char* what);
+
+// Device memory for plan work lists on the current device: `bytes` rounded
+// up to 256, from chunks the library keeps mapped (hipFree would
+// synchronize the whole device).  desc_free returns a range for reuse; the
+// caller guarantees no enqueued work still reads it.
+int desc_alloc(size_t bytes, void** out, int* device);
+void desc_free(void* p, size_t bytes, int device);
 
 // Free a plan whose enqueued work is known to have finished (no device
 // drain, unlike kvx_plan_destroy).

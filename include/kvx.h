@@ -219,10 +219,13 @@ void kvx_pool_destroy(kvx_pool* pool);
  * slot_bytes (KVX_E_MISMATCH).  src == dst is KVX_E_INVAL.
  * Unless KVX_PLAN_HOST_ONLY is set the device work list is uploaded on
  * `upload_stream` (NULL = the null stream); later device calls on any stream
- * are ordered after the upload.  The plan owns that one device buffer
- * (hipMalloc at build, hipFree at kvx_plan_destroy): 32 B per piece of at
- * most 32 KiB (twice for a plan in a one-wave launch shape, whose batched
- * launches read a destination-ordered copy) plus 16 B per planned block.
+ * are ordered after the upload.  The plan owns that one device buffer,
+ * carved from the library's work-list arena on the current device: 32 B per
+ * piece of at most 32 KiB (twice for a plan in a one-wave launch shape,
+ * whose batched launches read a destination-ordered copy) plus 16 B per
+ * planned block.  The arena takes chunks of at least 64 MiB from hipMalloc
+ * and keeps them for reuse until the process ends (hipFree would
+ * synchronize the whole device); it holds the peak of live work lists.
  * Validation order per request: token count, list lengths, source IDs, then
  * destination IDs.  Errors: INVAL (also: upload_stream is capturing a
  * graph), RANGE (ID outside its pool), DUPDST (a dst ID used twice in the

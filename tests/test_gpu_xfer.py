@@ -107,3 +107,42 @@ def test_xfer_reported_failure():
     x.forget(7)
     assert x.status(7) is None
     x.close()
+
+
+def test_poll_frees_plans_without_waiting_for_the_device():
+    """A finished request's plan is released inside kvx_xfer_poll once the
+    work enqueued with it is done.  Releasing it must not wait for unrelated
+    device work: a long compute kernel is still running on another stream
+    when that poll returns (hipFree would have waited for it)."""
+    spec = W.PoolSpec(2, 256, 16, 8, 128, W.BF16)
+    rng = np.random.Generator(np.random.PCG64(78))
+    need = [W.alloc_blocks(900, 16)]
+    st = W.split_tables(W.geometric_run_table(rng, 256, 3.0), need)
+    dt = W.split_tables(W.geometric_run_table(rng, 256, 3.0), need)
+    gs = S.device_side(spec, 6, 1)
+    gd = S.device_side(spec, 6, 2)
+    side = torch.cuda.Stream()
+    compute = torch.cuda.Stream()
+    x = kvx.Xfer(gs.pool, stream=side)
+    n = kvx.kvx_tokens_to_move(900, 0)
+    assert x.register(7, 0, gd.pool, dt[0], 0.0)
+    assert x.prefill(7, 0, n, st[0], 0.0)
+    for l in range(spec.num_layers):
+        assert x.save_layer(7, 0, l, 0.0)
+    assert x.seal(7, 0)
+    torch.cuda.synchronize()
+    x.poll(0.0)                  # a mark behind the writes
+    torch.cuda.synchronize()
+    x.poll(0.0)                  # the writes are seen done: DONE, its plan retired behind a new mark
+    assert x.status(7) == (0, kvx.KVX_REQ_DONE)
+    torch.cuda.synchronize()     # that mark has fired: the next poll releases the plan
+    sink = torch.empty(256 * 256, dtype=torch.float32, device="cuda")
+    B.layer_compute(sink, 100_000_000, 256, stream=compute)   # bounded: a fixed loop, tens of ms at least
+    busy = torch.cuda.Event()
+    busy.record(compute)
+    print("long compute kernel enqueued", flush=True)
+    x.poll(0.0)
+    assert not busy.query(), "kvx_xfer_poll waited for unrelated device work"
+    torch.cuda.synchronize()
+    assert x.pop_finished() == [(7, 0, kvx.KVX_REQ_DONE)]
+    x.close()
