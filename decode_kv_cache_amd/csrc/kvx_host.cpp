@@ -11,12 +11,10 @@
 #include <cstdint>
 #include <cstdio>
 #include <cstring>
-#include <iterator>
-#include <map>
-#include <mutex>
 #include <new>
 #include <vector>
 
+#include "kvx_arena.h"
 #include "kvx_internal.h"
 
 namespace kvx {
@@ -93,88 +91,40 @@ int check_launch(const char* what) {
 
 static int64_t pad16(int64_t x) { return (x + 15) / 16 * 16; }
 
-// Work-list arena, one per device.  Chunks of at least 64 MiB come from
-// hipMalloc and stay mapped until the process ends; work lists are carved
-// from them first fit, and a freed range merges with free neighbours of the
-// same chunk.  Freeing never calls hipFree, which synchronizes the whole
-// device: a finished request's plan is released while other work runs
-// (kvx_xfer_poll).  Memory held is the peak of live work lists.
-class DescArena {
- public:
-  int alloc(size_t n, void** out) {
-    std::lock_guard<std::mutex> lk(mu_);
-    for (auto it = free_.begin(); it != free_.end(); ++it) {
-      if (it->second.size < n) continue;
-      const uintptr_t a = it->first;
-      const Range r = it->second;
-      free_.erase(it);
-      if (r.size > n) free_.emplace(a + n, Range{r.size - n, r.chunk});
-      *out = reinterpret_cast<void*>(a);
-      return KVX_OK;
-    }
-    const size_t cs = std::max(kChunk, (n + kChunkAlign - 1) / kChunkAlign * kChunkAlign);
-    void* base = nullptr;
-    const hipError_t e = hipMalloc(&base, cs);
-    if (e != hipSuccess)
-      return e == hipErrorOutOfMemory ? fail(KVX_E_NOMEM, "kvx_plan: device work list (%zu B)", n)
-                                      : fail_hip(e, "hipMalloc(work-list chunk)");
-    const int id = int(chunks_.size());
-    chunks_.push_back({uintptr_t(base), cs});
-    if (cs > n) free_.emplace(uintptr_t(base) + n, Range{cs - n, id});
-    *out = base;
-    return KVX_OK;
-  }
-
-  void release(void* p, size_t n) {
-    std::lock_guard<std::mutex> lk(mu_);
-    const uintptr_t a = uintptr_t(p);
-    int id = -1;
-    for (size_t c = 0; c < chunks_.size(); ++c)
-      if (a >= chunks_[c].first && a < chunks_[c].first + chunks_[c].second) id = int(c);
-    if (id < 0) return;  // not from this arena
-    uintptr_t start = a;
-    auto next = free_.lower_bound(a);
-    if (next != free_.end() && next->first == a + n && next->second.chunk == id) {
-      n += next->second.size;
-      next = free_.erase(next);
-    }
-    if (next != free_.begin()) {
-      auto prev = std::prev(next);
-      if (prev->first + prev->second.size == a && prev->second.chunk == id) {
-        prev->second.size += n;
-        return;
-      }
-    }
-    free_.emplace(start, Range{n, id});
-  }
-
- private:
-  struct Range {
-    size_t size;
-    int chunk;
-  };
-  static constexpr size_t kChunk = size_t(64) << 20;
-  static constexpr size_t kChunkAlign = size_t(2) << 20;
-  std::mutex mu_;
-  std::map<uintptr_t, Range> free_;                   // start address -> free range
-  std::vector<std::pair<uintptr_t, size_t>> chunks_;  // (base, bytes)
-};
-
+// Work-list arena, one per device (RangeArena): chunks of at least 64 MiB
+// from hipMalloc, kept mapped until the process ends.  Freeing a work list
+// never calls hipFree, which synchronizes the whole device: a finished
+// request's plan is released while other work runs (kvx_xfer_poll).
 constexpr int kMaxDevices = 64;
-// Never destroyed: a plan may be freed while the process shuts down.
-static DescArena* const g_arena = new DescArena[kMaxDevices];
+constexpr size_t kArenaChunk = size_t(64) << 20;
+constexpr size_t kArenaChunkAlign = size_t(2) << 20;
+
+static RangeArena* make_arenas() {
+  // Never destroyed: a plan may be freed while the process shuts down.
+  RangeArena* a = static_cast<RangeArena*>(::operator new(sizeof(RangeArena) * kMaxDevices));
+  for (int d = 0; d < kMaxDevices; ++d) new (a + d) RangeArena(kArenaChunk, kArenaChunkAlign);
+  return a;
+}
+static RangeArena* const g_arena = make_arenas();
+
+static int hip_chunk(size_t bytes, void** out) { return int(hipMalloc(out, bytes)); }
 
 int desc_alloc(size_t bytes, void** out, int* device) {
   int dev = 0;
-  const hipError_t e = hipGetDevice(&dev);
+  hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return fail_hip(e, "hipGetDevice");
   if (dev < 0 || dev >= kMaxDevices) return fail(KVX_E_UNSUPPORTED, "kvx_plan: device %d beyond %d", dev, kMaxDevices);
   *device = dev;
-  return g_arena[dev].alloc((bytes + 255) / 256 * 256, out);
+  const size_t n = (bytes + 255) / 256 * 256;
+  const int rc = g_arena[dev].alloc(n, hip_chunk, out);
+  if (rc == 0) return KVX_OK;
+  e = hipError_t(rc);
+  return e == hipErrorOutOfMemory ? fail(KVX_E_NOMEM, "kvx_plan: device work list (%zu B)", n)
+                                  : fail_hip(e, "hipMalloc(work-list chunk)");
 }
 
 void desc_free(void* p, size_t bytes, int device) {
-  if (p && device >= 0 && device < kMaxDevices) g_arena[device].release(p, (bytes + 255) / 256 * 256);
+  if (p && device >= 0 && device < kMaxDevices) (void)g_arena[device].release(p, (bytes + 255) / 256 * 256);
 }
 
 void plan_free_idle(kvx_plan_t* p) {
