@@ -11,6 +11,7 @@
 #include <cstdint>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -465,6 +466,33 @@ void release(kvx_plan_t* p) {
   kvx::plan_free_idle(p);
 }
 
+// Plans released with kvx_plan_destroy_after, each with the event recorded
+// behind its last work; freed once the event has fired.
+std::mutex g_retire_mu;
+std::vector<std::pair<kvx_plan_t*, hipEvent_t>> g_retired;
+
+// Free the retired plans whose event has fired (wait: wait for each).
+// *pending receives how many remain.
+int reclaim(bool wait, int64_t* pending) {
+  std::lock_guard<std::mutex> lk(g_retire_mu);
+  int rc = KVX_OK;
+  for (size_t i = 0; i < g_retired.size();) {
+    const hipEvent_t ev = g_retired[i].second;
+    const hipError_t e = wait ? hipEventSynchronize(ev) : hipEventQuery(ev);
+    if (e == hipSuccess) {
+      (void)hipEventDestroy(ev);
+      kvx::plan_free_idle(g_retired[i].first);
+      g_retired[i] = g_retired.back();
+      g_retired.pop_back();
+      continue;
+    }
+    if (e != hipErrorNotReady && rc == KVX_OK) rc = fail_hip(e, "kvx_plan_reclaim: event");
+    ++i;
+  }
+  if (pending) *pending = int64_t(g_retired.size());
+  return rc;
+}
+
 // First token a sliding-window group moves ([MORI] §6: sliding-window layers
 // get their own geometry).  The receiving side's next query, at position n,
 // sees positions n-W+1 .. n; blocks holding none of them are skipped, so the
@@ -601,6 +629,7 @@ int kvx_plan(const kvx_pool* src, const kvx_pool* dst, int32_t num_requests,
              const int32_t* src_ids, const int32_t* dst_ids, uint32_t flags, hipStream_t upload_stream,
              kvx_plan_t** out) {
   if (!src || !dst || !out) return fail(KVX_E_INVAL, "kvx_plan: null pool or output");
+  if (!(flags & KVX_PLAN_HOST_ONLY)) (void)reclaim(false, nullptr);  // plans released earlier whose work is done
   if (src == dst) return fail(KVX_E_INVAL, "kvx_plan: src and dst are the same pool");
   if (flags & ~(KVX_PLAN_HOST_ONLY | KVX_PLAN_OVERLAP)) return fail(KVX_E_INVAL, "kvx_plan: unknown flags 0x%x", flags);
   if (!(flags & KVX_PLAN_HOST_ONLY) && capturing(upload_stream))
@@ -705,6 +734,33 @@ int kvx_plan_launch_shape(const kvx_plan_t* p, kvx_launch_shape* out) {
 }
 
 void kvx_plan_destroy(kvx_plan_t* p) { release(p); }
+
+int kvx_plan_destroy_after(kvx_plan_t* p, hipStream_t stream) {
+  if (!p) return KVX_OK;
+  if (!p->dev_buf) {  // host-only: nothing on the device
+    plan_free_idle(p);
+    return KVX_OK;
+  }
+  if (capturing(stream)) return fail(KVX_E_INVAL, "kvx_plan_destroy_after: the stream is capturing a graph");
+  hipEvent_t ev = nullptr;
+  hipError_t e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
+  if (e != hipSuccess) return fail_hip(e, "kvx_plan_destroy_after: hipEventCreate");
+  e = hipEventRecord(ev, stream);
+  if (e != hipSuccess) {
+    (void)hipEventDestroy(ev);
+    return fail_hip(e, "kvx_plan_destroy_after: hipEventRecord");
+  }
+  try {
+    std::lock_guard<std::mutex> lk(g_retire_mu);
+    g_retired.emplace_back(p, ev);
+  } catch (const std::bad_alloc&) {
+    (void)hipEventDestroy(ev);
+    return fail(KVX_E_NOMEM, "kvx_plan_destroy_after: out of host memory");
+  }
+  return reclaim(false, nullptr);
+}
+
+int kvx_plan_reclaim(int32_t wait, int64_t* pending) { return reclaim(wait != 0, pending); }
 
 int kvx_staging_bytes(const kvx_plan_t* p, int32_t l0, int32_t l1, int64_t* bytes) {
   if (!p || !bytes) return fail(KVX_E_INVAL, "kvx_staging_bytes: null argument");

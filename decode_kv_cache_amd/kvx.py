@@ -69,6 +69,8 @@ _SIGS = {
     "kvx_plan_bytes": (C.c_int, [_P, C.POINTER(_I64), C.POINTER(_I64)]),
     "kvx_plan_launch_shape": (C.c_int, [_P, C.POINTER(kvx_launch_shape)]),
     "kvx_plan_wait": (C.c_int, [_P]),
+    "kvx_plan_destroy_after": (C.c_int, [_P, _P]),
+    "kvx_plan_reclaim": (C.c_int, [_I32, C.POINTER(_I64)]),
     "kvx_plan_destroy": (None, [_P]),
     "kvx_push_layer": (C.c_int, [_P, _I32, _P, _P]),
     "kvx_push_layer_timed": (C.c_int, [_P, _I32, _P, _P, _P, _P]),
@@ -287,7 +289,21 @@ class Plan:
             self._L.kvx_plan_destroy(self.handle)
             self.handle = None
 
+    def close_after(self, stream=None):
+        """kvx_plan_destroy_after: freed once the work enqueued on ``stream``
+        so far has finished, without waiting on the host."""
+        if getattr(self, "handle", None):
+            h, self.handle = self.handle, None
+            _check("kvx_plan_destroy_after", self._L.kvx_plan_destroy_after(h, _stream(stream)))
+
     __del__ = close
+
+
+def kvx_plan_reclaim(wait: bool = False) -> int:
+    """Free released plans whose work has finished; returns how many remain."""
+    n = C.c_int64()
+    _check("kvx_plan_reclaim", lib().kvx_plan_reclaim(int(wait), C.byref(n)))
+    return n.value
 
 
 def _csr(tables):

@@ -32,7 +32,10 @@
  *     have been observed complete on the host: call kvx_plan_wait before
  *     capturing (KVX_E_INVAL otherwise; the capture stays valid).
  *     kvx_plan must be called outside a capture (KVX_E_INVAL when its
- *     upload stream is capturing).
+ *     upload stream is capturing).  kvx_plan, kvx_plan_destroy_after and
+ *     kvx_plan_reclaim allocate device memory or record and query events,
+ *     which invalidates a capture in global mode on any stream: call them
+ *     while no capture is in progress in the process.
  *   - Bytes are copied, never interpreted: bf16, fp8 or any other element type
  *     of 1, 2 or 4 bytes moves bit-exactly.
  */
@@ -46,7 +49,7 @@
 extern "C" {
 #endif
 
-#define KVX_ABI_VERSION 3
+#define KVX_ABI_VERSION 4
 
 /* Status codes. */
 enum {
@@ -285,6 +288,21 @@ int kvx_plan_bytes(const kvx_plan_t* plan, int64_t* read_bytes, int64_t* write_b
  * on any stream, so this first waits until the device is idle
  * (hipDeviceSynchronize).  NULL is a no-op. */
 void kvx_plan_destroy(kvx_plan_t* plan);
+
+/* Free a plan without waiting on the host: it is freed once the work
+ * enqueued on `stream` so far has finished.  The caller guarantees that no
+ * other stream still has work with the plan in flight (or that `stream`
+ * already waits for it), and enqueues nothing more with it.  The memory is
+ * reclaimed by a later kvx_plan (device plans), kvx_plan_destroy_after or
+ * kvx_plan_reclaim call after that point.  A host-only plan is freed at
+ * once; NULL is a no-op.  Errors: INVAL (`stream` is capturing a graph),
+ * NOMEM, HIP. */
+int kvx_plan_destroy_after(kvx_plan_t* plan, hipStream_t stream);
+
+/* Free the plans released with kvx_plan_destroy_after whose work has
+ * finished; with wait != 0, wait for the rest first.  *pending (nullable)
+ * receives how many remain.  Errors: HIP. */
+int kvx_plan_reclaim(int32_t wait, int64_t* pending);
 
 /*
  * Layerwise push: copy layer `layer`'s bytes of every planned token in every

@@ -38,6 +38,9 @@
  * in seconds on a clock of the caller's choice.
  *
  * Threading: calls on one kvx_xfer are serialized internally (a mutex).
+ * In device mode the calls build plans and record and query events: make
+ * them while no graph capture is in progress in the process (a global-mode
+ * capture on any stream would be invalidated).
  * Return values follow kvx.h (KVX_OK or KVX_E_*).  Unless a call lists
  * more: INVAL for a null handle or argument, HIP for a runtime failure
  * (device mode), NOMEM when host memory runs out.  `accepted` outputs

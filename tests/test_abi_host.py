@@ -35,7 +35,7 @@ def test_library_exports_every_declared_symbol():
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(kvx.EXPORTED)
-    assert kvx.kvx_abi_version() == 3
+    assert kvx.kvx_abi_version() == 4
     assert L.kvx_status_str(kvx.KVX_E_DUPDST) == b"KVX_E_DUPDST"
 
 
@@ -197,6 +197,10 @@ def test_argument_errors():
     assert L.kvx_copy_heads(plan.handle, 0, 0, 0, 1, None, None) == kvx.KVX_E_INVAL
     assert L.kvx_plan_wait(plan.handle) == kvx.KVX_OK          # nothing uploaded: returns at once
     assert L.kvx_plan_wait(None) == kvx.KVX_E_INVAL
+    assert L.kvx_plan_destroy_after(None, None) == kvx.KVX_OK   # NULL: no-op
+    other = kvx.kvx_plan_raw(sp, dp, 1, n, off, off, ids, ids)[1]
+    other.close_after(0)                                      # host-only: freed at once
+    assert other.handle is None and kvx.kvx_plan_reclaim(False) == 0
     with pytest.raises(kvx.KvxError):
         plan.triples(2, 0)
     b = ctypes.c_int64()

@@ -107,6 +107,52 @@ def test_plan_destroy_waits():
     assert np.array_equal(gd.kv.cpu().numpy(), exp.kv)
 
 
+
+def test_plan_released_after_its_stream():
+    """kvx_plan_destroy_after: a plan released right after its pushes were
+    enqueued stays intact until they ran, while plans built meanwhile get
+    work lists of their own (both destinations match the oracle).
+    Reclaiming a released plan does not wait for unrelated device work: a
+    long compute kernel on another stream is still running when it returns."""
+    from decode_kv_cache_amd import bench_support as B
+    spec = W.PoolSpec(8, 1024, 16, 8, 128, W.BF16)
+    hs, hd = W.host_values(spec, 7, 1), W.host_values(spec, 7, 2)
+    gs = S.device_side(spec, 7, 1, values=hs)
+    gd = S.device_side(spec, 7, 2, values=hd)
+    gd2 = S.device_side(spec, 7, 2, values=hd)
+    rng = np.random.Generator(np.random.PCG64(14))
+    st = [rng.permutation(1024)[:400].astype(np.int32)]
+    dt = [rng.permutation(1024)[:400].astype(np.int32)]
+    dt2 = [rng.permutation(1024)[:300].astype(np.int32)]
+    side = torch.cuda.Stream()
+    plan = kvx.kvx_plan(gs.pool, gd.pool, [400 * 16], st, dt, stream=side)
+    for l in range(8):
+        kvx.kvx_push_layer(plan, l, stream=side)
+    plan.close_after(side)                          # the pushes may still be queued
+    plan2 = kvx.kvx_plan(gs.pool, gd2.pool, [300 * 16], [st[0][:300]], dt2, stream=side)
+    for l in range(8):
+        kvx.kvx_push_layer(plan2, l, stream=side)
+    side.synchronize()
+    g = P.geom(O, spec)
+    exp = O.Pool(g, hd[0].copy(), None)
+    O.push(O.Pool(g, hs[0], None), exp, O.make_plan(g, g, [O.Request(400 * 16, st[0], dt[0])]))
+    assert np.array_equal(gd.kv.cpu().numpy(), exp.kv)
+    exp2 = O.Pool(g, hd[0].copy(), None)
+    O.push(O.Pool(g, hs[0], None), exp2, O.make_plan(g, g, [O.Request(300 * 16, st[0][:300], dt2[0])]))
+    assert np.array_equal(gd2.kv.cpu().numpy(), exp2.kv)
+    plan2.close_after(side)
+    side.synchronize()                              # plan2's work is done
+    compute = torch.cuda.Stream()
+    sink = torch.empty(256 * 256, dtype=torch.float32, device="cuda")
+    B.layer_compute(sink, 100_000_000, 256, stream=compute)   # bounded: a fixed loop, tens of ms at least
+    busy = torch.cuda.Event()
+    busy.record(compute)
+    print("long compute kernel enqueued", flush=True)
+    assert kvx.kvx_plan_reclaim(False) == 0          # both released plans freed
+    assert not busy.query(), "kvx_plan_reclaim waited for unrelated device work"
+    torch.cuda.synchronize()
+    assert kvx.kvx_plan_reclaim(True) == 0
+
 def test_overlap_plan_two_streams():
     """A plan built with KVX_PLAN_OVERLAP (whole 32 KiB blocks, 4 KiB pieces)
     pushed with its layers alternating over two side streams, each layer
