@@ -255,7 +255,9 @@ def kvx_state_pool_create(*, regions: Sequence[torch.Tensor], num_slots: int, sl
 
 
 class Plan:
-    """Owns a kvx_plan_t handle (destroyed on close / garbage collection)."""
+    """Owns a kvx_plan_t handle.  close() and garbage collection call
+    kvx_plan_destroy, which drains the device first; a plan used on one
+    stream is better released with close_after(stream), which does not wait."""
 
     def __init__(self, handle, src: Pool, dst: Pool):
         self.handle, self.src, self.dst, self._L = handle, src, dst, lib()
