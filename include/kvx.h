@@ -15,7 +15,8 @@
  *   - Return value: KVX_OK (0) or one of the KVX_E_* codes.  No call throws,
  *     aborts or prints.  kvx_last_error() holds a thread-local message for the
  *     last failing call on this thread.  Output parameters are written only
- *     when the call returns KVX_OK.
+ *     when the call returns KVX_OK.  A null handle or a null required pointer
+ *     is KVX_E_INVAL for every call that lists errors.
  *   - Ownership: the caller owns all pool memory, staging buffers, streams and
  *     events and must keep pool memory alive until enqueued work completes.
  *     The library owns the opaque kvx_pool / kvx_plan_t handles and each
