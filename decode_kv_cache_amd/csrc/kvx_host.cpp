@@ -489,7 +489,7 @@ int reclaim(bool wait, int64_t* pending) {
     if (e != hipErrorNotReady && rc == KVX_OK) rc = fail_hip(e, "kvx_plan_reclaim: event");
     ++i;
   }
-  if (pending) *pending = int64_t(g_retired.size());
+  if (pending && rc == KVX_OK) *pending = int64_t(g_retired.size());
   return rc;
 }
 

@@ -45,7 +45,10 @@
  * more: INVAL for a null handle or argument, HIP for a runtime failure
  * (device mode), NOMEM when host memory runs out.  `accepted` outputs
  * (nullable) report whether the message changed the state: 1 = applied,
- * 0 = ignored (stale attempt, finished request, duplicate).
+ * 0 = ignored (stale attempt, finished request, duplicate).  Unlike other
+ * outputs they are written whatever the return value: a registration
+ * whose plan fails to build is applied (the request turns FAILED) and
+ * returns the plan's error.
  *
  * Memory: a request's plan (and its device work list) is released when the
  * request finishes, once the writes already enqueued with it are done.  Its
