@@ -282,3 +282,10 @@ def test_reblock_errors():
         kvx.Pool(num_blocks=8, block_size=65536, num_heads=1, head_dim=16, elem_bytes=1, layout="NHD",
                  k_bases=[FAKE], v_bases=[FAKE * 2])
     assert e.value.code == kvx.KVX_E_UNSUPPORTED
+
+
+def test_build_entry_version_check():
+    """__graft_entry__.build() ends by comparing the built library's ABI
+    version with include/kvx.h; the same check without the compile."""
+    import __graft_entry__ as G
+    assert G.header_abi_version() == kvx.kvx_abi_version()
