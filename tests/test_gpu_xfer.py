@@ -146,3 +146,72 @@ def test_poll_frees_plans_without_waiting_for_the_device():
     torch.cuda.synchronize()
     assert x.pop_finished() == [(7, 0, kvx.KVX_REQ_DONE)]
     x.close()
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_xfer_random_device_sequences(seed):
+    """Seeded random schedules in device mode: each request registers before
+    a random layer or only after the forward pass (deferred writes, gated on
+    events captured at their save); each layer's compute writes a canary into
+    every request's source blocks and records the layer's event; layers are
+    saved for the whole batch at once or request by request in random
+    order; polls interleave with the work.  Every request ends DONE and the
+    consumer pool equals the oracle's push of the final source bytes."""
+    rng = np.random.Generator(np.random.PCG64(900 + seed))
+    spec = W.PoolSpec(4, 1024, 16, 8, 128, W.BF16) if seed % 2 else W.PoolSpec(5, 900, 16, 4, 64, W.BF16)
+    R, L = 8, spec.num_layers
+    plen = [int(x) for x in rng.integers(60, 1500, size=R)]
+    need = [W.alloc_blocks(p, 16) for p in plen]
+    st = W.split_tables(W.geometric_run_table(rng, spec.num_blocks, float(rng.choice([1.5, 6.0]))), need)
+    dt = W.split_tables(W.geometric_run_table(rng, spec.num_blocks, float(rng.choice([1.5, 6.0]))), need)
+    gs = S.device_side(spec, 8 + seed, 1)
+    gd = S.device_side(spec, 8 + seed, 2)
+    dst0 = gd.kv.cpu().numpy().copy()
+    side = torch.cuda.Stream()
+    compute = torch.cuda.Stream()
+    x = kvx.Xfer(gs.pool, stream=side)
+    toks = [kvx.kvx_tokens_to_move(p, 0) for p in plen]
+    bb = spec.block_size * spec.num_heads * spec.head_dim * spec.elem_bytes
+    sink = torch.empty(256 * 256, dtype=torch.float32, device="cuda")
+    blocks = torch.from_numpy(np.concatenate([st[r][:-(-toks[r] // 16)] for r in range(R)]).astype(np.int32)).cuda()
+    reg_at = [int(rng.integers(0, L + 1)) for _ in range(R)]     # L: after the forward pass
+    now = 0.0
+    for r in range(R):
+        assert x.prefill(r, 0, toks[r], st[r], now)
+    print(f"seed {seed}: registration layers {reg_at}", flush=True)
+    for l in range(L):
+        for r in range(R):
+            if reg_at[r] == l:
+                assert x.register(r, 0, gd.pool, dt[r], now)
+        B.layer_compute(sink, 2000, 64, gs.region(l, 0), gs.region(l, 1), blocks, bb, 0xC000 + 64 * seed + l,
+                        stream=compute)
+        ev = torch.cuda.Event()
+        ev.record(compute)
+        if rng.integers(0, 2):
+            assert all(x.save_layer_many(l, range(R), [0] * R, now, ready=ev))
+        else:
+            for r in rng.permutation(R):
+                assert x.save_layer(int(r), 0, l, now, ready=ev)
+        if rng.integers(0, 3) == 0:
+            x.poll(now)
+    for r in range(R):
+        assert x.seal(r, 0)
+    for r in range(R):
+        if reg_at[r] == L:
+            assert x.register(r, 0, gd.pool, dt[r], now)
+    done = {}
+    for _ in range(2000):
+        x.poll(now)
+        for rid, att, stt in x.pop_finished():
+            done[rid] = stt
+        if len(done) == R:
+            break
+        torch.cuda.synchronize()
+    assert done == {r: kvx.KVX_REQ_DONE for r in range(R)}, done
+    torch.cuda.synchronize()
+    g = P.geom(O, spec)
+    src = O.Pool(g, gs.kv.cpu().numpy(), None)
+    exp = O.Pool(g, dst0, None)
+    O.push(src, exp, O.make_plan(g, g, [O.Request(n, s, d) for n, s, d in zip(toks, st, dt)]))
+    assert np.array_equal(gd.kv.cpu().numpy(), exp.kv)
+    x.close()
