@@ -115,6 +115,8 @@ def test_plan_released_after_its_stream():
     Reclaiming a released plan does not wait for unrelated device work: a
     long compute kernel on another stream is still running when it returns."""
     from decode_kv_cache_amd import bench_support as B
+    torch.cuda.synchronize()
+    kvx.kvx_plan_reclaim(True)     # the release list is process-wide: start it empty
     spec = W.PoolSpec(8, 1024, 16, 8, 128, W.BF16)
     hs, hd = W.host_values(spec, 7, 1), W.host_values(spec, 7, 2)
     gs = S.device_side(spec, 7, 1, values=hs)
