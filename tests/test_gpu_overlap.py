@@ -36,8 +36,9 @@ def test_event_gating_canary():
     sink = torch.empty(256 * 256, dtype=torch.float32, device="cuda")
     compute = torch.cuda.current_stream()
     side = torch.cuda.Stream()
-    for rep in range(25):
-        print("rep", rep, flush=True)
+    for rep in range(100):
+        if rep % 10 == 0:
+            print("rep", rep, flush=True)
         canary = 0x1000 + rep
         evs = []
         for l in range(spec.num_layers):
