@@ -62,7 +62,7 @@ def log(*a):
 
 
 # The dominant kernel of each workload's bench line, as named in profiles/.
-COUNTER_KERNEL = {"tp4_share": "heads_kernel"}
+COUNTER_KERNEL = {"tp4_share": "heads_kernel", "pack_unpack": "many_kernel"}
 
 
 def counter_traffic(workload: str):
@@ -833,6 +833,10 @@ def bench_pack(args, torch, kvx, S, W):
     def step():
         kvx.kvx_pack(plan, 0, L, stg, stream=side)
         kvx.kvx_unpack(plan, 0, L, stg, stream=side)
+    if args.counters:   # each of a step's 4 launches (32 layers) reads and writes nbytes / 2
+        counters_run(torch, kvx, plan, side, 1, nbytes, launch=lambda _l: step())
+        plan.close()
+        return None
     for _ in range(args.warmup):
         step()
     with Timer(torch, side) as t:
@@ -1001,9 +1005,9 @@ def main():
           "tp4_share": bench_tp4, "multiturn_fp8": bench_multiturn, "pack_unpack": bench_pack,
           "dsr1_mla_push": bench_hybrid, "gptoss_swa_push": bench_hybrid,
           "qwen3next_state_push": bench_hybrid}[args.workload]
-    if args.counters and fn not in (bench_push, bench_batched, bench_tp4, bench_multiturn):
-        print("bench.py: --counters is for the qwen32b_push, tiny_push, batched_push, tp4_share and multiturn_fp8 "
-              "workloads", file=sys.stderr)
+    if args.counters and fn not in (bench_push, bench_batched, bench_tp4, bench_multiturn, bench_pack):
+        print("bench.py: --counters is for the qwen32b_push, tiny_push, batched_push, tp4_share, multiturn_fp8 and "
+              "pack_unpack workloads", file=sys.stderr)
         sys.exit(2)
     r = fn(args, torch, kvx, S, W)
     if r is None:

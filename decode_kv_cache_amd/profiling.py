@@ -26,7 +26,8 @@ from collections import defaultdict
 PKG = os.path.dirname(os.path.abspath(__file__))
 PUSH_KERNEL = "kvx::copy_kernel<0, "   # any launch shape of the push mode
 HEADS_KERNEL = "kvx::heads_kernel"
-KERNELS = {"push": PUSH_KERNEL, "heads": HEADS_KERNEL}
+MANY_KERNEL = "kvx::copy_many_kernel<"   # batched launches: pack / unpack over layers, kvx_push_many
+KERNELS = {"push": PUSH_KERNEL, "heads": HEADS_KERNEL, "many": MANY_KERNEL}
 CALIB_KERNEL = "copy_kernel(unsigned int __vector(4)*"   # kvxb_copy in libkvx_bench.so
 CALIB_BYTES = 1 << 30
 
