@@ -960,7 +960,7 @@ def bench_xfer(args, torch, kvx, S, W):
                    "step": f"{R} requests x {L} layers through kvx_xfer (half registered after the forward pass), "
                            f"one synthetic compute kernel per layer",
                    "host_us_per_save": round(host_us, 3), "one_plan_per_layer_GBs": round(raw, 1)},
-        "roofline": roofline(step_bytes // (R * L), ms * 1e3 / (R * L), "kvx::copy_kernel<0> via kvx_xfer",
+        "roofline": roofline(step_bytes // (R * L), ms * 1e3 / (R * L), "kvx::copy_many_kernel<0> (kvx_push_many via kvx_xfer)",
                              "xfer_pipeline", {"note": "per (request, layer) write, span of the whole step"}),
         "cpu_baseline": None,
     }
