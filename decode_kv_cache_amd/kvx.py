@@ -167,6 +167,23 @@ def kvx_should_reuse(reusable_tokens: int, threshold: int) -> bool:
     return bool(lib().kvx_should_reuse(reusable_tokens, threshold))
 
 
+def _require_device_tensor(fn: str, what: str, t, dtype) -> None:
+    """Refuse what the kernels cannot address safely: a host tensor, a tensor
+    on another device than the current one, a strided view (its span is not
+    numel x element size) or the wrong element type."""
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{fn}: {what} must be a torch tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{fn}: {what} is a host tensor; the kernels need device memory")
+    if t.device.index != torch.cuda.current_device():
+        raise ValueError(f"{fn}: {what} lives on cuda:{t.device.index}, the current device is "
+                         f"cuda:{torch.cuda.current_device()}")
+    if not t.is_contiguous():
+        raise ValueError(f"{fn}: {what} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{fn}: {what} must be {dtype}, got {t.dtype}")
+
+
 class Pool:
     """Owns a kvx_pool handle.  ``k_bases``/``v_bases``: one device address per
     logical layer (may repeat; ``v_bases`` None for a pool of one latent
@@ -210,6 +227,24 @@ def kvx_pool_create(*, kv, scales=None, num_layers: int, num_blocks: int, block_
     with optional fp32 ``scales`` of shape [P, R, num_blocks].  Logical layer
     l uses slab ``phys(l)`` (default l)."""
     phys = phys or (lambda l: l)
+    block_bytes = block_size * num_heads * head_dim * elem_bytes
+    _require_device_tensor("kvx_pool_create", "kv", kv, torch.uint8)
+    if kv.dim() != 3 or kv.shape[1] not in (1, 2):
+        raise ValueError(f"kvx_pool_create: kv must be uint8 [slabs, 1 or 2 regions, region bytes], got "
+                         f"{tuple(kv.shape)}")
+    if kv.shape[2] < num_blocks * block_bytes:
+        raise ValueError(f"kvx_pool_create: a region holds {kv.shape[2]} bytes, {num_blocks} blocks of "
+                         f"{block_bytes} bytes need {num_blocks * block_bytes}")
+    slabs = [phys(l) for l in range(num_layers)]
+    if any(not 0 <= p < kv.shape[0] for p in slabs):
+        raise ValueError(f"kvx_pool_create: a layer maps outside the {kv.shape[0]} slabs of kv")
+    if scales is not None:
+        _require_device_tensor("kvx_pool_create", "scales", scales, torch.float32)
+        if scales.dim() != 3 or tuple(scales.shape[:2]) != tuple(kv.shape[:2]) or scales.shape[2] < num_blocks:
+            raise ValueError(f"kvx_pool_create: scales must be float32 [{kv.shape[0]}, {kv.shape[1]}, "
+                             f">={num_blocks}], got {tuple(scales.shape)}")
+        if scales.device != kv.device:
+            raise ValueError("kvx_pool_create: scales and kv live on different devices")
     two = kv.shape[1] == 2
     kb = [kv[phys(l), 0].data_ptr() for l in range(num_layers)]
     vb = [kv[phys(l), 1].data_ptr() for l in range(num_layers)] if two else None
@@ -248,6 +283,15 @@ class StatePool:
 def kvx_state_pool_create(*, regions: Sequence[torch.Tensor], num_slots: int, slot_bytes) -> StatePool:
     """Register a state pool stored as two uint8 tensors [layers, num_slots *
     slot_bytes[r]] (r = 0: convolution state, 1: SSM state)."""
+    if len(regions) != 2:
+        raise ValueError("kvx_state_pool_create: two regions (convolution state, SSM state)")
+    for r, t in enumerate(regions):
+        _require_device_tensor("kvx_state_pool_create", f"regions[{r}]", t, torch.uint8)
+        if t.dim() != 2 or t.shape[1] < num_slots * slot_bytes[r]:
+            raise ValueError(f"kvx_state_pool_create: regions[{r}] must be uint8 [layers, >={num_slots} x "
+                             f"{slot_bytes[r]}], got {tuple(t.shape)}")
+    if regions[0].shape[0] != regions[1].shape[0] or regions[0].device != regions[1].device:
+        raise ValueError("kvx_state_pool_create: both regions need the same layer count and device")
     L = regions[0].shape[0]
     return StatePool(num_slots=num_slots, slot_bytes=slot_bytes,
                      bases0=[regions[0][l].data_ptr() for l in range(L)],
@@ -388,13 +432,18 @@ def kvx_staging_bytes(plan: Plan, l0: int, l1: int) -> int:
     return b.value
 
 
+def _staging_cap(fn: str, staging: torch.Tensor) -> int:
+    _require_device_tensor(fn, "staging", staging, None)
+    return staging.numel() * staging.element_size()
+
+
 def kvx_pack(plan: Plan, l0: int, l1: int, staging: torch.Tensor, stream=None) -> None:
-    cap = staging.numel() * staging.element_size()
+    cap = _staging_cap("kvx_pack", staging)
     _check("kvx_pack", lib().kvx_pack(plan.handle, l0, l1, staging.data_ptr(), cap, _stream(stream)))
 
 
 def kvx_unpack(plan: Plan, l0: int, l1: int, staging: torch.Tensor, stream=None) -> None:
-    cap = staging.numel() * staging.element_size()
+    cap = _staging_cap("kvx_unpack", staging)
     _check("kvx_unpack", lib().kvx_unpack(plan.handle, l0, l1, staging.data_ptr(), cap, _stream(stream)))
 
 

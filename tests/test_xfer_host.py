@@ -185,3 +185,73 @@ def test_threads_share_one_instance():
         done += got
     assert len(done) == T * PER and all(s == kvx.KVX_REQ_DONE for _, _, s in done)
     x.close()
+
+
+class NativeAsModel:
+    """The native state machine (host-only) behind the oracle model's
+    interface, so the hand-worked page scenarios pin it directly."""
+
+    # one 64-slot block holds every scenario's prompt; IDs up to 255, layers up to 7
+    SPEC = W.PoolSpec(8, 256, 64, 1, 16, W.U8)
+
+    def __init__(self, defer_timeout: float = 60.0, transfer_timeout: float = 30.0):
+        self._prod, self._cons = fake_pool(self.SPEC, 0), fake_pool(self.SPEC, 1)
+        self._x = kvx.Xfer(self._prod, defer_timeout=defer_timeout, transfer_timeout=transfer_timeout,
+                           host_only=True, log=True)
+
+    @property
+    def issued(self):
+        return [tuple(int(v) for v in e) for e in self._x.issued()]
+
+    def register(self, rid, attempt, dst_ids, now):
+        return self._x.register(rid, attempt, self._cons, dst_ids, now)
+
+    def prefill(self, rid, attempt, num_tokens, src_ids, now):
+        return self._x.prefill(rid, attempt, num_tokens, src_ids, now)
+
+    def save_layer(self, rid, attempt, layer, now):
+        return self._x.save_layer(rid, attempt, layer, now)
+
+    def save_layer_many(self, layer, rids, attempts, now):
+        return self._x.save_layer_many(layer, rids, attempts, now)
+
+    def seal(self, rid, attempt):
+        return self._x.seal(rid, attempt)
+
+    def complete(self, rid, attempt, layer):
+        self._x.complete(rid, attempt, layer, ok=True)
+
+    def fail(self, rid, attempt, layer):
+        self._x.complete(rid, attempt, layer, ok=False)
+
+    def tick(self, now):
+        self._x.poll(now)
+
+    def status(self, rid):
+        s = self._x.status(rid)
+        return None if s is None else (s[0], STATE[s[1]])
+
+    def pop_finished(self):
+        return [(int(r), int(a), STATE[s]) for r, a, s in self._x.pop_finished()]
+
+    def forget(self, rid):
+        try:
+            self._x.forget(rid)
+            return True
+        except kvx.KvxError:
+            return False
+
+    def recompute_blocks(self, rid):
+        return self._x.recompute_blocks(rid) or []
+
+
+def page_scenarios():
+    import test_xfer_oracle as T
+    return T.SCENARIOS
+
+
+@pytest.mark.parametrize("scenario", page_scenarios(), ids=lambda f: f.__name__)
+def test_native_follows_page_scenarios(scenario):
+    """Every hand-worked scenario that pins the model also holds for the
+    native state machine, forget and batched saves included."""
+    scenario(NativeAsModel)

@@ -164,9 +164,81 @@ def sc_many_requests_order(M):
     assert m.pop_finished() == [(10, 0, X.DONE)]
 
 
+def sc_forget(M):
+    """A request's record is dropped only once the request has finished
+    ([MORI] §3.2: a finished request frees what it holds; a pending one still
+    has writes in flight).  After that the ID is unknown: no status, no
+    recompute list, and a second forget finds nothing."""
+    m = M(defer_timeout=60.0, transfer_timeout=30.0)
+    # 40: DONE; 41: FAILED (its only write failed); 42: EXPIRED (never registered); 43: PENDING
+    for rid in (40, 41):
+        m.register(rid, 0, [rid, rid + 100], now=0.0)
+        m.prefill(rid, 0, 20, [1, 2], now=0.0)
+        m.save_layer(rid, 0, 0, now=0.0)
+        m.seal(rid, 0)
+    m.complete(40, 0, 0)
+    m.fail(41, 0, 0)
+    m.prefill(42, 0, 20, [5, 6], now=0.0)
+    m.save_layer(42, 0, 0, now=0.0)
+    m.register(43, 0, [7], now=0.0)
+    m.prefill(43, 0, 8, [8], now=0.0)
+    m.save_layer(43, 0, 0, now=0.0)
+    m.tick(60.0)                              # 42's deferral runs out; 43's write is 60 s old too
+    assert [m.status(r) for r in (40, 41, 42)] == [(0, X.DONE), (0, X.FAILED), (0, X.EXPIRED)]
+    assert m.status(43) == (0, X.FAILED)      # 43's write passed the 30 s transfer timeout
+    m2 = M()
+    m2.register(44, 0, [9], now=0.0)
+    m2.prefill(44, 0, 8, [9], now=0.0)
+    m2.save_layer(44, 0, 0, now=0.0)
+    assert not m2.forget(44)                  # still pending: refused, record kept
+    assert m2.status(44) == (0, X.PENDING)
+    m2.seal(44, 0)
+    m2.complete(44, 0, 0)
+    assert m2.forget(44)
+    assert m2.status(44) is None
+    assert not m2.forget(44)
+    assert m.recompute_blocks(41) == [41, 141]
+    assert m.forget(41) and m.forget(42) and m.forget(40)
+    assert [m.status(r) for r in (40, 41, 42)] == [None, None, None]
+    assert m.recompute_blocks(41) == []       # the failed request's list left with its record
+    assert m.pop_finished() == [(43, 0, X.FAILED)]   # forgotten requests are not reported
+    assert not m.forget(99)                   # never seen
+    # a forgotten ID starts over: a new registration is a new request
+    assert m.register(40, 0, [50], now=61.0)
+    assert m.status(40) == (0, X.PENDING)
+
+
+def sc_save_layer_many(M):
+    """One layer saved for a batch of requests ([MORI] §3.2, writes queued
+    per layer right after its compute): a request whose blocks are known on
+    both sides is written at once, one that still misses its registration is
+    deferred until it arrives, and a stale attempt, an unknown request or a
+    sealed request is refused.  The writes go out in batch order."""
+    m = M()
+    m.register(50, 0, [1], now=0.0)
+    m.prefill(50, 0, 8, [2], now=0.0)         # ready
+    m.prefill(51, 0, 8, [3], now=0.0)         # consumer not registered yet
+    m.register(52, 1, [4], now=0.0)
+    m.prefill(52, 1, 8, [5], now=0.0)         # attempt 1 is current
+    m.register(53, 0, [6], now=0.0)
+    m.prefill(53, 0, 8, [7], now=0.0)
+    m.save_layer(53, 0, 0, now=0.0)
+    m.seal(53, 0)                             # sealed: no more saves
+    m.register(54, 0, [8], now=0.0)
+    m.prefill(54, 0, 8, [9], now=0.0)         # ready, listed after 50
+    acc = m.save_layer_many(3, [54, 51, 52, 77, 53, 50], [0, 0, 0, 0, 0, 0], now=1.0)
+    assert acc == [True, True, False, False, False, True]
+    assert m.issued == [(53, 0, 0), (54, 0, 3), (50, 0, 3)]
+    m.register(51, 0, [10], now=2.0)          # the deferred write goes out now
+    assert m.issued[-1] == (51, 0, 3)
+    assert m.save_layer_many(3, [50, 51], [0, 0], now=3.0) == [True, True]   # repeats count once
+    assert len(m.issued) == 4
+    assert m.save_layer_many(4, [], [], now=3.0) == []
+
+
 SCENARIOS = [sc_register_first, sc_prefill_first, sc_defer_timeout, sc_expired_recompute,
              sc_seal_counts_queued_writes, sc_middle_layer_failure, sc_retry, sc_transfer_timeout,
-             sc_many_requests_order]
+             sc_many_requests_order, sc_forget, sc_save_layer_many]
 
 
 @pytest.mark.parametrize("scenario", SCENARIOS, ids=lambda f: f.__name__)
@@ -252,8 +324,43 @@ def mut_deferred_reverse_order(mod):
     mod.XferModel._flush_deferred = _flush_deferred
 
 
+def mut_forget_pending(mod):
+    def forget(self, rid):
+        if rid not in self.reqs:
+            return False
+        del self.reqs[rid]
+        return True
+    mod.XferModel.forget = forget
+
+
+def mut_forget_keeps_record(mod):
+    def forget(self, rid):
+        r = self.reqs.get(rid)
+        return r is not None and r.state != mod.PENDING
+    mod.XferModel.forget = forget
+
+
+def mut_many_ready_only(mod):
+    def save_layer_many(self, layer, rids, attempts, now):
+        out = []
+        for rid, a in zip(rids, attempts):
+            r = self._get(rid, a, create=False)
+            out.append(self.save_layer(rid, a, layer, now) if r is not None and self._ready(r) else False)
+        return out
+    mod.XferModel.save_layer_many = save_layer_many
+
+
+def mut_many_reverse_order(mod):
+    def save_layer_many(self, layer, rids, attempts, now):
+        pairs = list(zip(rids, attempts))
+        acc = [self.save_layer(r, a, layer, now) for r, a in reversed(pairs)]
+        return acc[::-1]
+    mod.XferModel.save_layer_many = save_layer_many
+
+
 MUTATIONS = [mut_latest_layer_only, mut_no_flush_on_register, mut_strict_defer, mut_expected_all_layers,
-             mut_stale_attempt_accepted, mut_deferred_reverse_order]
+             mut_stale_attempt_accepted, mut_deferred_reverse_order, mut_forget_pending,
+             mut_forget_keeps_record, mut_many_ready_only, mut_many_reverse_order]
 
 
 @pytest.mark.parametrize("mutation", MUTATIONS, ids=lambda f: f.__name__)
