@@ -33,7 +33,7 @@ COMMON = [
 HOST_CXX = [f"-isystem{os.path.join(ROCM, 'include')}", "-D__HIP_PLATFORM_AMD__=1"]
 
 TARGETS = {
-    "libkvx.so": ["kvx_host.cpp", "kvx_xfer.cpp", "kvx_kernels.hip"],
+    "libkvx.so": ["kvx_host.cpp", "kvx_xfer.cpp", "kvx_queue.cpp", "kvx_kernels.hip"],
     "libkvx_bench.so": ["kvx_bench_support.hip"],
 }
 

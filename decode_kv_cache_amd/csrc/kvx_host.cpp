@@ -62,6 +62,8 @@ static int wait_event_on(hipEvent_t ev, hipStream_t s, bool cap) {
 
 int wait_event(hipEvent_t ev, hipStream_t s) { return wait_event_on(ev, s, ev && capturing(s)); }
 
+bool stream_capturing(hipStream_t s) { return capturing(s); }
+
 int enqueue_waits(kvx_plan_t* p, hipEvent_t ready, hipStream_t s) {
   const bool seen = p->upload_seen.load(std::memory_order_acquire);
   const bool cap = (ready || !seen) && capturing(s);

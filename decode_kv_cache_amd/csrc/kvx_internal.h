@@ -143,6 +143,8 @@ int fail_hip(hipError_t e, const char* what);
 
 // Make `stream` wait for `ev` unless it has already fired (NULL: nothing).
 int wait_event(hipEvent_t ev, hipStream_t stream);
+// True while `stream` is capturing a graph.
+bool stream_capturing(hipStream_t stream);
 // Before a device call: enqueue the wait for `ready` and for the plan upload.
 int enqueue_waits(kvx_plan_t* plan, hipEvent_t ready, hipStream_t stream);
 // After a launch: turn a launch error into KVX_E_HIP.
@@ -158,5 +160,14 @@ void desc_free(void* p, size_t bytes, int device);
 // Free a plan whose enqueued work is known to have finished (no device
 // drain, unlike kvx_plan_destroy).
 void plan_free_idle(kvx_plan_t* plan);
+
+// Validate one (plan, layer) pair of a batched push (pair index i for the
+// message): a device plan with a push work list and a layer in range.
+int check_push_pair(const kvx_plan_t* plan, int32_t layer, const char* fn, int32_t i);
+
+// Enqueue the pushes of already validated pairs on `stream` (after each
+// plan's upload), batched into as few launches as kvx_push_many uses; no
+// ready wait.
+int push_batch(const kvx_plan_t* const* plans, const int32_t* layers, int32_t n, hipStream_t stream);
 
 }  // namespace kvx

@@ -419,6 +419,41 @@ static CopyArgs push_args(const kvx_plan_t* p, int32_t layer) {
   return a;
 }
 
+int check_push_pair(const kvx_plan_t* p, int32_t layer, const char* fn, int32_t i) {
+  int rc = check_device_plan(p, fn);
+  if (rc) return rc;
+  if (!p->push_ok) return fail(KVX_E_MISMATCH, "%s: pair %d: pools differ in head count or layout", fn, i);
+  if (layer < 0 || layer >= p->src.L)
+    return fail(KVX_E_RANGE, "%s: pair %d: layer %d outside [0,%d)", fn, i, layer, p->src.L);
+  return KVX_OK;
+}
+
+int push_batch(const kvx_plan_t* const* plans, const int32_t* layers, int32_t n, hipStream_t stream) {
+  for (int32_t i = 0; i < n; ++i) {
+    const int rc = enqueue_waits(const_cast<kvx_plan_t*>(plans[i]), nullptr, stream);
+    if (rc) return rc;
+  }
+  // Pairs without scales share launches (ManyBatch); a pair with scales, or
+  // too many pieces for one launch, is launched alone, in order.
+  ManyBatch<kPush> batch(stream);
+  for (int32_t i = 0; i < n; ++i) {
+    kvx_plan_t* p = const_cast<kvx_plan_t*>(plans[i]);
+    int rc;
+    if (p->src.scales || !ManyBatch<kPush>::fits(p)) {
+      if (p->pieces.empty() && p->blocks.empty()) continue;
+      rc = batch.flush();
+      if (rc) return rc;
+      rc = launch_copy<kPush>(p, push_args(p, layers[i]), int64_t(p->blocks.size()), stream);
+      if (rc) return rc;
+      continue;
+    }
+    const CopyArgs a = push_args(p, layers[i]);
+    rc = batch.add(p, a.in, a.out);
+    if (rc) return rc;
+  }
+  return batch.flush();
+}
+
 }  // namespace kvx
 
 using namespace kvx;
@@ -447,37 +482,12 @@ int kvx_push_many(const kvx_plan_t* const* plans, const int32_t* layers, int32_t
                   hipStream_t stream) {
   if (n < 0 || (n > 0 && (!plans || !layers))) return fail(KVX_E_INVAL, "kvx_push_many: bad arguments");
   for (int32_t i = 0; i < n; ++i) {
-    const kvx_plan_t* p = plans[i];
-    int rc = check_device_plan(p, "kvx_push_many");
+    int rc = check_push_pair(plans[i], layers[i], "kvx_push_many", i);
     if (rc) return rc;
-    if (!p->push_ok) return fail(KVX_E_MISMATCH, "kvx_push_many: pair %d: pools differ in head count or layout", i);
-    if (layers[i] < 0 || layers[i] >= p->src.L)
-      return fail(KVX_E_RANGE, "kvx_push_many: pair %d: layer %d outside [0,%d)", i, layers[i], p->src.L);
   }
   int rc = wait_event(ready, stream);
   if (rc) return rc;
-  for (int32_t i = 0; i < n; ++i) {
-    rc = enqueue_waits(const_cast<kvx_plan_t*>(plans[i]), nullptr, stream);
-    if (rc) return rc;
-  }
-  // Pairs without scales share launches (ManyBatch); a pair with scales, or
-  // too many pieces for one launch, is launched alone, in order.
-  ManyBatch<kPush> batch(stream);
-  for (int32_t i = 0; i < n; ++i) {
-    kvx_plan_t* p = const_cast<kvx_plan_t*>(plans[i]);
-    if (p->src.scales || !ManyBatch<kPush>::fits(p)) {
-      if (p->pieces.empty() && p->blocks.empty()) continue;
-      rc = batch.flush();
-      if (rc) return rc;
-      rc = launch_copy<kPush>(p, push_args(p, layers[i]), int64_t(p->blocks.size()), stream);
-      if (rc) return rc;
-      continue;
-    }
-    const CopyArgs a = push_args(p, layers[i]);
-    rc = batch.add(p, a.in, a.out);
-    if (rc) return rc;
-  }
-  return batch.flush();
+  return kvx::push_batch(plans, layers, n, stream);
 }
 
 static int staging_call(const kvx_plan_t* cp, int32_t l0, int32_t l1, const void* staging,

@@ -1,0 +1,279 @@
+// Layer write queue of one stream (kvx_queue_* in kvx.h).
+//
+// In push mode the producer queues each layer's write right after that
+// layer's compute, and the write goes out once the layer's event has fired;
+// at the end of the forward pass it waits for all of them ([MORI] §3.2,
+// WRITE mode; the worker hooks save_kv_layer and wait_for_save, [MORI] §6).
+// On a GPU every write is a kernel launch, and back-to-back launches on one
+// queue cost a few microseconds each on top of the copy.  The queue keeps at
+// most kInflight launch groups in flight on its stream; writes that become
+// ready while those run are held and leave together in the next launch
+// group (kvx_push_many's batched launch), so the fixed cost is paid per
+// group instead of per layer when writes back up, and every write still
+// starts only after its own layer's event.
+
+#include <hip/hip_runtime.h>
+
+#include <deque>
+#include <mutex>
+#include <vector>
+
+#include "kvx_internal.h"
+
+namespace {
+
+constexpr int kInflight = 2;
+
+struct Entry {
+  const kvx_plan_t* plan;
+  int32_t layer;
+  hipEvent_t ready;  // the queue's own copy of the caller's event; NULL once observed fired
+};
+
+}  // namespace
+
+struct kvx_queue {
+  hipStream_t stream = nullptr;
+  // Helper stream that turns a caller's event into one of the queue's own:
+  // a wait for the caller's event, then a record of an owned event.  The
+  // caller's event is consumed at the push (as by a stream wait) and may be
+  // re-recorded or destroyed right after.  It carries no kernels.
+  hipStream_t aux = nullptr;
+  std::vector<hipEvent_t> free_events;
+  std::vector<hipEvent_t> all_events;
+  std::mutex mu;
+  std::deque<Entry> pending;
+  hipEvent_t done[kInflight] = {};  // recorded behind each launch group, a ring, oldest at `head`
+  int head = 0, busy = 0;
+  int64_t writes = 0, groups = 0;
+};
+
+namespace kvx {
+namespace {
+
+void release_event(kvx_queue* q, hipEvent_t e) {
+  if (e) q->free_events.push_back(e);
+}
+
+// An owned event that fires when `ready` (as recorded now) has fired.
+int mirror_event(kvx_queue* q, hipEvent_t ready, hipEvent_t* out) {
+  hipEvent_t e;
+  if (!q->free_events.empty()) {
+    e = q->free_events.back();
+    q->free_events.pop_back();
+  } else {
+    const hipError_t c = hipEventCreateWithFlags(&e, hipEventDisableTiming);
+    if (c != hipSuccess) return fail_hip(c, "kvx_queue: hipEventCreateWithFlags");
+    q->all_events.push_back(e);
+  }
+  hipError_t r = hipStreamWaitEvent(q->aux, ready, 0);
+  if (r == hipSuccess) r = hipEventRecord(e, q->aux);
+  if (r != hipSuccess) {
+    q->free_events.push_back(e);
+    return fail_hip(r, "kvx_queue: mirroring the ready event");
+  }
+  *out = e;
+  return KVX_OK;
+}
+
+// 1: the entry may go out now (no event, or its event has fired); 0: not
+// yet; negative: -status of a failed query.
+int entry_ready(kvx_queue* qu, Entry& e) {
+  if (!e.ready) return 1;
+  const hipError_t q = hipEventQuery(e.ready);
+  if (q == hipSuccess) {
+    release_event(qu, e.ready);
+    e.ready = nullptr;
+    return 1;
+  }
+  if (q == hipErrorNotReady) return 0;
+  return -fail_hip(q, "kvx_queue: hipEventQuery(ready)");
+}
+
+int retire(kvx_queue* q) {
+  while (q->busy > 0) {
+    const hipError_t e = hipEventQuery(q->done[q->head]);
+    if (e == hipErrorNotReady) break;
+    if (e != hipSuccess) return fail_hip(e, "kvx_queue: hipEventQuery(launch)");
+    q->head = (q->head + 1) % kInflight;
+    --q->busy;
+  }
+  return KVX_OK;
+}
+
+// Mark the end of a launch group: an event behind everything enqueued so
+// far.  When the ring is full its oldest group is dropped from tracking
+// (stream order: it finishes before this one).
+int record_group(kvx_queue* q) {
+  if (q->busy == kInflight) {
+    q->head = (q->head + 1) % kInflight;
+    --q->busy;
+  }
+  const int slot = (q->head + q->busy) % kInflight;
+  const hipError_t e = hipEventRecord(q->done[slot], q->stream);
+  if (e != hipSuccess) return fail_hip(e, "kvx_queue: hipEventRecord");
+  ++q->busy;
+  ++q->groups;
+  return KVX_OK;
+}
+
+int launch(kvx_queue* q, const std::vector<const kvx_plan_t*>& plans, const std::vector<int32_t>& layers) {
+  if (plans.empty()) return KVX_OK;
+  return push_batch(plans.data(), layers.data(), int32_t(plans.size()), q->stream);
+}
+
+void drop_pending(kvx_queue* q) {
+  for (Entry& e : q->pending) release_event(q, e.ready);
+  q->pending.clear();
+}
+
+// Launch the ready front of the queue while fewer than kInflight groups run.
+int pump(kvx_queue* q) {
+  int rc = retire(q);
+  if (rc) return rc;
+  std::vector<const kvx_plan_t*> plans;
+  std::vector<int32_t> layers;
+  while (q->busy < kInflight && !q->pending.empty()) {
+    size_t n = 0;
+    while (n < q->pending.size()) {
+      const int r = entry_ready(q, q->pending[n]);
+      if (r < 0) return -r;
+      if (r == 0) break;
+      ++n;
+    }
+    if (n == 0) break;
+    plans.clear();
+    layers.clear();
+    for (size_t i = 0; i < n; ++i) {
+      plans.push_back(q->pending[i].plan);
+      layers.push_back(q->pending[i].layer);
+    }
+    q->pending.erase(q->pending.begin(), q->pending.begin() + std::ptrdiff_t(n));
+    rc = launch(q, plans, layers);
+    if (rc) return rc;
+    rc = record_group(q);
+    if (rc) return rc;
+  }
+  return KVX_OK;
+}
+
+// Enqueue every queued write: ready ones merged, each one still waiting for
+// its event behind a stream wait for that event.
+int flush(kvx_queue* q) {
+  int rc = pump(q);
+  if (rc) return rc;
+  if (q->pending.empty()) return KVX_OK;
+  std::vector<const kvx_plan_t*> plans;
+  std::vector<int32_t> layers;
+  std::deque<Entry> todo;
+  todo.swap(q->pending);
+  for (Entry& e : todo) {
+    const int r = entry_ready(q, e);
+    if (r < 0) return -r;
+    if (r == 0) {
+      rc = launch(q, plans, layers);
+      if (rc) return rc;
+      plans.clear();
+      layers.clear();
+      rc = wait_event(e.ready, q->stream);
+      release_event(q, e.ready);   // the wait has taken the event's state
+      e.ready = nullptr;
+      if (rc) return rc;
+    }
+    plans.push_back(e.plan);
+    layers.push_back(e.layer);
+  }
+  rc = launch(q, plans, layers);
+  if (rc) return rc;
+  return record_group(q);
+}
+
+}  // namespace
+}  // namespace kvx
+
+using namespace kvx;
+
+extern "C" {
+
+int kvx_queue_create(hipStream_t stream, kvx_queue** out) {
+  if (!out) return fail(KVX_E_INVAL, "kvx_queue_create: null out");
+  if (stream_capturing(stream)) return fail(KVX_E_INVAL, "kvx_queue_create: the stream is capturing a graph");
+  kvx_queue* q = new (std::nothrow) kvx_queue;
+  if (!q) return fail(KVX_E_NOMEM, "kvx_queue_create: out of host memory");
+  q->stream = stream;
+  hipError_t e = hipStreamCreateWithFlags(&q->aux, hipStreamNonBlocking);
+  if (e != hipSuccess) {
+    delete q;
+    return fail_hip(e, "kvx_queue_create: hipStreamCreateWithFlags");
+  }
+  for (int i = 0; i < kInflight; ++i) {
+    e = hipEventCreateWithFlags(&q->done[i], hipEventDisableTiming);
+    if (e != hipSuccess) {
+      for (int j = 0; j < i; ++j) (void)hipEventDestroy(q->done[j]);
+      (void)hipStreamDestroy(q->aux);
+      delete q;
+      return fail_hip(e, "kvx_queue_create: hipEventCreateWithFlags");
+    }
+  }
+  *out = q;
+  return KVX_OK;
+}
+
+int kvx_queue_push(kvx_queue* q, const kvx_plan_t* plan, int32_t layer, hipEvent_t ready) {
+  if (!q) return fail(KVX_E_INVAL, "kvx_queue_push: null queue");
+  int rc = check_push_pair(plan, layer, "kvx_queue_push", 0);
+  if (rc) return rc;
+  std::lock_guard<std::mutex> lk(q->mu);
+  if (stream_capturing(q->stream)) return fail(KVX_E_INVAL, "kvx_queue_push: the stream is capturing a graph");
+  Entry en{plan, layer, nullptr};
+  if (ready) {
+    const hipError_t r = hipEventQuery(ready);
+    if (r == hipErrorNotReady) {
+      rc = mirror_event(q, ready, &en.ready);
+      if (rc) return rc;
+    } else if (r != hipSuccess) {
+      return fail_hip(r, "kvx_queue_push: hipEventQuery(ready)");
+    }
+  }
+  q->pending.push_back(en);
+  ++q->writes;
+  rc = pump(q);
+  if (rc) drop_pending(q);
+  return rc;
+}
+
+int kvx_queue_flush(kvx_queue* q) {
+  if (!q) return fail(KVX_E_INVAL, "kvx_queue_flush: null queue");
+  std::lock_guard<std::mutex> lk(q->mu);
+  if (stream_capturing(q->stream)) return fail(KVX_E_INVAL, "kvx_queue_flush: the stream is capturing a graph");
+  const int rc = flush(q);
+  if (rc) drop_pending(q);
+  return rc;
+}
+
+int kvx_queue_stats(const kvx_queue* q, int64_t* writes, int64_t* groups) {
+  if (!q || !writes || !groups) return fail(KVX_E_INVAL, "kvx_queue_stats: null argument");
+  kvx_queue* m = const_cast<kvx_queue*>(q);
+  std::lock_guard<std::mutex> lk(m->mu);
+  *writes = m->writes;
+  *groups = m->groups;
+  return KVX_OK;
+}
+
+int kvx_queue_destroy(kvx_queue* q) {
+  if (!q) return KVX_OK;
+  int rc;
+  {
+    std::lock_guard<std::mutex> lk(q->mu);
+    rc = stream_capturing(q->stream) ? fail(KVX_E_INVAL, "kvx_queue_destroy: the stream is capturing a graph")
+                                     : flush(q);
+  }
+  drop_pending(q);
+  for (int i = 0; i < kInflight; ++i) (void)hipEventDestroy(q->done[i]);
+  for (hipEvent_t e : q->all_events) (void)hipEventDestroy(e);
+  (void)hipStreamDestroy(q->aux);
+  delete q;
+  return rc;
+}
+
+}  // extern "C"

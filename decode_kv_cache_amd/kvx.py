@@ -79,6 +79,11 @@ _SIGS = {
     "kvx_pack": (C.c_int, [_P, _I32, _I32, _P, _I64, _P]),
     "kvx_unpack": (C.c_int, [_P, _I32, _I32, _P, _I64, _P]),
     "kvx_copy_heads": (C.c_int, [_P, _I32, _I32, _I32, _I32, _P, _P]),
+    "kvx_queue_create": (C.c_int, [_P, C.POINTER(_P)]),
+    "kvx_queue_push": (C.c_int, [_P, _P, _I32, _P]),
+    "kvx_queue_flush": (C.c_int, [_P]),
+    "kvx_queue_stats": (C.c_int, [_P, C.POINTER(_I64), C.POINTER(_I64)]),
+    "kvx_queue_destroy": (C.c_int, [_P]),
 }
 _D = C.c_double
 _U64 = C.c_uint64
@@ -451,6 +456,43 @@ def kvx_copy_heads(plan: Plan, layer: int, src_head0: int, dst_head0: int, num_h
                    ready=None, stream=None) -> None:
     _check("kvx_copy_heads", lib().kvx_copy_heads(plan.handle, layer, src_head0, dst_head0, num_heads,
                                                   _event(ready), _stream(stream)))
+
+
+class Queue:
+    """Owns a kvx_queue handle: the layer write queue of one stream
+    (kvx_queue_push per layer save, kvx_queue_flush before waiting)."""
+
+    def __init__(self, stream=None):
+        h = C.c_void_p()
+        _check("kvx_queue_create", lib().kvx_queue_create(_stream(stream), C.byref(h)))
+        self.handle, self._L = h, lib()
+
+    def push(self, plan: Plan, layer: int, ready=None) -> None:
+        _check("kvx_queue_push", lib().kvx_queue_push(self.handle, plan.handle, layer, _event(ready)))
+
+    def flush(self) -> None:
+        _check("kvx_queue_flush", lib().kvx_queue_flush(self.handle))
+
+    def stats(self):
+        """(writes queued, launch groups enqueued) so far."""
+        w, g = C.c_int64(), C.c_int64()
+        _check("kvx_queue_stats", lib().kvx_queue_stats(self.handle, C.byref(w), C.byref(g)))
+        return w.value, g.value
+
+    def close(self) -> None:
+        if getattr(self, "handle", None):
+            h, self.handle = self.handle, None
+            _check("kvx_queue_destroy", self._L.kvx_queue_destroy(h))
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def kvx_queue_create(stream=None) -> Queue:
+    return Queue(stream)
 
 
 class Xfer:

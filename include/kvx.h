@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define KVX_ABI_VERSION 4
+#define KVX_ABI_VERSION 5
 
 /* Status codes. */
 enum {
@@ -352,6 +352,64 @@ int kvx_push_layer_timed(const kvx_plan_t* plan, int32_t layer, hipEvent_t ready
  */
 int kvx_push_many(const kvx_plan_t* const* plans, const int32_t* layers, int32_t n, hipEvent_t ready,
                   hipStream_t stream);
+
+/*
+ * Layer write queue of one stream.  In push mode the producer queues each
+ * layer's write right after that layer's compute; the write goes out once
+ * the layer's event has fired, and at the end of the forward pass the
+ * producer waits for all of them ([MORI] §3.2, WRITE mode, with the event
+ * sync before each layer write; [MORI] §6, the worker hooks save_kv_layer
+ * and wait_for_save).  kvx_queue_push is the save of one layer,
+ * kvx_queue_flush the point after which work enqueued on the stream (an
+ * event for wait_for_save) follows every queued write.
+ * Each launch on a stream costs a few microseconds beyond its copy, which a
+ * layer of tens of megabytes feels.  The queue therefore keeps at most two
+ * launch groups of its writes in flight on its stream: a write that is ready
+ * (its event has fired, or is NULL) while two groups still run waits in the
+ * queue, and the ready writes at its front leave together, as one batched
+ * launch of kvx_push_many, as soon as a group finishes.  A write whose event
+ * has not fired blocks the writes queued behind it until it fires (writes
+ * leave in queue order).  No write starts before its own event has fired;
+ * writes of one group may run at the same time, so writes queued between
+ * two flushes must not write the same destination bytes (repeating an
+ * identical write is harmless).  The queue observes its launches and the
+ * ready events only through event queries, so it never blocks the host.
+ * `ready` is consumed at the push, as a stream wait would: the write waits
+ * for the event's recording at that moment, and the caller may re-record or
+ * destroy the event right after.  (An event not yet fired is mirrored by an
+ * event of the queue's own, recorded behind a wait on a helper stream that
+ * the queue creates at the default priority and that carries no kernels.)
+ * A queue belongs to one stream on the current device and is not for graph
+ * capture (KVX_E_INVAL while the stream captures).  Plans must stay alive
+ * until the flush that enqueues their writes, then as for kvx_push_layer.
+ */
+typedef struct kvx_queue kvx_queue;
+
+/* Create the write queue of `stream` (NULL = the null stream).
+ * Errors: INVAL (null out, stream capturing), NOMEM, HIP. */
+int kvx_queue_create(hipStream_t stream, kvx_queue** out);
+
+/* Queue the write of layer `layer` of `plan` (what kvx_push_layer would
+ * copy), to go out after `ready` (nullable) fires.  May enqueue launches of
+ * earlier writes.  On an error the writes still queued are dropped.
+ * Errors: INVAL (null queue or plan, host-only plan, stream capturing),
+ * RANGE (layer), MISMATCH (a plan without a push work list), HIP. */
+int kvx_queue_push(kvx_queue* q, const kvx_plan_t* plan, int32_t layer, hipEvent_t ready);
+
+/* Enqueue every queued write on the queue's stream, each still waiting for
+ * its own event (a stream wait for an event not yet observed fired), so that
+ * work enqueued on the stream afterwards follows them all.  Returns without
+ * waiting on the host.  Errors: INVAL (null queue, stream capturing), HIP
+ * (the writes still queued are dropped). */
+int kvx_queue_flush(kvx_queue* q);
+
+/* Writes queued so far and launch groups enqueued so far (each group is one
+ * kvx_push_many launch sequence).  Errors: INVAL (null argument). */
+int kvx_queue_stats(const kvx_queue* q, int64_t* writes, int64_t* groups);
+
+/* Flush, then free the queue.  NULL is a no-op (KVX_OK).  Returns the
+ * flush's status; the queue is freed in every case. */
+int kvx_queue_destroy(kvx_queue* q);
 
 /* Staging bytes for layers [l0, l1): (l1 - l0) * sum over the layer's
  * regions of (payload + scale segment), where payload = sum of the region's
