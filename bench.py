@@ -62,7 +62,7 @@ def log(*a):
 
 
 # The dominant kernel of each workload's bench line, as named in profiles/.
-COUNTER_KERNEL = {"tp4_share": "heads_kernel", "pack_unpack": "many_kernel"}
+COUNTER_KERNEL = {"qwen32b_push": "many_kernel", "tp4_share": "heads_kernel", "pack_unpack": "many_kernel"}
 
 
 def counter_traffic(workload: str):
@@ -214,8 +214,130 @@ def workload(W, name: str, args):
     return ctor(**kw)
 
 
+def timed_steps(torch, stream, step, steps, warmup):
+    """W untimed steps, then `steps` steps with an event between consecutive
+    steps on `stream`: (total span ms, per-step spans ms)."""
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    marks[0].record(stream)
+    for i in range(steps):
+        step()
+        marks[i + 1].record(stream)
+    torch.cuda.synchronize()
+    per = np.array([marks[i].elapsed_time(marks[i + 1]) for i in range(steps)])
+    return marks[0].elapsed_time(marks[-1]), per
+
+
+def span_stats(per_step_ms) -> dict:
+    a = np.asarray(per_step_ms, dtype=np.float64)
+    return {"median_ms": round(float(np.median(a)), 4), "min_ms": round(float(a.min()), 4),
+            "p90_ms": round(float(np.percentile(a, 90)), 4), "mean_ms": round(float(a.mean()), 4),
+            "steps": int(a.size)}
+
+
+class QueueStep:
+    """The layerwise step through one write queue on `side`: for each (plan,
+    layer) pair, kvx_queue_push(plan, layer, ready[i]), then kvx_queue_flush."""
+
+    def __init__(self, kvx, side, pairs, ready):
+        self.kvx, self.side, self.pairs, self.ready = kvx, side, pairs, ready
+        self.q = kvx.Queue(side)
+
+    def __call__(self):
+        for i, (p, l) in enumerate(self.pairs):
+            self.q.push(p, l, ready=self.ready[i])
+        self.q.flush()
+
+    def timed(self, torch, steps, warmup):
+        """(span ms, per-step ms, launch groups per step, kernel launches per step)."""
+        w0, g0, n0 = self.q.stats3()
+        span, per = timed_steps(torch, self.side, self, steps, warmup)
+        w1, g1, n1 = self.q.stats3()
+        nsteps = (w1 - w0) / len(self.pairs)
+        return span, per, (g1 - g0) / nsteps, (n1 - n0) / nsteps
+
+    def kernel_us(self, torch, calls=5):
+        """Kernel time of the step's launches once writes back up (one
+        kvx_push_many over every pair), from the launches' own dispatch
+        timestamps: mean us per call."""
+        plans, layers = [p for p, _ in self.pairs], [l for _, l in self.pairs]
+        a = [torch.cuda.Event(enable_timing=True) for _ in range(calls)]
+        b = [torch.cuda.Event(enable_timing=True) for _ in range(calls)]
+        for i in range(calls):
+            self.kvx.kvx_push_many_timed(plans, layers, a[i], b[i], stream=self.side)
+        torch.cuda.synchronize()
+        return float(np.mean([a[i].elapsed_time(b[i]) for i in range(calls)]) * 1e3)
+
+    def close(self):
+        self.q.close()
+
+
+# ---------------------------------------------------------------------------
+# oracle leg: parity of the timed path (verification step before timing) and
+# the CPU baseline; the only part of this file that touches oracle/
+# ---------------------------------------------------------------------------
+def oracle_geom(O, spec, n_layers=None):
+    return O.Geometry(spec.num_layers if n_layers is None else n_layers, spec.num_blocks, spec.block_size,
+                      spec.num_heads, spec.head_dim, spec.elem_bytes, spec.layout, spec.has_scales, spec.regions,
+                      spec.window)
+
+
+def snap_layers(S, side, layers):
+    """Host copies (regions, scale bits) of the sampled layers' physical slabs."""
+    out = {}
+    for l in layers:
+        p = side.spec.phys(l)
+        out[p] = (side.kv[p].cpu().numpy().copy(),
+                  S.scale_bits(side.sc[p]).copy() if side.sc is not None else None)
+    return out
+
+
+def parity_push_layers(O, S, wl, gs, gd, src_snap, dst_snap, toks, layers, label):
+    """Every byte of the sampled layers' regions (and scales) against the
+    oracle's push of the pre-step source onto the pre-step destination; the
+    source must be unchanged."""
+    op = O.make_plan(oracle_geom(O, wl.src), oracle_geom(O, wl.dst),
+                     [O.Request(n, s, d) for n, s, d in zip(toks, wl.src_tables, wl.dst_tables)])
+    nbytes, bad = 0, []
+    for l in layers:
+        p = wl.src.phys(l)
+        skv, ssc = src_snap[p]
+        dkv, dsc = dst_snap[p]
+        for r in range(wl.src.regions):
+            exp = dkv[r].copy()
+            O.push_region(skv[r], exp, op.triples)
+            got = gd.kv[p, r].cpu().numpy()
+            nbytes += got.size
+            if not np.array_equal(got, exp):
+                bad.append(f"layer {l} region {r}")
+            if not np.array_equal(gs.kv[p, r].cpu().numpy(), skv[r]):
+                bad.append(f"layer {l} region {r}: source changed")
+            if ssc is not None:
+                es = dsc[r].copy()
+                O.push_scales(ssc[r], es, op.pairs)
+                if not np.array_equal(S.scale_bits(gd.sc[p, r]), es):
+                    bad.append(f"layer {l} region {r} scales")
+    return parity_record(bad, f"{label}: every byte of layers {layers} (K/V regions"
+                              f"{' and scales' if wl.src.has_scales else ''}) against the oracle", nbytes)
+
+
+def parity_record(bad, what, nbytes):
+    r = {"result": "fail" if bad else "pass", "checked": what, "bytes_compared": int(nbytes)}
+    if bad:
+        r["mismatches"] = bad[:8]
+    log(f"parity: {r['result']} ({what}; {nbytes} bytes)" + (f" MISMATCH {bad[:4]}" if bad else ""))
+    return r
+
+
 def bench_push(args, torch, kvx, S, W):
-    """qwen32b_push (default) and tiny_push: the layerwise push."""
+    """qwen32b_push (default), tiny_push and qwen32b_reblock: the layerwise
+    push.  The step: for each layer, kvx_queue_push(layer, ready[layer]) on
+    the side stream's write queue (the layer's write goes out once its event
+    has fired), then kvx_queue_flush; ready[layer] is the (already fired)
+    event of that layer's compute."""
+    from decode_kv_cache_amd import bench_support as B
     wl = workload(W, args.workload, args)
     gs, gd = S.device_side(wl.src, wl.seed, 1), S.device_side(wl.dst, wl.seed, 2)
     tokens = [kvx.kvx_tokens_to_move(p, 0) for p in wl.prompt_lens]
@@ -225,68 +347,74 @@ def bench_push(args, torch, kvx, S, W):
     plan_ms = steady_plan_ms(kvx, gs.pool, gd.pool, tokens, wl.src_tables, wl.dst_tables, side)
     rd, wr = plan.bytes_per_layer()
     L = wl.src.num_layers
-    step_bytes = (rd + wr) * L
+    layer_bytes = rd + wr
+    step_bytes = layer_bytes * L
     nruns = len(plan.runs()) if wl.src.block_size == wl.dst.block_size else None
     ntrip = len(plan.triples())
-    log(f"plan: {nruns} runs, {ntrip} triples/region, {rd + wr} B per layer, "
+    log(f"plan: {nruns} runs, {ntrip} triples/region, {layer_bytes} B per layer, "
         f"{step_bytes} B per step, host plan {plan_ms:.2f} ms")
 
-    if args.counters:
-        counters_run(torch, kvx, plan, side, L, rd + wr)
+    if args.counters:   # the queue's launches once writes back up: kvx_push_many of 32 layers per launch
+        counters_run(torch, kvx, plan, side, 1, layer_bytes * min(L, 32),
+                     launch=lambda _l: kvx.kvx_push_many([plan] * L, list(range(L)), stream=side))
         plan.close()
         return None
     digest = inputs_digest(wl.src_tables + wl.dst_tables, [gs, gd], wl.prompt_lens)
 
     # One ready event per layer, recorded on the compute stream.  The headline
-    # step uses events that have already fired (the layer's compute is done):
-    # kvx_push_layer then enqueues no wait and the side stream holds nothing
-    # but the push kernels.
+    # step uses events that have already fired (the layer's compute is done).
     ready = [torch.cuda.Event() for _ in range(L)]
     for e in ready:
         e.record(compute)
     torch.cuda.synchronize()
+    step = QueueStep(kvx, side, [(plan, l) for l in range(L)], ready)
 
-    def step():
-        for l in range(L):
-            kvx.kvx_push_layer(plan, l, ready=ready[l], stream=side)
+    # Verification step on the freshly filled pools, through the timed path.
+    parity = None
+    if not args.no_parity:
+        import oracle as O
+        layers = sorted({0, 1, L // 2 + 5, L - 1} & set(range(L)))
+        src_snap, dst_snap = snap_layers(S, gs, layers), snap_layers(S, gd, layers)
+        step()
+        torch.cuda.synchronize()
+        parity = parity_push_layers(O, S, wl, gs, gd, src_snap, dst_snap, tokens, layers,
+                                    "one step through kvx_queue on the fresh pools")
+        del src_snap, dst_snap
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
-    marks[0].record(side)
-    for i in range(args.steps):
-        step()
-        marks[i + 1].record(side)
-    torch.cuda.synchronize()
-    per_step = np.array([marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps)])  # ms
-    span_ms = marks[0].elapsed_time(marks[-1])
+    span_ms, per_step, groups_per_step, launches_per_step = step.timed(torch, args.steps, args.warmup)
     ms_per_step = span_ms / args.steps
     gbs = step_bytes * args.steps / (span_ms * 1e-3) / 1e9
-    log(f"span {span_ms:.3f} ms for {args.steps} steps ({ms_per_step * 1e3:.1f} us/step, "
-        f"min {per_step.min() * 1e3:.1f}, max {per_step.max() * 1e3:.1f}): "
-        f"{gbs:.1f} GB/s = {100 * gbs / HBM_PEAK_GBS:.1f}% of {HBM_PEAK_GBS:.0f} GB/s")
+    stats = span_stats(per_step)
+    log(f"queue step: span {span_ms:.3f} ms for {args.steps} steps ({ms_per_step * 1e3:.1f} us/step, median "
+        f"{stats['median_ms'] * 1e3:.1f}, min {stats['min_ms'] * 1e3:.1f}, p90 {stats['p90_ms'] * 1e3:.1f}); "
+        f"{groups_per_step:.2f} launch groups, {launches_per_step:.2f} launches per step: {gbs:.1f} GB/s = "
+        f"{100 * gbs / HBM_PEAK_GBS:.1f}% of {HBM_PEAK_GBS:.0f} GB/s")
 
-    # The side stream carries nothing but the push kernels, back to back (a
-    # kernel trace shows no gaps between them), so the timed region's span
-    # over its launches is the push kernel's average launch duration.
-    k_avg_us = ms_per_step * 1e3 / L
-    # Cross-check in a separate short pass: every push kernel records its own
-    # start/end timestamps (from the dispatch packet).  Such launches are
-    # spaced out on the queue, so this pass is not used for throughput.
-    n_chk = min(3, args.steps)
-    k0 = [torch.cuda.Event(enable_timing=True) for _ in range(L * n_chk)]
-    k1 = [torch.cuda.Event(enable_timing=True) for _ in range(L * n_chk)]
-    for i in range(n_chk):
+    # Kernel measurement for the roofline.  Once writes back up, the queue's
+    # groups are kvx_push_many launches of 32 layers each (two per step); the
+    # same launches, timed from their own dispatch timestamps.
+    launches_per_call = -(-L // 32)
+    k_avg_us = step.kernel_us(torch) / launches_per_call
+    log(f"batched push kernel: {k_avg_us:.2f} us per launch of {min(L, 32)} layers (dispatch timestamps, "
+        f"{launches_per_call} launches per call)")
+
+    # Secondary: one kvx_push_layer launch per layer on the side stream.
+    def layer_step():
         for l in range(L):
-            kvx.kvx_push_layer_timed(plan, l, k0[i * L + l], k1[i * L + l], ready=ready[l], stream=side)
+            kvx.kvx_push_layer(plan, l, ready=ready[l], stream=side)
+    lspan, lper = timed_steps(torch, side, layer_step, args.steps, 2)
+    layer_gbs = step_bytes * args.steps / (lspan * 1e-3) / 1e9
+    kd0 = [torch.cuda.Event(enable_timing=True) for _ in range(L)]
+    kd1 = [torch.cuda.Event(enable_timing=True) for _ in range(L)]
+    for l in range(L):
+        kvx.kvx_push_layer_timed(plan, l, kd0[l], kd1[l], ready=ready[l], stream=side)
     torch.cuda.synchronize()
-    kd = np.array([k0[j].elapsed_time(k1[j]) for j in range(L * n_chk)]) * 1e3  # us
-    log(f"push kernel: {k_avg_us:.2f} us per launch over the timed region; dispatch timestamps in a "
-        f"separate pass: avg {kd.mean():.2f} us (min {kd.min():.2f}, max {kd.max():.2f})")
+    layer_kernel_us = float(np.mean([kd0[l].elapsed_time(kd1[l]) for l in range(L)]) * 1e3)
+    log(f"one kvx_push_layer launch per layer: {layer_gbs:.1f} GB/s ({lspan / args.steps * 1e3 / L:.2f} us per "
+        f"layer; dispatch timestamps {layer_kernel_us:.2f} us per launch)")
 
-    # Secondary: the same step with fresh events (recorded on the compute
-    # stream right before each push, so each push enqueues a cross-stream wait).
+    # Secondary: fresh events (recorded on the compute stream right before each
+    # push, so each kvx_push_layer enqueues a cross-stream wait).
     def fresh_step():
         for l in range(L):
             ready[l].record(compute)
@@ -296,9 +424,12 @@ def bench_push(args, torch, kvx, S, W):
         for _ in range(args.steps):
             fresh_step()
     fresh_gbs = step_bytes * args.steps / (t.ms * 1e-3) / 1e9
-    log(f"with fresh per-layer events: {fresh_gbs:.1f} GB/s")
+    for e in ready:
+        e.record(compute)
+    torch.cuda.synchronize()
+    log(f"kvx_push_layer with fresh per-layer events: {fresh_gbs:.1f} GB/s")
 
-    # Secondary: the step captured once in a HIP graph and replayed.
+    # Secondary: the per-layer step captured once in a HIP graph and replayed.
     kvx.kvx_plan_wait(plan)
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph, stream=side):
@@ -310,35 +441,10 @@ def bench_push(args, torch, kvx, S, W):
             for _ in range(args.steps):
                 graph.replay()
     graph_gbs = step_bytes * args.steps / (t.ms * 1e-3) / 1e9
-    log(f"step replayed from a HIP graph: {graph_gbs:.1f} GB/s")
+    log(f"per-layer step replayed from a HIP graph: {graph_gbs:.1f} GB/s")
     del graph
 
-    # Secondary: the fresh-event step captured in a graph.  Each layer's
-    # event is recorded on a stream forked inside the capture (where the
-    # layer's compute would run), so each push's wait becomes a graph edge
-    # and costs no host time at replay.
-    fork = torch.cuda.Stream()
-    gready = [torch.cuda.Event() for _ in range(L)]   # events of the capture only
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph, stream=side):
-        cap = torch.cuda.current_stream()
-        fork.wait_stream(cap)
-        for l in range(L):
-            gready[l].record(fork)
-            kvx.kvx_push_layer(plan, l, ready=gready[l], stream=cap)
-        cap.wait_stream(fork)
-    with torch.cuda.stream(side):
-        graph.replay()
-        with Timer(torch, side) as t:
-            for _ in range(args.steps):
-                graph.replay()
-    graph_ev_gbs = step_bytes * args.steps / (t.ms * 1e-3) / 1e9
-    log(f"fresh-event step replayed from a HIP graph: {graph_ev_gbs:.1f} GB/s")
-    del graph
-
-    # Secondary: catch-up -- all layers' events already fired, pushed by one
-    # kvx_push_many call (it batches up to 32 layers per launch and streams
-    # them in 4 KiB chunks).
+    # Secondary: all layers in one kvx_push_many call.
     many_plans, many_layers = [plan] * L, list(range(L))
     kvx.kvx_push_many(many_plans, many_layers, stream=side)
     with Timer(torch, side) as t:
@@ -347,14 +453,69 @@ def bench_push(args, torch, kvx, S, W):
     many_gbs = step_bytes * args.steps / (t.ms * 1e-3) / 1e9
     log(f"all layers in one kvx_push_many call: {many_gbs:.1f} GB/s")
 
-    # Secondary: layers alternating over two side streams, with a plan built
-    # for overlapped launches (KVX_PLAN_OVERLAP: 4 KiB pieces of four-wave
-    # workgroups, a kernel instantiation of its own, so the headline kernel's
-    # trace average is unaffected).
+    # Secondary: layers alternating over two side streams, plan built with
+    # KVX_PLAN_OVERLAP.
     oplan = kvx.kvx_plan(gs.pool, gd.pool, tokens, wl.src_tables, wl.dst_tables, overlap=True, stream=side)
     two_gbs = two_stream_rate(torch, kvx, oplan, ready, side, L, args.steps, step_bytes)
     log(f"layers alternating over two side streams (overlap plan): {two_gbs:.1f} GB/s")
     oplan.close()
+
+    # Ceiling, same run: the same bytes without a block table.  Per layer, K
+    # and V each as one contiguous segment of the plan's payload bytes
+    # (layer l's regions of both pools), so no byte is served from a cache.
+    ceiling = None
+    if wl.src.block_size == wl.dst.block_size and wl.src.regions == 2:
+        seg = rd // 2
+        assert seg <= wl.src.region_bytes and seg <= wl.dst.region_bytes and seg % 16 == 0
+        sp = [[gs.region(l, r).data_ptr() for r in range(2)] for l in range(L)]
+        dp = [[gd.region(l, r).data_ptr() for r in range(2)] for l in range(L)]
+        lay_src = [torch.tensor(sp[l], dtype=torch.int64, device="cuda") for l in range(L)]
+        lay_dst = [torch.tensor(dp[l], dtype=torch.int64, device="cuda") for l in range(L)]
+        half = -(-L // 2)
+        grp_src = [torch.tensor([x for l in ls for x in sp[l]], dtype=torch.int64, device="cuda")
+                   for ls in (range(0, half), range(half, L))]
+        grp_dst = [torch.tensor([x for l in ls for x in dp[l]], dtype=torch.int64, device="cuda")
+                   for ls in (range(0, half), range(half, L))]
+
+        def plain_per_layer():
+            for l in range(L):
+                B.copy_segments(lay_src[l], lay_dst[l], seg, 0, stream=side)
+
+        def plain_stream():
+            for g in range(2):
+                B.copy_segments(grp_src[g], grp_dst[g], seg, 1, stream=side)
+        c_layer, _ = timed_steps(torch, side, plain_per_layer, args.steps, 2)
+        c_stream, _ = timed_steps(torch, side, plain_stream, args.steps, 2)
+        # the same runs squeezed into a dense window on each side (block i of
+        # the table -> the rank of its ID among the table's IDs), same queue step
+        def dense_tables(tables, bs):
+            used = [np.asarray(t[:-(-n // bs)], dtype=np.int64) for t, n in zip(tables, tokens)]
+            ranks = np.argsort(np.argsort(np.concatenate(used))).astype(np.int32)
+            cuts = np.cumsum([0] + [len(u) for u in used])
+            return [ranks[cuts[i]:cuts[i + 1]] for i in range(len(used))]
+        wplan = kvx.kvx_plan(gs.pool, gd.pool, tokens, dense_tables(wl.src_tables, wl.src.block_size),
+                             dense_tables(wl.dst_tables, wl.dst.block_size), stream=side)
+
+        wstep = QueueStep(kvx, side, [(wplan, l) for l in range(L)], ready)
+        c_window, _ = timed_steps(torch, side, wstep, args.steps, 2)
+        wstep.close()
+        wplan.close()
+        cl = step_bytes * args.steps / (c_layer * 1e-3) / 1e9
+        cs = step_bytes * args.steps / (c_stream * 1e-3) / 1e9
+        cw = step_bytes * args.steps / (c_window * 1e-3) / 1e9
+        ceiling = {
+            "plain_copy_per_layer_GBs": round(cl, 1),
+            "plain_copy_per_layer": f"{L} launches, one per layer: K and V each one contiguous segment of "
+                                    f"{seg} B, one-wave workgroups of 32 KiB chunks",
+            "plain_copy_streamed_GBs": round(cs, 1),
+            "plain_copy_streamed": f"2 launches of {half} layers: the same segments as 4 KiB chunks of four-wave "
+                                   f"workgroups (the launch shape of the queue's batched groups)",
+            "dense_window_queue_GBs": round(cw, 1),
+            "dense_window_queue": "the same runs renumbered into a dense window of each pool, same queue step",
+            "value_over_plain_copy_streamed": round(gbs / cs, 4),
+            "value_over_plain_copy_per_layer": round(gbs / cl, 4),
+        }
+        log(f"ceiling: plain copy per layer {cl:.1f}, streamed {cs:.1f}, dense-window queue step {cw:.1f} GB/s")
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -370,23 +531,35 @@ def bench_push(args, torch, kvx, S, W):
                            args.cpu_seconds, setup)
         log(f"cpu baseline: {cpu['value']} GB/s ({cpu['sample']})")
 
+    step.close()
     plan.close()
     return {
-        "value": gbs, "ms_per_step": ms_per_step, "dtype": "u8",
+        "value": gbs, "ms_per_step": ms_per_step, "dtype": "u8", "parity": parity, "span": stats,
         "config": {"workload": wl.name, "seed": wl.seed, "inputs_sha256_16": digest, "layers": L,
                    "kv_heads": wl.src.num_heads, "head_dim": wl.src.head_dim,
                    "block_size": wl.src.block_size, "payload_dtype": wl.src.dtype, "layout": wl.src.layout,
                    "prompt_tokens": wl.prompt_lens, "tokens_moved": tokens, "pool_blocks": wl.src.num_blocks,
                    "dst_block_size": wl.dst.block_size, "dst_pool_blocks": wl.dst.num_blocks,
                    "merged_runs": nruns, "triples_per_region": ntrip, "bytes_per_step": step_bytes,
-                   "step": f"{L} x kvx_push_layer on one side stream, each after its layer's (fired) event",
-                   "host_plan_ms": round(plan_ms, 3), "fresh_event_GBs": round(fresh_gbs, 1),
-                   "graph_replay_GBs": round(graph_gbs, 1),
-                   "graph_with_events_GBs": round(graph_ev_gbs, 1),
-                   "two_stream_GBs": None if two_gbs is None else round(two_gbs, 1),
+                   "step": f"{L} x kvx_queue_push(layer, ready[layer]) then kvx_queue_flush on one side stream; "
+                           f"each write goes out after its layer's (fired) event",
+                   "launch_groups_per_step": round(groups_per_step, 3),
+                   "kernel_launches_per_step": round(launches_per_step, 3),
+                   "host_plan_ms": round(plan_ms, 3),
+                   "push_layer_per_launch_GBs": round(layer_gbs, 1),
+                   "push_layer_span_us_per_layer": round(lspan / args.steps * 1e3 / L, 3),
+                   "push_layer_kernel_us_dispatch_stamps": round(layer_kernel_us, 3),
+                   "fresh_event_push_layer_GBs": round(fresh_gbs, 1),
+                   "graph_replay_push_layer_GBs": round(graph_gbs, 1),
+                   "two_stream_push_layer_GBs": None if two_gbs is None else round(two_gbs, 1),
                    "push_many_all_layers_GBs": round(many_gbs, 1)},
-        "roofline": roofline(rd + wr, k_avg_us, "kvx::copy_kernel<0> (kvx_push_layer)", args.workload,
-                             {"kernel_us_dispatch_stamps": round(float(kd.mean()), 3)}),
+        "ceiling": ceiling,
+        "roofline": roofline(layer_bytes * min(L, 32), k_avg_us,
+                             "kvx::copy_many_kernel<0, 256, 1> (kvx_queue groups / kvx_push_many)", args.workload,
+                             {"layers_per_launch": min(L, 32),
+                              "measured": f"dispatch timestamps of kvx_push_many_timed over all {L} layers "
+                                          f"({launches_per_call} launches), 5 calls",
+                              "span_us_per_launch": round(ms_per_step * 1e3 / launches_per_call, 3)}),
         "cpu_baseline": cpu,
     }
 
@@ -427,28 +600,77 @@ def bench_hybrid(args, torch, kvx, S, W):
     for e in ready:
         e.record(compute)
     torch.cuda.synchronize()
+    step = QueueStep(kvx, side, [(plans[gi], l) for gi, l in wl.layer_map], ready)
 
-    def step():
-        for i, (gi, l) in enumerate(wl.layer_map):
-            kvx.kvx_push_layer(plans[gi], l, ready=ready[i], stream=side)
+    # Verification step on the fresh pools, through the timed path: the first
+    # and last layer of every group against the oracle.
+    parity = None
+    if not args.no_parity:
+        import oracle as O
+        sample = []
+        for gi in range(len(wl.groups)):
+            ls = [l for x, l in wl.layer_map if x == gi]
+            sample += [(gi, ls[0]), (gi, ls[-1])]
 
-    for _ in range(args.warmup):
+        def snap(side_, layer):
+            if isinstance(side_, S.StateSide):
+                return [side_.regions[r][layer].cpu().numpy().copy() for r in range(2)], None
+            ph = side_.spec.phys(layer)
+            return ([side_.kv[ph, r].cpu().numpy().copy() for r in range(side_.spec.regions)],
+                    [S.scale_bits(side_.sc[ph, r]).copy() for r in range(side_.spec.regions)]
+                    if side_.sc is not None else None)
+        snaps = {k: (snap(sides[k[0]][0], k[1]), snap(sides[k[0]][1], k[1])) for k in sample}
         step()
-    torch.cuda.synchronize()
-    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
-    marks[0].record(side)
-    for i in range(args.steps):
-        step()
-        marks[i + 1].record(side)
-    torch.cuda.synchronize()
-    span_ms = marks[0].elapsed_time(marks[-1])
+        torch.cuda.synchronize()
+        bad, nbytes = [], 0
+        for gi, l in sample:
+            g = wl.groups[gi]
+            reqs = [O.Request(n, a, b) for n, a, b in zip(tokens, g.src_tables, g.dst_tables)]
+            if isinstance(g.src, W.StateSpec):
+                op = O.make_state_plan(O.StateGeometry(g.src.num_layers, g.src.num_slots, tuple(g.src.slot_bytes)),
+                                       O.StateGeometry(g.dst.num_layers, g.dst.num_slots, tuple(g.dst.slot_bytes)),
+                                       reqs)
+            else:
+                op = O.make_plan(oracle_geom(O, g.src), oracle_geom(O, g.dst), reqs)
+            (skv, ssc), (dkv, dsc) = snaps[(gi, l)]
+            (gkv, gsc), (s_after, _) = snap(sides[gi][1], l), snap(sides[gi][0], l)
+            for r in range(len(skv)):
+                tr = op.triples[r] if isinstance(op, O.StatePlan) else op.triples
+                exp = dkv[r].copy()
+                O.push_region(skv[r], exp, tr)
+                nbytes += exp.size
+                if not np.array_equal(gkv[r], exp):
+                    bad.append(f"group {g.name} layer {l} region {r}")
+                if not np.array_equal(s_after[r], skv[r]):
+                    bad.append(f"group {g.name} layer {l} region {r}: source changed")
+                if ssc is not None:
+                    es = dsc[r].copy()
+                    O.push_scales(ssc[r], es, op.pairs)
+                    if not np.array_equal(gsc[r], es):
+                        bad.append(f"group {g.name} layer {l} region {r} scales")
+        parity = parity_record(bad, "one step through kvx_queue on the fresh pools: every byte of the first and "
+                                    "last layer of each group against the oracle", nbytes)
+        del snaps
+
+    span_ms, per_step, groups_per_step, launches_per_step = step.timed(torch, args.steps, args.warmup)
     ms_per_step = span_ms / args.steps
     gbs = step_bytes * args.steps / (span_ms * 1e-3) / 1e9
-    log(f"span {span_ms:.3f} ms for {args.steps} steps ({ms_per_step * 1e3:.1f} us/step): {gbs:.1f} GB/s "
+    stats = span_stats(per_step)
+    log(f"queue step: span {span_ms:.3f} ms for {args.steps} steps ({ms_per_step * 1e3:.1f} us/step, median "
+        f"{stats['median_ms'] * 1e3:.1f}); {launches_per_step:.2f} launches per step: {gbs:.1f} GB/s "
         f"= {100 * gbs / HBM_PEAK_GBS:.1f}% of {HBM_PEAK_GBS:.0f} GB/s")
-    k_avg_us = ms_per_step * 1e3 / M
+    nl = max(1, round(launches_per_step))
+    k_call_us = step.kernel_us(torch)
 
-    # Per group: kernel durations from dispatch timestamps in a separate pass.
+    # Secondary: one kvx_push_layer launch per model layer.
+    def layer_step():
+        for i, (gi, l) in enumerate(wl.layer_map):
+            kvx.kvx_push_layer(plans[gi], l, ready=ready[i], stream=side)
+    lspan, _ = timed_steps(torch, side, layer_step, args.steps, 2)
+    layer_gbs = step_bytes * args.steps / (lspan * 1e-3) / 1e9
+    log(f"one kvx_push_layer launch per model layer: {layer_gbs:.1f} GB/s")
+
+    # Per group: kvx_push_layer kernel durations from dispatch timestamps.
     n_chk = min(3, args.steps)
     per_group = {gi: [] for gi in range(len(wl.groups))}
     evs = []
@@ -462,10 +684,10 @@ def bench_hybrid(args, torch, kvx, S, W):
         per_group[gi].append(a.elapsed_time(b) * 1e3)
     for gi, g in enumerate(wl.groups):
         us = float(np.mean(per_group[gi]))
-        groups_cfg[gi]["kernel_us_dispatch_stamps"] = round(us, 3)
-        groups_cfg[gi]["kernel_GBs"] = round(gbytes[gi] / (us * 1e-6) / 1e9, 1)
-        log(f"group {g.name}: push kernel {us:.2f} us per launch (dispatch stamps), "
-            f"{groups_cfg[gi]['kernel_GBs']} GB/s")
+        groups_cfg[gi]["push_layer_kernel_us_dispatch_stamps"] = round(us, 3)
+        groups_cfg[gi]["push_layer_kernel_GBs"] = round(gbytes[gi] / (us * 1e-6) / 1e9, 1)
+        log(f"group {g.name}: kvx_push_layer kernel {us:.2f} us per launch (dispatch stamps), "
+            f"{groups_cfg[gi]['push_layer_kernel_GBs']} GB/s")
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -500,16 +722,23 @@ def bench_hybrid(args, torch, kvx, S, W):
                            args.cpu_seconds, setup)
         log(f"cpu baseline: {cpu['value']} GB/s ({cpu['sample']})")
 
+    step.close()
     for p in plans:
         p.close()
     return {
-        "value": gbs, "ms_per_step": ms_per_step, "dtype": "u8",
-        "config": {"workload": wl.name, "seed": wl.seed, "inputs_sha256_16": digest, "model_layers": M, "prompt_tokens": wl.prompt_lens, "tokens_moved": tokens,
+        "value": gbs, "ms_per_step": ms_per_step, "dtype": "u8", "parity": parity, "span": stats,
+        "config": {"workload": wl.name, "seed": wl.seed, "inputs_sha256_16": digest, "model_layers": M,
+                   "prompt_tokens": wl.prompt_lens, "tokens_moved": tokens,
                    "groups": groups_cfg, "bytes_per_step": step_bytes, "host_plan_ms": round(plan_ms, 3),
-                   "step": f"{M} x kvx_push_layer in model order on one side stream, each after its layer's "
-                           f"(fired) event"},
-        "roofline": roofline(step_bytes // M, k_avg_us, "kvx::copy_kernel<0> (kvx_push_layer), all groups",
-                             args.workload, {"note": "bytes and duration averaged over the step's launches"}),
+                   "step": f"{M} x kvx_queue_push in model order, then kvx_queue_flush, on one side stream; each "
+                           f"write goes out after its layer's (fired) event",
+                   "launch_groups_per_step": round(groups_per_step, 3),
+                   "kernel_launches_per_step": round(launches_per_step, 3),
+                   "push_layer_per_launch_GBs": round(layer_gbs, 1)},
+        "roofline": roofline(step_bytes // nl, k_call_us / nl, "kvx::copy_many_kernel<0> (kvx_queue groups)",
+                             args.workload, {"measured": "dispatch timestamps of kvx_push_many_timed over every "
+                                                         "model layer; bytes and duration per launch averaged over "
+                                                         f"its {nl} launches"}),
         "cpu_baseline": cpu,
     }
 
@@ -558,10 +787,22 @@ def counters_run(torch, kvx, plan, side, L, bytes_per_launch, launch=None):
 
 
 def bench_batched(args, torch, kvx, S, W):
-    """batched_push: 64 requests; layer l's push waits for a synthetic compute
-    kernel of layer l running on the compute stream (ALU-bound, one workgroup
-    per CU so that push workgroups co-reside; it writes a canary into layer l's
-    planned source blocks as its last act, so the push must see it)."""
+    """batched_push: 64 requests; layer l's push (kvx_push_layer on a side
+    stream) waits for a synthetic compute kernel of layer l running
+    concurrently on the compute stream.  The compute kernel spins on FMAs and
+    then writes a canary into layer l's planned source blocks, so a push that
+    did not wait for it is caught.  Ways of sharing the chip, each measured
+    (push alone, compute alone, both):
+      bounded    one compute workgroup per CU, so push workgroups co-reside
+      full       the compute grid fills every CU's wave slots (as attention or
+                 a GEMM does)
+      full_split the full compute grid on a stream masked to 7/8 of the CUs,
+                 the push on a stream masked to the other 1/8 (full_split4:
+                 3/4 and 1/4)
+    The line's value is the --compute-mode variant (default: bounded, the
+    footprint of a tiled GEMM or attention kernel whose LDS tiles hold it to
+    one workgroup per CU); every variant is measured and reported in the
+    same line."""
     from decode_kv_cache_amd import bench_support as B
     wl = workload(W, "batched_push", args)
     gs, gd = S.device_side(wl.src, wl.seed, 1), S.device_side(wl.dst, wl.seed, 2)
@@ -583,69 +824,123 @@ def bench_batched(args, torch, kvx, S, W):
     bb = wl.src.block_size * wl.src.num_heads * wl.src.head_dim * wl.src.elem_bytes
     used = np.concatenate([t[:-(-n // wl.src.block_size)] for t, n in zip(wl.src_tables, tokens)])
     blocks = torch.from_numpy(used.astype(np.int32)).cuda()
-    grid = 256
-    sink = torch.empty(grid * 256, dtype=torch.float32, device="cuda")
+    props = torch.cuda.get_device_properties(0)
+    ncu = props.multi_processor_count
+    full_grid = ncu * props.max_threads_per_multi_processor // 256
+    sink = torch.empty(full_grid * 256, dtype=torch.float32, device="cuda")
     ready = [torch.cuda.Event() for _ in range(L)]
+    splits = {"full_split": max(1, ncu // 8), "full_split4": max(1, ncu // 4)}
+    masked = {}
 
-    def compute_layer(l, iters):
+    def streams(mode):
+        # CU masks must be contiguous ranges of CU indices here (the runtime
+        # refuses interleaved ones): the push takes the top `split` CUs
+        if mode not in splits:
+            return compute, side
+        if mode not in masked:
+            split = splits[mode]
+            masked[mode] = (B.CuMaskStream(range(ncu - split), ncu), B.CuMaskStream(range(ncu - split, ncu), ncu))
+        return masked[mode][0].torch, masked[mode][1].torch
+
+    def compute_layer(cs, grid, l, iters):
         B.layer_compute(sink, iters, grid, gs.region(l, 0), gs.region(l, 1), blocks, bb, 0xC0DE0000 + l,
-                        stream=compute)
+                        stream=cs)
 
-    def push_only():
+    def both_step(cs, ps, grid, iters):
         for l in range(L):
-            kvx.kvx_push_layer(plan, l, stream=side)
+            compute_layer(cs, grid, l, iters)
+            ready[l].record(cs)
+            kvx.kvx_push_layer(plan, l, ready=ready[l], stream=ps)
 
-    # push alone
-    push_only()
-    with Timer(torch, side) as t:
-        for _ in range(args.steps):
-            push_only()
-    t_p = t.ms / args.steps
-    # calibrate the compute kernel to about one layer's push time (five
-    # launches timed after two untimed ones, so clock ramp-up does not skew it)
-    probe = 20000
-    for _ in range(2):
-        compute_layer(0, probe)
-    with Timer(torch, compute) as t:
-        for _ in range(5):
-            compute_layer(0, probe)
-    iters = max(1000, int(probe * (t_p / L) / (t.ms / 5)))
+    def measure(mode):
+        cs, ps = streams(mode)
+        grid = ncu if mode == "bounded" else full_grid
 
-    def compute_only():
-        for l in range(L):
-            compute_layer(l, iters)
-    compute_only()
-    with Timer(torch, compute) as t:
-        for _ in range(args.steps):
-            compute_only()
-    t_c = t.ms / args.steps
+        def push_only():
+            for l in range(L):
+                kvx.kvx_push_layer(plan, l, stream=ps)
+        push_only()
+        with Timer(torch, ps) as t:
+            for _ in range(args.steps):
+                push_only()
+        t_p = t.ms / args.steps
+        # calibrate the compute kernel to about one layer's push time (five
+        # launches timed after two untimed ones, so clock ramp-up does not skew it)
+        probe = 4000 if grid > ncu else 20000
+        for _ in range(2):
+            compute_layer(cs, grid, 0, probe)
+        with Timer(torch, cs) as t:
+            for _ in range(5):
+                compute_layer(cs, grid, 0, probe)
+        iters = max(100, int(probe * (t_p / L) / (t.ms / 5)))
 
-    def both():
-        for l in range(L):
-            compute_layer(l, iters)
-            ready[l].record(compute)
-            kvx.kvx_push_layer(plan, l, ready=ready[l], stream=side)
-    both()
-    torch.cuda.synchronize()
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record(compute)
-    for _ in range(args.steps):
-        both()
-    j = torch.cuda.Event()
-    j.record(side)
-    compute.wait_event(j)
-    b.record(compute)
-    torch.cuda.synchronize()
-    t_b = a.elapsed_time(b) / args.steps
+        def compute_only():
+            for l in range(L):
+                compute_layer(cs, grid, l, iters)
+        compute_only()
+        with Timer(torch, cs) as t:
+            for _ in range(args.steps):
+                compute_only()
+        t_c = t.ms / args.steps
+        both_step(cs, ps, grid, iters)
+        torch.cuda.synchronize()
+        marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+        marks[0].record(cs)
+        for i in range(args.steps):
+            both_step(cs, ps, grid, iters)
+            j = torch.cuda.Event()
+            j.record(ps)
+            cs.wait_event(j)
+            marks[i + 1].record(cs)
+        torch.cuda.synchronize()
+        per = np.array([marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps)])
+        t_b = marks[0].elapsed_time(marks[-1]) / args.steps
+        eff = (t_c + t_p - t_b) / min(t_c, t_p)
+        r = {"mode": mode, "compute_grid": grid, "compute_iters": iters,
+             "push_cus": splits.get(mode, ncu), "compute_cus": ncu - splits.get(mode, 0),
+             "push_alone_ms": round(t_p, 3), "push_alone_GBs": round(step_bytes / (t_p * 1e-3) / 1e9, 1),
+             "compute_alone_ms": round(t_c, 3), "overlapped_ms": round(t_b, 3),
+             "overlapped_GBs": round(step_bytes / (t_b * 1e-3) / 1e9, 1),
+             "overlap_efficiency": round(eff, 3), "span": span_stats(per)}
+        log(f"{mode}: push alone {t_p:.2f} ms ({r['push_alone_GBs']} GB/s), compute alone {t_c:.2f} ms, "
+            f"overlapped {t_b:.2f} ms -> {r['overlapped_GBs']} GB/s, overlap efficiency {eff:.2f}")
+        return r, per
+
+    mode = args.compute_mode
+    # Verification step on the fresh pools, in the timed configuration: the
+    # pushes run beside the compute kernels, each gated by its layer's event.
+    parity = None
+    if not args.no_parity:
+        import oracle as O
+        slabs = [0, wl.src.n_phys - 1]
+        dst_snap = snap_layers(S, gd, slabs)
+        cs, ps = streams(mode)
+        both_step(cs, ps, ncu if mode == "bounded" else full_grid, 1000)
+        torch.cuda.synchronize()
+        # aliased logical layers rewrite a slab with the same bytes: the last
+        # push of each slab read the source as its own compute left it, which
+        # is the source as it stands now
+        src_after = snap_layers(S, gs, slabs)
+        parity = parity_push_layers(O, S, wl, gs, gd, src_after, dst_snap, tokens, slabs,
+                                    f"one overlapped step ({mode} compute beside the pushes) on the fresh pools")
+        del dst_snap, src_after
+
+    results = {}
+    for m in ("bounded", "full", "full_split", "full_split4"):
+        if m == mode:
+            continue
+        results[m] = measure(m)[0]
+    results[mode], per = measure(mode)
+    main = results[mode]
+    for pair in masked.values():
+        for s_ in pair:
+            s_.close()
     # canary delivered: layer L-1's pushed destination holds its compute's canary
     d0 = int(wl.dst_tables[0][0])
     got = gd.region(L - 1, 0)[d0 * bb:d0 * bb + 4].cpu().numpy().view(np.uint32)[0]
     canary_ok = bool(got == ((0xC0DE0000 + L - 1) & 0xFFFFFFFF))
+    t_b = main["overlapped_ms"]
     gbs = step_bytes / (t_b * 1e-3) / 1e9
-    push_alone = step_bytes / (t_p * 1e-3) / 1e9
-    eff = (t_c + t_p - t_b) / min(t_c, t_p)
-    log(f"push alone {t_p:.2f} ms ({push_alone:.1f} GB/s), compute alone {t_c:.2f} ms, overlapped {t_b:.2f} ms "
-        f"-> {gbs:.1f} GB/s, overlap efficiency {eff:.2f}, canary {'ok' if canary_ok else 'MISSING'}")
     cpu = None
     if not args.no_cpu_baseline:
         import oracle as O
@@ -660,7 +955,7 @@ def bench_batched(args, torch, kvx, S, W):
         log(f"cpu baseline: {cpu['value']} GB/s")
     plan.close()
     return {
-        "value": gbs, "ms_per_step": t_b, "dtype": "u8",
+        "value": gbs, "ms_per_step": t_b, "dtype": "u8", "parity": parity, "span": span_stats(per),
         "config": {"workload": wl.name, "seed": wl.seed, "inputs_sha256_16": digest, "layers": L,
                    "physical_layer_slabs": wl.src.n_phys,
                    "kv_heads": wl.src.num_heads, "head_dim": wl.src.head_dim, "block_size": wl.src.block_size,
@@ -668,12 +963,16 @@ def bench_batched(args, torch, kvx, S, W):
                    "pool_blocks": wl.src.num_blocks, "merged_runs": nruns, "bytes_per_step": step_bytes,
                    "step": f"{L} x (synthetic compute of layer l on the compute stream, its event, "
                            f"kvx_push_layer(l) on a side stream)",
-                   "push_alone_GBs": round(push_alone, 1), "push_alone_ms": round(t_p, 3),
-                   "compute_alone_ms": round(t_c, 3), "overlapped_ms": round(t_b, 3),
-                   "compute_iters": iters, "compute_grid": grid, "overlap_efficiency": round(eff, 3),
-                   "canary_delivered": canary_ok, "host_plan_ms": round(plan_ms, 2)},
-        "roofline": roofline(rd + wr, t_p * 1e3 / L, "kvx::copy_kernel<0> (kvx_push_layer)", wl.name,
-                             {"note": "push alone, span over its launches"}),
+                   "compute_mode": mode, "cu_sharing_knob": {
+                       "bounded": "compute grid bounded to one workgroup per CU; no CU mask",
+                       "full": "compute grid fills every CU's wave slots; no CU mask",
+                       "full_split": f"CU masks: compute on {ncu - splits['full_split']} CUs, push on "
+                                     f"{splits['full_split']}",
+                       "full_split4": f"CU masks: compute on {ncu - splits['full_split4']} CUs, push on "
+                                      f"{splits['full_split4']}"}[mode],
+                   "variants": results, "canary_delivered": canary_ok, "host_plan_ms": round(plan_ms, 2)},
+        "roofline": roofline(rd + wr, main["push_alone_ms"] * 1e3 / L, "kvx::copy_kernel<0> (kvx_push_layer)",
+                             wl.name, {"note": "push alone on its stream, span over its launches"}),
         "cpu_baseline": cpu,
     }
 
@@ -701,14 +1000,33 @@ def bench_tp4(args, torch, kvx, S, W):
                      launch=lambda l: kvx.kvx_copy_heads(plan, l, rank * nh, 0, nh, stream=side))
         plan.close()
         return None
-    for _ in range(args.warmup):
+    parity = None
+    if not args.no_parity:   # verification step on the fresh pools against the oracle
+        import oracle as O
+        layers = [0, L - 1]
+        pre_s, pre_d = snap_layers(S, gs, layers), snap_layers(S, gd, layers)
         step()
-    with Timer(torch, side) as t:
-        for _ in range(args.steps):
-            step()
-    ms = t.ms / args.steps
+        torch.cuda.synchronize()
+        reqs = [O.Request(n, a, b) for n, a, b in zip(tokens, wl.src_tables, wl.dst_tables)]
+        op = O.make_plan(oracle_geom(O, wl.src), oracle_geom(O, wl.dst), reqs)
+        sr, dr = O.head_rows(op, rank * nh, 0, nh, reqs)
+        bad, nbytes = [], 0
+        for l in layers:
+            for kv in (0, 1):
+                exp = pre_d[l][0][kv].copy()
+                O.copy_heads_region(pre_s[l][0][kv], exp, wl.src.head_dim * wl.src.elem_bytes, sr, dr)
+                got = gd.kv[l, kv].cpu().numpy()
+                nbytes += got.size
+                if not np.array_equal(got, exp):
+                    bad.append(f"layer {l} region {kv}")
+        parity = parity_record(bad, f"one step on the fresh pools: every byte of layers {layers} of the "
+                                    f"consumer against the oracle's head transform (TP rank {rank})", nbytes)
+        del pre_s, pre_d
+    span_ms, per_step = timed_steps(torch, side, step, args.steps, args.warmup)
+    ms = span_ms / args.steps
     gbs = step_bytes / (ms * 1e-3) / 1e9
     log(f"copy_heads: {ms * 1e3:.1f} us per step, {gbs:.1f} GB/s ({100 * gbs / HBM_PEAK_GBS:.1f}%)")
+
     cpu = None
     if not args.no_cpu_baseline:
         import oracle as O
@@ -727,7 +1045,7 @@ def bench_tp4(args, torch, kvx, S, W):
         log(f"cpu baseline: {cpu['value']} GB/s")
     plan.close()
     return {
-        "value": gbs, "ms_per_step": ms, "dtype": "u8",
+        "value": gbs, "ms_per_step": ms, "dtype": "u8", "parity": parity, "span": span_stats(per_step),
         "config": {"workload": wl.name, "seed": wl.seed, "inputs_sha256_16": digest, "layers": L,
                    "src": "NHD, 8 KV heads", "dst": f"HND, {nh} KV heads",
                    "tp_rank": rank, "tp_size": wl.extra["tp_size"], "head_dim": wl.src.head_dim,
@@ -773,16 +1091,62 @@ def bench_multiturn(args, torch, kvx, S, W):
         for _, p in plans:
             p.close()
         return None
+    parity = None
+    if not args.no_parity:   # verification step: turns 2..8 replayed on the oracle for sampled layers
+        import oracle as O
+        layers = [0, L - 1]
+        dsnap, psnap = snap_layers(S, dec, layers), snap_layers(S, pre, layers)
+        step()
+        torch.cuda.synchronize()
+        g = oracle_geom(O, wl.src)
+        state = {l: (psnap[l][0].copy(), psnap[l][1].copy()) for l in layers}
+        for t, _ in plans:
+            reqs = [O.reuse_request(t, ex["growth"], ex["threshold"], ex["decode_tables"][s_],
+                                    ex["prefill_tables"][t][s_]) for s_ in range(ex["sessions"])]
+            op = O.make_plan(g, g, reqs)
+            for l in layers:
+                for kv in (0, 1):
+                    O.push_region(dsnap[l][0][kv], state[l][0][kv], op.triples)
+                    O.push_scales(dsnap[l][1][kv], state[l][1][kv], op.pairs)
+        bad, nbytes = [], 0
+        for l in layers:
+            got = pre.kv[l].cpu().numpy()
+            nbytes += got.size
+            if not np.array_equal(got, state[l][0]):
+                bad.append(f"layer {l} payload")
+            if not np.array_equal(S.scale_bits(pre.sc[l]), state[l][1]):
+                bad.append(f"layer {l} scales")
+            if not np.array_equal(dec.kv[l].cpu().numpy(), dsnap[l][0]):
+                bad.append(f"layer {l}: decode pool changed")
+        parity = parity_record(bad, f"one step (turns {[t for t, _ in plans]}) on the fresh pools: every byte and "
+                                    f"scale of prefill-pool layers {layers} against the oracle's turn-by-turn "
+                                    f"replay", nbytes)
+        del dsnap, psnap, state
+    # per-turn spans: an event between the turns of every step
     for _ in range(args.warmup):
         step()
-    with Timer(torch, side) as t:
-        for _ in range(args.steps):
-            step()
-    ms = t.ms / args.steps
+    torch.cuda.synchronize()
+    nt = len(plans)
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps * nt + 1)]
+    marks[0].record(side)
+    for i in range(args.steps):
+        for j, (_, p) in enumerate(plans):
+            for l in range(L):
+                kvx.kvx_push_layer(p, l, stream=side)
+            marks[i * nt + j + 1].record(side)
+    torch.cuda.synchronize()
+    spans = np.array([marks[k].elapsed_time(marks[k + 1]) for k in range(args.steps * nt)]).reshape(args.steps, nt)
+    per_step = spans.sum(axis=1)
+    ms = marks[0].elapsed_time(marks[-1]) / args.steps
     gbs = step_bytes / (ms * 1e-3) / 1e9
     launches = len(plans) * L
+    turn_bytes = [sum(p.bytes_per_layer()) * L for _, p in plans]
+    per_turn = [{"turn": t, "median_ms": round(float(np.median(spans[:, j])), 4),
+                 "min_ms": round(float(spans[:, j].min()), 4), "p90_ms": round(float(np.percentile(spans[:, j], 90)), 4),
+                 "GBs_at_median": round(turn_bytes[j] / (np.median(spans[:, j]) * 1e-3) / 1e9, 1)}
+                for j, (t, _) in enumerate(plans)]
     log(f"multiturn: {ms:.2f} ms per step (turns {[t for t, _ in plans]}), {gbs:.1f} GB/s "
-        f"({100 * gbs / HBM_PEAK_GBS:.1f}%)")
+        f"({100 * gbs / HBM_PEAK_GBS:.1f}%); per turn median ms {[x['median_ms'] for x in per_turn]}")
     cpu = None
     if not args.no_cpu_baseline:
         import oracle as O
@@ -802,9 +1166,9 @@ def bench_multiturn(args, torch, kvx, S, W):
     for _, p in plans:
         p.close()
     return {
-        "value": gbs, "ms_per_step": ms, "dtype": "u8",
+        "value": gbs, "ms_per_step": ms, "dtype": "u8", "parity": parity, "span": span_stats(per_step),
         "config": {"workload": wl.name, "seed": wl.seed, "inputs_sha256_16": digest, "layers": L,
-                   "kv_heads": wl.src.num_heads, "head_dim": wl.src.head_dim,
+                   "kv_heads": wl.src.num_heads, "head_dim": wl.src.head_dim, "per_turn": per_turn,
                    "block_size": wl.src.block_size, "payload_dtype": wl.src.dtype, "scales": "fp32 per block",
                    "sessions": ex["sessions"], "turns_copied": turns, "threshold_tokens": ex["threshold"],
                    "bytes_per_step": step_bytes,
@@ -837,12 +1201,35 @@ def bench_pack(args, torch, kvx, S, W):
         counters_run(torch, kvx, plan, side, 1, nbytes, launch=lambda _l: step())
         plan.close()
         return None
-    for _ in range(args.warmup):
+    parity = None
+    if not args.no_parity:   # verification step: staging and consumer pool of sampled layers vs the oracle
+        import oracle as O
+        layers = [0, 37, L - 1]
+        pre_s, pre_d = snap_layers(S, gs, layers), snap_layers(S, gd, layers)
         step()
-    with Timer(torch, side) as t:
-        for _ in range(args.steps):
-            step()
-    ms = t.ms / args.steps
+        torch.cuda.synchronize()
+        g1s, g1d = oracle_geom(O, wl.src, 1), oracle_geom(O, wl.dst, 1)
+        op = O.make_plan(g1s, g1d, [O.Request(n, a, b) for n, a, b in zip(tokens, wl.src_tables, wl.dst_tables)])
+        per = nbytes // L
+        bad, cmp = [], 0
+        for l in layers:
+            src1 = O.Pool(g1s, pre_s[l][0][None], None)
+            exp_stg = O.pack(src1, op, 0, 1)
+            got_stg = stg[l * per:(l + 1) * per].cpu().numpy()
+            cmp += got_stg.size
+            if not np.array_equal(got_stg, exp_stg):
+                bad.append(f"layer {l} staging")
+            exp = O.Pool(g1d, pre_d[l][0][None].copy(), None)
+            O.unpack(exp_stg, exp, op, 0, 1)
+            got = gd.kv[l].cpu().numpy()
+            cmp += got.size
+            if not np.array_equal(got, exp.kv[0]):
+                bad.append(f"layer {l} consumer pool")
+        parity = parity_record(bad, f"one step on the fresh pools: staging of layers {layers} against the oracle's "
+                                    f"pack, their consumer regions against the oracle's unpack", cmp)
+        del pre_s, pre_d
+    span_ms, per_step = timed_steps(torch, side, step, args.steps, args.warmup)
+    ms = span_ms / args.steps
     gbs = step_bytes / (ms * 1e-3) / 1e9
     log(f"pack+unpack: {ms * 1e3:.1f} us per step for {nbytes} staged bytes, {gbs:.1f} GB/s")
     cpu = None
@@ -865,7 +1252,7 @@ def bench_pack(args, torch, kvx, S, W):
     assert not wl.src.has_scales
     launches = 2 * -(-L // 32)
     return {
-        "value": gbs, "ms_per_step": ms, "dtype": "u8",
+        "value": gbs, "ms_per_step": ms, "dtype": "u8", "parity": parity, "span": span_stats(per_step),
         "config": {"workload": "pack_unpack", "seed": wl.seed, "inputs_sha256_16": digest, "geometry": "qwen32b_push", "layers": L, "staging_bytes": nbytes,
                    "bytes_per_step": step_bytes,
                    "step": f"kvx_pack of {L} layers then kvx_unpack of {L} layers ({launches} launches)"},
@@ -937,7 +1324,18 @@ def bench_xfer(args, torch, kvx, S, W):
         x.close()
         return ms, t_host
 
-    run(0)
+    parity = None
+    if not args.no_parity:   # the first run on the fresh pools: sampled slabs against the oracle
+        import oracle as O
+        slabs = [0, wl.src.n_phys - 1]
+        pre_s, pre_d = snap_layers(S, gs, slabs), snap_layers(S, gd, slabs)
+        run(0)
+        torch.cuda.synchronize()
+        parity = parity_push_layers(O, S, wl, gs, gd, pre_s, pre_d, tokens, slabs,
+                                    "the first run through the transfer state machine on the fresh pools")
+        del pre_s, pre_d
+    else:
+        run(0)
     res = [run(i + 1) for i in range(args.steps)]
     ms = float(np.mean([r[0] for r in res]))
     host_us = float(np.mean([r[1] for r in res])) * 1e6 / (R * L)
@@ -954,7 +1352,7 @@ def bench_xfer(args, torch, kvx, S, W):
         f"one plan per layer without the state machine: {raw:.1f} GB/s")
     ref.close()
     return {
-        "value": gbs, "ms_per_step": ms, "dtype": "u8",
+        "value": gbs, "ms_per_step": ms, "dtype": "u8", "parity": parity, "span": span_stats([r[0] for r in res]),
         "config": {"workload": "xfer_pipeline", "seed": wl.seed, "inputs_sha256_16": digest, "geometry": "batched_push", "requests": R, "layers": L,
                    "bytes_per_step": step_bytes,
                    "step": f"{R} requests x {L} layers through kvx_xfer (half registered after the forward pass), "
@@ -974,6 +1372,9 @@ def main():
     ap.add_argument("--workload", default="qwen32b_push", choices=WORKLOAD_NAMES)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-parity", action="store_true", help="skip the verification step against the oracle")
+    ap.add_argument("--compute-mode", default="bounded", choices=["bounded", "full", "full_split", "full_split4"],
+                    help="batched_push: how the compute stand-in shares the chip with the push")
     ap.add_argument("--counters", action="store_true",
                     help="short run for rocprofv3 --pmc: a 1 GiB plain copy (calibration) x3, then 2 steps")
     ap.add_argument("--seed", type=int, default=None, help="workload seed (default: the workload's own)")
@@ -1017,6 +1418,8 @@ def main():
         "warmup": args.warmup, "ms_per_step": round(r["ms_per_step"], 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": r["dtype"], "data": "synthetic",
         "pct_of_hbm_peak": round(100 * r["value"] / HBM_PEAK_GBS, 2),
+        "parity": (r.get("parity") or {}).get("result", "skipped"), "parity_detail": r.get("parity"),
+        "span": r.get("span"), "ceiling": r.get("ceiling"),
         "config": r["config"], "roofline": r["roofline"], "cpu_baseline": r["cpu_baseline"],
     }
     print(json.dumps(out), flush=True)

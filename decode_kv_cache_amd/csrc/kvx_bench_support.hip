@@ -2,12 +2,14 @@
 // transfer path): a synthetic ALU-bound compute kernel standing in for a
 // model layer (it writes a canary into the layer's source KV blocks when it
 // finishes, so a push that does not wait for it is caught), a plain
-// contiguous copy (the practical HBM ceiling and the counter calibration
-// reference) and a cache-flush fill.
+// contiguous copy (the counter calibration reference), a plain segment copy
+// in the push kernel's shapes (the practical ceiling of the same bytes
+// without a block table) and a cache-flush fill.
 //
 // All entry points enqueue on `stream` and return a hipError_t value (0 on
 // success).
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -65,6 +67,35 @@ __global__ __launch_bounds__(kThreads) void copy_kernel(v4u* __restrict__ d, con
   for (; i < nvec; i += stride) __builtin_nontemporal_store(__builtin_nontemporal_load(s + i), d + i);
 }
 
+// Plain copy of `nseg` segments of seg_bytes each, segment i from src[i] to
+// dst[i], in the push kernel's workgroup shapes: T lanes keeping V 16-byte
+// vectors each in flight, one T x V x 16-byte chunk per workgroup, all of a
+// lane's loads issued before its first store, stores with the push kernel's
+// cache policy for that shape (SA: nt for one-wave chunks, nt sc0 sc1 for
+// four-wave ones).  The practical ceiling of the same bytes moved without
+// any block table.
+typedef const __attribute__((address_space(4))) uint64_t* ConstU64;
+template <int T, int V, int SA>
+__global__ __launch_bounds__(T) void segment_copy_kernel(const uint64_t* src, const uint64_t* dst, int64_t seg_bytes,
+                                                         int64_t chunks_per_seg) {
+  constexpr int kChunk = T * V * 16;
+  const int64_t x = blockIdx.x;
+  const int64_t seg = x / chunks_per_seg;
+  const int64_t off = (x - seg * chunks_per_seg) * kChunk;
+  const int64_t rest = seg_bytes - off;
+  const int len = rest < kChunk ? int(rest) : kChunk;
+  const uint64_t s = ((ConstU64)src)[seg], d = ((ConstU64)dst)[seg];
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(s + uint64_t(off)), (short)0, len, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rd =
+      __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(d + uint64_t(off)), (short)0, len, 0x00020000);
+  v4u r[V];
+#pragma unroll
+  for (int k = 0; k < V; ++k) r[k] = __builtin_amdgcn_raw_buffer_load_b128(rs, (threadIdx.x + k * T) * 16, 0, 2);
+#pragma unroll
+  for (int k = 0; k < V; ++k) __builtin_amdgcn_raw_buffer_store_b128(r[k], rd, (threadIdx.x + k * T) * 16, 0, SA);
+}
+
 __global__ __launch_bounds__(kThreads) void fill_kernel(v4u* d, int64_t nvec, uint32_t value) {
   const int64_t stride = int64_t(gridDim.x) * kThreads;
   const v4u v = {value, value, value, value};
@@ -95,6 +126,37 @@ int kvxb_copy(void* dst, const void* src, int64_t bytes, int32_t grid, hipStream
                      static_cast<const v4u*>(src), bytes / 16);
   return int(hipGetLastError());
 }
+
+// Plain copy of nseg segments: segment i copies seg_bytes from src_ptrs[i]
+// to dst_ptrs[i] (device arrays of nseg device addresses, 16-B aligned;
+// seg_bytes a multiple of 16).  shape 0: one-wave workgroups of 32 KiB
+// chunks; shape 1: four-wave workgroups of 4 KiB chunks.
+int kvxb_copy_segments(const uint64_t* src_ptrs, const uint64_t* dst_ptrs, int32_t nseg, int64_t seg_bytes,
+                       int32_t shape, hipStream_t stream) {
+  if (nseg < 1 || seg_bytes < 16 || (seg_bytes & 15) || !src_ptrs || !dst_ptrs || shape < 0 || shape > 1)
+    return int(hipErrorInvalidValue);
+  const int64_t chunk = shape == 0 ? 32768 : 4096;
+  const int64_t per = (seg_bytes + chunk - 1) / chunk;
+  if (per * nseg > (int64_t(1) << 31) - 1) return int(hipErrorInvalidValue);
+  const dim3 grid(unsigned(per * nseg));
+  if (shape == 0)
+    hipLaunchKernelGGL((segment_copy_kernel<64, 32, 2>), grid, dim3(64), 0, stream, src_ptrs, dst_ptrs, seg_bytes,
+                       per);
+  else
+    hipLaunchKernelGGL((segment_copy_kernel<256, 1, 19>), grid, dim3(256), 0, stream, src_ptrs, dst_ptrs,
+                       seg_bytes, per);
+  return int(hipGetLastError());
+}
+
+// A stream at the default priority restricted to the compute units whose bits
+// are set in mask[0..words) (bit i of word w = CU 32 w + i), for splitting
+// the chip between the compute stand-in and the push.
+int kvxb_stream_create_cu_mask(const uint32_t* mask, int32_t words, hipStream_t* out) {
+  if (!mask || words < 1 || !out) return int(hipErrorInvalidValue);
+  return int(hipExtStreamCreateWithCUMask(out, uint32_t(words), mask));
+}
+
+int kvxb_stream_destroy(hipStream_t s) { return int(hipStreamDestroy(s)); }
 
 // Fill dst[0, bytes) with a 32-bit pattern (used to flush L2 and MALL).
 int kvxb_fill(void* dst, int64_t bytes, uint32_t value, hipStream_t stream) {

@@ -167,7 +167,10 @@ int check_push_pair(const kvx_plan_t* plan, int32_t layer, const char* fn, int32
 
 // Enqueue the pushes of already validated pairs on `stream` (after each
 // plan's upload), batched into as few launches as kvx_push_many uses; no
-// ready wait.
-int push_batch(const kvx_plan_t* const* plans, const int32_t* layers, int32_t n, hipStream_t stream);
+// ready wait.  `started` / `finished` (nullable) receive the first launch's
+// start and the last launch's end timestamps; *launches (nullable) grows by
+// the kernel launches enqueued.
+int push_batch(const kvx_plan_t* const* plans, const int32_t* layers, int32_t n, hipStream_t stream,
+               hipEvent_t started = nullptr, hipEvent_t finished = nullptr, int64_t* launches = nullptr);
 
 }  // namespace kvx

@@ -262,7 +262,7 @@ static unsigned grid_y(const kvx_plan_t* p) { return p->nlists == 1 ? unsigned(p
 // lists.
 template <int MODE, int T, int V>
 static int launch_copy_shape(kvx_plan_t* p, CopyArgs a, int64_t scale_slots, hipStream_t s, hipEvent_t started,
-                             hipEvent_t finished) {
+                             hipEvent_t finished, int64_t* launches) {
   const int64_t np = int64_t(p->pieces.size());
   const bool scales = a.in_sc[0] != nullptr;
   const unsigned gy = grid_y(p);
@@ -273,6 +273,7 @@ static int launch_copy_shape(kvx_plan_t* p, CopyArgs a, int64_t scale_slots, hip
   int64_t first = 0;
   // Pieces in chunks of kMaxGridX; the scale workgroups ride on the last chunk.
   do {
+    if (launches) ++*launches;
     const int64_t cnt = std::min<int64_t>(np - first, kMaxGridX);
     const bool last = first + cnt >= np;
     a.pieces = p->d_pieces + first;
@@ -295,35 +296,39 @@ static int launch_copy_shape(kvx_plan_t* p, CopyArgs a, int64_t scale_slots, hip
 
 template <int MODE>
 static int launch_copy(kvx_plan_t* p, CopyArgs a, int64_t scale_slots, hipStream_t s,
-                       hipEvent_t started = nullptr, hipEvent_t finished = nullptr) {
+                       hipEvent_t started = nullptr, hipEvent_t finished = nullptr, int64_t* launches = nullptr) {
   switch (p->shape) {
     case kShapeLong:
-      return launch_copy_shape<MODE, kShapes[kShapeLong].threads, kShapes[kShapeLong].vecs>(p, a, scale_slots, s,
-                                                                                           started, finished);
+      return launch_copy_shape<MODE, kShapes[kShapeLong].threads, kShapes[kShapeLong].vecs>(
+          p, a, scale_slots, s, started, finished, launches);
     case kShapeLongSmall:
       return launch_copy_shape<MODE, kShapes[kShapeLongSmall].threads, kShapes[kShapeLongSmall].vecs>(
-          p, a, scale_slots, s, started, finished);
+          p, a, scale_slots, s, started, finished, launches);
     default:
-      return launch_copy_shape<MODE, kShapes[kShapeFine].threads, kShapes[kShapeFine].vecs>(p, a, scale_slots, s,
-                                                                                           started, finished);
+      return launch_copy_shape<MODE, kShapes[kShapeFine].threads, kShapes[kShapeFine].vecs>(
+          p, a, scale_slots, s, started, finished, launches);
   }
 }
 
+// `started` / `finished` (nullable): timestamps of this launch's dispatch
+// (hipExtLaunchKernelGGL adds no queue packets for them).
 template <int MODE>
-static void launch_many(const ManyArgs& m, int32_t shape, int64_t total, unsigned gy, hipStream_t s) {
+static void launch_many(const ManyArgs& m, int32_t shape, int64_t total, unsigned gy, hipStream_t s,
+                        hipEvent_t started, hipEvent_t finished) {
   const dim3 grid(unsigned(total), gy);
   switch (shape) {
     case kShapeLong:
-      hipLaunchKernelGGL((copy_many_kernel<MODE, kShapes[kShapeLong].threads, kShapes[kShapeLong].vecs>), grid,
-                         dim3(kShapes[kShapeLong].threads), 0, s, m);
+      hipExtLaunchKernelGGL((copy_many_kernel<MODE, kShapes[kShapeLong].threads, kShapes[kShapeLong].vecs>), grid,
+                            dim3(kShapes[kShapeLong].threads), 0, s, started, finished, 0u, m);
       break;
     case kShapeLongSmall:
-      hipLaunchKernelGGL((copy_many_kernel<MODE, kShapes[kShapeLongSmall].threads, kShapes[kShapeLongSmall].vecs>),
-                         grid, dim3(kShapes[kShapeLongSmall].threads), 0, s, m);
+      hipExtLaunchKernelGGL(
+          (copy_many_kernel<MODE, kShapes[kShapeLongSmall].threads, kShapes[kShapeLongSmall].vecs>), grid,
+          dim3(kShapes[kShapeLongSmall].threads), 0, s, started, finished, 0u, m);
       break;
     default:
-      hipLaunchKernelGGL((copy_many_kernel<MODE, kShapes[kShapeFine].threads, kShapes[kShapeFine].vecs>), grid,
-                         dim3(kShapes[kShapeFine].threads), 0, s, m);
+      hipExtLaunchKernelGGL((copy_many_kernel<MODE, kShapes[kShapeFine].threads, kShapes[kShapeFine].vecs>), grid,
+                            dim3(kShapes[kShapeFine].threads), 0, s, started, finished, 0u, m);
   }
 }
 
@@ -338,7 +343,10 @@ static void launch_many(const ManyArgs& m, int32_t shape, int64_t total, unsigne
 template <int MODE>
 class ManyBatch {
  public:
-  explicit ManyBatch(hipStream_t s) : s_(s) {}
+  // With `started` / `finished`, the first launch records its start into
+  // `started` and every launch its end into `finished` (the last one wins).
+  explicit ManyBatch(hipStream_t s, hipEvent_t started = nullptr, hipEvent_t finished = nullptr)
+      : s_(s), started_(started), finished_(finished) {}
 
   // Whether plan p's pieces fit a batched launch at all.
   static bool fits(const kvx_plan_t* p) {
@@ -380,7 +388,9 @@ class ManyBatch {
       if (!keep) m_.e[j].pieces = stream_[j];
       total += int64_t(np_[j]) << m_.e[j].shift;
     }
-    launch_many<MODE>(m_, keep ? shape_ : int32_t(kShapeFine), total, gy_, s_);
+    launch_many<MODE>(m_, keep ? shape_ : int32_t(kShapeFine), total, gy_, s_, started_, finished_);
+    started_ = nullptr;
+    ++launches_;
     m_.n = 0;
     n32_ = 0;
     fine_ = 0;
@@ -388,8 +398,21 @@ class ManyBatch {
     return check_launch("kvx copy_many kernel launch");
   }
 
+  // A launch outside the batch (a pair with scales) takes over the start
+  // timestamp when it comes first.
+  hipEvent_t take_started() {
+    hipEvent_t e = started_;
+    started_ = nullptr;
+    return e;
+  }
+  hipEvent_t finished() const { return finished_; }
+  // Kernel launches enqueued by flush so far.
+  int64_t launches() const { return launches_; }
+
  private:
   hipStream_t s_;
+  hipEvent_t started_, finished_;
+  int64_t launches_ = 0;
   ManyArgs m_{};
   int64_t n32_ = 0;   // 32 KiB pieces in the launch (all regions)
   int64_t fine_ = 0;  // workgroups of the launch in the 4 KiB shape
@@ -428,14 +451,16 @@ int check_push_pair(const kvx_plan_t* p, int32_t layer, const char* fn, int32_t 
   return KVX_OK;
 }
 
-int push_batch(const kvx_plan_t* const* plans, const int32_t* layers, int32_t n, hipStream_t stream) {
+int push_batch(const kvx_plan_t* const* plans, const int32_t* layers, int32_t n, hipStream_t stream,
+               hipEvent_t started, hipEvent_t finished, int64_t* launches) {
+  int64_t alone = 0;
   for (int32_t i = 0; i < n; ++i) {
     const int rc = enqueue_waits(const_cast<kvx_plan_t*>(plans[i]), nullptr, stream);
     if (rc) return rc;
   }
   // Pairs without scales share launches (ManyBatch); a pair with scales, or
   // too many pieces for one launch, is launched alone, in order.
-  ManyBatch<kPush> batch(stream);
+  ManyBatch<kPush> batch(stream, started, finished);
   for (int32_t i = 0; i < n; ++i) {
     kvx_plan_t* p = const_cast<kvx_plan_t*>(plans[i]);
     int rc;
@@ -443,7 +468,8 @@ int push_batch(const kvx_plan_t* const* plans, const int32_t* layers, int32_t n,
       if (p->pieces.empty() && p->blocks.empty()) continue;
       rc = batch.flush();
       if (rc) return rc;
-      rc = launch_copy<kPush>(p, push_args(p, layers[i]), int64_t(p->blocks.size()), stream);
+      rc = launch_copy<kPush>(p, push_args(p, layers[i]), int64_t(p->blocks.size()), stream,
+                              batch.take_started(), batch.finished(), &alone);
       if (rc) return rc;
       continue;
     }
@@ -451,7 +477,9 @@ int push_batch(const kvx_plan_t* const* plans, const int32_t* layers, int32_t n,
     rc = batch.add(p, a.in, a.out);
     if (rc) return rc;
   }
-  return batch.flush();
+  const int rc = batch.flush();
+  if (launches) *launches += alone + batch.launches();
+  return rc;
 }
 
 }  // namespace kvx
@@ -480,6 +508,11 @@ int kvx_push_layer_timed(const kvx_plan_t* cp, int32_t layer, hipEvent_t ready, 
 
 int kvx_push_many(const kvx_plan_t* const* plans, const int32_t* layers, int32_t n, hipEvent_t ready,
                   hipStream_t stream) {
+  return kvx_push_many_timed(plans, layers, n, ready, stream, nullptr, nullptr);
+}
+
+int kvx_push_many_timed(const kvx_plan_t* const* plans, const int32_t* layers, int32_t n, hipEvent_t ready,
+                        hipStream_t stream, hipEvent_t started, hipEvent_t finished) {
   if (n < 0 || (n > 0 && (!plans || !layers))) return fail(KVX_E_INVAL, "kvx_push_many: bad arguments");
   for (int32_t i = 0; i < n; ++i) {
     int rc = check_push_pair(plans[i], layers[i], "kvx_push_many", i);
@@ -487,7 +520,7 @@ int kvx_push_many(const kvx_plan_t* const* plans, const int32_t* layers, int32_t
   }
   int rc = wait_event(ready, stream);
   if (rc) return rc;
-  return kvx::push_batch(plans, layers, n, stream);
+  return kvx::push_batch(plans, layers, n, stream, started, finished);
 }
 
 static int staging_call(const kvx_plan_t* cp, int32_t l0, int32_t l1, const void* staging,

@@ -45,7 +45,7 @@ struct kvx_queue {
   std::deque<Entry> pending;
   hipEvent_t done[kInflight] = {};  // recorded behind each launch group, a ring, oldest at `head`
   int head = 0, busy = 0;
-  int64_t writes = 0, groups = 0;
+  int64_t writes = 0, groups = 0, launches = 0;
 };
 
 namespace kvx {
@@ -101,25 +101,37 @@ int retire(kvx_queue* q) {
   return KVX_OK;
 }
 
-// Mark the end of a launch group: an event behind everything enqueued so
-// far.  When the ring is full its oldest group is dropped from tracking
-// (stream order: it finishes before this one).
-int record_group(kvx_queue* q) {
+// The event that will mark the end of the next launch group.  When the ring
+// is full its oldest group is dropped from tracking (stream order: it
+// finishes before the next one).
+hipEvent_t next_done(kvx_queue* q) {
   if (q->busy == kInflight) {
     q->head = (q->head + 1) % kInflight;
     --q->busy;
   }
-  const int slot = (q->head + q->busy) % kInflight;
-  const hipError_t e = hipEventRecord(q->done[slot], q->stream);
-  if (e != hipSuccess) return fail_hip(e, "kvx_queue: hipEventRecord");
-  ++q->busy;
-  ++q->groups;
-  return KVX_OK;
+  return q->done[(q->head + q->busy) % kInflight];
 }
 
-int launch(kvx_queue* q, const std::vector<const kvx_plan_t*>& plans, const std::vector<int32_t>& layers) {
-  if (plans.empty()) return KVX_OK;
-  return push_batch(plans.data(), layers.data(), int32_t(plans.size()), q->stream);
+// Enqueue a group's launches.  With `done`, the group's last kernel records
+// its end into it from its own dispatch (no marker packet behind it); a
+// group that launched nothing records it on the stream instead.
+int launch(kvx_queue* q, const std::vector<const kvx_plan_t*>& plans, const std::vector<int32_t>& layers,
+           hipEvent_t done) {
+  const int64_t before = q->launches;
+  if (!plans.empty()) {
+    const int rc = push_batch(plans.data(), layers.data(), int32_t(plans.size()), q->stream, nullptr, done,
+                              &q->launches);
+    if (rc) return rc;
+  }
+  if (done) {
+    if (q->launches == before) {
+      const hipError_t e = hipEventRecord(done, q->stream);
+      if (e != hipSuccess) return fail_hip(e, "kvx_queue: hipEventRecord");
+    }
+    ++q->busy;
+    ++q->groups;
+  }
+  return KVX_OK;
 }
 
 void drop_pending(kvx_queue* q) {
@@ -149,9 +161,7 @@ int pump(kvx_queue* q) {
       layers.push_back(q->pending[i].layer);
     }
     q->pending.erase(q->pending.begin(), q->pending.begin() + std::ptrdiff_t(n));
-    rc = launch(q, plans, layers);
-    if (rc) return rc;
-    rc = record_group(q);
+    rc = launch(q, plans, layers, next_done(q));
     if (rc) return rc;
   }
   return KVX_OK;
@@ -171,7 +181,7 @@ int flush(kvx_queue* q) {
     const int r = entry_ready(q, e);
     if (r < 0) return -r;
     if (r == 0) {
-      rc = launch(q, plans, layers);
+      rc = launch(q, plans, layers, nullptr);
       if (rc) return rc;
       plans.clear();
       layers.clear();
@@ -183,9 +193,7 @@ int flush(kvx_queue* q) {
     plans.push_back(e.plan);
     layers.push_back(e.layer);
   }
-  rc = launch(q, plans, layers);
-  if (rc) return rc;
-  return record_group(q);
+  return launch(q, plans, layers, next_done(q));
 }
 
 }  // namespace
@@ -207,12 +215,12 @@ int kvx_queue_create(hipStream_t stream, kvx_queue** out) {
     return fail_hip(e, "kvx_queue_create: hipStreamCreateWithFlags");
   }
   for (int i = 0; i < kInflight; ++i) {
-    e = hipEventCreateWithFlags(&q->done[i], hipEventDisableTiming);
+    e = hipEventCreate(&q->done[i]);   // timing enabled: a kernel dispatch records into it
     if (e != hipSuccess) {
       for (int j = 0; j < i; ++j) (void)hipEventDestroy(q->done[j]);
       (void)hipStreamDestroy(q->aux);
       delete q;
-      return fail_hip(e, "kvx_queue_create: hipEventCreateWithFlags");
+      return fail_hip(e, "kvx_queue_create: hipEventCreate");
     }
   }
   *out = q;
@@ -251,12 +259,13 @@ int kvx_queue_flush(kvx_queue* q) {
   return rc;
 }
 
-int kvx_queue_stats(const kvx_queue* q, int64_t* writes, int64_t* groups) {
+int kvx_queue_stats(const kvx_queue* q, int64_t* writes, int64_t* groups, int64_t* launches) {
   if (!q || !writes || !groups) return fail(KVX_E_INVAL, "kvx_queue_stats: null argument");
   kvx_queue* m = const_cast<kvx_queue*>(q);
   std::lock_guard<std::mutex> lk(m->mu);
   *writes = m->writes;
   *groups = m->groups;
+  if (launches) *launches = m->launches;
   return KVX_OK;
 }
 

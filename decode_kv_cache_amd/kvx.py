@@ -75,6 +75,7 @@ _SIGS = {
     "kvx_push_layer": (C.c_int, [_P, _I32, _P, _P]),
     "kvx_push_layer_timed": (C.c_int, [_P, _I32, _P, _P, _P, _P]),
     "kvx_push_many": (C.c_int, [_P, _P, _I32, _P, _P]),
+    "kvx_push_many_timed": (C.c_int, [_P, _P, _I32, _P, _P, _P, _P]),
     "kvx_staging_bytes": (C.c_int, [_P, _I32, _I32, C.POINTER(_I64)]),
     "kvx_pack": (C.c_int, [_P, _I32, _I32, _P, _I64, _P]),
     "kvx_unpack": (C.c_int, [_P, _I32, _I32, _P, _I64, _P]),
@@ -82,7 +83,7 @@ _SIGS = {
     "kvx_queue_create": (C.c_int, [_P, C.POINTER(_P)]),
     "kvx_queue_push": (C.c_int, [_P, _P, _I32, _P]),
     "kvx_queue_flush": (C.c_int, [_P]),
-    "kvx_queue_stats": (C.c_int, [_P, C.POINTER(_I64), C.POINTER(_I64)]),
+    "kvx_queue_stats": (C.c_int, [_P, C.POINTER(_I64), C.POINTER(_I64), C.POINTER(_I64)]),
     "kvx_queue_destroy": (C.c_int, [_P]),
 }
 _D = C.c_double
@@ -431,6 +432,22 @@ def kvx_push_many(plans: Sequence[Plan], layers: Sequence[int], ready=None, stre
                                                 _stream(stream)))
 
 
+def kvx_push_many_timed(plans: Sequence[Plan], layers: Sequence[int], started, finished, ready=None,
+                        stream=None) -> None:
+    """kvx_push_many with its launches' start and end dispatch timestamps
+    recorded into two timing-enabled torch.cuda.Event objects."""
+    n = len(plans)
+    if len(layers) != n:
+        raise ValueError("one layer per plan")
+    for e in (started, finished):
+        if e is not None and not e.cuda_event:
+            e.record(torch.cuda.current_stream())
+    hp = (C.c_void_p * max(n, 1))(*[p.handle for p in plans])
+    ly = np.ascontiguousarray(layers, dtype=np.int32)
+    _check("kvx_push_many_timed", lib().kvx_push_many_timed(hp, ly.ctypes.data if n else None, n, _event(ready),
+                                                            _stream(stream), _event(started), _event(finished)))
+
+
 def kvx_staging_bytes(plan: Plan, l0: int, l1: int) -> int:
     b = C.c_int64()
     _check("kvx_staging_bytes", lib().kvx_staging_bytes(plan.handle, l0, l1, C.byref(b)))
@@ -475,9 +492,13 @@ class Queue:
 
     def stats(self):
         """(writes queued, launch groups enqueued) so far."""
-        w, g = C.c_int64(), C.c_int64()
-        _check("kvx_queue_stats", lib().kvx_queue_stats(self.handle, C.byref(w), C.byref(g)))
-        return w.value, g.value
+        return self.stats3()[:2]
+
+    def stats3(self):
+        """(writes queued, launch groups enqueued, kernel launches) so far."""
+        w, g, n = C.c_int64(), C.c_int64(), C.c_int64()
+        _check("kvx_queue_stats", lib().kvx_queue_stats(self.handle, C.byref(w), C.byref(g), C.byref(n)))
+        return w.value, g.value, n.value
 
     def close(self) -> None:
         if getattr(self, "handle", None):

@@ -353,6 +353,15 @@ int kvx_push_layer_timed(const kvx_plan_t* plan, int32_t layer, hipEvent_t ready
 int kvx_push_many(const kvx_plan_t* const* plans, const int32_t* layers, int32_t n, hipEvent_t ready,
                   hipStream_t stream);
 
+/* kvx_push_many whose first kernel records its start timestamp into
+ * `started` and whose last kernel records its end into `finished` (events
+ * with timing enabled; either may be NULL), taken from the dispatches
+ * themselves as in kvx_push_layer_timed: the elapsed time between them spans
+ * the call's launches.  Nothing launched leaves both untouched.  Same errors
+ * as kvx_push_many. */
+int kvx_push_many_timed(const kvx_plan_t* const* plans, const int32_t* layers, int32_t n, hipEvent_t ready,
+                        hipStream_t stream, hipEvent_t started, hipEvent_t finished);
+
 /*
  * Layer write queue of one stream.  In push mode the producer queues each
  * layer's write right after that layer's compute; the write goes out once
@@ -403,9 +412,10 @@ int kvx_queue_push(kvx_queue* q, const kvx_plan_t* plan, int32_t layer, hipEvent
  * (the writes still queued are dropped). */
 int kvx_queue_flush(kvx_queue* q);
 
-/* Writes queued so far and launch groups enqueued so far (each group is one
- * kvx_push_many launch sequence).  Errors: INVAL (null argument). */
-int kvx_queue_stats(const kvx_queue* q, int64_t* writes, int64_t* groups);
+/* Writes queued so far, launch groups enqueued so far (each group is one
+ * kvx_push_many launch sequence) and the kernel launches of those groups
+ * (`launches` may be NULL).  Errors: INVAL (null q, writes or groups). */
+int kvx_queue_stats(const kvx_queue* q, int64_t* writes, int64_t* groups, int64_t* launches);
 
 /* Flush, then free the queue.  NULL is a no-op (KVX_OK).  Returns the
  * flush's status; the queue is freed in every case. */

@@ -1,7 +1,8 @@
 """CPU oracle for paged-KV block transfer -- TEST INFRASTRUCTURE ONLY.
 
-Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
-``bench.py`` may import this package.  The HIP library never routes through
+Only ``tests/``, ``__graft_entry__.smoke()`` and the oracle leg of ``bench.py``
+(its verification step against the timed path, and its ``cpu_baseline``) may
+import this package.  The HIP library never routes through
 it, and it imports nothing from the HIP library.  See ``kv_oracle`` for the
 definitions and the passages of the pages each one follows.
 """

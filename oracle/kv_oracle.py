@@ -2,7 +2,8 @@
 
 TEST INFRASTRUCTURE ONLY.  Nothing in the product path may import, call or
 execute this module: only ``tests/``, ``__graft_entry__.smoke()`` and the
-``cpu_baseline`` leg of ``bench.py`` use it.  It shares no code with the HIP
+oracle leg of ``bench.py`` (the verification step before timing, and the
+``cpu_baseline``) use it.  It shares no code with the HIP
 library (``decode_kv_cache_amd``) and imports nothing from it.
 
 Sources (the pages this follows):
