@@ -133,13 +133,13 @@ def oracle_pools(wl, gs, gd, layers):
     return pool(wl.src, gs), pool(wl.dst, gd)
 
 
-def steady_plan_ms(kvx, src, dst, tokens, src_tables, dst_tables, stream, reps=5):
+def steady_plan_ms(kvx, src, dst, tokens, src_tables, dst_tables, stream, reps=5, runs=False):
     """Median host time of kvx_plan (build, upload enqueue) once the process
     is warm; the first plan of a process also pays one-time runtime set-up."""
     ts = []
     for _ in range(reps):
         t0 = time.perf_counter()
-        p = kvx.kvx_plan(src, dst, tokens, src_tables, dst_tables, stream=stream)
+        p = kvx.kvx_plan(src, dst, tokens, src_tables, dst_tables, runs=runs, stream=stream)
         ts.append((time.perf_counter() - t0) * 1e3)
         p.close()
     return float(np.median(ts))
@@ -235,6 +235,23 @@ def span_stats(per_step_ms) -> dict:
     return {"median_ms": round(float(np.median(a)), 4), "min_ms": round(float(a.min()), 4),
             "p90_ms": round(float(np.percentile(a, 90)), 4), "mean_ms": round(float(a.mean()), 4),
             "steps": int(a.size)}
+
+
+def worklist_bytes(plan) -> int:
+    """Device work-list bytes a plan uploads: 32 B per cut piece (twice for a
+    one-wave plan, which keeps a destination-ordered copy), or two run tables
+    of 16 B per triple plus their run indexes; 16 B per planned block either
+    way (the scale copies' block pairs)."""
+    sh = plan.launch_shape()
+    ntrip = len(plan.triples(0, 0))
+    regions = 2 if plan.src.regions == 2 else 1
+    blocks = len(plan.runs()) if plan.src.block_size == plan.dst.block_size else 0
+    if sh["run_table"]:
+        chunks = sh["pieces"] // regions
+        return 2 * 16 * ntrip + 2 * 4 * (-(-chunks // 8)) + 16 * blocks
+    pieces = sh["pieces"] // regions
+    copies = 2 if sh["lanes"] == 64 else 1
+    return copies * 32 * pieces + 16 * blocks
 
 
 class QueueStep:
@@ -816,8 +833,10 @@ def bench_batched(args, torch, kvx, S, W):
     step_bytes = (rd + wr) * L
     nruns = len(plan.runs())
     log(f"plan: {nruns} runs for {sum(tokens)} tokens, {rd + wr} B per layer, host plan {plan_ms:.1f} ms")
-    if args.counters:
-        counters_run(torch, kvx, plan, side, L, rd + wr)
+    if args.counters:   # --runs: the run-table plan's kernel instead
+        cplan = kvx.kvx_plan(gs.pool, gd.pool, tokens, wl.src_tables, wl.dst_tables, runs=True, stream=side) \
+            if args.runs else plan
+        counters_run(torch, kvx, cplan, side, L, rd + wr)
         plan.close()
         return None
     digest = inputs_digest(wl.src_tables + wl.dst_tables, [gs, gd], wl.prompt_lens)
@@ -935,6 +954,26 @@ def bench_batched(args, torch, kvx, S, W):
     for pair in masked.values():
         for s_ in pair:
             s_.close()
+    # Run tables instead of cut pieces (KVX_PLAN_RUNS), push alone, same pools.
+    rplan = kvx.kvx_plan(gs.pool, gd.pool, tokens, wl.src_tables, wl.dst_tables, runs=True, stream=side)
+    rplan_ms = steady_plan_ms(kvx, gs.pool, gd.pool, tokens, wl.src_tables, wl.dst_tables, side, runs=True)
+
+    def runs_only():
+        for l in range(L):
+            kvx.kvx_push_layer(rplan, l, stream=side)
+    runs_only()
+    with Timer(torch, side) as t:
+        for _ in range(args.steps):
+            runs_only()
+    t_r = t.ms / args.steps
+    run_table = {"taken": rplan.launch_shape()["run_table"], "host_plan_ms": round(rplan_ms, 3),
+                 "worklist_bytes": worklist_bytes(rplan), "push_alone_ms": round(t_r, 3),
+                 "push_alone_GBs": round(step_bytes / (t_r * 1e-3) / 1e9, 1),
+                 "pieces_worklist_bytes": worklist_bytes(plan), "pieces_host_plan_ms": round(plan_ms, 3),
+                 "pieces_push_alone_GBs": main["push_alone_GBs"]}
+    log(f"run tables: host plan {rplan_ms:.2f} ms (pieces {plan_ms:.2f}), work list {run_table['worklist_bytes']} B "
+        f"(pieces {run_table['pieces_worklist_bytes']}), push alone {run_table['push_alone_GBs']} GB/s")
+    rplan.close()
     # canary delivered: layer L-1's pushed destination holds its compute's canary
     d0 = int(wl.dst_tables[0][0])
     got = gd.region(L - 1, 0)[d0 * bb:d0 * bb + 4].cpu().numpy().view(np.uint32)[0]
@@ -970,7 +1009,8 @@ def bench_batched(args, torch, kvx, S, W):
                                      f"{splits['full_split']}",
                        "full_split4": f"CU masks: compute on {ncu - splits['full_split4']} CUs, push on "
                                       f"{splits['full_split4']}"}[mode],
-                   "variants": results, "canary_delivered": canary_ok, "host_plan_ms": round(plan_ms, 2)},
+                   "variants": results, "canary_delivered": canary_ok, "host_plan_ms": round(plan_ms, 2),
+                   "run_table_plan": run_table},
         "roofline": roofline(rd + wr, main["push_alone_ms"] * 1e3 / L, "kvx::copy_kernel<0> (kvx_push_layer)",
                              wl.name, {"note": "push alone on its stream, span over its launches"}),
         "cpu_baseline": cpu,
@@ -1075,7 +1115,7 @@ def bench_multiturn(args, torch, kvx, S, W):
             continue
         t0 = time.perf_counter()
         p = kvx.kvx_plan(dec.pool, pre.pool, [reusable] * ex["sessions"], ex["decode_tables"],
-                         ex["prefill_tables"][t], stream=side)
+                         ex["prefill_tables"][t], runs=args.runs, stream=side)
         plan_ms += (time.perf_counter() - t0) * 1e3
         plans.append((t, p))
         step_bytes += sum(p.bytes_per_layer()) * L
@@ -1147,6 +1187,30 @@ def bench_multiturn(args, torch, kvx, S, W):
                 for j, (t, _) in enumerate(plans)]
     log(f"multiturn: {ms:.2f} ms per step (turns {[t for t, _ in plans]}), {gbs:.1f} GB/s "
         f"({100 * gbs / HBM_PEAK_GBS:.1f}%); per turn median ms {[x['median_ms'] for x in per_turn]}")
+    # The other kind of work list (run tables or cut pieces), same pools and step.
+    alt = []
+    alt_ms = 0.0
+    for t, _ in plans:
+        t0 = time.perf_counter()
+        alt.append(kvx.kvx_plan(dec.pool, pre.pool, [ex["growth"] * (t - 1)] * ex["sessions"], ex["decode_tables"],
+                                ex["prefill_tables"][t], runs=not args.runs, stream=side))
+        alt_ms += (time.perf_counter() - t0) * 1e3
+
+    def alt_step():
+        for p in alt:
+            for l in range(L):
+                kvx.kvx_push_layer(p, l, stream=side)
+    alt_span, _ = timed_steps(torch, side, alt_step, args.steps, 1)
+    alt_gbs = step_bytes * args.steps / (alt_span * 1e-3) / 1e9
+    other = {"work_list": "cut pieces" if args.runs else "run tables (KVX_PLAN_RUNS)",
+             "taken": [p.launch_shape()["run_table"] for p in alt],
+             "GBs": round(alt_gbs, 1), "host_plan_ms_all_turns": round(alt_ms, 2),
+             "worklist_bytes": sum(worklist_bytes(p) for p in alt),
+             "this_line_worklist_bytes": sum(worklist_bytes(p) for _, p in plans)}
+    log(f"with {other['work_list']}: {alt_gbs:.1f} GB/s, host plans {alt_ms:.2f} ms (this line {plan_ms:.2f}), "
+        f"work lists {other['worklist_bytes']} B (this line {other['this_line_worklist_bytes']})")
+    for p in alt:
+        p.close()
     cpu = None
     if not args.no_cpu_baseline:
         import oracle as O
@@ -1169,6 +1233,8 @@ def bench_multiturn(args, torch, kvx, S, W):
         "value": gbs, "ms_per_step": ms, "dtype": "u8", "parity": parity, "span": span_stats(per_step),
         "config": {"workload": wl.name, "seed": wl.seed, "inputs_sha256_16": digest, "layers": L,
                    "kv_heads": wl.src.num_heads, "head_dim": wl.src.head_dim, "per_turn": per_turn,
+                   "work_list": "run tables (KVX_PLAN_RUNS)" if args.runs else "cut pieces",
+                   "other_work_list": other,
                    "block_size": wl.src.block_size, "payload_dtype": wl.src.dtype, "scales": "fp32 per block",
                    "sessions": ex["sessions"], "turns_copied": turns, "threshold_tokens": ex["threshold"],
                    "bytes_per_step": step_bytes,
@@ -1373,6 +1439,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-parity", action="store_true", help="skip the verification step against the oracle")
+    ap.add_argument("--runs", action="store_true",
+                    help="batched_push --counters and multiturn_fp8: plans keep run tables (KVX_PLAN_RUNS)")
     ap.add_argument("--compute-mode", default="bounded", choices=["bounded", "full", "full_split", "full_split4"],
                     help="batched_push: how the compute stand-in shares the chip with the push")
     ap.add_argument("--counters", action="store_true",

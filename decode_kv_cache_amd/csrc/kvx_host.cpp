@@ -372,11 +372,72 @@ int32_t pick_shape(kvx_plan_t* p) {
   return n32 >= kLongMinPieces ? kShapeLong : kShapeLongSmall;
 }
 
+// First run of each group of kRunGroupChunks chunks of a run table's flat
+// space: the run that holds the group's first 16-byte unit.
+std::vector<uint32_t> run_index(const std::vector<RunRec>& runs, uint32_t total16) {
+  const uint64_t chunks = (uint64_t(total16) + kRunChunk16 - 1) / kRunChunk16;
+  const uint64_t groups = (chunks + kRunGroupChunks - 1) / kRunGroupChunks;
+  std::vector<uint32_t> g(size_t(groups), 0);
+  size_t r = 0;
+  for (uint64_t k = 0; k < groups; ++k) {
+    const uint64_t target = k * uint64_t(kRunGroupChunks) * kRunChunk16;
+    while (r + 1 < runs.size() && uint64_t(runs[r].start16) + runs[r].len16 <= target) ++r;
+    g[size_t(k)] = uint32_t(r);
+  }
+  return g;
+}
+
+// Whether a plan can keep run tables: streaming launches, one triple list
+// shared by the regions, and regions (hence staging) below 4 GiB, so that
+// every byte offset fits 32 bits.
+bool runs_eligible(const kvx_plan_t* p) {
+  const int64_t lim = int64_t(1) << 32;
+  return p->want_runs && p->shape == kShapeFine && p->nlists == 1 &&
+         int64_t(p->src.NB) * p->src.block_bytes() < lim && int64_t(p->dst.NB) * p->dst.block_bytes() < lim;
+}
+
+// Run tables of the shared triple list (KVX_PLAN_RUNS): in plan order with
+// each run's staging offset as its flat position (pack, unpack), and in
+// destination order (push; the order streaming pieces take, for the same
+// reason).
+void build_runs(kvx_plan_t* p) {
+  const std::vector<kvx_triple>& tr = p->triples[0];
+  const size_t n = tr.size();
+  p->runs_plan.resize(n);
+  uint32_t pos = 0;
+  for (size_t i = 0; i < n; ++i) {
+    const kvx_triple& t = tr[i];
+    p->runs_plan[i] = RunRec{uint32_t(t.src_off / 16), uint32_t(t.dst_off / 16), uint32_t(t.len / 16), pos};
+    pos += uint32_t(t.len / 16);
+  }
+  p->run_total16 = pos;
+  p->payload[0] = p->payload[1] = int64_t(pos) * 16;
+  std::vector<int32_t> order(n);
+  for (size_t i = 0; i < n; ++i) order[i] = int32_t(i);
+  std::sort(order.begin(), order.end(), [&tr](int32_t a, int32_t b) { return tr[a].dst_off < tr[b].dst_off; });
+  p->runs_dst.resize(n);
+  pos = 0;
+  for (size_t k = 0; k < n; ++k) {
+    RunRec r = p->runs_plan[size_t(order[k])];
+    r.start16 = pos;
+    pos += r.len16;
+    p->runs_dst[k] = r;
+  }
+  p->gidx_plan = run_index(p->runs_plan, p->run_total16);
+  p->gidx_dst = run_index(p->runs_dst, p->run_total16);
+  p->runs_mode = true;
+}
+
 // Split each triple list into workgroup-sized pieces and give each its
 // offset in its region's staging (the exclusive prefix of the triple
-// lengths).  Pieces of list r carry r as their region tag.
+// lengths).  Pieces of list r carry r as their region tag.  A plan that
+// asked for run tables and can keep them gets those instead.
 void build_pieces(kvx_plan_t* p) {
   p->shape = pick_shape(p);
+  if (runs_eligible(p)) {
+    build_runs(p);
+    return;
+  }
   const int64_t piece = shape_piece_bytes(p->shape);
   // Streaming launches take their pieces in destination order: the
   // workgroups resident at any moment then write a narrow address range
@@ -425,7 +486,9 @@ int upload(kvx_plan_t* p, hipStream_t s) {
   const size_t pb = p->pieces.size() * sizeof(Piece);
   const size_t sb = p->stream_pieces.size() * sizeof(Piece);
   const size_t bb = p->blocks.size() * sizeof(BlockPair);
-  const size_t total = std::max<size_t>(pb + sb + bb, 256);
+  const size_t rb = p->runs_dst.size() * sizeof(RunRec);   // each of the two run tables
+  const size_t gb = (p->gidx_dst.size() * sizeof(uint32_t) + 15) / 16 * 16;  // each run index, 16-B padded
+  const size_t total = std::max<size_t>(pb + sb + bb + 2 * rb + 2 * gb, 256);
   int rc = desc_alloc(total, &p->dev_buf, &p->device);
   if (rc != KVX_OK) {
     p->dev_buf = nullptr;
@@ -448,6 +511,26 @@ int upload(kvx_plan_t* p, hipStream_t s) {
   if (bb) {
     e = hipMemcpyAsync(buf + pb + sb, p->blocks.data(), bb, hipMemcpyHostToDevice, s);
     if (e != hipSuccess) return fail_hip(e, "hipMemcpyAsync(blocks)");
+  }
+  if (p->runs_mode) {
+    char* const r0 = buf + pb + sb + bb;
+    p->d_runs_dst = reinterpret_cast<const RunRec*>(r0);
+    p->d_runs_plan = reinterpret_cast<const RunRec*>(r0 + rb);
+    p->d_gidx_dst = reinterpret_cast<const uint32_t*>(r0 + 2 * rb);
+    p->d_gidx_plan = reinterpret_cast<const uint32_t*>(r0 + 2 * rb + gb);
+    const struct {
+      const void* src;
+      char* dst;
+      size_t bytes;
+    } parts[4] = {{p->runs_dst.data(), r0, rb},
+                  {p->runs_plan.data(), r0 + rb, rb},
+                  {p->gidx_dst.data(), r0 + 2 * rb, p->gidx_dst.size() * sizeof(uint32_t)},
+                  {p->gidx_plan.data(), r0 + 2 * rb + gb, p->gidx_plan.size() * sizeof(uint32_t)}};
+    for (const auto& part : parts) {
+      if (!part.bytes) continue;
+      e = hipMemcpyAsync(part.dst, part.src, part.bytes, hipMemcpyHostToDevice, s);
+      if (e != hipSuccess) return fail_hip(e, "hipMemcpyAsync(run tables)");
+    }
   }
   e = hipEventCreateWithFlags(&p->upload_ev, hipEventDisableTiming);
   if (e != hipSuccess) {
@@ -633,7 +716,8 @@ int kvx_plan(const kvx_pool* src, const kvx_pool* dst, int32_t num_requests,
   if (!src || !dst || !out) return fail(KVX_E_INVAL, "kvx_plan: null pool or output");
   if (!(flags & KVX_PLAN_HOST_ONLY)) (void)reclaim(false, nullptr);  // plans released earlier whose work is done
   if (src == dst) return fail(KVX_E_INVAL, "kvx_plan: src and dst are the same pool");
-  if (flags & ~(KVX_PLAN_HOST_ONLY | KVX_PLAN_OVERLAP)) return fail(KVX_E_INVAL, "kvx_plan: unknown flags 0x%x", flags);
+  if (flags & ~(KVX_PLAN_HOST_ONLY | KVX_PLAN_OVERLAP | KVX_PLAN_RUNS))
+    return fail(KVX_E_INVAL, "kvx_plan: unknown flags 0x%x", flags);
   if (!(flags & KVX_PLAN_HOST_ONLY) && capturing(upload_stream))
     return fail(KVX_E_INVAL, "kvx_plan: the upload stream is capturing a graph (build plans outside a capture)");
   if (num_requests < 0) return fail(KVX_E_INVAL, "kvx_plan: negative request count");
@@ -663,6 +747,7 @@ int kvx_plan(const kvx_pool* src, const kvx_pool* dst, int32_t num_requests,
     p->push_ok = gs.state || (gs.H == gd.H && gs.layout == gd.layout);
     p->host_only = (flags & KVX_PLAN_HOST_ONLY) != 0;
     p->overlap = (flags & KVX_PLAN_OVERLAP) != 0;
+    p->want_runs = (flags & KVX_PLAN_RUNS) != 0;
     p->nreg = gs.nreg;
     p->nlists = gs.state ? 2 : 1;
     rc = gs.state ? build_state_plan(p, num_requests, num_tokens, src_offsets, dst_offsets, src_ids, dst_ids)
@@ -727,11 +812,12 @@ int kvx_plan_bytes(const kvx_plan_t* p, int64_t* rd, int64_t* wr) {
 int kvx_plan_launch_shape(const kvx_plan_t* p, kvx_launch_shape* out) {
   if (!p || !out) return fail(KVX_E_INVAL, "kvx_plan_launch_shape: null argument");
   if (!p->push_ok) return fail(KVX_E_MISMATCH, "kvx_plan_launch_shape: pools differ in head count or layout");
-  out->pieces = int64_t(p->pieces.size()) * (p->nlists == 1 ? p->nreg : 1);
+  out->pieces = p->runs_mode ? (int64_t(p->run_total16) + kRunChunk16 - 1) / kRunChunk16 * p->nreg
+                             : int64_t(p->pieces.size()) * (p->nlists == 1 ? p->nreg : 1);
   out->piece_bytes = int32_t(shape_piece_bytes(p->shape));
   out->lanes = kShapes[p->shape].threads;
   out->vectors = kShapes[p->shape].vecs;
-  out->pad = 0;
+  out->run_table = p->runs_mode ? 1 : 0;
   return KVX_OK;
 }
 

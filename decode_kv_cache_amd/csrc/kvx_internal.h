@@ -68,6 +68,22 @@ static_assert(piece_shift(kShapeLong) == 3 && piece_shift(kShapeLongSmall) == 2,
 constexpr int64_t kLongMinPieces = 608;
 constexpr int64_t kLongMaxPieces = 1312;
 
+// Run-table work list (KVX_PLAN_RUNS): one record per triple, a range
+// contiguous on both sides, with its position in the list's flat byte space
+// (the triples back to back in the table's order).  Every field is in
+// 16-byte units, so each fits 32 bits for regions and staging below 64 GiB
+// (the kernels address inside a region with 32-bit byte offsets, so run
+// tables are used for regions below 4 GiB).  A workgroup copies one 4 KiB
+// chunk of the flat space; a run index entry names the first run of each
+// group of kRunGroupChunks chunks, from which each wave walks the records
+// (scalar loads) to the runs of its 64 units.
+struct RunRec {
+  uint32_t src16, dst16, len16, start16;
+};
+static_assert(sizeof(RunRec) == 16, "RunRec is 16 bytes");
+constexpr int32_t kRunGroupChunks = 8;
+constexpr int32_t kRunChunk16 = 256;  // a 4 KiB chunk in 16-byte units
+
 // One side's layer group.  Attention pools: nreg regions (K and V, or one
 // latent region) of NB blocks.  State pools: two regions of NB slots of
 // slot_bytes[r] bytes; BS, H, D, E and layout are unused.
@@ -107,6 +123,15 @@ struct kvx_plan_s {
   int32_t shape = kvx::kShapeLong;  // launch shape of the copy kernels (CopyShape)
   int64_t n32 = 0;                  // 32 KiB pieces covering one layer's triples (all regions)
   bool overlap = false;             // KVX_PLAN_OVERLAP: launches of this plan overlap each other
+  // KVX_PLAN_RUNS honoured: streaming launches read run tables, no pieces.
+  // runs_dst: the triples in destination order (push), start16 = their flat
+  // position; runs_plan: plan order, start16 = the staging offset (pack,
+  // unpack).  gidx_*: first run of each group of kRunGroupChunks chunks.
+  bool want_runs = false;           // KVX_PLAN_RUNS was passed
+  bool runs_mode = false;
+  uint32_t run_total16 = 0;         // flat length of the (shared) list, 16-byte units
+  std::vector<kvx::RunRec> runs_dst, runs_plan;
+  std::vector<uint32_t> gidx_dst, gidx_plan;
   std::vector<kvx_run> runs;
   std::vector<kvx_triple> triples[2];
   std::vector<kvx::Piece> pieces;     // list 0's pieces, then list 1's
@@ -131,6 +156,10 @@ struct kvx_plan_s {
   const kvx::Piece* d_pieces = nullptr;
   const kvx::Piece* d_stream = nullptr;  // pieces in streaming order (d_pieces for streaming plans)
   const kvx::BlockPair* d_blocks = nullptr;
+  const kvx::RunRec* d_runs_dst = nullptr;
+  const kvx::RunRec* d_runs_plan = nullptr;
+  const uint32_t* d_gidx_dst = nullptr;
+  const uint32_t* d_gidx_plan = nullptr;
   hipEvent_t upload_ev = nullptr;
   std::atomic<bool> upload_seen{false};
 };

@@ -140,6 +140,95 @@ __global__ __launch_bounds__(T) void copy_kernel(CopyArgs a) {
   }
 }
 
+struct RunArgs {
+  const RunRec* runs;        // run table of the mode's order
+  const uint32_t* gidx;      // first run of each group of kRunGroupChunks chunks
+  const BlockPair* blocks;
+  uint32_t nruns, total16;   // runs; flat length in 16-byte units
+  int32_t n_chunks;          // 4 KiB chunks (workgroups before the scale workgroups)
+  int32_t n_blocks, n_scale_slots;
+  uint32_t in_bytes, out_bytes;  // bytes addressable from in[r] / out[r]
+  const uint8_t* in[2];
+  uint8_t* out[2];
+  const uint32_t* in_sc[2];
+  uint32_t* out_sc[2];
+};
+
+// One workgroup copies one 4 KiB chunk of a run table's flat space (the
+// runs back to back in the table's order) of region blockIdx.y.  Each wave
+// covers 64 consecutive 16-byte units.  Starting from the first run of the
+// chunk's group (a run index entry per kRunGroupChunks chunks), the wave
+// walks the run records with scalar loads: past the runs that end before its
+// first unit, then over the runs that start inside its 64 units, each lane
+// keeping the last one that starts at or before its unit.  Long runs make
+// this one or two record loads per wave.  No per-piece record exists: the
+// work list is the run table, 16 bytes per run, plus its run index.
+// Addresses are 32-bit byte offsets into one buffer resource per region.
+// Workgroups past the chunks copy the planned blocks' scales, as in
+// copy_kernel.
+typedef const __attribute__((address_space(4))) uint32_t* ConstU32;
+__device__ __forceinline__ RunRec load_run(const RunRec* t, uint32_t i) {
+  return __builtin_bit_cast(RunRec, ((ConstVecs)t)[i]);
+}
+template <int MODE>
+__global__ __launch_bounds__(256) void run_kernel(RunArgs a) {
+  const int x = blockIdx.x;
+  const int kv = blockIdx.y;
+  if (x < a.n_chunks) {
+    const uint32_t lane = threadIdx.x & 63u;
+    // the wave's first unit, made visibly wave-uniform so that the record
+    // walk below stays in scalar registers
+    const uint32_t fw = __builtin_amdgcn_readfirstlane(uint32_t(x) * uint32_t(kRunChunk16) + (threadIdx.x >> 6) * 64u);
+    if (fw >= a.total16) return;
+    const uint32_t fl = fw + lane;
+    const bool live = fl < a.total16;
+    const uint32_t wend = min(fw + 64u, a.total16);
+    uint32_t r = ((ConstU32)a.gidx)[uint32_t(x) / uint32_t(kRunGroupChunks)];
+    RunRec rec = load_run(a.runs, r);
+    // the run holding the wave's first unit (runs tile the flat space, so
+    // this ends within the table)
+    while (rec.start16 + rec.len16 <= fw && r + 1 < a.nruns) rec = load_run(a.runs, ++r);
+    uint32_t my_src = rec.src16, my_dst = rec.dst16, my_start = rec.start16;
+    uint32_t end = rec.start16 + rec.len16;
+    // the runs that start inside the wave's units
+    while (end < wend && r + 1 < a.nruns) {
+      rec = load_run(a.runs, ++r);
+      if (fl >= rec.start16) {
+        my_src = rec.src16;
+        my_dst = rec.dst16;
+        my_start = rec.start16;
+      }
+      end = rec.start16 + rec.len16;
+    }
+    const bool found = fl >= my_start;
+    if (!live || !found) return;
+    const uint32_t d = fl - my_start;
+    const uint32_t ioff = MODE == kUnpack ? fl * 16u : (my_src + d) * 16u;
+    const uint32_t ooff = MODE == kPack ? fl * 16u : (my_dst + d) * 16u;
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(pick(a.in, kv)), (short)0, int(a.in_bytes), kBufferWord3);
+    const __amdgpu_buffer_rsrc_t rd =
+        __builtin_amdgcn_make_buffer_rsrc(pick(a.out, kv), (short)0, int(a.out_bytes), kBufferWord3);
+    const v4u v = __builtin_amdgcn_raw_buffer_load_b128(rs, int(ioff), 0, KVX_LD_AUX);
+    __builtin_amdgcn_raw_buffer_store_b128(v, rd, int(ooff), 0, KVX_ST_AUX_FINE);
+    return;
+  }
+  const int i = (x - a.n_chunks) * 256 + threadIdx.x;
+  if (MODE == kPush) {
+    if (i < a.n_blocks) {
+      const BlockPair b = a.blocks[i];
+      a.out_sc[kv][b.dst] = a.in_sc[kv][b.src];
+    }
+  } else if (MODE == kPack) {
+    if (i < a.n_blocks)
+      a.out_sc[kv][i] = a.in_sc[kv][a.blocks[i].src];
+    else if (i < a.n_scale_slots)
+      a.out_sc[kv][i] = 0u;
+  } else {
+    if (i < a.n_blocks) a.out_sc[kv][a.blocks[i].dst] = a.in_sc[kv][i];
+  }
+}
+
 // Several (plan, layer) copies of one mode in one launch (kvx_push_many;
 // kvx_pack / kvx_unpack over several layers): entry j owns workgroups
 // [first_j, first_{j+1}) and copies its plan's pieces between its region
@@ -205,7 +294,13 @@ struct HeadArgs {
 #ifndef KVX_HEAD_ST_AUX
 #define KVX_HEAD_ST_AUX KVX_ST_AUX_FINE
 #endif
-constexpr int kHeadThreads = 256;
+// 512 lanes: on the TP4 head share (8 KiB per block, 512 vectors) every
+// lane moves one vector.  Side by side, us per layer: 512 lanes 49.3-49.8,
+// 256 lanes 50.2-51.5, 128 lanes 50.9-52.0; a workgroup taking two or four
+// planned blocks with all their loads ahead of the stores 51.9 and 52.2
+// against 49.6; launches allowed to overlap the previous one on the stream
+// made no consistent difference.
+constexpr int kHeadThreads = 512;
 constexpr int kHeadUnroll = 4;
 
 // One workgroup moves the head slice of one planned block (or block piece,
@@ -294,9 +389,43 @@ static int launch_copy_shape(kvx_plan_t* p, CopyArgs a, int64_t scale_slots, hip
   return check_launch("kvx copy kernel launch");
 }
 
+// Enqueue the run-table kernel for one layer (a run-mode plan).
+template <int MODE>
+static int launch_runs(kvx_plan_t* p, const CopyArgs& c, int64_t scale_slots, hipStream_t s, hipEvent_t started,
+                       hipEvent_t finished, int64_t* launches) {
+  RunArgs a{};
+  a.runs = MODE == kPush ? p->d_runs_dst : p->d_runs_plan;
+  a.gidx = MODE == kPush ? p->d_gidx_dst : p->d_gidx_plan;
+  a.blocks = p->d_blocks;
+  a.nruns = uint32_t(p->runs_dst.size());
+  a.total16 = p->run_total16;
+  a.n_chunks = int32_t((int64_t(p->run_total16) + kRunChunk16 - 1) / kRunChunk16);
+  a.n_blocks = int32_t(p->blocks.size());
+  a.n_scale_slots = int32_t(scale_slots);
+  const uint32_t src_region = uint32_t(int64_t(p->src.NB) * p->src.block_bytes());
+  const uint32_t dst_region = uint32_t(int64_t(p->dst.NB) * p->dst.block_bytes());
+  const uint32_t payload = uint32_t(int64_t(p->run_total16) * 16);
+  a.in_bytes = MODE == kUnpack ? payload : src_region;
+  a.out_bytes = MODE == kPack ? payload : dst_region;
+  for (int r = 0; r < 2; ++r) {
+    a.in[r] = c.in[r];
+    a.out[r] = c.out[r];
+    a.in_sc[r] = c.in_sc[r];
+    a.out_sc[r] = c.out_sc[r];
+  }
+  const int64_t nsw = c.in_sc[0] ? (scale_slots + 255) / 256 : 0;
+  const int64_t gx = a.n_chunks + nsw;
+  if (gx == 0) return KVX_OK;
+  if (gx > kMaxGridX) return fail(KVX_E_UNSUPPORTED, "kvx run-table launch: %lld workgroups", (long long)gx);
+  hipExtLaunchKernelGGL(run_kernel<MODE>, dim3(unsigned(gx), grid_y(p)), dim3(256), 0, s, started, finished, 0u, a);
+  if (launches) ++*launches;
+  return check_launch("kvx run-table kernel launch");
+}
+
 template <int MODE>
 static int launch_copy(kvx_plan_t* p, CopyArgs a, int64_t scale_slots, hipStream_t s,
                        hipEvent_t started = nullptr, hipEvent_t finished = nullptr, int64_t* launches = nullptr) {
+  if (p->runs_mode) return launch_runs<MODE>(p, a, scale_slots, s, started, finished, launches);
   switch (p->shape) {
     case kShapeLong:
       return launch_copy_shape<MODE, kShapes[kShapeLong].threads, kShapes[kShapeLong].vecs>(
@@ -349,8 +478,9 @@ class ManyBatch {
       : s_(s), started_(started), finished_(finished) {}
 
   // Whether plan p's pieces fit a batched launch at all.
+  // (Run-table plans have no pieces: they launch alone.)
   static bool fits(const kvx_plan_t* p) {
-    return (int64_t(p->pieces.size()) << piece_shift(p->shape)) <= kMaxGridX;
+    return !p->runs_mode && (int64_t(p->pieces.size()) << piece_shift(p->shape)) <= kMaxGridX;
   }
 
   int add(const kvx_plan_t* p, const uint8_t* const in[2], uint8_t* const out[2]) {

@@ -23,6 +23,7 @@ KVX_OK, KVX_E_INVAL, KVX_E_RANGE, KVX_E_DUPDST, KVX_E_MISMATCH, KVX_E_UNSUPPORTE
 KVX_NHD, KVX_HND = 0, 1
 KVX_PLAN_HOST_ONLY = 1
 KVX_PLAN_OVERLAP = 2
+KVX_PLAN_RUNS = 4
 LAYOUTS = {"NHD": KVX_NHD, "HND": KVX_HND}
 
 
@@ -45,7 +46,7 @@ class kvx_run(C.Structure):
 
 class kvx_launch_shape(C.Structure):
     _fields_ = [("pieces", C.c_int64), ("piece_bytes", C.c_int32), ("lanes", C.c_int32), ("vectors", C.c_int32),
-                ("pad", C.c_int32)]
+                ("run_table", C.c_int32)]
 
 
 class kvx_triple(C.Structure):
@@ -329,7 +330,8 @@ class Plan:
     def launch_shape(self) -> dict:
         s = kvx_launch_shape()
         _check("kvx_plan_launch_shape", lib().kvx_plan_launch_shape(self.handle, C.byref(s)))
-        return {"pieces": s.pieces, "piece_bytes": s.piece_bytes, "lanes": s.lanes, "vectors": s.vectors}
+        return {"pieces": s.pieces, "piece_bytes": s.piece_bytes, "lanes": s.lanes, "vectors": s.vectors,
+                "run_table": bool(s.run_table)}
 
     def bytes_per_layer(self):
         r, w = C.c_int64(), C.c_int64()
@@ -367,11 +369,12 @@ def _csr(tables):
 
 def kvx_plan(src: Pool, dst: Pool, num_tokens: Sequence[int], src_tables: Sequence[Sequence[int]],
              dst_tables: Sequence[Sequence[int]], *, host_only: bool = False, overlap: bool = False,
-             stream=None) -> Plan:
+             runs: bool = False, stream=None) -> Plan:
     """Build a plan.  ``num_tokens[r]`` tokens of request r move; its block
     lists are ``src_tables[r]`` / ``dst_tables[r]`` (each at least as long as
     its side needs).  ``overlap``: KVX_PLAN_OVERLAP (the caller keeps several
-    of the plan's device calls in flight at once)."""
+    of the plan's device calls in flight at once); ``runs``: KVX_PLAN_RUNS
+    (streaming launches read run tables instead of cut pieces)."""
     R = len(num_tokens)
     if len(src_tables) != R or len(dst_tables) != R:
         raise ValueError("one src and one dst block list per request")
@@ -382,7 +385,8 @@ def kvx_plan(src: Pool, dst: Pool, num_tokens: Sequence[int], src_tables: Sequen
     us = None if host_only else _stream(stream)
     rc = lib().kvx_plan(src.handle, dst.handle, R, nt.ctypes.data, so.ctypes.data, do.ctypes.data,
                         sid.ctypes.data if sid.size else None, did.ctypes.data if did.size else None,
-                        (KVX_PLAN_HOST_ONLY if host_only else 0) | (KVX_PLAN_OVERLAP if overlap else 0), us,
+                        (KVX_PLAN_HOST_ONLY if host_only else 0) | (KVX_PLAN_OVERLAP if overlap else 0)
+                        | (KVX_PLAN_RUNS if runs else 0), us,
                         C.byref(h))
     _check("kvx_plan", rc)
     return Plan(h, src, dst)

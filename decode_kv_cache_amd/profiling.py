@@ -61,12 +61,37 @@ def _short(name: str) -> str:
     return name if len(name) <= 90 else name[:87] + "..."
 
 
+def back_to_back(intervals):
+    """Launches of one kind in start order: the gaps between one launch's end
+    and the next one's start on its queue, and the union of their intervals
+    against the sum of their durations (equal when no two overlap)."""
+    iv = sorted(intervals)
+    gaps = [b[0] - a[1] for a, b in zip(iv, iv[1:])]
+    union, cur_s, cur_e = 0, None, None
+    for s_, e_ in iv:
+        if cur_e is None or s_ > cur_e:
+            if cur_e is not None:
+                union += cur_e - cur_s
+            cur_s, cur_e = s_, e_
+        else:
+            cur_e = max(cur_e, e_)
+    if cur_e is not None:
+        union += cur_e - cur_s
+    total = sum(e_ - s_ for s_, e_ in iv)
+    return gaps, union, total
+
+
 def trace_summary(d: str, command: str) -> str:
     rows = list(csv.DictReader(open(_one(os.path.join(d, "**", "*kernel_stats.csv")))))
     trace = list(csv.DictReader(open(_one(os.path.join(d, "**", "*kernel_trace.csv")))))
     per = defaultdict(list)
+    by_grid = defaultdict(list)
     for r in trace:
-        per[r["Kernel_Name"]].append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+        s_, e_ = int(r["Start_Timestamp"]), int(r["End_Timestamp"])
+        per[r["Kernel_Name"]].append(e_ - s_)
+        if "kvx::" in r["Kernel_Name"]:
+            key = (r["Kernel_Name"], int(r["Grid_Size_X"]), int(r["Grid_Size_Y"]), r.get("Queue_Id", ""))
+            by_grid[key].append((s_, e_))
     out = ["# rocprofv3 --kernel-trace --stats summary", f"command: {command}",
            f"kernel_source_sha256_16: {kernel_source_digest()}", "",
            "| kernel | calls | avg us | median us | min us | max us | share |", "|---|---|---|---|---|---|---|"]
@@ -76,6 +101,17 @@ def trace_summary(d: str, command: str) -> str:
         med = statistics.median(durs) / 1e3 if durs else float("nan")
         out.append(f"| {_short(name)} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | {med:.2f} | "
                    f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.1f}% |")
+    out += ["", "libkvx launches by kernel and grid (grid x = work-items along x; one queue each):", "",
+            "| kernel | grid x | grid y | queue | calls | avg us | median us | median gap to the next us | "
+            "union / sum of durations |", "|---|---|---|---|---|---|---|---|---|"]
+    for (name, gx, gy, qid), iv in sorted(by_grid.items(), key=lambda kv: -len(kv[1])):
+        if len(iv) < 2:
+            continue
+        durs = [e_ - s_ for s_, e_ in iv]
+        gaps, union, total = back_to_back(iv)
+        out.append(f"| {_short(name)} | {gx} | {gy} | {qid} | {len(iv)} | {statistics.mean(durs) / 1e3:.2f} | "
+                   f"{statistics.median(durs) / 1e3:.2f} | {statistics.median(gaps) / 1e3:.2f} | "
+                   f"{union / total:.4f} |")
     return "\n".join(out) + "\n"
 
 

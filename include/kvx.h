@@ -81,6 +81,16 @@ enum {
                                  plan in flight at once (e.g. layers alternating
                                  over two side streams): launches stream small
                                  pieces instead of filling the chip alone */
+#define KVX_PLAN_RUNS 4u      /* a plan whose launches stream (see
+                                 kvx_plan_launch_shape) and whose regions share
+                                 one triple list keeps a run table instead of
+                                 cut pieces: 16 bytes per triple (twice: in
+                                 destination and in plan order) plus 4 bytes
+                                 per 32 KiB; each workgroup finds the runs of
+                                 its 4 KiB chunk itself.  Ignored for one-wave
+                                 plans, state pools and regions or staging of
+                                 4 GiB or more.  The copied bytes do not
+                                 depend on it. */
 
 /*
  * Pool descriptor: the paged KV cache of one layer group on one side, as
@@ -268,7 +278,9 @@ int kvx_plan_triples(const kvx_plan_t* plan, int32_t layer, int32_t kv,
  * the copied bytes do not depend on it. */
 typedef struct kvx_launch_shape {
   int64_t pieces;
-  int32_t piece_bytes, lanes, vectors, pad;
+  int32_t piece_bytes, lanes, vectors;
+  int32_t run_table; /* 1: the plan keeps run tables (KVX_PLAN_RUNS honoured): `pieces`
+                        counts 4 KiB chunks of its flat space, found in the kernel */
 } kvx_launch_shape;
 
 /* Errors: INVAL (null), MISMATCH (no push work list). */

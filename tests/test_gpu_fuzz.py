@@ -5,7 +5,8 @@ draws a geometry of one of three kinds:
   - small random geometries (either layout, 1- or 2-byte elements, ragged
     tails, scales), whose plans take the 4 KiB shape;
   - different block sizes and head counts per side (head transform only).
-Each case is built with or without KVX_PLAN_OVERLAP. Where both pools have
+Each case is built with or without KVX_PLAN_OVERLAP and with or without
+KVX_PLAN_RUNS (streaming plans then read run tables). Where both pools have
 the same head count and layout, its requests are pushed layer by layer.
 They are also split into two plans with disjoint destinations, whose layers
 go out in one kvx_push_many call, and packed and unpacked over a random
@@ -80,6 +81,7 @@ def test_random_sweep():
         except ValueError:         # pools too small for the drawn requests
             continue
         overlap = bool(rng.integers(0, 2))
+        runs = bool(rng.integers(0, 2))
         src, dst = P.pools(O, wl)
         toks = [kvx.kvx_tokens_to_move(p, 0) for p in wl.prompt_lens]
         reqs = [O.Request(n, s, d) for n, s, d in zip(toks, wl.src_tables, wl.dst_tables)]
@@ -87,13 +89,13 @@ def test_random_sweep():
         gs = S.device_side(wl.src, wl.seed, 1, values=(src.kv, src.scales))
         L = wl.src.num_layers
         push_ok = wl.src.num_heads == wl.dst.num_heads and wl.src.layout == wl.dst.layout
-        say("case", i, kind, wl.name, "overlap" if overlap else "", wl.src, wl.dst)
+        say("case", i, kind, wl.name, "overlap" if overlap else "", "runs" if runs else "", wl.src, wl.dst)
         if push_ok:
             # layer by layer
             gd = fresh(wl, dst)
-            plan = kvx.kvx_plan(gs.pool, gd.pool, toks, wl.src_tables, wl.dst_tables, overlap=overlap)
+            plan = kvx.kvx_plan(gs.pool, gd.pool, toks, wl.src_tables, wl.dst_tables, overlap=overlap, runs=runs)
             sh = plan.launch_shape()
-            shapes.add((sh["lanes"], sh["vectors"]))
+            shapes.add((sh["lanes"], sh["vectors"]) + (("runs",) if sh["run_table"] else ()))
             for l in rng.permutation(L):
                 kvx.kvx_push_layer(plan, int(l))
             torch.cuda.synchronize()
@@ -106,7 +108,8 @@ def test_random_sweep():
             cut = int(rng.integers(0, len(toks) + 1))
             groups = [(toks[:cut], wl.src_tables[:cut], wl.dst_tables[:cut]),
                       (toks[cut:], wl.src_tables[cut:], wl.dst_tables[cut:])]
-            plans = [kvx.kvx_plan(gs.pool, gd.pool, t, s, d, overlap=bool(rng.integers(0, 2))) for t, s, d in groups]
+            plans = [kvx.kvx_plan(gs.pool, gd.pool, t, s, d, overlap=bool(rng.integers(0, 2)),
+                                  runs=bool(rng.integers(0, 2))) for t, s, d in groups]
             pairs = [(p, l) for l in range(L) for p in plans]
             order = rng.permutation(len(pairs))
             kvx.kvx_push_many([pairs[k][0] for k in order], [pairs[k][1] for k in order])
@@ -116,7 +119,7 @@ def test_random_sweep():
                 p.close()
             # pack and unpack over a random layer range
             gd = fresh(wl, dst)
-            plan = kvx.kvx_plan(gs.pool, gd.pool, toks, wl.src_tables, wl.dst_tables, overlap=overlap)
+            plan = kvx.kvx_plan(gs.pool, gd.pool, toks, wl.src_tables, wl.dst_tables, overlap=overlap, runs=runs)
             l0 = int(rng.integers(0, L))
             l1 = int(rng.integers(l0, L + 1))
             nbytes = kvx.kvx_staging_bytes(plan, l0, l1)
@@ -148,4 +151,4 @@ def test_random_sweep():
         done += 1
     say("cases run", done, "launch shapes seen", sorted(shapes))
     assert done >= CASES * 3 // 4
-    assert {(64, 32), (64, 16), (256, 1)} <= shapes, shapes   # every launch shape exercised
+    assert {(64, 32), (64, 16), (256, 1), (256, 1, "runs")} <= shapes, shapes   # every launch shape exercised

@@ -335,9 +335,60 @@ def test_qwen32b_pack_unpack_sampled():
     plan.close()
 
 
-def test_batched_push_full():
+def test_batched_push_full_with_compute():
+    """batched_push at full size in its timed configuration: layer l's
+    synthetic compute kernel runs on the compute stream and writes a canary
+    into layer l's planned source blocks before its event; kvx_push_layer(l)
+    waits for that event on a side stream while the next layer's compute
+    runs ([MORI] §3.2).  Logical layers alias 16 physical slabs and rewrite a
+    slab with the same bytes, so each slab's last push read the source as its
+    own compute left it: the consumer slab must equal the oracle's push of the
+    final source onto the pre-filled destination, byte for byte (2 GiB
+    regions, 64-bit offsets)."""
+    from decode_kv_cache_amd import bench_support as B
     wl = W.batched_push()
-    full_push(wl, [0, 15], "batched_push")
+    say("workload batched_push with concurrent compute")
+    gs = S.device_side(wl.src, wl.seed, 1)
+    gd = S.device_side(wl.dst, wl.seed, 2)
+    torch.cuda.synchronize()
+    slabs = [0, wl.src.n_phys - 1]
+    dst_snap = snapshot(gd, slabs)
+    toks = tokens(wl)
+    side = torch.cuda.Stream()
+    compute = torch.cuda.current_stream()
+    plan = kvx.kvx_plan(gs.pool, gd.pool, toks, wl.src_tables, wl.dst_tables, stream=side)
+    bs = wl.src.block_size
+    used = np.concatenate([t[:-(-n // bs)] for t, n in zip(wl.src_tables, toks)])
+    blocks = torch.from_numpy(used.astype(np.int32)).cuda()
+    bb = bs * wl.src.num_heads * wl.src.head_dim * wl.src.elem_bytes
+    ncu = torch.cuda.get_device_properties(0).multi_processor_count
+    sink = torch.empty(ncu * 256, dtype=torch.float32, device="cuda")
+    evs = []
+    for l in range(wl.src.num_layers):
+        B.layer_compute(sink, 20000, ncu, gs.region(l, 0), gs.region(l, 1), blocks, bb, 0xC0DE0000 + l,
+                        stream=compute)
+        e = torch.cuda.Event()
+        e.record(compute)
+        evs.append(e)
+        kvx.kvx_push_layer(plan, l, ready=e, stream=side)
+    torch.cuda.synchronize()
+    say("pushed; checking slabs", slabs)
+    src_after = snapshot(gs, slabs)
+    for p in slabs:   # every planned source block of slab p holds its last logical layer's canary
+        last = max(l for l in range(wl.src.num_layers) if wl.src.phys(l) == p)
+        c = (0xC0DE0000 + last) & 0xFFFFFFFF
+        want = np.array([c, c ^ 0x5A5A5A5A, (c + 1) & 0xFFFFFFFF, ~c & 0xFFFFFFFF], np.uint32)
+        heads = src_after[p][0][0].reshape(-1, bb)[used, :16].view(np.uint32)
+        assert (heads == want[None, :]).all(), p
+    op = O.make_plan(P.geom(O, wl.src), P.geom(O, wl.dst), oracle_requests(wl, toks))
+    for p in slabs:
+        for kv in (0, 1):
+            exp = dst_snap[p][0][kv].copy()
+            O.push_region(src_after[p][0][kv], exp, op.triples)
+            assert np.array_equal(gd.kv[p, kv].cpu().numpy(), exp), ("batched_push with compute", p, kv)
+    plan.close()
+    del gs, gd
+    torch.cuda.empty_cache()
 
 
 def test_tp4_share_full():

@@ -238,5 +238,29 @@ def test_launch_shape_overlap_flag():
     assert np.array_equal(a.triples(), b.triples()) and a.bytes_per_layer() == b.bytes_per_layer()
     rc, _ = kvx.kvx_plan_raw(sp, dp, 1, np.array([16], np.int64), np.array([0, 1], np.int64),
                              np.array([0, 1], np.int64), np.array([0], np.int32), np.array([0], np.int32),
-                             flags=kvx.KVX_PLAN_HOST_ONLY | kvx.KVX_PLAN_OVERLAP | 4)
+                             flags=kvx.KVX_PLAN_HOST_ONLY | kvx.KVX_PLAN_OVERLAP | 8)   # an unknown flag
     assert rc == kvx.KVX_E_INVAL
+
+
+def test_run_table_plans_host():
+    """KVX_PLAN_RUNS is honoured for streaming plans of K/V pools and ignored
+    for one-wave plans and state pools; the chunk count covers the flat
+    space of the shared list, and the triples do not depend on it."""
+    big = W.PoolSpec(1, 2000, 16, 8, 128, W.BF16)       # 32 KiB blocks
+    tiny = W.PoolSpec(1, 4000, 1, 1, 576, W.BF16)       # 1152-byte blocks
+    seq = list(range(2000))
+    one_wave = kvx.kvx_plan(fake_pool(big, 0), fake_pool(big, 1), [16 * 512], [seq[:512]], [seq[:512]],
+                            host_only=True, runs=True)
+    assert not one_wave.launch_shape()["run_table"]
+    scattered = list(range(0, 4000, 7))[:500]
+    a = kvx.kvx_plan(fake_pool(tiny, 0), fake_pool(tiny, 1), [500], [scattered], [scattered], host_only=True,
+                     runs=True)
+    b = kvx.kvx_plan(fake_pool(tiny, 0), fake_pool(tiny, 1), [500], [scattered], [scattered], host_only=True)
+    sa, sb = a.launch_shape(), b.launch_shape()
+    assert sa["run_table"] and not sb["run_table"]
+    assert (sa["lanes"], sa["vectors"], sa["piece_bytes"]) == (256, 1, 4096)
+    flat = int(a.triples(0, 0)[:, 2].sum())
+    assert sa["pieces"] == 2 * -(-flat // 4096)
+    assert np.array_equal(a.triples(0, 0), b.triples(0, 0))
+    assert a.bytes_per_layer() == b.bytes_per_layer()
+    assert kvx.kvx_staging_bytes(a, 0, 1) == kvx.kvx_staging_bytes(b, 0, 1)
