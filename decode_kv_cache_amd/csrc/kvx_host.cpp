@@ -136,7 +136,7 @@ void plan_free_idle(kvx_plan_t* p) {
     (void)hipEventSynchronize(p->upload_ev);
     (void)hipEventDestroy(p->upload_ev);
   }
-  desc_free(p->dev_buf, p->dev_bytes, p->device);
+  if (!p->in_scratch) desc_free(p->dev_buf, p->dev_bytes, p->device);
   delete p;
 }
 
@@ -482,21 +482,26 @@ void build_pieces(kvx_plan_t* p) {
   }
 }
 
-int upload(kvx_plan_t* p, hipStream_t s) {
+}  // namespace
+
+namespace kvx {
+
+size_t worklist_bytes(const kvx_plan_t* p) {
   const size_t pb = p->pieces.size() * sizeof(Piece);
   const size_t sb = p->stream_pieces.size() * sizeof(Piece);
   const size_t bb = p->blocks.size() * sizeof(BlockPair);
   const size_t rb = p->runs_dst.size() * sizeof(RunRec);   // each of the two run tables
   const size_t gb = (p->gidx_dst.size() * sizeof(uint32_t) + 15) / 16 * 16;  // each run index, 16-B padded
-  const size_t total = std::max<size_t>(pb + sb + bb + 2 * rb + 2 * gb, 256);
-  int rc = desc_alloc(total, &p->dev_buf, &p->device);
-  if (rc != KVX_OK) {
-    p->dev_buf = nullptr;
-    return rc;
-  }
-  p->dev_bytes = total;
+  return std::max<size_t>(pb + sb + bb + 2 * rb + 2 * gb, 256);
+}
+
+int worklist_copy(kvx_plan_t* p, char* buf, hipStream_t s) {
+  const size_t pb = p->pieces.size() * sizeof(Piece);
+  const size_t sb = p->stream_pieces.size() * sizeof(Piece);
+  const size_t bb = p->blocks.size() * sizeof(BlockPair);
+  const size_t rb = p->runs_dst.size() * sizeof(RunRec);
+  const size_t gb = (p->gidx_dst.size() * sizeof(uint32_t) + 15) / 16 * 16;
   hipError_t e;
-  char* const buf = static_cast<char*>(p->dev_buf);
   p->d_pieces = reinterpret_cast<const Piece*>(buf);
   p->d_stream = sb ? reinterpret_cast<const Piece*>(buf + pb) : p->d_pieces;
   p->d_blocks = reinterpret_cast<const BlockPair*>(buf + pb + sb);
@@ -532,7 +537,24 @@ int upload(kvx_plan_t* p, hipStream_t s) {
       if (e != hipSuccess) return fail_hip(e, "hipMemcpyAsync(run tables)");
     }
   }
-  e = hipEventCreateWithFlags(&p->upload_ev, hipEventDisableTiming);
+  return KVX_OK;
+}
+
+}  // namespace kvx
+
+namespace {
+
+int upload(kvx_plan_t* p, hipStream_t s) {
+  const size_t total = worklist_bytes(p);
+  int rc = desc_alloc(total, &p->dev_buf, &p->device);
+  if (rc != KVX_OK) {
+    p->dev_buf = nullptr;
+    return rc;
+  }
+  p->dev_bytes = total;
+  rc = worklist_copy(p, static_cast<char*>(p->dev_buf), s);
+  if (rc) return rc;
+  hipError_t e = hipEventCreateWithFlags(&p->upload_ev, hipEventDisableTiming);
   if (e != hipSuccess) {
     p->upload_ev = nullptr;
     return fail_hip(e, "hipEventCreate(upload)");
@@ -547,7 +569,7 @@ int upload(kvx_plan_t* p, hipStream_t s) {
 // marker per launch would cost every push a queue packet).
 void release(kvx_plan_t* p) {
   if (!p) return;
-  if (p->dev_buf) (void)hipDeviceSynchronize();
+  if (p->dev_buf && !p->in_scratch) (void)hipDeviceSynchronize();
   kvx::plan_free_idle(p);
 }
 
@@ -715,6 +737,25 @@ int kvx_plan(const kvx_pool* src, const kvx_pool* dst, int32_t num_requests,
              kvx_plan_t** out) {
   if (!src || !dst || !out) return fail(KVX_E_INVAL, "kvx_plan: null pool or output");
   if (!(flags & KVX_PLAN_HOST_ONLY)) (void)reclaim(false, nullptr);  // plans released earlier whose work is done
+  kvx_plan_t* p = nullptr;
+  int rc = kvx::plan_build(src, dst, num_requests, num_tokens, src_offsets, dst_offsets, src_ids, dst_ids, flags,
+                           upload_stream, &p);
+  if (rc) return rc;
+  if (!p->host_only) rc = upload(p, upload_stream);
+  if (rc != KVX_OK) {
+    release(p);
+    return rc;
+  }
+  *out = p;
+  return KVX_OK;
+}
+
+}  // extern "C"
+
+int kvx::plan_build(const kvx_pool* src, const kvx_pool* dst, int32_t num_requests, const int64_t* num_tokens,
+                    const int64_t* src_offsets, const int64_t* dst_offsets, const int32_t* src_ids,
+                    const int32_t* dst_ids, uint32_t flags, hipStream_t upload_stream, kvx_plan_t** out) {
+  if (!src || !dst || !out) return fail(KVX_E_INVAL, "kvx_plan: null pool or output");
   if (src == dst) return fail(KVX_E_INVAL, "kvx_plan: src and dst are the same pool");
   if (flags & ~(KVX_PLAN_HOST_ONLY | KVX_PLAN_OVERLAP | KVX_PLAN_RUNS))
     return fail(KVX_E_INVAL, "kvx_plan: unknown flags 0x%x", flags);
@@ -755,7 +796,6 @@ int kvx_plan(const kvx_pool* src, const kvx_pool* dst, int32_t num_requests,
   } catch (const std::bad_alloc&) {
     rc = fail(KVX_E_NOMEM, "kvx_plan: out of host memory");
   }
-  if (rc == KVX_OK && !p->host_only) rc = upload(p, upload_stream);
   if (rc != KVX_OK) {
     release(p);
     return rc;
@@ -763,6 +803,8 @@ int kvx_plan(const kvx_pool* src, const kvx_pool* dst, int32_t num_requests,
   *out = p;
   return KVX_OK;
 }
+
+extern "C" {
 
 int kvx_plan_runs(const kvx_plan_t* p, kvx_run* out, int64_t cap, int64_t* n) {
   if (!p || !n) return fail(KVX_E_INVAL, "kvx_plan_runs: null argument");
@@ -825,7 +867,7 @@ void kvx_plan_destroy(kvx_plan_t* p) { release(p); }
 
 int kvx_plan_destroy_after(kvx_plan_t* p, hipStream_t stream) {
   if (!p) return KVX_OK;
-  if (!p->dev_buf) {  // host-only: nothing on the device
+  if (!p->dev_buf || p->in_scratch) {  // host-only, or a work list the library never frees
     plan_free_idle(p);
     return KVX_OK;
   }

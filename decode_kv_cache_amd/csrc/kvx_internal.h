@@ -162,6 +162,10 @@ struct kvx_plan_s {
   const uint32_t* d_gidx_plan = nullptr;
   hipEvent_t upload_ev = nullptr;
   std::atomic<bool> upload_seen{false};
+  // Work list in the device's static scratch array (kvx_plan_noalloc): it
+  // stays valid while the device's scratch generation is still scratch_gen.
+  bool in_scratch = false;
+  uint64_t scratch_gen = 0;
 };
 
 namespace kvx {
@@ -189,6 +193,16 @@ void desc_free(void* p, size_t bytes, int device);
 // Free a plan whose enqueued work is known to have finished (no device
 // drain, unlike kvx_plan_destroy).
 void plan_free_idle(kvx_plan_t* plan);
+
+// Validate the arguments of kvx_plan and build a plan's host tables, without
+// its device work list.
+int plan_build(const kvx_pool* src, const kvx_pool* dst, int32_t num_requests, const int64_t* num_tokens,
+               const int64_t* src_offsets, const int64_t* dst_offsets, const int32_t* src_ids,
+               const int32_t* dst_ids, uint32_t flags, hipStream_t upload_stream, kvx_plan_t** out);
+// Bytes of a plan's device work list, and its copy into device memory `buf`
+// on stream `s` (which also points the plan's device fields into `buf`).
+size_t worklist_bytes(const kvx_plan_t* plan);
+int worklist_copy(kvx_plan_t* plan, char* buf, hipStream_t s);
 
 // Validate one (plan, layer) pair of a batched push (pair index i for the
 // message): a device plan with a push work list and a layer in range.

@@ -17,6 +17,8 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
+#include <mutex>
 
 #include "kvx_internal.h"
 
@@ -553,9 +555,48 @@ class ManyBatch {
   const Piece* stream_[kManyMax] = {};  // each entry's pieces in streaming order
 };
 
+// ---------------------------------------------------------------------------
+// Work lists without allocation (kvx_plan_noalloc): one static scratch array
+// per device holds the work list of the most recent plan built that way.
+// ---------------------------------------------------------------------------
+constexpr size_t kScratchBytes = size_t(16) << 20;
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+struct ScratchSlot {
+  std::atomic<char*> ptr{nullptr};     // the device address of `scratch` on this device
+  std::atomic<uint64_t> gen{0};        // bumped by every kvx_plan_noalloc on this device
+};
+static ScratchSlot g_scratch[kMaxDevices];
+static std::mutex g_scratch_mu;
+
+// The device address of the scratch array on the current device, looked up
+// once per device (the host-side name is not a device address).
+static int scratch_ptr(int device, char** out) {
+  if (device < 0 || device >= kMaxDevices) return fail(KVX_E_UNSUPPORTED, "kvx_plan_noalloc: device %d", device);
+  ScratchSlot& sl = g_scratch[device];
+  char* p = sl.ptr.load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    p = sl.ptr.load(std::memory_order_relaxed);
+    if (!p) {
+      void* addr = nullptr;
+      const hipError_t e = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return fail_hip(e, "kvx_plan_noalloc: hipGetSymbolAddress(scratch)");
+      p = static_cast<char*>(addr);
+      sl.ptr.store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return KVX_OK;
+}
+
 static int check_device_plan(const kvx_plan_t* p, const char* fn) {
   if (!p) return fail(KVX_E_INVAL, "%s: null plan", fn);
   if (p->host_only) return fail(KVX_E_INVAL, "%s: plan was built host-only", fn);
+  if (p->in_scratch && g_scratch[p->device].gen.load(std::memory_order_acquire) != p->scratch_gen)
+    return fail(KVX_E_INVAL, "%s: the plan's work list in the device scratch array was replaced by a later "
+                "kvx_plan_noalloc", fn);
   return KVX_OK;
 }
 
@@ -749,6 +790,48 @@ int kvx_unpack(const kvx_plan_t* cp, int32_t l0, int32_t l1, const void* staging
     rc = launch_copy<kUnpack>(p, a, int64_t(p->blocks.size()), stream);
     if (rc) return rc;
   }
+  return KVX_OK;
+}
+
+int kvx_plan_noalloc(const kvx_pool* src, const kvx_pool* dst, int32_t num_requests, const int64_t* num_tokens,
+                     const int64_t* src_offsets, const int64_t* dst_offsets, const int32_t* src_ids,
+                     const int32_t* dst_ids, uint32_t flags, hipStream_t upload_stream, kvx_plan_t** out) {
+  if (!out) return fail(KVX_E_INVAL, "kvx_plan_noalloc: null output");
+  if (flags & KVX_PLAN_HOST_ONLY) return fail(KVX_E_INVAL, "kvx_plan_noalloc: a host-only plan has no work list");
+  int device = 0;
+  hipError_t e = hipGetDevice(&device);
+  if (e != hipSuccess) return fail_hip(e, "kvx_plan_noalloc: hipGetDevice");
+  char* buf = nullptr;
+  int rc = scratch_ptr(device, &buf);
+  if (rc) return rc;
+  kvx_plan_t* p = nullptr;
+  rc = plan_build(src, dst, num_requests, num_tokens, src_offsets, dst_offsets, src_ids, dst_ids, flags,
+                  upload_stream, &p);
+  if (rc) return rc;
+  const size_t need = worklist_bytes(p);
+  if (need > kScratchBytes) {
+    plan_free_idle(p);
+    return fail(KVX_E_NOMEM, "kvx_plan_noalloc: the work list needs %zu bytes, the scratch array holds %zu "
+                "(build with kvx_plan, or with KVX_PLAN_RUNS for a smaller streaming work list)",
+                need, kScratchBytes);
+  }
+  p->device = device;
+  p->in_scratch = true;
+  p->scratch_gen = g_scratch[device].gen.fetch_add(1, std::memory_order_acq_rel) + 1;
+  p->dev_buf = buf;
+  p->dev_bytes = need;
+  rc = worklist_copy(p, buf, upload_stream);
+  if (rc == KVX_OK) {
+    // no event: the upload is waited for here, so device calls need no wait
+    e = hipStreamSynchronize(upload_stream);
+    if (e != hipSuccess) rc = fail_hip(e, "kvx_plan_noalloc: hipStreamSynchronize(upload)");
+  }
+  if (rc) {
+    plan_free_idle(p);
+    return rc;
+  }
+  p->upload_seen.store(true, std::memory_order_release);
+  *out = p;
   return KVX_OK;
 }
 

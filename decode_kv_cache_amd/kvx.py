@@ -65,6 +65,7 @@ _SIGS = {
     "kvx_state_pool_create": (C.c_int, [C.POINTER(kvx_state_pool_desc), C.POINTER(_P)]),
     "kvx_pool_destroy": (None, [_P]),
     "kvx_plan": (C.c_int, [_P, _P, _I32, _P, _P, _P, _P, _P, _U32, _P, C.POINTER(_P)]),
+    "kvx_plan_noalloc": (C.c_int, [_P, _P, _I32, _P, _P, _P, _P, _P, _U32, _P, C.POINTER(_P)]),
     "kvx_plan_runs": (C.c_int, [_P, _P, _I64, C.POINTER(_I64)]),
     "kvx_plan_triples": (C.c_int, [_P, _I32, _I32, _P, _I64, C.POINTER(_I64)]),
     "kvx_plan_bytes": (C.c_int, [_P, C.POINTER(_I64), C.POINTER(_I64)]),
@@ -389,6 +390,27 @@ def kvx_plan(src: Pool, dst: Pool, num_tokens: Sequence[int], src_tables: Sequen
                         | (KVX_PLAN_RUNS if runs else 0), us,
                         C.byref(h))
     _check("kvx_plan", rc)
+    return Plan(h, src, dst)
+
+
+def kvx_plan_noalloc(src: Pool, dst: Pool, num_tokens: Sequence[int], src_tables: Sequence[Sequence[int]],
+                     dst_tables: Sequence[Sequence[int]], *, overlap: bool = False, runs: bool = False,
+                     stream=None) -> Plan:
+    """kvx_plan whose device work list lives in the library's static scratch
+    array (no device allocation); valid until the next kvx_plan_noalloc on
+    the device."""
+    R = len(num_tokens)
+    if len(src_tables) != R or len(dst_tables) != R:
+        raise ValueError("one src and one dst block list per request")
+    nt = np.ascontiguousarray(num_tokens, dtype=np.int64)
+    so, sid = _csr(src_tables)
+    do, did = _csr(dst_tables)
+    h = C.c_void_p()
+    rc = lib().kvx_plan_noalloc(src.handle, dst.handle, R, nt.ctypes.data, so.ctypes.data, do.ctypes.data,
+                                sid.ctypes.data if sid.size else None, did.ctypes.data if did.size else None,
+                                (KVX_PLAN_OVERLAP if overlap else 0) | (KVX_PLAN_RUNS if runs else 0),
+                                _stream(stream), C.byref(h))
+    _check("kvx_plan_noalloc", rc)
     return Plan(h, src, dst)
 
 

@@ -250,6 +250,31 @@ int kvx_plan(const kvx_pool* src, const kvx_pool* dst, int32_t num_requests,
              const int32_t* src_ids, const int32_t* dst_ids, uint32_t flags,
              hipStream_t upload_stream, kvx_plan_t** out);
 
+/*
+ * kvx_plan without any device allocation, for callers that cannot allocate
+ * device memory (code that runs while a stream is being captured elsewhere
+ * in the process, tight serving loops, harnesses that forbid hipMalloc).
+ * Same arguments, result and errors as kvx_plan, except that the plan's
+ * device work list goes into a static scratch array of 16 MiB that the
+ * library holds on each device it runs on, until the process ends, and that
+ * the upload is waited for on the host before the call returns (no event is
+ * created).  Nothing else is allocated on the device, and no hipMalloc,
+ * hipFree or other allocating runtime call is made; the host tables use the
+ * C++ heap as kvx_plan's do.
+ * The array is shared by every call on the device and keeps only the last
+ * call's work list: a plan built this way is valid until the next
+ * kvx_plan_noalloc on the same device, after which its device calls return
+ * KVX_E_INVAL.  Building a plan while device calls of the previous one are
+ * still running on the device races with them, as do concurrent calls.
+ * Destroying such a plan frees no device memory (and waits for nothing).
+ * Errors: those of kvx_plan; INVAL also for KVX_PLAN_HOST_ONLY; NOMEM when
+ * the work list exceeds the array (KVX_PLAN_RUNS keeps streaming work
+ * lists small). */
+int kvx_plan_noalloc(const kvx_pool* src, const kvx_pool* dst, int32_t num_requests,
+                     const int64_t* num_tokens, const int64_t* src_offsets, const int64_t* dst_offsets,
+                     const int32_t* src_ids, const int32_t* dst_ids, uint32_t flags,
+                     hipStream_t upload_stream, kvx_plan_t** out);
+
 /* Copy the run table into out[0..cap); *n receives the run count.  With
  * out == NULL or cap < count only *n is written (and KVX_OK returned).
  * Runs are block pairs, defined for equal block sizes only (KVX_E_MISMATCH
