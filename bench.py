@@ -61,17 +61,21 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-# The dominant kernel of each workload's bench line, as named in profiles/.
-COUNTER_KERNEL = {"qwen32b_push": "many_kernel", "tp4_share": "heads_kernel", "pack_unpack": "many_kernel"}
+# The dominant kernel of each workload's bench line, as named in profiles/
+# (the kernel that the workload's --counters run launches).
+COUNTER_KERNEL = {"qwen32b_push": "many_kernel", "qwen32b_reblock": "many_kernel", "tiny_push": "many_kernel",
+                  "tp4_share": "heads_kernel", "pack_unpack": "many_kernel", "dsr1_mla_push": "many_kernel",
+                  "gptoss_swa_push": "many_kernel", "qwen3next_state_push": "many_kernel"}
 
 
-def counter_traffic(workload: str):
-    """HBM bytes per launch of the dominant kernel from the committed
-    rocprofv3 --pmc summary (FETCH_SIZE and WRITE_SIZE passes, each scaled by
-    the counter's reading for a plain copy of known size); None when there is
-    no summary or the kernel sources changed since it was taken."""
+def counter_ratio(workload: str, kernel: str = None):
+    """Measured HBM bytes over algorithmic bytes of the dominant kernel's
+    launches, from the committed rocprofv3 --pmc summary (FETCH_SIZE and
+    WRITE_SIZE passes, each scaled by the counter's reading for a plain copy
+    of known size); None when there is no summary or the kernel sources
+    changed since it was taken."""
     from decode_kv_cache_amd.profiling import kernel_source_digest
-    kernel = COUNTER_KERNEL.get(workload, "push_kernel")
+    kernel = kernel or COUNTER_KERNEL.get(workload, "push_kernel")
     path = os.path.join(PROFILES, f"{kernel}_{workload}_pmc.txt")
     if not os.path.exists(path):
         return None
@@ -83,8 +87,8 @@ def counter_traffic(workload: str):
     if kv.get("kernel_source_sha256_16") != kernel_source_digest():
         return None
     try:
-        return float(kv["calibrated_hbm_bytes_per_launch"])
-    except (KeyError, ValueError):
+        return float(kv["calibrated_hbm_bytes_per_launch"]) / float(kv["algorithmic_bytes_per_launch"])
+    except (KeyError, ValueError, ZeroDivisionError):
         return None
 
 
@@ -187,9 +191,15 @@ def inputs_digest(tables, sides, prompt_lens) -> str:
 
 
 def roofline(bytes_per_launch: int, avg_us: float, kernel: str, workload: str, extra=None):
+    """The line's roofline object.  `traffic` is HBM bytes per launch: the
+    counter summary's measured-over-algorithmic ratio for this kernel and
+    workload times the launch's algorithmic bytes."""
     ach = bytes_per_launch / (avg_us * 1e-6) / 1e9
+    ratio = counter_ratio(workload)
     r = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-         "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": counter_traffic(workload), "kernel": kernel,
+         "frac": round(ach / HBM_PEAK_GBS, 4),
+         "traffic": None if ratio is None else round(ratio * bytes_per_launch),
+         "traffic_over_algorithmic": None if ratio is None else round(ratio, 4), "kernel": kernel,
          "avg_launch_us": round(avg_us, 3), "algorithmic_bytes_per_launch": bytes_per_launch}
     if extra:
         r.update(extra)
@@ -275,17 +285,35 @@ class QueueStep:
         nsteps = (w1 - w0) / len(self.pairs)
         return span, per, (g1 - g0) / nsteps, (n1 - n0) / nsteps
 
-    def kernel_us(self, torch, calls=5):
-        """Kernel time of the step's launches once writes back up (one
-        kvx_push_many over every pair), from the launches' own dispatch
-        timestamps: mean us per call."""
-        plans, layers = [p for p, _ in self.pairs], [l for _, l in self.pairs]
-        a = [torch.cuda.Event(enable_timing=True) for _ in range(calls)]
-        b = [torch.cuda.Event(enable_timing=True) for _ in range(calls)]
-        for i in range(calls):
-            self.kvx.kvx_push_many_timed(plans, layers, a[i], b[i], stream=self.side)
+    def launches(self):
+        """The step's pairs as the launches they take once writes back up:
+        each plan's layers (plans in order of first appearance, layers in step
+        order) in runs of up to 32, one kvx_push_many launch each (a plan
+        with per-block scales launches each layer alone)."""
+        per_plan = {}
+        for p, l in self.pairs:
+            per_plan.setdefault(id(p), (p, []))[1].append(l)
+        out = []
+        for p, ls in per_plan.values():
+            k = 1 if getattr(p.src, "_ks", None) is not None else 32
+            out += [(p, ls[i:i + k]) for i in range(0, len(ls), k)]
+        return out
+
+    def launch_us(self, torch, rounds=3):
+        """Kernel time per launch once writes back up, from each launch's own
+        dispatch timestamps (kvx_push_many_timed over one launch's layers):
+        (mean us per launch, mean algorithmic bytes per launch, launches)."""
+        ls = self.launches()
+        ev = []
+        for _ in range(rounds):
+            for p, layers in ls:
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                self.kvx.kvx_push_many_timed([p] * len(layers), layers, a, b, stream=self.side)
+                ev.append((a, b))
         torch.cuda.synchronize()
-        return float(np.mean([a[i].elapsed_time(b[i]) for i in range(calls)]) * 1e3)
+        us = [a.elapsed_time(b) * 1e3 for a, b in ev]
+        nbytes = [sum(p.bytes_per_layer()) * len(layers) for p, layers in ls] * rounds
+        return float(np.mean(us)), float(np.mean(nbytes)), len(ls)
 
     def close(self):
         self.q.close()
@@ -409,11 +437,9 @@ def bench_push(args, torch, kvx, S, W):
 
     # Kernel measurement for the roofline.  Once writes back up, the queue's
     # groups are kvx_push_many launches of 32 layers each (two per step); the
-    # same launches, timed from their own dispatch timestamps.
-    launches_per_call = -(-L // 32)
-    k_avg_us = step.kernel_us(torch) / launches_per_call
-    log(f"batched push kernel: {k_avg_us:.2f} us per launch of {min(L, 32)} layers (dispatch timestamps, "
-        f"{launches_per_call} launches per call)")
+    # same launches, each timed from its own dispatch timestamps.
+    k_avg_us, k_bytes, _ = step.launch_us(torch)
+    log(f"batched push kernel: {k_avg_us:.2f} us per launch of {min(L, 32)} layers (dispatch timestamps)")
 
     # Secondary: one kvx_push_layer launch per layer on the side stream.
     def layer_step():
@@ -571,12 +597,12 @@ def bench_push(args, torch, kvx, S, W):
                    "two_stream_push_layer_GBs": None if two_gbs is None else round(two_gbs, 1),
                    "push_many_all_layers_GBs": round(many_gbs, 1)},
         "ceiling": ceiling,
-        "roofline": roofline(layer_bytes * min(L, 32), k_avg_us,
-                             "kvx::copy_many_kernel<0, 256, 1> (kvx_queue groups / kvx_push_many)", args.workload,
+        "roofline": roofline(round(k_bytes), k_avg_us, "kvx::copy_many_kernel<0> (kvx_queue groups / kvx_push_many)",
+                             args.workload,
                              {"layers_per_launch": min(L, 32),
-                              "measured": f"dispatch timestamps of kvx_push_many_timed over all {L} layers "
-                                          f"({launches_per_call} launches), 5 calls",
-                              "span_us_per_launch": round(ms_per_step * 1e3 / launches_per_call, 3)}),
+                              "measured": f"dispatch timestamps of each launch: kvx_push_many_timed over {min(L, 32)} "
+                                          f"layers (one launch), {-(-L // 32)} per step, 3 rounds",
+                              "span_us_per_launch": round(ms_per_step * 1e3 / -(-L // 32), 3)}),
         "cpu_baseline": cpu,
     }
 
@@ -613,6 +639,13 @@ def bench_hybrid(args, torch, kvx, S, W):
     step_bytes = sum(gbytes[gi] for gi, _ in wl.layer_map)
     log(f"{M} model layers, {step_bytes} B per step, host plans {plan_ms:.2f} ms")
 
+    if args.counters:   # the queue's launches once writes back up: kvx_push_many over every model layer
+        pl, ly = [plans[gi] for gi, _ in wl.layer_map], [l for _, l in wl.layer_map]
+        counters_run(torch, kvx, None, side, 1, step_bytes, launch=lambda _l: kvx.kvx_push_many(pl, ly, stream=side),
+                     what="bytes_per_call")
+        for p in plans:
+            p.close()
+        return None
     ready = [torch.cuda.Event() for _ in range(M)]
     for e in ready:
         e.record(compute)
@@ -676,8 +709,7 @@ def bench_hybrid(args, torch, kvx, S, W):
     log(f"queue step: span {span_ms:.3f} ms for {args.steps} steps ({ms_per_step * 1e3:.1f} us/step, median "
         f"{stats['median_ms'] * 1e3:.1f}); {launches_per_step:.2f} launches per step: {gbs:.1f} GB/s "
         f"= {100 * gbs / HBM_PEAK_GBS:.1f}% of {HBM_PEAK_GBS:.0f} GB/s")
-    nl = max(1, round(launches_per_step))
-    k_call_us = step.kernel_us(torch)
+    k_avg_us, k_bytes, k_launches = step.launch_us(torch)
 
     # Secondary: one kvx_push_layer launch per model layer.
     def layer_step():
@@ -752,10 +784,10 @@ def bench_hybrid(args, torch, kvx, S, W):
                    "launch_groups_per_step": round(groups_per_step, 3),
                    "kernel_launches_per_step": round(launches_per_step, 3),
                    "push_layer_per_launch_GBs": round(layer_gbs, 1)},
-        "roofline": roofline(step_bytes // nl, k_call_us / nl, "kvx::copy_many_kernel<0> (kvx_queue groups)",
-                             args.workload, {"measured": "dispatch timestamps of kvx_push_many_timed over every "
-                                                         "model layer; bytes and duration per launch averaged over "
-                                                         f"its {nl} launches"}),
+        "roofline": roofline(round(k_bytes), k_avg_us, "kvx::copy_many_kernel<0> (kvx_queue groups)",
+                             args.workload, {"measured": "dispatch timestamps of each launch (kvx_push_many_timed "
+                                                         "over up to 32 layers of one layer group); bytes and "
+                                                         f"duration per launch averaged over {k_launches} launches"}),
         "cpu_baseline": cpu,
     }
 
@@ -784,10 +816,12 @@ def two_stream_rate(torch, kvx, plan, ready, side, L, steps, step_bytes):
     return step_bytes * steps / (a.elapsed_time(b) * 1e-3) / 1e9
 
 
-def counters_run(torch, kvx, plan, side, L, bytes_per_launch, launch=None):
+def counters_run(torch, kvx, plan, side, L, bytes_per_launch, launch=None, what="bytes_per_launch"):
     """Kernels for a counter pass: kvxb_copy of CALIB_BYTES (known traffic:
     CALIB_BYTES read + CALIB_BYTES written) three times, then two steps of
-    `launch(layer)` over every layer (default: the layerwise push)."""
+    `launch(layer)` over every layer (default: the layerwise push).  The
+    printed line gives the algorithmic bytes of each `launch` call, or of
+    each kernel launch where those are all alike."""
     from decode_kv_cache_amd import bench_support as B
     if launch is None:
         def launch(l):
@@ -799,8 +833,8 @@ def counters_run(torch, kvx, plan, side, L, bytes_per_launch, launch=None):
         for l in range(L):
             launch(l)
     torch.cuda.synchronize()
-    print(json.dumps({"counters_run": True, "calib_copy_bytes": CALIB_BYTES, "launches": 2 * L,
-                      "bytes_per_launch": bytes_per_launch}), flush=True)
+    print(json.dumps({"counters_run": True, "calib_copy_bytes": CALIB_BYTES, "calls": 2 * L,
+                      what: bytes_per_launch}), flush=True)
 
 
 def bench_batched(args, torch, kvx, S, W):
@@ -970,7 +1004,8 @@ def bench_batched(args, torch, kvx, S, W):
                  "worklist_bytes": worklist_bytes(rplan), "push_alone_ms": round(t_r, 3),
                  "push_alone_GBs": round(step_bytes / (t_r * 1e-3) / 1e9, 1),
                  "pieces_worklist_bytes": worklist_bytes(plan), "pieces_host_plan_ms": round(plan_ms, 3),
-                 "pieces_push_alone_GBs": main["push_alone_GBs"]}
+                 "pieces_push_alone_GBs": main["push_alone_GBs"],
+                 "traffic_over_algorithmic": counter_ratio("batched_push", "run_kernel")}
     log(f"run tables: host plan {rplan_ms:.2f} ms (pieces {plan_ms:.2f}), work list {run_table['worklist_bytes']} B "
         f"(pieces {run_table['pieces_worklist_bytes']}), push alone {run_table['push_alone_GBs']} GB/s")
     rplan.close()
@@ -1474,9 +1509,8 @@ def main():
           "tp4_share": bench_tp4, "multiturn_fp8": bench_multiturn, "pack_unpack": bench_pack,
           "dsr1_mla_push": bench_hybrid, "gptoss_swa_push": bench_hybrid,
           "qwen3next_state_push": bench_hybrid}[args.workload]
-    if args.counters and fn not in (bench_push, bench_batched, bench_tp4, bench_multiturn, bench_pack):
-        print("bench.py: --counters is for the qwen32b_push, tiny_push, batched_push, tp4_share, multiturn_fp8 and "
-              "pack_unpack workloads", file=sys.stderr)
+    if args.counters and fn is bench_xfer:
+        print("bench.py: --counters is not available for xfer_pipeline", file=sys.stderr)
         sys.exit(2)
     r = fn(args, torch, kvx, S, W)
     if r is None:

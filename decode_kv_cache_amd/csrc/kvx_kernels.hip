@@ -522,52 +522,45 @@ class ManyBatch {
     return !p->runs_mode && (int64_t(p->pieces.size()) << piece_shift(p->shape)) <= kMaxGridX;
   }
 
+  // Entries of one-region and of two-region plans gather in launches of
+  // their own (the grid height is the region count), each in arrival order,
+  // so that interleaved layer groups of a hybrid model (attention layers
+  // beside state or latent layers) still fill whole launches.
   int add(const kvx_plan_t* p, const uint8_t* const in[2], uint8_t* const out[2]) {
     const int64_t np = int64_t(p->pieces.size());
     if (np == 0) return KVX_OK;
     const int32_t shift = piece_shift(p->shape);
-    if (m_.n == kManyMax || (m_.n > 0 && (grid_y(p) != gy_ || fine_ + (np << shift) > kMaxGridX))) {
-      const int rc = flush();
+    Group& g = g_[grid_y(p) - 1];
+    if (g.m.n == kManyMax || (g.m.n > 0 && g.fine + (np << shift) > kMaxGridX)) {
+      const int rc = flush_group(g);
       if (rc) return rc;
     }
-    shape_ = m_.n == 0 || p->shape == shape_ ? p->shape : -1;
-    gy_ = grid_y(p);
-    ManyEntry& e = m_.e[m_.n];
+    if (g.m.n == 0) g.seq = ++seq_;
+    g.shape = g.m.n == 0 || p->shape == g.shape ? p->shape : -1;
+    g.gy = grid_y(p);
+    ManyEntry& e = g.m.e[g.m.n];
     e.pieces = p->d_pieces;
-    stream_[m_.n] = p->d_stream;
+    g.stream[g.m.n] = p->d_stream;
     for (int r = 0; r < 2; ++r) {
       e.in[r] = r < p->nreg ? in[r] : nullptr;
       e.out[r] = r < p->nreg ? out[r] : nullptr;
     }
-    np_[m_.n] = int32_t(np);
-    shift_[m_.n] = shift;
-    ++m_.n;
-    n32_ += p->n32;
-    fine_ += np << shift;
+    g.np[g.m.n] = int32_t(np);
+    g.shift[g.m.n] = shift;
+    ++g.m.n;
+    g.n32 += p->n32;
+    g.fine += np << shift;
     return KVX_OK;
   }
 
+  // Launch whatever is gathered, the group started first first.
   int flush() {
-    if (m_.n == 0) return KVX_OK;
-    const bool keep = (shape_ == kShapeLong || shape_ == kShapeLongSmall) && n32_ <= kLongMaxPieces;
-    int64_t total = 0;
-    for (int32_t j = 0; j < m_.n; ++j) {
-      m_.e[j].first = int32_t(total);
-      m_.e[j].shift = keep ? 0 : shift_[j];
-      if (!keep) m_.e[j].pieces = stream_[j];
-      total += int64_t(np_[j]) << m_.e[j].shift;
-    }
-    m_.items = int32_t(total);
-    m_.xcd = xcd_on(!keep, total);
-    m_.span = int32_t(xcd_span(total, m_.xcd));
-    launch_many<MODE>(m_, keep ? shape_ : int32_t(kShapeFine), gy_, s_, started_, finished_);
-    started_ = nullptr;
-    ++launches_;
-    m_.n = 0;
-    n32_ = 0;
-    fine_ = 0;
-    shape_ = -1;
-    return check_launch("kvx copy_many kernel launch");
+    Group* a = &g_[0];
+    Group* b = &g_[1];
+    if (b->m.n && (!a->m.n || b->seq < a->seq)) std::swap(a, b);
+    int rc = flush_group(*a);
+    if (!rc) rc = flush_group(*b);
+    return rc;
   }
 
   // A launch outside the batch (a pair with scales) takes over the start
@@ -582,17 +575,46 @@ class ManyBatch {
   int64_t launches() const { return launches_; }
 
  private:
+  struct Group {
+    ManyArgs m{};
+    int64_t n32 = 0;   // 32 KiB pieces in the launch (all regions)
+    int64_t fine = 0;  // workgroups of the launch in the 4 KiB shape
+    unsigned gy = 0;
+    int32_t shape = -1;  // common shape of the entries, -1 when they differ
+    int64_t seq = 0;     // order of the group's first entry
+    int32_t np[kManyMax] = {};
+    int32_t shift[kManyMax] = {};
+    const Piece* stream[kManyMax] = {};  // each entry's pieces in streaming order
+  };
+
+  int flush_group(Group& g) {
+    if (g.m.n == 0) return KVX_OK;
+    const bool keep = (g.shape == kShapeLong || g.shape == kShapeLongSmall) && g.n32 <= kLongMaxPieces;
+    int64_t total = 0;
+    for (int32_t j = 0; j < g.m.n; ++j) {
+      g.m.e[j].first = int32_t(total);
+      g.m.e[j].shift = keep ? 0 : g.shift[j];
+      if (!keep) g.m.e[j].pieces = g.stream[j];
+      total += int64_t(g.np[j]) << g.m.e[j].shift;
+    }
+    g.m.items = int32_t(total);
+    g.m.xcd = xcd_on(!keep, total);
+    g.m.span = int32_t(xcd_span(total, g.m.xcd));
+    launch_many<MODE>(g.m, keep ? g.shape : int32_t(kShapeFine), g.gy, s_, started_, finished_);
+    started_ = nullptr;
+    ++launches_;
+    g.m.n = 0;
+    g.n32 = 0;
+    g.fine = 0;
+    g.shape = -1;
+    return check_launch("kvx copy_many kernel launch");
+  }
+
   hipStream_t s_;
   hipEvent_t started_, finished_;
   int64_t launches_ = 0;
-  ManyArgs m_{};
-  int64_t n32_ = 0;   // 32 KiB pieces in the launch (all regions)
-  int64_t fine_ = 0;  // workgroups of the launch in the 4 KiB shape
-  unsigned gy_ = 0;
-  int32_t shape_ = -1;  // common shape of the entries, -1 when they differ
-  int32_t np_[kManyMax] = {};
-  int32_t shift_[kManyMax] = {};
-  const Piece* stream_[kManyMax] = {};  // each entry's pieces in streaming order
+  int64_t seq_ = 0;
+  Group g_[2];
 };
 
 // ---------------------------------------------------------------------------

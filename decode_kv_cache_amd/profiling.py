@@ -1,13 +1,17 @@
 """Summaries of rocprofv3 CSV output for the files under profiles/.
 
-  python -m decode_kv_cache_amd.profiling trace <dir> <out.txt> --command "..."
+  python -m decode_kv_cache_amd.profiling trace <dir> <out.txt> --command "..." [--bench-json FILE]
       per-kernel call count and durations from <dir>/*_kernel_stats.csv and
-      *_kernel_trace.csv (rocprofv3 --kernel-trace --stats -f csv)
+      *_kernel_trace.csv (rocprofv3 --kernel-trace --stats -f csv), and the
+      roofline object of the bench.py line printed by the same run
   python -m decode_kv_cache_amd.profiling pmc <fetch_dir> <write_dir> <out.txt> \\
-          --workload NAME --command-fetch "..." --command-write "..."
-      HBM traffic per push-kernel dispatch from a FETCH_SIZE pass and a
+          --workload NAME --kernel K (--push-bytes B | --total-bytes B) \\
+          --command-fetch "..." --command-write "..."
+      HBM traffic per dispatch of kernel K from a FETCH_SIZE pass and a
       WRITE_SIZE pass of ``bench.py --counters``, each scaled by what the same
-      counter reads for the plain copy kernel of known size run first.
+      counter reads for the plain copy kernel of known size run first, against
+      the algorithmic bytes per dispatch (given, or the bytes of every
+      dispatch of K together divided by their number).
 
 The pmc summary carries the digest of the kernel sources it was taken with;
 bench.py reports its traffic only while the sources are unchanged.
@@ -27,7 +31,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 PUSH_KERNEL = "kvx::copy_kernel<0, "   # any launch shape of the push mode
 HEADS_KERNEL = "kvx::heads_kernel"
 MANY_KERNEL = "kvx::copy_many_kernel<"   # batched launches: pack / unpack over layers, kvx_push_many
-KERNELS = {"push": PUSH_KERNEL, "heads": HEADS_KERNEL, "many": MANY_KERNEL}
+RUN_KERNEL = "kvx::run_kernel<0>"       # push of a run-table plan
+KERNELS = {"push": PUSH_KERNEL, "heads": HEADS_KERNEL, "many": MANY_KERNEL, "runs": RUN_KERNEL}
 CALIB_KERNEL = "copy_kernel(unsigned int __vector(4)*"   # kvxb_copy in libkvx_bench.so
 CALIB_BYTES = 1 << 30
 
@@ -81,7 +86,26 @@ def back_to_back(intervals):
     return gaps, union, total
 
 
-def trace_summary(d: str, command: str) -> str:
+def bench_roofline(path: str) -> list:
+    """The roofline object of the last bench.py JSON line in `path`."""
+    import json
+    line = None
+    for ln in open(path):
+        ln = ln.strip()
+        if ln.startswith("{") and '"roofline"' in ln:
+            line = ln
+    if line is None:
+        return ["", "bench.py line: none found"]
+    r = json.loads(line)
+    rf = r["roofline"]
+    return ["", f"bench.py line of the same run: value {r['value']} {r['unit']}, workload {r['config']['workload']}",
+            f"roofline kernel: {rf.get('kernel')}",
+            f"roofline avg_launch_us (dispatch timestamps inside bench.py): {rf.get('avg_launch_us')}",
+            f"roofline algorithmic_bytes_per_launch: {rf.get('algorithmic_bytes_per_launch')}",
+            f"roofline achieved: {rf['achieved']} GB/s, frac {rf['frac']}"]
+
+
+def trace_summary(d: str, command: str, bench_json: str = None) -> str:
     rows = list(csv.DictReader(open(_one(os.path.join(d, "**", "*kernel_stats.csv")))))
     trace = list(csv.DictReader(open(_one(os.path.join(d, "**", "*kernel_trace.csv")))))
     per = defaultdict(list)
@@ -112,6 +136,8 @@ def trace_summary(d: str, command: str) -> str:
         out.append(f"| {_short(name)} | {gx} | {gy} | {qid} | {len(iv)} | {statistics.mean(durs) / 1e3:.2f} | "
                    f"{statistics.median(durs) / 1e3:.2f} | {statistics.median(gaps) / 1e3:.2f} | "
                    f"{union / total:.4f} |")
+    if bench_json:
+        out += bench_roofline(bench_json)
     return "\n".join(out) + "\n"
 
 
@@ -130,13 +156,17 @@ def _avg_for(per, key):
     return sum(vals) / len(vals), len(vals)
 
 
-def pmc_summary(fetch_dir: str, write_dir: str, workload: str, push_bytes: int, cmd_f: str, cmd_w: str,
-                kernel: str = "push") -> str:
+def pmc_summary(fetch_dir: str, write_dir: str, workload: str, push_bytes, cmd_f: str, cmd_w: str,
+                kernel: str = "push", total_bytes=None) -> str:
     f, w = counters(fetch_dir), counters(write_dir)
     cf, ncf = _avg_for(f, CALIB_KERNEL)
     cw, ncw = _avg_for(w, CALIB_KERNEL)
     pf, npf = _avg_for(f, KERNELS[kernel])
     pw, npw = _avg_for(w, KERNELS[kernel])
+    if npf != npw:
+        raise ValueError(f"{kernel}: {npf} dispatches in the FETCH_SIZE pass, {npw} in the WRITE_SIZE pass")
+    if push_bytes is None:
+        push_bytes = round(total_bytes / npf)
     ff = CALIB_BYTES / (cf * 1024)
     fw = CALIB_BYTES / (cw * 1024)
     rd = pf * 1024 * ff
@@ -169,21 +199,24 @@ def main():
     t.add_argument("dir")
     t.add_argument("out")
     t.add_argument("--command", required=True)
+    t.add_argument("--bench-json", default=None, help="stdout of the profiled bench.py run")
     p = sub.add_parser("pmc")
     p.add_argument("fetch_dir")
     p.add_argument("write_dir")
     p.add_argument("out")
     p.add_argument("--workload", required=True)
-    p.add_argument("--push-bytes", type=int, required=True)
+    b = p.add_mutually_exclusive_group(required=True)
+    b.add_argument("--push-bytes", type=int, help="algorithmic bytes per dispatch")
+    b.add_argument("--total-bytes", type=int, help="algorithmic bytes of every dispatch of the kernel together")
     p.add_argument("--command-fetch", required=True)
     p.add_argument("--command-write", required=True)
     p.add_argument("--kernel", choices=sorted(KERNELS), default="push")
     a = ap.parse_args()
     if a.what == "trace":
-        text = trace_summary(a.dir, a.command)
+        text = trace_summary(a.dir, a.command, a.bench_json)
     else:
         text = pmc_summary(a.fetch_dir, a.write_dir, a.workload, a.push_bytes, a.command_fetch, a.command_write,
-                           a.kernel)
+                           a.kernel, a.total_bytes)
     with open(a.out, "w") as fh:
         fh.write(text)
     print(text)
