@@ -375,9 +375,11 @@ int kvx_push_layer_timed(const kvx_plan_t* plan, int32_t layer, hipEvent_t ready
  * (offset, offset, size) lists ([MORI] §6), for requests whose plans were
  * built at different times (a transfer starts when its consumer registers),
  * and the flush of several deferred layers of one request.  Plans may have
- * different pools.  Consecutive pairs with the same region count share a
- * launch of up to 32 entries; pairs with per-block scales, or whose work
- * list alone fills a launch, run as launches of their own, in order.  A
+ * different pools.  Pairs with the same region count share launches of up
+ * to 32 entries, in their order (one-region and two-region pairs gather
+ * apart, so the launches of the two kinds may go out in either order); pairs
+ * with per-block scales, or whose work list alone fills a launch, run as
+ * launches of their own, in order.  A
  * shared launch runs in its plans' common one-wave shape when it stays
  * within about one round of it, else as 4 KiB chunks of every plan's pieces,
  * each plan's taken in destination order (see kvx_plan_launch_shape).
