@@ -13,6 +13,7 @@
 #include <cstring>
 #include <mutex>
 #include <new>
+#include <utility>
 #include <vector>
 
 #include "kvx_arena.h"
@@ -372,6 +373,40 @@ int32_t pick_shape(kvx_plan_t* p) {
   return n32 >= kLongMinPieces ? kShapeLong : kShapeLongSmall;
 }
 
+// Indices of a triple list in destination-offset order: an LSD radix sort of
+// (offset, index) pairs on 11-bit digits, skipping the digits every offset
+// shares (offsets below 4 GiB take three passes).  The comparison sort it
+// replaces took 1.5 ms for the batched push's 27k triples.
+std::vector<int32_t> dst_order(const std::vector<kvx_triple>& tr) {
+  constexpr int kBits = 11;
+  constexpr uint64_t kMask = (uint64_t(1) << kBits) - 1;
+  const size_t n = tr.size();
+  std::vector<std::pair<uint64_t, int32_t>> a(n), b(n);
+  uint64_t any = 0, all = ~uint64_t(0);
+  for (size_t i = 0; i < n; ++i) {
+    a[i] = {uint64_t(tr[i].dst_off), int32_t(i)};
+    any |= a[i].first;
+    all &= a[i].first;
+  }
+  std::vector<uint32_t> count(size_t(1) << kBits);
+  for (int shift = 0; shift < 64; shift += kBits) {
+    if ((((any ^ all) >> shift) & kMask) == 0) continue;  // this digit is the same in every offset
+    std::fill(count.begin(), count.end(), 0u);
+    for (const auto& e : a) ++count[(e.first >> shift) & kMask];
+    uint32_t sum = 0;
+    for (uint32_t& c : count) {
+      const uint32_t k = c;
+      c = sum;
+      sum += k;
+    }
+    for (const auto& e : a) b[count[(e.first >> shift) & kMask]++] = e;
+    a.swap(b);
+  }
+  std::vector<int32_t> order(n);
+  for (size_t i = 0; i < n; ++i) order[i] = a[i].second;
+  return order;
+}
+
 // First run of each group of kRunGroupChunks chunks of a run table's flat
 // space: the run that holds the group's first 16-byte unit.
 std::vector<uint32_t> run_index(const std::vector<RunRec>& runs, uint32_t total16) {
@@ -412,9 +447,7 @@ void build_runs(kvx_plan_t* p) {
   }
   p->run_total16 = pos;
   p->payload[0] = p->payload[1] = int64_t(pos) * 16;
-  std::vector<int32_t> order(n);
-  for (size_t i = 0; i < n; ++i) order[i] = int32_t(i);
-  std::sort(order.begin(), order.end(), [&tr](int32_t a, int32_t b) { return tr[a].dst_off < tr[b].dst_off; });
+  const std::vector<int32_t> order = dst_order(tr);
   p->runs_dst.resize(n);
   pos = 0;
   for (size_t k = 0; k < n; ++k) {
@@ -456,14 +489,20 @@ void build_pieces(kvx_plan_t* p) {
   const bool by_dst = p->shape == kShapeFine;
   std::vector<int64_t> stg;
   std::vector<int32_t> order;
+  size_t count = 0;
+  for (int32_t r = 0; r < p->nlists; ++r)
+    for (const kvx_triple& t : p->triples[r]) count += size_t((t.len + piece - 1) / piece);
+  p->pieces.reserve(count);
   for (int32_t r = 0; r < p->nlists; ++r) {
     const std::vector<kvx_triple>& tr = p->triples[r];
     stg.assign(tr.size() + 1, 0);
     for (size_t i = 0; i < tr.size(); ++i) stg[i + 1] = stg[i] + tr[i].len;
-    order.resize(tr.size());
-    for (size_t i = 0; i < tr.size(); ++i) order[i] = int32_t(i);
-    if (by_dst)
-      std::sort(order.begin(), order.end(), [&tr](int32_t a, int32_t b) { return tr[a].dst_off < tr[b].dst_off; });
+    if (by_dst) {
+      order = dst_order(tr);
+    } else {
+      order.resize(tr.size());
+      for (size_t i = 0; i < tr.size(); ++i) order[i] = int32_t(i);
+    }
     for (const int32_t i : order) {
       const kvx_triple& t = tr[size_t(i)];
       for (int64_t o = 0; o < t.len; o += piece) {
@@ -621,6 +660,11 @@ int build_plan(kvx_plan_t* p, int32_t R, const int64_t* num_tokens, const int64_
   const Geom& gd = p->dst;
   const int64_t bss = gs.BS, bsd = gd.BS;
   if (R > 0 && (so[0] < 0 || dof[0] < 0)) return fail(KVX_E_INVAL, "kvx_plan: negative first offset");
+  // Each planned block takes one source ID of the caller's lists, so their
+  // total length bounds the block list.  Nothing is validated yet, so the
+  // reservation is capped (4M blocks, 64 MiB); past that the list grows.
+  if (bss == bsd && R > 0 && so[R] > so[0])
+    p->blocks.reserve(size_t(std::min<int64_t>(so[R] - so[0], int64_t(1) << 22)));
   std::vector<uint8_t> dst_used(size_t(gd.NB), 0);
   for (int32_t r = 0; r < R; ++r) {
     const int64_t n = num_tokens[r];
