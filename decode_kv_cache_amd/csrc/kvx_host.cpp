@@ -323,6 +323,7 @@ void build_triples(kvx_plan_t* p) {
   const Geom& gs = p->src;
   const Geom& gd = p->dst;
   const int64_t tb = gs.token_bytes(), rb = gs.row_bytes();
+  p->triples[0].reserve(p->blocks.size() * (gs.layout == KVX_NHD ? 1 : size_t(gs.H)));
   for (const BlockPair& b : p->blocks) {
     const int64_t ss = slot_src(b.slots), ds = slot_dst(b.slots);
     const int64_t sbase = int64_t(b.src) * gs.block_bytes(), dbase = int64_t(b.dst) * gd.block_bytes();
@@ -663,8 +664,11 @@ int build_plan(kvx_plan_t* p, int32_t R, const int64_t* num_tokens, const int64_
   // Each planned block takes one source ID of the caller's lists, so their
   // total length bounds the block list.  Nothing is validated yet, so the
   // reservation is capped (4M blocks, 64 MiB); past that the list grows.
-  if (bss == bsd && R > 0 && so[R] > so[0])
-    p->blocks.reserve(size_t(std::min<int64_t>(so[R] - so[0], int64_t(1) << 22)));
+  if (bss == bsd && R > 0 && so[R] > so[0]) {
+    const size_t cap = size_t(std::min<int64_t>(so[R] - so[0], int64_t(1) << 22));
+    p->blocks.reserve(cap);
+    p->runs.reserve(cap);
+  }
   std::vector<uint8_t> dst_used(size_t(gd.NB), 0);
   for (int32_t r = 0; r < R; ++r) {
     const int64_t n = num_tokens[r];
