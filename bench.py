@@ -225,10 +225,20 @@ def workload(W, name: str, args):
 
 
 def timed_steps(torch, stream, step, steps, warmup):
-    """W untimed steps, then `steps` steps with an event between consecutive
-    steps on `stream`: (total span ms, per-step spans ms)."""
+    """W untimed steps; then `steps` steps between two events on `stream`,
+    after a synchronize on both sides (the span); then `steps` more with an
+    event between consecutive steps (the per-step spans).  (span ms,
+    per-step spans ms).  The events between steps are left out of the span:
+    each costs a few microseconds of the stream's time (about 9 us, 1.3%, on
+    a queue step of the Qwen3-32B-shaped push)."""
     for _ in range(warmup):
         step()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(steps):
+        step()
+    b.record(stream)
     torch.cuda.synchronize()
     marks = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     marks[0].record(stream)
@@ -237,14 +247,14 @@ def timed_steps(torch, stream, step, steps, warmup):
         marks[i + 1].record(stream)
     torch.cuda.synchronize()
     per = np.array([marks[i].elapsed_time(marks[i + 1]) for i in range(steps)])
-    return marks[0].elapsed_time(marks[-1]), per
+    return a.elapsed_time(b), per
 
 
-def span_stats(per_step_ms) -> dict:
+def span_stats(per_step_ms, how="a second pass of the steps, an event between consecutive steps") -> dict:
     a = np.asarray(per_step_ms, dtype=np.float64)
     return {"median_ms": round(float(np.median(a)), 4), "min_ms": round(float(a.min()), 4),
             "p90_ms": round(float(np.percentile(a, 90)), 4), "mean_ms": round(float(a.mean()), 4),
-            "steps": int(a.size)}
+            "steps": int(a.size), "pass": how}
 
 
 def worklist_bytes(plan) -> int:
@@ -954,7 +964,8 @@ def bench_batched(args, torch, kvx, S, W):
              "push_alone_ms": round(t_p, 3), "push_alone_GBs": round(step_bytes / (t_p * 1e-3) / 1e9, 1),
              "compute_alone_ms": round(t_c, 3), "overlapped_ms": round(t_b, 3),
              "overlapped_GBs": round(step_bytes / (t_b * 1e-3) / 1e9, 1),
-             "overlap_efficiency": round(eff, 3), "span": span_stats(per)}
+             "overlap_efficiency": round(eff, 3),
+             "span": span_stats(per, "the overlapped steps, an event between consecutive steps")}
         log(f"{mode}: push alone {t_p:.2f} ms ({r['push_alone_GBs']} GB/s), compute alone {t_c:.2f} ms, "
             f"overlapped {t_b:.2f} ms -> {r['overlapped_GBs']} GB/s, overlap efficiency {eff:.2f}")
         return r, per
@@ -1197,10 +1208,13 @@ def bench_multiturn(args, torch, kvx, S, W):
                                     f"scale of prefill-pool layers {layers} against the oracle's turn-by-turn "
                                     f"replay", nbytes)
         del dsnap, psnap, state
-    # per-turn spans: an event between the turns of every step
     for _ in range(args.warmup):
         step()
-    torch.cuda.synchronize()
+    with Timer(torch, side) as t:
+        for _ in range(args.steps):
+            step()
+    ms = t.ms / args.steps
+    # per-turn spans: a second pass, an event between the turns of every step
     nt = len(plans)
     marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps * nt + 1)]
     marks[0].record(side)
@@ -1212,7 +1226,6 @@ def bench_multiturn(args, torch, kvx, S, W):
     torch.cuda.synchronize()
     spans = np.array([marks[k].elapsed_time(marks[k + 1]) for k in range(args.steps * nt)]).reshape(args.steps, nt)
     per_step = spans.sum(axis=1)
-    ms = marks[0].elapsed_time(marks[-1]) / args.steps
     gbs = step_bytes / (ms * 1e-3) / 1e9
     launches = len(plans) * L
     turn_bytes = [sum(p.bytes_per_layer()) * L for _, p in plans]
@@ -1265,7 +1278,8 @@ def bench_multiturn(args, torch, kvx, S, W):
     for _, p in plans:
         p.close()
     return {
-        "value": gbs, "ms_per_step": ms, "dtype": "u8", "parity": parity, "span": span_stats(per_step),
+        "value": gbs, "ms_per_step": ms, "dtype": "u8", "parity": parity,
+        "span": span_stats(per_step, "a second pass of the steps, an event between consecutive turns"),
         "config": {"workload": wl.name, "seed": wl.seed, "inputs_sha256_16": digest, "layers": L,
                    "kv_heads": wl.src.num_heads, "head_dim": wl.src.head_dim, "per_turn": per_turn,
                    "work_list": "run tables (KVX_PLAN_RUNS)" if args.runs else "cut pieces",
@@ -1453,7 +1467,7 @@ def bench_xfer(args, torch, kvx, S, W):
         f"one plan per layer without the state machine: {raw:.1f} GB/s")
     ref.close()
     return {
-        "value": gbs, "ms_per_step": ms, "dtype": "u8", "parity": parity, "span": span_stats([r[0] for r in res]),
+        "value": gbs, "ms_per_step": ms, "dtype": "u8", "parity": parity, "span": span_stats([r[0] for r in res], "per step of the timed run (host-paced saves)"),
         "config": {"workload": "xfer_pipeline", "seed": wl.seed, "inputs_sha256_16": digest, "geometry": "batched_push", "requests": R, "layers": L,
                    "bytes_per_step": step_bytes,
                    "step": f"{R} requests x {L} layers through kvx_xfer (half registered after the forward pass), "
