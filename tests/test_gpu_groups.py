@@ -192,10 +192,13 @@ def _now(side, layer):
     return _snap(side, layer)
 
 
-def hybrid_full(wl, sample):
-    """Push every model layer in model order on one side stream; check the
-    sampled (group, layer-in-group) pairs against the oracle."""
-    say("workload", wl.name)
+def hybrid_full(wl, sample, via="layer"):
+    """Push every model layer in model order on one side stream (one
+    kvx_push_layer per layer, the stream's write queue with fired events, or
+    one kvx_push_many call over every layer: the last two gather one-region
+    and two-region layers into launches of their own); check the sampled
+    (group, layer-in-group) pairs against the oracle."""
+    say("workload", wl.name, "via", via)
     sides, plans, ops = [], [], []
     toks = toks_of(wl)
     for gi, g in enumerate(wl.groups):
@@ -211,10 +214,26 @@ def hybrid_full(wl, sample):
     torch.cuda.synchronize()
     snaps = {(gi, l): (_snap(sides[gi][0], l), _snap(sides[gi][1], l)) for gi, l in sample}
     side = torch.cuda.Stream()
-    for gi, l in wl.layer_map:
-        e = torch.cuda.Event()
-        e.record()
-        kvx.kvx_push_layer(plans[gi], l, ready=e, stream=side)
+    if via == "layer":
+        for gi, l in wl.layer_map:
+            e = torch.cuda.Event()
+            e.record()
+            kvx.kvx_push_layer(plans[gi], l, ready=e, stream=side)
+    elif via == "queue":   # events fired before the writes are queued: the writes back up and merge
+        evs = [torch.cuda.Event() for _ in wl.layer_map]
+        for e in evs:
+            e.record()
+        torch.cuda.synchronize()
+        q = kvx.Queue(side)
+        for (gi, l), e in zip(wl.layer_map, evs):
+            q.push(plans[gi], l, ready=e)
+        q.flush()
+        w, g, n = q.stats3()
+        assert w == len(wl.layer_map) and n < w, (w, g, n)
+        q.close()
+    else:
+        kvx.kvx_push_many([plans[gi] for gi, _ in wl.layer_map], [l for _, l in wl.layer_map],
+                          ready=torch.cuda.current_stream().record_event(), stream=side)
     side.synchronize()
     for gi, l in sample:
         (skv, ssc), (dkv, dsc) = snaps[(gi, l)]
@@ -248,3 +267,11 @@ def test_gptoss_swa_full():
 
 def test_qwen3next_state_full():
     hybrid_full(W.qwen3next_state_push(), [(0, 0), (0, 11), (1, 0), (1, 35)])
+
+
+def test_qwen3next_state_full_queue():
+    hybrid_full(W.qwen3next_state_push(), [(0, 0), (0, 11), (1, 0), (1, 35)], via="queue")
+
+
+def test_gptoss_swa_full_push_many():
+    hybrid_full(W.gptoss_swa_push(), [(0, 0), (0, 17), (1, 0), (1, 17)], via="many")
