@@ -30,7 +30,7 @@ from collections import defaultdict
 PKG = os.path.dirname(os.path.abspath(__file__))
 PUSH_KERNEL = "kvx::copy_kernel<0, "   # any launch shape of the push mode
 HEADS_KERNEL = "kvx::heads_kernel"
-MANY_KERNEL = "kvx::copy_many_kernel<"   # batched launches: pack / unpack over layers, kvx_push_many
+MANY_KERNEL = ("kvx::copy_many_kernel<", "kvx::scale_many_kernel<")   # batched launches and their scale launches
 RUN_KERNEL = "kvx::run_kernel<0>"       # push of a run-table plan
 KERNELS = {"push": PUSH_KERNEL, "heads": HEADS_KERNEL, "many": MANY_KERNEL, "runs": RUN_KERNEL}
 CALIB_KERNEL = "copy_kernel(unsigned int __vector(4)*"   # kvxb_copy in libkvx_bench.so
@@ -150,7 +150,8 @@ def counters(d: str):
 
 
 def _avg_for(per, key):
-    vals = [v for k, vs in per.items() if key in k for v in vs]
+    keys = key if isinstance(key, tuple) else (key,)
+    vals = [v for k, vs in per.items() if any(x in k for x in keys) for v in vs]
     if not vals:
         raise KeyError(key)
     return sum(vals) / len(vals), len(vals)

@@ -377,9 +377,10 @@ int kvx_push_layer_timed(const kvx_plan_t* plan, int32_t layer, hipEvent_t ready
  * and the flush of several deferred layers of one request.  Plans may have
  * different pools.  Pairs with the same region count share launches of up
  * to 32 entries, in their order (one-region and two-region pairs gather
- * apart, so the launches of the two kinds may go out in either order); pairs
- * with per-block scales, or whose work list alone fills a launch, run as
- * launches of their own, in order.  A
+ * apart, so the launches of the two kinds may go out in either order); the
+ * per-block scales of a launch's pairs follow in one small launch behind
+ * it; pairs whose work list alone fills a launch, and run-table plans, run
+ * as launches of their own, in order.  A
  * shared launch runs in its plans' common one-wave shape when it stays
  * within about one round of it, else as 4 KiB chunks of every plan's pieces,
  * each plan's taken in destination order (see kvx_plan_launch_shape).
@@ -476,9 +477,10 @@ int kvx_staging_bytes(const kvx_plan_t* plan, int32_t l0, int32_t l1, int64_t* b
  * (with scales) the planned blocks' fp32 scales in plan order, zero-padded to
  * 16 bytes.  `staging` is device memory, 16-B aligned, of `cap` bytes >=
  * kvx_staging_bytes.  The src pool of the plan is read; nothing else is
- * written.  Launches: a plan without scales copies up to 32 layers per
+ * written.  Launches: a plan of cut pieces copies up to 32 layers per
  * kernel launch (fewer when a launch would exceed 2^22 workgroups of 4 KiB),
- * a plan with scales one layer per launch.  Errors: INVAL (null, cap too
+ * with the scales, if any, in one small launch behind each; a run-table
+ * plan one layer per launch.  Errors: INVAL (null, cap too
  * small, host-only plan), RANGE, MISMATCH, UNSUPPORTED (staging
  * misaligned), HIP.
  */

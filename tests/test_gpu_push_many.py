@@ -3,9 +3,10 @@ launches, leaves every destination exactly as the oracle's push of each pair
 does.  The list mixes K/V, latent, sliding-window and state-slot plans with
 different pools (so grid heights differ between neighbours), more than 32
 pairs (several launches), the three launch shapes (long runs of whole
-blocks, long state slots in a small launch, short runs), a plan with scales
-and an empty plan in the middle (launched alone or skipped), and a pair
-repeated in a later call.
+blocks, long state slots in a small launch, short runs), plans with per-block
+scales (K/V in both layouts and a latent pool: their scales go out in a
+small launch behind each batched launch), an empty plan (skipped), and a
+pair repeated in a later call.
 Argument errors enqueue nothing."""
 import numpy as np
 import pytest
@@ -75,6 +76,10 @@ def cases():
                                   elem_bytes=1, has_scales=True, num_requests=3, max_tokens=300)))
     out.append(Case(W.random_case(9014, num_layers=4, num_blocks=64, block_size=16, num_heads=2, head_dim=64,
                                   num_requests=1, max_tokens=0)))
+    out.append(Case(W.random_case(9018, num_layers=4, num_blocks=700, block_size=4, num_heads=4, head_dim=32,
+                                  elem_bytes=1, has_scales=True, num_requests=4, max_tokens=500, layout="HND")))
+    out.append(Case(W.random_case(9019, num_layers=4, num_blocks=600, block_size=1, num_heads=1, head_dim=576,
+                                  elem_bytes=1, has_scales=True, num_requests=3, max_tokens=200, regions=1)))
     # whole 32 KiB blocks in long runs, enough of them for the 32 KiB one-wave
     # launch shape; and state slots of 64 KiB + 128 KiB (16 KiB one-wave shape)
     spec = W.PoolSpec(4, 1200, 16, 8, 128, W.BF16)
@@ -91,7 +96,7 @@ def cases():
 def test_push_many_matches_oracle():
     cs = cases()
     rng = np.random.Generator(np.random.PCG64(5))
-    # every (case, layer) pair once, shuffled: 52 pairs, destinations disjoint
+    # every (case, layer) pair once, shuffled: 60 pairs, destinations disjoint
     pairs = [(c, l) for c in cs for l in range(4)]
     order = rng.permutation(len(pairs))
     pairs = [pairs[i] for i in order]
