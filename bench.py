@@ -64,6 +64,7 @@ def log(*a):
 # The dominant kernel of each workload's bench line, as named in profiles/
 # (the kernel that the workload's --counters run launches).
 COUNTER_KERNEL = {"qwen32b_push": "many_kernel", "qwen32b_reblock": "many_kernel", "tiny_push": "many_kernel",
+                  "multiturn_fp8": "many_kernel",
                   "tp4_share": "heads_kernel", "pack_unpack": "many_kernel", "dsr1_mla_push": "many_kernel",
                   "gptoss_swa_push": "many_kernel", "qwen3next_state_push": "many_kernel"}
 
@@ -274,6 +275,37 @@ def worklist_bytes(plan) -> int:
     return copies * 32 * pieces + 16 * blocks
 
 
+def launch_groups(pairs):
+    """(plan, layer) pairs as the launches they take once writes back up:
+    each plan's layers (plans in order of first appearance, layers in the
+    pairs' order) in runs of up to 32, one kvx_push_many launch each (with
+    per-block scales, that launch and the small scale launch behind it)."""
+    per_plan = {}
+    for p, l in pairs:
+        per_plan.setdefault(id(p), (p, []))[1].append(l)
+    out = []
+    for p, ls in per_plan.values():
+        out += [(p, ls[i:i + 32]) for i in range(0, len(ls), 32)]
+    return out
+
+
+def launch_group_us(torch, kvx, side, pairs, rounds=3):
+    """Kernel time per launch group once writes back up, from the launches'
+    own dispatch timestamps (kvx_push_many_timed over one group's layers):
+    (mean us per group, mean algorithmic bytes per group, groups)."""
+    ls = launch_groups(pairs)
+    ev = []
+    for _ in range(rounds):
+        for p, layers in ls:
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            kvx.kvx_push_many_timed([p] * len(layers), layers, a, b, stream=side)
+            ev.append((a, b))
+    torch.cuda.synchronize()
+    us = [a.elapsed_time(b) * 1e3 for a, b in ev]
+    nbytes = [sum(p.bytes_per_layer()) * len(layers) for p, layers in ls] * rounds
+    return float(np.mean(us)), float(np.mean(nbytes)), len(ls)
+
+
 class QueueStep:
     """The layerwise step through one write queue on `side`: for each (plan,
     layer) pair, kvx_queue_push(plan, layer, ready[i]), then kvx_queue_flush."""
@@ -295,35 +327,8 @@ class QueueStep:
         nsteps = (w1 - w0) / len(self.pairs)
         return span, per, (g1 - g0) / nsteps, (n1 - n0) / nsteps
 
-    def launches(self):
-        """The step's pairs as the launches they take once writes back up:
-        each plan's layers (plans in order of first appearance, layers in step
-        order) in runs of up to 32, one kvx_push_many launch each (a plan
-        with per-block scales launches each layer alone)."""
-        per_plan = {}
-        for p, l in self.pairs:
-            per_plan.setdefault(id(p), (p, []))[1].append(l)
-        out = []
-        for p, ls in per_plan.values():
-            k = 1 if getattr(p.src, "_ks", None) is not None else 32
-            out += [(p, ls[i:i + k]) for i in range(0, len(ls), k)]
-        return out
-
     def launch_us(self, torch, rounds=3):
-        """Kernel time per launch once writes back up, from each launch's own
-        dispatch timestamps (kvx_push_many_timed over one launch's layers):
-        (mean us per launch, mean algorithmic bytes per launch, launches)."""
-        ls = self.launches()
-        ev = []
-        for _ in range(rounds):
-            for p, layers in ls:
-                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                self.kvx.kvx_push_many_timed([p] * len(layers), layers, a, b, stream=self.side)
-                ev.append((a, b))
-        torch.cuda.synchronize()
-        us = [a.elapsed_time(b) * 1e3 for a, b in ev]
-        nbytes = [sum(p.bytes_per_layer()) * len(layers) for p, layers in ls] * rounds
-        return float(np.mean(us)), float(np.mean(nbytes)), len(ls)
+        return launch_group_us(torch, self.kvx, self.side, self.pairs, rounds)
 
     def close(self):
         self.q.close()
@@ -1146,7 +1151,8 @@ def bench_tp4(args, torch, kvx, S, W):
 def bench_multiturn(args, torch, kvx, S, W):
     """multiturn_fp8: turns 2..8, each copies every session's retained prefix
     (2048 (t-1) tokens, reused because it reaches the 512-token threshold)
-    from the decode pool back to the prefill pool, layer by layer."""
+    from the decode pool back to the prefill pool: every layer's write
+    through the side stream's write queue, one flush per turn."""
     wl = workload(W, "multiturn_fp8", args)
     ex = wl.extra
     dec, pre = S.device_side(wl.src, wl.seed, 1), S.device_side(wl.dst, wl.seed, 2)
@@ -1166,14 +1172,27 @@ def bench_multiturn(args, torch, kvx, S, W):
         plans.append((t, p))
         step_bytes += sum(p.bytes_per_layer()) * L
 
+    # The step: each turn's layers through the side stream's write queue (the
+    # decode side holds every layer already, so the writes are ready at
+    # once), then a flush: the turns write the same prefill pool, so each
+    # turn's writes go out behind the previous turn's.
+    q = kvx.Queue(side)
+
     def step():
         for _, p in plans:
             for l in range(L):
+                q.push(p, l)
+            q.flush()
+
+    def layer_step():
+        for _, p in plans:
+            for l in range(L):
                 kvx.kvx_push_layer(p, l, stream=side)
-    if args.counters:   # every (turn, layer) launch of a step; bytes are the average per launch
-        n = len(plans) * L
-        counters_run(torch, kvx, None, side, n, step_bytes // n,
-                     launch=lambda i: kvx.kvx_push_layer(plans[i // L][1], i % L, stream=side))
+    if args.counters:   # a step's batched launches: kvx_push_many over every layer of each turn
+        counters_run(torch, kvx, None, side, len(plans), step_bytes // len(plans),
+                     launch=lambda i: kvx.kvx_push_many([plans[i][1]] * L, list(range(L)), stream=side),
+                     what="bytes_per_call")
+        q.close()
         for _, p in plans:
             p.close()
         return None
@@ -1204,7 +1223,7 @@ def bench_multiturn(args, torch, kvx, S, W):
                 bad.append(f"layer {l} scales")
             if not np.array_equal(dec.kv[l].cpu().numpy(), dsnap[l][0]):
                 bad.append(f"layer {l}: decode pool changed")
-        parity = parity_record(bad, f"one step (turns {[t for t, _ in plans]}) on the fresh pools: every byte and "
+        parity = parity_record(bad, f"one step through kvx_queue (turns {[t for t, _ in plans]}) on the fresh pools: every byte and "
                                     f"scale of prefill-pool layers {layers} against the oracle's turn-by-turn "
                                     f"replay", nbytes)
         del dsnap, psnap, state
@@ -1214,20 +1233,28 @@ def bench_multiturn(args, torch, kvx, S, W):
         for _ in range(args.steps):
             step()
     ms = t.ms / args.steps
-    # per-turn spans: a second pass, an event between the turns of every step
+    # per-turn spans: a second pass, an event behind each turn's flush
     nt = len(plans)
+    w0, g0, n0 = q.stats3()
     marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps * nt + 1)]
     marks[0].record(side)
     for i in range(args.steps):
         for j, (_, p) in enumerate(plans):
             for l in range(L):
-                kvx.kvx_push_layer(p, l, stream=side)
+                q.push(p, l)
+            q.flush()
             marks[i * nt + j + 1].record(side)
     torch.cuda.synchronize()
+    w1, g1, n1 = q.stats3()
+    launches_per_step = (n1 - n0) / args.steps
+    k_us, k_bytes, k_groups = launch_group_us(torch, kvx, side, [(p, l) for _, p in plans for l in range(L)])
+    lspan, _ = timed_steps(torch, side, layer_step, args.steps, 1)
+    layer_gbs = step_bytes * args.steps / (lspan * 1e-3) / 1e9
+    log(f"queue: {launches_per_step:.1f} launches per step; batched launch groups {k_us:.1f} us each; "
+        f"one kvx_push_layer launch per layer: {layer_gbs:.1f} GB/s")
     spans = np.array([marks[k].elapsed_time(marks[k + 1]) for k in range(args.steps * nt)]).reshape(args.steps, nt)
     per_step = spans.sum(axis=1)
     gbs = step_bytes / (ms * 1e-3) / 1e9
-    launches = len(plans) * L
     turn_bytes = [sum(p.bytes_per_layer()) * L for _, p in plans]
     per_turn = [{"turn": t, "median_ms": round(float(np.median(spans[:, j])), 4),
                  "min_ms": round(float(spans[:, j].min()), 4), "p90_ms": round(float(np.percentile(spans[:, j], 90)), 4),
@@ -1252,7 +1279,9 @@ def bench_multiturn(args, torch, kvx, S, W):
     alt_gbs = step_bytes * args.steps / (alt_span * 1e-3) / 1e9
     other = {"work_list": "cut pieces" if args.runs else "run tables (KVX_PLAN_RUNS)",
              "taken": [p.launch_shape()["run_table"] for p in alt],
-             "GBs": round(alt_gbs, 1), "host_plan_ms_all_turns": round(alt_ms, 2),
+             "GBs_one_launch_per_layer": round(alt_gbs, 1),
+             "this_line_GBs_one_launch_per_layer": round(layer_gbs, 1),
+             "host_plan_ms_all_turns": round(alt_ms, 2),
              "worklist_bytes": sum(worklist_bytes(p) for p in alt),
              "this_line_worklist_bytes": sum(worklist_bytes(p) for _, p in plans)}
     log(f"with {other['work_list']}: {alt_gbs:.1f} GB/s, host plans {alt_ms:.2f} ms (this line {plan_ms:.2f}), "
@@ -1275,6 +1304,7 @@ def bench_multiturn(args, torch, kvx, S, W):
                            args.cpu_seconds, setup)
         log(f"cpu baseline: {cpu['value']} GB/s")
     turns = [t for t, _ in plans]
+    q.close()
     for _, p in plans:
         p.close()
     return {
@@ -1287,10 +1317,17 @@ def bench_multiturn(args, torch, kvx, S, W):
                    "block_size": wl.src.block_size, "payload_dtype": wl.src.dtype, "scales": "fp32 per block",
                    "sessions": ex["sessions"], "turns_copied": turns, "threshold_tokens": ex["threshold"],
                    "bytes_per_step": step_bytes,
-                   "step": f"turns 2..8: {L} x kvx_push_layer (decode -> prefill) per turn",
+                   "step": f"turns 2..8: {L} x kvx_queue_push (decode -> prefill, no event) per turn, then "
+                           f"kvx_queue_flush, on one side stream",
+                   "kernel_launches_per_step": round(launches_per_step, 2),
+                   "push_layer_per_launch_GBs": round(layer_gbs, 1),
                    "host_plan_ms_all_turns": round(plan_ms, 2)},
-        "roofline": roofline(step_bytes // launches, ms * 1e3 / launches, "kvx::copy_kernel<0> (kvx_push_layer)",
-                             wl.name, {"note": "average over the turns' launches (sizes grow with the turn)"}),
+        "roofline": roofline(round(k_bytes), k_us, "kvx::copy_many_kernel<0> + kvx::scale_many_kernel<0> (kvx_queue "
+                             "groups)", wl.name,
+                             {"measured": f"dispatch timestamps of each launch group (kvx_push_many_timed over up to "
+                                          f"32 layers of one turn: the payload launch and the small scale launch "
+                                          f"behind it), {k_groups} groups per step, 3 rounds; sizes grow with the "
+                                          f"turn"}),
         "cpu_baseline": cpu,
     }
 
