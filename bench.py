@@ -1069,7 +1069,7 @@ def bench_batched(args, torch, kvx, S, W):
 
 
 def bench_tp4(args, torch, kvx, S, W):
-    """tp4_share: per layer, TP4 rank 0's 2-head slice NHD -> HND."""
+    """tp4_share: TP4 rank 0's 2-head slice NHD -> HND of every layer (kvx_copy_heads_layers)."""
     wl = workload(W, "tp4_share", args)
     gs, gd = S.device_side(wl.src, wl.seed, 1), S.device_side(wl.dst, wl.seed, 2)
     digest = inputs_digest(wl.src_tables + wl.dst_tables, [gs, gd], wl.prompt_lens)
@@ -1083,12 +1083,17 @@ def bench_tp4(args, torch, kvx, S, W):
     per_layer = 2 * 2 * sum(tokens) * nh * row   # K and V, read + write
     step_bytes = per_layer * L
 
-    def step():
+    per_launch = min(L, 32)
+    launches = -(-L // per_launch)
+
+    def step():   # every layer's share, 32 layers per launch
+        kvx.kvx_copy_heads_layers(plan, 0, L, rank * nh, 0, nh, stream=side)
+
+    def layer_step():
         for l in range(L):
             kvx.kvx_copy_heads(plan, l, rank * nh, 0, nh, stream=side)
     if args.counters:
-        counters_run(torch, kvx, plan, side, L, per_layer,
-                     launch=lambda l: kvx.kvx_copy_heads(plan, l, rank * nh, 0, nh, stream=side))
+        counters_run(torch, kvx, plan, side, 1, per_layer * per_launch, launch=lambda _l: step())
         plan.close()
         return None
     parity = None
@@ -1116,7 +1121,10 @@ def bench_tp4(args, torch, kvx, S, W):
     span_ms, per_step = timed_steps(torch, side, step, args.steps, args.warmup)
     ms = span_ms / args.steps
     gbs = step_bytes / (ms * 1e-3) / 1e9
-    log(f"copy_heads: {ms * 1e3:.1f} us per step, {gbs:.1f} GB/s ({100 * gbs / HBM_PEAK_GBS:.1f}%)")
+    log(f"copy_heads_layers: {ms * 1e3:.1f} us per step, {gbs:.1f} GB/s ({100 * gbs / HBM_PEAK_GBS:.1f}%)")
+    lspan, _ = timed_steps(torch, side, layer_step, args.steps, 1)
+    layer_gbs = step_bytes * args.steps / (lspan * 1e-3) / 1e9
+    log(f"one kvx_copy_heads launch per layer: {layer_gbs:.1f} GB/s")
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -1142,8 +1150,12 @@ def bench_tp4(args, torch, kvx, S, W):
                    "tp_rank": rank, "tp_size": wl.extra["tp_size"], "head_dim": wl.src.head_dim,
                    "block_size": wl.src.block_size, "payload_dtype": wl.src.dtype, "requests": len(tokens),
                    "tokens_moved": tokens[0], "bytes_per_step": step_bytes,
-                   "step": f"{L} x kvx_copy_heads(rank {rank} slice) on one stream"},
-        "roofline": roofline(per_layer, ms * 1e3 / L, "kvx::heads_kernel (kvx_copy_heads)", wl.name),
+                   "step": f"kvx_copy_heads_layers over all {L} layers (rank {rank} slice), {launches} launches "
+                           f"of {per_launch} layers, on one stream",
+                   "copy_heads_per_layer_GBs": round(layer_gbs, 1)},
+        "roofline": roofline(per_layer * per_launch, ms * 1e3 / launches,
+                             "kvx::heads_many_kernel (kvx_copy_heads_layers)", wl.name,
+                             {"measured": f"span of back-to-back launches of {per_launch} layers"}),
         "cpu_baseline": cpu,
     }
 

@@ -403,11 +403,10 @@ constexpr int kHeadUnroll = 4;
 // with different block sizes per side) of region blockIdx.y (K, V or the
 // latent region).  Lanes walk the block's rows in destination order so
 // stores are contiguous; each lane keeps kHeadUnroll vectors in flight.
-__global__ __launch_bounds__(kHeadThreads) void heads_kernel(HeadArgs a) {
-  const int kv = blockIdx.y;
-  const BlockPair b = a.blocks[blockIdx.x];
-  const uint8_t* sb = a.in[kv] + int64_t(b.src) * a.s_blk + slot_src(b.slots) * a.s_slot;
-  uint8_t* db = a.out[kv] + int64_t(b.dst) * a.d_blk + slot_dst(b.slots) * a.d_slot;
+__device__ __forceinline__ void heads_block(const HeadArgs& a, const BlockPair b, const uint8_t* in, uint8_t* out,
+                                            const uint32_t* in_sc, uint32_t* out_sc) {
+  const uint8_t* sb = in + int64_t(b.src) * a.s_blk + slot_src(b.slots) * a.s_slot;
+  uint8_t* db = out + int64_t(b.dst) * a.d_blk + slot_dst(b.slots) * a.d_slot;
   // buffer resources over one block's bytes from the slice's first row on
   // (every offset below stays inside the block)
   const __amdgpu_buffer_rsrc_t rs =
@@ -442,7 +441,36 @@ __global__ __launch_bounds__(kHeadThreads) void heads_kernel(HeadArgs a) {
       if (i < total) __builtin_amdgcn_raw_buffer_store_b128(r[k], rd, doff[k], 0, KVX_HEAD_ST_AUX);
     }
   }
-  if (a.out_sc[kv] && threadIdx.x == 0) a.out_sc[kv][b.dst] = a.in_sc[kv][b.src];
+  if (out_sc && threadIdx.x == 0) out_sc[b.dst] = in_sc[b.src];
+}
+
+__global__ __launch_bounds__(kHeadThreads) void heads_kernel(HeadArgs a) {
+  const int kv = blockIdx.y;
+  heads_block(a, a.blocks[blockIdx.x], a.in[kv], a.out[kv], a.in_sc[kv], a.out_sc[kv]);
+}
+
+// Several layers of one plan's head transform in one launch
+// (kvx_copy_heads_layers): workgroup x moves planned block x mod `per` of
+// layer entry x / `per`, with the strides and the block list of `c`.
+struct HeadLayer {
+  const uint8_t* in[2];
+  uint8_t* out[2];
+  const uint32_t* in_sc[2];
+  uint32_t* out_sc[2];
+};
+constexpr int kHeadLayersMax = 32;
+struct HeadManyArgs {
+  HeadArgs c;
+  int32_t n, per;  // layer entries; planned blocks per entry
+  HeadLayer e[kHeadLayersMax];
+};
+
+__global__ __launch_bounds__(kHeadThreads) void heads_many_kernel(HeadManyArgs a) {
+  const int kv = blockIdx.y;
+  const int lo = int(blockIdx.x) / a.per;
+  const int bi = int(blockIdx.x) - lo * a.per;
+  const HeadLayer& e = a.e[lo];
+  heads_block(a.c, a.c.blocks[bi], e.in[kv], e.out[kv], e.in_sc[kv], e.out_sc[kv]);
 }
 
 // One shared piece list: one y row per region; one list per region: the tags.
@@ -961,34 +989,29 @@ int kvx_plan_noalloc(const kvx_pool* src, const kvx_pool* dst, int32_t num_reque
   return KVX_OK;
 }
 
-int kvx_copy_heads(const kvx_plan_t* cp, int32_t layer, int32_t src_head0, int32_t dst_head0,
-                   int32_t num_heads, hipEvent_t ready, hipStream_t stream) {
-  int rc = check_device_plan(cp, "kvx_copy_heads");
+}  // extern "C"
+
+// Checks shared by the head-transform calls, for layers [l0, l1).
+static int heads_check(const kvx_plan_t* cp, int64_t l0, int64_t l1, int32_t src_head0, int32_t dst_head0,
+                       int32_t num_heads, const char* fn) {
+  int rc = check_device_plan(cp, fn);
   if (rc) return rc;
-  kvx_plan_t* p = const_cast<kvx_plan_t*>(cp);
-  if (p->src.state) return fail(KVX_E_MISMATCH, "kvx_copy_heads: state pools have no heads");
+  if (cp->src.state) return fail(KVX_E_MISMATCH, "%s: state pools have no heads", fn);
   if (src_head0 < 0 || dst_head0 < 0 || num_heads < 0)
-    return fail(KVX_E_INVAL, "kvx_copy_heads: negative head index or count");
-  if (layer < 0 || layer >= p->src.L)
-    return fail(KVX_E_RANGE, "kvx_copy_heads: layer %d outside [0,%d)", layer, p->src.L);
-  if (int64_t(src_head0) + num_heads > p->src.H || int64_t(dst_head0) + num_heads > p->dst.H)
-    return fail(KVX_E_RANGE, "kvx_copy_heads: head slice [%d,+%d) -> [%d,+%d) outside %d / %d heads",
-                src_head0, num_heads, dst_head0, num_heads, p->src.H, p->dst.H);
-  rc = enqueue_waits(p, ready, stream);
-  if (rc) return rc;
-  if (p->blocks.empty()) return KVX_OK;
-  if (num_heads == 0) return KVX_OK;
+    return fail(KVX_E_INVAL, "%s: negative head index or count", fn);
+  if (l0 < 0 || l1 < l0 || l1 > cp->src.L)
+    return fail(KVX_E_RANGE, "%s: layers [%lld,%lld) outside [0,%d)", fn, (long long)l0, (long long)l1, cp->src.L);
+  if (int64_t(src_head0) + num_heads > cp->src.H || int64_t(dst_head0) + num_heads > cp->dst.H)
+    return fail(KVX_E_RANGE, "%s: head slice [%d,+%d) -> [%d,+%d) outside %d / %d heads", fn, src_head0,
+                num_heads, dst_head0, num_heads, cp->src.H, cp->dst.H);
+  return KVX_OK;
+}
+
+// Strides and slice of a plan's head transform (no layer bases yet).
+static HeadArgs heads_common(const kvx_plan_t* p, int32_t num_heads) {
   const Geom& gs = p->src;
   const Geom& gd = p->dst;
   HeadArgs a{};
-  for (int r = 0; r < p->nreg; ++r) {
-    a.in[r] = static_cast<const uint8_t*>(gs.base(r, layer)) + int64_t(src_head0) * gs.head_stride();
-    a.out[r] = static_cast<uint8_t*>(gd.base(r, layer)) + int64_t(dst_head0) * gd.head_stride();
-    if (gs.scales) {
-      a.in_sc[r] = reinterpret_cast<const uint32_t*>(gs.scale(r, layer));
-      a.out_sc[r] = reinterpret_cast<uint32_t*>(gd.scale(r, layer));
-    }
-  }
   a.s_blk = gs.block_bytes();
   a.s_slot = gs.slot_stride();
   a.s_head = gs.head_stride();
@@ -998,11 +1021,80 @@ int kvx_copy_heads(const kvx_plan_t* cp, int32_t layer, int32_t src_head0, int32
   a.vpr = int32_t(gs.row_bytes() / 16);
   a.nh = num_heads;
   a.dst_head_major = gd.layout == KVX_HND;
+  return a;
+}
+
+// Region bases of one layer's head slice.
+static HeadLayer heads_layer(const kvx_plan_t* p, int32_t layer, int32_t src_head0, int32_t dst_head0) {
+  const Geom& gs = p->src;
+  const Geom& gd = p->dst;
+  HeadLayer e{};
+  for (int r = 0; r < p->nreg; ++r) {
+    e.in[r] = static_cast<const uint8_t*>(gs.base(r, layer)) + int64_t(src_head0) * gs.head_stride();
+    e.out[r] = static_cast<uint8_t*>(gd.base(r, layer)) + int64_t(dst_head0) * gd.head_stride();
+    if (gs.scales) {
+      e.in_sc[r] = reinterpret_cast<const uint32_t*>(gs.scale(r, layer));
+      e.out_sc[r] = reinterpret_cast<uint32_t*>(gd.scale(r, layer));
+    }
+  }
+  return e;
+}
+
+// One layer, in launches of at most kMaxGridX planned blocks.
+static void heads_launch_layer(const kvx_plan_t* p, const HeadArgs& common, const HeadLayer& e, hipStream_t stream) {
+  HeadArgs a = common;
+  for (int r = 0; r < 2; ++r) {
+    a.in[r] = e.in[r];
+    a.out[r] = e.out[r];
+    a.in_sc[r] = e.in_sc[r];
+    a.out_sc[r] = e.out_sc[r];
+  }
   const int64_t nb = int64_t(p->blocks.size());
   for (int64_t first = 0; first < nb; first += kMaxGridX) {
     const int64_t cnt = std::min<int64_t>(nb - first, kMaxGridX);
     a.blocks = p->d_blocks + first;
     hipLaunchKernelGGL(heads_kernel, dim3(unsigned(cnt), unsigned(p->nreg)), dim3(kHeadThreads), 0, stream, a);
+  }
+}
+
+extern "C" {
+
+int kvx_copy_heads(const kvx_plan_t* cp, int32_t layer, int32_t src_head0, int32_t dst_head0,
+                   int32_t num_heads, hipEvent_t ready, hipStream_t stream) {
+  int rc = heads_check(cp, layer, int64_t(layer) + 1, src_head0, dst_head0, num_heads, "kvx_copy_heads");
+  if (rc) return rc;
+  kvx_plan_t* p = const_cast<kvx_plan_t*>(cp);
+  rc = enqueue_waits(p, ready, stream);
+  if (rc) return rc;
+  if (p->blocks.empty() || num_heads == 0) return KVX_OK;
+  heads_launch_layer(p, heads_common(p, num_heads), heads_layer(p, layer, src_head0, dst_head0), stream);
+  return check_launch("kvx heads kernel launch");
+}
+
+int kvx_copy_heads_layers(const kvx_plan_t* cp, int32_t l0, int32_t l1, int32_t src_head0, int32_t dst_head0,
+                          int32_t num_heads, hipEvent_t ready, hipStream_t stream) {
+  int rc = heads_check(cp, l0, l1, src_head0, dst_head0, num_heads, "kvx_copy_heads_layers");
+  if (rc) return rc;
+  kvx_plan_t* p = const_cast<kvx_plan_t*>(cp);
+  rc = enqueue_waits(p, ready, stream);
+  if (rc) return rc;
+  if (p->blocks.empty() || num_heads == 0 || l1 == l0) return KVX_OK;
+  const HeadArgs common = heads_common(p, num_heads);
+  const int64_t nb = int64_t(p->blocks.size());
+  if (nb > kMaxGridX / 2) {  // a layer fills a launch: one launch (or more) per layer
+    for (int32_t l = l0; l < l1; ++l) heads_launch_layer(p, common, heads_layer(p, l, src_head0, dst_head0), stream);
+    return check_launch("kvx heads kernel launch");
+  }
+  const int32_t per_launch = int32_t(std::min<int64_t>(kHeadLayersMax, kMaxGridX / nb));
+  HeadManyArgs m{};
+  m.c = common;
+  m.c.blocks = p->d_blocks;
+  m.per = int32_t(nb);
+  for (int32_t l = l0; l < l1; l += per_launch) {
+    m.n = std::min(per_launch, l1 - l);
+    for (int32_t j = 0; j < m.n; ++j) m.e[j] = heads_layer(p, l + j, src_head0, dst_head0);
+    hipLaunchKernelGGL(heads_many_kernel, dim3(unsigned(int64_t(m.n) * nb), unsigned(p->nreg)), dim3(kHeadThreads), 0,
+                       stream, m);
   }
   return check_launch("kvx heads kernel launch");
 }

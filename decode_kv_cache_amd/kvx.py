@@ -82,6 +82,7 @@ _SIGS = {
     "kvx_pack": (C.c_int, [_P, _I32, _I32, _P, _I64, _P]),
     "kvx_unpack": (C.c_int, [_P, _I32, _I32, _P, _I64, _P]),
     "kvx_copy_heads": (C.c_int, [_P, _I32, _I32, _I32, _I32, _P, _P]),
+    "kvx_copy_heads_layers": (C.c_int, [_P, _I32, _I32, _I32, _I32, _I32, _P, _P]),
     "kvx_queue_create": (C.c_int, [_P, C.POINTER(_P)]),
     "kvx_queue_push": (C.c_int, [_P, _P, _I32, _P]),
     "kvx_queue_flush": (C.c_int, [_P]),
@@ -499,6 +500,13 @@ def kvx_copy_heads(plan: Plan, layer: int, src_head0: int, dst_head0: int, num_h
                    ready=None, stream=None) -> None:
     _check("kvx_copy_heads", lib().kvx_copy_heads(plan.handle, layer, src_head0, dst_head0, num_heads,
                                                   _event(ready), _stream(stream)))
+
+
+def kvx_copy_heads_layers(plan: Plan, l0: int, l1: int, src_head0: int, dst_head0: int, num_heads: int,
+                          ready=None, stream=None) -> None:
+    """kvx_copy_heads over layers [l0, l1), up to 32 layers per launch."""
+    _check("kvx_copy_heads_layers", lib().kvx_copy_heads_layers(plan.handle, l0, l1, src_head0, dst_head0,
+                                                                num_heads, _event(ready), _stream(stream)))
 
 
 class Queue:

@@ -29,7 +29,7 @@ from collections import defaultdict
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 PUSH_KERNEL = "kvx::copy_kernel<0, "   # any launch shape of the push mode
-HEADS_KERNEL = "kvx::heads_kernel"
+HEADS_KERNEL = ("kvx::heads_kernel", "kvx::heads_many_kernel")
 MANY_KERNEL = ("kvx::copy_many_kernel<", "kvx::scale_many_kernel<")   # batched launches and their scale launches
 RUN_KERNEL = "kvx::run_kernel<0>"       # push of a run-table plan
 KERNELS = {"push": PUSH_KERNEL, "heads": HEADS_KERNEL, "many": MANY_KERNEL, "runs": RUN_KERNEL}

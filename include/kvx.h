@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define KVX_ABI_VERSION 5
+#define KVX_ABI_VERSION 6
 
 /* Status codes. */
 enum {
@@ -506,6 +506,18 @@ int kvx_unpack(const kvx_plan_t* plan, int32_t l0, int32_t l1, const void* stagi
  */
 int kvx_copy_heads(const kvx_plan_t* plan, int32_t layer, int32_t src_head0, int32_t dst_head0,
                    int32_t num_heads, hipEvent_t ready, hipStream_t stream);
+
+/*
+ * kvx_copy_heads for every layer in [l0, l1), the same head slice in each:
+ * a TP rank's share of several layers whose KV is complete, as when a
+ * request's layers are written out together.  Up to 32 layers share one
+ * kernel launch (one launch per layer when a layer's planned blocks alone
+ * fill half a launch's 2^22 workgroups).  Everything is ordered after
+ * `ready`.  Errors: those of kvx_copy_heads, with RANGE for a layer range
+ * outside [0, num_layers] or l1 < l0; an empty range is a no-op.
+ */
+int kvx_copy_heads_layers(const kvx_plan_t* plan, int32_t l0, int32_t l1, int32_t src_head0, int32_t dst_head0,
+                          int32_t num_heads, hipEvent_t ready, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -136,6 +136,49 @@ def test_copy_heads_random_small():
 
 
 
+def test_copy_heads_layers_random_small():
+    """kvx_copy_heads_layers over a random layer range equals the oracle's
+    head transform of each layer in it; layers outside it stay untouched;
+    an empty range is a no-op and a range outside the pools is refused."""
+    rng = np.random.Generator(np.random.PCG64(33))
+    for i, (sl, dl) in enumerate([("NHD", "HND"), ("HND", "NHD"), ("NHD", "NHD"), ("HND", "HND")] * 4):
+        hs = int(rng.integers(1, 9))
+        hd = int(rng.integers(1, 9))
+        L = int(rng.integers(1, 6))
+        wl = W.random_case(8100 + i, layout=sl, dst_layout=dl, elem_bytes=int(rng.choice([1, 2])),
+                           num_layers=L, num_blocks=120, block_size=int(rng.choice([1, 4, 16])),
+                           num_heads=hs, dst_heads=hd, head_dim=int(rng.choice([16, 64, 128])),
+                           has_scales=bool(i % 2), num_requests=3, max_tokens=40, run_mean=2.0)
+        say("case", wl.name, sl, dl, hs, hd, L)
+        src, dst, gs, gd = host_sides(wl)
+        toks = tokens(wl)
+        reqs = oracle_requests(wl, toks)
+        plan = kvx.kvx_plan(gs.pool, gd.pool, toks, wl.src_tables, wl.dst_tables)
+        op = O.make_plan(src.geom, dst.geom, reqs)
+        nh = int(rng.integers(0, min(hs, hd) + 1))
+        s0 = int(rng.integers(0, hs - nh + 1))
+        d0 = int(rng.integers(0, hd - nh + 1))
+        l0 = int(rng.integers(0, L))
+        l1 = int(rng.integers(l0, L + 1))
+        exp = dst.copy()
+        kvx.kvx_copy_heads_layers(plan, l0, l1, s0, d0, nh)
+        kvx.kvx_copy_heads_layers(plan, l1, l1, s0, d0, nh)
+        for l in range(l0, l1):
+            if nh:
+                O.copy_heads(src, exp, op, reqs, l, s0, d0, nh)
+        torch.cuda.synchronize()
+        assert np.array_equal(gd.kv.cpu().numpy(), exp.kv), (wl.name, l0, l1, s0, d0, nh)
+        if exp.scales is not None:
+            assert np.array_equal(dev_scales(gd), exp.scales)
+        for a, b in ((0, L + 1), (1, 0), (-1, 1)):
+            if a == 1 and L == 0:
+                continue
+            with pytest.raises(kvx.KvxError) as e:
+                kvx.kvx_copy_heads_layers(plan, a, b, s0, d0, nh)
+            assert e.value.status == "KVX_E_RANGE", (a, b)
+        plan.close()
+
+
 def test_copy_heads_shared_source_prefix():
     """Head transform (4 heads NHD -> 2 heads HND, so copy_heads is the plan's
     only device call) for requests that share a source prefix: equal source
@@ -402,10 +445,13 @@ def test_tp4_share_full():
     reqs = oracle_requests(wl, toks)
     op = O.make_plan(P.geom(O, wl.src), P.geom(O, wl.dst), reqs)
     layers = [0, 63]
-    for rank in range(4):
+    for rank in range(4):   # ranks 1 and 3 through kvx_copy_heads_layers (32 layers per launch)
         pre_s, pre_d = snapshot(gs, layers), snapshot(gd, layers)
-        for l in range(wl.src.num_layers):
-            kvx.kvx_copy_heads(plan, l, 2 * rank, 0, 2)
+        if rank % 2:
+            kvx.kvx_copy_heads_layers(plan, 0, wl.src.num_layers, 2 * rank, 0, 2)
+        else:
+            for l in range(wl.src.num_layers):
+                kvx.kvx_copy_heads(plan, l, 2 * rank, 0, 2)
         torch.cuda.synchronize()
         for l in layers:
             exp = O.Pool(P.geom(O, wl.dst), pre_d[l][0][None].copy(), None)
