@@ -589,9 +589,10 @@ static void launch_many(const ManyArgs& m, int32_t shape, unsigned gy, hipStream
   }
 }
 
-// Entries of one mode batched into as few launches as the limits allow, in
-// order: consecutive entries with the same grid height share a launch (up
-// to kManyMax entries and kMaxGridX workgroups).  A launch whose entries all
+// Entries of one mode batched into as few launches as the limits allow:
+// entries with the same grid height share a launch, in their order (up to
+// kManyMax entries and kMaxGridX workgroups), and the entries' scale copies,
+// if any, follow in one small launch behind it.  A launch whose entries all
 // take the same one-wave shape and together stay within one round of it (at
 // most kLongMaxPieces pieces of 32 KiB) runs in that shape; any other launch
 // streams its pieces as 4 KiB chunks of four-wave workgroups, the shape that
