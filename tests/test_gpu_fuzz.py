@@ -10,7 +10,8 @@ KVX_PLAN_RUNS (streaming plans then read run tables). Where both pools have
 the same head count and layout, its requests are pushed layer by layer.
 They are also split into two plans with disjoint destinations, whose layers
 go out in one kvx_push_many call, and packed and unpacked over a random
-layer range.  Otherwise a random head slice is transformed layer by layer.
+layer range.  Otherwise a random head slice is transformed, the first
+layers one launch each and the rest in one kvx_copy_heads_layers call.
 Every destination byte, staging byte and scale must equal the oracle's."""
 import os
 
@@ -141,11 +142,14 @@ def test_random_sweep():
             s0 = int(rng.integers(0, wl.src.num_heads - nh + 1))
             d0 = int(rng.integers(0, wl.dst.num_heads - nh + 1))
             exp = dst.copy()
-            for l in range(L):
+            l0 = int(rng.integers(0, L + 1))   # [0, l0) one launch per layer, [l0, L) in batched launches
+            for l in range(l0):
                 kvx.kvx_copy_heads(plan, l, s0, d0, nh)
+            kvx.kvx_copy_heads_layers(plan, l0, L, s0, d0, nh)
+            for l in range(L):
                 O.copy_heads(src, exp, op, reqs, l, s0, d0, nh)
             torch.cuda.synchronize()
-            check_pool(gd, exp, (wl.name, "copy_heads", s0, d0, nh))
+            check_pool(gd, exp, (wl.name, "copy_heads", s0, d0, nh, l0))
             plan.close()
         assert np.array_equal(gs.kv.cpu().numpy(), src.kv), (wl.name, "source changed")
         done += 1
