@@ -544,6 +544,21 @@ def bench_push(args, torch, kvx, S, W):
                 B.copy_segments(grp_src[g], grp_dst[g], seg, 1, stream=side)
         c_layer, _ = timed_steps(torch, side, plain_per_layer, args.steps, 2)
         c_stream, _ = timed_steps(torch, side, plain_stream, args.steps, 2)
+        # the chip's plain-copy rate: the step's read bytes as one contiguous
+        # segment of each pool, rotating over four windows so that no window
+        # repeats within four steps (the pools are scratch by now)
+        tot = rd * L
+        win = min(gs.kv.numel(), gd.kv.numel()) // 4 // 4096 * 4096
+        assert tot <= win and tot % 16 == 0
+        wins = [(torch.tensor([gs.kv.data_ptr() + w * win], dtype=torch.int64, device="cuda"),
+                 torch.tensor([gd.kv.data_ptr() + w * win], dtype=torch.int64, device="cuda")) for w in range(4)]
+        turn = [0]
+
+        def plain_contiguous():
+            s_, d_ = wins[turn[0] % 4]
+            turn[0] += 1
+            B.copy_segments(s_, d_, tot, 1, stream=side)
+        c_contig, _ = timed_steps(torch, side, plain_contiguous, args.steps, 2)
         # the same runs squeezed into a dense window on each side (block i of
         # the table -> the rank of its ID among the table's IDs), same queue step
         def dense_tables(tables, bs):
@@ -561,6 +576,7 @@ def bench_push(args, torch, kvx, S, W):
         cl = step_bytes * args.steps / (c_layer * 1e-3) / 1e9
         cs = step_bytes * args.steps / (c_stream * 1e-3) / 1e9
         cw = step_bytes * args.steps / (c_window * 1e-3) / 1e9
+        cc = step_bytes * args.steps / (c_contig * 1e-3) / 1e9
         ceiling = {
             "plain_copy_per_layer_GBs": round(cl, 1),
             "plain_copy_per_layer": f"{L} launches, one per layer: K and V each one contiguous segment of "
@@ -568,12 +584,17 @@ def bench_push(args, torch, kvx, S, W):
             "plain_copy_streamed_GBs": round(cs, 1),
             "plain_copy_streamed": f"2 launches of {half} layers: the same segments as 4 KiB chunks of four-wave "
                                    f"workgroups (the launch shape of the queue's batched groups)",
+            "plain_copy_contiguous_GBs": round(cc, 1),
+            "plain_copy_contiguous": f"one launch per step: the step's {tot} read bytes as one contiguous segment of "
+                                     f"each pool, 4 KiB chunks of four-wave workgroups (four rotating windows)",
+            "value_over_plain_copy_contiguous": round(gbs / cc, 4),
             "dense_window_queue_GBs": round(cw, 1),
             "dense_window_queue": "the same runs renumbered into a dense window of each pool, same queue step",
             "value_over_plain_copy_streamed": round(gbs / cs, 4),
             "value_over_plain_copy_per_layer": round(gbs / cl, 4),
         }
-        log(f"ceiling: plain copy per layer {cl:.1f}, streamed {cs:.1f}, dense-window queue step {cw:.1f} GB/s")
+        log(f"ceiling: plain copy per layer {cl:.1f}, streamed {cs:.1f}, contiguous {cc:.1f}, dense-window queue step "
+        f"{cw:.1f} GB/s")
 
     cpu = None
     if not args.no_cpu_baseline:
