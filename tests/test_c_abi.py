@@ -44,8 +44,10 @@ def test_c_program(prog, tmp_path):
 @pytest.mark.gpu
 def test_device_calls_from_c(tmp_path):
     """tests/c_abi/push_from_c.c: device pools allocated from C, then
-    kvx_push_layer, kvx_pack + kvx_unpack and kvx_push_many, each checked
-    byte for byte against the per-token definition written in the program."""
+    kvx_push_layer, kvx_pack + kvx_unpack, kvx_push_many, the write queue
+    behind another stream's events, and kvx_copy_heads_layers into a one-head
+    HND pool, each checked byte for byte against the per-token definition
+    written in the program."""
     lib = os.path.join(PKG, "libkvx.so")
     assert os.path.exists(lib), "build libkvx.so first (python -m decode_kv_cache_amd.build)"
     rocm_lib = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "lib")
