@@ -1090,7 +1090,9 @@ def bench_batched(args, torch, kvx, S, W):
 
 
 def bench_tp4(args, torch, kvx, S, W):
-    """tp4_share: TP4 rank 0's 2-head slice NHD -> HND of every layer (kvx_copy_heads_layers)."""
+    """tp4_share: TP4 rank 0's 2-head slice NHD -> HND of every layer: one
+    head-slice write per layer through the side stream's write queue
+    (kvx_queue_push_heads), then a flush."""
     wl = workload(W, "tp4_share", args)
     gs, gd = S.device_side(wl.src, wl.seed, 1), S.device_side(wl.dst, wl.seed, 2)
     digest = inputs_digest(wl.src_tables + wl.dst_tables, [gs, gd], wl.prompt_lens)
@@ -1106,15 +1108,22 @@ def bench_tp4(args, torch, kvx, S, W):
 
     per_launch = min(L, 32)
     launches = -(-L // per_launch)
+    q = kvx.Queue(side)
 
-    def step():   # every layer's share, 32 layers per launch
+    def step():   # one head-slice write per layer through the queue
+        for l in range(L):
+            q.push_heads(plan, l, rank * nh, 0, nh)
+        q.flush()
+
+    def layers_step():   # every layer's share in one call, 32 layers per launch
         kvx.kvx_copy_heads_layers(plan, 0, L, rank * nh, 0, nh, stream=side)
 
     def layer_step():
         for l in range(L):
             kvx.kvx_copy_heads(plan, l, rank * nh, 0, nh, stream=side)
     if args.counters:
-        counters_run(torch, kvx, plan, side, 1, per_layer * per_launch, launch=lambda _l: step())
+        counters_run(torch, kvx, plan, side, 1, per_layer * per_launch, launch=lambda _l: layers_step())
+        q.close()
         plan.close()
         return None
     parity = None
@@ -1136,13 +1145,24 @@ def bench_tp4(args, torch, kvx, S, W):
                 nbytes += got.size
                 if not np.array_equal(got, exp):
                     bad.append(f"layer {l} region {kv}")
-        parity = parity_record(bad, f"one step on the fresh pools: every byte of layers {layers} of the "
-                                    f"consumer against the oracle's head transform (TP rank {rank})", nbytes)
+        parity = parity_record(bad, f"one step through kvx_queue_push_heads on the fresh pools: every byte of "
+                                    f"layers {layers} of the consumer against the oracle's head transform "
+                                    f"(TP rank {rank})", nbytes)
         del pre_s, pre_d
     span_ms, per_step = timed_steps(torch, side, step, args.steps, args.warmup)
     ms = span_ms / args.steps
     gbs = step_bytes / (ms * 1e-3) / 1e9
-    log(f"copy_heads_layers: {ms * 1e3:.1f} us per step, {gbs:.1f} GB/s ({100 * gbs / HBM_PEAK_GBS:.1f}%)")
+    w0, g0, n0 = q.stats3()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    w1, g1, n1 = q.stats3()
+    log(f"queue step: {ms * 1e3:.1f} us per step, {gbs:.1f} GB/s ({100 * gbs / HBM_PEAK_GBS:.1f}%), "
+        f"{(n1 - n0) / args.steps:.2f} launches per step")
+    mspan, _ = timed_steps(torch, side, layers_step, args.steps, 1)
+    many_ms = mspan / args.steps
+    many_gbs = step_bytes / (many_ms * 1e-3) / 1e9
+    log(f"kvx_copy_heads_layers, {launches} launches of {per_launch} layers: {many_gbs:.1f} GB/s")
     lspan, _ = timed_steps(torch, side, layer_step, args.steps, 1)
     layer_gbs = step_bytes * args.steps / (lspan * 1e-3) / 1e9
     log(f"one kvx_copy_heads launch per layer: {layer_gbs:.1f} GB/s")
@@ -1163,6 +1183,7 @@ def bench_tp4(args, torch, kvx, S, W):
         cpu = cpu_baseline(f"oracle copy_heads (numpy row gather/scatter) of {len(layers)} of {L} layers", one,
                            len(layers) * per_layer, args.cpu_seconds, setup)
         log(f"cpu baseline: {cpu['value']} GB/s")
+    q.close()
     plan.close()
     return {
         "value": gbs, "ms_per_step": ms, "dtype": "u8", "parity": parity, "span": span_stats(per_step),
@@ -1171,12 +1192,16 @@ def bench_tp4(args, torch, kvx, S, W):
                    "tp_rank": rank, "tp_size": wl.extra["tp_size"], "head_dim": wl.src.head_dim,
                    "block_size": wl.src.block_size, "payload_dtype": wl.src.dtype, "requests": len(tokens),
                    "tokens_moved": tokens[0], "bytes_per_step": step_bytes,
-                   "step": f"kvx_copy_heads_layers over all {L} layers (rank {rank} slice), {launches} launches "
-                           f"of {per_launch} layers, on one stream",
+                   "step": f"{L} x kvx_queue_push_heads(layer, rank {rank} slice) then kvx_queue_flush on one "
+                           f"side stream; the writes have no pending events, so they leave in merged launches",
+                   "kernel_launches_per_step": round((n1 - n0) / args.steps, 3),
+                   "launch_groups_per_step": round((g1 - g0) / args.steps, 3),
+                   "copy_heads_layers_GBs": round(many_gbs, 1),
                    "copy_heads_per_layer_GBs": round(layer_gbs, 1)},
-        "roofline": roofline(per_layer * per_launch, ms * 1e3 / launches,
-                             "kvx::heads_many_kernel (kvx_copy_heads_layers)", wl.name,
-                             {"measured": f"span of back-to-back launches of {per_launch} layers"}),
+        "roofline": roofline(per_layer * per_launch, many_ms * 1e3 / launches,
+                             "kvx::heads_many_kernel (kvx_queue_push_heads groups / kvx_copy_heads_layers)",
+                             wl.name, {"measured": f"span of back-to-back kvx_copy_heads_layers launches of "
+                                                   f"{per_launch} layers"}),
         "cpu_baseline": cpu,
     }
 

@@ -216,4 +216,19 @@ int check_push_pair(const kvx_plan_t* plan, int32_t layer, const char* fn, int32
 int push_batch(const kvx_plan_t* const* plans, const int32_t* layers, int32_t n, hipStream_t stream,
                hipEvent_t started = nullptr, hipEvent_t finished = nullptr, int64_t* launches = nullptr);
 
+// One layer's head-slice write (what kvx_copy_heads copies).
+struct HeadsWrite {
+  const kvx_plan_t* plan;
+  int32_t layer, src_head0, dst_head0, num_heads;
+};
+// Validate a head-slice write as kvx_copy_heads does.
+int check_heads_write(const HeadsWrite& w, const char* fn);
+// Enqueue already validated head-slice writes on `stream` (after each plan's
+// upload): consecutive writes of one plan and head slice share launches of
+// up to 32 layers, as in kvx_copy_heads_layers.  Every launch records its
+// end into `finished` (nullable; the last one wins); *launches (nullable)
+// grows by the kernel launches enqueued.
+int heads_batch(const HeadsWrite* writes, int32_t n, hipStream_t stream, hipEvent_t finished = nullptr,
+                int64_t* launches = nullptr);
+
 }  // namespace kvx

@@ -1041,8 +1041,10 @@ static HeadLayer heads_layer(const kvx_plan_t* p, int32_t layer, int32_t src_hea
   return e;
 }
 
-// One layer, in launches of at most kMaxGridX planned blocks.
-static void heads_launch_layer(const kvx_plan_t* p, const HeadArgs& common, const HeadLayer& e, hipStream_t stream) {
+// One layer, in launches of at most kMaxGridX planned blocks, each
+// recording its end into `finished` (nullable).
+static int64_t heads_launch_layer(const kvx_plan_t* p, const HeadArgs& common, const HeadLayer& e, hipStream_t stream,
+                                  hipEvent_t finished = nullptr) {
   HeadArgs a = common;
   for (int r = 0; r < 2; ++r) {
     a.in[r] = e.in[r];
@@ -1051,11 +1053,70 @@ static void heads_launch_layer(const kvx_plan_t* p, const HeadArgs& common, cons
     a.out_sc[r] = e.out_sc[r];
   }
   const int64_t nb = int64_t(p->blocks.size());
+  int64_t launches = 0;
   for (int64_t first = 0; first < nb; first += kMaxGridX) {
     const int64_t cnt = std::min<int64_t>(nb - first, kMaxGridX);
     a.blocks = p->d_blocks + first;
-    hipLaunchKernelGGL(heads_kernel, dim3(unsigned(cnt), unsigned(p->nreg)), dim3(kHeadThreads), 0, stream, a);
+    hipExtLaunchKernelGGL(heads_kernel, dim3(unsigned(cnt), unsigned(p->nreg)), dim3(kHeadThreads), 0, stream,
+                          nullptr, finished, 0u, a);
+    ++launches;
   }
+  return launches;
+}
+
+// Launches of up to kHeadLayersMax layers of one plan and head slice
+// (kvx_copy_heads_layers and the write queue), one per layer when a layer's
+// planned blocks alone fill half a launch; every launch records its end into
+// `finished` (nullable).  Returns the launches enqueued.
+static int64_t heads_launch_layers(const kvx_plan_t* p, const int32_t* layers, int32_t n, int32_t src_head0,
+                                   int32_t dst_head0, int32_t num_heads, hipStream_t stream, hipEvent_t finished) {
+  if (p->blocks.empty() || num_heads == 0 || n == 0) return 0;
+  const HeadArgs common = heads_common(p, num_heads);
+  const int64_t nb = int64_t(p->blocks.size());
+  int64_t launches = 0;
+  if (nb > kMaxGridX / 2) {
+    for (int32_t j = 0; j < n; ++j)
+      launches += heads_launch_layer(p, common, heads_layer(p, layers[j], src_head0, dst_head0), stream, finished);
+    return launches;
+  }
+  const int32_t per_launch = int32_t(std::min<int64_t>(kHeadLayersMax, kMaxGridX / nb));
+  HeadManyArgs m{};
+  m.c = common;
+  m.c.blocks = p->d_blocks;
+  m.per = int32_t(nb);
+  for (int32_t j0 = 0; j0 < n; j0 += per_launch) {
+    m.n = std::min(per_launch, n - j0);
+    for (int32_t j = 0; j < m.n; ++j) m.e[j] = heads_layer(p, layers[j0 + j], src_head0, dst_head0);
+    hipExtLaunchKernelGGL(heads_many_kernel, dim3(unsigned(int64_t(m.n) * nb), unsigned(p->nreg)),
+                          dim3(kHeadThreads), 0, stream, nullptr, finished, 0u, m);
+    ++launches;
+  }
+  return launches;
+}
+
+int kvx::check_heads_write(const HeadsWrite& w, const char* fn) {
+  return heads_check(w.plan, w.layer, int64_t(w.layer) + 1, w.src_head0, w.dst_head0, w.num_heads, fn);
+}
+
+int kvx::heads_batch(const HeadsWrite* w, int32_t n, hipStream_t stream, hipEvent_t finished, int64_t* launches) {
+  for (int32_t i = 0; i < n; ++i) {
+    const int rc = enqueue_waits(const_cast<kvx_plan_t*>(w[i].plan), nullptr, stream);
+    if (rc) return rc;
+  }
+  std::vector<int32_t> layers;
+  int64_t count = 0;
+  for (int32_t i = 0; i < n;) {
+    int32_t j = i;
+    layers.clear();
+    while (j < n && w[j].plan == w[i].plan && w[j].src_head0 == w[i].src_head0 &&
+           w[j].dst_head0 == w[i].dst_head0 && w[j].num_heads == w[i].num_heads)
+      layers.push_back(w[j++].layer);
+    count += heads_launch_layers(w[i].plan, layers.data(), int32_t(layers.size()), w[i].src_head0, w[i].dst_head0,
+                                 w[i].num_heads, stream, finished);
+    i = j;
+  }
+  if (launches) *launches += count;
+  return count ? check_launch("kvx heads kernel launch") : KVX_OK;
 }
 
 extern "C" {
@@ -1080,23 +1141,9 @@ int kvx_copy_heads_layers(const kvx_plan_t* cp, int32_t l0, int32_t l1, int32_t 
   rc = enqueue_waits(p, ready, stream);
   if (rc) return rc;
   if (p->blocks.empty() || num_heads == 0 || l1 == l0) return KVX_OK;
-  const HeadArgs common = heads_common(p, num_heads);
-  const int64_t nb = int64_t(p->blocks.size());
-  if (nb > kMaxGridX / 2) {  // a layer fills a launch: one launch (or more) per layer
-    for (int32_t l = l0; l < l1; ++l) heads_launch_layer(p, common, heads_layer(p, l, src_head0, dst_head0), stream);
-    return check_launch("kvx heads kernel launch");
-  }
-  const int32_t per_launch = int32_t(std::min<int64_t>(kHeadLayersMax, kMaxGridX / nb));
-  HeadManyArgs m{};
-  m.c = common;
-  m.c.blocks = p->d_blocks;
-  m.per = int32_t(nb);
-  for (int32_t l = l0; l < l1; l += per_launch) {
-    m.n = std::min(per_launch, l1 - l);
-    for (int32_t j = 0; j < m.n; ++j) m.e[j] = heads_layer(p, l + j, src_head0, dst_head0);
-    hipLaunchKernelGGL(heads_many_kernel, dim3(unsigned(int64_t(m.n) * nb), unsigned(p->nreg)), dim3(kHeadThreads), 0,
-                       stream, m);
-  }
+  std::vector<int32_t> layers;
+  for (int32_t l = l0; l < l1; ++l) layers.push_back(l);
+  heads_launch_layers(p, layers.data(), l1 - l0, src_head0, dst_head0, num_heads, stream, nullptr);
   return check_launch("kvx heads kernel launch");
 }
 

@@ -10,7 +10,10 @@
 // ready while those run are held and leave together in the next launch
 // group (kvx_push_many's batched launch), so the fixed cost is paid per
 // group instead of per layer when writes back up, and every write still
-// starts only after its own layer's event.
+// starts only after its own layer's event.  A write may also be one TP
+// rank's head slice of a layer (kvx_copy_heads), for a consumer whose ranks
+// each hold a share of the heads ([PUSH] "Implementierungsdetails" step 3);
+// such writes batch like kvx_copy_heads_layers.
 
 #include <hip/hip_runtime.h>
 
@@ -28,6 +31,8 @@ struct Entry {
   const kvx_plan_t* plan;
   int32_t layer;
   hipEvent_t ready;  // the queue's own copy of the caller's event; NULL once observed fired
+  bool heads;        // a head-slice write (the slice below) rather than a push
+  int32_t src_head0, dst_head0, num_heads;
 };
 
 }  // namespace
@@ -112,15 +117,30 @@ hipEvent_t next_done(kvx_queue* q) {
   return q->done[(q->head + q->busy) % kInflight];
 }
 
-// Enqueue a group's launches.  With `done`, the group's last kernel records
-// its end into it from its own dispatch (no marker packet behind it); a
-// group that launched nothing records it on the stream instead.
-int launch(kvx_queue* q, const std::vector<const kvx_plan_t*>& plans, const std::vector<int32_t>& layers,
-           hipEvent_t done) {
+// Enqueue a group's launches: its pushes, then its head-slice writes.  With
+// `done`, the group's last kernel records its end into it from its own
+// dispatch (no marker packet behind it); a group that launched nothing
+// records it on the stream instead.
+int launch(kvx_queue* q, const std::vector<Entry>& group, hipEvent_t done) {
   const int64_t before = q->launches;
+  std::vector<const kvx_plan_t*> plans;
+  std::vector<int32_t> layers;
+  std::vector<HeadsWrite> heads;
+  for (const Entry& e : group) {
+    if (e.heads) {
+      heads.push_back(HeadsWrite{e.plan, e.layer, e.src_head0, e.dst_head0, e.num_heads});
+    } else {
+      plans.push_back(e.plan);
+      layers.push_back(e.layer);
+    }
+  }
   if (!plans.empty()) {
     const int rc = push_batch(plans.data(), layers.data(), int32_t(plans.size()), q->stream, nullptr, done,
                               &q->launches);
+    if (rc) return rc;
+  }
+  if (!heads.empty()) {
+    const int rc = heads_batch(heads.data(), int32_t(heads.size()), q->stream, done, &q->launches);
     if (rc) return rc;
   }
   if (done) {
@@ -143,8 +163,7 @@ void drop_pending(kvx_queue* q) {
 int pump(kvx_queue* q) {
   int rc = retire(q);
   if (rc) return rc;
-  std::vector<const kvx_plan_t*> plans;
-  std::vector<int32_t> layers;
+  std::vector<Entry> group;
   while (q->busy < kInflight && !q->pending.empty()) {
     size_t n = 0;
     while (n < q->pending.size()) {
@@ -154,14 +173,9 @@ int pump(kvx_queue* q) {
       ++n;
     }
     if (n == 0) break;
-    plans.clear();
-    layers.clear();
-    for (size_t i = 0; i < n; ++i) {
-      plans.push_back(q->pending[i].plan);
-      layers.push_back(q->pending[i].layer);
-    }
+    group.assign(q->pending.begin(), q->pending.begin() + std::ptrdiff_t(n));
     q->pending.erase(q->pending.begin(), q->pending.begin() + std::ptrdiff_t(n));
-    rc = launch(q, plans, layers, next_done(q));
+    rc = launch(q, group, next_done(q));
     if (rc) return rc;
   }
   return KVX_OK;
@@ -173,27 +187,24 @@ int flush(kvx_queue* q) {
   int rc = pump(q);
   if (rc) return rc;
   if (q->pending.empty()) return KVX_OK;
-  std::vector<const kvx_plan_t*> plans;
-  std::vector<int32_t> layers;
+  std::vector<Entry> group;
   std::deque<Entry> todo;
   todo.swap(q->pending);
   for (Entry& e : todo) {
     const int r = entry_ready(q, e);
     if (r < 0) return -r;
     if (r == 0) {
-      rc = launch(q, plans, layers, nullptr);
+      rc = launch(q, group, nullptr);
       if (rc) return rc;
-      plans.clear();
-      layers.clear();
+      group.clear();
       rc = wait_event(e.ready, q->stream);
       release_event(q, e.ready);   // the wait has taken the event's state
       e.ready = nullptr;
       if (rc) return rc;
     }
-    plans.push_back(e.plan);
-    layers.push_back(e.layer);
+    group.push_back(e);
   }
-  return launch(q, plans, layers, next_done(q));
+  return launch(q, group, next_done(q));
 }
 
 }  // namespace
@@ -227,27 +238,40 @@ int kvx_queue_create(hipStream_t stream, kvx_queue** out) {
   return KVX_OK;
 }
 
-int kvx_queue_push(kvx_queue* q, const kvx_plan_t* plan, int32_t layer, hipEvent_t ready) {
-  if (!q) return fail(KVX_E_INVAL, "kvx_queue_push: null queue");
-  int rc = check_push_pair(plan, layer, "kvx_queue_push", 0);
-  if (rc) return rc;
+// Queue an already validated write behind `ready` (nullable).
+static int queue_write(kvx_queue* q, Entry en, hipEvent_t ready, const char* fn) {
   std::lock_guard<std::mutex> lk(q->mu);
-  if (stream_capturing(q->stream)) return fail(KVX_E_INVAL, "kvx_queue_push: the stream is capturing a graph");
-  Entry en{plan, layer, nullptr};
+  if (stream_capturing(q->stream)) return fail(KVX_E_INVAL, "%s: the stream is capturing a graph", fn);
   if (ready) {
     const hipError_t r = hipEventQuery(ready);
     if (r == hipErrorNotReady) {
-      rc = mirror_event(q, ready, &en.ready);
+      const int rc = mirror_event(q, ready, &en.ready);
       if (rc) return rc;
     } else if (r != hipSuccess) {
-      return fail_hip(r, "kvx_queue_push: hipEventQuery(ready)");
+      return fail_hip(r, "kvx_queue: hipEventQuery(ready)");
     }
   }
   q->pending.push_back(en);
   ++q->writes;
-  rc = pump(q);
+  const int rc = pump(q);
   if (rc) drop_pending(q);
   return rc;
+}
+
+int kvx_queue_push(kvx_queue* q, const kvx_plan_t* plan, int32_t layer, hipEvent_t ready) {
+  if (!q) return fail(KVX_E_INVAL, "kvx_queue_push: null queue");
+  const int rc = check_push_pair(plan, layer, "kvx_queue_push", 0);
+  if (rc) return rc;
+  return queue_write(q, Entry{plan, layer, nullptr, false, 0, 0, 0}, ready, "kvx_queue_push");
+}
+
+int kvx_queue_push_heads(kvx_queue* q, const kvx_plan_t* plan, int32_t layer, int32_t src_head0,
+                         int32_t dst_head0, int32_t num_heads, hipEvent_t ready) {
+  if (!q) return fail(KVX_E_INVAL, "kvx_queue_push_heads: null queue");
+  const int rc = check_heads_write(HeadsWrite{plan, layer, src_head0, dst_head0, num_heads}, "kvx_queue_push_heads");
+  if (rc) return rc;
+  return queue_write(q, Entry{plan, layer, nullptr, true, src_head0, dst_head0, num_heads}, ready,
+                     "kvx_queue_push_heads");
 }
 
 int kvx_queue_flush(kvx_queue* q) {

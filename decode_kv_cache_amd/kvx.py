@@ -85,6 +85,7 @@ _SIGS = {
     "kvx_copy_heads_layers": (C.c_int, [_P, _I32, _I32, _I32, _I32, _I32, _P, _P]),
     "kvx_queue_create": (C.c_int, [_P, C.POINTER(_P)]),
     "kvx_queue_push": (C.c_int, [_P, _P, _I32, _P]),
+    "kvx_queue_push_heads": (C.c_int, [_P, _P, _I32, _I32, _I32, _I32, _P]),
     "kvx_queue_flush": (C.c_int, [_P]),
     "kvx_queue_stats": (C.c_int, [_P, C.POINTER(_I64), C.POINTER(_I64), C.POINTER(_I64)]),
     "kvx_queue_destroy": (C.c_int, [_P]),
@@ -520,6 +521,11 @@ class Queue:
 
     def push(self, plan: Plan, layer: int, ready=None) -> None:
         _check("kvx_queue_push", lib().kvx_queue_push(self.handle, plan.handle, layer, _event(ready)))
+
+    def push_heads(self, plan: Plan, layer: int, src_head0: int, dst_head0: int, num_heads: int,
+                   ready=None) -> None:
+        _check("kvx_queue_push_heads", lib().kvx_queue_push_heads(self.handle, plan.handle, layer, src_head0,
+                                                                  dst_head0, num_heads, _event(ready)))
 
     def flush(self) -> None:
         _check("kvx_queue_flush", lib().kvx_queue_flush(self.handle))

@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define KVX_ABI_VERSION 6
+#define KVX_ABI_VERSION 7
 
 /* Status codes. */
 enum {
@@ -444,6 +444,20 @@ int kvx_queue_create(hipStream_t stream, kvx_queue** out);
  * Errors: INVAL (null queue or plan, host-only plan, stream capturing),
  * RANGE (layer), MISMATCH (a plan without a push work list), HIP. */
 int kvx_queue_push(kvx_queue* q, const kvx_plan_t* plan, int32_t layer, hipEvent_t ready);
+
+/* Queue one TP rank's head-slice write of layer `layer` of `plan` (what
+ * kvx_copy_heads would copy: source heads [src_head0, src_head0 +
+ * num_heads) onto destination heads [dst_head0, ...), each side in its own
+ * layout, scales with their blocks), to go out after `ready` (nullable)
+ * fires: the layerwise write that addresses each target TP rank ([PUSH]
+ * "Implementierungsdetails" step 3; [MORI] §3.2 for the per-layer trigger).
+ * Ready head-slice writes of one plan and slice that leave together share
+ * launches of up to 32 layers, as in kvx_copy_heads_layers; a group's pushes
+ * go out before its head-slice writes.  Errors: those of kvx_copy_heads for
+ * one layer, INVAL for a null queue or a capturing stream; on an error the
+ * writes still queued are dropped. */
+int kvx_queue_push_heads(kvx_queue* q, const kvx_plan_t* plan, int32_t layer, int32_t src_head0,
+                         int32_t dst_head0, int32_t num_heads, hipEvent_t ready);
 
 /* Enqueue every queued write on the queue's stream, each still waiting for
  * its own event (a stream wait for an event not yet observed fired), so that

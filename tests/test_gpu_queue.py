@@ -10,6 +10,10 @@
 - Random small cases: several plans with disjoint destinations, layers in
   random order, a mix of fired, pending and absent events, flushes in
   between; pool bytes and scales against the oracle.
+- Head-slice writes (kvx_queue_push_heads) in random layouts and slices,
+  mixed in one queue with pushes of the same source into a pool of its own
+  geometry, under the same mix of events: both consumer pools and their
+  scales against the oracle's head transform and push.
 - Argument errors, and refusal under graph capture."""
 import sys
 
@@ -23,7 +27,7 @@ from decode_kv_cache_amd import bench_support as B
 from decode_kv_cache_amd import kvx
 from decode_kv_cache_amd import session as S
 from decode_kv_cache_amd import workloads as W
-from test_gpu_parity import check_layers, oracle_requests, snapshot, tokens
+from test_gpu_parity import check_layers, dev_scales, host_sides, oracle_requests, snapshot, tokens
 
 pytestmark = pytest.mark.gpu
 
@@ -176,6 +180,105 @@ def test_queue_random_small():
             assert np.array_equal(S.scale_bits(gd.sc), exp.scales), case
         for p in plans:
             p.close()
+
+
+def test_queue_heads_random_small():
+    rng = np.random.Generator(np.random.PCG64(23))
+    sink = torch.empty(64 * 256, dtype=torch.float32, device="cuda")
+    compute = torch.cuda.Stream()
+    for i, (sl, dl) in enumerate([("NHD", "HND"), ("HND", "NHD"), ("NHD", "NHD"), ("HND", "HND")] * 3):
+        hs = int(rng.integers(1, 9))
+        hd = int(rng.integers(1, 9))
+        L = int(rng.integers(1, 6))
+        wl = W.random_case(8300 + i, layout=sl, dst_layout=dl, elem_bytes=int(rng.choice([1, 2])),
+                           num_layers=L, num_blocks=120, block_size=int(rng.choice([1, 4, 16])),
+                           num_heads=hs, dst_heads=hd, head_dim=int(rng.choice([16, 64, 128])),
+                           has_scales=bool(i % 2), num_requests=3, max_tokens=40, run_mean=2.0)
+        src, dst, gs, gd = host_sides(wl)
+        toks = tokens(wl)
+        reqs = oracle_requests(wl, toks)
+        nh = int(rng.integers(0, min(hs, hd) + 1))
+        s0 = int(rng.integers(0, hs - nh + 1))
+        d0 = int(rng.integers(0, hd - nh + 1))
+        say("case", wl.name, sl, dl, hs, hd, L, (s0, d0, nh))
+        hplan = kvx.kvx_plan(gs.pool, gd.pool, toks, wl.src_tables, wl.dst_tables)
+        # a second consumer with the source's geometry, pushed in the same queue
+        h2 = W.host_values(wl.src, wl.seed, 3)
+        g2 = S.device_side(wl.src, wl.seed, 3, values=h2)
+        pplan = kvx.kvx_plan(gs.pool, g2.pool, toks, wl.src_tables, wl.dst_tables)
+        side = torch.cuda.Stream()
+        q = kvx.Queue(side)
+        writes = [(kind, l) for kind in ("heads", "push") for l in range(L)]
+        rng.shuffle(writes)
+        for kind, l in writes:
+            ev_kind = int(rng.integers(0, 3))
+            ev = None
+            if ev_kind == 1:      # fired
+                ev = torch.cuda.Event()
+                ev.record(compute)
+                compute.synchronize()
+            elif ev_kind == 2:    # likely still pending when queued
+                B.layer_compute(sink, 5000, 64, stream=compute)
+                ev = torch.cuda.Event()
+                ev.record(compute)
+            if kind == "heads":
+                q.push_heads(hplan, l, s0, d0, nh, ready=ev)
+            else:
+                q.push(pplan, l, ready=ev)
+            if rng.random() < 0.2:
+                q.flush()
+        q.close()
+        torch.cuda.synchronize()
+        exp = dst.copy()
+        if nh:
+            op = O.make_plan(src.geom, dst.geom, reqs)
+            for l in range(L):
+                O.copy_heads(src, exp, op, reqs, l, s0, d0, nh)
+        assert np.array_equal(gd.kv.cpu().numpy(), exp.kv), wl.name
+        if exp.scales is not None:
+            assert np.array_equal(dev_scales(gd), exp.scales), wl.name
+        exp2 = O.Pool(src.geom, h2[0].copy(), None if h2[1] is None else h2[1].copy())
+        O.push(src, exp2, O.make_plan(src.geom, src.geom, reqs))
+        assert np.array_equal(g2.kv.cpu().numpy(), exp2.kv), wl.name
+        if exp2.scales is not None:
+            assert np.array_equal(dev_scales(g2), exp2.scales), wl.name
+        hplan.close()
+        pplan.close()
+
+
+def test_queue_heads_errors():
+    """kvx_queue_push_heads validates as kvx_copy_heads does, and a state
+    pool has no heads."""
+    src_spec = W.PoolSpec(2, 64, 4, 4, 16, W.BF16, "NHD")
+    dst_spec = W.PoolSpec(2, 64, 4, 2, 16, W.BF16, "HND")
+    gs, gd = S.device_side(src_spec, 5, 1), S.device_side(dst_spec, 5, 2)
+    plan = kvx.kvx_plan(gs.pool, gd.pool, [8], [[1, 2]], [[3, 4]])
+    q = kvx.Queue()
+    for args, code in (((2, 0, 0, 1), kvx.KVX_E_RANGE), ((0, 3, 0, 2), kvx.KVX_E_RANGE),
+                       ((0, 0, 1, 2), kvx.KVX_E_RANGE), ((0, -1, 0, 1), kvx.KVX_E_INVAL)):
+        with pytest.raises(kvx.KvxError) as e:
+            q.push_heads(plan, *args)
+        assert e.value.code == code, args
+    # a plan between pools of different head counts admits no push
+    with pytest.raises(kvx.KvxError) as e:
+        q.push(plan, 0)
+    assert e.value.code == kvx.KVX_E_MISMATCH
+    st = W.StateSpec(2, 8, (64, 128))
+    ss, sd = S.state_device_side(st, 5, 1), S.state_device_side(st, 5, 2)
+    splan = kvx.kvx_plan(ss.pool, sd.pool, [4], [[1]], [[2]])
+    with pytest.raises(kvx.KvxError) as e:
+        q.push_heads(splan, 0, 0, 0, 1)
+    assert e.value.code == kvx.KVX_E_MISMATCH
+    L = kvx.lib()
+    assert L.kvx_queue_push_heads(None, plan.handle, 0, 0, 0, 1, None) == kvx.KVX_E_INVAL
+    assert L.kvx_queue_push_heads(q.handle, None, 0, 0, 0, 1, None) == kvx.KVX_E_INVAL
+    q.push_heads(plan, 1, 0, 0, 0)   # an empty slice is a write that moves nothing
+    q.flush()
+    torch.cuda.synchronize()
+    assert q.stats()[0] == 1
+    q.close()
+    plan.close()
+    splan.close()
 
 
 def test_queue_errors():
