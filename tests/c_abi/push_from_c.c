@@ -9,8 +9,9 @@
  * of H*D*E bytes).  The staging buffer is the moved token rows in (layer,
  * region, request, token) order.  Last, one TP rank's head slice: source
  * head 1 of every moved token lands as head 0 of a one-head HND pool
- * ([blk][head][slot][d]) through kvx_copy_heads_layers.  Prints "ok" and
- * exits 0 when every check holds. */
+ * ([blk][head][slot][d]) through kvx_copy_heads_layers, and again layer by
+ * layer through a write queue.  Prints "ok" and exits 0 when every check
+ * holds. */
 #include <stdint.h>
 #include <stdio.h>
 #include <stdlib.h>
@@ -259,6 +260,29 @@ int main(void) {
     if (memcmp(h_hgot, h_hwant, HPOOL_BYTES) != 0) {
       fprintf(stderr, "kvx_copy_heads_layers: head-slice pool differs from the per-token definition\n");
       ++failures;
+    }
+    /* the same slice layer by layer through a write queue */
+    {
+      kvx_queue* hq = NULL;
+      hipEvent_t hdone;
+      HIP_OK(hipMemcpy(d_h, h_hinit, HPOOL_BYTES, hipMemcpyHostToDevice));
+      HIP_OK(hipEventCreateWithFlags(&hdone, hipEventDisableTiming));
+      KVX_OK_(kvx_queue_create(s, &hq));
+      for (l = 0; l < L; ++l) KVX_OK_(kvx_queue_push_heads(hq, hplan, l, 1, 0, 1, NULL));
+      KVX_OK_(kvx_queue_flush(hq));
+      HIP_OK(hipEventRecord(hdone, s));
+      HIP_OK(hipEventSynchronize(hdone));
+      HIP_OK(hipMemcpy(h_hgot, d_h, HPOOL_BYTES, hipMemcpyDeviceToHost));
+      if (memcmp(h_hgot, h_hwant, HPOOL_BYTES) != 0) {
+        fprintf(stderr, "kvx_queue_push_heads: head-slice pool differs from the per-token definition\n");
+        ++failures;
+      }
+      if (kvx_queue_push_heads(hq, hplan, 0, 0, 0, 2, NULL) != KVX_E_RANGE) {
+        fprintf(stderr, "a queued two-head slice of a one-head pool was not refused\n");
+        ++failures;
+      }
+      KVX_OK_(kvx_queue_destroy(hq));
+      HIP_OK(hipEventDestroy(hdone));
     }
     /* a slice past the destination's one head is refused */
     if (kvx_copy_heads(hplan, 0, 0, 0, 2, NULL, s) != KVX_E_RANGE) {
