@@ -12,7 +12,9 @@ They are also split into two plans with disjoint destinations, whose layers
 go out in one kvx_push_many call, and packed and unpacked over a random
 layer range.  Otherwise a random head slice is transformed, the first
 layers one launch each and the rest in one kvx_copy_heads_layers call.
-Every destination byte, staging byte and scale must equal the oracle's."""
+Either way every layer's write also goes through a write queue once, in a
+random layer order (kvx_queue_push, kvx_queue_push_heads).  Every
+destination byte, staging byte and scale must equal the oracle's."""
 import os
 
 import numpy as np
@@ -104,6 +106,16 @@ def test_random_sweep():
             O.push(src, exp, op)
             check_pool(gd, exp, (wl.name, "push"))
             plan.close()
+            # the same writes through a write queue, layers in a random order
+            gd = fresh(wl, dst)
+            plan = kvx.kvx_plan(gs.pool, gd.pool, toks, wl.src_tables, wl.dst_tables, overlap=overlap, runs=runs)
+            q = kvx.Queue()
+            for l in rng.permutation(L):
+                q.push(plan, int(l))
+            q.close()
+            torch.cuda.synchronize()
+            check_pool(gd, exp, (wl.name, "queue"))
+            plan.close()
             # two plans over disjoint request groups, every layer in one kvx_push_many call
             gd = fresh(wl, dst)
             cut = int(rng.integers(0, len(toks) + 1))
@@ -150,6 +162,16 @@ def test_random_sweep():
                 O.copy_heads(src, exp, op, reqs, l, s0, d0, nh)
             torch.cuda.synchronize()
             check_pool(gd, exp, (wl.name, "copy_heads", s0, d0, nh, l0))
+            plan.close()
+            # the same slice through a write queue, layers in a random order
+            gd = fresh(wl, dst)
+            plan = kvx.kvx_plan(gs.pool, gd.pool, toks, wl.src_tables, wl.dst_tables, overlap=overlap)
+            q = kvx.Queue()
+            for l in rng.permutation(L):
+                q.push_heads(plan, int(l), s0, d0, nh)
+            q.close()
+            torch.cuda.synchronize()
+            check_pool(gd, exp, (wl.name, "queue_heads", s0, d0, nh))
             plan.close()
         assert np.array_equal(gs.kv.cpu().numpy(), src.kv), (wl.name, "source changed")
         done += 1
