@@ -415,8 +415,9 @@ int kvx_push_many_timed(const kvx_plan_t* const* plans, const int32_t* layers, i
  * layer of tens of megabytes feels.  The queue therefore keeps at most two
  * launch groups of its writes in flight on its stream: a write that is ready
  * (its event has fired, or is NULL) while two groups still run waits in the
- * queue, and the ready writes at its front leave together, as one batched
- * launch of kvx_push_many, as soon as a group finishes.  A write whose event
+ * queue, and the ready writes at its front leave together, as one launch
+ * group (kvx_push_many's batched launches for pushes, kvx_copy_heads_layers'
+ * for head-slice writes), as soon as a group finishes.  A write whose event
  * has not fired blocks the writes queued behind it until it fires (writes
  * leave in queue order).  No write starts before its own event has fired;
  * writes of one group may run at the same time, so writes queued between
