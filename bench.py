@@ -450,6 +450,29 @@ def bench_push(args, torch, kvx, S, W):
         f"{groups_per_step:.2f} launch groups, {launches_per_step:.2f} launches per step: {gbs:.1f} GB/s = "
         f"{100 * gbs / HBM_PEAK_GBS:.1f}% of {HBM_PEAK_GBS:.0f} GB/s")
 
+    # Cold caches: each step after a 1 GiB fill of a scratch buffer on the
+    # side stream, which leaves none of the step's bytes in the L2s or the
+    # 256 MB MALL, timed from an event behind the fill to one behind the
+    # step.  Its counterpart is the span's second pass, which also has an
+    # event between consecutive steps.
+    scratch = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    marks = []
+    for i in range(args.steps):
+        B.fill(scratch, i & 0xFF, stream=side)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(side)
+        step()
+        b.record(side)
+        marks.append((a, b))
+    torch.cuda.synchronize()
+    cold = np.array([a.elapsed_time(b) for a, b in marks])
+    del scratch, marks
+    cold_stats = span_stats(cold, "each step after a 1 GiB fill of a scratch buffer on the side stream (outside "
+                                  "the timed interval); compare span.median_ms")
+    cold_stats["GBs_at_median"] = round(step_bytes / (cold_stats["median_ms"] * 1e-3) / 1e9, 1)
+    log(f"cold-cache steps: median {cold_stats['median_ms'] * 1e3:.1f} us ({cold_stats['GBs_at_median']} GB/s) "
+        f"against {stats['median_ms'] * 1e3:.1f} us in the span's second pass")
+
     # Kernel measurement for the roofline.  Once writes back up, the queue's
     # groups are kvx_push_many launches of 32 layers each (two per step); the
     # same launches, each timed from its own dispatch timestamps.
@@ -631,7 +654,8 @@ def bench_push(args, torch, kvx, S, W):
                    "fresh_event_push_layer_GBs": round(fresh_gbs, 1),
                    "graph_replay_push_layer_GBs": round(graph_gbs, 1),
                    "two_stream_push_layer_GBs": None if two_gbs is None else round(two_gbs, 1),
-                   "push_many_all_layers_GBs": round(many_gbs, 1)},
+                   "push_many_all_layers_GBs": round(many_gbs, 1),
+                   "cold_cache_steps": cold_stats},
         "ceiling": ceiling,
         "roofline": roofline(round(k_bytes), k_avg_us, "kvx::copy_many_kernel<0> (kvx_queue groups / kvx_push_many)",
                              args.workload,
