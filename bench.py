@@ -1648,6 +1648,9 @@ def main():
     r = fn(args, torch, kvx, S, W)
     if r is None:
         return
+    # Every step copies: what it reads (payload and scales) it writes once.
+    if "bytes_per_step" in r["config"]:
+        r["config"]["bytes_read_per_step"] = r["config"]["bytes_written_per_step"] = r["config"]["bytes_per_step"] // 2
     out = {
         "metric": METRIC, "value": round(r["value"], 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(r["ms_per_step"], 4), "higher_is_better": True,
