@@ -6,7 +6,8 @@ draws a geometry of one of three kinds:
     tails, scales), whose plans take the 4 KiB shape;
   - different block sizes and head counts per side (head transform only).
 Each case is built with or without KVX_PLAN_OVERLAP and with or without
-KVX_PLAN_RUNS (streaming plans then read run tables). Where both pools have
+KVX_PLAN_RUNS (streaming plans then read run tables; a head transform
+reads its block pairs either way). Where both pools have
 the same head count and layout, its requests are pushed layer by layer.
 They are also split into two plans with disjoint destinations, whose layers
 go out in one kvx_push_many call, and packed and unpacked over a random
@@ -149,7 +150,7 @@ def test_random_sweep():
             plan.close()
         else:
             gd = fresh(wl, dst)
-            plan = kvx.kvx_plan(gs.pool, gd.pool, toks, wl.src_tables, wl.dst_tables, overlap=overlap)
+            plan = kvx.kvx_plan(gs.pool, gd.pool, toks, wl.src_tables, wl.dst_tables, overlap=overlap, runs=runs)
             nh = int(rng.integers(1, min(wl.src.num_heads, wl.dst.num_heads) + 1))
             s0 = int(rng.integers(0, wl.src.num_heads - nh + 1))
             d0 = int(rng.integers(0, wl.dst.num_heads - nh + 1))
@@ -165,7 +166,7 @@ def test_random_sweep():
             plan.close()
             # the same slice through a write queue, layers in a random order
             gd = fresh(wl, dst)
-            plan = kvx.kvx_plan(gs.pool, gd.pool, toks, wl.src_tables, wl.dst_tables, overlap=overlap)
+            plan = kvx.kvx_plan(gs.pool, gd.pool, toks, wl.src_tables, wl.dst_tables, overlap=overlap, runs=runs)
             q = kvx.Queue()
             for l in rng.permutation(L):
                 q.push_heads(plan, int(l), s0, d0, nh)
