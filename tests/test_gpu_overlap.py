@@ -6,7 +6,6 @@ source blocks, and the compute stream records ev[l].  kvx_push_layer(l,
 ready=ev[l]) on a side stream must deliver the canary: the write waits for the
 layer's event ([MORI] 3.2).  Also: two plans with disjoint destinations pushed
 concurrently on two streams give the same bytes as one after the other."""
-import sys
 
 import numpy as np
 import pytest

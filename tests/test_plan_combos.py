@@ -1,7 +1,6 @@
 """Host-only planning against the oracle on random cases that combine the
 geometry options (regions, sliding window, block sizes per side, scales,
 layouts, null entries of dropped blocks)."""
-import numpy as np
 
 import oracle as O
 import oracle_pins as P
